@@ -1,0 +1,455 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Every test here runs on the CPU. Each one is chosen so that a plausible mistake
+in the oracle (a dropped term, a wrong sign or index, half-even instead of
+half-away rounding, truncation, a transposed operand, a wrong clip range)
+fails it. Pages: [IS] Integer Scale summary page, [QB] "量化基礎" blog,
+[QN] "Quantization" notes.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def golden(name):
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                k, v = (t.strip() for t in line.split("="))
+                out[k] = int(v)
+    return out
+
+
+# ------------------------------------------------------------------ O1 symmetric int8
+
+def test_sym_hand_vector_ties_round_half_away(orc):
+    # absmax 127 -> s = 1 exactly; ties +-0.5 and 2.5 go away from zero ("四舍五入",
+    # [QB] §2.2); half-even would give 0, 0, 2 instead.
+    x = np.array([[127.0, 0.5, -0.5, 2.5, -63.5, 1.49, -126.6]], np.float32)
+    q, s = orc.quant_sym_i8(x)
+    assert s[0] == np.float32(1.0)
+    assert q.tolist() == [[127, 1, -1, 3, -64, 1, -127]]
+
+
+def test_sym_range_and_absmax_maps_to_qmax(orc):
+    r = golden("quant_ranges.txt")
+    x = synth.activations(3, 33, 1000)
+    x[5, 17] = -1e3      # the row's absmax is negative
+    q, s = orc.quant_sym_i8(x)
+    assert q.min() >= r["sym_int8_qmin"] and q.max() <= r["sym_int8_qmax"]
+    am = np.abs(x).argmax(axis=1)
+    picked = q[np.arange(33), am].astype(int)
+    assert np.all(np.abs(picked) == 127)
+    assert picked[5] == -127
+    np.testing.assert_array_equal(s, (np.abs(x).max(axis=1) / np.float32(127.0)).astype(np.float32))
+
+
+def test_sym_rounding_error_bound_and_sign(orc):
+    # |x - s q| <= s/2 (plus one float rounding of x/s); truncation would break it.
+    x = synth.activations(4, 64, 512)
+    q, s = orc.quant_sym_i8(x)
+    err = np.abs(x.astype(np.float64) - s[:, None].astype(np.float64) * q)
+    assert np.all(err <= s[:, None] * (0.5 + 2.0 ** -20))
+    assert np.all((q == 0) | (np.sign(q) == np.sign(x)))
+
+
+def test_sym_error_variance_is_s2_over_12(orc):
+    # [QB] §2.2 quantization error: sigma^2 ~ s^2/12 for round-to-nearest.
+    # A uniform row makes the rounding error uniform on [-s/2, s/2].
+    g = synth.rng(11, 99)
+    x = g.uniform(-1.0, 1.0, size=(1, 1_000_000)).astype(np.float32)
+    q, s = orc.quant_sym_i8(x)
+    mse = np.mean((x.astype(np.float64) - float(s[0]) * q) ** 2)
+    assert abs(mse / (float(s[0]) ** 2 / 12.0) - 1.0) < 0.05
+
+
+def test_sym_zero_row(orc):
+    x = np.zeros((2, 64), np.float32)
+    x[1, 3] = 2.0
+    q, s = orc.quant_sym_i8(x)
+    assert s[0] == 0 and not q[0].any()
+    assert q[1, 3] == 127 and s[1] == np.float32(2.0) / np.float32(127.0)
+
+
+# ----------------------------------------------------------------- O5 asymmetric uint8
+
+def test_asym_hand_vector(orc):
+    # x_min = -1, x_max = 254: s = 255/255 = 1, z = round(0 - (-1)/1) = 1.
+    x = np.array([[-1.0, 254.0, 0.0, 0.5, -0.5, 100.4]], np.float32)
+    q, s, z, rs = orc.quant_asym_u8(x)
+    assert s[0] == 1.0 and z[0] == 1
+    # round(x/s) + z: 0.5 -> 1+1, -0.5 -> -1+1 (half away from zero, then add z)
+    assert q.tolist() == [[0, 255, 1, 2, 0, 101]]
+    assert rs[0] == sum(q[0].astype(int))
+
+
+def test_asym_min_max_map_to_ends(orc):
+    r = golden("quant_ranges.txt")
+    x = synth.activations(5, 40, 777, outlier_frac=0.0, mean=0.5)
+    q, s, z, rs = orc.quant_asym_u8(x)
+    assert q.min() >= r["asym_uint8_qmin"] and q.max() <= r["asym_uint8_qmax"]
+    i = np.arange(40)
+    assert np.all(q[i, x.argmin(axis=1)] == 0)
+    assert np.all(q[i, x.argmax(axis=1)] >= 254)
+    np.testing.assert_array_equal(rs, q.astype(np.int64).sum(axis=1))
+    # dequantization s(q - z) is within half a step of x, except clipped top codes
+    xh = s[:, None].astype(np.float64) * (q.astype(np.int64) - z[:, None])
+    err = np.abs(x - xh)
+    ok = err <= s[:, None] * (0.5 + 2.0 ** -18)
+    assert np.all(ok | (q == 255))
+
+
+def test_asym_degenerate_row(orc):
+    x = np.full((1, 16), 3.0, np.float32)
+    q, s, z, rs = orc.quant_asym_u8(x)
+    assert s[0] == 0 and z[0] == 0 and rs[0] == 0 and not q.any()
+
+
+# --------------------------------------------------------------- O2 int4 group quant
+
+def test_group_scale_count_matches_page():
+    f = golden("is_method_facts.txt")
+    G = f["layer_k"] // f["group"]
+    assert G * f["layer_n"] == f["float_scale_count"]
+
+
+def test_group_quant_shapes_and_count(orc):
+    f = golden("is_method_facts.txt")
+    w = synth.weights(0, 512, 64)
+    codes, fs = orc.group_quant_int4(w, 128)
+    assert fs.shape == (4, 64) and codes.shape == (512, 64)
+    # the page's 4096x4096 count, from the oracle's own shape rule
+    assert (f["layer_k"] // f["group"]) * f["layer_n"] == f["float_scale_count"]
+
+
+def test_group_quant_hand_group(orc):
+    # one column, one group of 128: absmax 7 -> s = 1; ties away from zero; clip [-7,7]
+    w = np.zeros((128, 16), np.float32)
+    w[:8, 0] = [7.0, 3.5, -3.5, 0.5, -0.49, -7.0, 6.6, 2.5]
+    w[:, 1] = np.linspace(-1, 1, 128)
+    codes, fs = orc.group_quant_int4(w, 128)
+    assert fs[0, 0] == 1.0
+    assert codes[:8, 0].tolist() == [7, 4, -4, 1, 0, -7, 7, 3]
+    assert fs[0, 2] == 0 and not codes[:, 2].any()          # all-zero group
+    assert codes[:, 1].min() == -7 and codes[:, 1].max() == 7
+
+
+def test_group_quant_bound_and_grouping(orc):
+    w = synth.weights(1, 384, 48, outlier_prob=0.01)
+    codes, fs = orc.group_quant_int4(w, 128)
+    for l in range(3):
+        blk = w[128 * l:128 * (l + 1)]
+        np.testing.assert_array_equal(fs[l], (np.abs(blk).max(axis=0) / np.float32(7)).astype(np.float32))
+        err = np.abs(blk.astype(np.float64) - fs[l].astype(np.float64) * codes[128 * l:128 * (l + 1)])
+        assert np.all(err <= fs[l] * (0.5 + 2.0 ** -20))
+    assert codes.min() >= -7 and codes.max() <= 7
+
+
+# ------------------------------------------------------------------ packed layout
+
+def test_pack_unpack_roundtrip_all_codes(orc):
+    K, N = 256, 32
+    g = synth.rng(7, 1)
+    codes = g.integers(-8, 8, size=(K, N)).astype(np.int8)
+    codes[0, :16] = np.arange(-8, 8)
+    p = orc.pack_int4(codes)
+    assert p.size == N * K // 2
+    np.testing.assert_array_equal(orc.unpack_int4(p, K, N), codes)
+
+
+@pytest.mark.parametrize("k,j,byte,high", [
+    (0, 0, 0, False), (4, 0, 0, True), (1, 0, 1, False), (7, 0, 3, True),
+    (8, 0, 4, False), (12, 0, 4, True), (15, 0, 7, True),
+    (64, 0, 8, False), (16, 0, 256, False), (0, 1, 16, False), (48, 15, 3 * 256 + 15 * 16, False),
+    (128, 0, 1024, False), (0, 16, 2 * 1024, False), (127, 31, 2048 + 1023, True),
+    (255, 31, 2048 + 1024 + 1023, True),
+])
+def test_pack_layout_positions(orc, k, j, byte, high):
+    # K=256 (G=2), N=32 (2 column tiles): single code 5 at (k, j), all others 0
+    K, N = 256, 32
+    codes = np.zeros((K, N), np.int8)
+    codes[k, j] = 5
+    p = orc.pack_int4(codes)
+    nz = np.flatnonzero(p)
+    assert nz.tolist() == [byte]
+    assert p[byte] == (0x50 if high else 0x05)
+
+
+def test_pack_twos_complement(orc):
+    codes = np.zeros((128, 16), np.int8)
+    codes[0, 0], codes[4, 0] = -1, -8
+    p = orc.pack_int4(codes)
+    assert p[0] == 0x8F
+
+
+# --------------------------------------------------------------- amplifier search
+
+def _search_as_printed(scale_min):
+    # the procedure printed on the [IS] 方法 page, executed as written
+    n, tmp = 0, scale_min
+    while tmp < 1:
+        tmp = scale_min * (2 ** n)
+        n += 1
+    return 2 ** (n - 1)
+
+
+@pytest.mark.parametrize("smin", [0.3, 2.0 ** -10, 0.001, 0.0009, 0.5, 0.75, 2.0 ** -20 * 1.5, 0.999])
+def test_amplifier_matches_printed_search(orc, smin):
+    f = np.array([[smin, 0.9, 5.0], [0.0, 1.0, 0.4 + smin]], np.float32)
+    n = orc.amplifier_log2(f)
+    assert 2 ** n == _search_as_printed(float(np.float32(smin)))
+    s = float(np.float32(smin))
+    assert s * 2 ** n >= 1 and s * 2 ** (n - 1) < 1           # smallest such power
+
+
+def test_amplifier_closed_form_sweep(orc):
+    g = synth.rng(3, 3)
+    for v in g.uniform(1e-7, 0.999, 500).astype(np.float32):
+        m, e = math.frexp(float(v))                     # v = m 2^e, m in [0.5, 1)
+        assert orc.amplifier_log2(np.array([v], np.float32)) == 1 - e
+
+
+def test_amplifier_edges(orc):
+    # scales already >= 1: the printed code would return 2^-1; the text says the
+    # search starts from 1, so the amplifier is 1. Zero scales are ignored.
+    assert orc.amplifier_log2(np.array([1.0, 3.0], np.float32)) == 0
+    assert orc.amplifier_log2(np.array([0.0, 0.0], np.float32)) == 0
+    assert orc.amplifier_log2(np.array([0.0, 0.25], np.float32)) == 2
+    assert orc.amplifier_log2(np.array([2.0 ** -40], np.float32), 30) == -1
+
+
+def test_default_amplifier_and_iscale_width(orc):
+    f = golden("is_method_facts.txt")
+    assert f["default_amplifier"] == 2 ** f["amplifier_log2"]
+    w = synth.weights(0, 1024, 512, outlier_prob=0.001)
+    _, fs = orc.group_quant_int4(w, 128)
+    isc = orc.integer_scales(fs, f["default_amplifier"])
+    assert isc.min() >= 0 and int(isc.max()) < 2 ** f["iscale_bits_max"]
+    # round half away on s*alpha, exact product
+    prod = fs.astype(np.float64) * f["default_amplifier"]
+    assert np.all(np.abs(isc - prod) <= 0.5)
+    ties = np.array([[0.5 / 1024, 1.5 / 1024, 2.5 / 1024]], np.float32)
+    assert orc.integer_scales(ties, 1024).tolist() == [[1, 2, 3]]
+
+
+# -------------------------------------------------------------------- O3 IS GEMM
+
+def _tiny_case(seed, M, K, N, iscale_hi=300):
+    g = synth.rng(seed, 50)
+    qx = g.integers(-127, 128, size=(M, K)).astype(np.int8)
+    qw = g.integers(-7, 8, size=(K, N)).astype(np.int8)
+    isc = g.integers(0, iscale_hi, size=(K // 128, N)).astype(np.int32)
+    sx = g.uniform(0.001, 0.1, size=M).astype(np.float32)
+    return qx, qw, isc, sx
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 128, 1), (2, 256, 3), (3, 256, 2), (3, 384, 5)])
+def test_is_brute_force_ungrouped(orc, M, K, N):
+    # distributivity: sum_l iscale_l sum_{k in l} qx qw == sum_k qx qw iscale_{l(k)}
+    qx, qw, isc, sx = _tiny_case(M * 7 + K + N, M, K, N)
+    A, y, ov = orc.w4a8_gemm_is(qx, sx, qw, isc, 1024)
+    ref = np.zeros((M, N), np.int64)
+    for i in range(M):
+        for j in range(N):
+            ref[i, j] = sum(int(qx[i, k]) * int(qw[k, j]) * int(isc[k // 128, j]) for k in range(K))
+    np.testing.assert_array_equal(A, ref)
+    assert ov == 0
+
+
+def test_is_unit_scales_is_int_matmul(orc):
+    qx, qw, _, sx = _tiny_case(1, 9, 512, 20)
+    isc = np.ones((4, 20), np.int32)
+    A, _, _ = orc.w4a8_gemm_is(qx, sx, qw, isc, 1)
+    np.testing.assert_array_equal(A, qx.astype(np.int64) @ qw.astype(np.int64))
+
+
+def test_is_single_group_is_per_channel(orc):
+    qx, qw, isc, sx = _tiny_case(2, 5, 128, 12)
+    A, y, _ = orc.w4a8_gemm_is(qx, sx, qw, isc, 1024)
+    np.testing.assert_array_equal(A, (qx.astype(np.int64) @ qw.astype(np.int64)) * isc[0][None, :])
+
+
+def test_is_output_closed_form(orc):
+    # y = RN(float(A) * s) * 2^-10; the double product of two floats is exact,
+    # so float32(double product) is the single rounding.
+    qx, qw, isc, sx = _tiny_case(3, 7, 512, 33, iscale_hi=130)
+    A, y, _ = orc.w4a8_gemm_is(qx, sx, qw, isc, 1024)
+    Af = A.astype(np.int32).astype(np.float32).astype(np.float64)
+    ref = (Af * sx[:, None].astype(np.float64)).astype(np.float32) * np.float32(2.0 ** -10)
+    np.testing.assert_array_equal(y, ref)
+
+
+def test_is_row_col_selection(orc):
+    qx, qw, isc, sx = _tiny_case(4, 6, 256, 10)
+    A, y, _ = orc.w4a8_gemm_is(qx, sx, qw, isc, 1024)
+    rows, cols = [5, 0, 3], [9, 2]
+    A2, y2, _ = orc.w4a8_gemm_is(qx, sx, qw, isc, 1024, rows=rows, cols=cols)
+    np.testing.assert_array_equal(A2, A[np.ix_(rows, cols)])
+    np.testing.assert_array_equal(y2, y[np.ix_(rows, cols)])
+
+
+def test_is_overflow_flag_and_wrap(orc):
+    r = golden("quant_ranges.txt")
+    # int32 accumulator ([QB] §1.4); crafted maximal codes push A past 2^31
+    M, K, N = 2, 4096, 3
+    qx = np.full((M, K), 127, np.int8)
+    qw = np.full((K, N), 7, np.int8)
+    isc = np.full((K // 128, N), 600, np.int32)
+    isc[:, 2] = 500
+    sx = np.ones(M, np.float32)
+    A, y, ov = orc.w4a8_gemm_is(qx, sx, qw, isc, 1)
+    assert A[0, 0] == 32 * 128 * 127 * 7 * 600 and A[0, 0] >= 2 ** (r["accumulator_bits"] - 1)
+    assert A[0, 2] < 2 ** 31
+    assert ov == M * 2
+    wrapped = ((A[0, 0] + 2 ** 31) % 2 ** 32) - 2 ** 31
+    assert y[0, 0] == np.float32(wrapped)
+
+
+def test_is_equals_fs_when_scales_are_exact(orc):
+    # weights built so that s * alpha is an integer: then integer and float scales agree
+    # exactly (every partial float sum is a multiple of 2^-10 below 2^24 * 2^-10)
+    M, K, N = 4, 512, 24
+    g = synth.rng(9, 9)
+    m = g.integers(1, 200, size=(K // 128, N))
+    w = g.uniform(-1, 1, size=(K, N)).astype(np.float32)
+    for l in range(K // 128):
+        blk = w[128 * l:128 * (l + 1)]
+        blk /= np.abs(blk).max(axis=0)
+        blk *= (7.0 * m[l] / 1024.0).astype(np.float32)
+        blk[0] = (7.0 * m[l] / 1024.0).astype(np.float32)
+    codes, fs = orc.group_quant_int4(w, 128)
+    np.testing.assert_array_equal(fs.astype(np.float64) * 1024, m)
+    isc = orc.integer_scales(fs, 1024)
+    x = synth.activations(9, M, K)
+    qx, sx = orc.quant_sym_i8(x)
+    _, y_is, _ = orc.w4a8_gemm_is(qx, sx, codes, isc, 1024)
+    y_fs = orc.w4a8_gemm_fs(qx, sx, codes, fs)
+    np.testing.assert_array_equal(y_is, y_fs)
+
+
+def _dequant_matmul(qx, sx, codes, fs):
+    wq = codes.astype(np.float64) * np.repeat(fs.astype(np.float64), 128, axis=0)
+    return (qx.astype(np.float64) * sx[:, None].astype(np.float64)) @ wq
+
+
+def test_is_error_bound_vs_float_scales(orc):
+    # |y_IS - y_exact| <= s_i/alpha * sum_l |p_l| |iscale - alpha s_l| + fp32 rounding
+    x, w = synth.single_gemm_inputs(0)
+    x, w = x[:4], w[:, :96]
+    codes, fs = orc.group_quant_int4(w)
+    isc = orc.integer_scales(fs, 1024)
+    qx, sx = orc.quant_sym_i8(x)
+    _, y, _ = orc.w4a8_gemm_is(qx, sx, codes, isc, 1024)
+    exact = _dequant_matmul(qx, sx, codes, fs)
+    G = fs.shape[0]
+    p = np.stack([qx[:, 128 * l:128 * (l + 1)].astype(np.int64) @ codes[128 * l:128 * (l + 1)].astype(np.int64)
+                  for l in range(G)])                       # G x M x N
+    dev = np.abs(isc.astype(np.float64) - 1024 * fs.astype(np.float64))   # G x N
+    bound = sx[:, None] / 1024.0 * np.einsum("lmn,ln->mn", np.abs(p), dev)
+    bound += np.abs(exact) * 2.0 ** -22 + 1e-30
+    assert np.all(np.abs(y - exact) <= bound)
+
+
+def test_is_full_path_approximates_matmul(orc):
+    # the method approximates Y = X W ([IS] 方法 Fig. 3): relative Frobenius error of the
+    # W4A8 integer-scale path against the float64 product stays at int4 rounding level
+    x, w = synth.single_gemm_inputs(0)
+    x, w = x[:8], w[:, :256]
+    pw = orc.pack_weights(w, 128, 1024)
+    qx, sx = orc.quant_sym_i8(x)
+    _, y, _ = orc.w4a8_gemm_is(qx, sx, pw["codes"], pw["iscale"], pw["alpha"])
+    ref = x.astype(np.float64) @ w.astype(np.float64)
+    rel = np.linalg.norm(y - ref) / np.linalg.norm(ref)
+    assert 0.02 < rel < 0.2          # int4 weights: a few percent, never exact
+
+
+# -------------------------------------------------------------------- O4 FS GEMM
+
+def test_fs_fma_chain_small_case(orc):
+    # two groups, hand-checkable: p0 = 3, p1 = -2 with scales 0.5, 0.25 -> 1.0, times s=2
+    qx = np.zeros((1, 256), np.int8)
+    qw = np.zeros((256, 16), np.int8)
+    qx[0, 0], qw[0, 0] = 3, 1
+    qx[0, 130], qw[130, 0] = -2, 1
+    fs = np.full((2, 16), 0.5, np.float32)
+    fs[1, 0] = 0.25
+    y = orc.w4a8_gemm_fs(qx, np.array([2.0], np.float32), qw, fs)
+    assert y[0, 0] == np.float32(2.0) and not y[0, 1:].any()
+
+
+def test_fs_close_to_exact(orc):
+    x, w = synth.single_gemm_inputs(1)
+    x, w = x[:3], w[:, :64]
+    codes, fs = orc.group_quant_int4(w)
+    qx, sx = orc.quant_sym_i8(x)
+    y = orc.w4a8_gemm_fs(qx, sx, codes, fs)
+    exact = _dequant_matmul(qx, sx, codes, fs)
+    G = fs.shape[0]
+    mag = _dequant_matmul(np.abs(qx), sx, np.abs(codes), fs)
+    assert np.all(np.abs(y - exact) <= (G + 2) * 2.0 ** -24 * mag + 1e-30)
+
+
+# ------------------------------------------------------------------- O5 W8A8 ZP
+
+def _w8a8_case(orc, seed, M, K, N, relu=False):
+    x, w = synth.w8a8_inputs(seed, M, K, N, relu=relu)
+    qx, sx, zx, rx = orc.quant_asym_u8(x)
+    qw, sw, zw, cw = orc.quant_asym_u8(np.ascontiguousarray(w.T))
+    return x, w, (qx, sx, zx, rx, qw, sw, zw, cw)
+
+
+def test_w8a8_expansion_identity(orc):
+    # [QN] 矩阵乘法中的量化计算: the expanded four-term form equals the direct
+    # product of zero-point-shifted codes, exactly in integers
+    _, _, (qx, sx, zx, rx, qw, sw, zw, cw) = _w8a8_case(orc, 0, 7, 384, 21)
+    A, y, ov = orc.w8a8_gemm_zp(qx, sx, zx, rx, qw, sw, zw, cw)
+    direct = (qx.astype(np.int64) - zx[:, None]) @ (qw.astype(np.int64) - zw[:, None]).T
+    np.testing.assert_array_equal(A, direct)
+    assert ov == 0
+    assert zx.min() > 0 and zw.min() > 0                      # all four terms live
+    ref = (A.astype(np.float32) * (sx[:, None] * sw[None, :])).astype(np.float32)
+    np.testing.assert_array_equal(y, ref)
+
+
+def test_w8a8_zero_points_zero_reduce_to_plain_product(orc):
+    g = synth.rng(2, 2)
+    qx = g.integers(0, 256, size=(5, 256)).astype(np.uint8)
+    qw = g.integers(0, 256, size=(6, 256)).astype(np.uint8)
+    z5, z6 = np.zeros(5, np.int32), np.zeros(6, np.int32)
+    A, _, _ = orc.w8a8_gemm_zp(qx, np.ones(5, np.float32), z5, qx.sum(1).astype(np.int32),
+                               qw, np.ones(6, np.float32), z6, qw.sum(1).astype(np.int32))
+    np.testing.assert_array_equal(A, qx.astype(np.int64) @ qw.astype(np.int64).T)
+
+
+def test_w8a8_recentred_codes_same_accumulator(orc):
+    # shifting codes and zero points by 128 leaves every (q - z) unchanged
+    _, _, (qx, sx, zx, rx, qw, sw, zw, cw) = _w8a8_case(orc, 1, 4, 256, 9)
+    A, _, _ = orc.w8a8_gemm_zp(qx, sx, zx, rx, qw, sw, zw, cw)
+    sx_ = (qx.astype(np.int64) - 128)
+    sw_ = (qw.astype(np.int64) - 128)
+    direct = (sx_ - (zx[:, None] - 128)) @ (sw_ - (zw[:, None] - 128)).T
+    np.testing.assert_array_equal(A, direct)
+    assert np.abs(A).max() <= 256 * 255 ** 2
+
+
+def test_w8a8_relu_activations_zero_point_zero(orc):
+    x, w, (qx, sx, zx, rx, qw, sw, zw, cw) = _w8a8_case(orc, 0, 16, 256, 8, relu=True)
+    assert np.all(zx == 0)
+    A, y, _ = orc.w8a8_gemm_zp(qx, sx, zx, rx, qw, sw, zw, cw)
+    ref = x.astype(np.float64) @ w.astype(np.float64)
+    assert np.linalg.norm(y - ref) / np.linalg.norm(ref) < 0.05
+
+
+def test_w8a8_approximates_matmul(orc):
+    x, w, (qx, sx, zx, rx, qw, sw, zw, cw) = _w8a8_case(orc, 3, 16, 512, 32)
+    _, y, _ = orc.w8a8_gemm_zp(qx, sx, zx, rx, qw, sw, zw, cw)
+    ref = x.astype(np.float64) @ w.astype(np.float64)
+    assert np.linalg.norm(y - ref) / np.linalg.norm(ref) < 0.05
