@@ -1,0 +1,271 @@
+"""Benchmark of the W4A8 integer-scale linear layer on one MI355X.
+
+Default workload (the decode-regime sweep): the K=4096, N=22016 layer with
+group 128 and amplifier 1024; one step is one pass of the hot path for every
+M in {1, 4, 16, 64, 256}: per-token int8 quantization of X (M x 4096 fp32)
+followed by the integer-scale W4A8 GEMM. Weights are packed once before
+timing (the offline step) and then replicated into R buffers whose total
+exceeds twice the 256 MB Infinity Cache; consecutive GEMMs read different
+buffers, so weight bytes come from HBM.
+
+value = algorithmic bytes of one step / step time (GB/s); the per-launch
+algorithmic bytes of a W4A8 GEMM are N*K/2 (packed int4) + 4*G*N (integer
+scales) + M*K (int8 codes) + 4*M (token scales) + 4*M*N (fp32 output), and
+5*M*K + 4*M for the activation quantizer.
+
+Other workloads (--workload): prefill (M in 512..4096, integer- and
+float-scale GEMMs side by side; value in TOPS), single (M=16, K=N=4096),
+w8a8 (asymmetric W8A8 control, M=256, K=N=4096), block (LLaMA-2-7B decoder
+block linears at M=1 and M=512).
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, TOP/s
+MALL_BYTES = 256 << 20
+METRIC = "W4A8 integer-scale GEMM TOPS + HBM GB/s, K=4096 N=22016, M=1..4096"
+
+
+def gemm_bytes(M, N, K):
+    G = K // 128
+    return N * K // 2 + 4 * G * N + M * K + 4 * M + 4 * M * N
+
+
+def quant_bytes(M, K):
+    return 5 * M * K + 4 * M
+
+
+def gemm_ops(M, N, K):
+    return 2 * M * N * K
+
+
+def skinny_kernel_name(M, fs=False):
+    if M > 64:
+        return "k_gemm_tiled<2, 2, %s>" % ("FS" if fs else "IS")
+    mr = (M + 15) // 16
+    return "k_w4a8_skinny<%d, %d, %s>" % (mr, 1 if fs else 4, "true" if fs else "false")
+
+
+# --------------------------------------------------------------------- CPU side
+def cpu_baseline(x, w, M=16, ncols=2048):
+    """Time the oracle on a bounded sample of the decode workload."""
+    import oracle
+    oracle.build()
+    cols = np.arange(ncols)
+    K = x.shape[1]
+    xs = np.ascontiguousarray(x[:M])
+    ws = np.ascontiguousarray(w[:, :ncols])
+    t0 = time.perf_counter()
+    q, s = oracle.quant_sym_i8(xs)
+    pw = oracle.pack_weights(ws, 128, 1024)
+    t1 = time.perf_counter()
+    oracle.w4a8_gemm_is(q, s, pw["codes"], pw["iscale"], pw["alpha"], cols=cols)
+    t2 = time.perf_counter()
+    byts = quant_bytes(M, K) + gemm_bytes(M, ncols, K)
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    gemm_s = t2 - t1
+    return {
+        "value": round(byts / ((t2 - t1) + 0.0) / 1e9 if False else byts / (gemm_s + (t1 - t0) * 0) / 1e9, 4),
+        "unit": "GB/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"quant_act + w4a8_gemm_is, M={M} rows x {ncols} of 22016 columns, K={K} "
+                  f"(GEMM {gemm_s:.2f} s; offline packing excluded)",
+    }
+
+
+# --------------------------------------------------------------------- GPU side
+class Rotor:
+    """R copies of the packed weights and integer scales (same values, distinct memory)."""
+
+    def __init__(self, torch, packed, iscale, fscale, min_bytes=2 * MALL_BYTES):
+        per = packed.numel() + iscale.numel() * 4 + fscale.numel() * 4
+        self.R = max(2, math.ceil(min_bytes / per))
+        self.bufs = [(packed.clone(), iscale.clone(), fscale.clone()) for _ in range(self.R)]
+        self.i = 0
+
+    def next(self):
+        b = self.bufs[self.i % self.R]
+        self.i += 1
+        return b
+
+
+def run_decode(args, torch, bgt, dev):
+    K, N = synth.K_LAYER, synth.N_LAYER
+    Ms = list(synth.DECODE_M)
+    x, w = synth.layer_inputs(0, M=max(Ms), K=K, N=N)
+    xd = torch.from_numpy(x).to(dev)
+    xs = {M: xd[:M].contiguous() for M in Ms}
+    pw = bgt.pack_weights_int4(torch.from_numpy(w).to(dev), alpha=synth.ALPHA)
+    rot = Rotor(torch, pw["packed"], pw["iscale"], pw["fscale"])
+    qbuf = {M: (torch.empty((M, K), dtype=torch.int8, device=dev),
+                torch.empty(M, dtype=torch.float32, device=dev)) for M in Ms}
+    ybuf = {M: torch.empty((M, N), dtype=torch.float32, device=dev) for M in Ms}
+
+    def step(events=None):
+        for M in Ms:
+            q, s = qbuf[M]
+            bgt.quantize_act(xs[M], q=q, scale=s)
+            packed, iscale, _ = rot.next()
+            if events is not None:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+            bgt.w4a8_gemm_is(q, s, packed, iscale, pw["alpha"], N, y=ybuf[M])
+            if events is not None:
+                e1.record()
+                events.append((M, e0, e1))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(events)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+
+    per_m = {M: [] for M in Ms}
+    for M, e0, e1 in events:
+        per_m[M].append(e0.elapsed_time(e1) * 1e3)     # us
+    step_bytes = sum(gemm_bytes(M, N, K) + quant_bytes(M, K) for M in Ms)
+    sweep = {}
+    for M in Ms:
+        us = float(np.median(per_m[M]))
+        b = gemm_bytes(M, N, K)
+        sweep[str(M)] = {"gemm_us_median": round(us, 3), "gemm_GBps": round(b / us / 1e3, 1),
+                         "gemm_TOPS": round(gemm_ops(M, N, K) / us / 1e6, 2),
+                         "hbm_frac": round(b / us / 1e3 / HBM_PEAK_GBS, 4),
+                         "kernel": skinny_kernel_name(M)}
+    # dominant GEMM kernel: largest summed time over the step
+    by_kernel = {}
+    for M in Ms:
+        k = skinny_kernel_name(M)
+        by_kernel.setdefault(k, []).append(M)
+    dom = max(by_kernel, key=lambda k: sum(np.mean(per_m[M]) for M in by_kernel[k]))
+    dMs = by_kernel[dom]
+    durs = [u for M in dMs for u in per_m[M]]
+    avg_us = float(np.mean(durs))
+    avg_bytes = float(np.mean([gemm_bytes(M, N, K) for M in dMs]))
+    achieved = avg_bytes / avg_us / 1e3
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": dom, "launch_M": dMs, "avg_launch_us": round(avg_us, 3),
+            "bytes_per_launch": int(avg_bytes)}
+    out = {
+        "metric": METRIC, "value": round(step_bytes / (ms_step * 1e-3) / 1e9, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8xint4->int32",
+        "data": "synthetic (seeded; X ~N(0,1) + 1% channels x20, W ~N(0,0.02) + 0.1% x10)",
+        "config": {"workload": "decode sweep: W4A8-IS quant_act + GEMM, K=4096 N=22016 g=128 "
+                               "alpha=1024, M in {1,4,16,64,256} per step",
+                   "weight_buffers_rotated": rot.R},
+        "roofline": roof, "sweep": sweep,
+    }
+    return out, (x, w)
+
+
+def run_prefill(args, torch, bgt, dev):
+    K, N = synth.K_LAYER, synth.N_LAYER
+    Ms = list(synth.PREFILL_M)
+    x, w = synth.layer_inputs(0, M=max(Ms), K=K, N=N)
+    xd = torch.from_numpy(x).to(dev)
+    pw = bgt.pack_weights_int4(torch.from_numpy(w).to(dev), alpha=synth.ALPHA)
+    rot = Rotor(torch, pw["packed"], pw["iscale"], pw["fscale"])
+    qs = {M: bgt.quantize_act(xd[:M].contiguous())[:2] for M in Ms}
+    ys = {M: torch.empty((M, N), dtype=torch.float32, device=dev) for M in Ms}
+    res = {}
+    tot_ops = 0
+    tot_us = 0.0
+    for fs in (False, True):
+        for M in Ms:
+            q, s = qs[M]
+            ts = []
+            for it in range(args.warmup + args.steps):
+                packed, iscale, fscale = rot.next()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                if fs:
+                    bgt.w4a8_gemm_fs(q, s, packed, fscale, N, y=ys[M])
+                else:
+                    bgt.w4a8_gemm_is(q, s, packed, iscale, pw["alpha"], N, y=ys[M])
+                e1.record()
+                if it >= args.warmup:
+                    ts.append((e0, e1))
+            torch.cuda.synchronize()
+            us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in ts]))
+            tops = gemm_ops(M, N, K) / us / 1e6
+            res[("fs" if fs else "is") + str(M)] = {
+                "us_median": round(us, 2), "TOPS": round(tops, 1),
+                "mfma_frac": round(tops / INT8_PEAK_TOPS, 4), "kernel": skinny_kernel_name(M, fs)}
+            if not fs:
+                tot_ops += gemm_ops(M, N, K)
+                tot_us += us
+    big = max(Ms)
+    r = res["is%d" % big]
+    out = {
+        "metric": METRIC, "value": round(tot_ops / tot_us / 1e6, 1), "unit": "TOPS",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(tot_us / 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8xint4->int32", "data": "synthetic (seeded)",
+        "config": {"workload": "prefill sweep: W4A8-IS GEMM K=4096 N=22016, M in {512,1024,2048,4096}"},
+        "roofline": {"bound": "mfma", "achieved": r["TOPS"], "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
+                     "frac": r["mfma_frac"], "traffic": None, "kernel": r["kernel"], "launch_M": [big],
+                     "avg_launch_us": r["us_median"]},
+        "sweep": res,
+    }
+    return out, (x, w)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode", choices=["decode", "prefill"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer shards column-parallel with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bit_gemm_token_amd as bgt
+    bgt.lib()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    if args.workload == "decode":
+        out, (x, w) = run_decode(args, torch, bgt, dev)
+    else:
+        out, (x, w) = run_prefill(args, torch, bgt, dev)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(x, w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,239 @@
+"""bit_gemm_token_amd -- fine-grained W4A8 integer-scale linear layer for MI355X.
+
+A thin Python binding over libbgt.so (include/bgt.h): it checks tensor dtypes,
+devices and shapes, passes data pointers and torch's current HIP stream, and
+turns non-zero status codes into exceptions. Every step of the computation
+runs in the HIP kernels of libbgt; there is no fallback. If the library is not
+built, importing the entry points raises.
+
+Entry points (same names as the C ABI without the ``bgt_`` prefix):
+    quantize_act(x, mode="sym")            -> (q, scale[, zero], rowsum)
+    pack_weights_int4(w, alpha=1024)       -> dict(packed, fscale, iscale, alpha, status)
+    w4a8_gemm_is(qx, sx, packed, iscale, alpha, N)   -> y
+    w4a8_gemm_fs(qx, sx, packed, fscale, N)          -> y
+    w8a8_gemm_zp(qx, sx, zx, rowsum_x, qw, sw, zw, colsum_w) -> y
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbgt.so")
+
+BGT_OK = 0
+BGT_WARN_ACC_MAY_OVERFLOW = 1
+BGT_ERR_NULL = -1
+BGT_ERR_SHAPE = -2
+BGT_ERR_ALIGN = -3
+BGT_ERR_ALPHA = -4
+BGT_ERR_MODE = -5
+BGT_ERR_HIP = -6
+BGT_ERR_RANGE = -7
+BGT_QUANT_SYM_I8 = 0
+BGT_QUANT_ASYM_U8 = 1
+GROUP = 128
+
+EXPORTED = (
+    "bgt_quantize_act", "bgt_pack_weights_int4", "bgt_w4a8_gemm_is", "bgt_w4a8_gemm_fs",
+    "bgt_w8a8_gemm_zp", "bgt_status_string", "bgt_abi_version",
+)
+
+_lib = None
+
+
+class BgtError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn}: {status_string(status)} ({status})")
+
+
+def lib():
+    """The loaded libbgt.so (ctypes), with argument types declared."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m bit_gemm_token_amd.build` (or __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.bgt_quantize_act.argtypes = [P, I64, I64, I64, I, P, P, P, P, P]
+        L.bgt_pack_weights_int4.argtypes = [P, I64, I64, I64, I, P, P, P, ctypes.POINTER(I), P]
+        L.bgt_w4a8_gemm_is.argtypes = [P, P, P, P, I, I64, I64, I64, P, P, P]
+        L.bgt_w4a8_gemm_fs.argtypes = [P, P, P, P, I64, I64, I64, P, P]
+        L.bgt_w8a8_gemm_zp.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, P, P, P]
+        L.bgt_status_string.argtypes = [I]
+        L.bgt_status_string.restype = ctypes.c_char_p
+        L.bgt_abi_version.restype = I
+        for f in EXPORTED:
+            if f not in ("bgt_status_string", "bgt_abi_version"):
+                getattr(L, f).restype = I
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().bgt_status_string(int(status)).decode()
+
+
+# ----------------------------------------------------------------- marshalling
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device=None):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(t, name, dtype, shape=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _raise(fn, st):
+    if st < 0:
+        raise BgtError(fn, st)
+    return st
+
+
+# ------------------------------------------------------------------ entry points
+def quantize_act(x, mode: str = "sym", q=None, scale=None, zero=None, rowsum=None,
+                 want_rowsum: bool = False):
+    """Per-row dynamic quantization of x (rows x cols float32, row-major).
+
+    mode "sym": int8 codes in [-127, 127] and one scale per row.
+    mode "asym": uint8 codes in [0, 255], scale, zero point and code row sum.
+    Returns (q, scale, rowsum) for "sym" (rowsum None unless asked for) and
+    (q, scale, zero, rowsum) for "asym".
+    """
+    torch = _torch()
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    rows, cols = x.shape
+    if x.dtype != torch.float32 or not x.is_cuda or x.stride(1) != 1:
+        raise ValueError("x must be a float32 GPU tensor with unit column stride")
+    ld = x.stride(0)
+    asym = mode == "asym"
+    if mode not in ("sym", "asym"):
+        raise ValueError("mode must be 'sym' or 'asym'")
+    dev = x.device
+    qdt = torch.uint8 if asym else torch.int8
+    q = torch.empty((rows, cols), dtype=qdt, device=dev) if q is None else q
+    scale = torch.empty(rows, dtype=torch.float32, device=dev) if scale is None else scale
+    if asym and zero is None:
+        zero = torch.empty(rows, dtype=torch.int32, device=dev)
+    if (asym or want_rowsum) and rowsum is None:
+        rowsum = torch.empty(rows, dtype=torch.int32, device=dev)
+    _check(q, "q", qdt, (rows, cols))
+    _check(scale, "scale", torch.float32, (rows,))
+    if zero is not None:
+        _check(zero, "zero", torch.int32, (rows,))
+    if rowsum is not None:
+        _check(rowsum, "rowsum", torch.int32, (rows,))
+    st = lib().bgt_quantize_act(_ptr(x), rows, cols, ld,
+                                BGT_QUANT_ASYM_U8 if asym else BGT_QUANT_SYM_I8,
+                                _ptr(q), _ptr(scale), _ptr(zero), _ptr(rowsum), _stream(dev))
+    _raise("bgt_quantize_act", st)
+    return (q, scale, zero, rowsum) if asym else (q, scale, rowsum)
+
+
+def pack_weights_int4(w, alpha: int = 1024, group: int = GROUP, packed=None, fscale=None,
+                      iscale=None):
+    """Offline int4 group quantization of w (K x N float32) and its integer scales.
+
+    alpha=0 runs the amplifier search. Synchronous. Returns a dict with
+    packed (N*K/2 uint8), fscale, iscale ((K/128) x N), alpha and status
+    (0, or 1 = the worst-case accumulator may exceed int32).
+    """
+    torch = _torch()
+    _check(w, "w", torch.float32)
+    K, N = w.shape
+    dev = w.device
+    G = K // group if group else 0
+    packed = torch.empty(N * K // 2, dtype=torch.uint8, device=dev) if packed is None else packed
+    fscale = torch.empty((G, N), dtype=torch.float32, device=dev) if fscale is None else fscale
+    iscale = torch.empty((G, N), dtype=torch.int32, device=dev) if iscale is None else iscale
+    _check(packed, "packed", torch.uint8, (N * K // 2,))
+    _check(fscale, "fscale", torch.float32, (G, N))
+    _check(iscale, "iscale", torch.int32, (G, N))
+    a_out = ctypes.c_int(0)
+    st = lib().bgt_pack_weights_int4(_ptr(w), K, N, group, int(alpha), _ptr(packed), _ptr(fscale),
+                                     _ptr(iscale), ctypes.byref(a_out), _stream(dev))
+    _raise("bgt_pack_weights_int4", st)
+    return {"packed": packed, "fscale": fscale, "iscale": iscale, "alpha": a_out.value,
+            "status": st}
+
+
+def _gemm_common(qx, sx, packed, scale, scale_dtype, N):
+    torch = _torch()
+    _check(qx, "qx", torch.int8)
+    M, K = qx.shape
+    _check(sx, "sx", torch.float32, (M,))
+    _check(packed, "packed", torch.uint8, (N * K // 2,))
+    _check(scale, "scale", scale_dtype, (K // GROUP, N))
+    return M, K
+
+
+def w4a8_gemm_is(qx, sx, packed, iscale, alpha: int, N: int, y=None, acc_out=None):
+    """Y = X.W with the integer-scale epilogue; returns y (M x N float32)."""
+    torch = _torch()
+    M, K = _gemm_common(qx, sx, packed, iscale, torch.int32, N)
+    y = torch.empty((M, N), dtype=torch.float32, device=qx.device) if y is None else y
+    _check(y, "y", torch.float32, (M, N))
+    if acc_out is not None:
+        _check(acc_out, "acc_out", torch.int32, (M, N))
+    st = lib().bgt_w4a8_gemm_is(_ptr(qx), _ptr(sx), _ptr(packed), _ptr(iscale), int(alpha), M, N,
+                                K, _ptr(y), _ptr(acc_out), _stream(qx.device))
+    _raise("bgt_w4a8_gemm_is", st)
+    return y
+
+
+def w4a8_gemm_fs(qx, sx, packed, fscale, N: int, y=None):
+    """Y = X.W with the float-scale epilogue (the control); returns y."""
+    torch = _torch()
+    M, K = _gemm_common(qx, sx, packed, fscale, torch.float32, N)
+    y = torch.empty((M, N), dtype=torch.float32, device=qx.device) if y is None else y
+    _check(y, "y", torch.float32, (M, N))
+    st = lib().bgt_w4a8_gemm_fs(_ptr(qx), _ptr(sx), _ptr(packed), _ptr(fscale), M, N, K, _ptr(y),
+                                _stream(qx.device))
+    _raise("bgt_w4a8_gemm_fs", st)
+    return y
+
+
+def w8a8_gemm_zp(qx, sx, zx, rowsum_x, qw, sw, zw, colsum_w, y=None, acc_out=None):
+    """Asymmetric W8A8 GEMM via the zero-point expansion; returns y (M x N)."""
+    torch = _torch()
+    _check(qx, "qx", torch.uint8)
+    _check(qw, "qw", torch.uint8)
+    M, K = qx.shape
+    N = qw.shape[0]
+    if qw.shape[1] != K:
+        raise ValueError("qw must be N x K")
+    for t, n, nm in ((sx, M, "sx"), (sw, N, "sw")):
+        _check(t, nm, torch.float32, (n,))
+    for t, n, nm in ((zx, M, "zx"), (rowsum_x, M, "rowsum_x"), (zw, N, "zw"), (colsum_w, N, "colsum_w")):
+        _check(t, nm, torch.int32, (n,))
+    y = torch.empty((M, N), dtype=torch.float32, device=qx.device) if y is None else y
+    _check(y, "y", torch.float32, (M, N))
+    if acc_out is not None:
+        _check(acc_out, "acc_out", torch.int32, (M, N))
+    st = lib().bgt_w8a8_gemm_zp(_ptr(qx), _ptr(sx), _ptr(zx), _ptr(rowsum_x), _ptr(qw), _ptr(sw),
+                                _ptr(zw), _ptr(colsum_w), M, N, K, _ptr(y), _ptr(acc_out),
+                                _stream(qx.device))
+    _raise("bgt_w8a8_gemm_zp", st)
+    return y

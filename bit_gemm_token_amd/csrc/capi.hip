@@ -1,0 +1,147 @@
+// capi.hip -- the extern "C" entry points of libbgt (see include/bgt.h).
+//
+// Every argument is validated on the host before the first HIP call, so a
+// rejected call touches neither the device nor any output. Kernels are
+// enqueued on the caller's stream; nothing is allocated on the device.
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "bgt.h"
+#include "launch.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool pow2_alpha(int a) { return a >= 1 && a <= (1 << 30) && (a & (a - 1)) == 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? BGT_OK : BGT_ERR_HIP; }
+
+int check_gemm_shape(int64_t M, int64_t N, int64_t K, int64_t kmax) {
+  if (M < 1 || M > 65536) return BGT_ERR_SHAPE;
+  if (N < 16 || N > (1 << 24) || N % 16 != 0) return BGT_ERR_SHAPE;
+  if (K < BGT_GROUP || K > kmax || K % BGT_GROUP != 0) return BGT_ERR_SHAPE;
+  return BGT_OK;
+}
+
+// Amplifier search of the Integer Scale page (方法): the smallest 2^n, n >= 0,
+// with smin * 2^n >= 1. With smin = m * 2^e, m in [0.5, 1): n = max(0, 1 - e).
+int searched_alpha_log2(float smin) {
+  if (!(smin > 0.0f) || isinf(smin) || smin >= 1.0f) return 0;
+  int e = 0;
+  frexpf(smin, &e);
+  return 1 - e;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bgt_abi_version(void) { return 100; }
+
+const char* bgt_status_string(int status) {
+  switch (status) {
+    case BGT_OK: return "ok";
+    case BGT_WARN_ACC_MAY_OVERFLOW: return "warning: worst-case accumulator may exceed int32";
+    case BGT_ERR_NULL: return "error: required pointer is NULL";
+    case BGT_ERR_SHAPE: return "error: size out of range or not a required multiple";
+    case BGT_ERR_ALIGN: return "error: pointer or leading dimension misaligned";
+    case BGT_ERR_ALPHA: return "error: amplifier must be a power of two in [1, 2^30]";
+    case BGT_ERR_MODE: return "error: unknown quantization mode";
+    case BGT_ERR_HIP: return "error: HIP call failed";
+    case BGT_ERR_RANGE: return "error: integer scale out of range [0, 2^23)";
+    default: return "unknown status";
+  }
+}
+
+int bgt_quantize_act(const float* x, int64_t rows, int64_t cols, int64_t ld, int mode, void* q,
+                     float* scale, int32_t* zero, int32_t* rowsum, void* stream) {
+  if (mode != BGT_QUANT_SYM_I8 && mode != BGT_QUANT_ASYM_U8) return BGT_ERR_MODE;
+  if (!x || !q || !scale) return BGT_ERR_NULL;
+  if (mode == BGT_QUANT_ASYM_U8 && !zero) return BGT_ERR_NULL;
+  if (rows < 1 || rows > 0x7FFFFFFF || cols < 1 || cols > (1 << 24) || ld < cols)
+    return BGT_ERR_SHAPE;
+  return hip_status(bgt::launch_quant_rows(x, rows, cols, ld, mode == BGT_QUANT_ASYM_U8, q, scale,
+                                           zero, rowsum, static_cast<hipStream_t>(stream)));
+}
+
+int bgt_pack_weights_int4(const float* w, int64_t K, int64_t N, int64_t group, int alpha,
+                          uint8_t* packed, float* fscale, int32_t* iscale, int* alpha_out,
+                          void* stream) {
+  if (!w || !packed || !fscale || !iscale || !alpha_out) return BGT_ERR_NULL;
+  if (group != BGT_GROUP) return BGT_ERR_SHAPE;
+  if (K < BGT_GROUP || K > 65536 || K % BGT_GROUP != 0) return BGT_ERR_SHAPE;
+  if (N < 16 || N > (1 << 24) || N % 16 != 0) return BGT_ERR_SHAPE;
+  if (alpha != 0 && !pow2_alpha(alpha)) return BGT_ERR_ALPHA;
+  if (!aligned16(packed)) return BGT_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t G = K / BGT_GROUP;
+
+  hipError_t e = bgt::launch_group_quant_pack(w, K, N, packed, fscale, iscale, s);
+  if (e != hipSuccess) return BGT_ERR_HIP;
+  uint32_t bits[2];
+  e = hipMemcpyAsync(bits, iscale, sizeof(bits), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return BGT_ERR_HIP;
+  float smin, smax;
+  memcpy(&smin, &bits[0], 4);
+  memcpy(&smax, &bits[1], 4);
+
+  int a = alpha;
+  if (a == 0) {
+    const int n = searched_alpha_log2(smin);
+    if (n > 30) return BGT_ERR_ALPHA;
+    a = 1 << n;
+  }
+  *alpha_out = a;
+  const double top = roundf(smax * (float)a);     // largest integer scale
+  if (!(top < 8388608.0)) return BGT_ERR_RANGE;   // 2^23
+
+  e = bgt::launch_integer_scales(fscale, G * N, a, iscale, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return BGT_ERR_HIP;
+  // |p| <= 128 * 127 * 7 = 113792 per group with the packer's codes
+  if (113792.0 * (double)G * top >= 2147483648.0) return BGT_WARN_ACC_MAY_OVERFLOW;
+  return BGT_OK;
+}
+
+int bgt_w4a8_gemm_is(const int8_t* qx, const float* sx, const uint8_t* packed,
+                     const int32_t* iscale, int alpha, int64_t M, int64_t N, int64_t K, float* y,
+                     int32_t* acc_out, void* stream) {
+  if (!qx || !sx || !packed || !iscale || !y) return BGT_ERR_NULL;
+  int st = check_gemm_shape(M, N, K, 65536);
+  if (st != BGT_OK) return st;
+  if (!pow2_alpha(alpha)) return BGT_ERR_ALPHA;
+  if (!aligned16(qx) || !aligned16(packed) || !aligned16(y) || (acc_out && !aligned16(acc_out)))
+    return BGT_ERR_ALIGN;
+  return hip_status(bgt::launch_w4a8(false, qx, sx, packed, iscale, nullptr, alpha, M, N, K, y,
+                                     acc_out, static_cast<hipStream_t>(stream)));
+}
+
+int bgt_w4a8_gemm_fs(const int8_t* qx, const float* sx, const uint8_t* packed,
+                     const float* fscale, int64_t M, int64_t N, int64_t K, float* y,
+                     void* stream) {
+  if (!qx || !sx || !packed || !fscale || !y) return BGT_ERR_NULL;
+  int st = check_gemm_shape(M, N, K, 65536);
+  if (st != BGT_OK) return st;
+  if (!aligned16(qx) || !aligned16(packed) || !aligned16(y)) return BGT_ERR_ALIGN;
+  return hip_status(bgt::launch_w4a8(true, qx, sx, packed, nullptr, fscale, 1, M, N, K, y,
+                                     nullptr, static_cast<hipStream_t>(stream)));
+}
+
+int bgt_w8a8_gemm_zp(const uint8_t* qx, const float* sx, const int32_t* zx,
+                     const int32_t* rowsum_x, const uint8_t* qw, const float* sw,
+                     const int32_t* zw, const int32_t* colsum_w, int64_t M, int64_t N, int64_t K,
+                     float* y, int32_t* acc_out, void* stream) {
+  if (!qx || !sx || !zx || !rowsum_x || !qw || !sw || !zw || !colsum_w || !y) return BGT_ERR_NULL;
+  int st = check_gemm_shape(M, N, K, 32768);
+  if (st != BGT_OK) return st;
+  if (!aligned16(qx) || !aligned16(qw) || !aligned16(y) || (acc_out && !aligned16(acc_out)))
+    return BGT_ERR_ALIGN;
+  return hip_status(bgt::launch_w8a8_zp(qx, sx, zx, rowsum_x, qw, sw, zw, colsum_w, M, N, K, y,
+                                        acc_out, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,83 @@
+// device_common.h -- helpers shared by the gfx950 kernels of libbgt (internal).
+//
+// Wave64 reductions, the half-away-from-zero rounding the quantizers use, the
+// int4 -> int8 unpacks of the packed weight layout, and MFMA operand types.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bgt {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+constexpr int kGroup = 128;
+
+// ----------------------------------------------------------------- rounding
+// round() of the pages: half away from zero (C roundf). llvm.round lowers to
+// trunc + |x - trunc(x)| >= 0.5 correction, exact for every float.
+__device__ __forceinline__ float round_away(float v) { return __builtin_roundf(v); }
+
+__device__ __forceinline__ int clamp_int(int v, int lo, int hi) {
+  return v < lo ? lo : (v > hi ? hi : v);
+}
+
+// ------------------------------------------------------------ wave reductions
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// ----------------------------------------------------------- int4 unpacking
+// A 32-bit word of the packed layout holds 8 consecutive codes e0..e7 of one
+// column: byte b carries e_b in its low nibble and e_{b+4} in its high nibble.
+//
+// unpack_x16: nibble moved to the high half of each byte, i.e. each int8 is
+// 16 * code (exact for codes in [-8, 7]). Two ops per four codes; the x16 is
+// divided out of the int32 dot product afterwards (an exact shift).
+__device__ __forceinline__ void unpack_x16(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  lo = (w << 4) & 0xF0F0F0F0u;   // bytes: 16*e0, 16*e1, 16*e2, 16*e3
+  hi = w & 0xF0F0F0F0u;          // bytes: 16*e4, 16*e5, 16*e6, 16*e7
+}
+
+// unpack_i8: true int8 codes (sign-extended nibbles). Per byte, with u the
+// unsigned nibble, ((u ^ 8) + 0x78) ^ 0x80 == u - 16*(u >= 8); no carry crosses
+// a byte because (u ^ 8) + 0x78 <= 0x87.
+__device__ __forceinline__ uint32_t sext_nibbles(uint32_t u) {
+  return ((u ^ 0x08080808u) + 0x78787878u) ^ 0x80808080u;
+}
+__device__ __forceinline__ void unpack_i8(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  lo = sext_nibbles(w & 0x0F0F0F0Fu);
+  hi = sext_nibbles((w >> 4) & 0x0F0F0F0Fu);
+}
+
+// ----------------------------------------------------------- memory helpers
+template <typename T>
+__device__ __forceinline__ T load_nt(const T* p) { return __builtin_nontemporal_load(p); }
+
+__device__ __forceinline__ uint4 load_u4_nt(const uint4* p) {
+  // streamed once per launch: non-temporal so it does not evict reused data
+  const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+  typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+  u4v v = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(q));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ v4i load_v4i(const int8_t* p) {
+  return *reinterpret_cast<const v4i*>(p);
+}
+
+}  // namespace bgt

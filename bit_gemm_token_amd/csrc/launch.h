@@ -1,0 +1,31 @@
+// launch.h -- internal launchers of libbgt (host side). Arguments are already
+// validated by the C ABI layer (capi.hip) when these run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bgt {
+
+hipError_t launch_quant_rows(const float* x, int64_t rows, int64_t cols, int64_t ld, bool asym,
+                             void* q, float* scale, int32_t* zero, int32_t* rowsum,
+                             hipStream_t stream);
+
+// Group quantization + packing; also leaves min(positive s) and max(s) as float
+// bits in iscale[0], iscale[1] (scratch until launch_integer_scales overwrites them).
+hipError_t launch_group_quant_pack(const float* w, int64_t K, int64_t N, uint8_t* packed,
+                                   float* fscale, int32_t* iscale, hipStream_t stream);
+
+hipError_t launch_integer_scales(const float* fscale, int64_t count, int alpha, int32_t* iscale,
+                                 hipStream_t stream);
+
+hipError_t launch_w4a8(bool float_scale, const int8_t* qx, const float* sx, const uint8_t* packed,
+                       const int32_t* iscale, const float* fscale, int alpha, int64_t M, int64_t N,
+                       int64_t K, float* y, int32_t* acc_out, hipStream_t stream);
+
+hipError_t launch_w8a8_zp(const uint8_t* qx, const float* sx, const int32_t* zx,
+                          const int32_t* rowsum_x, const uint8_t* qw, const float* sw,
+                          const int32_t* zw, const int32_t* colsum_w, int64_t M, int64_t N,
+                          int64_t K, float* y, int32_t* acc_out, hipStream_t stream);
+
+}  // namespace bgt

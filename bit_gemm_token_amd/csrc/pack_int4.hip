@@ -1,0 +1,105 @@
+// pack_int4.hip -- offline group-wise int4 weight quantization and packing (gfx950).
+//
+// Per column j and group l of 128 rows of W (K x N row-major), following the
+// Integer Scale page (方法, Fig. 3(a): weights split into groups quantized
+// independently) with the symmetric closed forms of the "Quantization" notes
+// page at q_max = 7:
+//     s = max|w| / 7,  q = clip(round(w / s), -7, 7),  fscale = s,
+// then the integer scales round(s * alpha) of Fig. 3(c).
+//
+// One thread per (column, group): the 128 values of its group are a strided
+// column walk, coalesced across the 256 threads of a workgroup (consecutive
+// columns). The thread builds the group's 64 packed bytes in registers and
+// writes them as four 16-byte stores into the four lane slots of the
+// (16-column tile, group) block of the packed layout.
+#include "device_common.h"
+#include "launch.h"
+
+namespace bgt {
+
+constexpr int kPThreads = 256;
+
+// packed word index (0..15) and bit offset of code r (0..127) within a
+// column's 64-byte slice of a group block; see the layout in bgt.h
+__device__ __forceinline__ void code_slot(int r, int& word, int& shift) {
+  const int h = r / 64, s = (r % 64) / 16, e = r % 16;
+  word = 4 * s + 2 * h + e / 8;
+  shift = 8 * (e % 4) + 4 * ((e % 8) >= 4);
+}
+
+__global__ __launch_bounds__(kPThreads) void k_group_quant_pack(
+    const float* __restrict__ w, int64_t K, int64_t N, uint4* __restrict__ packed,
+    float* __restrict__ fscale, int32_t* __restrict__ minmax) {
+  const int64_t j = (int64_t)blockIdx.x * kPThreads + threadIdx.x;
+  const int64_t l = blockIdx.y;
+  const int64_t G = K / kGroup;
+  float s = 0.0f;
+  const bool active = j < N;
+  if (active) {
+    const float* col = w + (l * kGroup) * N + j;
+    float v[kGroup];
+    float a = 0.0f;
+#pragma unroll
+    for (int r = 0; r < kGroup; ++r) {
+      v[r] = col[(int64_t)r * N];
+      a = fmaxf(a, fabsf(v[r]));
+    }
+    s = a / 7.0f;
+    uint32_t words[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) words[i] = 0u;
+#pragma unroll
+    for (int r = 0; r < kGroup; ++r) {
+      int code = 0;
+      if (s != 0.0f) code = clamp_int((int)round_away(v[r] / s), -7, 7);
+      int word, shift;
+      code_slot(r, word, shift);
+      words[word] |= ((uint32_t)code & 0xFu) << shift;
+    }
+    const int64_t t = j / 16, c = j % 16;
+    uint4* blk = packed + (t * G + l) * 64 + c;
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl)
+      blk[16 * sl] = make_uint4(words[4 * sl], words[4 * sl + 1], words[4 * sl + 2], words[4 * sl + 3]);
+    fscale[l * N + j] = s;
+  }
+  // min over positive scales and max over all scales, as ordered float bits
+  // (non-negative floats order like their bit patterns)
+  const float pos = (active && s > 0.0f) ? s : INFINITY;
+  const float mn = wave_min(pos);
+  const float mx = wave_max(active ? s : 0.0f);
+  if ((threadIdx.x % kWave) == 0) {
+    atomicMin(&minmax[0], (int32_t)__float_as_uint(mn));
+    atomicMax(&minmax[1], (int32_t)__float_as_uint(mx));
+  }
+}
+
+__global__ void k_init_minmax(int32_t* minmax) {
+  minmax[0] = (int32_t)__float_as_uint(INFINITY);
+  minmax[1] = 0;
+}
+
+__global__ __launch_bounds__(kPThreads) void k_integer_scales(
+    const float* __restrict__ fscale, int64_t count, float alpha, int32_t* __restrict__ iscale) {
+  const int64_t i = (int64_t)blockIdx.x * kPThreads + threadIdx.x;
+  if (i < count) iscale[i] = (int32_t)round_away(fscale[i] * alpha);   // exact product: alpha = 2^n
+}
+
+hipError_t launch_group_quant_pack(const float* w, int64_t K, int64_t N, uint8_t* packed,
+                                   float* fscale, int32_t* iscale, hipStream_t stream) {
+  hipLaunchKernelGGL(k_init_minmax, dim3(1), dim3(1), 0, stream, iscale);
+  dim3 grid((unsigned)((N + kPThreads - 1) / kPThreads), (unsigned)(K / kGroup));
+  hipLaunchKernelGGL(k_group_quant_pack, grid, dim3(kPThreads), 0, stream, w, K, N,
+                     reinterpret_cast<uint4*>(packed), fscale, iscale);
+  return hipGetLastError();
+}
+
+hipError_t launch_integer_scales(const float* fscale, int64_t count, int alpha, int32_t* iscale,
+                                 hipStream_t stream) {
+  dim3 grid((unsigned)((count + kPThreads - 1) / kPThreads));
+  hipLaunchKernelGGL(k_integer_scales, grid, dim3(kPThreads), 0, stream, fscale, count,
+                     (float)alpha, iscale);
+  return hipGetLastError();
+}
+
+}  // namespace bgt

