@@ -36,7 +36,7 @@ GROUP = 128
 
 EXPORTED = (
     "bgt_quantize_act", "bgt_pack_weights_int4", "bgt_w4a8_gemm_is", "bgt_w4a8_gemm_fs",
-    "bgt_w8a8_gemm_zp", "bgt_status_string", "bgt_abi_version",
+    "bgt_w8a8_gemm_zp", "bgt_status_string", "bgt_abi_version", "bgt_w4a8_kernel_name",
 )
 
 _lib = None
@@ -65,8 +65,10 @@ def lib():
         L.bgt_status_string.argtypes = [I]
         L.bgt_status_string.restype = ctypes.c_char_p
         L.bgt_abi_version.restype = I
+        L.bgt_w4a8_kernel_name.argtypes = [I64, I64, I64, I]
+        L.bgt_w4a8_kernel_name.restype = ctypes.c_char_p
         for f in EXPORTED:
-            if f not in ("bgt_status_string", "bgt_abi_version"):
+            if f not in ("bgt_status_string", "bgt_abi_version", "bgt_w4a8_kernel_name"):
                 getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -74,6 +76,11 @@ def lib():
 
 def status_string(status: int) -> str:
     return lib().bgt_status_string(int(status)).decode()
+
+
+def w4a8_kernel_name(M: int, N: int, K: int, float_scale: bool = False) -> str:
+    """Name of the GEMM kernel a W4A8 call of this shape launches (profiling aid)."""
+    return lib().bgt_w4a8_kernel_name(int(M), int(N), int(K), 1 if float_scale else 0).decode()
 
 
 # ----------------------------------------------------------------- marshalling

@@ -18,6 +18,9 @@
 // The K order inside one MFMA does not matter as long as A and B use the same
 // one (it is a dot product), which is what lets the packed weight layout put
 // each lane's 16 bytes next to each other.
+#include <mutex>
+#include <vector>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -355,6 +358,167 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tiled(
     }
 }
 
+// =====================================================================
+// Streaming kernel (small M, the memory-bound decode regime).
+// Persistent workgroups of KS loader waves plus one finisher wave.
+//   Loader wave w owns groups [w*GPW, (w+1)*GPW) for the whole launch and
+//   keeps their activation fragments in registers (loaded once), so the only
+//   per-tile traffic is the packed weights and their scales. The workgroup
+//   walks column tiles t = blockIdx.x, blockIdx.x + gridDim.x, ...; two
+//   register sets ping-pong so the next tile's blocks are in flight while the
+//   current one is contracted. Loader waves issue loads only, all of them
+//   unconditional (indices clamped, unused data ignored), so their waits
+//   count exactly the loads still needed.
+//   The finisher wave does every global store: it adds the loaders' partial
+//   results from LDS, converts once and writes y (stores and loads never
+//   share a wave's memory counter, so stores cannot stall the prefetch).
+// Exchange through LDS, two copies (tile parity), one barrier per tile:
+//   integer scale: per-wave int32 partial sums, added in any order (exact);
+//   float scale:   the per-group int32 results and scales, so the finisher can
+//                  run the ascending fma chain of Fig. 3(b) per output.
+// A copy is rewritten two tiles later, after the finisher has passed the
+// intermediate barrier, i.e. after it finished reading that copy.
+// =====================================================================
+template <int MR, int GPW, bool FS, int MAXT, int WPE>
+__global__ __launch_bounds__(MAXT) __attribute__((amdgpu_waves_per_eu(WPE))) void k_w4a8_stream(
+    const int8_t* __restrict__ qx, const float* __restrict__ sx,
+    const uint4* __restrict__ packed, const int32_t* __restrict__ iscale,
+    const float* __restrict__ fscale, float inv_alpha, int M, int N, int K,
+    float* __restrict__ y, int32_t* __restrict__ acc_out) {
+  extern __shared__ int lds[];
+  constexpr int NR = MR * 4;                       // accumulator registers per lane
+  const int G = K / kGroup, T = N / 16;
+  const int KS = blockDim.x / kWave - 1;           // loader waves
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform
+  const int lane = threadIdx.x % kWave;
+  const int c = lane % 16, s4 = lane / 16;
+  // one exchange copy: IS = KS x NR x 64 ints; FS = G x NR x 64 ints + G x 16 floats
+  const int area = FS ? (G * NR * kWave + G * 16) : (KS * NR * kWave);
+  const int P = gridDim.x;
+
+  if (wave == KS) {
+    // ------------------------------------------------------------- finisher
+    float srow[NR];
+#pragma unroll
+    for (int idx = 0; idx < NR; ++idx) {
+      const int i = (idx / 4) * 16 + 4 * s4 + (idx % 4);
+      srow[idx] = sx[i < M ? i : M - 1];
+    }
+    int it = 0;
+    for (int t = blockIdx.x; t < T; t += P, ++it) {
+      __syncthreads();
+      const int* xa = lds + (it & 1) * area;
+      const int j = t * 16 + c;
+#pragma unroll
+      for (int idx = 0; idx < NR; ++idx) {
+        const int i = (idx / 4) * 16 + 4 * s4 + (idx % 4);
+        if (FS) {
+          const float* fb = reinterpret_cast<const float*>(xa + G * NR * kWave);
+          float a = 0.0f;
+          for (int l = 0; l < G; ++l)
+            a = __builtin_fmaf((float)xa[(l * NR + idx) * kWave + lane], fb[l * 16 + c], a);
+          if (i < M) y[(int64_t)i * N + j] = a * srow[idx];
+        } else {
+          int sum = 0;
+          for (int w = 0; w < KS; ++w) sum += xa[(w * NR + idx) * kWave + lane];
+          if (i < M) {
+            const float t0 = (float)sum * srow[idx];
+            y[(int64_t)i * N + j] = t0 * inv_alpha;
+            if (acc_out) acc_out[(int64_t)i * N + j] = sum;
+          }
+        }
+      }
+    }
+    return;
+  }
+
+  // --------------------------------------------------------------- loaders
+  const int gb = wave * GPW;
+  bool gvalid[GPW];
+  int gcl[GPW];
+#pragma unroll
+  for (int u = 0; u < GPW; ++u) {
+    gvalid[u] = gb + u < G;
+    gcl[u] = gb + u < G ? gb + u : G - 1;
+  }
+  v4i a0[GPW][MR], a1[GPW][MR];
+#pragma unroll
+  for (int u = 0; u < GPW; ++u)
+#pragma unroll
+    for (int rb = 0; rb < MR; ++rb) {
+      const int i = rb * 16 + c;
+      const int8_t* src = qx + (int64_t)(i < M ? i : M - 1) * K + (int64_t)gcl[u] * kGroup + 16 * s4;
+      a0[u][rb] = load_v4i(src);
+      a1[u][rb] = load_v4i(src + 64);
+    }
+  // rows beyond M contribute zero (their outputs are never stored; zeroing keeps
+  // the accumulators of valid rows independent of clamped duplicates anyway)
+  const bool rvalid0 = c < M;
+
+  auto issue = [&](int t, uint4* b, int* is, float* fs) {
+    const int tc = t < T ? t : T - 1;
+#pragma unroll
+    for (int u = 0; u < GPW; ++u) {
+      b[u] = load_u4_nt(packed + ((int64_t)tc * G + gcl[u]) * 64 + lane);
+      if (FS) fs[u] = fscale[(int64_t)gcl[u] * N + tc * 16 + c];
+      else is[u] = iscale[(int64_t)gcl[u] * N + tc * 16 + c];
+    }
+  };
+  auto contract = [&](int it, const uint4* b, const int* is, const float* fs) {
+    int* xa = lds + (it & 1) * area;
+    int acc[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) acc[r] = 0;
+#pragma unroll
+    for (int u = 0; u < GPW; ++u) {
+      if (!gvalid[u]) continue;                     // wave-uniform
+      uint32_t x0, x1, x2, x3, x4, x5, x6, x7;
+      unpack_x16(b[u].x, x0, x1);
+      unpack_x16(b[u].y, x2, x3);
+      unpack_x16(b[u].z, x4, x5);
+      unpack_x16(b[u].w, x6, x7);
+      const v4i b0 = {(int)x0, (int)x1, (int)x2, (int)x3};
+      const v4i b1 = {(int)x4, (int)x5, (int)x6, (int)x7};
+#pragma unroll
+      for (int rb = 0; rb < MR; ++rb) {
+        const bool rv = rb == 0 ? rvalid0 : (rb * 16 + c < M);
+        const v4i z = {0, 0, 0, 0};
+        v4i p = __builtin_amdgcn_mfma_i32_16x16x64_i8(rv ? a0[u][rb] : z, b0, z, 0, 0, 0);
+        p = __builtin_amdgcn_mfma_i32_16x16x64_i8(rv ? a1[u][rb] : z, b1, p, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int pv = p[r] >> 4;        // B codes entered the MFMA as 16*q
+          if (FS) xa[(gb + u) * NR * kWave + (rb * 4 + r) * kWave + lane] = pv;
+          else acc[rb * 4 + r] = mad24(pv, is[u], acc[rb * 4 + r]);
+        }
+      }
+      if (FS && s4 == 0) reinterpret_cast<float*>(xa + G * NR * kWave)[(gb + u) * 16 + c] = fs[u];
+    }
+    if (!FS) {
+#pragma unroll
+      for (int r = 0; r < NR; ++r) xa[(wave * NR + r) * kWave + lane] = acc[r];
+    }
+    __syncthreads();
+  };
+
+  uint4 bA[GPW], bB[GPW];
+  int iA[GPW], iB[GPW];
+  float fA[GPW], fB[GPW];
+  int t = blockIdx.x, it = 0;
+  issue(t, bA, iA, fA);
+  while (t < T) {
+    issue(t + P, bB, iB, fB);
+    contract(it, bA, iA, fA);
+    ++it;
+    t += P;
+    if (t >= T) break;
+    issue(t + P, bA, iA, fA);
+    contract(it, bB, iB, fB);
+    ++it;
+    t += P;
+  }
+}
+
 // ------------------------------------------------------------------ launchers
 template <int MR, bool FS>
 static void launch_skinny(const int8_t* qx, const float* sx, const uint8_t* packed,
@@ -367,28 +531,130 @@ static void launch_skinny(const int8_t* qx, const float* sx, const uint8_t* pack
                      acc_out);
 }
 
+// Workgroups that fit on the device at once for kernel k (block threads,
+// dyn_lds bytes), cached per (device, kernel, block, lds).
+static int resident_blocks(const void* k, int block, size_t dyn_lds) {
+  struct Entry { int dev; const void* k; int block; size_t lds; int n; };
+  static std::mutex mu;
+  static std::vector<Entry> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  {
+    std::lock_guard<std::mutex> g(mu);
+    for (const Entry& e : cache)
+      if (e.dev == dev && e.k == k && e.block == block && e.lds == dyn_lds) return e.n;
+  }
+  int ncu = 0, occ = 0;
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k, block, dyn_lds) != hipSuccess) return 0;
+  const int n = (occ < 1 ? 1 : occ) * ncu;
+  std::lock_guard<std::mutex> g(mu);
+  cache.push_back({dev, k, block, dyn_lds, n});
+  return n;
+}
+
+// Stream-kernel configuration per row-block count: groups per loader wave,
+// block size bound and waves per SIMD (chosen so no variant spills).
+template <int MR> struct StreamCfg;
+template <> struct StreamCfg<1> { static constexpr int GPW = 4, MAXT = 576, WPE = 5; };
+template <> struct StreamCfg<2> { static constexpr int GPW = 4, MAXT = 576, WPE = 3; };
+template <> struct StreamCfg<3> { static constexpr int GPW = 3, MAXT = 768, WPE = 3; };
+template <> struct StreamCfg<4> { static constexpr int GPW = 3, MAXT = 768, WPE = 3; };
+
+constexpr size_t kLdsCap = 160 * 1024;             // gfx950 LDS per workgroup
+
+static size_t stream_lds_bytes(int MR, int GPW, bool FS, int G) {
+  const int NR = MR * 4, KS = (G + GPW - 1) / GPW;
+  const size_t area = 4u * (FS ? (size_t)G * NR * kWave + (size_t)G * 16 : (size_t)KS * NR * kWave);
+  return 2 * area;                                 // two copies, tile parity
+}
+
+enum class W4Path { Stream, Skinny, Tiled };
+struct W4Plan { W4Path path; int mr; };
+
+// The kernel a W4A8 GEMM of this shape runs: small M streams the weights
+// (stream kernel while its loader waves and exchange area fit a workgroup,
+// skinny kernel otherwise); larger M takes the LDS-tiled MFMA kernel.
+static W4Plan plan_w4a8(int M, int K, bool fs) {
+  if (M > 64) return {W4Path::Tiled, 0};
+  const int mr = (M + 15) / 16, G = K / kGroup;
+  int gpw = 0, maxt = 0;
+  switch (mr) {
+    case 1: gpw = StreamCfg<1>::GPW; maxt = StreamCfg<1>::MAXT; break;
+    case 2: gpw = StreamCfg<2>::GPW; maxt = StreamCfg<2>::MAXT; break;
+    case 3: gpw = StreamCfg<3>::GPW; maxt = StreamCfg<3>::MAXT; break;
+    default: gpw = StreamCfg<4>::GPW; maxt = StreamCfg<4>::MAXT; break;
+  }
+  const int ks = (G + gpw - 1) / gpw;
+  const bool fits = (ks + 1) * kWave <= maxt && stream_lds_bytes(mr, gpw, fs, G) <= kLdsCap;
+  return {fits ? W4Path::Stream : W4Path::Skinny, mr};
+}
+
+template <int MR, bool FS>
+static bool launch_stream(const int8_t* qx, const float* sx, const uint8_t* packed,
+                          const int32_t* iscale, const float* fscale, float inv_alpha, int M,
+                          int N, int K, float* y, int32_t* acc_out, hipStream_t stream) {
+  using C = StreamCfg<MR>;
+  const int G = K / kGroup, T = N / 16;
+  const int KS = (G + C::GPW - 1) / C::GPW;        // loader waves (+1 finisher)
+  const size_t lds = stream_lds_bytes(MR, C::GPW, FS, G);
+  auto kern = k_w4a8_stream<MR, C::GPW, FS, C::MAXT, C::WPE>;
+  const int pmax = resident_blocks(reinterpret_cast<const void*>(kern), (KS + 1) * kWave, lds);
+  if (pmax < 1) return false;
+  const int per = (T + pmax - 1) / pmax;          // tiles per workgroup
+  const int grid = (T + per - 1) / per;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3((KS + 1) * kWave), lds, stream, qx, sx,
+                     reinterpret_cast<const uint4*>(packed), iscale, fscale, inv_alpha, M, N, K,
+                     y, acc_out);
+  return true;
+}
+
+template <bool FS>
+static void launch_small_m(const W4Plan& plan, const int8_t* qx, const float* sx,
+                           const uint8_t* packed, const int32_t* iscale, const float* fscale,
+                           float inv_alpha, int M, int N, int K, float* y, int32_t* acc_out,
+                           hipStream_t stream) {
+  bool done = false;
+  if (plan.path == W4Path::Stream) {
+    switch (plan.mr) {
+      case 1: done = launch_stream<1, FS>(qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream); break;
+      case 2: done = launch_stream<2, FS>(qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream); break;
+      case 3: done = launch_stream<3, FS>(qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream); break;
+      default: done = launch_stream<4, FS>(qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream); break;
+    }
+  }
+  if (done) return;
+  switch (plan.mr) {
+    case 1: launch_skinny<1, FS>(qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream); break;
+    case 2: launch_skinny<2, FS>(qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream); break;
+    case 3: launch_skinny<3, FS>(qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream); break;
+    default: launch_skinny<4, FS>(qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream); break;
+  }
+}
+
+const char* w4a8_kernel_name(int64_t M, int64_t K, bool float_scale) {
+  static const char* names[2][3][4] = {
+      {{"k_w4a8_stream<1,IS>", "k_w4a8_stream<2,IS>", "k_w4a8_stream<3,IS>", "k_w4a8_stream<4,IS>"},
+       {"k_w4a8_skinny<1,4,IS>", "k_w4a8_skinny<2,4,IS>", "k_w4a8_skinny<3,4,IS>", "k_w4a8_skinny<4,4,IS>"},
+       {"k_gemm_tiled<2,2,IS>", "", "", ""}},
+      {{"k_w4a8_stream<1,FS>", "k_w4a8_stream<2,FS>", "k_w4a8_stream<3,FS>", "k_w4a8_stream<4,FS>"},
+       {"k_w4a8_skinny<1,1,FS>", "k_w4a8_skinny<2,1,FS>", "k_w4a8_skinny<3,1,FS>", "k_w4a8_skinny<4,1,FS>"},
+       {"k_gemm_tiled<2,2,FS>", "", "", ""}}};
+  const W4Plan p = plan_w4a8((int)M, (int)K, float_scale);
+  const int fs = float_scale ? 1 : 0;
+  if (p.path == W4Path::Tiled) return names[fs][2][0];
+  return names[fs][p.path == W4Path::Stream ? 0 : 1][p.mr - 1];
+}
+
 hipError_t launch_w4a8(bool float_scale, const int8_t* qx, const float* sx, const uint8_t* packed,
                        const int32_t* iscale, const float* fscale, int alpha, int64_t M64,
                        int64_t N64, int64_t K64, float* y, int32_t* acc_out, hipStream_t stream) {
   const int M = (int)M64, N = (int)N64, K = (int)K64;
   const float inv_alpha = 1.0f / (float)alpha;   // exact: alpha = 2^n
-  if (M <= 64) {
-    const int mr = (M + 15) / 16;
-    if (float_scale) {
-      switch (mr) {
-        case 1: launch_skinny<1, true>(qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream); break;
-        case 2: launch_skinny<2, true>(qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream); break;
-        case 3: launch_skinny<3, true>(qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream); break;
-        default: launch_skinny<4, true>(qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream); break;
-      }
-    } else {
-      switch (mr) {
-        case 1: launch_skinny<1, false>(qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream); break;
-        case 2: launch_skinny<2, false>(qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream); break;
-        case 3: launch_skinny<3, false>(qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream); break;
-        default: launch_skinny<4, false>(qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream); break;
-      }
-    }
+  const W4Plan plan = plan_w4a8(M, K, float_scale);
+  if (plan.path != W4Path::Tiled) {
+    if (float_scale) launch_small_m<true>(plan, qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream);
+    else launch_small_m<false>(plan, qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream);
   } else {
     constexpr int TM = 2, TN = 2, BM = 2 * TM * 32, BN = 2 * TN * 32;
     dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM), block(256);

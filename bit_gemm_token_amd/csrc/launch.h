@@ -23,6 +23,9 @@ hipError_t launch_w4a8(bool float_scale, const int8_t* qx, const float* sx, cons
                        const int32_t* iscale, const float* fscale, int alpha, int64_t M, int64_t N,
                        int64_t K, float* y, int32_t* acc_out, hipStream_t stream);
 
+// name of the kernel a W4A8 GEMM of this shape dispatches to (diagnostics)
+const char* w4a8_kernel_name(int64_t M, int64_t K, bool float_scale);
+
 hipError_t launch_w8a8_zp(const uint8_t* qx, const float* sx, const int32_t* zx,
                           const int32_t* rowsum_x, const uint8_t* qw, const float* sw,
                           const int32_t* zw, const int32_t* colsum_w, int64_t M, int64_t N,

@@ -174,6 +174,11 @@ const char* bgt_status_string(int status);
 /* ABI version of this header (major*100 + minor). */
 int bgt_abi_version(void);
 
+/* Diagnostics: name of the GEMM kernel that bgt_w4a8_gemm_is (float_scale = 0)
+ * or bgt_w4a8_gemm_fs (float_scale = 1) launches for this shape, as it
+ * appears in profiler traces (static storage; "invalid shape" if rejected). */
+const char* bgt_w4a8_kernel_name(int64_t M, int64_t N, int64_t K, int float_scale);
+
 #ifdef __cplusplus
 }
 #endif
