@@ -529,18 +529,22 @@ __global__ __launch_bounds__(MAXT) __attribute__((amdgpu_waves_per_eu(WPE))) voi
 
 // =====================================================================
 // Prefill kernel (large M, compute-bound): BM x BN output tile per
-// workgroup of WM x WN waves (two waves per SIMD), each wave TMW x TNW blocks
-// of 32 x 32 (v_mfma_i32_32x32x32_i8). One K step is one group of 128.
-//   A: the waves stream the BM x 128 int8 tile straight into LDS
+// workgroup of WM x WN waves (two waves per SIMD), each wave 2 x 2 blocks of
+// 32 x 32 (v_mfma_i32_32x32x32_i8). One K step is one group of 128.
+//   A: the waves copy the BM x 128 int8 tile straight into LDS
 //      (global_load_lds_dwordx4: lane L of an instruction fills bytes
 //      16L..16L+15 of a 1 KiB block = 8 rows); rows are stored unpadded with
 //      their 16-byte chunks XOR-swizzled by (row % 8), so the 32 rows read by
-//      one MFMA operand fetch hit distinct banks.
-//   B: the packed int4 blocks are loaded into registers, unpacked once per
-//      workgroup to true int8 and written to LDS ([column][128 k], padded),
-//      together with the group's scales.
-//   Two LDS stages: group l+1 is in flight while group l is multiplied; the
-//   loop is unrolled by two so each stage is a compile-time choice.
+//      one MFMA operand fetch hit distinct banks. The group's scales follow.
+//   B: each lane copies one 16-byte packed int4 chunk into LDS, later
+//      unpacks that same chunk to true int8 and writes it to the unpacked B
+//      stage ([column][128 k], padded rows).
+// Pipeline: three A/packed stages and two unpacked B stages. Step l runs the
+// MFMAs of group l in four blocks; between blocks 1 and 2 the waves unpack
+// group l+1, meet at a barrier and request group l+3. The operand fragments
+// of group l+1 are read from LDS under the MFMAs of blocks 2, 3 of step l and
+// blocks 0, 1 of step l+1, and each block's scale epilogue runs under the
+// next block's MFMAs.
 // Integer-scale epilogue per group: acc += p * iscale (24-bit multiply-add,
 // exact mod 2^32); float-scale control: acc = fma((float)p, fscale, acc).
 // Workgroups are mapped so consecutive tiles of one XCD (WG id % 8) share
@@ -595,36 +599,6 @@ __device__ __forceinline__ uint4 lds_read_own_copy(const uint4* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// Four 16-byte LDS reads (an MFMA operand set) and two 4-byte ones, each
-// group as one asm block that waits for its results: the data was written by
-// LDS copies whose completion the caller established with its own waits.
-__device__ __forceinline__ void lds_read4(v4i (&v)[4], uint32_t a0, uint32_t a1, uint32_t a2,
-                                          uint32_t a3) {
-  asm volatile(
-      "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\t"
-      "ds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\ts_waitcnt lgkmcnt(0)"
-      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
-      : "v"(a0), "v"(a1), "v"(a2), "v"(a3));
-}
-// The two 32-column B operand sets of a wave: rows cl and cl+32 of the
-// unpacked stage (row pitch 144 bytes), 16-byte reads at +0..48.
-__device__ __forceinline__ void lds_read_b_pair(v4i (&b)[2][4], uint32_t base) {
-  asm volatile(
-      "ds_read_b128 %0, %8\n\tds_read_b128 %1, %8 offset:16\n\t"
-      "ds_read_b128 %2, %8 offset:32\n\tds_read_b128 %3, %8 offset:48\n\t"
-      "ds_read_b128 %4, %8 offset:4608\n\tds_read_b128 %5, %8 offset:4624\n\t"
-      "ds_read_b128 %6, %8 offset:4640\n\tds_read_b128 %7, %8 offset:4656\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(b[0][0]), "=&v"(b[0][1]), "=&v"(b[0][2]), "=&v"(b[0][3]),
-        "=&v"(b[1][0]), "=&v"(b[1][1]), "=&v"(b[1][2]), "=&v"(b[1][3])
-      : "v"(base));
-}
-__device__ __forceinline__ void lds_read2_b32(int32_t& x, int32_t& y, uint32_t a0, uint32_t a1) {
-  asm volatile("ds_read_b32 %0, %2\n\tds_read_b32 %1, %3\n\ts_waitcnt lgkmcnt(0)"
-               : "=&v"(x), "=&v"(y)
-               : "v"(a0), "v"(a1));
-}
-
 // Workgroup barrier for the LDS ring: the caller has already waited for its
 // own LDS stores (lgkmcnt) and LDS-DMA loads (vmcnt); a plain s_barrier then
 // suffices, with no fence that would also drain the loads still in flight.
@@ -636,25 +610,23 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
     const uint4* __restrict__ packed, const int32_t* __restrict__ iscale,
     const float* __restrict__ fscale, float inv_alpha, int M, int N, int K,
     float* __restrict__ y, int32_t* __restrict__ acc_out) {
+  static_assert(TMW == 2 && TNW == 2, "four 32 x 32 blocks per wave");
   constexpr int NW = WM * WN, NT = NW * 64;
   constexpr int BM = WM * TMW * 32, BN = WN * TNW * 32, NB = TMW * TNW;
   constexpr int A_INSTR = BM / (8 * NW);            // 1 KiB (8-row) blocks per wave per group
   constexpr int B_CH = BN * 4 / NT;                 // packed 16-byte chunks per thread per group
-  constexpr int LOADS = A_INSTR + 1 + B_CH;         // vector-memory instructions per group per wave
+  constexpr int LOADS = A_INSTR + 1 + B_CH;         // LDS copies per group per wave
   static_assert(A_INSTR >= 1 && B_CH >= 1 && BN <= NT, "tile too small for the workgroup");
-  static_assert(BN <= 2 * 64 && NW >= BN / 64, "scales: one 64-column slice per wave");
-  // three A stages (groups l, l+1, l+2 in flight), each followed by its
-  // group's scales (NW slices of 64; slices 0..BN/64-1 are the ones read);
-  // two unpacked B stages; two packed B stages (groups l+1, l+2). Few
-  // distinct LDS objects let the compiler tell the copies in flight apart.
-  constexpr int A_BYTES = BM * 128, STAGE = A_BYTES + NW * 64 * 4;
-  __shared__ __align__(16) int8_t As0[STAGE];
-  __shared__ __align__(16) int8_t As1[STAGE];
-  __shared__ __align__(16) int8_t As2[STAGE];
-  __shared__ __align__(16) int8_t Bs0[BN * kBRow];
-  __shared__ __align__(16) int8_t Bs1[BN * kBRow];
-  __shared__ __align__(16) uint4 Ps0[BN * 4];
-  __shared__ __align__(16) uint4 Ps1[BN * 4];
+  static_assert(BN % 64 == 0 && NW >= BN / 64, "scales: one 64-column slice per wave");
+  constexpr int A_BYTES = BM * 128, STAGE = A_BYTES + BN * 4;
+  __shared__ __align__(16) int8_t SA0[STAGE];
+  __shared__ __align__(16) int8_t SA1[STAGE];
+  __shared__ __align__(16) int8_t SA2[STAGE];
+  __shared__ __align__(16) int8_t SB0[BN * kBRow];
+  __shared__ __align__(16) int8_t SB1[BN * kBRow];
+  __shared__ __align__(16) uint4 SP0[BN * 4];
+  __shared__ __align__(16) uint4 SP1[BN * 4];
+  __shared__ __align__(16) uint4 SP2[BN * 4];
 
   const int G = K / kGroup, T = N / 16;
   const int tid = threadIdx.x;
@@ -666,9 +638,11 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
   tile_of(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
-  // ---- A: lane L of block b fills row 8b + L/8, chunk slot L%8, with the
-  // row's global chunk (L%8) ^ (row % 8); row % 8 == L/8 here. Addresses are a
-  // wave-uniform base plus a 32-bit lane offset.
+  // ---- copies of one group (a group index past the end is clamped to the
+  // last group: those copies land in a free stage and are never read, and
+  // they keep the number of copies per step fixed for the wait counts)
+  // A: lane L of block b fills row 8b + L/8, chunk slot L%8, with the row's
+  // global chunk (L%8) ^ (row % 8); row % 8 == L/8 here.
   const int8_t* abase = qx + (int64_t)m0 * K;
   int aoff[A_INSTR];
 #pragma unroll
@@ -677,29 +651,13 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
     const int rr = m0 + r < M ? r : M - 1 - m0;
     aoff[i] = rr * K + 16 * ((lane % 8) ^ (lane / 8));
   }
-  auto issue_a = [&](int l, int8_t* As) {
-    const int8_t* base = abase + (int64_t)l * kGroup;
-#pragma unroll
-    for (int i = 0; i < A_INSTR; ++i)
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(base + aoff[i]),
-          (__attribute__((address_space(3))) void*)(As + (i * NW + wave) * 1024), 16, 0, 0);
-  };
-  // ---- scales: wave w streams a 64-column slice (w % (BN/64)) into its own
-  // 256-byte slot of the stage; slots 0..BN/64-1 are the ones read
+  // scales: wave w copies the 64-column slice w % (BN/64) (several waves
+  // write the same slice with the same values)
   const int32_t* ssrc = FS ? reinterpret_cast<const int32_t*>(fscale) : iscale;
-  const int scol = n0 + (wave % (BN / 64)) * 64 + lane;
+  const int sslot = wave % (BN / 64);
+  const int scol = n0 + sslot * 64 + lane;
   const int soff = scol < N ? scol : N - 1;
-  auto issue_s = [&](int l, int8_t* As) {
-    __builtin_amdgcn_global_load_lds(
-        (const __attribute__((address_space(1))) void*)(ssrc + (int64_t)l * N + soff),
-        (__attribute__((address_space(3))) void*)(As + A_BYTES + wave * 256), 4, 0, 0);
-  };
-  // ---- B: packed 16-byte chunk q (= tid + NT*u) of the tile's group block is
-  // copied by its own lane into packed stage slot q, then unpacked by the same
-  // lane into the int8 B stage. Every load of the loop is thus an LDS copy,
-  // which keeps the wait counts exact (register loads mixed with LDS copies
-  // would make the compiler wait for all of them).
+  // B: chunk q = tid + NT*u of the tile's packed group block
   const uint4* bsrc[B_CH];
 #pragma unroll
   for (int u = 0; u < B_CH; ++u) {
@@ -707,33 +665,59 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
     const int tg = n0 / 16 + tl < T ? n0 / 16 + tl : T - 1;
     bsrc[u] = packed + (int64_t)tg * G * 64 + lb;
   }
-  auto issue_b = [&](int l, uint4* Ps) {
+  auto issue_group = [&](int g, int8_t* SA, uint4* SP) {
+    const int gc = g < G ? g : G - 1;
+    const int8_t* base = abase + (int64_t)gc * kGroup;
+#pragma unroll
+    for (int i = 0; i < A_INSTR; ++i)
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(base + aoff[i]),
+          (__attribute__((address_space(3))) void*)(SA + (i * NW + wave) * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(
+        (const __attribute__((address_space(1))) void*)(ssrc + (int64_t)gc * N + soff),
+        (__attribute__((address_space(3))) void*)(SA + A_BYTES + sslot * 256), 4, 0, 0);
 #pragma unroll
     for (int u = 0; u < B_CH; ++u)
       __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(bsrc[u] + (int64_t)l * 64),
-          (__attribute__((address_space(3))) void*)(Ps + (u * NW + wave) * 64), 16, 0, 0);
+          (const __attribute__((address_space(1))) void*)(bsrc[u] + (int64_t)gc * 64),
+          (__attribute__((address_space(3))) void*)(SP + (u * NW + wave) * 64), 16, 0, 0);
   };
-  auto store_b = [&](const uint4* Ps, int8_t* Bs) {
+  // unpack this lane's own packed chunk(s) into the int8 B stage
+  auto store_b = [&](const uint4* SP, int8_t* SB) {
 #pragma unroll
     for (int u = 0; u < B_CH; ++u) {
       const int q = tid + NT * u, tl = q / 64, lb = q % 64, s = lb / 16, cc = lb % 16;
-      const uint4 w = lds_read_own_copy(Ps + q);
+      const uint4 w = lds_read_own_copy(SP + q);
       uint32_t l0, h0, l1, h1, l2, h2, l3, h3;
       unpack_i8(w.x, l0, h0);
       unpack_i8(w.y, l1, h1);
       unpack_i8(w.z, l2, h2);
       unpack_i8(w.w, l3, h3);
-      int8_t* dst = Bs + (tl * 16 + cc) * kBRow + 16 * s;
+      int8_t* dst = SB + (tl * 16 + cc) * kBRow + 16 * s;
       *reinterpret_cast<uint4*>(dst) = make_uint4(l0, h0, l1, h1);        // k = 16s + 0..15
       *reinterpret_cast<uint4*>(dst + 64) = make_uint4(l2, h2, l3, h3);   // k = 64 + 16s + 0..15
     }
   };
-  // all LOADS copies of one group; they complete in issue order
-  auto issue_group = [&](int l, int8_t* As, uint4* Ps) {
-    issue_a(l, As);
-    issue_s(l, As);
-    issue_b(l, Ps);
+
+  // ---- operand fragments (32 rows or columns, K order 64*hf + 16*m + e)
+  v4i av[TMW][4], bv[TNW][4];
+  int32_t scb[TNW], scn[TNW], spc = 0;
+  auto read_av = [&](int a, const int8_t* SA) {
+    const int row = wm * (TMW * 32) + a * 32 + lr;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      av[a][m] = *reinterpret_cast<const v4i*>(SA + row * 128 + 16 * ((4 * hf + m) ^ (row % 8)));
+  };
+  auto read_bv = [&](int b, const int8_t* SB) {
+    const int cl = wn * (TNW * 32) + b * 32 + lr;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      bv[b][m] = *reinterpret_cast<const v4i*>(SB + cl * kBRow + 64 * hf + 16 * m);
+  };
+  auto read_sc = [&](const int8_t* SA, int32_t (&sc)[TNW]) {
+    const int32_t* S = reinterpret_cast<const int32_t*>(SA + A_BYTES);
+#pragma unroll
+    for (int b = 0; b < TNW; ++b) sc[b] = S[wn * (TNW * 32) + b * 32 + lr];
   };
 
   int acc[NB][16];
@@ -743,114 +727,94 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
 #pragma unroll
     for (int r = 0; r < 16; ++r) { acc[k][r] = 0; facc[k][r] = 0.0f; }
 
-  static_assert(TNW == 2 && kBRow == 144, "B and scale reads are paired, rows 32 apart");
-  auto compute = [&](const int8_t* As, const int8_t* Bs) {
-    const uint32_t abase_lds = lds_addr(As), sbase_lds = abase_lds + A_BYTES;
-    v4i bv[TNW][4];
-    int32_t scb[TNW];
-    {
-      const int cl = wn * (TNW * 32) + lr;
-      lds_read_b_pair(bv, lds_addr(Bs) + cl * kBRow + 64 * hf);
-      lds_read2_b32(scb[0], scb[1], sbase_lds + 4 * cl, sbase_lds + 4 * (cl + 32));
-    }
+  // block k: MFMA chain over the group's 128 k while the VALU applies the
+  // scale to block k-1's partials (1 MFMA : 4 VALU); `pre` issues LDS reads
+  // of fragments needed later. The last block's partials carry into the next
+  // step (pc[1]).
+  v16i pc[2] = {v16i{0}, v16i{0}};
+  auto epilogue = [&](auto kk, const v16i& p, int32_t sc) {
+    constexpr int k = decltype(kk)::value;
 #pragma unroll
-    for (int a = 0; a < TMW; ++a) {
-      const int row = wm * (TMW * 32) + a * 32 + lr;
-      const uint32_t rb = abase_lds + row * 128;
-      v4i av[4];
-      lds_read4(av, rb + 16 * ((4 * hf + 0) ^ (row % 8)), rb + 16 * ((4 * hf + 1) ^ (row % 8)),
-                rb + 16 * ((4 * hf + 2) ^ (row % 8)), rb + 16 * ((4 * hf + 3) ^ (row % 8)));
-#pragma unroll
-      for (int b = 0; b < TNW; ++b) {
-        v16i p = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[0], bv[b][0], v16i{0}, 0, 0, 0);
-#pragma unroll
-        for (int m = 1; m < 4; ++m) p = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[m], bv[b][m], p, 0, 0, 0);
-        const int k = a * TNW + b;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if (FS) facc[k][r] = __builtin_fmaf((float)p[r], __int_as_float(scb[b]), facc[k][r]);
-          else acc[k][r] = mad24(p[r], scb[b], acc[k][r]);
-        }
-        // keep one block's MFMA results live at a time; the SIMD's other wave
-        // covers the MFMA latency
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    for (int r = 0; r < 16; ++r) {
+      if (FS) facc[k][r] = __builtin_fmaf((float)p[r], __int_as_float(sc), facc[k][r]);
+      else acc[k][r] = mad24(p[r], sc, acc[k][r]);
     }
   };
+  auto block = [&](auto kk, const v4i (&a)[4], const v4i (&b)[4], int32_t sc_prev, auto pre) {
+    constexpr int k = decltype(kk)::value;
+    constexpr int kp = (k + NB - 1) % NB;
+    v16i p = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[0], b[0], v16i{0}, 0, 0, 0);
+#pragma unroll
+    for (int m = 1; m < 4; ++m) p = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[m], b[m], p, 0, 0, 0);
+    epilogue(IC<kp>{}, pc[(k + 1) % 2], sc_prev);
+    pc[k % 2] = p;
+    pre();
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);     // LDS reads
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // VALU
+      if (i < 3) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
-  // one group step; L6 = l mod 6 fixes the stages at compile time:
-  // A/scales stage l % 3, unpacked and packed B stages l % 2.
-  // ISSUE: request group l+2; NEXT: group l+1 exists (unpack its B).
-  auto step = [&](int l, auto l6, auto issue, auto next) {
+  // ---- step l; L6 = l mod 6 fixes the stages at compile time: A/packed
+  // stage l % 3, unpacked B stage l % 2.
+  auto step = [&](int l, auto l6) {
     constexpr int L6 = decltype(l6)::value;
-    constexpr bool ISSUE = decltype(issue)::value, NEXT = decltype(next)::value;
-    constexpr int a0 = L6 % 3, a2 = (L6 + 2) % 3, b0 = L6 % 2;
-    int8_t* Ac = a0 == 0 ? As0 : (a0 == 1 ? As1 : As2);
-    int8_t* An2 = a2 == 0 ? As0 : (a2 == 1 ? As1 : As2);
-    int8_t* Bc = b0 == 0 ? Bs0 : Bs1;
-    int8_t* Bn = b0 == 0 ? Bs1 : Bs0;
-    uint4* Pn2 = b0 == 0 ? Ps0 : Ps1;         // group l was unpacked before the last barrier
-    const uint4* Pn = b0 == 0 ? Ps1 : Ps0;    // group l+1
-    if (ISSUE) issue_group(l + 2, An2, Pn2);
-    compute(Ac, Bc);
-#pragma unroll
-    for (int k = 0; k < NB; ++k)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (FS) opaque_reg(facc[k][r]);
-        else opaque_reg(acc[k][r]);
-      }
-    if (NEXT) {
-      if (ISSUE) wait_vm<LOADS>();                  // own copies of group l+1 landed
-      else wait_vm<0>();
-      store_b(Pn, Bn);
-    }
-    // group l+1 complete in LDS (all but this step's LOADS requests), own LDS
-    // stores done; then the barrier
-    if (ISSUE) wait_vm_lds0<LOADS>();
-    else wait_vm_lds0<0>();
+    constexpr int s0 = L6 % 3, s1 = (L6 + 1) % 3, b1 = (L6 + 1) % 2, b0 = L6 % 2;
+    int8_t* A0 = s0 == 0 ? SA0 : (s0 == 1 ? SA1 : SA2);
+    int8_t* A1 = s1 == 0 ? SA0 : (s1 == 1 ? SA1 : SA2);
+    uint4* P0 = s0 == 0 ? SP0 : (s0 == 1 ? SP1 : SP2);
+    uint4* P1 = s1 == 0 ? SP0 : (s1 == 1 ? SP1 : SP2);
+    int8_t* B0 = b0 == 0 ? SB0 : SB1;
+    int8_t* B1 = b1 == 0 ? SB0 : SB1;
+    block(IC<0>{}, av[0], bv[0], spc, [&] { read_bv(1, B0); });
+    block(IC<1>{}, av[0], bv[1], scb[0], [&] { read_av(1, A0); });
+    // group l+1: own copies landed (group l+2 may still be in flight), unpack
+    // its B, all LDS traffic of this wave done, barrier; then request l+3
+    // into the stage group l leaves
+    wait_vm<LOADS>();
+    store_b(P1, B1);
+    wait_vm_lds0<LOADS>();
     lds_barrier();
+    issue_group(l + 3, A0, P0);
+    block(IC<2>{}, av[1], bv[0], scb[1], [&] { read_av(0, A1); read_sc(A1, scn); });
+    block(IC<3>{}, av[1], bv[1], scb[0], [&] { read_bv(0, B1); });
+    spc = scb[1];
+#pragma unroll
+    for (int b = 0; b < TNW; ++b) scb[b] = scn[b];
   };
-  using T1 = std::integral_constant<bool, true>;
-  using F0 = std::integral_constant<bool, false>;
 
-  // ---- prologue: groups 0 and 1 requested; group 0 unpacked into B stage 0
-  issue_group(0, As0, Ps0);
-  if (G > 1) {
-    issue_group(1, As1, Ps1);
-    wait_vm_lds0<LOADS>();                          // group 0 landed, group 1 in flight
-  } else {
-    wait_vm_lds0<0>();
-  }
-  store_b(Ps0, Bs0);
-  wait_vm_lds0<LOADS>();
+  // ---- prologue: groups 0, 1, 2 requested; group 0 unpacked and its first
+  // fragments read
+  issue_group(0, SA0, SP0);
+  issue_group(1, SA1, SP1);
+  issue_group(2, SA2, SP2);
+  wait_vm<2 * LOADS>();
+  store_b(SP0, SB0);
+  wait_vm_lds0<2 * LOADS>();
   lds_barrier();
+  read_av(0, SA0);
+  read_sc(SA0, scb);
+  read_bv(0, SB0);
 
-  int l = 0;
-  for (; l + 8 <= G; l += 6) {                      // six steps, each requesting group l+2 < G
-    step(l + 0, IC<0>{}, T1{}, T1{});
-    step(l + 1, IC<1>{}, T1{}, T1{});
-    step(l + 2, IC<2>{}, T1{}, T1{});
-    step(l + 3, IC<3>{}, T1{}, T1{});
-    step(l + 4, IC<4>{}, T1{}, T1{});
-    step(l + 5, IC<5>{}, T1{}, T1{});
+  for (int l = 0; l < G; l += 6) {
+    step(l + 0, IC<0>{});
+    if (l + 1 >= G) break;
+    step(l + 1, IC<1>{});
+    if (l + 2 >= G) break;
+    step(l + 2, IC<2>{});
+    if (l + 3 >= G) break;
+    step(l + 3, IC<3>{});
+    if (l + 4 >= G) break;
+    step(l + 4, IC<4>{});
+    if (l + 5 >= G) break;
+    step(l + 5, IC<5>{});
   }
-  // remaining 0..7 groups (l is a multiple of 6: stage phase 0)
-  auto tail = [&](int i, auto l6) {
-    const int r = G - l;                            // groups left including this one
-    if (i >= r) return;
-    if (i + 2 < r) step(l + i, l6, T1{}, T1{});
-    else if (i + 1 < r) step(l + i, l6, F0{}, T1{});
-    else step(l + i, l6, F0{}, F0{});
-  };
-  tail(0, IC<0>{});
-  tail(1, IC<1>{});
-  tail(2, IC<2>{});
-  tail(3, IC<3>{});
-  tail(4, IC<4>{});
-  tail(5, IC<5>{});
-  tail(6, IC<0>{});
-  tail(7, IC<1>{});
+  epilogue(IC<NB - 1>{}, pc[(NB - 1) % 2], spc);
+  wait_vm_lds0<0>();                                // surplus copies of the last steps
 
   // ---- one conversion per output
 #pragma unroll
@@ -991,13 +955,13 @@ const char* w4a8_kernel_name(int64_t M, int64_t K, bool float_scale) {
   static const char* names[2][3][4] = {
       {{"k_w4a8_stream<1,IS>", "k_w4a8_stream<2,IS>", "k_w4a8_stream<3,IS>", "k_w4a8_stream<4,IS>"},
        {"k_w4a8_skinny<1,4,IS>", "k_w4a8_skinny<2,4,IS>", "k_w4a8_skinny<3,4,IS>", "k_w4a8_skinny<4,4,IS>"},
-       {"k_w4a8_prefill<4,2,2,2,IS>", "k_w4a8_prefill<2,2,2,2,IS>", "", ""}},
+       {"k_w4a8_prefill<4,2,2,2,IS>", "", "", ""}},
       {{"k_w4a8_stream<1,FS>", "k_w4a8_stream<2,FS>", "k_w4a8_stream<3,FS>", "k_w4a8_stream<4,FS>"},
        {"k_w4a8_skinny<1,1,FS>", "k_w4a8_skinny<2,1,FS>", "k_w4a8_skinny<3,1,FS>", "k_w4a8_skinny<4,1,FS>"},
-       {"k_w4a8_prefill<4,2,2,2,FS>", "k_w4a8_prefill<2,2,2,2,FS>", "", ""}}};
+       {"k_w4a8_prefill<4,2,2,2,FS>", "", "", ""}}};
   const W4Plan p = plan_w4a8((int)M, (int)K, float_scale);
   const int fs = float_scale ? 1 : 0;
-  if (p.path == W4Path::Tiled) return names[fs][2][M > 512 ? 0 : 1];
+  if (p.path == W4Path::Tiled) return names[fs][2][0];
   return names[fs][p.path == W4Path::Stream ? 0 : 1][p.mr - 1];
 }
 
@@ -1011,26 +975,15 @@ hipError_t launch_w4a8(bool float_scale, const int8_t* qx, const float* sx, cons
     if (float_scale) launch_small_m<true>(plan, qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream);
     else launch_small_m<false>(plan, qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream);
   } else {
-    // 256 x 128 tiles (8 waves of 64 x 64) once there are enough of them to fill the
-    // chip; 128 x 128 tiles (4 waves) below
+    // 256 x 128 tiles, 8 waves of 64 x 64
     const uint4* pk = reinterpret_cast<const uint4*>(packed);
-    if (M > 512) {
-      const int tiles = ((M + 255) / 256) * ((N + 127) / 128);
-      if (float_scale)
-        hipLaunchKernelGGL((k_w4a8_prefill<4, 2, 2, 2, true>), dim3(tiles), dim3(512), 0, stream,
-                           qx, sx, pk, iscale, fscale, inv_alpha, M, N, K, y, nullptr);
-      else
-        hipLaunchKernelGGL((k_w4a8_prefill<4, 2, 2, 2, false>), dim3(tiles), dim3(512), 0, stream,
-                           qx, sx, pk, iscale, fscale, inv_alpha, M, N, K, y, acc_out);
-    } else {
-      const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
-      if (float_scale)
-        hipLaunchKernelGGL((k_w4a8_prefill<2, 2, 2, 2, true>), dim3(tiles), dim3(256), 0, stream,
-                           qx, sx, pk, iscale, fscale, inv_alpha, M, N, K, y, nullptr);
-      else
-        hipLaunchKernelGGL((k_w4a8_prefill<2, 2, 2, 2, false>), dim3(tiles), dim3(256), 0, stream,
-                           qx, sx, pk, iscale, fscale, inv_alpha, M, N, K, y, acc_out);
-    }
+    const int tiles = ((M + 255) / 256) * ((N + 127) / 128);
+    if (float_scale)
+      hipLaunchKernelGGL((k_w4a8_prefill<4, 2, 2, 2, true>), dim3(tiles), dim3(512), 0, stream,
+                         qx, sx, pk, iscale, fscale, inv_alpha, M, N, K, y, nullptr);
+    else
+      hipLaunchKernelGGL((k_w4a8_prefill<4, 2, 2, 2, false>), dim3(tiles), dim3(512), 0, stream,
+                         qx, sx, pk, iscale, fscale, inv_alpha, M, N, K, y, acc_out);
   }
   return hipGetLastError();
 }
