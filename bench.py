@@ -13,10 +13,13 @@ algorithmic bytes of a W4A8 GEMM are N*K/2 (packed int4) + 4*G*N (integer
 scales) + M*K (int8 codes) + 4*M (token scales) + 4*M*N (fp32 output), and
 5*M*K + 4*M for the activation quantizer.
 
-Other workloads (--workload): prefill (M in 512..4096, integer- and
-float-scale GEMMs side by side; value in TOPS), single (M=16, K=N=4096),
-w8a8 (asymmetric W8A8 control, M=256, K=N=4096), block (LLaMA-2-7B decoder
-block linears at M=1 and M=512).
+Other workload (--workload prefill): M in 512..4096, integer- and
+float-scale GEMMs side by side; value in TOPS.
+
+Profiling aids (not benchmark lines): --profile-m M runs only the
+quantizer and the integer-scale GEMM at that M (decode layer shape) for
+--steps iterations; --copy-probe-mb S copies an S MiB buffer --steps times
+(a plain copy of known size, to calibrate the HBM byte counters).
 
 Prints one JSON line.
 """
@@ -41,6 +44,27 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, TOP/s
 MALL_BYTES = 256 << 20
 METRIC = "W4A8 integer-scale GEMM TOPS + HBM GB/s, K=4096 N=22016, M=1..4096"
+
+
+# HBM bytes per GEMM launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
+# (read counts x2.0, write counts x1.0, both from a plain copy of known size;
+# profiles/w4a8_gemm_kernels__M16_M256_M4096__hbm_bytes.txt), keyed by
+# (kernel, M). They hold only for the kernel source they were taken on: when
+# gemm.hip differs from that source, traffic is reported as null.
+TRAFFIC_GEMM_SHA = "759eec42bfa11b7e"
+TRAFFIC = {("k_w4a8_stream<1,IS>", 16): 53143094,
+           ("k_w4a8_prefill<4,2,2,2,IS>", 256): 79132284,
+           ("k_w4a8_prefill<4,2,2,2,IS>", 4096): 922084441}
+
+
+def measured_traffic(kernel, Ms):
+    import hashlib
+    src = os.path.join(ROOT, "bit_gemm_token_amd", "csrc", "gemm.hip")
+    with open(src, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest()[:16] != TRAFFIC_GEMM_SHA:
+            return None
+    vals = [TRAFFIC.get((kernel, M)) for M in Ms]
+    return None if any(v is None for v in vals) else int(np.mean(vals))
 
 
 def gemm_bytes(M, N, K):
@@ -163,7 +187,7 @@ def run_decode(args, torch, bgt, dev):
     avg_bytes = float(np.mean([gemm_bytes(M, N, K) for M in dMs]))
     achieved = avg_bytes / avg_us / 1e3
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(dom, dMs),
             "kernel": dom, "launch_M": dMs, "avg_launch_us": round(avg_us, 3),
             "bytes_per_launch": int(avg_bytes)}
     out = {
@@ -225,11 +249,42 @@ def run_prefill(args, torch, bgt, dev):
         "vs_baseline": None, "dtype": "int8xint4->int32", "data": "synthetic (seeded)",
         "config": {"workload": "prefill sweep: W4A8-IS GEMM K=4096 N=22016, M in {512,1024,2048,4096}"},
         "roofline": {"bound": "mfma", "achieved": r["TOPS"], "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
-                     "frac": r["mfma_frac"], "traffic": None, "kernel": r["kernel"], "launch_M": [big],
+                     "frac": r["mfma_frac"], "traffic": measured_traffic(r["kernel"], [big]),
+                     "kernel": r["kernel"], "launch_M": [big],
                      "avg_launch_us": r["us_median"]},
         "sweep": res,
     }
     return out, (x, w)
+
+
+def run_profile_m(args, torch, bgt, dev, M):
+    """Quantizer + integer-scale GEMM at one M of the decode layer, nothing else."""
+    K, N = synth.K_LAYER, synth.N_LAYER
+    x, w = synth.layer_inputs(0, M=M, K=K, N=N)
+    xd = torch.from_numpy(x).to(dev)
+    pw = bgt.pack_weights_int4(torch.from_numpy(w).to(dev), alpha=synth.ALPHA)
+    q = torch.empty((M, K), dtype=torch.int8, device=dev)
+    s = torch.empty(M, dtype=torch.float32, device=dev)
+    y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup + args.steps):
+        bgt.quantize_act(xd, q=q, scale=s)
+        bgt.w4a8_gemm_is(q, s, pw["packed"], pw["iscale"], pw["alpha"], N, y=y)
+    torch.cuda.synchronize()
+    return {"profile_m": M, "launches": args.warmup + args.steps,
+            "kernel": bgt.w4a8_kernel_name(M, N, K), "gemm_bytes": gemm_bytes(M, N, K)}
+
+
+def run_copy_probe(args, torch, dev, mib):
+    """A plain device copy of known size (read mib MiB, write mib MiB) per launch."""
+    n = (mib << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup + args.steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    return {"copy_probe_bytes_each_way": n * 4, "launches": args.warmup + args.steps}
 
 
 def main():
@@ -239,6 +294,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-m", type=int, default=0)
+    ap.add_argument("--copy-probe-mb", type=int, default=0)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -253,6 +310,11 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.profile_m or args.copy_probe_mb:
+        r = (run_profile_m(args, torch, bgt, dev, args.profile_m) if args.profile_m
+             else run_copy_probe(args, torch, dev, args.copy_probe_mb))
+        print(json.dumps(r), flush=True)
+        return
     if args.workload == "decode":
         out, (x, w) = run_decode(args, torch, bgt, dev)
     else:
