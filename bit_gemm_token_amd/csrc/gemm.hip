@@ -581,6 +581,11 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// s_waitcnt lgkmcnt(0) only (vmcnt field at its maximum: no memory wait).
+__device__ __forceinline__ void wait_lds0() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
+}
+
 // LDS byte address of a pointer into a __shared__ array.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(
@@ -816,23 +821,152 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
   epilogue(IC<NB - 1>{}, pc[(NB - 1) % 2], spc);
   wait_vm_lds0<0>();                                // surplus copies of the last steps
 
-  // ---- one conversion per output
+  // ---- one conversion per output. The lane's 32 token scales are loaded
+  // first (row indices clamped), so the stores below need no waits; full
+  // tiles store without per-element predicates.
+  float srow[TMW][16];
+#pragma unroll
+  for (int a = 0; a < TMW; ++a)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = m0 + wm * (TMW * 32) + a * 32 + 8 * (r / 4) + 4 * hf + (r % 4);
+      srow[a][r] = sx[i < M ? i : M - 1];
+    }
+  const bool full = m0 + BM <= M && n0 + BN <= N;
 #pragma unroll
   for (int k = 0; k < NB; ++k) {
     const int a = k / TNW, b = k % TNW;
     const int j = n0 + wn * (TNW * 32) + b * 32 + lr;
-    if (j >= N) continue;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int i = m0 + wm * (TMW * 32) + a * 32 + 8 * (r / 4) + 4 * hf + (r % 4);
+      if (!full && (i >= M || j >= N)) continue;
+      const int64_t o = (int64_t)i * N + j;
+      if (FS) {
+        y[o] = facc[k][r] * srow[a][r];
+      } else {
+        const float t0 = (float)acc[k][r] * srow[a][r];
+        y[o] = t0 * inv_alpha;
+        if (acc_out) acc_out[o] = acc[k][r];
+      }
+    }
+  }
+}
+
+// =====================================================================
+// Decode kernel (M <= 64, weight streaming): one wave owns one 16-column tile
+// for all K and one 16-row block of X, so no partial sums cross waves.
+//   X: the workgroup copies its 16 rows x K int8 once into LDS in MFMA
+//      fragment order (fragment (g, h) = 1 KiB: lane L holds row L%16,
+//      k = 128g + 64h + 16(L/16) .. +15), rows past M clamped.
+//   W: each wave keeps D packed 1 KiB group blocks of its tile (16 bytes per
+//      lane, non-temporal) and their D scales in flight, refilling one slot
+//      per group; unpack by nibble-to-high-half (codes enter as 16*q), two
+//      v_mfma_i32_16x16x64_i8 per group, partial >> 4, then the group's
+//      integer scale by v_mad_i32_i24 (float-scale control: ascending fma).
+// Workgroup id -> (tile set, row block) keeps the row blocks of one tile set
+// on one XCD (same id mod 8), so their weight reads after the first hit L2.
+// =====================================================================
+template <bool FS, int W, int D, int G>
+__global__ __launch_bounds__(W * 64) void k_w4a8_decode(
+    const int8_t* __restrict__ qx, const float* __restrict__ sx,
+    const uint4* __restrict__ packed, const int32_t* __restrict__ iscale,
+    const float* __restrict__ fscale, float inv_alpha, int M, int N, int RB,
+    float* __restrict__ y, int32_t* __restrict__ acc_out) {
+  static_assert(G % D == 0 && (2 * G) % W == 0, "groups per wave");
+  __shared__ __align__(16) int8_t sA[2 * G * 1024];  // 2G fragments of 1 KiB
+  constexpr int K = G * kGroup;
+  const int T = N / 16;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int c = lane % 16, s4 = lane / 16;
+  const int id = blockIdx.x, rest = id / 8;
+  const int rb = rest % RB, ts = (rest / RB) * 8 + id % 8;
+  const int t = ts * W + wave;
+  const bool tvalid = t < T;
+  const int tc = tvalid ? t : T - 1;
+  const int r0 = rb * 16;
+
+  // ---- X rows r0..r0+15 (clamped) into LDS: this wave's fragments
+  // f = wave + W*i (indices past the last one repeat it: same bytes written
+  // twice). Plain loads issued first, so every load of the kernel is a
+  // register load and the wait counts stay exact.
+  constexpr int FPW = 2 * G / W;
+  v4i xa[FPW];
+  {
+    const int row = r0 + c < M ? r0 + c : M - 1;
+    const int8_t* xr = qx + (int64_t)row * K + 16 * s4;
+#pragma unroll
+    for (int i = 0; i < FPW; ++i) xa[i] = load_v4i(xr + 64 * (wave + W * i));
+  }
+  // ---- first D groups of the tile in flight
+  const uint4* wsrc = packed + (int64_t)tc * G * 64 + lane;
+  const int32_t* ssrc = FS ? reinterpret_cast<const int32_t*>(fscale) + tc * 16 + c
+                           : iscale + tc * 16 + c;
+  uint4 wb[D];
+  int32_t ws[D];
+#pragma unroll
+  for (int j = 0; j < D; ++j) {
+    wb[j] = load_u4_nt(wsrc + (int64_t)j * 64);
+    ws[j] = ssrc[(int64_t)j * N];
+  }
+  float srow[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int i = r0 + 4 * s4 + r;
+    srow[r] = sx[i < M ? i : M - 1];
+  }
+#pragma unroll
+  for (int i = 0; i < FPW; ++i)
+    *reinterpret_cast<v4i*>(sA + (wave + W * i) * 1024 + lane * 16) = xa[i];
+  wait_lds0();
+  lds_barrier();
+
+  int acc[4] = {0, 0, 0, 0};
+  float facc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto group = [&](int g, const uint4& w, int32_t sc) {
+    const v4i a0 = *reinterpret_cast<const v4i*>(sA + (2 * g) * 1024 + lane * 16);
+    const v4i a1 = *reinterpret_cast<const v4i*>(sA + (2 * g + 1) * 1024 + lane * 16);
+    uint32_t x0, x1, x2, x3, x4, x5, x6, x7;
+    unpack_x16(w.x, x0, x1);
+    unpack_x16(w.y, x2, x3);
+    unpack_x16(w.z, x4, x5);
+    unpack_x16(w.w, x6, x7);
+    const v4i b0 = {(int)x0, (int)x1, (int)x2, (int)x3};
+    const v4i b1 = {(int)x4, (int)x5, (int)x6, (int)x7};
+    v4i p = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, v4i{0, 0, 0, 0}, 0, 0, 0);
+    p = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, p, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int pv = p[r] >> 4;                      // exact: every product is 16 * q_x * q_w
+      if (FS) facc[r] = __builtin_fmaf((float)pv, __int_as_float(sc), facc[r]);
+      else acc[r] = mad24(pv, sc, acc[r]);
+    }
+  };
+  // all groups unrolled: slot g % D is refilled with group g + D
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    group(g, wb[g % D], ws[g % D]);
+    if (g + D < G) {
+      wb[g % D] = load_u4_nt(wsrc + (int64_t)(g + D) * 64);
+      ws[g % D] = ssrc[(int64_t)(g + D) * N];
+    }
+  }
+
+  // ---- one conversion per output
+  if (tvalid) {
+    const int j = t * 16 + c;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = r0 + 4 * s4 + r;
       if (i >= M) continue;
       const int64_t o = (int64_t)i * N + j;
       if (FS) {
-        y[o] = facc[k][r] * sx[i];
+        y[o] = facc[r] * srow[r];
       } else {
-        const float t0 = (float)acc[k][r] * sx[i];
+        const float t0 = (float)acc[r] * srow[r];
         y[o] = t0 * inv_alpha;
-        if (acc_out) acc_out[o] = acc[k][r];
+        if (acc_out) acc_out[o] = acc[r];
       }
     }
   }
@@ -888,15 +1022,20 @@ static size_t stream_lds_bytes(int MR, int GPW, bool FS, int G) {
   return 2 * area;                                 // two copies, tile parity
 }
 
-enum class W4Path { Stream, Skinny, Tiled };
+enum class W4Path { Decode, Stream, Skinny, Tiled };
 struct W4Plan { W4Path path; int mr; };
 
 // The kernel a W4A8 GEMM of this shape runs: small M streams the weights
-// (stream kernel while its loader waves and exchange area fit a workgroup,
-// skinny kernel otherwise); larger M takes the LDS-tiled MFMA kernel.
+// (decode kernel when K is a multiple of 16 groups and the X block fits LDS;
+// else the stream kernel while its loader waves and exchange area fit a
+// workgroup; else the skinny kernel); larger M takes the LDS-tiled MFMA kernel.
+constexpr int kDecodeW = 8;                        // waves (tiles) per decode workgroup
+constexpr int kDecodeD = 16;                       // group blocks in flight per wave
+
 static W4Plan plan_w4a8(int M, int K, bool fs) {
   if (M > 64) return {W4Path::Tiled, 0};
   const int mr = (M + 15) / 16, G = K / kGroup;
+  if (G == 16 || G == 32) return {W4Path::Decode, mr};
   int gpw = 0, maxt = 0;
   switch (mr) {
     case 1: gpw = StreamCfg<1>::GPW; maxt = StreamCfg<1>::MAXT; break;
@@ -962,6 +1101,7 @@ const char* w4a8_kernel_name(int64_t M, int64_t K, bool float_scale) {
   const W4Plan p = plan_w4a8((int)M, (int)K, float_scale);
   const int fs = float_scale ? 1 : 0;
   if (p.path == W4Path::Tiled) return names[fs][2][0];
+  if (p.path == W4Path::Decode) return float_scale ? "k_w4a8_decode<FS>" : "k_w4a8_decode<IS>";
   return names[fs][p.path == W4Path::Stream ? 0 : 1][p.mr - 1];
 }
 
@@ -971,7 +1111,25 @@ hipError_t launch_w4a8(bool float_scale, const int8_t* qx, const float* sx, cons
   const int M = (int)M64, N = (int)N64, K = (int)K64;
   const float inv_alpha = 1.0f / (float)alpha;   // exact: alpha = 2^n
   const W4Plan plan = plan_w4a8(M, K, float_scale);
-  if (plan.path != W4Path::Tiled) {
+  if (plan.path == W4Path::Decode) {
+    // one 16-column tile per wave, one 16-row block per workgroup; tile sets
+    // padded to a multiple of 8 for the XCD-aware id mapping
+    const int T = N / 16, RB = plan.mr;
+    const dim3 grid(((T + kDecodeW - 1) / kDecodeW + 7) / 8 * 8 * RB), block(kDecodeW * kWave);
+    const uint4* pk = reinterpret_cast<const uint4*>(packed);
+    const bool g32 = K / kGroup == 32;
+    if (float_scale) {
+      if (g32) hipLaunchKernelGGL((k_w4a8_decode<true, kDecodeW, kDecodeD, 32>), grid, block, 0, stream,
+                                  qx, sx, pk, iscale, fscale, inv_alpha, M, N, RB, y, nullptr);
+      else hipLaunchKernelGGL((k_w4a8_decode<true, kDecodeW, kDecodeD, 16>), grid, block, 0, stream,
+                              qx, sx, pk, iscale, fscale, inv_alpha, M, N, RB, y, nullptr);
+    } else {
+      if (g32) hipLaunchKernelGGL((k_w4a8_decode<false, kDecodeW, kDecodeD, 32>), grid, block, 0, stream,
+                                  qx, sx, pk, iscale, fscale, inv_alpha, M, N, RB, y, acc_out);
+      else hipLaunchKernelGGL((k_w4a8_decode<false, kDecodeW, kDecodeD, 16>), grid, block, 0, stream,
+                              qx, sx, pk, iscale, fscale, inv_alpha, M, N, RB, y, acc_out);
+    }
+  } else if (plan.path != W4Path::Tiled) {
     if (float_scale) launch_small_m<true>(plan, qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream);
     else launch_small_m<false>(plan, qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream);
   } else {

@@ -166,7 +166,11 @@ def _w4_case(orc, bgt, dev, seed, M, K, N, alpha=1024):
 
 SHAPES = [(1, 128, 16), (3, 384, 48), (16, 1024, 144), (17, 512, 64), (33, 256, 272),
           (64, 1024, 128), (65, 512, 144), (100, 384, 272), (128, 1024, 256), (200, 640, 400),
-          (257, 256, 528)]
+          (257, 256, 528),
+          # K of 16 or 32 groups with M <= 64: the one-wave-per-tile kernel (ragged rows,
+          # row blocks, tile sets with idle waves)
+          (1, 2048, 64), (5, 4096, 48), (17, 2048, 96), (33, 4096, 80), (40, 4096, 16),
+          (64, 2048, 160)]
 
 
 @pytest.mark.parametrize("M,K,N", SHAPES)
