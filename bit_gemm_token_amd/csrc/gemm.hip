@@ -534,8 +534,10 @@ __global__ __launch_bounds__(MAXT) __attribute__((amdgpu_waves_per_eu(WPE))) voi
 //   A: the waves copy the BM x 128 int8 tile straight into LDS
 //      (global_load_lds_dwordx4: lane L of an instruction fills bytes
 //      16L..16L+15 of a 1 KiB block = 8 rows); rows are stored unpadded with
-//      their 16-byte chunks XOR-swizzled by (row % 8), so the 32 rows read by
-//      one MFMA operand fetch hit distinct banks. The group's scales follow.
+//      their 16-byte chunks XOR-swizzled by (row / 2) % 8: a row spans 32 of
+//      the 64 banks (rows of one parity share them), so within any 16
+//      consecutive rows each (parity, chunk) pair is distinct and a 16-lane
+//      read phase of an MFMA operand fetch is conflict-free. The group's scales follow.
 //   B: each lane copies one 16-byte packed int4 chunk into LDS, later
 //      unpacks that same chunk to true int8 and writes it to the unpacked B
 //      stage ([column][128 k], padded rows).
@@ -647,14 +649,14 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
   // last group: those copies land in a free stage and are never read, and
   // they keep the number of copies per step fixed for the wait counts)
   // A: lane L of block b fills row 8b + L/8, chunk slot L%8, with the row's
-  // global chunk (L%8) ^ (row % 8); row % 8 == L/8 here.
+  // global chunk (L%8) ^ ((row / 2) % 8), row = 8b + L/8.
   const int8_t* abase = qx + (int64_t)m0 * K;
   int aoff[A_INSTR];
 #pragma unroll
   for (int i = 0; i < A_INSTR; ++i) {
     const int r = 8 * (i * NW + wave) + lane / 8;
     const int rr = m0 + r < M ? r : M - 1 - m0;
-    aoff[i] = rr * K + 16 * ((lane % 8) ^ (lane / 8));
+    aoff[i] = rr * K + 16 * ((lane % 8) ^ ((r >> 1) & 7));
   }
   // scales: wave w copies the 64-column slice w % (BN/64) (several waves
   // write the same slice with the same values)
@@ -711,7 +713,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
     const int row = wm * (TMW * 32) + a * 32 + lr;
 #pragma unroll
     for (int m = 0; m < 4; ++m)
-      av[a][m] = *reinterpret_cast<const v4i*>(SA + row * 128 + 16 * ((4 * hf + m) ^ (row % 8)));
+      av[a][m] = *reinterpret_cast<const v4i*>(SA + row * 128 + 16 * ((4 * hf + m) ^ ((row >> 1) & 7)));
   };
   auto read_bv = [&](int b, const int8_t* SB) {
     const int cl = wn * (TNW * 32) + b * 32 + lr;
@@ -855,78 +857,105 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
 
 // =====================================================================
 // Decode kernel (M <= 64, weight streaming): one wave owns one 16-column tile
-// for all K and one 16-row block of X, so no partial sums cross waves.
-//   X: the workgroup copies its 16 rows x K int8 once into LDS in MFMA
-//      fragment order (fragment (g, h) = 1 KiB: lane L holds row L%16,
-//      k = 128g + 64h + 16(L/16) .. +15), rows past M clamped.
+// for all K and all MR 16-row blocks of X, so no partial sums cross waves.
+//   X: the workgroup stages X (16*MR rows, clamped past M) in LDS in MFMA
+//      fragment order, one K chunk of CG groups (at most 64 KiB) at a time,
+//      double-buffered: fragment (g, rb, h) of a chunk = 1 KiB where lane L
+//      holds row 16rb + L%16, k = 128g + 64h + 16(L/16) .. +15. The next
+//      chunk's rows are loaded into registers under the current chunk's work.
 //   W: each wave keeps D packed 1 KiB group blocks of its tile (16 bytes per
 //      lane, non-temporal) and their D scales in flight, refilling one slot
 //      per group; unpack by nibble-to-high-half (codes enter as 16*q), two
-//      v_mfma_i32_16x16x64_i8 per group, partial >> 4, then the group's
-//      integer scale by v_mad_i32_i24 (float-scale control: ascending fma).
-// Workgroup id -> (tile set, row block) keeps the row blocks of one tile set
-// on one XCD (same id mod 8), so their weight reads after the first hit L2.
+//      v_mfma_i32_16x16x64_i8 per group and row block, partial >> 4, then the
+//      group's integer scale by v_mad_i32_i24 (float-scale control: the
+//      ascending fma chain).
+// Every load is a register load, so the compiler's wait counts stay exact.
 // =====================================================================
-template <bool FS, int W, int D, int G>
+template <bool FS, int W, int D, int G, int MR>
 __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
     const int8_t* __restrict__ qx, const float* __restrict__ sx,
     const uint4* __restrict__ packed, const int32_t* __restrict__ iscale,
-    const float* __restrict__ fscale, float inv_alpha, int M, int N, int RB,
+    const float* __restrict__ fscale, float inv_alpha, int M, int N,
     float* __restrict__ y, int32_t* __restrict__ acc_out) {
-  static_assert(G % D == 0 && (2 * G) % W == 0, "groups per wave");
-  __shared__ __align__(16) int8_t sA[2 * G * 1024];  // 2G fragments of 1 KiB
+  constexpr int CGM = MR == 1 ? 32 : 8;
+  constexpr int CG = G < CGM ? G : CGM;              // groups per X chunk (<= 64 KiB)
+  constexpr int NCH = G / CG;                        // chunks
+  constexpr int CFR = CG * MR * 2;                   // 1 KiB fragments per chunk
+  constexpr int FPW = CFR / W;                       // fragments per wave per chunk
+  constexpr int SCW = W * 16;                        // scale columns of the workgroup
+  constexpr int SCH = G * SCW / 4 / (W * 64);        // 16-byte scale chunks per thread
+  static_assert(G % D == 0 && G % CG == 0 && CFR % W == 0, "shape of the pipeline");
+  static_assert((G * SCW / 4) % (W * 64) == 0, "scale staging");
+  constexpr int NBUF = NCH > 1 ? 2 : 1;
+  __shared__ __align__(16) int8_t sA[NBUF * CFR * 1024];
+  __shared__ __align__(16) int32_t sS[G * SCW];      // [group][column of the workgroup]
   constexpr int K = G * kGroup;
   const int T = N / 16;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   const int c = lane % 16, s4 = lane / 16;
-  const int id = blockIdx.x, rest = id / 8;
-  const int rb = rest % RB, ts = (rest / RB) * 8 + id % 8;
-  const int t = ts * W + wave;
+  const int t = blockIdx.x * W + wave;
   const bool tvalid = t < T;
   const int tc = tvalid ? t : T - 1;
-  const int r0 = rb * 16;
 
-  // ---- X rows r0..r0+15 (clamped) into LDS: this wave's fragments
-  // f = wave + W*i (indices past the last one repeat it: same bytes written
-  // twice). Plain loads issued first, so every load of the kernel is a
-  // register load and the wait counts stay exact.
-  constexpr int FPW = 2 * G / W;
+  // ---- X chunk staging: this wave's fragments f = wave + W*i of chunk ch
+  // (32-bit offsets from the X base)
   v4i xa[FPW];
-  {
-    const int row = r0 + c < M ? r0 + c : M - 1;
-    const int8_t* xr = qx + (int64_t)row * K + 16 * s4;
+  auto load_chunk = [&](int ch) {
 #pragma unroll
-    for (int i = 0; i < FPW; ++i) xa[i] = load_v4i(xr + 64 * (wave + W * i));
+    for (int i = 0; i < FPW; ++i) {
+      const int f = wave + W * i, gl = f / (2 * MR), rb = (f / 2) % MR, h = f % 2;
+      const int row = 16 * rb + c < M ? 16 * rb + c : M - 1;
+      xa[i] = load_v4i(qx + (row * K + 128 * (ch * CG + gl) + 64 * h + 16 * s4));
+    }
+  };
+  auto store_chunk = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < FPW; ++i)
+      *reinterpret_cast<v4i*>(sA + (buf * CFR + wave + W * i) * 1024 + lane * 16) = xa[i];
+  };
+  load_chunk(0);
+  // ---- the workgroup's scales for all groups (columns past N clamped)
+  const int32_t* scl = FS ? reinterpret_cast<const int32_t*>(fscale) : iscale;
+  v4i sv[SCH];
+#pragma unroll
+  for (int u = 0; u < SCH; ++u) {
+    const int q = threadIdx.x + W * 64 * u, g = q / (SCW / 4), c4 = (q % (SCW / 4)) * 4;
+    const int col = blockIdx.x * SCW + c4 < N ? blockIdx.x * SCW + c4 : N - 4;
+    sv[u] = load_v4i(reinterpret_cast<const int8_t*>(scl + ((int64_t)g * N + col)));
   }
   // ---- first D groups of the tile in flight
   const uint4* wsrc = packed + (int64_t)tc * G * 64 + lane;
-  const int32_t* ssrc = FS ? reinterpret_cast<const int32_t*>(fscale) + tc * 16 + c
-                           : iscale + tc * 16 + c;
   uint4 wb[D];
-  int32_t ws[D];
 #pragma unroll
-  for (int j = 0; j < D; ++j) {
-    wb[j] = load_u4_nt(wsrc + (int64_t)j * 64);
-    ws[j] = ssrc[(int64_t)j * N];
+  for (int j = 0; j < D; ++j) wb[j] = load_u4_nt(wsrc + (int64_t)j * 64);
+  float srow[MR][4];
+#pragma unroll
+  for (int rb = 0; rb < MR; ++rb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * rb + 4 * s4 + r;
+      srow[rb][r] = sx[i < M ? i : M - 1];
+    }
+  store_chunk(0);
+#pragma unroll
+  for (int u = 0; u < SCH; ++u) {
+    const int q = threadIdx.x + W * 64 * u;
+    *reinterpret_cast<v4i*>(sS + q * 4) = sv[u];
   }
-  float srow[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int i = r0 + 4 * s4 + r;
-    srow[r] = sx[i < M ? i : M - 1];
-  }
-#pragma unroll
-  for (int i = 0; i < FPW; ++i)
-    *reinterpret_cast<v4i*>(sA + (wave + W * i) * 1024 + lane * 16) = xa[i];
+  if (NCH > 1) load_chunk(1);
   wait_lds0();
   lds_barrier();
 
-  int acc[4] = {0, 0, 0, 0};
-  float facc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  auto group = [&](int g, const uint4& w, int32_t sc) {
-    const v4i a0 = *reinterpret_cast<const v4i*>(sA + (2 * g) * 1024 + lane * 16);
-    const v4i a1 = *reinterpret_cast<const v4i*>(sA + (2 * g + 1) * 1024 + lane * 16);
+  int acc[MR][4];
+  float facc[MR][4];
+#pragma unroll
+  for (int rb = 0; rb < MR; ++rb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) { acc[rb][r] = 0; facc[rb][r] = 0.0f; }
+  auto group = [&](int g, const uint4& w) {
+    const int32_t sc = sS[g * SCW + wave * 16 + c];
+    const int8_t* base = sA + ((g / CG) % NBUF) * CFR * 1024 + (g % CG) * MR * 2048 + lane * 16;
     uint32_t x0, x1, x2, x3, x4, x5, x6, x7;
     unpack_x16(w.x, x0, x1);
     unpack_x16(w.y, x2, x3);
@@ -934,41 +963,62 @@ __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
     unpack_x16(w.w, x6, x7);
     const v4i b0 = {(int)x0, (int)x1, (int)x2, (int)x3};
     const v4i b1 = {(int)x4, (int)x5, (int)x6, (int)x7};
-    v4i p = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, v4i{0, 0, 0, 0}, 0, 0, 0);
-    p = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, p, 0, 0, 0);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int pv = p[r] >> 4;                      // exact: every product is 16 * q_x * q_w
-      if (FS) facc[r] = __builtin_fmaf((float)pv, __int_as_float(sc), facc[r]);
-      else acc[r] = mad24(pv, sc, acc[r]);
+    for (int rb = 0; rb < MR; ++rb) {
+      const v4i a0 = *reinterpret_cast<const v4i*>(base + rb * 2048);
+      const v4i a1 = *reinterpret_cast<const v4i*>(base + rb * 2048 + 1024);
+      v4i p = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, v4i{0, 0, 0, 0}, 0, 0, 0);
+      p = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, p, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int pv = p[r] >> 4;                    // exact: every product is 16 * q_x * q_w
+        if (FS) facc[rb][r] = __builtin_fmaf((float)pv, __int_as_float(sc), facc[rb][r]);
+        else acc[rb][r] = mad24(pv, sc, acc[rb][r]);
+      }
     }
   };
-  // all groups unrolled: slot g % D is refilled with group g + D
+  // chunk ch: groups ch*CG .. ch*CG+CG-1 (slot = group % D, D divides CG);
+  // every chunk but the last refills each slot with group g + D, then hands
+  // the staged rows of chunk ch+1 to LDS and requests those of ch+2
+  static_assert(CG % D == 0, "ring slots repeat per chunk");
+  auto chunk = [&](int ch, auto last) {
+    constexpr bool LAST = decltype(last)::value;
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    group(g, wb[g % D], ws[g % D]);
-    if (g + D < G) {
-      wb[g % D] = load_u4_nt(wsrc + (int64_t)(g + D) * 64);
-      ws[g % D] = ssrc[(int64_t)(g + D) * N];
+    for (int gl = 0; gl < CG; ++gl) {
+      const int g = ch * CG + gl;
+      group(g, wb[gl % D]);
+      if (!LAST || gl + D < CG) wb[gl % D] = load_u4_nt(wsrc + (int64_t)(g + D) * 64);
+      __builtin_amdgcn_sched_barrier(0);             // keep each group's fragments short-lived
     }
-  }
+    if (!LAST) {
+      store_chunk((ch + 1) % NBUF);
+      if (ch + 2 < NCH) load_chunk(ch + 2);
+      wait_lds0();
+      lds_barrier();
+    }
+  };
+#pragma unroll 1
+  for (int ch = 0; ch < NCH - 1; ++ch) chunk(ch, std::false_type{});
+  chunk(NCH - 1, std::true_type{});
 
   // ---- one conversion per output
   if (tvalid) {
     const int j = t * 16 + c;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = r0 + 4 * s4 + r;
-      if (i >= M) continue;
-      const int64_t o = (int64_t)i * N + j;
-      if (FS) {
-        y[o] = facc[r] * srow[r];
-      } else {
-        const float t0 = (float)acc[r] * srow[r];
-        y[o] = t0 * inv_alpha;
-        if (acc_out) acc_out[o] = acc[r];
+    for (int rb = 0; rb < MR; ++rb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * rb + 4 * s4 + r;
+        if (i >= M) continue;
+        const int64_t o = (int64_t)i * N + j;
+        if (FS) {
+          y[o] = facc[rb][r] * srow[rb][r];
+        } else {
+          const float t0 = (float)acc[rb][r] * srow[rb][r];
+          y[o] = t0 * inv_alpha;
+          if (acc_out) acc_out[o] = acc[rb][r];
+        }
       }
-    }
   }
 }
 
@@ -1030,7 +1080,8 @@ struct W4Plan { W4Path path; int mr; };
 // else the stream kernel while its loader waves and exchange area fit a
 // workgroup; else the skinny kernel); larger M takes the LDS-tiled MFMA kernel.
 constexpr int kDecodeW = 8;                        // waves (tiles) per decode workgroup
-constexpr int kDecodeD = 16;                       // group blocks in flight per wave
+// group blocks in flight per wave: fewer when each wave also holds several row blocks
+constexpr int decode_depth(int mr) { return mr == 1 ? 16 : 8; }
 
 static W4Plan plan_w4a8(int M, int K, bool fs) {
   if (M > 64) return {W4Path::Tiled, 0};
@@ -1105,6 +1156,23 @@ const char* w4a8_kernel_name(int64_t M, int64_t K, bool float_scale) {
   return names[fs][p.path == W4Path::Stream ? 0 : 1][p.mr - 1];
 }
 
+template <bool FS, int G>
+static void launch_decode(int mr, dim3 grid, dim3 block, hipStream_t stream, const int8_t* qx,
+                          const float* sx, const uint4* pk, const int32_t* iscale,
+                          const float* fscale, float inv_alpha, int M, int N, float* y,
+                          int32_t* acc_out) {
+  switch (mr) {
+    case 1: hipLaunchKernelGGL((k_w4a8_decode<FS, kDecodeW, decode_depth(1), G, 1>), grid, block, 0, stream,
+                               qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out); break;
+    case 2: hipLaunchKernelGGL((k_w4a8_decode<FS, kDecodeW, decode_depth(2), G, 2>), grid, block, 0, stream,
+                               qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out); break;
+    case 3: hipLaunchKernelGGL((k_w4a8_decode<FS, kDecodeW, decode_depth(3), G, 3>), grid, block, 0, stream,
+                               qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out); break;
+    default: hipLaunchKernelGGL((k_w4a8_decode<FS, kDecodeW, decode_depth(4), G, 4>), grid, block, 0, stream,
+                                qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out); break;
+  }
+}
+
 hipError_t launch_w4a8(bool float_scale, const int8_t* qx, const float* sx, const uint8_t* packed,
                        const int32_t* iscale, const float* fscale, int alpha, int64_t M64,
                        int64_t N64, int64_t K64, float* y, int32_t* acc_out, hipStream_t stream) {
@@ -1112,22 +1180,17 @@ hipError_t launch_w4a8(bool float_scale, const int8_t* qx, const float* sx, cons
   const float inv_alpha = 1.0f / (float)alpha;   // exact: alpha = 2^n
   const W4Plan plan = plan_w4a8(M, K, float_scale);
   if (plan.path == W4Path::Decode) {
-    // one 16-column tile per wave, one 16-row block per workgroup; tile sets
-    // padded to a multiple of 8 for the XCD-aware id mapping
-    const int T = N / 16, RB = plan.mr;
-    const dim3 grid(((T + kDecodeW - 1) / kDecodeW + 7) / 8 * 8 * RB), block(kDecodeW * kWave);
+    // one 16-column tile per wave, all rows per workgroup
+    const int T = N / 16;
+    const dim3 grid((T + kDecodeW - 1) / kDecodeW), block(kDecodeW * kWave);
     const uint4* pk = reinterpret_cast<const uint4*>(packed);
     const bool g32 = K / kGroup == 32;
     if (float_scale) {
-      if (g32) hipLaunchKernelGGL((k_w4a8_decode<true, kDecodeW, kDecodeD, 32>), grid, block, 0, stream,
-                                  qx, sx, pk, iscale, fscale, inv_alpha, M, N, RB, y, nullptr);
-      else hipLaunchKernelGGL((k_w4a8_decode<true, kDecodeW, kDecodeD, 16>), grid, block, 0, stream,
-                              qx, sx, pk, iscale, fscale, inv_alpha, M, N, RB, y, nullptr);
+      if (g32) launch_decode<true, 32>(plan.mr, grid, block, stream, qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, nullptr);
+      else launch_decode<true, 16>(plan.mr, grid, block, stream, qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, nullptr);
     } else {
-      if (g32) hipLaunchKernelGGL((k_w4a8_decode<false, kDecodeW, kDecodeD, 32>), grid, block, 0, stream,
-                                  qx, sx, pk, iscale, fscale, inv_alpha, M, N, RB, y, acc_out);
-      else hipLaunchKernelGGL((k_w4a8_decode<false, kDecodeW, kDecodeD, 16>), grid, block, 0, stream,
-                              qx, sx, pk, iscale, fscale, inv_alpha, M, N, RB, y, acc_out);
+      if (g32) launch_decode<false, 32>(plan.mr, grid, block, stream, qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out);
+      else launch_decode<false, 16>(plan.mr, grid, block, stream, qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out);
     }
   } else if (plan.path != W4Path::Tiled) {
     if (float_scale) launch_small_m<true>(plan, qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream);
