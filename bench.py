@@ -13,8 +13,12 @@ algorithmic bytes of a W4A8 GEMM are N*K/2 (packed int4) + 4*G*N (integer
 scales) + M*K (int8 codes) + 4*M (token scales) + 4*M*N (fp32 output), and
 5*M*K + 4*M for the activation quantizer.
 
-Other workload (--workload prefill): M in 512..4096, integer- and
-float-scale GEMMs side by side; value in TOPS.
+Other workloads: --workload prefill (M in 512..4096, integer- and
+float-scale GEMMs side by side; value in TOPS); --workload w8a8 (the
+asymmetric W8A8 control with zero-point correction at M=256, K=N=4096;
+activation quantization per step, weights quantized offline; value in GB/s
+with algorithmic bytes N*K + M*K + 12*(M+N) + 4*M*N, plus 5*M*K + 12*M for
+the activation quantizer).
 
 Profiling aids (not benchmark lines): --profile-m M runs only the
 quantizer and the integer-scale GEMM at that M (decode layer shape) for
@@ -257,6 +261,61 @@ def run_prefill(args, torch, bgt, dev):
     return out, (x, w)
 
 
+def run_w8a8(args, torch, bgt, dev):
+    """Asymmetric W8A8 control: per-token uint8 X with zero points, per-channel W."""
+    M, K, N = 256, 4096, 4096
+    x, w = synth.w8a8_inputs(0, M, K, N)
+    xd = torch.from_numpy(x).to(dev)
+    wt = torch.from_numpy(np.ascontiguousarray(w.T)).to(dev)
+    qw, sw, zw, cw = bgt.quantize_act(wt, mode="asym")          # offline
+    rot = [(qw.clone(), sw.clone(), zw.clone(), cw.clone())
+           for _ in range(max(2, math.ceil(2 * MALL_BYTES / qw.numel())))]
+    qx = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    sx = torch.empty(M, dtype=torch.float32, device=dev)
+    zx = torch.empty(M, dtype=torch.int32, device=dev)
+    rx = torch.empty(M, dtype=torch.int32, device=dev)
+    y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    gb = N * K + M * K + 12 * (M + N) + 4 * M * N
+    qb = 5 * M * K + 12 * M
+    ts = []
+    it = 0
+    torch.cuda.synchronize()
+    t0 = None
+    for i in range(args.warmup + args.steps):
+        if i == args.warmup:
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+        bgt.quantize_act(xd, mode="asym", q=qx, scale=sx, zero=zx, rowsum=rx)
+        a, b, c, d = rot[it % len(rot)]
+        it += 1
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        bgt.w8a8_gemm_zp(qx, sx, zx, rx, a, b, c, d, y=y)
+        e1.record()
+        if i >= args.warmup:
+            ts.append((e0, e1))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in ts]))
+    avg = float(np.mean([a.elapsed_time(b) * 1e3 for a, b in ts]))
+    ms_step = wall * 1e3 / args.steps
+    achieved = gb / avg / 1e3
+    return {
+        "metric": METRIC, "value": round((gb + qb) / (ms_step * 1e-3) / 1e9, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u8xu8->int32",
+        "data": "synthetic (seeded; X ~N(0.5,1), W ~N(0,0.02))",
+        "config": {"workload": "W8A8 asymmetric control: quant_act(asym) + w8a8_gemm_zp, M=256 K=4096 N=4096",
+                   "weight_buffers_rotated": len(rot)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "k_gemm_tiled<1,1,ZP>", "launch_M": [M], "avg_launch_us": round(avg, 3),
+                     "bytes_per_launch": gb},
+        "sweep": {"gemm_us_median": round(us, 3), "gemm_TOPS": round(2 * M * N * K / us / 1e6, 2)},
+    }, (x, w)
+
+
 def run_profile_m(args, torch, bgt, dev, M):
     """Quantizer + integer-scale GEMM at one M of the decode layer, nothing else."""
     K, N = synth.K_LAYER, synth.N_LAYER
@@ -292,7 +351,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="decode", choices=["decode", "prefill"])
+    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "w8a8"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-m", type=int, default=0)
     ap.add_argument("--copy-probe-mb", type=int, default=0)
@@ -317,9 +376,11 @@ def main():
         return
     if args.workload == "decode":
         out, (x, w) = run_decode(args, torch, bgt, dev)
-    else:
+    elif args.workload == "prefill":
         out, (x, w) = run_prefill(args, torch, bgt, dev)
-    if not args.no_cpu_baseline:
+    else:
+        out, (x, w) = run_w8a8(args, torch, bgt, dev)
+    if not args.no_cpu_baseline and args.workload != "w8a8":
         out["cpu_baseline"] = cpu_baseline(x, w)
     print(json.dumps(out), flush=True)
 
