@@ -52,13 +52,17 @@ METRIC = "W4A8 integer-scale GEMM TOPS + HBM GB/s, K=4096 N=22016, M=1..4096"
 
 # HBM bytes per GEMM launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
 # (read counts x2.0, write counts x1.0, both from a plain copy of known size;
-# profiles/w4a8_gemm_kernels__M16_M256_M4096__hbm_bytes.txt), keyed by
+# profiles/w4a8_gemm_kernels__M1_to_M4096__hbm_bytes.txt), keyed by
 # (kernel, M). They hold only for the kernel source they were taken on: when
 # gemm.hip differs from that source, traffic is reported as null.
-TRAFFIC_GEMM_SHA = "759eec42bfa11b7e"
-TRAFFIC = {("k_w4a8_stream<1,IS>", 16): 53143094,
-           ("k_w4a8_prefill<4,2,2,2,IS>", 256): 79132284,
-           ("k_w4a8_prefill<4,2,2,2,IS>", 4096): 922084441}
+TRAFFIC_GEMM_SHA = "89a8b95fcf027b86"
+TRAFFIC = {("k_w4a8_decode<IS>", 1): 48165840,
+           ("k_w4a8_decode<IS>", 4): 48528327,
+           ("k_w4a8_decode<IS>", 16): 49978271,
+           ("k_w4a8_decode<IS>", 64): 67820087,
+           ("k_w4a8_prefill<4,2,2,2,IS>", 256): 79138575,
+           ("k_w4a8_prefill<4,2,2,2,IS>", 4096): 922114849,
+           ("k_gemm_tiled<1,1,ZP>", 256): 29525414}
 
 
 def measured_traffic(kernel, Ms):
@@ -309,7 +313,8 @@ def run_w8a8(args, torch, bgt, dev):
         "config": {"workload": "W8A8 asymmetric control: quant_act(asym) + w8a8_gemm_zp, M=256 K=4096 N=4096",
                    "weight_buffers_rotated": len(rot)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("k_gemm_tiled<1,1,ZP>", [M]),
                      "kernel": "k_gemm_tiled<1,1,ZP>", "launch_M": [M], "avg_launch_us": round(avg, 3),
                      "bytes_per_launch": gb},
         "sweep": {"gemm_us_median": round(us, 3), "gemm_TOPS": round(2 * M * N * K / us / 1e6, 2)},
