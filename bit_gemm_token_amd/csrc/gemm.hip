@@ -889,6 +889,7 @@ __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
   constexpr int NBUF = NCH > 1 ? 2 : 1;
   __shared__ __align__(16) int8_t sA[NBUF * CFR * 1024];
   __shared__ __align__(16) int32_t sS[G * SCW];      // [group][column of the workgroup]
+  __shared__ float sX[16 * MR];                      // token scales
   constexpr int K = G * kGroup;
   const int T = N / 16;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -929,15 +930,10 @@ __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
   uint4 wb[D];
 #pragma unroll
   for (int j = 0; j < D; ++j) wb[j] = load_u4_nt(wsrc + (int64_t)j * 64);
-  float srow[MR][4];
-#pragma unroll
-  for (int rb = 0; rb < MR; ++rb)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = 16 * rb + 4 * s4 + r;
-      srow[rb][r] = sx[i < M ? i : M - 1];
-    }
+  // token scales of the (at most 64) rows, read back from LDS at the end
+  const float sxi = threadIdx.x < 16 * MR ? sx[threadIdx.x < M ? threadIdx.x : M - 1] : 0.0f;
   store_chunk(0);
+  if (threadIdx.x < 16 * MR) sX[threadIdx.x] = sxi;
 #pragma unroll
   for (int u = 0; u < SCH; ++u) {
     const int q = threadIdx.x + W * 64 * u;
@@ -1011,10 +1007,11 @@ __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
         const int i = 16 * rb + 4 * s4 + r;
         if (i >= M) continue;
         const int64_t o = (int64_t)i * N + j;
+        const float si = sX[i];
         if (FS) {
-          y[o] = facc[rb][r] * srow[rb][r];
+          y[o] = facc[rb][r] * si;
         } else {
-          const float t0 = (float)acc[rb][r] * srow[rb][r];
+          const float t0 = (float)acc[rb][r] * si;
           y[o] = t0 * inv_alpha;
           if (acc_out) acc_out[o] = acc[rb][r];
         }
