@@ -6,7 +6,12 @@ M in {1, 4, 16, 64, 256}: per-token int8 quantization of X (M x 4096 fp32)
 followed by the integer-scale W4A8 GEMM. Weights are packed once before
 timing (the offline step) and then replicated into R buffers whose total
 exceeds twice the 256 MB Infinity Cache; consecutive GEMMs read different
-buffers, so weight bytes come from HBM.
+buffers, so weight bytes come from HBM. Each timed step is replayed from a
+HIP graph captured once per step, the way a serving loop issues a decode
+step; the same steps run first with every launch issued from Python, and that
+rate is reported alongside ("eager"; --launch eager makes it the reported
+one). Per-launch GEMM durations come from a graph of 2R back-to-back GEMM
+launches at one M, timed with two events around its replays.
 
 value = algorithmic bytes of one step / step time (GB/s); the per-launch
 algorithmic bytes of a W4A8 GEMM are N*K/2 (packed int4) + 4*G*N (integer
@@ -133,6 +138,55 @@ class Rotor:
         self.i += 1
         return b
 
+    def get(self, i):
+        return self.bufs[i % self.R]
+
+
+def graph_steps(torch, step, steps, warmup):
+    """Capture step(k) for k < steps into one HIP graph each, replay `warmup`
+    of them untimed, then replay every graph once; returns ms per step."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for k in range(steps):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(k)
+        graphs.append(g)
+    for k in range(warmup):
+        graphs[k % steps].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for g in graphs:
+        g.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def graph_launch_us(torch, launch, n, reps=5):
+    """Per-launch duration of launch(j), j < n, captured back to back in one HIP
+    graph and replayed `reps` times between two events on the stream the
+    kernels run on; returns one duration (us) per replay."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for j in range(n):
+            launch(j)
+    g.replay()
+    ev = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) * 1e3 / n for a, b in ev]
+
 
 def run_decode(args, torch, bgt, dev):
     K, N = synth.K_LAYER, synth.N_LAYER
@@ -146,11 +200,14 @@ def run_decode(args, torch, bgt, dev):
                 torch.empty(M, dtype=torch.float32, device=dev)) for M in Ms}
     ybuf = {M: torch.empty((M, N), dtype=torch.float32, device=dev) for M in Ms}
 
-    def step(events=None):
-        for M in Ms:
+    def step(k, events=None):
+        """Step k: quantizer + GEMM per M; the GEMMs of step k read weight copies
+        k*len(Ms) .. k*len(Ms)+len(Ms)-1 (mod R), so consecutive GEMMs never
+        share a copy."""
+        for i, M in enumerate(Ms):
             q, s = qbuf[M]
             bgt.quantize_act(xs[M], q=q, scale=s)
-            packed, iscale, _ = rot.next()
+            packed, iscale, _ = rot.get(k * len(Ms) + i)
             if events is not None:
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
@@ -160,28 +217,44 @@ def run_decode(args, torch, bgt, dev):
                 e1.record()
                 events.append((M, e0, e1))
 
-    for _ in range(args.warmup):
-        step()
+    # eager launches: every call issued from Python as the step runs
+    for k in range(args.warmup):
+        step(k)
     torch.cuda.synchronize()
-    events = []
+    eager_events = []
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(events)
+    for k in range(args.steps):
+        step(k, eager_events)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
+    eager_ms = (time.perf_counter() - t0) * 1e3 / args.steps
 
-    per_m = {M: [] for M in Ms}
-    for M, e0, e1 in events:
-        per_m[M].append(e0.elapsed_time(e1) * 1e3)     # us
+    # HIP graphs: step k captured once, then replayed; the timed region
+    # replays each step's graph exactly once
+    ms_step = graph_steps(torch, step, args.steps, args.warmup) if args.launch == "graph" else eager_ms
+
+    # per-launch GEMM duration: back-to-back GEMM launches at one M, weight
+    # copies rotating as in the step
+    per_m = {}
+    for M in Ms:
+        q, s = qbuf[M]
+
+        def launch(j, q=q, s=s, M=M):
+            packed, iscale, _ = rot.get(j)
+            bgt.w4a8_gemm_is(q, s, packed, iscale, pw["alpha"], N, y=ybuf[M])
+        per_m[M] = graph_launch_us(torch, launch, 2 * rot.R)
+
+    eager_per_m = {M: [] for M in Ms}
+    for M, e0, e1 in eager_events:
+        eager_per_m[M].append(e0.elapsed_time(e1) * 1e3)     # us
     step_bytes = sum(gemm_bytes(M, N, K) + quant_bytes(M, K) for M in Ms)
     sweep = {}
     for M in Ms:
-        us = float(np.median(per_m[M]))
+        us = float(np.mean(per_m[M]))
         b = gemm_bytes(M, N, K)
-        sweep[str(M)] = {"gemm_us_median": round(us, 3), "gemm_GBps": round(b / us / 1e3, 1),
+        sweep[str(M)] = {"gemm_us": round(us, 3), "gemm_GBps": round(b / us / 1e3, 1),
                          "gemm_TOPS": round(gemm_ops(M, N, K) / us / 1e6, 2),
                          "hbm_frac": round(b / us / 1e3 / HBM_PEAK_GBS, 4),
+                         "eager_gemm_us_median": round(float(np.median(eager_per_m[M])), 3),
                          "kernel": bgt.w4a8_kernel_name(M, N, K)}
     # dominant GEMM kernel: largest summed time over the step
     by_kernel = {}
@@ -205,7 +278,10 @@ def run_decode(args, torch, bgt, dev):
         "data": "synthetic (seeded; X ~N(0,1) + 1% channels x20, W ~N(0,0.02) + 0.1% x10)",
         "config": {"workload": "decode sweep: W4A8-IS quant_act + GEMM, K=4096 N=22016 g=128 "
                                "alpha=1024, M in {1,4,16,64,256} per step",
+                   "launch": "hip_graph" if args.launch == "graph" else "eager",
                    "weight_buffers_rotated": rot.R},
+        "eager": {"ms_per_step": round(eager_ms, 4),
+                  "value": round(step_bytes / (eager_ms * 1e-3) / 1e9, 1)},
         "roofline": roof, "sweep": sweep,
     }
     return out, (x, w)
@@ -281,29 +357,36 @@ def run_w8a8(args, torch, bgt, dev):
     y = torch.empty((M, N), dtype=torch.float32, device=dev)
     gb = N * K + M * K + 12 * (M + N) + 4 * M * N
     qb = 5 * M * K + 12 * M
-    ts = []
-    it = 0
-    torch.cuda.synchronize()
-    t0 = None
-    for i in range(args.warmup + args.steps):
-        if i == args.warmup:
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
+
+    def step(k, events=None):
         bgt.quantize_act(xd, mode="asym", q=qx, scale=sx, zero=zx, rowsum=rx)
-        a, b, c, d = rot[it % len(rot)]
-        it += 1
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
+        a, b, c, d = rot[k % len(rot)]
+        if events is not None:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
         bgt.w8a8_gemm_zp(qx, sx, zx, rx, a, b, c, d, y=y)
-        e1.record()
-        if i >= args.warmup:
-            ts.append((e0, e1))
+        if events is not None:
+            e1.record()
+            events.append((e0, e1))
+
+    for k in range(args.warmup):
+        step(k)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in ts]))
-    avg = float(np.mean([a.elapsed_time(b) * 1e3 for a, b in ts]))
-    ms_step = wall * 1e3 / args.steps
+    ts = []
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(k, ts)
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    eager_us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in ts]))
+    ms_step = graph_steps(torch, step, args.steps, args.warmup) if args.launch == "graph" else eager_ms
+
+    def launch(j):
+        a, b, c, d = rot[j % len(rot)]
+        bgt.w8a8_gemm_zp(qx, sx, zx, rx, a, b, c, d, y=y)
+    durs = graph_launch_us(torch, launch, 2 * len(rot))
+    avg = float(np.mean(durs))
     achieved = gb / avg / 1e3
     return {
         "metric": METRIC, "value": round((gb + qb) / (ms_step * 1e-3) / 1e9, 1), "unit": "GB/s",
@@ -311,13 +394,16 @@ def run_w8a8(args, torch, bgt, dev):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u8xu8->int32",
         "data": "synthetic (seeded; X ~N(0.5,1), W ~N(0,0.02))",
         "config": {"workload": "W8A8 asymmetric control: quant_act(asym) + w8a8_gemm_zp, M=256 K=4096 N=4096",
+                   "launch": "hip_graph" if args.launch == "graph" else "eager",
                    "weight_buffers_rotated": len(rot)},
+        "eager": {"ms_per_step": round(eager_ms, 4), "value": round((gb + qb) / (eager_ms * 1e-3) / 1e9, 1),
+                  "gemm_us_median": round(eager_us, 3)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("k_gemm_tiled<1,1,ZP>", [M]),
                      "kernel": "k_gemm_tiled<1,1,ZP>", "launch_M": [M], "avg_launch_us": round(avg, 3),
                      "bytes_per_launch": gb},
-        "sweep": {"gemm_us_median": round(us, 3), "gemm_TOPS": round(2 * M * N * K / us / 1e6, 2)},
+        "sweep": {"gemm_us": round(avg, 3), "gemm_TOPS": round(2 * M * N * K / avg / 1e6, 2)},
     }, (x, w)
 
 
@@ -358,6 +444,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "w8a8"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--launch", default="graph", choices=["graph", "eager"],
+                    help="decode workload: replay each step from a HIP graph (default) or "
+                         "issue every launch from Python")
     ap.add_argument("--profile-m", type=int, default=0)
     ap.add_argument("--copy-probe-mb", type=int, default=0)
     args = ap.parse_args()
