@@ -60,14 +60,14 @@ METRIC = "W4A8 integer-scale GEMM TOPS + HBM GB/s, K=4096 N=22016, M=1..4096"
 # profiles/w4a8_gemm_kernels__M1_to_M4096__hbm_bytes.txt), keyed by
 # (kernel, M). They hold only for the kernel source they were taken on: when
 # gemm.hip differs from that source, traffic is reported as null.
-TRAFFIC_GEMM_SHA = "89a8b95fcf027b86"
-TRAFFIC = {("k_w4a8_decode<IS>", 1): 48165840,
-           ("k_w4a8_decode<IS>", 4): 48528327,
-           ("k_w4a8_decode<IS>", 16): 49978271,
-           ("k_w4a8_decode<IS>", 64): 67820087,
-           ("k_w4a8_prefill<4,2,2,2,IS>", 256): 79138575,
-           ("k_w4a8_prefill<4,2,2,2,IS>", 4096): 922114849,
-           ("k_gemm_tiled<1,1,ZP>", 256): 29525414}
+TRAFFIC_GEMM_SHA = "1488fd7d04e88ee3"
+TRAFFIC = {("k_w4a8_decode<IS>", 1): 48166887,
+           ("k_w4a8_decode<IS>", 4): 48530397,
+           ("k_w4a8_decode<IS>", 16): 49980342,
+           ("k_w4a8_decode<IS>", 64): 55828244,
+           ("k_w4a8_prefill<4,2,2,2,IS>", 256): 79138687,
+           ("k_w4a8_prefill<4,2,2,2,IS>", 4096): 922106797,
+           ("k_gemm_tiled<1,1,ZP>", 256): 29524652}
 
 
 def measured_traffic(kernel, Ms):
