@@ -18,6 +18,9 @@ algorithmic bytes of a W4A8 GEMM are N*K/2 (packed int4) + 4*G*N (integer
 scales) + M*K (int8 codes) + 4*M (token scales) + 4*M*N (fp32 output), and
 5*M*K + 4*M for the activation quantizer.
 
+--iscale-bits 8 or 16 stores the integer scales as uint8 / uint16 (the same
+values, narrowed offline) and counts their bytes at that width.
+
 Other workloads: --workload prefill (M in 512..4096, integer- and
 float-scale GEMMs side by side; value in TOPS); --workload w8a8 (the
 asymmetric W8A8 control with zero-point correction at M=256, K=N=4096;
@@ -80,9 +83,9 @@ def measured_traffic(kernel, Ms):
     return None if any(v is None for v in vals) else int(np.mean(vals))
 
 
-def gemm_bytes(M, N, K):
+def gemm_bytes(M, N, K, scale_bytes=4):
     G = K // 128
-    return N * K // 2 + 4 * G * N + M * K + 4 * M + 4 * M * N
+    return N * K // 2 + scale_bytes * G * N + M * K + 4 * M + 4 * M * N
 
 
 def quant_bytes(M, K):
@@ -195,6 +198,9 @@ def run_decode(args, torch, bgt, dev):
     xd = torch.from_numpy(x).to(dev)
     xs = {M: xd[:M].contiguous() for M in Ms}
     pw = bgt.pack_weights_int4(torch.from_numpy(w).to(dev), alpha=synth.ALPHA)
+    sb = args.iscale_bits // 8                     # bytes per stored integer scale
+    if sb != 4:                                    # offline: narrow storage, same values
+        pw["iscale"] = bgt.narrow_iscale(pw["iscale"], sb)
     rot = Rotor(torch, pw["packed"], pw["iscale"], pw["fscale"])
     qbuf = {M: (torch.empty((M, K), dtype=torch.int8, device=dev),
                 torch.empty(M, dtype=torch.float32, device=dev)) for M in Ms}
@@ -212,7 +218,7 @@ def run_decode(args, torch, bgt, dev):
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record()
-            bgt.w4a8_gemm_is(q, s, packed, iscale, pw["alpha"], N, y=ybuf[M])
+            bgt.w4a8_gemm_is_narrow(q, s, packed, iscale, pw["alpha"], N, y=ybuf[M])
             if events is not None:
                 e1.record()
                 events.append((M, e0, e1))
@@ -240,17 +246,17 @@ def run_decode(args, torch, bgt, dev):
 
         def launch(j, q=q, s=s, M=M):
             packed, iscale, _ = rot.get(j)
-            bgt.w4a8_gemm_is(q, s, packed, iscale, pw["alpha"], N, y=ybuf[M])
+            bgt.w4a8_gemm_is_narrow(q, s, packed, iscale, pw["alpha"], N, y=ybuf[M])
         per_m[M] = graph_launch_us(torch, launch, 2 * rot.R)
 
     eager_per_m = {M: [] for M in Ms}
     for M, e0, e1 in eager_events:
         eager_per_m[M].append(e0.elapsed_time(e1) * 1e3)     # us
-    step_bytes = sum(gemm_bytes(M, N, K) + quant_bytes(M, K) for M in Ms)
+    step_bytes = sum(gemm_bytes(M, N, K, sb) + quant_bytes(M, K) for M in Ms)
     sweep = {}
     for M in Ms:
         us = float(np.mean(per_m[M]))
-        b = gemm_bytes(M, N, K)
+        b = gemm_bytes(M, N, K, sb)
         sweep[str(M)] = {"gemm_us": round(us, 3), "gemm_GBps": round(b / us / 1e3, 1),
                          "gemm_TOPS": round(gemm_ops(M, N, K) / us / 1e6, 2),
                          "hbm_frac": round(b / us / 1e3 / HBM_PEAK_GBS, 4),
@@ -265,10 +271,11 @@ def run_decode(args, torch, bgt, dev):
     dMs = by_kernel[dom]
     durs = [u for M in dMs for u in per_m[M]]
     avg_us = float(np.mean(durs))
-    avg_bytes = float(np.mean([gemm_bytes(M, N, K) for M in dMs]))
+    avg_bytes = float(np.mean([gemm_bytes(M, N, K, sb) for M in dMs]))
     achieved = avg_bytes / avg_us / 1e3
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(dom, dMs),
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(dom, dMs) if sb == 4 else None,
             "kernel": dom, "launch_M": dMs, "avg_launch_us": round(avg_us, 3),
             "bytes_per_launch": int(avg_bytes)}
     out = {
@@ -279,6 +286,7 @@ def run_decode(args, torch, bgt, dev):
         "config": {"workload": "decode sweep: W4A8-IS quant_act + GEMM, K=4096 N=22016 g=128 "
                                "alpha=1024, M in {1,4,16,64,256} per step",
                    "launch": "hip_graph" if args.launch == "graph" else "eager",
+                   "iscale_storage": {4: "int32", 2: "uint16", 1: "uint8"}[sb],
                    "weight_buffers_rotated": rot.R},
         "eager": {"ms_per_step": round(eager_ms, 4),
                   "value": round(step_bytes / (eager_ms * 1e-3) / 1e9, 1)},
@@ -444,6 +452,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "w8a8"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--iscale-bits", type=int, default=32, choices=[8, 16, 32],
+                    help="decode workload: integer scales stored as uint8 / uint16 / int32 "
+                         "(same values; bytes counted at the stored width)")
     ap.add_argument("--launch", default="graph", choices=["graph", "eager"],
                     help="decode workload: replay each step from a HIP graph (default) or "
                          "issue every launch from Python")

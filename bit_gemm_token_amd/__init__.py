@@ -37,6 +37,7 @@ GROUP = 128
 EXPORTED = (
     "bgt_quantize_act", "bgt_pack_weights_int4", "bgt_w4a8_gemm_is", "bgt_w4a8_gemm_fs",
     "bgt_w8a8_gemm_zp", "bgt_status_string", "bgt_abi_version", "bgt_w4a8_kernel_name",
+    "bgt_narrow_iscale", "bgt_w4a8_gemm_is_narrow",
 )
 
 _lib = None
@@ -61,6 +62,8 @@ def lib():
         L.bgt_pack_weights_int4.argtypes = [P, I64, I64, I64, I, P, P, P, ctypes.POINTER(I), P]
         L.bgt_w4a8_gemm_is.argtypes = [P, P, P, P, I, I64, I64, I64, P, P, P]
         L.bgt_w4a8_gemm_fs.argtypes = [P, P, P, P, I64, I64, I64, P, P]
+        L.bgt_narrow_iscale.argtypes = [P, I64, I, P, P]
+        L.bgt_w4a8_gemm_is_narrow.argtypes = [P, P, P, P, I, I, I64, I64, I64, P, P, P]
         L.bgt_w8a8_gemm_zp.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, P, P, P]
         L.bgt_status_string.argtypes = [I]
         L.bgt_status_string.restype = ctypes.c_char_p
@@ -207,6 +210,46 @@ def w4a8_gemm_is(qx, sx, packed, iscale, alpha: int, N: int, y=None, acc_out=Non
     st = lib().bgt_w4a8_gemm_is(_ptr(qx), _ptr(sx), _ptr(packed), _ptr(iscale), int(alpha), M, N,
                                 K, _ptr(y), _ptr(acc_out), _stream(qx.device))
     _raise("bgt_w4a8_gemm_is", st)
+    return y
+
+
+_NARROW = {1: "uint8", 2: "uint16", 4: "int32"}
+
+
+def narrow_iscale(iscale, width: int, out=None):
+    """Integer scales stored in `width`-byte elements (1: uint8, 2: uint16).
+
+    Same values; raises BgtError (BGT_ERR_RANGE) if one does not fit.
+    Blocks until the scales have been checked on the host."""
+    torch = _torch()
+    _check(iscale, "iscale", torch.int32)
+    if width not in (1, 2):
+        raise ValueError("width must be 1 or 2")
+    dt = getattr(torch, _NARROW[width])
+    out = torch.empty(iscale.shape, dtype=dt, device=iscale.device) if out is None else out
+    _check(out, "out", dt, tuple(iscale.shape))
+    st = lib().bgt_narrow_iscale(_ptr(iscale), iscale.numel(), int(width), _ptr(out),
+                                 _stream(iscale.device))
+    _raise("bgt_narrow_iscale", st)
+    return out
+
+
+def w4a8_gemm_is_narrow(qx, sx, packed, iscale, alpha: int, N: int, y=None, acc_out=None):
+    """w4a8_gemm_is with integer scales stored as uint8, uint16 or int32
+    (width taken from iscale's dtype); returns y (M x N float32)."""
+    torch = _torch()
+    widths = {torch.uint8: 1, torch.uint16: 2, torch.int32: 4}
+    if not isinstance(iscale, torch.Tensor) or iscale.dtype not in widths:
+        raise TypeError("iscale must be a uint8, uint16 or int32 tensor")
+    M, K = _gemm_common(qx, sx, packed, iscale, iscale.dtype, N)
+    y = torch.empty((M, N), dtype=torch.float32, device=qx.device) if y is None else y
+    _check(y, "y", torch.float32, (M, N))
+    if acc_out is not None:
+        _check(acc_out, "acc_out", torch.int32, (M, N))
+    st = lib().bgt_w4a8_gemm_is_narrow(_ptr(qx), _ptr(sx), _ptr(packed), _ptr(iscale),
+                                       widths[iscale.dtype], int(alpha), M, N, K, _ptr(y),
+                                       _ptr(acc_out), _stream(qx.device))
+    _raise("bgt_w4a8_gemm_is_narrow", st)
     return y
 
 

@@ -8,6 +8,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <vector>
+
 #include "bgt.h"
 #include "launch.h"
 
@@ -39,7 +41,7 @@ int searched_alpha_log2(float smin) {
 
 extern "C" {
 
-int bgt_abi_version(void) { return 100; }
+int bgt_abi_version(void) { return 101; }
 
 const char* bgt_w4a8_kernel_name(int64_t M, int64_t N, int64_t K, int float_scale) {
   if (check_gemm_shape(M, N, K, 65536) != BGT_OK) return "invalid shape";
@@ -56,7 +58,7 @@ const char* bgt_status_string(int status) {
     case BGT_ERR_ALPHA: return "error: amplifier must be a power of two in [1, 2^30]";
     case BGT_ERR_MODE: return "error: unknown quantization mode";
     case BGT_ERR_HIP: return "error: HIP call failed";
-    case BGT_ERR_RANGE: return "error: integer scale out of range [0, 2^23)";
+    case BGT_ERR_RANGE: return "error: integer scale out of range (pack: >= 2^23; narrow: above the element type)";
     default: return "unknown status";
   }
 }
@@ -115,14 +117,22 @@ int bgt_pack_weights_int4(const float* w, int64_t K, int64_t N, int64_t group, i
 int bgt_w4a8_gemm_is(const int8_t* qx, const float* sx, const uint8_t* packed,
                      const int32_t* iscale, int alpha, int64_t M, int64_t N, int64_t K, float* y,
                      int32_t* acc_out, void* stream) {
+  return bgt_w4a8_gemm_is_narrow(qx, sx, packed, iscale, 4, alpha, M, N, K, y, acc_out, stream);
+}
+
+int bgt_w4a8_gemm_is_narrow(const int8_t* qx, const float* sx, const uint8_t* packed,
+                            const void* iscale, int width, int alpha, int64_t M, int64_t N,
+                            int64_t K, float* y, int32_t* acc_out, void* stream) {
   if (!qx || !sx || !packed || !iscale || !y) return BGT_ERR_NULL;
+  if (width != 1 && width != 2 && width != 4) return BGT_ERR_MODE;
   int st = check_gemm_shape(M, N, K, 65536);
   if (st != BGT_OK) return st;
   if (!pow2_alpha(alpha)) return BGT_ERR_ALPHA;
-  if (!aligned16(qx) || !aligned16(packed) || !aligned16(y) || (acc_out && !aligned16(acc_out)))
+  if (!aligned16(qx) || !aligned16(packed) || !aligned16(iscale) || !aligned16(y) ||
+      (acc_out && !aligned16(acc_out)))
     return BGT_ERR_ALIGN;
-  return hip_status(bgt::launch_w4a8(false, qx, sx, packed, iscale, nullptr, alpha, M, N, K, y,
-                                     acc_out, static_cast<hipStream_t>(stream)));
+  return hip_status(bgt::launch_w4a8(false, qx, sx, packed, iscale, width, nullptr, alpha, M, N,
+                                     K, y, acc_out, static_cast<hipStream_t>(stream)));
 }
 
 int bgt_w4a8_gemm_fs(const int8_t* qx, const float* sx, const uint8_t* packed,
@@ -131,9 +141,28 @@ int bgt_w4a8_gemm_fs(const int8_t* qx, const float* sx, const uint8_t* packed,
   if (!qx || !sx || !packed || !fscale || !y) return BGT_ERR_NULL;
   int st = check_gemm_shape(M, N, K, 65536);
   if (st != BGT_OK) return st;
-  if (!aligned16(qx) || !aligned16(packed) || !aligned16(y)) return BGT_ERR_ALIGN;
-  return hip_status(bgt::launch_w4a8(true, qx, sx, packed, nullptr, fscale, 1, M, N, K, y,
+  if (!aligned16(qx) || !aligned16(packed) || !aligned16(fscale) || !aligned16(y))
+    return BGT_ERR_ALIGN;
+  return hip_status(bgt::launch_w4a8(true, qx, sx, packed, nullptr, 4, fscale, 1, M, N, K, y,
                                      nullptr, static_cast<hipStream_t>(stream)));
+}
+
+int bgt_narrow_iscale(const int32_t* iscale, int64_t count, int width, void* out, void* stream) {
+  if (!iscale || !out) return BGT_ERR_NULL;
+  if (width != 1 && width != 2) return BGT_ERR_MODE;
+  if (count < 1 || count > ((int64_t)1 << 36)) return BGT_ERR_SHAPE;
+  if (!aligned16(iscale) || !aligned16(out)) return BGT_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // range check on the host (an offline step): every value in [0, 2^(8*width))
+  std::vector<int32_t> h((size_t)count);
+  hipError_t e = hipMemcpyAsync(h.data(), iscale, (size_t)count * sizeof(int32_t),
+                                hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return BGT_ERR_HIP;
+  const int32_t top = width == 1 ? 255 : 65535;
+  for (int32_t v : h)
+    if (v < 0 || v > top) return BGT_ERR_RANGE;
+  return hip_status(bgt::launch_narrow_scales(iscale, count, width, out, s));
 }
 
 int bgt_w8a8_gemm_zp(const uint8_t* qx, const float* sx, const int32_t* zx,

@@ -46,10 +46,10 @@ __device__ __forceinline__ void opaque_reg(T& v) { asm volatile("" : "+v"(v)); }
 // block. Integer partial sums of the waves meet in LDS (exact, any order).
 // The float-scale control keeps its ascending fma chain in one wave (KS = 1).
 // =====================================================================
-template <int MR, int KS, bool FS>
+template <int MR, int KS, bool FS, typename ST>
 __global__ __launch_bounds__(kWave * KS) void k_w4a8_skinny(
     const int8_t* __restrict__ qx, const float* __restrict__ sx,
-    const uint4* __restrict__ packed, const int32_t* __restrict__ iscale,
+    const uint4* __restrict__ packed, const ST* __restrict__ iscale,
     const float* __restrict__ fscale, float inv_alpha, int M, int N, int K,
     float* __restrict__ y, int32_t* __restrict__ acc_out) {
   constexpr int CH = (MR <= 2) ? 8 : 4;   // group blocks in flight per batch
@@ -87,7 +87,10 @@ __global__ __launch_bounds__(kWave * KS) void k_w4a8_skinny(
       if (l < ge) {
         bw[u] = load_u4_nt(bp + (int64_t)l * 64);
         if (FS) fsc[u] = fscale[(int64_t)l * N + j];
-        else isc[u] = iscale[(int64_t)l * N + j];
+        else {
+          isc[u] = (int)iscale[(int64_t)l * N + j];
+          if (sizeof(ST) < 4) opaque_reg(isc[u]);   // keep the 24-bit multiply-adds as written
+        }
       } else {
         bw[u] = make_uint4(0, 0, 0, 0);
         isc[u] = 0;
@@ -387,10 +390,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tiled(
 // A copy is rewritten two tiles later, after the finisher has passed the
 // intermediate barrier, i.e. after it finished reading that copy.
 // =====================================================================
-template <int MR, int GPW, bool FS, int MAXT, int WPE>
+template <int MR, int GPW, bool FS, int MAXT, int WPE, typename ST>
 __global__ __launch_bounds__(MAXT) __attribute__((amdgpu_waves_per_eu(WPE))) void k_w4a8_stream(
     const int8_t* __restrict__ qx, const float* __restrict__ sx,
-    const uint4* __restrict__ packed, const int32_t* __restrict__ iscale,
+    const uint4* __restrict__ packed, const ST* __restrict__ iscale,
     const float* __restrict__ fscale, float inv_alpha, int M, int N, int K,
     float* __restrict__ y, int32_t* __restrict__ acc_out) {
   extern __shared__ int lds[];
@@ -469,7 +472,10 @@ __global__ __launch_bounds__(MAXT) __attribute__((amdgpu_waves_per_eu(WPE))) voi
     for (int u = 0; u < GPW; ++u) {
       b[u] = load_u4_nt(packed + ((int64_t)tc * G + gcl[u]) * 64 + lane);
       if (FS) fs[u] = fscale[(int64_t)gcl[u] * N + tc * 16 + c];
-      else is[u] = iscale[(int64_t)gcl[u] * N + tc * 16 + c];
+      else {
+        is[u] = (int)iscale[(int64_t)gcl[u] * N + tc * 16 + c];
+        if (sizeof(ST) < 4) opaque_reg(is[u]);     // keep the 24-bit multiply-adds as written
+      }
     }
   };
   auto contract = [&](int it, const uint4* b, const int* is, const float* fs) {
@@ -611,10 +617,10 @@ __device__ __forceinline__ uint4 lds_read_own_copy(const uint4* p) {
 // suffices, with no fence that would also drain the loads still in flight.
 __device__ __forceinline__ void lds_barrier() { __builtin_amdgcn_s_barrier(); }
 
-template <int WM, int WN, int TMW, int TNW, bool FS>
+template <int WM, int WN, int TMW, int TNW, bool FS, typename ST>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_w4a8_prefill(
     const int8_t* __restrict__ qx, const float* __restrict__ sx,
-    const uint4* __restrict__ packed, const int32_t* __restrict__ iscale,
+    const uint4* __restrict__ packed, const ST* __restrict__ iscale,
     const float* __restrict__ fscale, float inv_alpha, int M, int N, int K,
     float* __restrict__ y, int32_t* __restrict__ acc_out) {
   static_assert(TMW == 2 && TNW == 2, "four 32 x 32 blocks per wave");
@@ -658,12 +664,18 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
     const int rr = m0 + r < M ? r : M - 1 - m0;
     aoff[i] = rr * K + 16 * ((lane % 8) ^ ((r >> 1) & 7));
   }
-  // scales: wave w copies the 64-column slice w % (BN/64) (several waves
-  // write the same slice with the same values)
-  const int32_t* ssrc = FS ? reinterpret_cast<const int32_t*>(fscale) : iscale;
+  // scales: wave w copies the 64-column slice w % (BN/64) into a 256-byte
+  // slot (several waves write the same slice with the same values); each lane
+  // copies 4 bytes = CPL scale elements. With narrow elements (CPL > 1) the
+  // lanes past the slice, and any lane past N, copy clamped in-bounds columns
+  // into the unused rest of the slot.
+  using SL = typename std::conditional<FS, int32_t, ST>::type;   // scale element as stored
+  constexpr int SB = sizeof(SL), CPL = 4 / SB;
+  static_assert(SB == 1 || SB == 2 || SB == 4, "scale element of 1, 2 or 4 bytes");
+  const char* ssrc = FS ? reinterpret_cast<const char*>(fscale) : reinterpret_cast<const char*>(iscale);
   const int sslot = wave % (BN / 64);
-  const int scol = n0 + sslot * 64 + lane;
-  const int soff = scol < N ? scol : N - 1;
+  const int scol = n0 + sslot * 64 + lane * CPL;
+  const int soff = scol <= N - CPL ? scol : N - CPL;
   // B: chunk q = tid + NT*u of the tile's packed group block
   const uint4* bsrc[B_CH];
 #pragma unroll
@@ -681,7 +693,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
           (const __attribute__((address_space(1))) void*)(base + aoff[i]),
           (__attribute__((address_space(3))) void*)(SA + (i * NW + wave) * 1024), 16, 0, 0);
     __builtin_amdgcn_global_load_lds(
-        (const __attribute__((address_space(1))) void*)(ssrc + (int64_t)gc * N + soff),
+        (const __attribute__((address_space(1))) void*)(ssrc + ((int64_t)gc * N + soff) * SB),
         (__attribute__((address_space(3))) void*)(SA + A_BYTES + sslot * 256), 4, 0, 0);
 #pragma unroll
     for (int u = 0; u < B_CH; ++u)
@@ -722,9 +734,18 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
       bv[b][m] = *reinterpret_cast<const v4i*>(SB + cl * kBRow + 64 * hf + 16 * m);
   };
   auto read_sc = [&](const int8_t* SA, int32_t (&sc)[TNW]) {
-    const int32_t* S = reinterpret_cast<const int32_t*>(SA + A_BYTES);
+    // one aligned dword read per scale; narrow elements are shifted out of it
+    const uint32_t* S = reinterpret_cast<const uint32_t*>(SA + A_BYTES);
 #pragma unroll
-    for (int b = 0; b < TNW; ++b) sc[b] = S[wn * (TNW * 32) + b * 32 + lr];
+    for (int b = 0; b < TNW; ++b) {
+      const int col = wn * (TNW * 32) + b * 32 + lr;           // column within the tile
+      const int byte = (col / 64) * 256 + (col % 64) * SB;      // slot col/64
+      const uint32_t w = S[byte / 4];
+      sc[b] = SB == 4 ? (int32_t)w : (int32_t)((w >> (8 * (byte % 4))) & ((1u << (8 * SB)) - 1u));
+      // hide the narrow value range: with it the compiler rewrites the 24-bit
+      // multiply-adds and re-associates them across groups (register blow-up)
+      if (SB != 4) opaque_reg(sc[b]);
+    }
   };
 
   int acc[NB][16];
@@ -871,10 +892,10 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
 //      ascending fma chain).
 // Every load is a register load, so the compiler's wait counts stay exact.
 // =====================================================================
-template <bool FS, int W, int D, int G, int MR>
+template <bool FS, int W, int D, int G, int MR, typename ST>
 __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
     const int8_t* __restrict__ qx, const float* __restrict__ sx,
-    const uint4* __restrict__ packed, const int32_t* __restrict__ iscale,
+    const uint4* __restrict__ packed, const ST* __restrict__ iscale,
     const float* __restrict__ fscale, float inv_alpha, int M, int N,
     float* __restrict__ y, int32_t* __restrict__ acc_out) {
   constexpr int CGM = MR == 1 ? 32 : 8;
@@ -882,13 +903,16 @@ __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
   constexpr int NCH = G / CG;                        // chunks
   constexpr int CFR = CG * MR * 2;                   // 1 KiB fragments per chunk
   constexpr int FPW = CFR / W;                       // fragments per wave per chunk
+  using SL = typename std::conditional<FS, int32_t, ST>::type;   // scale element as stored
   constexpr int SCW = W * 16;                        // scale columns of the workgroup
-  constexpr int SCH = G * SCW / 4 / (W * 64);        // 16-byte scale chunks per thread
+  constexpr int SEL = 16 / sizeof(SL);               // scale elements per 16-byte chunk
+  constexpr int SCT = G * SCW / SEL;                 // 16-byte scale chunks of the workgroup
+  constexpr int SCH = (SCT + W * 64 - 1) / (W * 64); // ... per thread
   static_assert(G % D == 0 && G % CG == 0 && CFR % W == 0, "shape of the pipeline");
-  static_assert((G * SCW / 4) % (W * 64) == 0, "scale staging");
+  static_assert(SCW % SEL == 0, "scale staging");
   constexpr int NBUF = NCH > 1 ? 2 : 1;
   __shared__ __align__(16) int8_t sA[NBUF * CFR * 1024];
-  __shared__ __align__(16) int32_t sS[G * SCW];      // [group][column of the workgroup]
+  __shared__ __align__(16) SL sS[G * SCW];           // [group][column of the workgroup]
   __shared__ float sX[16 * MR];                      // token scales
   constexpr int K = G * kGroup;
   const int T = N / 16;
@@ -916,14 +940,16 @@ __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
       *reinterpret_cast<v4i*>(sA + (buf * CFR + wave + W * i) * 1024 + lane * 16) = xa[i];
   };
   load_chunk(0);
-  // ---- the workgroup's scales for all groups (columns past N clamped)
-  const int32_t* scl = FS ? reinterpret_cast<const int32_t*>(fscale) : iscale;
+  // ---- the workgroup's scales for all groups, 16-byte chunks of SEL
+  // elements (columns past N clamped; chunk q lands at byte 16q of sS)
+  const SL* scl = FS ? reinterpret_cast<const SL*>(fscale) : reinterpret_cast<const SL*>(iscale);
   v4i sv[SCH];
 #pragma unroll
   for (int u = 0; u < SCH; ++u) {
-    const int q = threadIdx.x + W * 64 * u, g = q / (SCW / 4), c4 = (q % (SCW / 4)) * 4;
-    const int col = blockIdx.x * SCW + c4 < N ? blockIdx.x * SCW + c4 : N - 4;
-    sv[u] = load_v4i(reinterpret_cast<const int8_t*>(scl + ((int64_t)g * N + col)));
+    const int q = threadIdx.x + W * 64 * u, g = q / (SCW / SEL), c0 = (q % (SCW / SEL)) * SEL;
+    const int col = blockIdx.x * SCW + c0 < N ? blockIdx.x * SCW + c0 : N - SEL;
+    if (SCT % (W * 64) == 0 || q < SCT)
+      sv[u] = load_v4i(reinterpret_cast<const int8_t*>(scl + ((int64_t)g * N + col)));
   }
   // ---- first D groups of the tile in flight
   const uint4* wsrc = packed + (int64_t)tc * G * 64 + lane;
@@ -937,7 +963,7 @@ __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
 #pragma unroll
   for (int u = 0; u < SCH; ++u) {
     const int q = threadIdx.x + W * 64 * u;
-    *reinterpret_cast<v4i*>(sS + q * 4) = sv[u];
+    if (SCT % (W * 64) == 0 || q < SCT) *reinterpret_cast<v4i*>(sS + q * SEL) = sv[u];
   }
   if (NCH > 1) load_chunk(1);
   wait_lds0();
@@ -950,7 +976,8 @@ __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
 #pragma unroll
     for (int r = 0; r < 4; ++r) { acc[rb][r] = 0; facc[rb][r] = 0.0f; }
   auto group = [&](int g, const uint4& w) {
-    const int32_t sc = sS[g * SCW + wave * 16 + c];
+    int32_t sc = (int32_t)sS[g * SCW + wave * 16 + c];
+    if (sizeof(SL) < 4) opaque_reg(sc);              // keep the 24-bit multiply-adds as written
     const int8_t* base = sA + ((g / CG) % NBUF) * CFR * 1024 + (g % CG) * MR * 2048 + lane * 16;
     uint32_t x0, x1, x2, x3, x4, x5, x6, x7;
     unpack_x16(w.x, x0, x1);
@@ -1020,13 +1047,13 @@ __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
 }
 
 // ------------------------------------------------------------------ launchers
-template <int MR, bool FS>
+template <int MR, bool FS, typename ST>
 static void launch_skinny(const int8_t* qx, const float* sx, const uint8_t* packed,
-                          const int32_t* iscale, const float* fscale, float inv_alpha, int M,
+                          const ST* iscale, const float* fscale, float inv_alpha, int M,
                           int N, int K, float* y, int32_t* acc_out, hipStream_t stream) {
   constexpr int KS = FS ? 1 : 4;
   dim3 grid(N / 16), block(kWave * KS);
-  hipLaunchKernelGGL((k_w4a8_skinny<MR, KS, FS>), grid, block, 0, stream, qx, sx,
+  hipLaunchKernelGGL((k_w4a8_skinny<MR, KS, FS, ST>), grid, block, 0, stream, qx, sx,
                      reinterpret_cast<const uint4*>(packed), iscale, fscale, inv_alpha, M, N, K, y,
                      acc_out);
 }
@@ -1096,15 +1123,15 @@ static W4Plan plan_w4a8(int M, int K, bool fs) {
   return {fits ? W4Path::Stream : W4Path::Skinny, mr};
 }
 
-template <int MR, bool FS>
+template <int MR, bool FS, typename ST>
 static bool launch_stream(const int8_t* qx, const float* sx, const uint8_t* packed,
-                          const int32_t* iscale, const float* fscale, float inv_alpha, int M,
+                          const ST* iscale, const float* fscale, float inv_alpha, int M,
                           int N, int K, float* y, int32_t* acc_out, hipStream_t stream) {
   using C = StreamCfg<MR>;
   const int G = K / kGroup, T = N / 16;
   const int KS = (G + C::GPW - 1) / C::GPW;        // loader waves (+1 finisher)
   const size_t lds = stream_lds_bytes(MR, C::GPW, FS, G);
-  auto kern = k_w4a8_stream<MR, C::GPW, FS, C::MAXT, C::WPE>;
+  auto kern = k_w4a8_stream<MR, C::GPW, FS, C::MAXT, C::WPE, ST>;
   const int pmax = resident_blocks(reinterpret_cast<const void*>(kern), (KS + 1) * kWave, lds);
   if (pmax < 1) return false;
   const int per = (T + pmax - 1) / pmax;          // tiles per workgroup
@@ -1115,26 +1142,26 @@ static bool launch_stream(const int8_t* qx, const float* sx, const uint8_t* pack
   return true;
 }
 
-template <bool FS>
+template <bool FS, typename ST>
 static void launch_small_m(const W4Plan& plan, const int8_t* qx, const float* sx,
-                           const uint8_t* packed, const int32_t* iscale, const float* fscale,
+                           const uint8_t* packed, const ST* iscale, const float* fscale,
                            float inv_alpha, int M, int N, int K, float* y, int32_t* acc_out,
                            hipStream_t stream) {
   bool done = false;
   if (plan.path == W4Path::Stream) {
     switch (plan.mr) {
-      case 1: done = launch_stream<1, FS>(qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream); break;
-      case 2: done = launch_stream<2, FS>(qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream); break;
-      case 3: done = launch_stream<3, FS>(qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream); break;
-      default: done = launch_stream<4, FS>(qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream); break;
+      case 1: done = launch_stream<1, FS, ST>(qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream); break;
+      case 2: done = launch_stream<2, FS, ST>(qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream); break;
+      case 3: done = launch_stream<3, FS, ST>(qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream); break;
+      default: done = launch_stream<4, FS, ST>(qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream); break;
     }
   }
   if (done) return;
   switch (plan.mr) {
-    case 1: launch_skinny<1, FS>(qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream); break;
-    case 2: launch_skinny<2, FS>(qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream); break;
-    case 3: launch_skinny<3, FS>(qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream); break;
-    default: launch_skinny<4, FS>(qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream); break;
+    case 1: launch_skinny<1, FS, ST>(qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream); break;
+    case 2: launch_skinny<2, FS, ST>(qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream); break;
+    case 3: launch_skinny<3, FS, ST>(qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream); break;
+    default: launch_skinny<4, FS, ST>(qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream); break;
   }
 }
 
@@ -1153,56 +1180,67 @@ const char* w4a8_kernel_name(int64_t M, int64_t K, bool float_scale) {
   return names[fs][p.path == W4Path::Stream ? 0 : 1][p.mr - 1];
 }
 
-template <bool FS, int G>
+template <bool FS, int G, typename ST>
 static void launch_decode(int mr, dim3 grid, dim3 block, hipStream_t stream, const int8_t* qx,
-                          const float* sx, const uint4* pk, const int32_t* iscale,
+                          const float* sx, const uint4* pk, const ST* iscale,
                           const float* fscale, float inv_alpha, int M, int N, float* y,
                           int32_t* acc_out) {
   switch (mr) {
-    case 1: hipLaunchKernelGGL((k_w4a8_decode<FS, kDecodeW, decode_depth(1), G, 1>), grid, block, 0, stream,
+    case 1: hipLaunchKernelGGL((k_w4a8_decode<FS, kDecodeW, decode_depth(1), G, 1, ST>), grid, block, 0, stream,
                                qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out); break;
-    case 2: hipLaunchKernelGGL((k_w4a8_decode<FS, kDecodeW, decode_depth(2), G, 2>), grid, block, 0, stream,
+    case 2: hipLaunchKernelGGL((k_w4a8_decode<FS, kDecodeW, decode_depth(2), G, 2, ST>), grid, block, 0, stream,
                                qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out); break;
-    case 3: hipLaunchKernelGGL((k_w4a8_decode<FS, kDecodeW, decode_depth(3), G, 3>), grid, block, 0, stream,
+    case 3: hipLaunchKernelGGL((k_w4a8_decode<FS, kDecodeW, decode_depth(3), G, 3, ST>), grid, block, 0, stream,
                                qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out); break;
-    default: hipLaunchKernelGGL((k_w4a8_decode<FS, kDecodeW, decode_depth(4), G, 4>), grid, block, 0, stream,
+    default: hipLaunchKernelGGL((k_w4a8_decode<FS, kDecodeW, decode_depth(4), G, 4, ST>), grid, block, 0, stream,
                                 qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out); break;
   }
 }
 
-hipError_t launch_w4a8(bool float_scale, const int8_t* qx, const float* sx, const uint8_t* packed,
-                       const int32_t* iscale, const float* fscale, int alpha, int64_t M64,
-                       int64_t N64, int64_t K64, float* y, int32_t* acc_out, hipStream_t stream) {
-  const int M = (int)M64, N = (int)N64, K = (int)K64;
-  const float inv_alpha = 1.0f / (float)alpha;   // exact: alpha = 2^n
-  const W4Plan plan = plan_w4a8(M, K, float_scale);
+template <bool FS, typename ST>
+static void launch_w4a8_t(const int8_t* qx, const float* sx, const uint8_t* packed,
+                          const ST* iscale, const float* fscale, float inv_alpha, int M, int N,
+                          int K, float* y, int32_t* acc_out, hipStream_t stream) {
+  const W4Plan plan = plan_w4a8(M, K, FS);
+  if (FS) acc_out = nullptr;
   if (plan.path == W4Path::Decode) {
     // one 16-column tile per wave, all rows per workgroup
     const int T = N / 16;
     const dim3 grid((T + kDecodeW - 1) / kDecodeW), block(kDecodeW * kWave);
     const uint4* pk = reinterpret_cast<const uint4*>(packed);
-    const bool g32 = K / kGroup == 32;
-    if (float_scale) {
-      if (g32) launch_decode<true, 32>(plan.mr, grid, block, stream, qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, nullptr);
-      else launch_decode<true, 16>(plan.mr, grid, block, stream, qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, nullptr);
-    } else {
-      if (g32) launch_decode<false, 32>(plan.mr, grid, block, stream, qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out);
-      else launch_decode<false, 16>(plan.mr, grid, block, stream, qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out);
-    }
+    if (K / kGroup == 32)
+      launch_decode<FS, 32>(plan.mr, grid, block, stream, qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out);
+    else
+      launch_decode<FS, 16>(plan.mr, grid, block, stream, qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out);
   } else if (plan.path != W4Path::Tiled) {
-    if (float_scale) launch_small_m<true>(plan, qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream);
-    else launch_small_m<false>(plan, qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream);
+    launch_small_m<FS>(plan, qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream);
   } else {
     // 256 x 128 tiles, 8 waves of 64 x 64
     const uint4* pk = reinterpret_cast<const uint4*>(packed);
     const int tiles = ((M + 255) / 256) * ((N + 127) / 128);
-    if (float_scale)
-      hipLaunchKernelGGL((k_w4a8_prefill<4, 2, 2, 2, true>), dim3(tiles), dim3(512), 0, stream,
-                         qx, sx, pk, iscale, fscale, inv_alpha, M, N, K, y, nullptr);
-    else
-      hipLaunchKernelGGL((k_w4a8_prefill<4, 2, 2, 2, false>), dim3(tiles), dim3(512), 0, stream,
-                         qx, sx, pk, iscale, fscale, inv_alpha, M, N, K, y, acc_out);
+    hipLaunchKernelGGL((k_w4a8_prefill<4, 2, 2, 2, FS, ST>), dim3(tiles), dim3(512), 0, stream,
+                       qx, sx, pk, iscale, fscale, inv_alpha, M, N, K, y, acc_out);
   }
+}
+
+hipError_t launch_w4a8(bool float_scale, const int8_t* qx, const float* sx, const uint8_t* packed,
+                       const void* iscale, int iscale_bytes, const float* fscale, int alpha,
+                       int64_t M64, int64_t N64, int64_t K64, float* y, int32_t* acc_out,
+                       hipStream_t stream) {
+  const int M = (int)M64, N = (int)N64, K = (int)K64;
+  const float inv_alpha = 1.0f / (float)alpha;   // exact: alpha = 2^n
+  if (float_scale)
+    launch_w4a8_t<true>(qx, sx, packed, static_cast<const int32_t*>(nullptr), fscale, inv_alpha,
+                        M, N, K, y, nullptr, stream);
+  else if (iscale_bytes == 4)
+    launch_w4a8_t<false>(qx, sx, packed, static_cast<const int32_t*>(iscale), nullptr, inv_alpha,
+                         M, N, K, y, acc_out, stream);
+  else if (iscale_bytes == 2)
+    launch_w4a8_t<false>(qx, sx, packed, static_cast<const uint16_t*>(iscale), nullptr, inv_alpha,
+                         M, N, K, y, acc_out, stream);
+  else
+    launch_w4a8_t<false>(qx, sx, packed, static_cast<const uint8_t*>(iscale), nullptr, inv_alpha,
+                         M, N, K, y, acc_out, stream);
   return hipGetLastError();
 }
 

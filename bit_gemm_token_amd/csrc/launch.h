@@ -19,9 +19,16 @@ hipError_t launch_group_quant_pack(const float* w, int64_t K, int64_t N, uint8_t
 hipError_t launch_integer_scales(const float* fscale, int64_t count, int alpha, int32_t* iscale,
                                  hipStream_t stream);
 
+// iscale holds (K/128) x N integer scales of iscale_bytes bytes each (4: int32,
+// 2: uint16, 1: uint8); ignored (and fscale used) when float_scale is set.
 hipError_t launch_w4a8(bool float_scale, const int8_t* qx, const float* sx, const uint8_t* packed,
-                       const int32_t* iscale, const float* fscale, int alpha, int64_t M, int64_t N,
-                       int64_t K, float* y, int32_t* acc_out, hipStream_t stream);
+                       const void* iscale, int iscale_bytes, const float* fscale, int alpha,
+                       int64_t M, int64_t N, int64_t K, float* y, int32_t* acc_out,
+                       hipStream_t stream);
+
+// narrow (K/128) x N integer scales to 2-byte or 1-byte elements (values must fit)
+hipError_t launch_narrow_scales(const int32_t* in, int64_t count, int out_bytes, void* out,
+                                hipStream_t stream);
 
 // name of the kernel a W4A8 GEMM of this shape dispatches to (diagnostics)
 const char* w4a8_kernel_name(int64_t M, int64_t K, bool float_scale);

@@ -102,4 +102,25 @@ hipError_t launch_integer_scales(const float* fscale, int64_t count, int alpha, 
   return hipGetLastError();
 }
 
+// Narrow storage of integer scales: the same values in 2-byte or 1-byte
+// unsigned elements (the caller has checked that every value fits).
+template <typename T>
+__global__ __launch_bounds__(kPThreads) void k_narrow_scales(
+    const int32_t* __restrict__ in, int64_t count, T* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * kPThreads + threadIdx.x;
+  if (i < count) out[i] = (T)in[i];
+}
+
+hipError_t launch_narrow_scales(const int32_t* in, int64_t count, int out_bytes, void* out,
+                                hipStream_t stream) {
+  dim3 grid((unsigned)((count + kPThreads - 1) / kPThreads));
+  if (out_bytes == 2)
+    hipLaunchKernelGGL(k_narrow_scales<uint16_t>, grid, dim3(kPThreads), 0, stream, in, count,
+                       static_cast<uint16_t*>(out));
+  else
+    hipLaunchKernelGGL(k_narrow_scales<uint8_t>, grid, dim3(kPThreads), 0, stream, in, count,
+                       static_cast<uint8_t*>(out));
+  return hipGetLastError();
+}
+
 }  // namespace bgt

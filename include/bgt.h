@@ -43,7 +43,7 @@ extern "C" {
 #define BGT_ERR_ALPHA             -4   /* amplifier not a power of two in [1, 2^30]     */
 #define BGT_ERR_MODE              -5   /* unknown quantization mode                    */
 #define BGT_ERR_HIP               -6   /* a HIP call failed                             */
-#define BGT_ERR_RANGE             -7   /* pack: some integer scale >= 2^23              */
+#define BGT_ERR_RANGE             -7   /* an integer scale does not fit its element     */
 
 /* Quantization modes of bgt_quantize_act. */
 #define BGT_QUANT_SYM_I8   0
@@ -125,7 +125,7 @@ int bgt_pack_weights_int4(const float* w, int64_t K, int64_t N, int64_t group, i
  *
  *   qx      M x K int8 (codes of bgt_quantize_act SYM), sx [M] float32.
  *   packed  the layout of bgt_pack_weights_int4; iscale (K/128) x N int32 with
- *           every entry in [0, 2^23).
+ *           every entry in [0, 2^23), 16-byte aligned.
  *   alpha   power of two in [1, 2^30], the one the integer scales were made with.
  *   y       M x N float32.
  *   acc_out optional M x N int32 (NULL = not written): A_ij itself.
@@ -135,6 +135,36 @@ int bgt_pack_weights_int4(const float* w, int64_t K, int64_t N, int64_t group, i
 int bgt_w4a8_gemm_is(const int8_t* qx, const float* sx, const uint8_t* packed,
                      const int32_t* iscale, int alpha, int64_t M, int64_t N, int64_t K,
                      float* y, int32_t* acc_out, void* stream);
+
+/*
+ * bgt_narrow_iscale -- store integer scales in narrower elements ([IS] 方法:
+ * the amplified scales of Fig. 4(a) fit 16-bit integers at alpha = 2^10, most
+ * of them 8 bits). out[i] = iscale[i] as uint8 (width 1) or uint16 (width 2);
+ * the values, and so every GEMM result, are unchanged. Decode-regime GEMMs
+ * stream the scales with the weights, so 1-byte scales cut their bytes by
+ * 3*G*N (2.1 MB of 48 MB for K=4096, N=22016).
+ *
+ *   iscale  count int32 values (device), e.g. the (K/128) x N output of
+ *           bgt_pack_weights_int4.
+ *   out     count * width bytes (device).
+ * Requirements: width 1 or 2 (else BGT_ERR_MODE), 1 <= count <= 2^36, both
+ * pointers 16-byte aligned. Returns BGT_ERR_RANGE, writing nothing, if some
+ * value is negative or does not fit the element (> 255 or > 65535).
+ * Blocking: iscale is copied to the host and checked before the narrowing is
+ * enqueued on `stream`.
+ */
+int bgt_narrow_iscale(const int32_t* iscale, int64_t count, int width, void* out, void* stream);
+
+/*
+ * bgt_w4a8_gemm_is_narrow -- bgt_w4a8_gemm_is with the integer scales stored
+ * in elements of `width` bytes: 1 (uint8), 2 (uint16) or 4 (int32, the same
+ * call as bgt_w4a8_gemm_is). Same formulas, arguments and requirements;
+ * iscale must be 16-byte aligned. Results are bit-identical to the int32 call
+ * on the same scale values. Unknown width: BGT_ERR_MODE.
+ */
+int bgt_w4a8_gemm_is_narrow(const int8_t* qx, const float* sx, const uint8_t* packed,
+                            const void* iscale, int width, int alpha, int64_t M, int64_t N,
+                            int64_t K, float* y, int32_t* acc_out, void* stream);
 
 /*
  * bgt_w4a8_gemm_fs -- the float-scale control ([IS] 方法 Fig. 3(b)): every
@@ -171,7 +201,8 @@ int bgt_w8a8_gemm_zp(const uint8_t* qx, const float* sx, const int32_t* zx,
 /* Human-readable text of a status code (static storage). */
 const char* bgt_status_string(int status);
 
-/* ABI version of this header (major*100 + minor). */
+/* ABI version of this header (major*100 + minor): 101 adds the narrow
+ * integer-scale entry points. */
 int bgt_abi_version(void);
 
 /* Diagnostics: name of the GEMM kernel that bgt_w4a8_gemm_is (float_scale = 0)

@@ -49,6 +49,10 @@ def _load():
         lib.orc_amplifier_log2.argtypes = [P, I64, I]
         lib.orc_amplifier_log2.restype = I
         lib.orc_integer_scales.argtypes = [P, I64, I, P]
+        lib.orc_narrow_iscale.argtypes = [P, I64, I, P]
+        lib.orc_narrow_iscale.restype = I64
+        lib.orc_weight_mse_is_fs.argtypes = [P, P, P, I, I64, I64, I64, P, P]
+        lib.orc_weight_mse_is_fs.restype = ctypes.c_double
         lib.orc_pack_int4.argtypes = [P, I64, I64, P]
         lib.orc_unpack_int4.argtypes = [P, I64, I64, P]
         lib.orc_w4a8_gemm_is.argtypes = [P, P, P, P, I, I64, I64, I64, I64, P, I64, P, I64, P, P]
@@ -114,6 +118,33 @@ def integer_scales(fscale, alpha: int):
     out = np.empty(f.shape, np.int32)
     _load().orc_integer_scales(_p(f), f.size, int(alpha), _p(out))
     return out
+
+
+def narrow_iscale(iscale, width: int):
+    """Integer scales as uint8 (width 1) or uint16 (width 2), same values.
+
+    Returns (array, 0), or (None, number of values that do not fit)."""
+    i = _c(iscale, np.int32)
+    out = np.empty(i.shape, np.uint8 if width == 1 else np.uint16)
+    bad = int(_load().orc_narrow_iscale(_p(i), i.size, int(width), _p(out)))
+    if bad < 0:
+        raise ValueError("width must be 1 or 2")
+    return (out, 0) if bad == 0 else (None, bad)
+
+
+def weight_mse_is_fs(codes, fscale, iscale, alpha: int, g: int = 128):
+    """Weight MSE between integer-scale (q*S/alpha) and float-scale (q*s)
+    dequantized weights, the largest integer scale, and how many integer
+    scales need more than 8 bits."""
+    codes = _c(codes, np.int8)
+    f = _c(fscale, np.float32)
+    i = _c(iscale, np.int32)
+    K, N = codes.shape
+    mx = ctypes.c_int32(0)
+    wide = ctypes.c_int64(0)
+    mse = _load().orc_weight_mse_is_fs(_p(codes), _p(f), _p(i), int(alpha), K, N, g,
+                                       ctypes.byref(mx), ctypes.byref(wide))
+    return float(mse), int(mx.value), int(wide.value)
 
 
 def pack_int4(codes):

@@ -178,6 +178,66 @@ EXPORT void orc_integer_scales(const float* fscale, int64_t count, int alpha, in
 }
 
 /* ------------------------------------------------------------------------
+ * Narrow storage of integer scales ([IS] 方法, Fig. 4(a): at alpha = 2^10
+ * the amplified scales fit 16-bit integers, most of them 8 bits). The values
+ * are unchanged; only the element width differs. width 1: uint8, width 2:
+ * uint16. Returns the number of values that do not fit the element (negative
+ * or too large); when that number is not zero, nothing is written. Returns -1
+ * for an unknown width.
+ * ---------------------------------------------------------------------- */
+EXPORT int64_t orc_narrow_iscale(const int32_t* iscale, int64_t count, int width, void* out)
+{
+    if (width != 1 && width != 2) return -1;
+    const int64_t top = width == 1 ? 255 : 65535;
+    int64_t bad = 0;
+    for (int64_t i = 0; i < count; ++i)
+        if (iscale[i] < 0 || iscale[i] > top) ++bad;
+    if (bad) return bad;
+    for (int64_t i = 0; i < count; ++i) {
+        if (width == 1) ((uint8_t*)out)[i] = (uint8_t)iscale[i];
+        else ((uint16_t*)out)[i] = (uint16_t)iscale[i];
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------
+ * Weight MSE between the integer-scale and the float-scale dequantized
+ * weights ([IS] 方法, Fig. 4(c): "weight MSE between integer and float
+ * scales under different amplifiers"). With codes q (K x N), float scales s
+ * and integer scales S = round(s * alpha) of group l:
+ *     w_fs = q * s,   w_is = q * S / alpha,
+ *     MSE  = (1 / (K N)) * sum_{k,j} (w_is - w_fs)^2        (double).
+ * Also returns, through the pointers (each may be NULL), the largest integer
+ * scale and the number of integer scales above 255 (those that need more
+ * than 8 bits; Fig. 4(a)).
+ * ---------------------------------------------------------------------- */
+EXPORT double orc_weight_mse_is_fs(const int8_t* codes, const float* fscale,
+                                   const int32_t* iscale, int alpha, int64_t K, int64_t N,
+                                   int64_t g, int32_t* max_iscale, int64_t* above_8bit)
+{
+    const int64_t G = K / g;
+    double sum = 0.0;
+    int32_t mx = 0;
+    int64_t wide = 0;
+    for (int64_t l = 0; l < G; ++l)
+        for (int64_t j = 0; j < N; ++j) {
+            const int32_t S = iscale[l * N + j];
+            if (S > mx) mx = S;
+            if (S > 255) ++wide;
+            const double d = (double)S / (double)alpha - (double)fscale[l * N + j];
+            double q2 = 0.0;
+            for (int64_t r = 0; r < g; ++r) {
+                const double q = (double)codes[(l * g + r) * N + j];
+                q2 += q * q;
+            }
+            sum += q2 * d * d;
+        }
+    if (max_iscale) *max_iscale = mx;
+    if (above_8bit) *above_8bit = wide;
+    return sum / ((double)K * (double)N);
+}
+
+/* ------------------------------------------------------------------------
  * Packed int4 layout ([EX] "data packing": two 4-bit codes per byte). The
  * index map is the one the library header declares; it is restated here
  * from that declaration, independently of the kernels:

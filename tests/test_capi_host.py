@@ -37,7 +37,7 @@ def test_status_strings(L):
     assert bgt.status_string(0) == "ok"
     for st in (-1, -2, -3, -4, -5, -6, -7, 1):
         assert "error" in bgt.status_string(st) or "warning" in bgt.status_string(st)
-    assert L.bgt_abi_version() == 100
+    assert L.bgt_abi_version() == 101
 
 
 def test_quantize_act_validation(L):
@@ -92,12 +92,41 @@ def test_gemm_is_validation(L):
     assert call(acc=MIS) == bgt.BGT_ERR_ALIGN
 
 
+def test_gemm_is_narrow_validation(L):
+    g = L.bgt_w4a8_gemm_is_narrow
+
+    def call(isc=FAKE, width=1, alpha=1024, M=16, N=64, K=256, y=FAKE):
+        return g(FAKE, FAKE, FAKE, isc, width, alpha, M, N, K, y, None, None)
+
+    assert call(isc=None) == bgt.BGT_ERR_NULL
+    for bad in (0, 3, 8, -1):
+        assert call(width=bad) == bgt.BGT_ERR_MODE
+    assert call(N=40) == bgt.BGT_ERR_SHAPE
+    assert call(alpha=1000) == bgt.BGT_ERR_ALPHA
+    assert call(isc=MIS) == bgt.BGT_ERR_ALIGN
+    assert call(isc=MIS, width=4) == bgt.BGT_ERR_ALIGN
+    # the int32 entry point shares the same checks
+    assert L.bgt_w4a8_gemm_is(FAKE, FAKE, FAKE, MIS, 1024, 16, 64, 256, FAKE, None, None) == bgt.BGT_ERR_ALIGN
+
+
+def test_narrow_iscale_validation(L):
+    n = L.bgt_narrow_iscale
+    assert n(None, 64, 1, FAKE, None) == bgt.BGT_ERR_NULL
+    assert n(FAKE, 64, 1, None, None) == bgt.BGT_ERR_NULL
+    assert n(FAKE, 64, 4, FAKE, None) == bgt.BGT_ERR_MODE      # int32 needs no narrowing
+    assert n(FAKE, 64, 3, FAKE, None) == bgt.BGT_ERR_MODE
+    assert n(FAKE, 0, 1, FAKE, None) == bgt.BGT_ERR_SHAPE
+    assert n(MIS, 64, 2, FAKE, None) == bgt.BGT_ERR_ALIGN
+    assert n(FAKE, 64, 2, MIS, None) == bgt.BGT_ERR_ALIGN
+
+
 def test_gemm_fs_validation(L):
     g = L.bgt_w4a8_gemm_fs
     assert g(FAKE, FAKE, FAKE, None, 16, 64, 256, FAKE, None) == bgt.BGT_ERR_NULL
     assert g(FAKE, FAKE, FAKE, FAKE, 16, 63, 256, FAKE, None) == bgt.BGT_ERR_SHAPE
     assert g(FAKE, FAKE, FAKE, FAKE, 16, 64, 100, FAKE, None) == bgt.BGT_ERR_SHAPE
     assert g(FAKE, FAKE, MIS, FAKE, 16, 64, 256, FAKE, None) == bgt.BGT_ERR_ALIGN
+    assert g(FAKE, FAKE, FAKE, MIS, 16, 64, 256, FAKE, None) == bgt.BGT_ERR_ALIGN   # fscale
 
 
 def test_w8a8_validation(L):

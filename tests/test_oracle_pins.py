@@ -240,6 +240,116 @@ def test_default_amplifier_and_iscale_width(orc):
     assert orc.integer_scales(ties, 1024).tolist() == [[1, 2, 3]]
 
 
+# ------------------------------------------- narrow integer scales, weight MSE
+
+@pytest.mark.parametrize("width,top", [(1, 255), (2, 65535)])
+def test_narrow_iscale_bounds_and_identity(orc, width, top):
+    # the element holds exactly [0, 2^(8 width) - 1]; stored values are unchanged
+    ok = np.array([[0, 1, top - 1, top]], np.int32)
+    out, bad = orc.narrow_iscale(ok, width)
+    assert bad == 0 and out.dtype == (np.uint8 if width == 1 else np.uint16)
+    assert out.astype(np.int64).tolist() == ok.astype(np.int64).tolist()
+    for v in (top + 1, -1, 2 ** 23 - 1):
+        out, bad = orc.narrow_iscale(np.array([[3, v, 5]], np.int32), width)
+        assert out is None and bad == 1
+    with pytest.raises(ValueError):
+        orc.narrow_iscale(ok, 3)
+
+
+def test_default_amplifier_scales_fit_8_bits_on_synthetic_layers(orc):
+    # the pages find the alpha = 2^10 scales of LLaMA-2-7B within 16 bits, most
+    # within 8; the synthetic N(0, 0.02) layers (with 0.1% x10 outliers) fit 8 bits
+    w = synth.weights(4, 1024, 512, std=0.02, outlier_prob=0.001, outlier_scale=10.0)
+    _, fs = orc.group_quant_int4(w, 128)
+    isc = orc.integer_scales(fs, 1024)
+    out, bad = orc.narrow_iscale(isc, 1)
+    assert bad == 0 and out.max() <= 255
+
+
+def _mse_case(orc, seed=12, K=512, N=64):
+    w = synth.weights(seed, K, N, std=0.02, outlier_prob=0.001, outlier_scale=10.0)
+    codes, fs = orc.group_quant_int4(w, 128)
+    return codes, fs
+
+
+def test_weight_mse_zero_when_scales_are_exact(orc):
+    # weights built so that s * alpha is an integer: both dequantizations agree exactly
+    K, N, alpha = 384, 16, 1024
+    g = synth.rng(21, 9)
+    m = g.integers(1, 200, size=(K // 128, N))
+    w = g.uniform(-1, 1, size=(K, N)).astype(np.float32)
+    for l in range(K // 128):
+        blk = w[128 * l:128 * (l + 1)]
+        blk /= np.abs(blk).max(axis=0)
+        blk *= (7.0 * m[l] / alpha).astype(np.float32)
+        blk[0] = (7.0 * m[l] / alpha).astype(np.float32)
+    codes, fs = orc.group_quant_int4(w, 128)
+    isc = orc.integer_scales(fs, alpha)
+    mse, mx, wide = orc.weight_mse_is_fs(codes, fs, isc, alpha)
+    assert mse == 0.0 and mx == m.max() and wide == 0
+
+
+@pytest.mark.parametrize("log2a", [4, 8, 10, 14])
+def test_weight_mse_rounding_bound(orc, log2a):
+    # |S/alpha - s| <= 1/(2 alpha), so MSE <= sum q^2 / (4 alpha^2 K N)
+    codes, fs = _mse_case(orc)
+    alpha = 1 << log2a
+    isc = orc.integer_scales(fs, alpha)
+    mse, _, _ = orc.weight_mse_is_fs(codes, fs, isc, alpha)
+    q2 = float((codes.astype(np.float64) ** 2).sum())
+    bound = q2 / (4.0 * alpha * alpha * codes.size)
+    assert 0.0 < mse <= bound * (1 + 1e-12)
+
+
+def test_weight_mse_scales_as_alpha_squared(orc):
+    # once alpha * s spans many integers the rounding errors are uniform on
+    # [-1/2, 1/2]: MSE -> E[q^2]/(12 alpha^2), a quarter per doubling of alpha
+    codes, fs = _mse_case(orc, K=1024, N=256)
+    q2 = float((codes.astype(np.float64) ** 2).mean())
+    for log2a in (14, 16, 18):
+        alpha = 1 << log2a
+        mse, _, _ = orc.weight_mse_is_fs(codes, fs, orc.integer_scales(fs, alpha), alpha)
+        assert mse * alpha * alpha == pytest.approx(q2 / 12.0, rel=0.1)
+
+
+def test_weight_mse_alpha_one_drops_small_scales(orc):
+    # alpha = 1 and every s < 1/2: every integer scale rounds to 0, so the
+    # integer-scale weights vanish and the MSE is the mean square of q*s
+    codes, fs = _mse_case(orc)
+    assert fs.max() < 0.5
+    isc = orc.integer_scales(fs, 1)
+    assert (isc == 0).all()
+    mse, mx, _ = orc.weight_mse_is_fs(codes, fs, isc, 1)
+    wfs = codes.astype(np.float64) * np.repeat(fs.astype(np.float64), 128, axis=0)
+    assert mx == 0
+    assert mse == pytest.approx(float((wfs ** 2).mean()), rel=1e-12)
+
+
+def test_weight_mse_reports_wide_scales(orc):
+    codes, fs = _mse_case(orc)
+    alpha = 1 << 14
+    isc = orc.integer_scales(fs, alpha)
+    _, mx, wide = orc.weight_mse_is_fs(codes, fs, isc, alpha)
+    assert mx == int(isc.max()) and wide == int((isc > 255).sum()) and wide > 0
+
+
+def test_scale_table_fixture_relations():
+    # the analysis table written from the oracle by tests/golden/make_scale_table.py:
+    # each searched amplifier is the smallest 2^n lifting the smallest scale to >= 1,
+    # the weight MSE falls as alpha grows (by ~16x per 4x once rounding is uniform),
+    # and at alpha = 2^10 every integer scale of these layers fits 8 bits
+    path = os.path.join(os.path.dirname(__file__), "golden", "scale_table_synthetic.txt")
+    rows = [ln.split("|") for ln in open(path, encoding="utf-8") if ln.strip() and not ln.startswith("#")]
+    assert len(rows) == 8
+    for r in rows:
+        smin, n, mx, wide = float(r[2]), int(r[3]), int(r[4]), int(r[5])
+        mse = [float(v) for v in r[6].split()]
+        assert smin * 2.0 ** n >= 1.0 > smin * 2.0 ** (n - 1)
+        assert all(a >= b for a, b in zip(mse, mse[1:]))
+        assert 12.0 < mse[-2] / mse[-1] < 20.0
+        assert wide == 0 and mx <= 255
+
+
 # -------------------------------------------------------------------- O3 IS GEMM
 
 def _tiny_case(seed, M, K, N, iscale_hi=300):
