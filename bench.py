@@ -18,6 +18,10 @@ algorithmic bytes of a W4A8 GEMM are N*K/2 (packed int4) + 4*G*N (integer
 scales) + M*K (int8 codes) + 4*M (token scales) + 4*M*N (fp32 output), and
 5*M*K + 4*M for the activation quantizer.
 
+Each M runs through the fused entry point bgt_w4a8_linear_is: one launch that
+quantizes and multiplies for M <= 4, the quantizer and the GEMM otherwise
+(--no-fused-quant: always the two calls).
+
 --iscale-bits 8 or 16 stores the integer scales as uint8 / uint16 (the same
 values, narrowed offline) and counts their bytes at that width.
 
@@ -206,19 +210,28 @@ def run_decode(args, torch, bgt, dev):
                 torch.empty(M, dtype=torch.float32, device=dev)) for M in Ms}
     ybuf = {M: torch.empty((M, N), dtype=torch.float32, device=dev) for M in Ms}
 
-    def step(k, events=None):
-        """Step k: quantizer + GEMM per M; the GEMMs of step k read weight copies
-        k*len(Ms) .. k*len(Ms)+len(Ms)-1 (mod R), so consecutive GEMMs never
-        share a copy."""
-        for i, M in enumerate(Ms):
-            q, s = qbuf[M]
+    def linear(M, packed, iscale):
+        """Per-token quantization of X then the integer-scale GEMM: one call of
+        the fused entry point (a single launch for M <= 4), or the quantizer and
+        the GEMM as two calls with --no-fused-quant."""
+        q, s = qbuf[M]
+        if args.fused_quant:
+            bgt.w4a8_linear_is(xs[M], packed, iscale, pw["alpha"], N, qx=q, sx=s, y=ybuf[M])
+        else:
             bgt.quantize_act(xs[M], q=q, scale=s)
+            bgt.w4a8_gemm_is_narrow(q, s, packed, iscale, pw["alpha"], N, y=ybuf[M])
+
+    def step(k, events=None):
+        """Step k: quantization + GEMM per M; the GEMMs of step k read weight
+        copies k*len(Ms) .. k*len(Ms)+len(Ms)-1 (mod R), so consecutive GEMMs
+        never share a copy."""
+        for i, M in enumerate(Ms):
             packed, iscale, _ = rot.get(k * len(Ms) + i)
             if events is not None:
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record()
-            bgt.w4a8_gemm_is_narrow(q, s, packed, iscale, pw["alpha"], N, y=ybuf[M])
+            linear(M, packed, iscale)
             if events is not None:
                 e1.record()
                 events.append((M, e0, e1))
@@ -238,16 +251,21 @@ def run_decode(args, torch, bgt, dev):
     # replays each step's graph exactly once
     ms_step = graph_steps(torch, step, args.steps, args.warmup) if args.launch == "graph" else eager_ms
 
-    # per-launch GEMM duration: back-to-back GEMM launches at one M, weight
-    # copies rotating as in the step
-    per_m = {}
+    # per-launch GEMM duration (and quantization + GEMM duration): back-to-back
+    # launches at one M, weight copies rotating as in the step
+    per_m, lin_m = {}, {}
     for M in Ms:
         q, s = qbuf[M]
 
         def launch(j, q=q, s=s, M=M):
             packed, iscale, _ = rot.get(j)
             bgt.w4a8_gemm_is_narrow(q, s, packed, iscale, pw["alpha"], N, y=ybuf[M])
+
+        def launch_lin(j, M=M):
+            packed, iscale, _ = rot.get(j)
+            linear(M, packed, iscale)
         per_m[M] = graph_launch_us(torch, launch, 2 * rot.R)
+        lin_m[M] = graph_launch_us(torch, launch_lin, 2 * rot.R)
 
     eager_per_m = {M: [] for M in Ms}
     for M, e0, e1 in eager_events:
@@ -260,7 +278,9 @@ def run_decode(args, torch, bgt, dev):
         sweep[str(M)] = {"gemm_us": round(us, 3), "gemm_GBps": round(b / us / 1e3, 1),
                          "gemm_TOPS": round(gemm_ops(M, N, K) / us / 1e6, 2),
                          "hbm_frac": round(b / us / 1e3 / HBM_PEAK_GBS, 4),
-                         "eager_gemm_us_median": round(float(np.median(eager_per_m[M])), 3),
+                         "quant_gemm_us": round(float(np.mean(lin_m[M])), 3),
+                         "quant_gemm_launches": 1 if args.fused_quant and bgt.w4a8_linear_fused(xs[M]) else 2,
+                         "eager_quant_gemm_us_median": round(float(np.median(eager_per_m[M])), 3),
                          "kernel": bgt.w4a8_kernel_name(M, N, K)}
     # dominant GEMM kernel: largest summed time over the step
     by_kernel = {}
@@ -287,6 +307,7 @@ def run_decode(args, torch, bgt, dev):
                                "alpha=1024, M in {1,4,16,64,256} per step",
                    "launch": "hip_graph" if args.launch == "graph" else "eager",
                    "iscale_storage": {4: "int32", 2: "uint16", 1: "uint8"}[sb],
+                   "quantization": "fused into the GEMM for M <= 4" if args.fused_quant else "separate launch",
                    "weight_buffers_rotated": rot.R},
         "eager": {"ms_per_step": round(eager_ms, 4),
                   "value": round(step_bytes / (eager_ms * 1e-3) / 1e9, 1)},
@@ -455,6 +476,9 @@ def main():
     ap.add_argument("--iscale-bits", type=int, default=32, choices=[8, 16, 32],
                     help="decode workload: integer scales stored as uint8 / uint16 / int32 "
                          "(same values; bytes counted at the stored width)")
+    ap.add_argument("--no-fused-quant", dest="fused_quant", action="store_false",
+                    help="decode workload: run the quantizer and the GEMM as two calls for "
+                         "every M (default: the fused entry point, one launch for M <= 4)")
     ap.add_argument("--launch", default="graph", choices=["graph", "eager"],
                     help="decode workload: replay each step from a HIP graph (default) or "
                          "issue every launch from Python")

@@ -37,7 +37,7 @@ GROUP = 128
 EXPORTED = (
     "bgt_quantize_act", "bgt_pack_weights_int4", "bgt_w4a8_gemm_is", "bgt_w4a8_gemm_fs",
     "bgt_w8a8_gemm_zp", "bgt_status_string", "bgt_abi_version", "bgt_w4a8_kernel_name",
-    "bgt_narrow_iscale", "bgt_w4a8_gemm_is_narrow",
+    "bgt_narrow_iscale", "bgt_w4a8_gemm_is_narrow", "bgt_w4a8_linear_is", "bgt_w4a8_linear_fused",
 )
 
 _lib = None
@@ -64,6 +64,8 @@ def lib():
         L.bgt_w4a8_gemm_fs.argtypes = [P, P, P, P, I64, I64, I64, P, P]
         L.bgt_narrow_iscale.argtypes = [P, I64, I, P, P]
         L.bgt_w4a8_gemm_is_narrow.argtypes = [P, P, P, P, I, I, I64, I64, I64, P, P, P]
+        L.bgt_w4a8_linear_is.argtypes = [P, I64, P, P, I, I, I64, I64, I64, P, P, P, P]
+        L.bgt_w4a8_linear_fused.argtypes = [I64, I64, P, I64]
         L.bgt_w8a8_gemm_zp.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, P, P, P]
         L.bgt_status_string.argtypes = [I]
         L.bgt_status_string.restype = ctypes.c_char_p
@@ -251,6 +253,41 @@ def w4a8_gemm_is_narrow(qx, sx, packed, iscale, alpha: int, N: int, y=None, acc_
                                        _ptr(acc_out), _stream(qx.device))
     _raise("bgt_w4a8_gemm_is_narrow", st)
     return y
+
+
+def w4a8_linear_is(x, packed, iscale, alpha: int, N: int, qx=None, sx=None, y=None):
+    """Per-token quantization of x (M x K float32) and the integer-scale GEMM.
+
+    One launch for M <= 4 on the decode path (see w4a8_linear_fused); returns
+    (y, qx, sx), the quantized activations included."""
+    torch = _torch()
+    if not isinstance(x, torch.Tensor) or x.dtype != torch.float32 or not x.is_cuda \
+            or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D float32 GPU tensor with unit column stride")
+    M, K = x.shape
+    widths = {torch.uint8: 1, torch.uint16: 2, torch.int32: 4}
+    if not isinstance(iscale, torch.Tensor) or iscale.dtype not in widths:
+        raise TypeError("iscale must be a uint8, uint16 or int32 tensor")
+    _check(packed, "packed", torch.uint8, (N * K // 2,))
+    _check(iscale, "iscale", iscale.dtype, (K // GROUP, N))
+    dev = x.device
+    qx = torch.empty((M, K), dtype=torch.int8, device=dev) if qx is None else qx
+    sx = torch.empty(M, dtype=torch.float32, device=dev) if sx is None else sx
+    y = torch.empty((M, N), dtype=torch.float32, device=dev) if y is None else y
+    _check(qx, "qx", torch.int8, (M, K))
+    _check(sx, "sx", torch.float32, (M,))
+    _check(y, "y", torch.float32, (M, N))
+    st = lib().bgt_w4a8_linear_is(_ptr(x), x.stride(0), _ptr(packed), _ptr(iscale),
+                                  widths[iscale.dtype], int(alpha), M, N, K, _ptr(qx), _ptr(sx),
+                                  _ptr(y), _stream(dev))
+    _raise("bgt_w4a8_linear_is", st)
+    return y, qx, sx
+
+
+def w4a8_linear_fused(x) -> bool:
+    """True when w4a8_linear_is runs as a single launch for this x."""
+    M, K = x.shape
+    return bool(lib().bgt_w4a8_linear_fused(M, K, _ptr(x), x.stride(0)))
 
 
 def w4a8_gemm_fs(qx, sx, packed, fscale, N: int, y=None):

@@ -41,7 +41,11 @@ int searched_alpha_log2(float smin) {
 
 extern "C" {
 
-int bgt_abi_version(void) { return 101; }
+int bgt_abi_version(void) { return 102; }
+
+int bgt_w4a8_linear_fused(int64_t M, int64_t K, const float* x, int64_t ldx) {
+  return bgt::w4a8_linear_fused(M, K, x, ldx) ? 1 : 0;
+}
 
 const char* bgt_w4a8_kernel_name(int64_t M, int64_t N, int64_t K, int float_scale) {
   if (check_gemm_shape(M, N, K, 65536) != BGT_OK) return "invalid shape";
@@ -133,6 +137,21 @@ int bgt_w4a8_gemm_is_narrow(const int8_t* qx, const float* sx, const uint8_t* pa
     return BGT_ERR_ALIGN;
   return hip_status(bgt::launch_w4a8(false, qx, sx, packed, iscale, width, nullptr, alpha, M, N,
                                      K, y, acc_out, static_cast<hipStream_t>(stream)));
+}
+
+int bgt_w4a8_linear_is(const float* x, int64_t ldx, const uint8_t* packed, const void* iscale,
+                       int width, int alpha, int64_t M, int64_t N, int64_t K, int8_t* qx,
+                       float* sx, float* y, void* stream) {
+  if (!x || !packed || !iscale || !qx || !sx || !y) return BGT_ERR_NULL;
+  if (width != 1 && width != 2 && width != 4) return BGT_ERR_MODE;
+  int st = check_gemm_shape(M, N, K, 65536);
+  if (st != BGT_OK) return st;
+  if (ldx < K) return BGT_ERR_SHAPE;
+  if (!pow2_alpha(alpha)) return BGT_ERR_ALPHA;
+  if (!aligned16(packed) || !aligned16(iscale) || !aligned16(qx) || !aligned16(y))
+    return BGT_ERR_ALIGN;
+  return hip_status(bgt::launch_w4a8_linear(x, ldx, packed, iscale, width, alpha, M, N, K, qx, sx,
+                                            y, static_cast<hipStream_t>(stream)));
 }
 
 int bgt_w4a8_gemm_fs(const int8_t* qx, const float* sx, const uint8_t* packed,

@@ -892,12 +892,13 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
 //      ascending fma chain).
 // Every load is a register load, so the compiler's wait counts stay exact.
 // =====================================================================
-template <bool FS, int W, int D, int G, int MR, typename ST>
+template <bool FS, int W, int D, int G, int MR, typename ST, bool FQ>
 __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
     const int8_t* __restrict__ qx, const float* __restrict__ sx,
     const uint4* __restrict__ packed, const ST* __restrict__ iscale,
     const float* __restrict__ fscale, float inv_alpha, int M, int N,
-    float* __restrict__ y, int32_t* __restrict__ acc_out) {
+    float* __restrict__ y, int32_t* __restrict__ acc_out,
+    const float* __restrict__ xf, int ldx, int8_t* __restrict__ q_out, float* __restrict__ s_out) {
   constexpr int CGM = MR == 1 ? 32 : 8;
   constexpr int CG = G < CGM ? G : CGM;              // groups per X chunk (<= 64 KiB)
   constexpr int NCH = G / CG;                        // chunks
@@ -910,6 +911,7 @@ __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
   constexpr int SCH = (SCT + W * 64 - 1) / (W * 64); // ... per thread
   static_assert(G % D == 0 && G % CG == 0 && CFR % W == 0, "shape of the pipeline");
   static_assert(SCW % SEL == 0, "scale staging");
+  static_assert(!FQ || (MR == 1 && NCH == 1 && !FS), "fused quantization: one row block, one chunk");
   constexpr int NBUF = NCH > 1 ? 2 : 1;
   __shared__ __align__(16) int8_t sA[NBUF * CFR * 1024];
   __shared__ __align__(16) SL sS[G * SCW];           // [group][column of the workgroup]
@@ -939,7 +941,22 @@ __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
     for (int i = 0; i < FPW; ++i)
       *reinterpret_cast<v4i*>(sA + (buf * CFR + wave + W * i) * 1024 + lane * 16) = xa[i];
   };
-  load_chunk(0);
+  // fused quantization (FQ, M <= 4): the fp32 rows, each thread XV float4 of
+  // every row, requested before the scales and the weights
+  constexpr int XV = FQ ? K / 4 / (W * 64) : 1;
+  static_assert(!FQ || XV * W * 64 * 4 == K, "row split");
+  float4 xv[4][XV];
+  if constexpr (FQ) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int v = 0; v < XV; ++v)
+        if (i < M)
+          xv[i][v] = *reinterpret_cast<const float4*>(xf + (int64_t)i * ldx +
+                                                      4 * (threadIdx.x + W * 64 * v));
+  } else {
+    load_chunk(0);
+  }
   // ---- the workgroup's scales for all groups, 16-byte chunks of SEL
   // elements (columns past N clamped; chunk q lands at byte 16q of sS)
   const SL* scl = FS ? reinterpret_cast<const SL*>(fscale) : reinterpret_cast<const SL*>(iscale);
@@ -956,10 +973,94 @@ __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
   uint4 wb[D];
 #pragma unroll
   for (int j = 0; j < D; ++j) wb[j] = load_u4_nt(wsrc + (int64_t)j * 64);
-  // token scales of the (at most 64) rows, read back from LDS at the end
-  const float sxi = threadIdx.x < 16 * MR ? sx[threadIdx.x < M ? threadIdx.x : M - 1] : 0.0f;
-  store_chunk(0);
-  if (threadIdx.x < 16 * MR) sX[threadIdx.x] = sxi;
+  if constexpr (FQ) {
+    // ---- per-token quantization of the rows, as the quantizer computes it:
+    // a = max|x|, s = a / 127, q = clamp(round(x / s), -127, 127) (s = 0 -> 0).
+    // x / s is Markstein's corrected quotient (P. Markstein, IBM J. Res. Dev.
+    // 1990): with r = 1/s correctly rounded, q0 = x*r, e = fma(-q0, s, x)
+    // (exact), fma(e, r, q0) is x / s correctly rounded while s, r and the
+    // residual stay normal; rows with an extreme scale take the division.
+    __shared__ float sAm[4 * W];
+    float am[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      am[i] = 0.0f;
+      if (i < M)
+#pragma unroll
+        for (int v = 0; v < XV; ++v)
+          am[i] = fmaxf(am[i], fmaxf(fmaxf(fabsf(xv[i][v].x), fabsf(xv[i][v].y)),
+                                     fmaxf(fabsf(xv[i][v].z), fabsf(xv[i][v].w))));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)                 // the four rows' butterflies side by side
+#pragma unroll
+      for (int i = 0; i < 4; ++i) am[i] = fmaxf(am[i], __shfl_xor(am[i], o, kWave));
+    if (lane == 0)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sAm[i * W + wave] = am[i];
+    // rows M..15 of the fragment block are zero codes
+#pragma unroll
+    for (int i = 0; i < FPW; ++i)
+      if (c >= M) *reinterpret_cast<v4i*>(sA + (wave + W * i) * 1024 + lane * 16) = v4i{0, 0, 0, 0};
+    wait_lds0();
+    lds_barrier();
+    // codes of one float4: MODE 0 all zero (s = 0), 1 corrected product, 2 division
+    auto quant4 = [&](const float4& x, float sc, float r, auto mode) -> uint32_t {
+      constexpr int MODE = decltype(mode)::value;
+      if (MODE == 0) return 0u;
+      auto one = [&](float e) -> uint32_t {
+        float q;
+        if (MODE == 1) {
+          const float q0 = e * r;
+          q = __builtin_fmaf(__builtin_fmaf(-q0, sc, e), r, q0);
+        } else {
+          q = e / sc;
+        }
+        return (uint32_t)clamp_int((int)round_away(q), -127, 127) & 0xFFu;
+      };
+      return one(x.x) | (one(x.y) << 8) | (one(x.z) << 16) | (one(x.w) << 24);
+    };
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (i < M) {
+        float a = sAm[i * W];
+#pragma unroll
+        for (int w = 1; w < W; ++w) a = fmaxf(a, sAm[i * W + w]);
+        const float sc = a / 127.0f;
+        const float r = 1.0f / sc;
+        if (threadIdx.x == i) {
+          sX[i] = sc;
+          if (blockIdx.x == 0) s_out[i] = sc;
+        }
+        uint32_t word[XV];
+        // row-uniform choice (the corrected product needs s, 1/s and the
+        // residual to stay normal)
+        if (sc == 0.0f) {
+#pragma unroll
+          for (int v = 0; v < XV; ++v) word[v] = quant4(xv[i][v], sc, r, IC<0>{});
+        } else if (sc >= 0x1.0p-100f && sc <= 0x1.0p100f) {
+#pragma unroll
+          for (int v = 0; v < XV; ++v) word[v] = quant4(xv[i][v], sc, r, IC<1>{});
+        } else {
+#pragma unroll
+          for (int v = 0; v < XV; ++v) word[v] = quant4(xv[i][v], sc, r, IC<2>{});
+        }
+#pragma unroll
+        for (int v = 0; v < XV; ++v) {
+          const int k = 4 * (threadIdx.x + W * 64 * v);
+          // fragment (group g, half h) lane 16*(k%64/16) + row, byte k%16
+          const int g = k / 128, h = (k % 128) / 64, sq = (k % 64) / 16;
+          *reinterpret_cast<uint32_t*>(sA + (g * 2 + h) * 1024 + (16 * sq + i) * 16 + k % 16) = word[v];
+          if (blockIdx.x == 0) *reinterpret_cast<uint32_t*>(q_out + (int64_t)i * K + k) = word[v];
+        }
+      }
+    if (threadIdx.x >= M && threadIdx.x < 16) sX[threadIdx.x] = 0.0f;
+  } else {
+    // token scales of the (at most 64) rows, read back from LDS at the end
+    const float sxi = threadIdx.x < 16 * MR ? sx[threadIdx.x < M ? threadIdx.x : M - 1] : 0.0f;
+    store_chunk(0);
+    if (threadIdx.x < 16 * MR) sX[threadIdx.x] = sxi;
+  }
 #pragma unroll
   for (int u = 0; u < SCH; ++u) {
     const int q = threadIdx.x + W * 64 * u;
@@ -1185,15 +1286,18 @@ static void launch_decode(int mr, dim3 grid, dim3 block, hipStream_t stream, con
                           const float* sx, const uint4* pk, const ST* iscale,
                           const float* fscale, float inv_alpha, int M, int N, float* y,
                           int32_t* acc_out) {
+  const float* nx = nullptr;
+  int8_t* nq = nullptr;
+  float* ns = nullptr;
   switch (mr) {
-    case 1: hipLaunchKernelGGL((k_w4a8_decode<FS, kDecodeW, decode_depth(1), G, 1, ST>), grid, block, 0, stream,
-                               qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out); break;
-    case 2: hipLaunchKernelGGL((k_w4a8_decode<FS, kDecodeW, decode_depth(2), G, 2, ST>), grid, block, 0, stream,
-                               qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out); break;
-    case 3: hipLaunchKernelGGL((k_w4a8_decode<FS, kDecodeW, decode_depth(3), G, 3, ST>), grid, block, 0, stream,
-                               qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out); break;
-    default: hipLaunchKernelGGL((k_w4a8_decode<FS, kDecodeW, decode_depth(4), G, 4, ST>), grid, block, 0, stream,
-                                qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out); break;
+    case 1: hipLaunchKernelGGL((k_w4a8_decode<FS, kDecodeW, decode_depth(1), G, 1, ST, false>), grid, block, 0, stream,
+                               qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out, nx, 0, nq, ns); break;
+    case 2: hipLaunchKernelGGL((k_w4a8_decode<FS, kDecodeW, decode_depth(2), G, 2, ST, false>), grid, block, 0, stream,
+                               qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out, nx, 0, nq, ns); break;
+    case 3: hipLaunchKernelGGL((k_w4a8_decode<FS, kDecodeW, decode_depth(3), G, 3, ST, false>), grid, block, 0, stream,
+                               qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out, nx, 0, nq, ns); break;
+    default: hipLaunchKernelGGL((k_w4a8_decode<FS, kDecodeW, decode_depth(4), G, 4, ST, false>), grid, block, 0, stream,
+                                qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out, nx, 0, nq, ns); break;
   }
 }
 
@@ -1241,6 +1345,55 @@ hipError_t launch_w4a8(bool float_scale, const int8_t* qx, const float* sx, cons
   else
     launch_w4a8_t<false>(qx, sx, packed, static_cast<const uint8_t*>(iscale), nullptr, inv_alpha,
                          M, N, K, y, acc_out, stream);
+  return hipGetLastError();
+}
+
+// Quantize + GEMM in one launch for M <= 4 on the decode path (the decode
+// kernel quantizes the fp32 rows itself); otherwise the quantizer and the GEMM.
+template <typename ST>
+static void launch_linear_fused(const float* x, int ldx, const uint8_t* packed, const ST* iscale,
+                                float inv_alpha, int M, int N, int K, int8_t* q_out,
+                                float* s_out, float* y, hipStream_t stream) {
+  const int T = N / 16;
+  const dim3 grid((T + kDecodeW - 1) / kDecodeW), block(kDecodeW * kWave);
+  const uint4* pk = reinterpret_cast<const uint4*>(packed);
+  if (K / kGroup == 32)
+    hipLaunchKernelGGL((k_w4a8_decode<false, kDecodeW, decode_depth(1), 32, 1, ST, true>), grid,
+                       block, 0, stream, nullptr, nullptr, pk, iscale, nullptr, inv_alpha, M, N,
+                       y, nullptr, x, ldx, q_out, s_out);
+  else
+    hipLaunchKernelGGL((k_w4a8_decode<false, kDecodeW, decode_depth(1), 16, 1, ST, true>), grid,
+                       block, 0, stream, nullptr, nullptr, pk, iscale, nullptr, inv_alpha, M, N,
+                       y, nullptr, x, ldx, q_out, s_out);
+}
+
+bool w4a8_linear_fused(int64_t M, int64_t K, const float* x, int64_t ldx) {
+  const int64_t G = K / kGroup;
+  return M <= 4 && (G == 16 || G == 32) && (reinterpret_cast<uintptr_t>(x) & 15u) == 0 &&
+         ldx % 4 == 0 && ldx <= (1ll << 28);
+}
+
+hipError_t launch_w4a8_linear(const float* x, int64_t ldx, const uint8_t* packed,
+                              const void* iscale, int iscale_bytes, int alpha, int64_t M64,
+                              int64_t N64, int64_t K64, int8_t* q_out, float* s_out, float* y,
+                              hipStream_t stream) {
+  if (!w4a8_linear_fused(M64, K64, x, ldx)) {
+    hipError_t e = launch_quant_rows(x, M64, K64, ldx, false, q_out, s_out, nullptr, nullptr, stream);
+    if (e != hipSuccess) return e;
+    return launch_w4a8(false, q_out, s_out, packed, iscale, iscale_bytes, nullptr, alpha, M64, N64,
+                       K64, y, nullptr, stream);
+  }
+  const int M = (int)M64, N = (int)N64, K = (int)K64, ld = (int)ldx;
+  const float inv_alpha = 1.0f / (float)alpha;   // exact: alpha = 2^n
+  if (iscale_bytes == 4)
+    launch_linear_fused(x, ld, packed, static_cast<const int32_t*>(iscale), inv_alpha, M, N, K,
+                        q_out, s_out, y, stream);
+  else if (iscale_bytes == 2)
+    launch_linear_fused(x, ld, packed, static_cast<const uint16_t*>(iscale), inv_alpha, M, N, K,
+                        q_out, s_out, y, stream);
+  else
+    launch_linear_fused(x, ld, packed, static_cast<const uint8_t*>(iscale), inv_alpha, M, N, K,
+                        q_out, s_out, y, stream);
   return hipGetLastError();
 }
 

@@ -26,6 +26,16 @@ hipError_t launch_w4a8(bool float_scale, const int8_t* qx, const float* sx, cons
                        int64_t M, int64_t N, int64_t K, float* y, int32_t* acc_out,
                        hipStream_t stream);
 
+// per-token quantization of x (M x K fp32, leading dimension ldx) into q_out /
+// s_out, then the integer-scale GEMM into y; one launch when
+// w4a8_linear_fused() holds (M <= 4, K/128 in {16, 32}, x 16-byte aligned,
+// ldx % 4 == 0), else the quantizer and the GEMM.
+bool w4a8_linear_fused(int64_t M, int64_t K, const float* x, int64_t ldx);
+hipError_t launch_w4a8_linear(const float* x, int64_t ldx, const uint8_t* packed,
+                              const void* iscale, int iscale_bytes, int alpha, int64_t M,
+                              int64_t N, int64_t K, int8_t* q_out, float* s_out, float* y,
+                              hipStream_t stream);
+
 // narrow (K/128) x N integer scales to 2-byte or 1-byte elements (values must fit)
 hipError_t launch_narrow_scales(const int32_t* in, int64_t count, int out_bytes, void* out,
                                 hipStream_t stream);

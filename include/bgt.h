@@ -167,6 +167,31 @@ int bgt_w4a8_gemm_is_narrow(const int8_t* qx, const float* sx, const uint8_t* pa
                             int64_t K, float* y, int32_t* acc_out, void* stream);
 
 /*
+ * bgt_w4a8_linear_is -- the whole decode-time linear layer from fp32
+ * activations: per-token quantization of x exactly as bgt_quantize_act SYM
+ * computes it (codes into qx, scales into sx), then bgt_w4a8_gemm_is_narrow
+ * on those codes. For M <= 4 with K/128 = 16 or 32, x 16-byte aligned and
+ * ldx % 4 == 0 this is one launch: every workgroup of the decode kernel
+ * quantizes the rows itself while its weight stream is in flight, so the
+ * separate quantizer launch disappears (the fusion of the quantization into
+ * the GEMM that [QB] §2.4.1 dynamic quantization invites); otherwise it is the
+ * quantizer followed by the GEMM. qx, sx and y are bit-identical either way.
+ *
+ *   x       M x K float32 (finite), leading dimension ldx >= K (elements).
+ *   packed, iscale, width, alpha: as bgt_w4a8_gemm_is_narrow.
+ *   qx      M x K int8 (dense), sx [M] float32: written (the quantized activations).
+ *   y       M x N float32.
+ * Requirements: those of bgt_w4a8_gemm_is_narrow; qx 16-byte aligned.
+ */
+int bgt_w4a8_linear_is(const float* x, int64_t ldx, const uint8_t* packed, const void* iscale,
+                       int width, int alpha, int64_t M, int64_t N, int64_t K, int8_t* qx,
+                       float* sx, float* y, void* stream);
+
+/* Diagnostics: 1 when bgt_w4a8_linear_is runs as one launch for these
+ * arguments (M, K, x, ldx), 0 when it runs the quantizer and the GEMM. */
+int bgt_w4a8_linear_fused(int64_t M, int64_t K, const float* x, int64_t ldx);
+
+/*
  * bgt_w4a8_gemm_fs -- the float-scale control ([IS] 方法 Fig. 3(b)): every
  * group's integer result is converted to float and scaled by its float scale,
  * groups in ascending order, one fused multiply-add each:
@@ -202,7 +227,7 @@ int bgt_w8a8_gemm_zp(const uint8_t* qx, const float* sx, const int32_t* zx,
 const char* bgt_status_string(int status);
 
 /* ABI version of this header (major*100 + minor): 101 adds the narrow
- * integer-scale entry points. */
+ * integer-scale entry points, 102 the fused linear layer. */
 int bgt_abi_version(void);
 
 /* Diagnostics: name of the GEMM kernel that bgt_w4a8_gemm_is (float_scale = 0)

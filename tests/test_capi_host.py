@@ -37,7 +37,7 @@ def test_status_strings(L):
     assert bgt.status_string(0) == "ok"
     for st in (-1, -2, -3, -4, -5, -6, -7, 1):
         assert "error" in bgt.status_string(st) or "warning" in bgt.status_string(st)
-    assert L.bgt_abi_version() == 101
+    assert L.bgt_abi_version() == 102
 
 
 def test_quantize_act_validation(L):
@@ -107,6 +107,30 @@ def test_gemm_is_narrow_validation(L):
     assert call(isc=MIS, width=4) == bgt.BGT_ERR_ALIGN
     # the int32 entry point shares the same checks
     assert L.bgt_w4a8_gemm_is(FAKE, FAKE, FAKE, MIS, 1024, 16, 64, 256, FAKE, None, None) == bgt.BGT_ERR_ALIGN
+
+
+def test_linear_is_validation(L):
+    g = L.bgt_w4a8_linear_is
+
+    def call(x=FAKE, ldx=256, isc=FAKE, width=4, alpha=1024, M=4, N=64, K=256, qx=FAKE, sx=FAKE, y=FAKE):
+        return g(x, ldx, FAKE, isc, width, alpha, M, N, K, qx, sx, y, None)
+
+    assert call(x=None) == bgt.BGT_ERR_NULL
+    assert call(qx=None) == bgt.BGT_ERR_NULL
+    assert call(sx=None) == bgt.BGT_ERR_NULL
+    assert call(width=3) == bgt.BGT_ERR_MODE
+    assert call(ldx=255) == bgt.BGT_ERR_SHAPE
+    assert call(K=200, ldx=300) == bgt.BGT_ERR_SHAPE
+    assert call(alpha=12) == bgt.BGT_ERR_ALPHA
+    assert call(qx=MIS) == bgt.BGT_ERR_ALIGN
+    assert call(isc=MIS) == bgt.BGT_ERR_ALIGN
+    f = L.bgt_w4a8_linear_fused
+    assert f(4, 4096, FAKE, 4096) == 1
+    assert f(1, 2048, FAKE, 2048) == 1
+    assert f(5, 4096, FAKE, 4096) == 0          # more than 4 rows
+    assert f(4, 1152, FAKE, 1152) == 0          # not 16 or 32 groups
+    assert f(4, 4096, MIS, 4096) == 0           # x not 16-byte aligned
+    assert f(4, 4096, FAKE, 4097) == 0          # row stride not a multiple of 4
 
 
 def test_narrow_iscale_validation(L):
