@@ -7,7 +7,8 @@ followed by the integer-scale W4A8 GEMM. Weights are packed once before
 timing (the offline step) and then replicated into R buffers whose total
 exceeds twice the 256 MB Infinity Cache; consecutive GEMMs read different
 buffers, so weight bytes come from HBM. Each timed step is replayed from a
-HIP graph captured once per step, the way a serving loop issues a decode
+HIP graph (all K timed steps captured into one graph, replayed once; the
+warm-up steps into another), the way a serving loop replays a captured decode
 step; the same steps run first with every launch issued from Python, and that
 rate is reported alongside ("eager"; --launch eager makes it the reported
 one). Per-launch GEMM durations come from a graph of 2R back-to-back GEMM
@@ -74,7 +75,7 @@ TRAFFIC = {("k_w4a8_decode<IS>", 1): 48166887,
            ("k_w4a8_decode<IS>", 64): 55828244,
            ("k_w4a8_prefill<4,2,2,2,IS>", 256): 79138687,
            ("k_w4a8_prefill<4,2,2,2,IS>", 4096): 922106797,
-           ("k_gemm_tiled<1,1,ZP>", 256): 29524652}
+           ("k_w8a8_zp<9,32>", 256): 29524652}
 
 
 def measured_traffic(kernel, Ms):
@@ -150,26 +151,28 @@ class Rotor:
 
 
 def graph_steps(torch, step, steps, warmup):
-    """Capture step(k) for k < steps into one HIP graph each, replay `warmup`
-    of them untimed, then replay every graph once; returns ms per step."""
+    """Capture step(k) for k < steps into one HIP graph (and `warmup` steps
+    into another), replay the warm-up graph untimed, then time one replay of
+    the K-step graph; returns ms per step. One graph for the whole timed region
+    keeps host-side launch cost out of short steps."""
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
         step(0)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    graphs = []
-    for k in range(steps):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
+    g_warm = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_warm):
+        for k in range(max(1, warmup)):
             step(k)
-        graphs.append(g)
-    for k in range(warmup):
-        graphs[k % steps].replay()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for k in range(steps):
+            step(k)
+    g_warm.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for g in graphs:
-        g.replay()
+    g.replay()
     torch.cuda.synchronize()
     return (time.perf_counter() - t0) * 1e3 / steps
 
@@ -429,8 +432,8 @@ def run_w8a8(args, torch, bgt, dev):
                   "gemm_us_median": round(eager_us, 3)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic("k_gemm_tiled<1,1,ZP>", [M]),
-                     "kernel": "k_gemm_tiled<1,1,ZP>", "launch_M": [M], "avg_launch_us": round(avg, 3),
+                     "traffic": measured_traffic("k_w8a8_zp<9,32>", [M]),
+                     "kernel": "k_w8a8_zp<9,32>", "launch_M": [M], "avg_launch_us": round(avg, 3),
                      "bytes_per_launch": gb},
         "sweep": {"gemm_us": round(avg, 3), "gemm_TOPS": round(2 * M * N * K / avg / 1e6, 2)},
     }, (x, w)

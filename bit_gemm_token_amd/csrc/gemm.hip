@@ -163,213 +163,6 @@ __global__ __launch_bounds__(kWave * KS) void k_w4a8_skinny(
 }
 
 // =====================================================================
-// Tiled kernel (larger M): a BM x BN output tile per 256-thread workgroup,
-// 2 x 2 waves, each wave TM x TN blocks of 32 x 32. One K step is one group
-// of 128. A (int8 rows) and B are staged in LDS as [row or column][128 bytes]
-// with a 16-byte pad (conflict-free 16-byte reads of 8 consecutive lanes).
-// The next group's A and B are loaded into registers while the current one
-// is multiplied. For W4, B is unpacked once per workgroup into true int8 in
-// LDS; for the W8A8 control the uint8 codes of both operands are re-centred
-// by 128 (x ^ 0x80) so the signed MFMA sees the same differences q - z.
-// =====================================================================
-enum class Epi { IS, FS, ZP };
-
-constexpr int kLdsRow = 144;   // 128 bytes of K + 16 pad
-
-template <int TM, int TN, Epi E>
-__global__ __launch_bounds__(256, 2) void k_gemm_tiled(
-    const uint8_t* __restrict__ xa,          // A codes: M x K (int8 for W4, uint8 for ZP)
-    const float* __restrict__ sx,
-    const uint8_t* __restrict__ wb,          // W4: packed layout; ZP: qw N x K uint8
-    const int32_t* __restrict__ iscale, const float* __restrict__ fscale,
-    const int32_t* __restrict__ zx, const int32_t* __restrict__ rowsum_x,
-    const float* __restrict__ sw, const int32_t* __restrict__ zw,
-    const int32_t* __restrict__ colsum_w, float inv_alpha, int M, int N, int K,
-    float* __restrict__ y, int32_t* __restrict__ acc_out) {
-  constexpr int BM = 2 * TM * 32, BN = 2 * TN * 32;
-  constexpr bool W4 = (E != Epi::ZP);
-  constexpr int A_CH = BM * 8 / 256;                       // 16-byte chunks per thread
-  constexpr int B_CH = W4 ? (BN * 4 / 256) : (BN * 8 / 256);
-  static_assert(A_CH >= 1 && B_CH >= 1, "tile too small for 256 threads");
-  __shared__ __align__(16) uint8_t As[BM * kLdsRow];
-  __shared__ __align__(16) uint8_t Bs[BN * kLdsRow];
-
-  const int G = K / kGroup;
-  const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-  const int wm = wave / 2, wn = wave % 2;
-  const int ntiles = N / 16;
-
-  uint4 ra[A_CH], rbuf[B_CH];
-  auto load_group = [&](int l) {
-#pragma unroll
-    for (int u = 0; u < A_CH; ++u) {
-      const int q = tid + 256 * u, row = q / 8, k16 = q % 8;
-      const int gi = m0 + row;
-      const uint4* src = reinterpret_cast<const uint4*>(
-          xa + (int64_t)(gi < M ? gi : M - 1) * K + (int64_t)l * kGroup + 16 * k16);
-      ra[u] = (gi < M) ? *src : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < B_CH; ++u) {
-      const int q = tid + 256 * u;
-      if (W4) {
-        const int tl = q / 64, lb = q % 64, tg = n0 / 16 + tl;
-        const uint4* src = reinterpret_cast<const uint4*>(wb) +
-                           ((int64_t)(tg < ntiles ? tg : ntiles - 1) * G + l) * 64 + lb;
-        rbuf[u] = (tg < ntiles) ? load_u4_nt(src) : make_uint4(0, 0, 0, 0);
-      } else {
-        const int col = q / 8, k16 = q % 8, gj = n0 + col;
-        const uint4* src = reinterpret_cast<const uint4*>(
-            wb + (int64_t)(gj < N ? gj : N - 1) * K + (int64_t)l * kGroup + 16 * k16);
-        rbuf[u] = (gj < N) ? *src : make_uint4(0x80808080u, 0x80808080u, 0x80808080u, 0x80808080u);
-      }
-    }
-  };
-  auto store_group = [&]() {
-#pragma unroll
-    for (int u = 0; u < A_CH; ++u) {
-      const int q = tid + 256 * u, row = q / 8, k16 = q % 8;
-      uint4 v = ra[u];
-      if (!W4) { v.x ^= 0x80808080u; v.y ^= 0x80808080u; v.z ^= 0x80808080u; v.w ^= 0x80808080u; }
-      *reinterpret_cast<uint4*>(As + row * kLdsRow + 16 * k16) = v;
-    }
-#pragma unroll
-    for (int u = 0; u < B_CH; ++u) {
-      const int q = tid + 256 * u;
-      if (W4) {
-        const int tl = q / 64, lb = q % 64, s = lb / 16, cc = lb % 16;
-        uint32_t l0, h0, l1, h1, l2, h2, l3, h3;
-        unpack_i8(rbuf[u].x, l0, h0);
-        unpack_i8(rbuf[u].y, l1, h1);
-        unpack_i8(rbuf[u].z, l2, h2);
-        unpack_i8(rbuf[u].w, l3, h3);
-        uint8_t* dst = Bs + (tl * 16 + cc) * kLdsRow + 16 * s;
-        *reinterpret_cast<uint4*>(dst) = make_uint4(l0, h0, l1, h1);        // k = 16s + 0..15
-        *reinterpret_cast<uint4*>(dst + 64) = make_uint4(l2, h2, l3, h3);   // k = 64 + 16s + 0..15
-      } else {
-        const int col = q / 8, k16 = q % 8;
-        uint4 v = rbuf[u];
-        v.x ^= 0x80808080u; v.y ^= 0x80808080u; v.z ^= 0x80808080u; v.w ^= 0x80808080u;
-        *reinterpret_cast<uint4*>(Bs + col * kLdsRow + 16 * k16) = v;
-      }
-    }
-  };
-
-  // per-lane accumulators
-  int acc[TM][TN][16];
-  float facc[TM][TN][16];
-#pragma unroll
-  for (int a = 0; a < TM; ++a)
-#pragma unroll
-    for (int b = 0; b < TN; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) { acc[a][b][r] = 0; facc[a][b][r] = 0.0f; }
-
-  const int lr = lane % 32, hf = lane / 32;
-  int colj[TN];
-#pragma unroll
-  for (int b = 0; b < TN; ++b) colj[b] = n0 + wn * (TN * 32) + b * 32 + lr;
-
-  int isc[TN], iscn[TN];
-  float fsc[TN], fscn[TN];
-  auto load_scales = [&](int l, int* is, float* fs) {
-#pragma unroll
-    for (int b = 0; b < TN; ++b) {
-      const int jj = colj[b] < N ? colj[b] : N - 1;
-      if (E == Epi::IS) is[b] = iscale[(int64_t)l * N + jj];
-      if (E == Epi::FS) fs[b] = fscale[(int64_t)l * N + jj];
-    }
-  };
-
-  load_group(0);
-  if (E != Epi::ZP) load_scales(0, isc, fsc);
-  for (int l = 0; l < G; ++l) {
-    __syncthreads();
-    store_group();
-    __syncthreads();
-    if (l + 1 < G) {
-      load_group(l + 1);
-      if (E != Epi::ZP) load_scales(l + 1, iscn, fscn);
-    }
-    v16i p[TM][TN];
-#pragma unroll
-    for (int a = 0; a < TM; ++a)
-#pragma unroll
-      for (int b = 0; b < TN; ++b)
-        if (E == Epi::ZP) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) p[a][b][r] = acc[a][b][r];
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) p[a][b][r] = 0;
-        }
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      v4i av[TM], bv[TN];
-#pragma unroll
-      for (int a = 0; a < TM; ++a)
-        av[a] = *reinterpret_cast<const v4i*>(As + (wm * TM * 32 + a * 32 + lr) * kLdsRow + 64 * hf + 16 * m);
-#pragma unroll
-      for (int b = 0; b < TN; ++b)
-        bv[b] = *reinterpret_cast<const v4i*>(Bs + (wn * TN * 32 + b * 32 + lr) * kLdsRow + 64 * hf + 16 * m);
-#pragma unroll
-      for (int a = 0; a < TM; ++a)
-#pragma unroll
-        for (int b = 0; b < TN; ++b)
-          p[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[a], bv[b], p[a][b], 0, 0, 0);
-    }
-#pragma unroll
-    for (int a = 0; a < TM; ++a)
-#pragma unroll
-      for (int b = 0; b < TN; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if (E == Epi::IS) acc[a][b][r] = mad24(p[a][b][r], isc[b], acc[a][b][r]);
-          else if (E == Epi::FS) facc[a][b][r] = __builtin_fmaf((float)p[a][b][r], fsc[b], facc[a][b][r]);
-          else acc[a][b][r] = p[a][b][r];
-        }
-    if (E != Epi::ZP) {
-#pragma unroll
-      for (int b = 0; b < TN; ++b) { isc[b] = iscn[b]; fsc[b] = fscn[b]; }
-    }
-  }
-
-  // epilogue: one conversion per output
-#pragma unroll
-  for (int a = 0; a < TM; ++a)
-#pragma unroll
-    for (int b = 0; b < TN; ++b) {
-      const int j = colj[b];
-      if (j >= N) continue;
-      int32_t zwj = 0, cwj = 0;
-      float swj = 0.0f;
-      if (E == Epi::ZP) { zwj = zw[j] - 128; cwj = colsum_w[j] - 128 * K; swj = sw[j]; }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = m0 + wm * (TM * 32) + a * 32 + 8 * (r / 4) + 4 * hf + (r % 4);
-        if (i >= M) continue;
-        const int64_t o = (int64_t)i * N + j;
-        if (E == Epi::IS) {
-          const float t0 = (float)acc[a][b][r] * sx[i];
-          y[o] = t0 * inv_alpha;
-          if (acc_out) acc_out[o] = acc[a][b][r];
-        } else if (E == Epi::FS) {
-          y[o] = facc[a][b][r] * sx[i];
-        } else {
-          // acc = sum (qw-128)(qx-128); expand (qw - zw)(qx - zx) with the re-centred
-          // codes and zero points (same differences), all exact mod 2^32
-          const int32_t zxi = zx[i] - 128, rxi = rowsum_x[i] - 128 * K;
-          const int32_t A = acc[a][b][r] - zwj * rxi - zxi * cwj + K * zwj * zxi;
-          const float sc = sx[i] * swj;
-          y[o] = (float)A * sc;
-          if (acc_out) acc_out[o] = A;
-        }
-      }
-    }
-}
-
-// =====================================================================
 // Streaming kernel (small M, the memory-bound decode regime).
 // Persistent workgroups of KS loader waves plus one finisher wave.
 //   Loader wave w owns groups [w*GPW, (w+1)*GPW) for the whole launch and
@@ -873,6 +666,191 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
         if (acc_out) acc_out[o] = acc[k][r];
       }
     }
+  }
+}
+
+// =====================================================================
+// Asymmetric W8A8 control through the zero-point expansion: 64 x 64 output
+// tiles, 8 waves. Every load is an LDS copy (global_load_lds) of 1 KiB
+// blocks (8 rows x 128 k, 16-byte chunks XOR-swizzled by (row/2) % 8 so the
+// 32 x 32 x 32 fragment reads are conflict-free); nine copy stages of 128 k
+// (A and B rows), eight in flight, each its own array so the compiler's wait
+// counts stay per stage. Waves 0-3 and 4-7 take the two 64-k halves of a
+// stage on the same 2 x 2 arrangement of 32 x 32 blocks; the halves meet
+// once through LDS before the epilogue. uint8 codes enter the int8 MFMA
+// re-centred by 128 (xor 0x80), and the epilogue expands with the re-centred
+// zero points and row sums (the same differences), exact mod 2^32.
+// =====================================================================
+constexpr int kW8Waves = 8;                        // waves per W8A8 workgroup
+
+template <int NST, int GC, int NW>
+__global__ __launch_bounds__(NW * 64) void k_w8a8_zp(
+    const uint8_t* __restrict__ qx, const float* __restrict__ sx, const int32_t* __restrict__ zx,
+    const int32_t* __restrict__ rowsum_x, const uint8_t* __restrict__ qw,
+    const float* __restrict__ sw, const int32_t* __restrict__ zw,
+    const int32_t* __restrict__ colsum_w, int M, int N, int K, float* __restrict__ y,
+    int32_t* __restrict__ acc_out) {
+  static_assert(NST == 9, "nine copy stages");
+  static_assert(NW == 8 || NW == 16, "8 or 16 waves: 2 or 4 k slices of the 2 x 2 blocks");
+  // GC > 0: K / 128 fixed at compile time, the step loop unrolls completely
+  // (a loop header would make the compiler wait for every copy in flight)
+  constexpr int BM = 64, BN = 64, STG = (BM + BN) * 128;
+  constexpr int KSPL = NW / 4;                       // k slices of a stage
+  constexpr int MPW = 4 / KSPL;                      // 32-k MFMA steps per wave per stage
+  constexpr int LOADS = 16 / NW;                     // 1 KiB copies per stage per wave
+  __shared__ __align__(16) int8_t S0[STG];
+  __shared__ __align__(16) int8_t S1[STG];
+  __shared__ __align__(16) int8_t S2[STG];
+  __shared__ __align__(16) int8_t S3[STG];
+  __shared__ __align__(16) int8_t S4[STG];
+  __shared__ __align__(16) int8_t S5[STG];
+  __shared__ __align__(16) int8_t S6[STG];
+  __shared__ __align__(16) int8_t S7[STG];
+  __shared__ __align__(16) int8_t S8[STG];
+  auto stage = [&](auto ic) -> int8_t* {
+    constexpr int i = decltype(ic)::value;
+    if constexpr (i == 0) return S0;
+    else if constexpr (i == 1) return S1;
+    else if constexpr (i == 2) return S2;
+    else if constexpr (i == 3) return S3;
+    else if constexpr (i == 4) return S4;
+    else if constexpr (i == 5) return S5;
+    else if constexpr (i == 6) return S6;
+    else if constexpr (i == 7) return S7;
+    else return S8;
+  };
+  const int G = GC > 0 ? GC : K / kGroup;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid % kWave;
+  const int kh = wave / 4, wm = (wave % 4) / 2, wn = wave % 2;
+  const int lr = lane % 32, hf = lane / 32;
+  const int ntn = (N + BN - 1) / BN;
+  const int n0 = (blockIdx.x % ntn) * BN, m0 = (blockIdx.x / ntn) * BM;
+
+  // copies: the 16 blocks of a stage (A rows 8b..8b+7 for b < 8, then B)
+  // are spread over the waves, LOADS each; lane L of block b fills row
+  // 8(b%8) + L/8, chunk slot L%8, with the row's global chunk
+  // (L%8) ^ ((row/2) % 8); rows past M or N re-read the last row
+  const uint8_t* src[LOADS];
+  int dst[LOADS];
+#pragma unroll
+  for (int u = 0; u < LOADS; ++u) {
+    const int b = wave * LOADS + u, isb = b / 8, r8 = 8 * (b % 8) + lane / 8;
+    const int ck = 16 * ((lane % 8) ^ ((r8 >> 1) & 7));
+    src[u] = isb == 0 ? qx + (int64_t)(m0 + r8 < M ? m0 + r8 : M - 1) * K + ck
+                      : qw + (int64_t)(n0 + r8 < N ? n0 + r8 : N - 1) * K + ck;
+    dst[u] = isb * BM * 128 + (b % 8) * 1024;
+  }
+  auto issue = [&](int g, int8_t* S) {
+    const int gc = g < G ? g : G - 1;              // past the end: a surplus copy, never read
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u)
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(src[u] + (int64_t)gc * kGroup),
+          (__attribute__((address_space(3))) void*)(S + dst[u]), 16, 0, 0);
+  };
+
+  v16i acc = v16i{0};
+  const int ra = wm * 32 + lr, rb = wn * 32 + lr;
+  auto compute = [&](const int8_t* S) {
+    v4i av[MPW], bv[MPW];
+#pragma unroll
+    for (int mm = 0; mm < MPW; ++mm) {
+      const int m = MPW * kh + mm;
+      av[mm] = *reinterpret_cast<const v4i*>(S + ra * 128 + 16 * ((4 * hf + m) ^ ((ra >> 1) & 7)));
+      bv[mm] = *reinterpret_cast<const v4i*>(S + BM * 128 + rb * 128 + 16 * ((4 * hf + m) ^ ((rb >> 1) & 7)));
+    }
+#pragma unroll
+    for (int mm = 0; mm < MPW; ++mm) {
+      const v4i c80 = {(int)0x80808080, (int)0x80808080, (int)0x80808080, (int)0x80808080};
+      acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[mm] ^ c80, bv[mm] ^ c80, acc, 0, 0, 0);
+    }
+  };
+  // step l (slot J = l % NST): stage l landed in every wave, then request
+  // stage l + NST - 1 into the slot stage l - 1 used
+  auto step = [&](int l, auto j) {
+    constexpr int J = decltype(j)::value;
+    wait_vm_lds0<(NST - 2) * LOADS>();
+    lds_barrier();
+    issue(l + NST - 1, stage(IC<(J + NST - 1) % NST>{}));
+    compute(stage(IC<J>{}));
+  };
+  issue(0, S0);
+  issue(1, S1);
+  issue(2, S2);
+  issue(3, S3);
+  issue(4, S4);
+  issue(5, S5);
+  issue(6, S6);
+  issue(7, S7);
+#pragma unroll
+  for (int l = 0; l < G; l += NST) {
+    step(l + 0, IC<0>{});
+    if (l + 1 >= G) break;
+    step(l + 1, IC<1>{});
+    if (l + 2 >= G) break;
+    step(l + 2, IC<2>{});
+    if (l + 3 >= G) break;
+    step(l + 3, IC<3>{});
+    if (l + 4 >= G) break;
+    step(l + 4, IC<4>{});
+    if (l + 5 >= G) break;
+    step(l + 5, IC<5>{});
+    if (l + 6 >= G) break;
+    step(l + 6, IC<6>{});
+    if (l + 7 >= G) break;
+    step(l + 7, IC<7>{});
+    if (l + 8 >= G) break;
+    step(l + 8, IC<8>{});
+  }
+  // the k slices meet: slices 1..KSPL-1 park their sums in the (now free)
+  // stages 0..KSPL-2, slice 0 adds them
+  wait_vm_lds0<0>();
+  lds_barrier();
+  if (kh > 0) {
+    int32_t* R = reinterpret_cast<int32_t*>(kh == 1 ? S0 : (kh == 2 ? S1 : S2));
+#pragma unroll
+    for (int r = 0; r < 16; ++r) R[((wave % 4) * 16 + r) * 64 + lane] = acc[r];
+  }
+  wait_lds0();
+  lds_barrier();
+  if (kh > 0) return;
+#pragma unroll
+  for (int q = 1; q < KSPL; ++q) {
+    const int32_t* R = reinterpret_cast<const int32_t*>(q == 1 ? S0 : (q == 2 ? S1 : S2));
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] += R[((wave % 4) * 16 + r) * 64 + lane];
+  }
+
+  const int j = n0 + rb;
+  if (j >= N) return;
+  // the lane's 16 rows' terms are loaded together first (rows past M clamped),
+  // so the stores below wait for nothing
+  const int32_t zwj = zw[j] - 128, cwj = colsum_w[j] - 128 * K;
+  const float swj = sw[j];
+  int32_t zxr[16], rxr[16];
+  float sxr[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int i = m0 + wm * 32 + 8 * (r / 4) + 4 * hf + (r % 4);
+    const int ic = i < M ? i : M - 1;
+    zxr[r] = zx[ic];
+    rxr[r] = rowsum_x[ic];
+    sxr[r] = sx[ic];
+  }
+  // acc = sum (qw-128)(qx-128); expand (qw - zw)(qx - zx) with the re-centred
+  // codes and zero points (same differences), all exact mod 2^32
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int i = m0 + wm * 32 + 8 * (r / 4) + 4 * hf + (r % 4);
+    if (i >= M) continue;
+    const int32_t zxi = zxr[r] - 128, rxi = rxr[r] - 128 * K;
+    const int32_t A = acc[r] - zwj * rxi - zxi * cwj + K * zwj * zxi;
+    const float sc = sxr[r] * swj;
+    const int64_t o = (int64_t)i * N + j;
+    y[o] = (float)A * sc;
+    if (acc_out) acc_out[o] = A;
   }
 }
 
@@ -1402,10 +1380,18 @@ hipError_t launch_w8a8_zp(const uint8_t* qx, const float* sx, const int32_t* zx,
                           const int32_t* zw, const int32_t* colsum_w, int64_t M64, int64_t N64,
                           int64_t K64, float* y, int32_t* acc_out, hipStream_t stream) {
   const int M = (int)M64, N = (int)N64, K = (int)K64;
-  constexpr int TM = 1, TN = 1, BM = 64, BN = 64;
-  dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM), block(256);
-  hipLaunchKernelGGL((k_gemm_tiled<TM, TN, Epi::ZP>), grid, block, 0, stream, qx, sx, qw,
-                     nullptr, nullptr, zx, rowsum_x, sw, zw, colsum_w, 1.0f, M, N, K, y, acc_out);
+  const int tiles = ((M + 63) / 64) * ((N + 63) / 64);
+  const int G = K / kGroup;
+  constexpr int NW = kW8Waves;
+  if (G == 32)
+    hipLaunchKernelGGL((k_w8a8_zp<9, 32, NW>), dim3(tiles), dim3(NW * 64), 0, stream, qx, sx, zx,
+                       rowsum_x, qw, sw, zw, colsum_w, M, N, K, y, acc_out);
+  else if (G == 16)
+    hipLaunchKernelGGL((k_w8a8_zp<9, 16, NW>), dim3(tiles), dim3(NW * 64), 0, stream, qx, sx, zx,
+                       rowsum_x, qw, sw, zw, colsum_w, M, N, K, y, acc_out);
+  else
+    hipLaunchKernelGGL((k_w8a8_zp<9, 0, NW>), dim3(tiles), dim3(NW * 64), 0, stream, qx, sx, zx,
+                       rowsum_x, qw, sw, zw, colsum_w, M, N, K, y, acc_out);
   return hipGetLastError();
 }
 

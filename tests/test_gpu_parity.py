@@ -233,7 +233,8 @@ def test_w4a8_deterministic(bgt, orc, dev):
 # ------------------------------------------------------------------ W8A8 ZP
 
 @pytest.mark.parametrize("M,K,N,relu", [(1, 128, 16, False), (37, 384, 80, False), (256, 4096, 4096, False),
-                                        (256, 4096, 4096, True), (130, 1024, 208, False)])
+                                        (256, 4096, 4096, True), (130, 1024, 208, False),
+                                        (65, 2048, 144, False), (64, 4096, 64, True), (3, 896, 48, False)])
 def test_w8a8_zp(bgt, orc, dev, M, K, N, relu):
     say(f"w8a8_gemm_zp M={M} K={K} N={N} relu={relu}")
     x, w = synth.w8a8_inputs(M + K, M, K, N, relu=relu)
