@@ -68,14 +68,14 @@ METRIC = "W4A8 integer-scale GEMM TOPS + HBM GB/s, K=4096 N=22016, M=1..4096"
 # profiles/w4a8_gemm_kernels__M1_to_M4096__hbm_bytes.txt), keyed by
 # (kernel, M). They hold only for the kernel source they were taken on: when
 # gemm.hip differs from that source, traffic is reported as null.
-TRAFFIC_GEMM_SHA = "1488fd7d04e88ee3"
-TRAFFIC = {("k_w4a8_decode<IS>", 1): 48166887,
-           ("k_w4a8_decode<IS>", 4): 48530397,
-           ("k_w4a8_decode<IS>", 16): 49980342,
-           ("k_w4a8_decode<IS>", 64): 55828244,
-           ("k_w4a8_prefill<4,2,2,2,IS>", 256): 79138687,
-           ("k_w4a8_prefill<4,2,2,2,IS>", 4096): 922106797,
-           ("k_w8a8_zp<9,32>", 256): 29524652}
+TRAFFIC_GEMM_SHA = "34a9ce114de72d48"
+TRAFFIC = {("k_w4a8_decode<IS>", 1): 48162780,
+           ("k_w4a8_decode<IS>", 4): 48530386,
+           ("k_w4a8_decode<IS>", 16): 49980330,
+           ("k_w4a8_decode<IS>", 64): 55824137,
+           ("k_w4a8_prefill<4,2,2,2,IS>", 256): 79137927,
+           ("k_w4a8_prefill<4,2,2,2,IS>", 4096): 922100563,
+           ("k_w8a8_zp<9,32>", 256): 29644447}
 
 
 def measured_traffic(kernel, Ms):
