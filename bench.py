@@ -88,9 +88,9 @@ def measured_traffic(kernel, Ms):
     return None if any(v is None for v in vals) else int(np.mean(vals))
 
 
-def gemm_bytes(M, N, K, scale_bytes=4):
+def gemm_bytes(M, N, K, scale_bytes=4, out_bytes=4):
     G = K // 128
-    return N * K // 2 + scale_bytes * G * N + M * K + 4 * M + 4 * M * N
+    return N * K // 2 + scale_bytes * G * N + M * K + 4 * M + out_bytes * M * N
 
 
 def quant_bytes(M, K):
@@ -327,7 +327,9 @@ def run_prefill(args, torch, bgt, dev):
     pw = bgt.pack_weights_int4(torch.from_numpy(w).to(dev), alpha=synth.ALPHA)
     rot = Rotor(torch, pw["packed"], pw["iscale"], pw["fscale"])
     qs = {M: bgt.quantize_act(xd[:M].contiguous())[:2] for M in Ms}
-    ys = {M: torch.empty((M, N), dtype=torch.float32, device=dev) for M in Ms}
+    odt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[args.out_dtype]
+    ob = 4 if args.out_dtype == "f32" else 2
+    ys = {M: torch.empty((M, N), dtype=odt, device=dev) for M in Ms}
     res = {}
     tot_ops = 0
     tot_us = 0.0
@@ -343,7 +345,7 @@ def run_prefill(args, torch, bgt, dev):
                 if fs:
                     bgt.w4a8_gemm_fs(q, s, packed, fscale, N, y=ys[M])
                 else:
-                    bgt.w4a8_gemm_is(q, s, packed, iscale, pw["alpha"], N, y=ys[M])
+                    bgt.w4a8_gemm_is_narrow(q, s, packed, iscale, pw["alpha"], N, y=ys[M])
                 e1.record()
                 if it >= args.warmup:
                     ts.append((e0, e1))
@@ -363,9 +365,11 @@ def run_prefill(args, torch, bgt, dev):
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(tot_us / 1e3, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "int8xint4->int32", "data": "synthetic (seeded)",
-        "config": {"workload": "prefill sweep: W4A8-IS GEMM K=4096 N=22016, M in {512,1024,2048,4096}"},
+        "config": {"workload": "prefill sweep: W4A8-IS GEMM K=4096 N=22016, M in {512,1024,2048,4096}",
+                   "output": {"f32": "float32", "f16": "float16", "bf16": "bfloat16"}[args.out_dtype]},
         "roofline": {"bound": "mfma", "achieved": r["TOPS"], "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
-                     "frac": r["mfma_frac"], "traffic": measured_traffic(r["kernel"], [big]),
+                     "frac": r["mfma_frac"],
+                     "traffic": measured_traffic(r["kernel"], [big]) if ob == 4 else None,
                      "kernel": r["kernel"], "launch_M": [big],
                      "avg_launch_us": r["us_median"]},
         "sweep": res,
@@ -482,6 +486,8 @@ def main():
     ap.add_argument("--no-fused-quant", dest="fused_quant", action="store_false",
                     help="decode workload: run the quantizer and the GEMM as two calls for "
                          "every M (default: the fused entry point, one launch for M <= 4)")
+    ap.add_argument("--out-dtype", default="f32", choices=["f32", "f16", "bf16"],
+                    help="prefill workload: element type of y (fp32 result rounded once)")
     ap.add_argument("--launch", default="graph", choices=["graph", "eager"],
                     help="decode workload: replay each step from a HIP graph (default) or "
                          "issue every launch from Python")

@@ -30,6 +30,9 @@ BGT_ERR_ALPHA = -4
 BGT_ERR_MODE = -5
 BGT_ERR_HIP = -6
 BGT_ERR_RANGE = -7
+BGT_F32 = 0
+BGT_F16 = 1
+BGT_BF16 = 2
 BGT_QUANT_SYM_I8 = 0
 BGT_QUANT_ASYM_U8 = 1
 GROUP = 128
@@ -38,6 +41,7 @@ EXPORTED = (
     "bgt_quantize_act", "bgt_pack_weights_int4", "bgt_w4a8_gemm_is", "bgt_w4a8_gemm_fs",
     "bgt_w8a8_gemm_zp", "bgt_status_string", "bgt_abi_version", "bgt_w4a8_kernel_name",
     "bgt_narrow_iscale", "bgt_w4a8_gemm_is_narrow", "bgt_w4a8_linear_is", "bgt_w4a8_linear_fused",
+    "bgt_quantize_act_ex", "bgt_w4a8_gemm_is_ex", "bgt_w4a8_gemm_fs_ex",
 )
 
 _lib = None
@@ -64,7 +68,10 @@ def lib():
         L.bgt_w4a8_gemm_fs.argtypes = [P, P, P, P, I64, I64, I64, P, P]
         L.bgt_narrow_iscale.argtypes = [P, I64, I, P, P]
         L.bgt_w4a8_gemm_is_narrow.argtypes = [P, P, P, P, I, I, I64, I64, I64, P, P, P]
-        L.bgt_w4a8_linear_is.argtypes = [P, I64, P, P, I, I, I64, I64, I64, P, P, P, P]
+        L.bgt_w4a8_linear_is.argtypes = [P, I, I64, P, P, I, I, I64, I64, I64, P, P, P, I, P]
+        L.bgt_quantize_act_ex.argtypes = [P, I, I64, I64, I64, I, P, P, P, P, P]
+        L.bgt_w4a8_gemm_is_ex.argtypes = [P, P, P, P, I, I, I64, I64, I64, P, I, P, P]
+        L.bgt_w4a8_gemm_fs_ex.argtypes = [P, P, P, P, I64, I64, I64, P, I, P]
         L.bgt_w4a8_linear_fused.argtypes = [I64, I64, P, I64]
         L.bgt_w8a8_gemm_zp.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, P, P, P]
         L.bgt_status_string.argtypes = [I]
@@ -117,6 +124,15 @@ def _check(t, name, dtype, shape=None):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
+def _elem_type(t, name):
+    """BGT element-type code of a float32 / float16 / bfloat16 tensor."""
+    torch = _torch()
+    codes = {torch.float32: BGT_F32, torch.float16: BGT_F16, torch.bfloat16: BGT_BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"{name} must be float32, float16 or bfloat16, got {t.dtype}")
+    return codes[t.dtype]
+
+
 def _raise(fn, st):
     if st < 0:
         raise BgtError(fn, st)
@@ -126,7 +142,8 @@ def _raise(fn, st):
 # ------------------------------------------------------------------ entry points
 def quantize_act(x, mode: str = "sym", q=None, scale=None, zero=None, rowsum=None,
                  want_rowsum: bool = False):
-    """Per-row dynamic quantization of x (rows x cols float32, row-major).
+    """Per-row dynamic quantization of x (rows x cols float32, float16 or
+    bfloat16, row-major; half types are widened to fp32 exactly).
 
     mode "sym": int8 codes in [-127, 127] and one scale per row.
     mode "asym": uint8 codes in [0, 255], scale, zero point and code row sum.
@@ -137,8 +154,9 @@ def quantize_act(x, mode: str = "sym", q=None, scale=None, zero=None, rowsum=Non
     if x.dim() != 2:
         raise ValueError("x must be 2-D")
     rows, cols = x.shape
-    if x.dtype != torch.float32 or not x.is_cuda or x.stride(1) != 1:
-        raise ValueError("x must be a float32 GPU tensor with unit column stride")
+    if not x.is_cuda or x.stride(1) != 1:
+        raise ValueError("x must be a GPU tensor with unit column stride")
+    xt = _elem_type(x, "x")
     ld = x.stride(0)
     asym = mode == "asym"
     if mode not in ("sym", "asym"):
@@ -157,10 +175,10 @@ def quantize_act(x, mode: str = "sym", q=None, scale=None, zero=None, rowsum=Non
         _check(zero, "zero", torch.int32, (rows,))
     if rowsum is not None:
         _check(rowsum, "rowsum", torch.int32, (rows,))
-    st = lib().bgt_quantize_act(_ptr(x), rows, cols, ld,
-                                BGT_QUANT_ASYM_U8 if asym else BGT_QUANT_SYM_I8,
-                                _ptr(q), _ptr(scale), _ptr(zero), _ptr(rowsum), _stream(dev))
-    _raise("bgt_quantize_act", st)
+    st = lib().bgt_quantize_act_ex(_ptr(x), xt, rows, cols, ld,
+                                   BGT_QUANT_ASYM_U8 if asym else BGT_QUANT_SYM_I8,
+                                   _ptr(q), _ptr(scale), _ptr(zero), _ptr(rowsum), _stream(dev))
+    _raise("bgt_quantize_act_ex", st)
     return (q, scale, zero, rowsum) if asym else (q, scale, rowsum)
 
 
@@ -236,34 +254,41 @@ def narrow_iscale(iscale, width: int, out=None):
     return out
 
 
-def w4a8_gemm_is_narrow(qx, sx, packed, iscale, alpha: int, N: int, y=None, acc_out=None):
+def w4a8_gemm_is_narrow(qx, sx, packed, iscale, alpha: int, N: int, y=None, acc_out=None,
+                        out_dtype=None):
     """w4a8_gemm_is with integer scales stored as uint8, uint16 or int32
-    (width taken from iscale's dtype); returns y (M x N float32)."""
+    (width taken from iscale's dtype) and y as float32, float16 or bfloat16
+    (y's dtype, or out_dtype when y is not given); returns y (M x N)."""
     torch = _torch()
     widths = {torch.uint8: 1, torch.uint16: 2, torch.int32: 4}
     if not isinstance(iscale, torch.Tensor) or iscale.dtype not in widths:
         raise TypeError("iscale must be a uint8, uint16 or int32 tensor")
     M, K = _gemm_common(qx, sx, packed, iscale, iscale.dtype, N)
-    y = torch.empty((M, N), dtype=torch.float32, device=qx.device) if y is None else y
-    _check(y, "y", torch.float32, (M, N))
+    if y is None:
+        y = torch.empty((M, N), dtype=out_dtype or torch.float32, device=qx.device)
+    _check(y, "y", y.dtype, (M, N))
+    yt = _elem_type(y, "y")
     if acc_out is not None:
         _check(acc_out, "acc_out", torch.int32, (M, N))
-    st = lib().bgt_w4a8_gemm_is_narrow(_ptr(qx), _ptr(sx), _ptr(packed), _ptr(iscale),
-                                       widths[iscale.dtype], int(alpha), M, N, K, _ptr(y),
-                                       _ptr(acc_out), _stream(qx.device))
-    _raise("bgt_w4a8_gemm_is_narrow", st)
+    st = lib().bgt_w4a8_gemm_is_ex(_ptr(qx), _ptr(sx), _ptr(packed), _ptr(iscale),
+                                   widths[iscale.dtype], int(alpha), M, N, K, _ptr(y), yt,
+                                   _ptr(acc_out), _stream(qx.device))
+    _raise("bgt_w4a8_gemm_is_ex", st)
     return y
 
 
-def w4a8_linear_is(x, packed, iscale, alpha: int, N: int, qx=None, sx=None, y=None):
-    """Per-token quantization of x (M x K float32) and the integer-scale GEMM.
+def w4a8_linear_is(x, packed, iscale, alpha: int, N: int, qx=None, sx=None, y=None,
+                   out_dtype=None):
+    """Per-token quantization of x (M x K float32, float16 or bfloat16) and the
+    integer-scale GEMM; y float32, float16 or bfloat16 (y's dtype, else
+    out_dtype, else x's dtype).
 
     One launch for M <= 4 on the decode path (see w4a8_linear_fused); returns
     (y, qx, sx), the quantized activations included."""
     torch = _torch()
-    if not isinstance(x, torch.Tensor) or x.dtype != torch.float32 or not x.is_cuda \
-            or x.dim() != 2 or x.stride(1) != 1:
-        raise ValueError("x must be a 2-D float32 GPU tensor with unit column stride")
+    if not isinstance(x, torch.Tensor) or not x.is_cuda or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D GPU tensor with unit column stride")
+    xt = _elem_type(x, "x")
     M, K = x.shape
     widths = {torch.uint8: 1, torch.uint16: 2, torch.int32: 4}
     if not isinstance(iscale, torch.Tensor) or iscale.dtype not in widths:
@@ -273,13 +298,15 @@ def w4a8_linear_is(x, packed, iscale, alpha: int, N: int, qx=None, sx=None, y=No
     dev = x.device
     qx = torch.empty((M, K), dtype=torch.int8, device=dev) if qx is None else qx
     sx = torch.empty(M, dtype=torch.float32, device=dev) if sx is None else sx
-    y = torch.empty((M, N), dtype=torch.float32, device=dev) if y is None else y
+    if y is None:
+        y = torch.empty((M, N), dtype=out_dtype or x.dtype, device=dev)
     _check(qx, "qx", torch.int8, (M, K))
     _check(sx, "sx", torch.float32, (M,))
-    _check(y, "y", torch.float32, (M, N))
-    st = lib().bgt_w4a8_linear_is(_ptr(x), x.stride(0), _ptr(packed), _ptr(iscale),
+    _check(y, "y", y.dtype, (M, N))
+    yt = _elem_type(y, "y")
+    st = lib().bgt_w4a8_linear_is(_ptr(x), xt, x.stride(0), _ptr(packed), _ptr(iscale),
                                   widths[iscale.dtype], int(alpha), M, N, K, _ptr(qx), _ptr(sx),
-                                  _ptr(y), _stream(dev))
+                                  _ptr(y), yt, _stream(dev))
     _raise("bgt_w4a8_linear_is", st)
     return y, qx, sx
 
@@ -290,15 +317,18 @@ def w4a8_linear_fused(x) -> bool:
     return bool(lib().bgt_w4a8_linear_fused(M, K, _ptr(x), x.stride(0)))
 
 
-def w4a8_gemm_fs(qx, sx, packed, fscale, N: int, y=None):
-    """Y = X.W with the float-scale epilogue (the control); returns y."""
+def w4a8_gemm_fs(qx, sx, packed, fscale, N: int, y=None, out_dtype=None):
+    """Y = X.W with the float-scale epilogue (the control); y float32, float16
+    or bfloat16 (y's dtype, or out_dtype); returns y."""
     torch = _torch()
     M, K = _gemm_common(qx, sx, packed, fscale, torch.float32, N)
-    y = torch.empty((M, N), dtype=torch.float32, device=qx.device) if y is None else y
-    _check(y, "y", torch.float32, (M, N))
-    st = lib().bgt_w4a8_gemm_fs(_ptr(qx), _ptr(sx), _ptr(packed), _ptr(fscale), M, N, K, _ptr(y),
-                                _stream(qx.device))
-    _raise("bgt_w4a8_gemm_fs", st)
+    if y is None:
+        y = torch.empty((M, N), dtype=out_dtype or torch.float32, device=qx.device)
+    _check(y, "y", y.dtype, (M, N))
+    yt = _elem_type(y, "y")
+    st = lib().bgt_w4a8_gemm_fs_ex(_ptr(qx), _ptr(sx), _ptr(packed), _ptr(fscale), M, N, K,
+                                   _ptr(y), yt, _stream(qx.device))
+    _raise("bgt_w4a8_gemm_fs_ex", st)
     return y
 
 

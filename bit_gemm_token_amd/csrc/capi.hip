@@ -19,6 +19,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool pow2_alpha(int a) { return a >= 1 && a <= (1 << 30) && (a & (a - 1)) == 0; }
 
+bool valid_type(int t) { return t == BGT_F32 || t == BGT_F16 || t == BGT_BF16; }
+
 int hip_status(hipError_t e) { return e == hipSuccess ? BGT_OK : BGT_ERR_HIP; }
 
 int check_gemm_shape(int64_t M, int64_t N, int64_t K, int64_t kmax) {
@@ -41,9 +43,9 @@ int searched_alpha_log2(float smin) {
 
 extern "C" {
 
-int bgt_abi_version(void) { return 102; }
+int bgt_abi_version(void) { return 103; }
 
-int bgt_w4a8_linear_fused(int64_t M, int64_t K, const float* x, int64_t ldx) {
+int bgt_w4a8_linear_fused(int64_t M, int64_t K, const void* x, int64_t ldx) {
   return bgt::w4a8_linear_fused(M, K, x, ldx) ? 1 : 0;
 }
 
@@ -60,7 +62,7 @@ const char* bgt_status_string(int status) {
     case BGT_ERR_SHAPE: return "error: size out of range or not a required multiple";
     case BGT_ERR_ALIGN: return "error: pointer or leading dimension misaligned";
     case BGT_ERR_ALPHA: return "error: amplifier must be a power of two in [1, 2^30]";
-    case BGT_ERR_MODE: return "error: unknown quantization mode";
+    case BGT_ERR_MODE: return "error: unknown quantization mode, element type or scale width";
     case BGT_ERR_HIP: return "error: HIP call failed";
     case BGT_ERR_RANGE: return "error: integer scale out of range (pack: >= 2^23; narrow: above the element type)";
     default: return "unknown status";
@@ -69,13 +71,20 @@ const char* bgt_status_string(int status) {
 
 int bgt_quantize_act(const float* x, int64_t rows, int64_t cols, int64_t ld, int mode, void* q,
                      float* scale, int32_t* zero, int32_t* rowsum, void* stream) {
+  return bgt_quantize_act_ex(x, BGT_F32, rows, cols, ld, mode, q, scale, zero, rowsum, stream);
+}
+
+int bgt_quantize_act_ex(const void* x, int x_type, int64_t rows, int64_t cols, int64_t ld,
+                        int mode, void* q, float* scale, int32_t* zero, int32_t* rowsum,
+                        void* stream) {
   if (mode != BGT_QUANT_SYM_I8 && mode != BGT_QUANT_ASYM_U8) return BGT_ERR_MODE;
+  if (!valid_type(x_type)) return BGT_ERR_MODE;
   if (!x || !q || !scale) return BGT_ERR_NULL;
   if (mode == BGT_QUANT_ASYM_U8 && !zero) return BGT_ERR_NULL;
   if (rows < 1 || rows > 0x7FFFFFFF || cols < 1 || cols > (1 << 24) || ld < cols)
     return BGT_ERR_SHAPE;
-  return hip_status(bgt::launch_quant_rows(x, rows, cols, ld, mode == BGT_QUANT_ASYM_U8, q, scale,
-                                           zero, rowsum, static_cast<hipStream_t>(stream)));
+  return hip_status(bgt::launch_quant_rows(x, x_type, rows, cols, ld, mode == BGT_QUANT_ASYM_U8, q,
+                                           scale, zero, rowsum, static_cast<hipStream_t>(stream)));
 }
 
 int bgt_pack_weights_int4(const float* w, int64_t K, int64_t N, int64_t group, int alpha,
@@ -127,8 +136,16 @@ int bgt_w4a8_gemm_is(const int8_t* qx, const float* sx, const uint8_t* packed,
 int bgt_w4a8_gemm_is_narrow(const int8_t* qx, const float* sx, const uint8_t* packed,
                             const void* iscale, int width, int alpha, int64_t M, int64_t N,
                             int64_t K, float* y, int32_t* acc_out, void* stream) {
+  return bgt_w4a8_gemm_is_ex(qx, sx, packed, iscale, width, alpha, M, N, K, y, BGT_F32, acc_out,
+                             stream);
+}
+
+int bgt_w4a8_gemm_is_ex(const int8_t* qx, const float* sx, const uint8_t* packed,
+                        const void* iscale, int width, int alpha, int64_t M, int64_t N, int64_t K,
+                        void* y, int y_type, int32_t* acc_out, void* stream) {
   if (!qx || !sx || !packed || !iscale || !y) return BGT_ERR_NULL;
   if (width != 1 && width != 2 && width != 4) return BGT_ERR_MODE;
+  if (!valid_type(y_type)) return BGT_ERR_MODE;
   int st = check_gemm_shape(M, N, K, 65536);
   if (st != BGT_OK) return st;
   if (!pow2_alpha(alpha)) return BGT_ERR_ALPHA;
@@ -136,34 +153,45 @@ int bgt_w4a8_gemm_is_narrow(const int8_t* qx, const float* sx, const uint8_t* pa
       (acc_out && !aligned16(acc_out)))
     return BGT_ERR_ALIGN;
   return hip_status(bgt::launch_w4a8(false, qx, sx, packed, iscale, width, nullptr, alpha, M, N,
-                                     K, y, acc_out, static_cast<hipStream_t>(stream)));
+                                     K, bgt::OutY{y, y_type}, acc_out,
+                                     static_cast<hipStream_t>(stream)));
 }
 
-int bgt_w4a8_linear_is(const float* x, int64_t ldx, const uint8_t* packed, const void* iscale,
-                       int width, int alpha, int64_t M, int64_t N, int64_t K, int8_t* qx,
-                       float* sx, float* y, void* stream) {
+int bgt_w4a8_linear_is(const void* x, int x_type, int64_t ldx, const uint8_t* packed,
+                       const void* iscale, int width, int alpha, int64_t M, int64_t N, int64_t K,
+                       int8_t* qx, float* sx, void* y, int y_type, void* stream) {
   if (!x || !packed || !iscale || !qx || !sx || !y) return BGT_ERR_NULL;
   if (width != 1 && width != 2 && width != 4) return BGT_ERR_MODE;
+  if (!valid_type(x_type) || !valid_type(y_type)) return BGT_ERR_MODE;
   int st = check_gemm_shape(M, N, K, 65536);
   if (st != BGT_OK) return st;
   if (ldx < K) return BGT_ERR_SHAPE;
   if (!pow2_alpha(alpha)) return BGT_ERR_ALPHA;
   if (!aligned16(packed) || !aligned16(iscale) || !aligned16(qx) || !aligned16(y))
     return BGT_ERR_ALIGN;
-  return hip_status(bgt::launch_w4a8_linear(x, ldx, packed, iscale, width, alpha, M, N, K, qx, sx,
-                                            y, static_cast<hipStream_t>(stream)));
+  return hip_status(bgt::launch_w4a8_linear(x, x_type, ldx, packed, iscale, width, alpha, M, N, K,
+                                            qx, sx, bgt::OutY{y, y_type},
+                                            static_cast<hipStream_t>(stream)));
 }
 
 int bgt_w4a8_gemm_fs(const int8_t* qx, const float* sx, const uint8_t* packed,
                      const float* fscale, int64_t M, int64_t N, int64_t K, float* y,
                      void* stream) {
+  return bgt_w4a8_gemm_fs_ex(qx, sx, packed, fscale, M, N, K, y, BGT_F32, stream);
+}
+
+int bgt_w4a8_gemm_fs_ex(const int8_t* qx, const float* sx, const uint8_t* packed,
+                        const float* fscale, int64_t M, int64_t N, int64_t K, void* y, int y_type,
+                        void* stream) {
   if (!qx || !sx || !packed || !fscale || !y) return BGT_ERR_NULL;
+  if (!valid_type(y_type)) return BGT_ERR_MODE;
   int st = check_gemm_shape(M, N, K, 65536);
   if (st != BGT_OK) return st;
   if (!aligned16(qx) || !aligned16(packed) || !aligned16(fscale) || !aligned16(y))
     return BGT_ERR_ALIGN;
-  return hip_status(bgt::launch_w4a8(true, qx, sx, packed, nullptr, 4, fscale, 1, M, N, K, y,
-                                     nullptr, static_cast<hipStream_t>(stream)));
+  return hip_status(bgt::launch_w4a8(true, qx, sx, packed, nullptr, 4, fscale, 1, M, N, K,
+                                     bgt::OutY{y, y_type}, nullptr,
+                                     static_cast<hipStream_t>(stream)));
 }
 
 int bgt_narrow_iscale(const int32_t* iscale, int64_t count, int width, void* out, void* stream) {

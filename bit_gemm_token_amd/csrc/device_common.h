@@ -4,10 +4,54 @@
 // int4 -> int8 unpacks of the packed weight layout, and MFMA operand types.
 #pragma once
 
+#include <hip/hip_bf16.h>
+#include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace bgt {
+
+// Element types of activations and outputs (the BGT_F32 / BGT_F16 / BGT_BF16
+// codes of the C ABI).
+constexpr int kF32 = 0, kF16 = 1, kBF16 = 2;
+
+// Four consecutive activation elements x[4*i .. 4*i+3] of element type IT,
+// widened to fp32 (exact for fp16 and bf16); one 16-byte (fp32) or 8-byte
+// load. And one element.
+template <int IT>
+__device__ __forceinline__ float4 load_x4(const void* x, int64_t i) {
+  if constexpr (IT == kF32) {
+    return reinterpret_cast<const float4*>(x)[i];
+  } else {
+    const uint2 u = reinterpret_cast<const uint2*>(x)[i];
+    if constexpr (IT == kF16) {
+      const __half2 a = *reinterpret_cast<const __half2*>(&u.x);
+      const __half2 b = *reinterpret_cast<const __half2*>(&u.y);
+      return make_float4(__low2float(a), __high2float(a), __low2float(b), __high2float(b));
+    } else {
+      return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                         __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
+    }
+  }
+}
+template <int IT>
+__device__ __forceinline__ float load_x1(const void* x, int64_t i) {
+  if constexpr (IT == kF32) return static_cast<const float*>(x)[i];
+  else if constexpr (IT == kF16) return __half2float(static_cast<const __half*>(x)[i]);
+  else return __uint_as_float((uint32_t)static_cast<const uint16_t*>(x)[i] << 16);
+}
+
+// The output matrix y and its element type. Values are computed in fp32 and
+// rounded once to the stored type (fp16, bf16: round to nearest even).
+struct OutY {
+  void* p;
+  int type;
+  __device__ __forceinline__ void put(int64_t o, float v) const {
+    if (type == kF32) static_cast<float*>(p)[o] = v;
+    else if (type == kF16) static_cast<__half*>(p)[o] = __float2half(v);
+    else static_cast<__hip_bfloat16*>(p)[o] = __float2bfloat16(v);
+  }
+};
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));

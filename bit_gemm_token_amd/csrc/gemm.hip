@@ -51,7 +51,7 @@ __global__ __launch_bounds__(kWave * KS) void k_w4a8_skinny(
     const int8_t* __restrict__ qx, const float* __restrict__ sx,
     const uint4* __restrict__ packed, const ST* __restrict__ iscale,
     const float* __restrict__ fscale, float inv_alpha, int M, int N, int K,
-    float* __restrict__ y, int32_t* __restrict__ acc_out) {
+    OutY y, int32_t* __restrict__ acc_out) {
   constexpr int CH = (MR <= 2) ? 8 : 4;   // group blocks in flight per batch
   const int G = K / kGroup;
   const int t = blockIdx.x;
@@ -152,10 +152,10 @@ __global__ __launch_bounds__(kWave * KS) void k_w4a8_skinny(
       if (i < M) {
         const int64_t o = (int64_t)i * N + j;
         if (FS) {
-          y[o] = facc[rb][r] * sx[i];
+          y.put(o, facc[rb][r] * sx[i]);
         } else {
           const float t0 = (float)acc[rb][r] * sx[i];
-          y[o] = t0 * inv_alpha;
+          y.put(o, t0 * inv_alpha);
           if (acc_out) acc_out[o] = acc[rb][r];
         }
       }
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(MAXT) __attribute__((amdgpu_waves_per_eu(WPE))) voi
     const int8_t* __restrict__ qx, const float* __restrict__ sx,
     const uint4* __restrict__ packed, const ST* __restrict__ iscale,
     const float* __restrict__ fscale, float inv_alpha, int M, int N, int K,
-    float* __restrict__ y, int32_t* __restrict__ acc_out) {
+    OutY y, int32_t* __restrict__ acc_out) {
   extern __shared__ int lds[];
   constexpr int NR = MR * 4;                       // accumulator registers per lane
   const int G = K / kGroup, T = N / 16;
@@ -221,13 +221,13 @@ __global__ __launch_bounds__(MAXT) __attribute__((amdgpu_waves_per_eu(WPE))) voi
           float a = 0.0f;
           for (int l = 0; l < G; ++l)
             a = __builtin_fmaf((float)xa[(l * NR + idx) * kWave + lane], fb[l * 16 + c], a);
-          if (i < M) y[(int64_t)i * N + j] = a * srow[idx];
+          if (i < M) y.put((int64_t)i * N + j, a * srow[idx]);
         } else {
           int sum = 0;
           for (int w = 0; w < KS; ++w) sum += xa[(w * NR + idx) * kWave + lane];
           if (i < M) {
             const float t0 = (float)sum * srow[idx];
-            y[(int64_t)i * N + j] = t0 * inv_alpha;
+            y.put((int64_t)i * N + j, t0 * inv_alpha);
             if (acc_out) acc_out[(int64_t)i * N + j] = sum;
           }
         }
@@ -415,7 +415,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
     const int8_t* __restrict__ qx, const float* __restrict__ sx,
     const uint4* __restrict__ packed, const ST* __restrict__ iscale,
     const float* __restrict__ fscale, float inv_alpha, int M, int N, int K,
-    float* __restrict__ y, int32_t* __restrict__ acc_out) {
+    OutY y, int32_t* __restrict__ acc_out) {
   static_assert(TMW == 2 && TNW == 2, "four 32 x 32 blocks per wave");
   constexpr int NW = WM * WN, NT = NW * 64;
   constexpr int BM = WM * TMW * 32, BN = WN * TNW * 32, NB = TMW * TNW;
@@ -659,10 +659,10 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
       if (!full && (i >= M || j >= N)) continue;
       const int64_t o = (int64_t)i * N + j;
       if (FS) {
-        y[o] = facc[k][r] * srow[a][r];
+        y.put(o, facc[k][r] * srow[a][r]);
       } else {
         const float t0 = (float)acc[k][r] * srow[a][r];
-        y[o] = t0 * inv_alpha;
+        y.put(o, t0 * inv_alpha);
         if (acc_out) acc_out[o] = acc[k][r];
       }
     }
@@ -688,7 +688,7 @@ __global__ __launch_bounds__(NW * 64) void k_w8a8_zp(
     const uint8_t* __restrict__ qx, const float* __restrict__ sx, const int32_t* __restrict__ zx,
     const int32_t* __restrict__ rowsum_x, const uint8_t* __restrict__ qw,
     const float* __restrict__ sw, const int32_t* __restrict__ zw,
-    const int32_t* __restrict__ colsum_w, int M, int N, int K, float* __restrict__ y,
+    const int32_t* __restrict__ colsum_w, int M, int N, int K, OutY y,
     int32_t* __restrict__ acc_out) {
   static_assert(NST == 9, "nine copy stages");
   static_assert(NW == 8 || NW == 16, "8 or 16 waves: 2 or 4 k slices of the 2 x 2 blocks");
@@ -849,7 +849,7 @@ __global__ __launch_bounds__(NW * 64) void k_w8a8_zp(
     const int32_t A = acc[r] - zwj * rxi - zxi * cwj + K * zwj * zxi;
     const float sc = sxr[r] * swj;
     const int64_t o = (int64_t)i * N + j;
-    y[o] = (float)A * sc;
+    y.put(o, (float)A * sc);
     if (acc_out) acc_out[o] = A;
   }
 }
@@ -870,13 +870,13 @@ __global__ __launch_bounds__(NW * 64) void k_w8a8_zp(
 //      ascending fma chain).
 // Every load is a register load, so the compiler's wait counts stay exact.
 // =====================================================================
-template <bool FS, int W, int D, int G, int MR, typename ST, bool FQ>
+template <bool FS, int W, int D, int G, int MR, typename ST, bool FQ, int IT>
 __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
     const int8_t* __restrict__ qx, const float* __restrict__ sx,
     const uint4* __restrict__ packed, const ST* __restrict__ iscale,
     const float* __restrict__ fscale, float inv_alpha, int M, int N,
-    float* __restrict__ y, int32_t* __restrict__ acc_out,
-    const float* __restrict__ xf, int ldx, int8_t* __restrict__ q_out, float* __restrict__ s_out) {
+    OutY y, int32_t* __restrict__ acc_out,
+    const void* __restrict__ xf, int ldx, int8_t* __restrict__ q_out, float* __restrict__ s_out) {
   constexpr int CGM = MR == 1 ? 32 : 8;
   constexpr int CG = G < CGM ? G : CGM;              // groups per X chunk (<= 64 KiB)
   constexpr int NCH = G / CG;                        // chunks
@@ -919,8 +919,9 @@ __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
     for (int i = 0; i < FPW; ++i)
       *reinterpret_cast<v4i*>(sA + (buf * CFR + wave + W * i) * 1024 + lane * 16) = xa[i];
   };
-  // fused quantization (FQ, M <= 4): the fp32 rows, each thread XV float4 of
-  // every row, requested before the scales and the weights
+  // fused quantization (FQ, M <= 4): the rows (element type IT, widened to
+  // fp32), each thread XV groups of 4 of every row, requested before the
+  // scales and the weights
   constexpr int XV = FQ ? K / 4 / (W * 64) : 1;
   static_assert(!FQ || XV * W * 64 * 4 == K, "row split");
   float4 xv[4][XV];
@@ -930,8 +931,7 @@ __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
 #pragma unroll
       for (int v = 0; v < XV; ++v)
         if (i < M)
-          xv[i][v] = *reinterpret_cast<const float4*>(xf + (int64_t)i * ldx +
-                                                      4 * (threadIdx.x + W * 64 * v));
+          xv[i][v] = load_x4<IT>(xf, (int64_t)i * (ldx / 4) + threadIdx.x + W * 64 * v);
   } else {
     load_chunk(0);
   }
@@ -1115,10 +1115,10 @@ __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
         const int64_t o = (int64_t)i * N + j;
         const float si = sX[i];
         if (FS) {
-          y[o] = facc[rb][r] * si;
+          y.put(o, facc[rb][r] * si);
         } else {
           const float t0 = (float)acc[rb][r] * si;
-          y[o] = t0 * inv_alpha;
+          y.put(o, t0 * inv_alpha);
           if (acc_out) acc_out[o] = acc[rb][r];
         }
       }
@@ -1129,7 +1129,7 @@ __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
 template <int MR, bool FS, typename ST>
 static void launch_skinny(const int8_t* qx, const float* sx, const uint8_t* packed,
                           const ST* iscale, const float* fscale, float inv_alpha, int M,
-                          int N, int K, float* y, int32_t* acc_out, hipStream_t stream) {
+                          int N, int K, OutY y, int32_t* acc_out, hipStream_t stream) {
   constexpr int KS = FS ? 1 : 4;
   dim3 grid(N / 16), block(kWave * KS);
   hipLaunchKernelGGL((k_w4a8_skinny<MR, KS, FS, ST>), grid, block, 0, stream, qx, sx,
@@ -1205,7 +1205,7 @@ static W4Plan plan_w4a8(int M, int K, bool fs) {
 template <int MR, bool FS, typename ST>
 static bool launch_stream(const int8_t* qx, const float* sx, const uint8_t* packed,
                           const ST* iscale, const float* fscale, float inv_alpha, int M,
-                          int N, int K, float* y, int32_t* acc_out, hipStream_t stream) {
+                          int N, int K, OutY y, int32_t* acc_out, hipStream_t stream) {
   using C = StreamCfg<MR>;
   const int G = K / kGroup, T = N / 16;
   const int KS = (G + C::GPW - 1) / C::GPW;        // loader waves (+1 finisher)
@@ -1224,7 +1224,7 @@ static bool launch_stream(const int8_t* qx, const float* sx, const uint8_t* pack
 template <bool FS, typename ST>
 static void launch_small_m(const W4Plan& plan, const int8_t* qx, const float* sx,
                            const uint8_t* packed, const ST* iscale, const float* fscale,
-                           float inv_alpha, int M, int N, int K, float* y, int32_t* acc_out,
+                           float inv_alpha, int M, int N, int K, OutY y, int32_t* acc_out,
                            hipStream_t stream) {
   bool done = false;
   if (plan.path == W4Path::Stream) {
@@ -1262,19 +1262,19 @@ const char* w4a8_kernel_name(int64_t M, int64_t K, bool float_scale) {
 template <bool FS, int G, typename ST>
 static void launch_decode(int mr, dim3 grid, dim3 block, hipStream_t stream, const int8_t* qx,
                           const float* sx, const uint4* pk, const ST* iscale,
-                          const float* fscale, float inv_alpha, int M, int N, float* y,
+                          const float* fscale, float inv_alpha, int M, int N, OutY y,
                           int32_t* acc_out) {
-  const float* nx = nullptr;
+  const void* nx = nullptr;
   int8_t* nq = nullptr;
   float* ns = nullptr;
   switch (mr) {
-    case 1: hipLaunchKernelGGL((k_w4a8_decode<FS, kDecodeW, decode_depth(1), G, 1, ST, false>), grid, block, 0, stream,
+    case 1: hipLaunchKernelGGL((k_w4a8_decode<FS, kDecodeW, decode_depth(1), G, 1, ST, false, kF32>), grid, block, 0, stream,
                                qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out, nx, 0, nq, ns); break;
-    case 2: hipLaunchKernelGGL((k_w4a8_decode<FS, kDecodeW, decode_depth(2), G, 2, ST, false>), grid, block, 0, stream,
+    case 2: hipLaunchKernelGGL((k_w4a8_decode<FS, kDecodeW, decode_depth(2), G, 2, ST, false, kF32>), grid, block, 0, stream,
                                qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out, nx, 0, nq, ns); break;
-    case 3: hipLaunchKernelGGL((k_w4a8_decode<FS, kDecodeW, decode_depth(3), G, 3, ST, false>), grid, block, 0, stream,
+    case 3: hipLaunchKernelGGL((k_w4a8_decode<FS, kDecodeW, decode_depth(3), G, 3, ST, false, kF32>), grid, block, 0, stream,
                                qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out, nx, 0, nq, ns); break;
-    default: hipLaunchKernelGGL((k_w4a8_decode<FS, kDecodeW, decode_depth(4), G, 4, ST, false>), grid, block, 0, stream,
+    default: hipLaunchKernelGGL((k_w4a8_decode<FS, kDecodeW, decode_depth(4), G, 4, ST, false, kF32>), grid, block, 0, stream,
                                 qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out, nx, 0, nq, ns); break;
   }
 }
@@ -1282,7 +1282,7 @@ static void launch_decode(int mr, dim3 grid, dim3 block, hipStream_t stream, con
 template <bool FS, typename ST>
 static void launch_w4a8_t(const int8_t* qx, const float* sx, const uint8_t* packed,
                           const ST* iscale, const float* fscale, float inv_alpha, int M, int N,
-                          int K, float* y, int32_t* acc_out, hipStream_t stream) {
+                          int K, OutY y, int32_t* acc_out, hipStream_t stream) {
   const W4Plan plan = plan_w4a8(M, K, FS);
   if (FS) acc_out = nullptr;
   if (plan.path == W4Path::Decode) {
@@ -1307,7 +1307,7 @@ static void launch_w4a8_t(const int8_t* qx, const float* sx, const uint8_t* pack
 
 hipError_t launch_w4a8(bool float_scale, const int8_t* qx, const float* sx, const uint8_t* packed,
                        const void* iscale, int iscale_bytes, const float* fscale, int alpha,
-                       int64_t M64, int64_t N64, int64_t K64, float* y, int32_t* acc_out,
+                       int64_t M64, int64_t N64, int64_t K64, OutY y, int32_t* acc_out,
                        hipStream_t stream) {
   const int M = (int)M64, N = (int)N64, K = (int)K64;
   const float inv_alpha = 1.0f / (float)alpha;   // exact: alpha = 2^n
@@ -1328,50 +1328,63 @@ hipError_t launch_w4a8(bool float_scale, const int8_t* qx, const float* sx, cons
 
 // Quantize + GEMM in one launch for M <= 4 on the decode path (the decode
 // kernel quantizes the fp32 rows itself); otherwise the quantizer and the GEMM.
-template <typename ST>
-static void launch_linear_fused(const float* x, int ldx, const uint8_t* packed, const ST* iscale,
+template <int IT, typename ST>
+static void launch_linear_fused(const void* x, int ldx, const uint8_t* packed, const ST* iscale,
                                 float inv_alpha, int M, int N, int K, int8_t* q_out,
-                                float* s_out, float* y, hipStream_t stream) {
+                                float* s_out, OutY y, hipStream_t stream) {
   const int T = N / 16;
   const dim3 grid((T + kDecodeW - 1) / kDecodeW), block(kDecodeW * kWave);
   const uint4* pk = reinterpret_cast<const uint4*>(packed);
   if (K / kGroup == 32)
-    hipLaunchKernelGGL((k_w4a8_decode<false, kDecodeW, decode_depth(1), 32, 1, ST, true>), grid,
+    hipLaunchKernelGGL((k_w4a8_decode<false, kDecodeW, decode_depth(1), 32, 1, ST, true, IT>), grid,
                        block, 0, stream, nullptr, nullptr, pk, iscale, nullptr, inv_alpha, M, N,
                        y, nullptr, x, ldx, q_out, s_out);
   else
-    hipLaunchKernelGGL((k_w4a8_decode<false, kDecodeW, decode_depth(1), 16, 1, ST, true>), grid,
+    hipLaunchKernelGGL((k_w4a8_decode<false, kDecodeW, decode_depth(1), 16, 1, ST, true, IT>), grid,
                        block, 0, stream, nullptr, nullptr, pk, iscale, nullptr, inv_alpha, M, N,
                        y, nullptr, x, ldx, q_out, s_out);
 }
 
-bool w4a8_linear_fused(int64_t M, int64_t K, const float* x, int64_t ldx) {
+bool w4a8_linear_fused(int64_t M, int64_t K, const void* x, int64_t ldx) {
   const int64_t G = K / kGroup;
   return M <= 4 && (G == 16 || G == 32) && (reinterpret_cast<uintptr_t>(x) & 15u) == 0 &&
          ldx % 4 == 0 && ldx <= (1ll << 28);
 }
 
-hipError_t launch_w4a8_linear(const float* x, int64_t ldx, const uint8_t* packed,
+template <int IT>
+static void launch_linear_fused_st(const void* x, int ld, const uint8_t* packed, const void* iscale,
+                                   int iscale_bytes, float inv_alpha, int M, int N, int K,
+                                   int8_t* q_out, float* s_out, OutY y, hipStream_t stream) {
+  if (iscale_bytes == 4)
+    launch_linear_fused<IT>(x, ld, packed, static_cast<const int32_t*>(iscale), inv_alpha, M, N, K,
+                            q_out, s_out, y, stream);
+  else if (iscale_bytes == 2)
+    launch_linear_fused<IT>(x, ld, packed, static_cast<const uint16_t*>(iscale), inv_alpha, M, N, K,
+                            q_out, s_out, y, stream);
+  else
+    launch_linear_fused<IT>(x, ld, packed, static_cast<const uint8_t*>(iscale), inv_alpha, M, N, K,
+                            q_out, s_out, y, stream);
+}
+
+hipError_t launch_w4a8_linear(const void* x, int x_type, int64_t ldx, const uint8_t* packed,
                               const void* iscale, int iscale_bytes, int alpha, int64_t M64,
-                              int64_t N64, int64_t K64, int8_t* q_out, float* s_out, float* y,
+                              int64_t N64, int64_t K64, int8_t* q_out, float* s_out, OutY y,
                               hipStream_t stream) {
   if (!w4a8_linear_fused(M64, K64, x, ldx)) {
-    hipError_t e = launch_quant_rows(x, M64, K64, ldx, false, q_out, s_out, nullptr, nullptr, stream);
+    hipError_t e = launch_quant_rows(x, x_type, M64, K64, ldx, false, q_out, s_out, nullptr,
+                                     nullptr, stream);
     if (e != hipSuccess) return e;
     return launch_w4a8(false, q_out, s_out, packed, iscale, iscale_bytes, nullptr, alpha, M64, N64,
                        K64, y, nullptr, stream);
   }
   const int M = (int)M64, N = (int)N64, K = (int)K64, ld = (int)ldx;
   const float inv_alpha = 1.0f / (float)alpha;   // exact: alpha = 2^n
-  if (iscale_bytes == 4)
-    launch_linear_fused(x, ld, packed, static_cast<const int32_t*>(iscale), inv_alpha, M, N, K,
-                        q_out, s_out, y, stream);
-  else if (iscale_bytes == 2)
-    launch_linear_fused(x, ld, packed, static_cast<const uint16_t*>(iscale), inv_alpha, M, N, K,
-                        q_out, s_out, y, stream);
+  if (x_type == kF16)
+    launch_linear_fused_st<kF16>(x, ld, packed, iscale, iscale_bytes, inv_alpha, M, N, K, q_out, s_out, y, stream);
+  else if (x_type == kBF16)
+    launch_linear_fused_st<kBF16>(x, ld, packed, iscale, iscale_bytes, inv_alpha, M, N, K, q_out, s_out, y, stream);
   else
-    launch_linear_fused(x, ld, packed, static_cast<const uint8_t*>(iscale), inv_alpha, M, N, K,
-                        q_out, s_out, y, stream);
+    launch_linear_fused_st<kF32>(x, ld, packed, iscale, iscale_bytes, inv_alpha, M, N, K, q_out, s_out, y, stream);
   return hipGetLastError();
 }
 
@@ -1385,13 +1398,13 @@ hipError_t launch_w8a8_zp(const uint8_t* qx, const float* sx, const int32_t* zx,
   constexpr int NW = kW8Waves;
   if (G == 32)
     hipLaunchKernelGGL((k_w8a8_zp<9, 32, NW>), dim3(tiles), dim3(NW * 64), 0, stream, qx, sx, zx,
-                       rowsum_x, qw, sw, zw, colsum_w, M, N, K, y, acc_out);
+                       rowsum_x, qw, sw, zw, colsum_w, M, N, K, OutY{y, kF32}, acc_out);
   else if (G == 16)
     hipLaunchKernelGGL((k_w8a8_zp<9, 16, NW>), dim3(tiles), dim3(NW * 64), 0, stream, qx, sx, zx,
-                       rowsum_x, qw, sw, zw, colsum_w, M, N, K, y, acc_out);
+                       rowsum_x, qw, sw, zw, colsum_w, M, N, K, OutY{y, kF32}, acc_out);
   else
     hipLaunchKernelGGL((k_w8a8_zp<9, 0, NW>), dim3(tiles), dim3(NW * 64), 0, stream, qx, sx, zx,
-                       rowsum_x, qw, sw, zw, colsum_w, M, N, K, y, acc_out);
+                       rowsum_x, qw, sw, zw, colsum_w, M, N, K, OutY{y, kF32}, acc_out);
   return hipGetLastError();
 }
 

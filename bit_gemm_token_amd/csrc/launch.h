@@ -5,10 +5,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "device_common.h"
+
 namespace bgt {
 
-hipError_t launch_quant_rows(const float* x, int64_t rows, int64_t cols, int64_t ld, bool asym,
-                             void* q, float* scale, int32_t* zero, int32_t* rowsum,
+// x: rows x cols activations of element type x_type (kF32, kF16, kBF16)
+hipError_t launch_quant_rows(const void* x, int x_type, int64_t rows, int64_t cols, int64_t ld,
+                             bool asym, void* q, float* scale, int32_t* zero, int32_t* rowsum,
                              hipStream_t stream);
 
 // Group quantization + packing; also leaves min(positive s) and max(s) as float
@@ -23,17 +26,18 @@ hipError_t launch_integer_scales(const float* fscale, int64_t count, int alpha, 
 // 2: uint16, 1: uint8); ignored (and fscale used) when float_scale is set.
 hipError_t launch_w4a8(bool float_scale, const int8_t* qx, const float* sx, const uint8_t* packed,
                        const void* iscale, int iscale_bytes, const float* fscale, int alpha,
-                       int64_t M, int64_t N, int64_t K, float* y, int32_t* acc_out,
+                       int64_t M, int64_t N, int64_t K, OutY y, int32_t* acc_out,
                        hipStream_t stream);
 
-// per-token quantization of x (M x K fp32, leading dimension ldx) into q_out /
+// per-token quantization of x (M x K of element type x_type, leading dimension
+// ldx) into q_out /
 // s_out, then the integer-scale GEMM into y; one launch when
 // w4a8_linear_fused() holds (M <= 4, K/128 in {16, 32}, x 16-byte aligned,
 // ldx % 4 == 0), else the quantizer and the GEMM.
-bool w4a8_linear_fused(int64_t M, int64_t K, const float* x, int64_t ldx);
-hipError_t launch_w4a8_linear(const float* x, int64_t ldx, const uint8_t* packed,
+bool w4a8_linear_fused(int64_t M, int64_t K, const void* x, int64_t ldx);
+hipError_t launch_w4a8_linear(const void* x, int x_type, int64_t ldx, const uint8_t* packed,
                               const void* iscale, int iscale_bytes, int alpha, int64_t M,
-                              int64_t N, int64_t K, int8_t* q_out, float* s_out, float* y,
+                              int64_t N, int64_t K, int8_t* q_out, float* s_out, OutY y,
                               hipStream_t stream);
 
 // narrow (K/128) x N integer scales to 2-byte or 1-byte elements (values must fit)

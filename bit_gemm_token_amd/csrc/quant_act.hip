@@ -67,13 +67,13 @@ __device__ __forceinline__ int quant_code(float x, float s, int z) {
 }
 
 // Vector path: cols % 16 == 0, ld % 4 == 0, x and q 16-byte aligned.
-template <bool ASYM>
+template <bool ASYM, int IT>
 __global__ __launch_bounds__(kQThreads) void k_quant_rows_vec(
-    const float* __restrict__ x, int64_t cols, int64_t ld, uint8_t* __restrict__ q,
+    const void* __restrict__ x, int64_t cols, int64_t ld, uint8_t* __restrict__ q,
     float* __restrict__ scale, int32_t* __restrict__ zero, int32_t* __restrict__ rowsum) {
   __shared__ float lds[2 * kQWaves];
   const int64_t row = blockIdx.x;
-  const float4* xr = reinterpret_cast<const float4*>(x + row * ld);
+  const int64_t xr = row * ld / 4;                   // row start, in 4-element units
   uint32_t* qr = reinterpret_cast<uint32_t*>(q + row * cols);
   const int64_t nvec = cols / 4;
   const int t = threadIdx.x;
@@ -84,7 +84,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_rows_vec(
   for (int u = 0; u < kVecPerThread; ++u) {
     const int64_t v = t + (int64_t)u * kQThreads;
     if (v < nvec) {
-      float4 f = xr[v];
+      float4 f = load_x4<IT>(x, xr + v);
       cache[u] = f;
       if (ASYM) {
         st.a = fmaxf(st.a, fmaxf(fmaxf(f.x, f.y), fmaxf(f.z, f.w)));
@@ -95,7 +95,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_rows_vec(
     }
   }
   for (int64_t v = t + (int64_t)kVecPerThread * kQThreads; v < nvec; v += kQThreads) {
-    float4 f = xr[v];
+    float4 f = load_x4<IT>(x, xr + v);
     if (ASYM) {
       st.a = fmaxf(st.a, fmaxf(fmaxf(f.x, f.y), fmaxf(f.z, f.w)));
       st.b = fminf(st.b, fminf(fminf(f.x, f.y), fminf(f.z, f.w)));
@@ -127,7 +127,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_rows_vec(
     const int64_t v = t + (int64_t)u * kQThreads;
     if (v < nvec) emit(v, cache[u]);
   }
-  for (int64_t v = t + (int64_t)kVecPerThread * kQThreads; v < nvec; v += kQThreads) emit(v, xr[v]);
+  for (int64_t v = t + (int64_t)kVecPerThread * kQThreads; v < nvec; v += kQThreads) emit(v, load_x4<IT>(x, xr + v));
 
   if (rowsum != nullptr || ASYM) {
     const int total = block_sum(sum, reinterpret_cast<int*>(lds));
@@ -142,18 +142,18 @@ __global__ __launch_bounds__(kQThreads) void k_quant_rows_vec(
 }
 
 // Scalar path: any cols, any ld, any alignment.
-template <bool ASYM>
+template <bool ASYM, int IT>
 __global__ __launch_bounds__(kQThreads) void k_quant_rows_scalar(
-    const float* __restrict__ x, int64_t cols, int64_t ld, uint8_t* __restrict__ q,
+    const void* __restrict__ x, int64_t cols, int64_t ld, uint8_t* __restrict__ q,
     float* __restrict__ scale, int32_t* __restrict__ zero, int32_t* __restrict__ rowsum) {
   __shared__ float lds[2 * kQWaves];
   const int64_t row = blockIdx.x;
-  const float* xr = x + row * ld;
+  const int64_t xr = row * ld;
   uint8_t* qr = q + row * cols;
   const int t = threadIdx.x;
   RowStat<ASYM> st{ASYM ? -INFINITY : 0.0f, ASYM ? INFINITY : 0.0f};
   for (int64_t k = t; k < cols; k += kQThreads) {
-    const float f = xr[k];
+    const float f = load_x1<IT>(x, xr + k);
     if (ASYM) { st.a = fmaxf(st.a, f); st.b = fminf(st.b, f); }
     else st.a = fmaxf(st.a, fabsf(f));
   }
@@ -168,7 +168,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_rows_scalar(
   }
   int sum = 0;
   for (int64_t k = t; k < cols; k += kQThreads) {
-    const int c = quant_code<ASYM>(xr[k], s, z);
+    const int c = quant_code<ASYM>(load_x1<IT>(x, xr + k), s, z);
     sum += c;
     qr[k] = (uint8_t)(c & 0xFF);
   }
@@ -182,21 +182,32 @@ __global__ __launch_bounds__(kQThreads) void k_quant_rows_scalar(
   }
 }
 
-hipError_t launch_quant_rows(const float* x, int64_t rows, int64_t cols, int64_t ld, bool asym,
-                             void* q, float* scale, int32_t* zero, int32_t* rowsum,
+template <int IT>
+static void launch_quant_rows_t(bool vec, bool asym, dim3 grid, dim3 block, hipStream_t stream,
+                                const void* x, int64_t cols, int64_t ld, uint8_t* qb, float* scale,
+                                int32_t* zero, int32_t* rowsum) {
+  if (vec) {
+    if (asym) hipLaunchKernelGGL((k_quant_rows_vec<true, IT>), grid, block, 0, stream, x, cols, ld, qb, scale, zero, rowsum);
+    else hipLaunchKernelGGL((k_quant_rows_vec<false, IT>), grid, block, 0, stream, x, cols, ld, qb, scale, zero, rowsum);
+  } else {
+    if (asym) hipLaunchKernelGGL((k_quant_rows_scalar<true, IT>), grid, block, 0, stream, x, cols, ld, qb, scale, zero, rowsum);
+    else hipLaunchKernelGGL((k_quant_rows_scalar<false, IT>), grid, block, 0, stream, x, cols, ld, qb, scale, zero, rowsum);
+  }
+}
+
+hipError_t launch_quant_rows(const void* x, int x_type, int64_t rows, int64_t cols, int64_t ld,
+                             bool asym, void* q, float* scale, int32_t* zero, int32_t* rowsum,
                              hipStream_t stream) {
+  // vector path: 4-element loads (16 bytes fp32, 8 bytes fp16 / bf16) and
+  // packed 4-byte code stores
   const bool vec = (cols % 16 == 0) && (ld % 4 == 0) &&
                    (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
                    (reinterpret_cast<uintptr_t>(q) % 16 == 0);
   dim3 grid((unsigned)rows), block(kQThreads);
   uint8_t* qb = static_cast<uint8_t*>(q);
-  if (vec) {
-    if (asym) hipLaunchKernelGGL(k_quant_rows_vec<true>, grid, block, 0, stream, x, cols, ld, qb, scale, zero, rowsum);
-    else hipLaunchKernelGGL(k_quant_rows_vec<false>, grid, block, 0, stream, x, cols, ld, qb, scale, zero, rowsum);
-  } else {
-    if (asym) hipLaunchKernelGGL(k_quant_rows_scalar<true>, grid, block, 0, stream, x, cols, ld, qb, scale, zero, rowsum);
-    else hipLaunchKernelGGL(k_quant_rows_scalar<false>, grid, block, 0, stream, x, cols, ld, qb, scale, zero, rowsum);
-  }
+  if (x_type == kF16) launch_quant_rows_t<kF16>(vec, asym, grid, block, stream, x, cols, ld, qb, scale, zero, rowsum);
+  else if (x_type == kBF16) launch_quant_rows_t<kBF16>(vec, asym, grid, block, stream, x, cols, ld, qb, scale, zero, rowsum);
+  else launch_quant_rows_t<kF32>(vec, asym, grid, block, stream, x, cols, ld, qb, scale, zero, rowsum);
   return hipGetLastError();
 }
 

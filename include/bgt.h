@@ -41,9 +41,17 @@ extern "C" {
 #define BGT_ERR_SHAPE             -2   /* a size is out of range or not a multiple     */
 #define BGT_ERR_ALIGN             -3   /* a pointer or leading dimension is misaligned */
 #define BGT_ERR_ALPHA             -4   /* amplifier not a power of two in [1, 2^30]     */
-#define BGT_ERR_MODE              -5   /* unknown quantization mode                    */
+#define BGT_ERR_MODE              -5   /* unknown mode, element type or scale width    */
 #define BGT_ERR_HIP               -6   /* a HIP call failed                             */
 #define BGT_ERR_RANGE             -7   /* an integer scale does not fit its element     */
+
+/* Element types of activations (x) and outputs (y) in the _ex entry points
+ * and bgt_w4a8_linear_is: IEEE binary32, IEEE binary16, bfloat16. Every
+ * computation is in fp32 / int32; an fp16 or bf16 x is widened exactly, an
+ * fp16 or bf16 y is the fp32 result rounded once, to nearest even. */
+#define BGT_F32   0
+#define BGT_F16   1
+#define BGT_BF16  2
 
 /* Quantization modes of bgt_quantize_act. */
 #define BGT_QUANT_SYM_I8   0
@@ -78,6 +86,15 @@ extern "C" {
  */
 int bgt_quantize_act(const float* x, int64_t rows, int64_t cols, int64_t ld, int mode,
                      void* q, float* scale, int32_t* zero, int32_t* rowsum, void* stream);
+
+/* bgt_quantize_act with x of element type x_type (BGT_F32, BGT_F16 or BGT_BF16;
+ * the activations of the [IS] page's models are FP16). fp16 / bf16 values are
+ * widened to fp32 exactly; everything else is bgt_quantize_act. The vector
+ * path needs x 16-byte aligned, ld % 4 == 0 and cols % 16 == 0. Unknown
+ * x_type: BGT_ERR_MODE. */
+int bgt_quantize_act_ex(const void* x, int x_type, int64_t rows, int64_t cols, int64_t ld,
+                        int mode, void* q, float* scale, int32_t* zero, int32_t* rowsum,
+                        void* stream);
 
 /*
  * bgt_pack_weights_int4 -- offline group-wise int4 weight quantization,
@@ -166,6 +183,13 @@ int bgt_w4a8_gemm_is_narrow(const int8_t* qx, const float* sx, const uint8_t* pa
                             const void* iscale, int width, int alpha, int64_t M, int64_t N,
                             int64_t K, float* y, int32_t* acc_out, void* stream);
 
+/* bgt_w4a8_gemm_is_narrow with y of element type y_type (BGT_F32, BGT_F16 or
+ * BGT_BF16): y_ij is the fp32 value of bgt_w4a8_gemm_is rounded once to the
+ * type (round to nearest even). acc_out is unchanged (int32). */
+int bgt_w4a8_gemm_is_ex(const int8_t* qx, const float* sx, const uint8_t* packed,
+                        const void* iscale, int width, int alpha, int64_t M, int64_t N, int64_t K,
+                        void* y, int y_type, int32_t* acc_out, void* stream);
+
 /*
  * bgt_w4a8_linear_is -- the whole decode-time linear layer from fp32
  * activations: per-token quantization of x exactly as bgt_quantize_act SYM
@@ -177,19 +201,20 @@ int bgt_w4a8_gemm_is_narrow(const int8_t* qx, const float* sx, const uint8_t* pa
  * the GEMM that [QB] §2.4.1 dynamic quantization invites); otherwise it is the
  * quantizer followed by the GEMM. qx, sx and y are bit-identical either way.
  *
- *   x       M x K float32 (finite), leading dimension ldx >= K (elements).
+ *   x       M x K of element type x_type (BGT_F32, BGT_F16, BGT_BF16; finite),
+ *           leading dimension ldx >= K (elements).
  *   packed, iscale, width, alpha: as bgt_w4a8_gemm_is_narrow.
  *   qx      M x K int8 (dense), sx [M] float32: written (the quantized activations).
- *   y       M x N float32.
+ *   y       M x N of element type y_type (fp32 result rounded once).
  * Requirements: those of bgt_w4a8_gemm_is_narrow; qx 16-byte aligned.
  */
-int bgt_w4a8_linear_is(const float* x, int64_t ldx, const uint8_t* packed, const void* iscale,
-                       int width, int alpha, int64_t M, int64_t N, int64_t K, int8_t* qx,
-                       float* sx, float* y, void* stream);
+int bgt_w4a8_linear_is(const void* x, int x_type, int64_t ldx, const uint8_t* packed,
+                       const void* iscale, int width, int alpha, int64_t M, int64_t N, int64_t K,
+                       int8_t* qx, float* sx, void* y, int y_type, void* stream);
 
 /* Diagnostics: 1 when bgt_w4a8_linear_is runs as one launch for these
  * arguments (M, K, x, ldx), 0 when it runs the quantizer and the GEMM. */
-int bgt_w4a8_linear_fused(int64_t M, int64_t K, const float* x, int64_t ldx);
+int bgt_w4a8_linear_fused(int64_t M, int64_t K, const void* x, int64_t ldx);
 
 /*
  * bgt_w4a8_gemm_fs -- the float-scale control ([IS] 方法 Fig. 3(b)): every
@@ -203,6 +228,11 @@ int bgt_w4a8_linear_fused(int64_t M, int64_t K, const float* x, int64_t ldx);
 int bgt_w4a8_gemm_fs(const int8_t* qx, const float* sx, const uint8_t* packed,
                      const float* fscale, int64_t M, int64_t N, int64_t K, float* y,
                      void* stream);
+
+/* bgt_w4a8_gemm_fs with y of element type y_type (fp32 result rounded once). */
+int bgt_w4a8_gemm_fs_ex(const int8_t* qx, const float* sx, const uint8_t* packed,
+                        const float* fscale, int64_t M, int64_t N, int64_t K, void* y, int y_type,
+                        void* stream);
 
 /*
  * bgt_w8a8_gemm_zp -- the asymmetric W8A8 control through the zero-point
@@ -227,7 +257,8 @@ int bgt_w8a8_gemm_zp(const uint8_t* qx, const float* sx, const int32_t* zx,
 const char* bgt_status_string(int status);
 
 /* ABI version of this header (major*100 + minor): 101 adds the narrow
- * integer-scale entry points, 102 the fused linear layer. */
+ * integer-scale entry points, 102 the fused linear layer, 103 fp16 / bf16
+ * activation and output types. */
 int bgt_abi_version(void);
 
 /* Diagnostics: name of the GEMM kernel that bgt_w4a8_gemm_is (float_scale = 0)

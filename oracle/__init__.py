@@ -49,6 +49,7 @@ def _load():
         lib.orc_amplifier_log2.argtypes = [P, I64, I]
         lib.orc_amplifier_log2.restype = I
         lib.orc_integer_scales.argtypes = [P, I64, I, P]
+        lib.orc_f32_to_bf16.argtypes = [P, I64, P]
         lib.orc_narrow_iscale.argtypes = [P, I64, I, P]
         lib.orc_narrow_iscale.restype = I64
         lib.orc_weight_mse_is_fs.argtypes = [P, P, P, I, I64, I64, I64, P, P]
@@ -118,6 +119,19 @@ def integer_scales(fscale, alpha: int):
     out = np.empty(f.shape, np.int32)
     _load().orc_integer_scales(_p(f), f.size, int(alpha), _p(out))
     return out
+
+
+def f32_to_bf16_bits(x):
+    """bfloat16 bit patterns (uint16) of float32 values, round to nearest even."""
+    x = _c(x, np.float32)
+    out = np.empty(x.shape, np.uint16)
+    _load().orc_f32_to_bf16(_p(x), x.size, _p(out))
+    return out
+
+
+def bf16_bits_to_f32(b):
+    """float32 values of bfloat16 bit patterns (exact: the low 16 bits are zero)."""
+    return (np.ascontiguousarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
 def narrow_iscale(iscale, width: int):

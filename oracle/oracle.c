@@ -201,6 +201,29 @@ EXPORT int64_t orc_narrow_iscale(const int32_t* iscale, int64_t count, int width
 }
 
 /* ------------------------------------------------------------------------
+ * fp32 -> bfloat16, round to nearest, ties to even (the bfloat16 format keeps
+ * the sign, the 8 exponent bits and the top 7 fraction bits of binary32).
+ * Written from that definition: the dropped 16 bits decide the rounding; a
+ * NaN stays a (quiet) NaN. Used for the fp16 / bf16 output types, where the
+ * output is the fp32 result rounded once.
+ * ---------------------------------------------------------------------- */
+EXPORT void orc_f32_to_bf16(const float* in, int64_t n, uint16_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        uint32_t b;
+        memcpy(&b, &in[i], 4);
+        if ((b & 0x7F800000u) == 0x7F800000u && (b & 0x007FFFFFu)) {   /* NaN */
+            out[i] = (uint16_t)((b >> 16) | 0x0040u);
+            continue;
+        }
+        const uint32_t keep = b >> 16, drop = b & 0xFFFFu;
+        uint32_t r = keep;
+        if (drop > 0x8000u || (drop == 0x8000u && (keep & 1u))) r = keep + 1u;
+        out[i] = (uint16_t)r;
+    }
+}
+
+/* ------------------------------------------------------------------------
  * Weight MSE between the integer-scale and the float-scale dequantized
  * weights ([IS] 方法, Fig. 4(c): "weight MSE between integer and float
  * scales under different amplifiers"). With codes q (K x N), float scales s

@@ -37,7 +37,7 @@ def test_status_strings(L):
     assert bgt.status_string(0) == "ok"
     for st in (-1, -2, -3, -4, -5, -6, -7, 1):
         assert "error" in bgt.status_string(st) or "warning" in bgt.status_string(st)
-    assert L.bgt_abi_version() == 102
+    assert L.bgt_abi_version() == 103
 
 
 def test_quantize_act_validation(L):
@@ -112,13 +112,16 @@ def test_gemm_is_narrow_validation(L):
 def test_linear_is_validation(L):
     g = L.bgt_w4a8_linear_is
 
-    def call(x=FAKE, ldx=256, isc=FAKE, width=4, alpha=1024, M=4, N=64, K=256, qx=FAKE, sx=FAKE, y=FAKE):
-        return g(x, ldx, FAKE, isc, width, alpha, M, N, K, qx, sx, y, None)
+    def call(x=FAKE, ldx=256, isc=FAKE, width=4, alpha=1024, M=4, N=64, K=256, qx=FAKE, sx=FAKE, y=FAKE,
+             xt=0, yt=0):
+        return g(x, xt, ldx, FAKE, isc, width, alpha, M, N, K, qx, sx, y, yt, None)
 
     assert call(x=None) == bgt.BGT_ERR_NULL
     assert call(qx=None) == bgt.BGT_ERR_NULL
     assert call(sx=None) == bgt.BGT_ERR_NULL
     assert call(width=3) == bgt.BGT_ERR_MODE
+    assert call(xt=3) == bgt.BGT_ERR_MODE
+    assert call(yt=-1) == bgt.BGT_ERR_MODE
     assert call(ldx=255) == bgt.BGT_ERR_SHAPE
     assert call(K=200, ldx=300) == bgt.BGT_ERR_SHAPE
     assert call(alpha=12) == bgt.BGT_ERR_ALPHA
@@ -131,6 +134,19 @@ def test_linear_is_validation(L):
     assert f(4, 1152, FAKE, 1152) == 0          # not 16 or 32 groups
     assert f(4, 4096, MIS, 4096) == 0           # x not 16-byte aligned
     assert f(4, 4096, FAKE, 4097) == 0          # row stride not a multiple of 4
+
+
+def test_typed_entry_points_validation(L):
+    q = L.bgt_quantize_act_ex
+    assert q(FAKE, 3, 4, 64, 64, 0, FAKE, FAKE, None, None, None) == bgt.BGT_ERR_MODE
+    assert q(None, 1, 4, 64, 64, 0, FAKE, FAKE, None, None, None) == bgt.BGT_ERR_NULL
+    assert q(FAKE, 2, 4, 64, 32, 0, FAKE, FAKE, None, None, None) == bgt.BGT_ERR_SHAPE
+    g = L.bgt_w4a8_gemm_is_ex
+    assert g(FAKE, FAKE, FAKE, FAKE, 4, 1024, 16, 64, 256, FAKE, 5, None, None) == bgt.BGT_ERR_MODE
+    assert g(FAKE, FAKE, FAKE, FAKE, 4, 1024, 16, 64, 256, MIS, 1, None, None) == bgt.BGT_ERR_ALIGN
+    f = L.bgt_w4a8_gemm_fs_ex
+    assert f(FAKE, FAKE, FAKE, FAKE, 16, 64, 256, FAKE, 7, None) == bgt.BGT_ERR_MODE
+    assert f(FAKE, FAKE, FAKE, FAKE, 16, 63, 256, FAKE, 2, None) == bgt.BGT_ERR_SHAPE
 
 
 def test_narrow_iscale_validation(L):

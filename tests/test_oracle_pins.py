@@ -350,6 +350,36 @@ def test_scale_table_fixture_relations():
         assert wide == 0 and mx <= 255
 
 
+# ----------------------------------------------------- bf16 output rounding
+
+def test_bf16_ties_to_even_and_exact_values(orc):
+    v = np.array([1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 1 + 2 ** -8 + 2 ** -20,
+                  2.0 ** -130, 0.0, -0.0], np.float32)
+    got = orc.f32_to_bf16_bits(v)
+    assert [int(b) for b in got] == [0x3F80, 0x3F80, 0x3F82, 0xBF80, 0x3F81, 0x0008, 0x0000, 0x8000]
+    # values already representable in bfloat16 are unchanged
+    g = np.random.default_rng(3)
+    b = g.integers(0, 0x7F80, size=5000).astype(np.uint16)
+    b = np.concatenate([b, b | 0x8000]).astype(np.uint16)
+    assert np.array_equal(orc.f32_to_bf16_bits(orc.bf16_bits_to_f32(b)), b)
+
+
+def test_bf16_half_ulp_bound_monotone_overflow_nan(orc):
+    g = np.random.default_rng(4)
+    x = (g.standard_normal(20000) * 10.0 ** g.uniform(-30, 30, 20000)).astype(np.float32)
+    r = orc.bf16_bits_to_f32(orc.f32_to_bf16_bits(x)).astype(np.float64)
+    xd = x.astype(np.float64)
+    normal = np.abs(xd) >= 2.0 ** -126
+    assert np.all(np.abs(r - xd)[normal] <= np.abs(xd)[normal] * 2.0 ** -8)   # half an ulp of 8 bits
+    xs = np.sort(x)
+    rs = orc.bf16_bits_to_f32(orc.f32_to_bf16_bits(xs))
+    assert np.all(np.diff(rs.astype(np.float64)) >= 0)
+    big = np.array([3.4e38, -3.4e38, np.float32(np.finfo(np.float32).max)], np.float32)
+    assert [int(b) for b in orc.f32_to_bf16_bits(big)] == [0x7F80, 0xFF80, 0x7F80]
+    nan = orc.f32_to_bf16_bits(np.array([np.nan], np.float32))
+    assert np.isnan(orc.bf16_bits_to_f32(nan)[0])
+
+
 # -------------------------------------------------------------------- O3 IS GEMM
 
 def _tiny_case(seed, M, K, N, iscale_hi=300):
