@@ -46,6 +46,9 @@ def _load():
         lib.orc_quant_sym_i8.argtypes = [P, I64, I64, I64, P, P]
         lib.orc_quant_asym_u8.argtypes = [P, I64, I64, I64, P, P, P, P]
         lib.orc_group_quant_int4.argtypes = [P, I64, I64, I64, P, P]
+        lib.orc_group_quant_int8.argtypes = [P, I64, I64, I64, P, P]
+        lib.orc_layout_int8.argtypes = [P, I64, I64, P]
+        lib.orc_unlayout_int8.argtypes = [P, I64, I64, P]
         lib.orc_amplifier_log2.argtypes = [P, I64, I]
         lib.orc_amplifier_log2.restype = I
         lib.orc_integer_scales.argtypes = [P, I64, I, P]
@@ -106,6 +109,43 @@ def group_quant_int4(w, g: int = 128):
     fscale = np.empty((K // g, N), np.float32)
     _load().orc_group_quant_int4(_p(w), K, N, g, _p(codes), _p(fscale))
     return codes, fscale
+
+
+def group_quant_int8(w, g: int = 128):
+    """Group-wise int8 codes (K x N int8, [-127, 127]) and float scales ((K/g) x N) of W."""
+    w = _c(w, np.float32)
+    K, N = w.shape
+    codes = np.empty((K, N), np.int8)
+    fscale = np.empty((K // g, N), np.float32)
+    _load().orc_group_quant_int8(_p(w), K, N, g, _p(codes), _p(fscale))
+    return codes, fscale
+
+
+def layout_int8(codes):
+    """K x N int8 codes in the int8 fragment layout (N*K bytes)."""
+    codes = _c(codes, np.int8)
+    K, N = codes.shape
+    out = np.empty(N * K, np.int8)
+    _load().orc_layout_int8(_p(codes), K, N, _p(out))
+    return out
+
+
+def unlayout_int8(qw, K: int, N: int):
+    qw = _c(qw, np.int8)
+    codes = np.empty((K, N), np.int8)
+    _load().orc_unlayout_int8(_p(qw), K, N, _p(codes))
+    return codes
+
+
+def pack_weights_int8(w, g: int = 128, alpha: int = 0):
+    """Offline path of the fine-grained W8A8 integer-scale layer: codes (K x N),
+    their int8 fragment layout qw, float and integer scales, and alpha
+    (0 = the amplifier search)."""
+    codes, fscale = group_quant_int8(w, g)
+    if alpha == 0:
+        alpha = 1 << amplifier_log2(fscale)
+    return {"codes": codes, "qw": layout_int8(codes), "fscale": fscale,
+            "iscale": integer_scales(fscale, alpha), "alpha": alpha}
 
 
 def amplifier_log2(fscale, max_log2: int = 30) -> int:
@@ -216,6 +256,13 @@ def w4a8_gemm_is(qx, sx, codes, iscale, alpha: int, g: int = 128, rows=None, col
     ov = _load().orc_w4a8_gemm_is(_p(qx), _p(sx), _p(codes), _p(iscale), int(alpha), M, N, K, g,
                                   _p(r), nr, _p(c), nc, _p(A), _p(y))
     return A, y, int(ov)
+
+
+def w8a8_gemm_is(qx, sx, codes, iscale, alpha: int, g: int = 128, rows=None, cols=None):
+    """Fine-grained W8A8 GEMM with the integer-scale epilogue: the definition of
+    O3 with int8 weight codes in [-127, 127] (the epilogue does not depend on
+    the weight width). Returns (A int64, y float32, overflow count)."""
+    return w4a8_gemm_is(qx, sx, codes, iscale, alpha, g, rows, cols)
 
 
 def w4a8_gemm_fs(qx, sx, codes, fscale, g: int = 128, rows=None, cols=None):

@@ -20,7 +20,8 @@
  *        Quantization, Per-Channel, 矩阵乘法中的量化计算 (zero-point expansion).
  *   [IS] "Integer Scale: A Free Lunch for Faster Fine-grained Quantization of
  *        LLMs" summary page (dignews.cc): 動機 3.1-3.2, 方法 (Fig. 3 a/b/c, the
- *        amplifier search code, default amplifier), 實驗 5.1 Table 1.
+ *        amplifier search code, default amplifier), 實驗 5.1 Table 1, 5.4
+ *        (LLaMA-3 scheme: fine-grained W8A8 for the down projection).
  *   [EX] "extreme quantization LLMs" (apxml.com): data packing of sub-byte codes.
  *
  * Readings where the pages are silent or garbled (each also listed in the
@@ -119,8 +120,8 @@ EXPORT void orc_quant_asym_u8(const float* x, int64_t rows, int64_t cols, int64_
  * with q_max = 7.
  * w: K x N row-major. codes: K x N row-major int8. fscale: (K/g) x N.
  * ---------------------------------------------------------------------- */
-EXPORT void orc_group_quant_int4(const float* w, int64_t K, int64_t N, int64_t g,
-                                 int8_t* codes, float* fscale)
+static void group_quant_sym(const float* w, int64_t K, int64_t N, int64_t g, int qmax,
+                            int8_t* codes, float* fscale)
 {
     const int64_t G = K / g;
     #pragma omp parallel for schedule(static)
@@ -131,18 +132,33 @@ EXPORT void orc_group_quant_int4(const float* w, int64_t K, int64_t N, int64_t g
                 float v = fabsf(w[(l * g + r) * N + j]);
                 if (v > a) a = v;
             }
-            float sl = a / 7.0f;
+            float sl = a / (float)qmax;
             fscale[l * N + j] = sl;
             for (int64_t r = 0; r < g; ++r) {
                 int code = 0;
                 if (sl != 0.0f) {
                     float t = roundf(w[(l * g + r) * N + j] / sl);
-                    code = clampi((long)t, -7, 7);
+                    code = clampi((long)t, -qmax, qmax);
                 }
                 codes[(l * g + r) * N + j] = (int8_t)code;
             }
         }
     }
+}
+
+EXPORT void orc_group_quant_int4(const float* w, int64_t K, int64_t N, int64_t g,
+                                 int8_t* codes, float* fscale)
+{
+    group_quant_sym(w, K, N, g, 7, codes, fscale);
+}
+
+/* O2 with q_max = 127: group-wise symmetric int8 weights, the fine-grained
+ * W8A8 of the [IS] page's LLaMA-3 recipe (5.4 LLaMA-3 量化方案: 8-bit weights
+ * for the down projection, groups of 128); same closed forms as O1. */
+EXPORT void orc_group_quant_int8(const float* w, int64_t K, int64_t N, int64_t g,
+                                 int8_t* codes, float* fscale)
+{
+    group_quant_sym(w, K, N, g, 127, codes, fscale);
 }
 
 /* ------------------------------------------------------------------------
@@ -303,6 +319,32 @@ EXPORT void orc_unpack_int4(const uint8_t* packed, int64_t K, int64_t N, int8_t*
             int nib = high ? (packed[b] >> 4) & 0xF : packed[b] & 0xF;
             codes[k * N + j] = (int8_t)(nib >= 8 ? nib - 16 : nib);
         }
+}
+
+/* Int8 fragment layout of the fine-grained W8A8 weights (the byte formula
+ * stated with bgt_pack_weights_int8): for t = j/16, c = j%16, l = k/128,
+ * r = k%128, h = r/64, s = (r%64)/16, e = r%16,
+ *     byte(k, j) = (((t*G + l)*2 + h)*64 + 16*s + c)*16 + e.
+ * A pure permutation of the N*K codes; the inverse reads them back. */
+static int64_t layout8_byte(int64_t k, int64_t j, int64_t G)
+{
+    int64_t t = j / 16, c = j % 16, l = k / 128, r = k % 128;
+    int64_t h = r / 64, s = (r % 64) / 16, e = r % 16;
+    return (((t * G + l) * 2 + h) * 64 + 16 * s + c) * 16 + e;
+}
+
+EXPORT void orc_layout_int8(const int8_t* codes, int64_t K, int64_t N, int8_t* out)
+{
+    const int64_t G = K / 128;
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t j = 0; j < N; ++j) out[layout8_byte(k, j, G)] = codes[k * N + j];
+}
+
+EXPORT void orc_unlayout_int8(const int8_t* in, int64_t K, int64_t N, int8_t* codes)
+{
+    const int64_t G = K / 128;
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t j = 0; j < N; ++j) codes[k * N + j] = in[layout8_byte(k, j, G)];
 }
 
 /* ------------------------------------------------------------------------

@@ -593,3 +593,138 @@ def test_w8a8_approximates_matmul(orc):
     _, y, _ = orc.w8a8_gemm_zp(qx, sx, zx, rx, qw, sw, zw, cw)
     ref = x.astype(np.float64) @ w.astype(np.float64)
     assert np.linalg.norm(y - ref) / np.linalg.norm(ref) < 0.05
+
+
+# ------------------------------------------------- fine-grained W8A8 integer scale
+# [IS] 5.4 (the LLaMA-3 scheme): 8-bit group-wise weights for the down projection,
+# with the same integer-scale epilogue.
+
+def test_group_quant_int8_hand_group(orc):
+    # absmax 127 -> s = 1; ties away from zero; clip [-127, 127]
+    w = np.zeros((128, 16), np.float32)
+    w[:8, 0] = [127.0, 63.5, -63.5, 0.5, -0.49, -127.0, 126.6, 2.5]
+    w[:, 1] = np.linspace(-1, 1, 128)
+    codes, fs = orc.group_quant_int8(w, 128)
+    assert fs[0, 0] == 1.0
+    assert codes[:8, 0].tolist() == [127, 64, -64, 1, 0, -127, 127, 3]
+    assert fs[0, 2] == 0 and not codes[:, 2].any()          # all-zero group
+    assert codes[:, 1].min() == -127 and codes[:, 1].max() == 127
+    # the int4 quantizer on the same group differs (q_max 7): not a shared constant
+    c4, f4 = orc.group_quant_int4(w, 128)
+    assert f4[0, 0] == np.float32(127.0 / 7.0) and c4[:8, 0].max() == 7
+
+
+def test_group_quant_int8_bound_and_grouping(orc):
+    w = synth.weights(2, 384, 48, outlier_prob=0.01)
+    codes, fs = orc.group_quant_int8(w, 128)
+    for l in range(3):
+        blk = w[128 * l:128 * (l + 1)]
+        np.testing.assert_array_equal(fs[l], (np.abs(blk).max(axis=0) / np.float32(127)).astype(np.float32))
+        err = np.abs(blk.astype(np.float64) - fs[l].astype(np.float64) * codes[128 * l:128 * (l + 1)])
+        assert np.all(err <= fs[l] * (0.5 + 2.0 ** -20))
+        # the group's absmax element maps to +-127
+        assert np.all(np.abs(codes[128 * l:128 * (l + 1)]).max(axis=0) == 127)
+    assert codes.min() >= -127 and codes.max() <= 127
+
+
+def test_int8_layout_roundtrip_and_permutation(orc):
+    K, N = 384, 48
+    codes = synth.rng(11, 3).integers(-127, 128, size=(K, N)).astype(np.int8)
+    qw = orc.layout_int8(codes)
+    assert qw.size == N * K
+    np.testing.assert_array_equal(np.sort(qw), np.sort(codes.ravel()))
+    np.testing.assert_array_equal(orc.unlayout_int8(qw, K, N), codes)
+
+
+@pytest.mark.parametrize("k,j,byte", [
+    (0, 0, 0), (1, 0, 1), (15, 0, 15), (16, 0, 256), (0, 1, 16), (64, 0, 1024),
+    (128, 0, 2048), (0, 16, 4096), (100, 5, 1620), (255, 31, 8191),
+])
+def test_int8_layout_positions(orc, k, j, byte):
+    # K=256 (G=2), N=32 (2 column tiles): a single code 9 at (k, j)
+    K, N = 256, 32
+    codes = np.zeros((K, N), np.int8)
+    codes[k, j] = 9
+    qw = orc.layout_int8(codes)
+    assert np.flatnonzero(qw).tolist() == [byte]
+
+
+def test_w8is_brute_force_ungrouped(orc):
+    # full int8 weight range; distributivity against a per-k brute force
+    M, K, N = 3, 384, 4
+    g = synth.rng(12, 5)
+    qx = g.integers(-127, 128, size=(M, K)).astype(np.int8)
+    qw = g.integers(-127, 128, size=(K, N)).astype(np.int8)
+    isc = g.integers(0, 70, size=(K // 128, N)).astype(np.int32)
+    sx = g.uniform(0.001, 0.1, size=M).astype(np.float32)
+    A, _, ov = orc.w8a8_gemm_is(qx, sx, qw, isc, 1 << 14)
+    ref = np.zeros((M, N), np.int64)
+    for i in range(M):
+        for j in range(N):
+            ref[i, j] = sum(int(qx[i, k]) * int(qw[k, j]) * int(isc[k // 128, j]) for k in range(K))
+    np.testing.assert_array_equal(A, ref)
+    assert ov == 0
+
+
+def test_w8is_unit_scales_is_int_matmul_and_group_bound(orc):
+    g = synth.rng(13, 5)
+    qx = g.integers(-127, 128, size=(5, 512)).astype(np.int8)
+    qw = g.integers(-127, 128, size=(512, 20)).astype(np.int8)
+    A, _, _ = orc.w8a8_gemm_is(qx, np.ones(5, np.float32), qw, np.ones((4, 20), np.int32), 1)
+    np.testing.assert_array_equal(A, qx.astype(np.int64) @ qw.astype(np.int64))
+    # one group's |p| stays below 2^23 even at the extreme codes
+    ext = np.full((1, 128), -127, np.int8)
+    A1, _, _ = orc.w8a8_gemm_is(ext, np.ones(1, np.float32), np.full((128, 16), 127, np.int8),
+                                np.ones((1, 16), np.int32), 1)
+    assert A1[0, 0] == -128 * 127 * 127 and abs(A1[0, 0]) < 2 ** 23
+
+
+def test_w8is_overflow_flag(orc):
+    K, N = 1024, 2
+    qx = np.full((1, K), 127, np.int8)
+    qw = np.full((K, N), 127, np.int8)
+    isc = np.full((K // 128, N), 200, np.int32)
+    isc[:, 1] = 100
+    A, y, ov = orc.w8a8_gemm_is(qx, np.ones(1, np.float32), qw, isc, 1)
+    assert A[0, 0] == 8 * 128 * 127 * 127 * 200 and A[0, 0] >= 2 ** 31
+    assert A[0, 1] < 2 ** 31 and ov == 1
+
+
+def test_w8is_error_bound_and_accuracy(orc):
+    # |y_IS - y_FS-exact| <= s_i/alpha * sum_l |p_l| |iscale - alpha s_l| + rounding; at
+    # alpha = 2^18 the integer scales (still below 2^8 here) cost almost nothing over the
+    # float scales, and the int8 path is much closer to X W than the int4 one
+    x, w = synth.single_gemm_inputs(0)
+    x, w = x[:4], w[:, :96]
+    alpha = 1 << 18
+    pw = orc.pack_weights_int8(w, 128, alpha)
+    codes, fs, isc = pw["codes"], pw["fscale"], pw["iscale"]
+    qx, sx = orc.quant_sym_i8(x)
+    _, y, ov = orc.w8a8_gemm_is(qx, sx, codes, isc, alpha)
+    assert ov == 0
+    exact = _dequant_matmul(qx, sx, codes, fs)
+    G = fs.shape[0]
+    p = np.stack([qx[:, 128 * l:128 * (l + 1)].astype(np.int64) @ codes[128 * l:128 * (l + 1)].astype(np.int64)
+                  for l in range(G)])
+    dev = np.abs(isc.astype(np.float64) - alpha * fs.astype(np.float64))
+    bound = sx[:, None] / alpha * np.einsum("lmn,ln->mn", np.abs(p), dev)
+    bound += np.abs(exact) * 2.0 ** -22 + 1e-30
+    assert np.all(np.abs(y - exact) <= bound)
+    assert isc.max() <= 255
+    ref = x.astype(np.float64) @ w.astype(np.float64)
+    rel8 = np.linalg.norm(y - ref) / np.linalg.norm(ref)
+    relfs = np.linalg.norm(orc.w4a8_gemm_fs(qx, sx, codes, fs) - ref) / np.linalg.norm(ref)
+    p4 = orc.pack_weights(w, 128, 1024)
+    _, y4, _ = orc.w4a8_gemm_is(qx, sx, p4["codes"], p4["iscale"], 1024)
+    rel4 = np.linalg.norm(y4 - ref) / np.linalg.norm(ref)
+    assert rel8 <= 1.02 * relfs and rel8 < rel4 / 2
+
+
+def test_w8is_searched_alpha_rule(orc):
+    # alpha 0 runs the same search as for int4: smallest 2^n with min scale * 2^n >= 1
+    w = synth.weights(3, 256, 32, outlier_prob=0.001)
+    pw = orc.pack_weights_int8(w, 128, 0)
+    smin = pw["fscale"][pw["fscale"] > 0].min()
+    a = pw["alpha"]
+    assert smin * a >= 1 and smin * (a // 2) < 1
+    assert pw["iscale"].min() >= 1
