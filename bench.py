@@ -31,7 +31,11 @@ float-scale GEMMs side by side; value in TOPS); --workload w8a8 (the
 asymmetric W8A8 control with zero-point correction at M=256, K=N=4096;
 activation quantization per step, weights quantized offline; value in GB/s
 with algorithmic bytes N*K + M*K + 12*(M+N) + 4*M*N, plus 5*M*K + 12*M for
-the activation quantizer).
+the activation quantizer); --workload w8is (fine-grained W8A8 with integer
+scales at the LLaMA-3-8B down projection K=14336, N=4096, alpha=2^16: a
+decode step over M in {1,4,16,64} in GB/s with algorithmic bytes
+N*K + 4*G*N + M*K + 4*M + 4*M*N per GEMM, plus per-launch GEMM rates at
+M in {256,1024,4096}).
 
 Profiling aids (not benchmark lines): --profile-m M runs only the
 quantizer and the integer-scale GEMM at that M (decode layer shape) for
@@ -443,6 +447,104 @@ def run_w8a8(args, torch, bgt, dev):
     }, (x, w)
 
 
+W8IS_K, W8IS_N, W8IS_ALPHA = 14336, 4096, 1 << 16
+W8IS_DECODE_M = (1, 4, 16, 64)
+W8IS_PREFILL_M = (256, 1024, 4096)
+
+
+def w8is_bytes(M, N, K, scale_bytes=4, out_bytes=4):
+    G = K // 128
+    return N * K + scale_bytes * G * N + M * K + 4 * M + out_bytes * M * N
+
+
+def run_w8is(args, torch, bgt, dev):
+    """Fine-grained W8A8 with integer scales at the LLaMA-3-8B down projection
+    (K=14336, N=4096, g=128, alpha=2^16): one step is quant_act + GEMM for each
+    M in {1, 4, 16, 64} (value in GB/s, as the decode workload); per-launch
+    GEMM durations for those M and for M in {256, 1024, 4096} (TOPS)."""
+    K, N, alpha = W8IS_K, W8IS_N, W8IS_ALPHA
+    Ms = list(W8IS_DECODE_M)
+    Ps = list(W8IS_PREFILL_M)
+    x = synth.activations(900, max(Ps), K)
+    w = synth.weights(901, K, N, std=0.02, outlier_prob=0.001)
+    xd = torch.from_numpy(x).to(dev)
+    pw = bgt.pack_weights_int8(torch.from_numpy(w).to(dev), alpha=alpha)
+    assert pw["alpha"] == alpha
+    sb = args.iscale_bits // 8
+    isc0 = pw["iscale"] if sb == 4 else bgt.narrow_iscale(pw["iscale"], sb)
+    per = pw["qw"].numel() + isc0.numel() * sb
+    R = max(2, math.ceil(2 * MALL_BYTES / per))
+    rot = [(pw["qw"].clone(), isc0.clone()) for _ in range(R)]
+    xs = {M: xd[:M].contiguous() for M in Ms + Ps}
+    qbuf = {M: (torch.empty((M, K), dtype=torch.int8, device=dev),
+                torch.empty(M, dtype=torch.float32, device=dev)) for M in Ms + Ps}
+    ybuf = {M: torch.empty((M, N), dtype=torch.float32, device=dev) for M in Ms + Ps}
+    for M in Ps:
+        bgt.quantize_act(xs[M], q=qbuf[M][0], scale=qbuf[M][1])
+
+    def step(k):
+        for i, M in enumerate(Ms):
+            qw, isc = rot[(k * len(Ms) + i) % R]
+            q, s = qbuf[M]
+            bgt.quantize_act(xs[M], q=q, scale=s)
+            bgt.w8a8_gemm_is(q, s, qw, isc, alpha, N, y=ybuf[M])
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(k)
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms_step = graph_steps(torch, step, args.steps, args.warmup) if args.launch == "graph" else eager_ms
+
+    per_m = {}
+    for M in Ms + Ps:
+        q, s = qbuf[M]
+        if M in Ms:
+            bgt.quantize_act(xs[M], q=q, scale=s)
+
+        def launch(j, q=q, s=s, M=M):
+            qw, isc = rot[j % R]
+            bgt.w8a8_gemm_is(q, s, qw, isc, alpha, N, y=ybuf[M])
+        per_m[M] = graph_launch_us(torch, launch, 2 * R if M <= 256 else R, reps=3 if M > 256 else 5)
+    sweep = {}
+    for M in Ms + Ps:
+        us = float(np.mean(per_m[M]))
+        b = w8is_bytes(M, N, K, sb)
+        sweep[str(M)] = {"gemm_us": round(us, 3), "gemm_GBps": round(b / us / 1e3, 1),
+                         "gemm_TOPS": round(gemm_ops(M, N, K) / us / 1e6, 2),
+                         "hbm_frac": round(b / us / 1e3 / HBM_PEAK_GBS, 4),
+                         "mfma_frac": round(gemm_ops(M, N, K) / us / 1e6 / INT8_PEAK_TOPS, 4),
+                         "kernel": bgt.w8a8_is_kernel_name(M, N, K)}
+    step_bytes = sum(w8is_bytes(M, N, K, sb) + quant_bytes(M, K) for M in Ms)
+    durs = [u for M in Ms for u in per_m[M]]
+    avg_us = float(np.mean(durs))
+    avg_bytes = float(np.mean([w8is_bytes(M, N, K, sb) for M in Ms]))
+    achieved = avg_bytes / avg_us / 1e3
+    kern = bgt.w8a8_is_kernel_name(1, N, K)
+    return {
+        "metric": "fine-grained W8A8 integer-scale GEMM HBM GB/s, K=14336 N=4096",
+        "value": round(step_bytes / (ms_step * 1e-3) / 1e9, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8xint8->int32",
+        "data": "synthetic (seeded; X ~N(0,1) + 1% channels x20, W ~N(0,0.02) + 0.1% x10)",
+        "config": {"workload": "W8A8-IS decode sweep (LLaMA-3-8B down_proj): quant_act + GEMM, "
+                               "K=14336 N=4096 g=128 alpha=2^16, M in {1,4,16,64} per step",
+                   "launch": "hip_graph" if args.launch == "graph" else "eager",
+                   "iscale_storage": {4: "int32", 2: "uint16", 1: "uint8"}[sb],
+                   "weight_buffers_rotated": R},
+        "eager": {"ms_per_step": round(eager_ms, 4),
+                  "value": round(step_bytes / (eager_ms * 1e-3) / 1e9, 1)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": kern, "launch_M": Ms, "avg_launch_us": round(avg_us, 3),
+                     "bytes_per_launch": int(avg_bytes)},
+        "sweep": sweep,
+    }, (x, w)
+
+
 def run_profile_m(args, torch, bgt, dev, M):
     """Quantizer + integer-scale GEMM at one M of the decode layer, nothing else."""
     K, N = synth.K_LAYER, synth.N_LAYER
@@ -478,7 +580,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "w8a8"])
+    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "w8a8", "w8is"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--iscale-bits", type=int, default=32, choices=[8, 16, 32],
                     help="decode workload: integer scales stored as uint8 / uint16 / int32 "
@@ -516,9 +618,11 @@ def main():
         out, (x, w) = run_decode(args, torch, bgt, dev)
     elif args.workload == "prefill":
         out, (x, w) = run_prefill(args, torch, bgt, dev)
+    elif args.workload == "w8is":
+        out, (x, w) = run_w8is(args, torch, bgt, dev)
     else:
         out, (x, w) = run_w8a8(args, torch, bgt, dev)
-    if not args.no_cpu_baseline and args.workload != "w8a8":
+    if not args.no_cpu_baseline and args.workload in ("decode", "prefill"):
         out["cpu_baseline"] = cpu_baseline(x, w)
     print(json.dumps(out), flush=True)
 

@@ -12,6 +12,8 @@ Entry points (same names as the C ABI without the ``bgt_`` prefix):
     w4a8_gemm_is(qx, sx, packed, iscale, alpha, N)   -> y
     w4a8_gemm_fs(qx, sx, packed, fscale, N)          -> y
     w8a8_gemm_zp(qx, sx, zx, rowsum_x, qw, sw, zw, colsum_w) -> y
+    pack_weights_int8(w, alpha=0)          -> dict(qw, fscale, iscale, alpha, status)
+    w8a8_gemm_is(qx, sx, qw, iscale, alpha, N)       -> y
 """
 from __future__ import annotations
 
@@ -42,7 +44,9 @@ EXPORTED = (
     "bgt_w8a8_gemm_zp", "bgt_status_string", "bgt_abi_version", "bgt_w4a8_kernel_name",
     "bgt_narrow_iscale", "bgt_w4a8_gemm_is_narrow", "bgt_w4a8_linear_is", "bgt_w4a8_linear_fused",
     "bgt_quantize_act_ex", "bgt_w4a8_gemm_is_ex", "bgt_w4a8_gemm_fs_ex",
+    "bgt_pack_weights_int8", "bgt_w8a8_gemm_is", "bgt_w8a8_is_kernel_name",
 )
+_NAMES = ("bgt_status_string", "bgt_w4a8_kernel_name", "bgt_w8a8_is_kernel_name")
 
 _lib = None
 
@@ -78,10 +82,11 @@ def lib():
         L.bgt_status_string.restype = ctypes.c_char_p
         L.bgt_abi_version.restype = I
         L.bgt_w4a8_kernel_name.argtypes = [I64, I64, I64, I]
-        L.bgt_w4a8_kernel_name.restype = ctypes.c_char_p
+        L.bgt_pack_weights_int8.argtypes = [P, I64, I64, I64, I, P, P, P, ctypes.POINTER(I), P]
+        L.bgt_w8a8_gemm_is.argtypes = [P, P, P, P, I, I, I64, I64, I64, P, I, P, P]
+        L.bgt_w8a8_is_kernel_name.argtypes = [I64, I64, I64]
         for f in EXPORTED:
-            if f not in ("bgt_status_string", "bgt_abi_version", "bgt_w4a8_kernel_name"):
-                getattr(L, f).restype = I
+            getattr(L, f).restype = ctypes.c_char_p if f in _NAMES else I
         _lib = L
     return _lib
 
@@ -93,6 +98,11 @@ def status_string(status: int) -> str:
 def w4a8_kernel_name(M: int, N: int, K: int, float_scale: bool = False) -> str:
     """Name of the GEMM kernel a W4A8 call of this shape launches (profiling aid)."""
     return lib().bgt_w4a8_kernel_name(int(M), int(N), int(K), 1 if float_scale else 0).decode()
+
+
+def w8a8_is_kernel_name(M: int, N: int, K: int) -> str:
+    """Name of the kernel a fine-grained W8A8 integer-scale call launches."""
+    return lib().bgt_w8a8_is_kernel_name(int(M), int(N), int(K)).decode()
 
 
 # ----------------------------------------------------------------- marshalling
@@ -353,4 +363,56 @@ def w8a8_gemm_zp(qx, sx, zx, rowsum_x, qw, sw, zw, colsum_w, y=None, acc_out=Non
                                 _ptr(zw), _ptr(colsum_w), M, N, K, _ptr(y), _ptr(acc_out),
                                 _stream(qx.device))
     _raise("bgt_w8a8_gemm_zp", st)
+    return y
+
+
+def pack_weights_int8(w, alpha: int = 0, group: int = GROUP, qw=None, fscale=None, iscale=None):
+    """Offline int8 group quantization of w (K x N float32) into the int8
+    fragment layout, with float and integer scales.
+
+    alpha=0 runs the amplifier search. Synchronous. Returns a dict with qw
+    (N*K int8), fscale, iscale ((K/128) x N), alpha and status (0, or 1 = the
+    worst-case accumulator may exceed int32).
+    """
+    torch = _torch()
+    _check(w, "w", torch.float32)
+    K, N = w.shape
+    dev = w.device
+    G = K // group if group else 0
+    qw = torch.empty(N * K, dtype=torch.int8, device=dev) if qw is None else qw
+    fscale = torch.empty((G, N), dtype=torch.float32, device=dev) if fscale is None else fscale
+    iscale = torch.empty((G, N), dtype=torch.int32, device=dev) if iscale is None else iscale
+    _check(qw, "qw", torch.int8, (N * K,))
+    _check(fscale, "fscale", torch.float32, (G, N))
+    _check(iscale, "iscale", torch.int32, (G, N))
+    a_out = ctypes.c_int(0)
+    st = lib().bgt_pack_weights_int8(_ptr(w), K, N, group, int(alpha), _ptr(qw), _ptr(fscale),
+                                     _ptr(iscale), ctypes.byref(a_out), _stream(dev))
+    _raise("bgt_pack_weights_int8", st)
+    return {"qw": qw, "fscale": fscale, "iscale": iscale, "alpha": a_out.value, "status": st}
+
+
+def w8a8_gemm_is(qx, sx, qw, iscale, alpha: int, N: int, y=None, acc_out=None, out_dtype=None):
+    """Fine-grained W8A8 Y = X.W with the integer-scale epilogue. iscale is
+    uint8, uint16 or int32 ((K/128) x N); y float32, float16 or bfloat16
+    (y's dtype, or out_dtype when y is not given). Returns y (M x N)."""
+    torch = _torch()
+    widths = {torch.uint8: 1, torch.uint16: 2, torch.int32: 4}
+    if not isinstance(iscale, torch.Tensor) or iscale.dtype not in widths:
+        raise TypeError("iscale must be a uint8, uint16 or int32 tensor")
+    _check(qx, "qx", torch.int8)
+    M, K = qx.shape
+    _check(sx, "sx", torch.float32, (M,))
+    _check(qw, "qw", torch.int8, (N * K,))
+    _check(iscale, "iscale", iscale.dtype, (K // GROUP, N))
+    if y is None:
+        y = torch.empty((M, N), dtype=out_dtype or torch.float32, device=qx.device)
+    _check(y, "y", y.dtype, (M, N))
+    yt = _elem_type(y, "y")
+    if acc_out is not None:
+        _check(acc_out, "acc_out", torch.int32, (M, N))
+    st = lib().bgt_w8a8_gemm_is(_ptr(qx), _ptr(sx), _ptr(qw), _ptr(iscale), widths[iscale.dtype],
+                                int(alpha), M, N, K, _ptr(y), yt, _ptr(acc_out),
+                                _stream(qx.device))
+    _raise("bgt_w8a8_gemm_is", st)
     return y

@@ -43,7 +43,7 @@ int searched_alpha_log2(float smin) {
 
 extern "C" {
 
-int bgt_abi_version(void) { return 103; }
+int bgt_abi_version(void) { return 104; }
 
 int bgt_w4a8_linear_fused(int64_t M, int64_t K, const void* x, int64_t ldx) {
   return bgt::w4a8_linear_fused(M, K, x, ldx) ? 1 : 0;
@@ -87,19 +87,24 @@ int bgt_quantize_act_ex(const void* x, int x_type, int64_t rows, int64_t cols, i
                                            scale, zero, rowsum, static_cast<hipStream_t>(stream)));
 }
 
-int bgt_pack_weights_int4(const float* w, int64_t K, int64_t N, int64_t group, int alpha,
-                          uint8_t* packed, float* fscale, int32_t* iscale, int* alpha_out,
-                          void* stream) {
-  if (!w || !packed || !fscale || !iscale || !alpha_out) return BGT_ERR_NULL;
+namespace {
+
+// Shared by the int4 and int8 packers: group quantization into `codes`, then
+// the amplifier (given or searched), the range check and the integer scales.
+// pmax: the largest |p| of one group with these codes (128 * 127 * q_max).
+int pack_weights(bool int8_codes, double pmax, const float* w, int64_t K, int64_t N,
+                 int64_t group, int alpha, void* codes, float* fscale, int32_t* iscale,
+                 int* alpha_out, void* stream) {
+  if (!w || !codes || !fscale || !iscale || !alpha_out) return BGT_ERR_NULL;
   if (group != BGT_GROUP) return BGT_ERR_SHAPE;
   if (K < BGT_GROUP || K > 65536 || K % BGT_GROUP != 0) return BGT_ERR_SHAPE;
   if (N < 16 || N > (1 << 24) || N % 16 != 0) return BGT_ERR_SHAPE;
   if (alpha != 0 && !pow2_alpha(alpha)) return BGT_ERR_ALPHA;
-  if (!aligned16(packed)) return BGT_ERR_ALIGN;
+  if (!aligned16(codes)) return BGT_ERR_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t G = K / BGT_GROUP;
 
-  hipError_t e = bgt::launch_group_quant_pack(w, K, N, packed, fscale, iscale, s);
+  hipError_t e = bgt::launch_group_quant_pack(int8_codes, w, K, N, codes, fscale, iscale, s);
   if (e != hipSuccess) return BGT_ERR_HIP;
   uint32_t bits[2];
   e = hipMemcpyAsync(bits, iscale, sizeof(bits), hipMemcpyDeviceToHost, s);
@@ -122,9 +127,26 @@ int bgt_pack_weights_int4(const float* w, int64_t K, int64_t N, int64_t group, i
   e = bgt::launch_integer_scales(fscale, G * N, a, iscale, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return BGT_ERR_HIP;
-  // |p| <= 128 * 127 * 7 = 113792 per group with the packer's codes
-  if (113792.0 * (double)G * top >= 2147483648.0) return BGT_WARN_ACC_MAY_OVERFLOW;
+  if (pmax * (double)G * top >= 2147483648.0) return BGT_WARN_ACC_MAY_OVERFLOW;
   return BGT_OK;
+}
+
+}  // namespace
+
+int bgt_pack_weights_int4(const float* w, int64_t K, int64_t N, int64_t group, int alpha,
+                          uint8_t* packed, float* fscale, int32_t* iscale, int* alpha_out,
+                          void* stream) {
+  // |p| <= 128 * 127 * 7 = 113792 per group with the packer's codes
+  return pack_weights(false, 113792.0, w, K, N, group, alpha, packed, fscale, iscale, alpha_out,
+                      stream);
+}
+
+int bgt_pack_weights_int8(const float* w, int64_t K, int64_t N, int64_t group, int alpha,
+                          int8_t* qw, float* fscale, int32_t* iscale, int* alpha_out,
+                          void* stream) {
+  // |p| <= 128 * 127 * 127 = 2064512 per group
+  return pack_weights(true, 2064512.0, w, K, N, group, alpha, qw, fscale, iscale, alpha_out,
+                      stream);
 }
 
 int bgt_w4a8_gemm_is(const int8_t* qx, const float* sx, const uint8_t* packed,
@@ -210,6 +232,28 @@ int bgt_narrow_iscale(const int32_t* iscale, int64_t count, int width, void* out
   for (int32_t v : h)
     if (v < 0 || v > top) return BGT_ERR_RANGE;
   return hip_status(bgt::launch_narrow_scales(iscale, count, width, out, s));
+}
+
+int bgt_w8a8_gemm_is(const int8_t* qx, const float* sx, const int8_t* qw, const void* iscale,
+                     int width, int alpha, int64_t M, int64_t N, int64_t K, void* y, int y_type,
+                     int32_t* acc_out, void* stream) {
+  if (!qx || !sx || !qw || !iscale || !y) return BGT_ERR_NULL;
+  if (width != 1 && width != 2 && width != 4) return BGT_ERR_MODE;
+  if (!valid_type(y_type)) return BGT_ERR_MODE;
+  int st = check_gemm_shape(M, N, K, 65536);
+  if (st != BGT_OK) return st;
+  if (!pow2_alpha(alpha)) return BGT_ERR_ALPHA;
+  if (!aligned16(qx) || !aligned16(qw) || !aligned16(iscale) || !aligned16(y) ||
+      (acc_out && !aligned16(acc_out)))
+    return BGT_ERR_ALIGN;
+  return hip_status(bgt::launch_w8a8_is(qx, sx, qw, iscale, width, alpha, M, N, K,
+                                        bgt::OutY{y, y_type}, acc_out,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+const char* bgt_w8a8_is_kernel_name(int64_t M, int64_t N, int64_t K) {
+  if (check_gemm_shape(M, N, K, 65536) != BGT_OK) return "invalid shape";
+  return bgt::w8a8_is_kernel_name(M, N, K);
 }
 
 int bgt_w8a8_gemm_zp(const uint8_t* qx, const float* sx, const int32_t* zx,

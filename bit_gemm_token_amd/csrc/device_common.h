@@ -124,4 +124,52 @@ __device__ __forceinline__ v4i load_v4i(const int8_t* p) {
   return *reinterpret_cast<const v4i*>(p);
 }
 
+// ------------------------------------------------------ integer epilogue
+// 24-bit signed multiply-add: exact mod 2^32 while |p| < 2^23 and
+// 0 <= iscale < 2^23 (guaranteed: a group's |p| is at most 128*127*8 with int4
+// weights and 128*127*127 with int8 weights; iscale range checked at pack)
+__device__ __forceinline__ int mad24(int a, int b, int c) { return __mul24(a, b) + c; }
+
+// Marks a register value as rewritten here, so the compiler cannot re-associate
+// accumulations across this point (re-associating a group's multiply-adds with
+// the next group's keeps every product of a group live and exhausts the
+// register file). Emits no instruction.
+template <typename T>
+__device__ __forceinline__ void opaque_reg(T& v) { asm volatile("" : "+v"(v)); }
+
+// ------------------------------------------------------- waits, barriers
+// compile-time integer (selects an LDS stage array by index)
+template <int N_> struct IC { static constexpr int value = N_; };
+
+// s_waitcnt vmcnt(VM) lgkmcnt(0) (gfx9 encoding: vmcnt[3:0] and [15:14],
+// expcnt[6:4] = 7 meaning "don't wait", lgkmcnt[11:8]).
+template <int VM>
+__device__ __forceinline__ void wait_vm_lds0() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4));
+}
+
+// s_waitcnt vmcnt(VM) only (lgkmcnt field at its maximum: no LDS wait).
+template <int VM>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// s_waitcnt lgkmcnt(0) only (vmcnt field at its maximum: no memory wait).
+__device__ __forceinline__ void wait_lds0() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
+}
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p));
+}
+
+// Workgroup barrier for the LDS ring: the caller has already waited for its
+// own LDS stores (lgkmcnt) and LDS-DMA loads (vmcnt); a plain s_barrier then
+// suffices, with no fence that would also drain the loads still in flight.
+__device__ __forceinline__ void lds_barrier() { __builtin_amdgcn_s_barrier(); }
+
 }  // namespace bgt

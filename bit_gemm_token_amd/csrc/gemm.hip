@@ -27,17 +27,6 @@
 
 namespace bgt {
 
-// 24-bit signed multiply-add: exact mod 2^32 while |p| < 2^23 and
-// 0 <= iscale < 2^23 (guaranteed: |p| <= 128*127*8, iscale range checked at pack)
-__device__ __forceinline__ int mad24(int a, int b, int c) { return __mul24(a, b) + c; }
-
-// Marks a register value as rewritten here, so the compiler cannot re-associate
-// accumulations across this point (re-associating a group's multiply-adds with
-// the next group's keeps every product of a group live and exhausts the
-// register file). Emits no instruction.
-template <typename T>
-__device__ __forceinline__ void opaque_reg(T& v) { asm volatile("" : "+v"(v)); }
-
 // =====================================================================
 // Skinny kernel (small M): one workgroup per 16-column tile; its KS waves
 // split the groups; each wave streams its share of the tile's packed 1 KiB
@@ -365,34 +354,6 @@ __device__ __forceinline__ void tile_of(int pid, int ntm, int ntn, int& tm, int&
   tn = in / gsz;
 }
 
-template <int N_> struct IC { static constexpr int value = N_; };
-
-// s_waitcnt vmcnt(VM) lgkmcnt(0) (gfx9 encoding: vmcnt[3:0] and [15:14],
-// expcnt[6:4] = 7 meaning "don't wait", lgkmcnt[11:8]).
-template <int VM>
-__device__ __forceinline__ void wait_vm_lds0() {
-  static_assert(VM >= 0 && VM < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4));
-}
-
-// s_waitcnt vmcnt(VM) only (lgkmcnt field at its maximum: no LDS wait).
-template <int VM>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(VM >= 0 && VM < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-// s_waitcnt lgkmcnt(0) only (vmcnt field at its maximum: no memory wait).
-__device__ __forceinline__ void wait_lds0() {
-  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
-}
-
-// LDS byte address of a pointer into a __shared__ array.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p));
-}
-
 // 16-byte LDS read of data that this lane's own LDS copy wrote, after the
 // caller's s_waitcnt on vmcnt. Written as one asm block that waits for its
 // own result, so the compiler does not add a wait for every copy in flight
@@ -405,10 +366,6 @@ __device__ __forceinline__ uint4 lds_read_own_copy(const uint4* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// Workgroup barrier for the LDS ring: the caller has already waited for its
-// own LDS stores (lgkmcnt) and LDS-DMA loads (vmcnt); a plain s_barrier then
-// suffices, with no fence that would also drain the loads still in flight.
-__device__ __forceinline__ void lds_barrier() { __builtin_amdgcn_s_barrier(); }
 
 template <int WM, int WN, int TMW, int TNW, bool FS, typename ST>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_w4a8_prefill(

@@ -1,0 +1,403 @@
+// gemm_w8is.hip -- fine-grained W8A8 GEMM with the integer-scale epilogue (gfx950).
+//
+// The Integer Scale page (5.4, the LLaMA-3 scheme) keeps the down projection
+// at 8-bit weights, fine-grained: per-token int8 activations, group-wise (128)
+// symmetric int8 weights, and the same integer-scale epilogue as the W4A8
+// layer (方法, Fig. 3(c)):
+//     p_ilj = sum_{k in group l} qx[i][k] * qw[k][j]      (|p| <= 128*127*127 < 2^23)
+//     A_ij  = sum_l p_ilj * iscale[l][j]                   (int32, mod 2^32)
+//     y_ij  = ((float)A_ij * sx[i]) * (1/alpha).
+//
+// Weights are in the int8 fragment layout (bgt_pack_weights_int8): each
+// (16-column tile, group) pair is 2 KiB, two 1 KiB halves of 64 k, lane L of a
+// half holding column L%16 and the 16 codes k = 16*(L/16) .. +15 of the half,
+// i.e. one B operand of v_mfma_i32_16x16x64_i8 per half, read with one
+// contiguous 16-byte load per lane.
+//
+// Two kernels:
+//   split (M <= 64, weight streaming): one workgroup per 16-column tile, its
+//     KS waves split the groups; each wave keeps D groups of weights, their
+//     activation fragments and scales in flight in registers, runs two MFMAs
+//     per group and row block and applies the group's integer scale with a
+//     24-bit multiply-add. The waves' int32 sums (exact, any order) meet in LDS.
+//   tiled (M > 64): 64 x 64 output tiles, 8 waves, nine LDS-copy stages of one
+//     group (activations row-major with XOR-swizzled 16-byte chunks, weights
+//     straight from the fragment layout, the group's 64 scales), eight in
+//     flight; waves 0-3 and 4-7 take the two 64-k halves of a group on a 2 x 2
+//     arrangement of 32 x 32 blocks (v_mfma_i32_32x32x32_i8), apply the
+//     group's scale to their half's partial and meet once at the end.
+#include <type_traits>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace bgt {
+
+// =====================================================================
+// Split kernel
+// =====================================================================
+constexpr int kSplitMaxWaves = 16;
+constexpr int split_max_waves(int mr) { return mr == 4 ? 8 : kSplitMaxWaves; }
+
+template <int MR, int D, typename ST>
+__global__ __launch_bounds__(split_max_waves(MR) * 64) void k_w8is_split(
+    const int8_t* __restrict__ qx, const float* __restrict__ sx, const uint4* __restrict__ qw,
+    const ST* __restrict__ iscale, float inv_alpha, int M, int N, int K, OutY y,
+    int32_t* __restrict__ acc_out) {
+  __shared__ int32_t red[split_max_waves(MR) * MR * 4 * 64];
+  const int G = K / kGroup;
+  const int KS = blockDim.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int c = lane % 16, s4 = lane / 16;
+  const int t = blockIdx.x;
+  const int g0 = wave * G / KS, g1 = (wave + 1) * G / KS;   // this wave's groups
+
+  const uint4* wsrc = qw + (int64_t)t * G * 128 + lane;       // + 128 g + 64 h
+  const ST* ssrc = iscale + 16 * t + c;                       // + N g
+  // activation fragments: row 16 rb + c, bytes 16 s4 .. of each 64-k half;
+  // rows past M are zero
+  const int8_t* xsrc[MR];
+  bool xrow[MR];
+#pragma unroll
+  for (int rb = 0; rb < MR; ++rb) {
+    xrow[rb] = 16 * rb + c < M;
+    xsrc[rb] = qx + (int64_t)(xrow[rb] ? 16 * rb + c : 0) * K + 16 * s4;
+  }
+
+  uint4 wb[D][2];
+  v4i xb[D][MR][2];
+  int32_t sb[D];
+  auto fetch = [&](int j, int g) {
+    wb[j][0] = load_u4_nt(wsrc + (int64_t)g * 128);
+    wb[j][1] = load_u4_nt(wsrc + (int64_t)g * 128 + 64);
+    sb[j] = (int32_t)ssrc[(int64_t)g * N];
+#pragma unroll
+    for (int rb = 0; rb < MR; ++rb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        xb[j][rb][h] = v4i{0, 0, 0, 0};
+        if (xrow[rb]) xb[j][rb][h] = load_v4i(xsrc[rb] + 128 * g + 64 * h);
+      }
+  };
+
+  int acc[MR][4];
+#pragma unroll
+  for (int rb = 0; rb < MR; ++rb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[rb][r] = 0;
+
+#pragma unroll
+  for (int j = 0; j < D; ++j)
+    if (g0 + j < g1) fetch(j, g0 + j);
+#pragma unroll 1
+  for (int g = g0; g < g1; g += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      if (g + j < g1) {
+        int32_t sc = sb[j];
+        if (sizeof(ST) < 4) opaque_reg(sc);            // keep the 24-bit multiply-adds as written
+        const v4i b0 = {(int)wb[j][0].x, (int)wb[j][0].y, (int)wb[j][0].z, (int)wb[j][0].w};
+        const v4i b1 = {(int)wb[j][1].x, (int)wb[j][1].y, (int)wb[j][1].z, (int)wb[j][1].w};
+#pragma unroll
+        for (int rb = 0; rb < MR; ++rb) {
+          v4i p = __builtin_amdgcn_mfma_i32_16x16x64_i8(xb[j][rb][0], b0, v4i{0, 0, 0, 0}, 0, 0, 0);
+          p = __builtin_amdgcn_mfma_i32_16x16x64_i8(xb[j][rb][1], b1, p, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[rb][r] = mad24(p[r], sc, acc[rb][r]);
+        }
+        if (g + j + D < g1) fetch(j, g + j + D);
+      }
+    }
+  }
+
+  // the waves' sums meet in LDS: red[wave][rb*4 + r][lane]; then thread
+  // e < MR*256 adds element (rb*4 + r, lane) over the waves (wrapping adds)
+#pragma unroll
+  for (int rb = 0; rb < MR; ++rb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[(wave * MR * 4 + rb * 4 + r) * 64 + lane] = acc[rb][r];
+  __syncthreads();
+  for (int e = threadIdx.x; e < MR * 4 * 64; e += blockDim.x) {
+    const int i4 = e / 64, ln = e % 64;
+    const int row = 16 * (i4 / 4) + 4 * (ln / 16) + i4 % 4;
+    if (row >= M) continue;
+    uint32_t a = 0u;
+    for (int w = 0; w < KS; ++w) a += (uint32_t)red[(w * MR * 4 + i4) * 64 + ln];
+    const int32_t A = (int32_t)a;
+    const int64_t o = (int64_t)row * N + 16 * t + ln % 16;
+    const float t0 = (float)A * sx[row];
+    y.put(o, t0 * inv_alpha);
+    if (acc_out) acc_out[o] = A;
+  }
+}
+
+// =====================================================================
+// Tiled kernel
+// =====================================================================
+constexpr int kW8isWaves = 8;
+
+template <int GC, typename ST>
+__global__ __launch_bounds__(kW8isWaves * 64) void k_w8is_tiled(
+    const int8_t* __restrict__ qx, const float* __restrict__ sx, const int8_t* __restrict__ qw,
+    const ST* __restrict__ iscale, float inv_alpha, int M, int N, int K, OutY y,
+    int32_t* __restrict__ acc_out) {
+  // GC > 0: K / 128 fixed at compile time and the step loop unrolls completely
+  constexpr int NST = 9, BM = 64, BN = 64;
+  constexpr int SB = sizeof(ST);
+  constexpr int AB = (BM + BN) * 128;                 // operand bytes of a stage
+  constexpr int STG = AB + 256;                       // + the group's 64 scales (<= 256 B)
+  constexpr int LOADS = 3;                            // copies per stage per wave: 2 operand KiB + scales
+  __shared__ __align__(16) int8_t S0[STG];
+  __shared__ __align__(16) int8_t S1[STG];
+  __shared__ __align__(16) int8_t S2[STG];
+  __shared__ __align__(16) int8_t S3[STG];
+  __shared__ __align__(16) int8_t S4[STG];
+  __shared__ __align__(16) int8_t S5[STG];
+  __shared__ __align__(16) int8_t S6[STG];
+  __shared__ __align__(16) int8_t S7[STG];
+  __shared__ __align__(16) int8_t S8[STG];
+  auto stage = [&](auto ic) -> int8_t* {
+    constexpr int i = decltype(ic)::value;
+    if constexpr (i == 0) return S0;
+    else if constexpr (i == 1) return S1;
+    else if constexpr (i == 2) return S2;
+    else if constexpr (i == 3) return S3;
+    else if constexpr (i == 4) return S4;
+    else if constexpr (i == 5) return S5;
+    else if constexpr (i == 6) return S6;
+    else if constexpr (i == 7) return S7;
+    else return S8;
+  };
+  const int G = GC > 0 ? GC : K / kGroup;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid % kWave;
+  const int kh = wave / 4, wm = (wave % 4) / 2, wn = wave % 2;
+  const int lr = lane % 32, hf = lane / 32;
+  const int ntn = (N + BN - 1) / BN;
+  const int n0 = (blockIdx.x % ntn) * BN, m0 = (blockIdx.x / ntn) * BM;
+  const int T = N / 16;
+
+  // operand copies: the 16 KiB blocks of a stage are spread over the waves, two
+  // each. Block b < 8: activation rows 8b .. 8b+7, lane L fills row 8b + L/8,
+  // chunk slot L%8 with the row's chunk (L%8) ^ ((row/2) % 8) (rows past M
+  // re-read the last row). Block b >= 8: half (b-8)%2 of weight tile
+  // n0/16 + (b-8)/2 (tiles past N re-read the last tile), copied as it is.
+  const int8_t* src[2];
+  int dst[2];
+  int64_t gstep[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int b = wave * 2 + u;
+    if (b < 8) {
+      const int r8 = 8 * b + lane / 8;
+      const int ck = 16 * ((lane % 8) ^ ((r8 >> 1) & 7));
+      src[u] = qx + (int64_t)(m0 + r8 < M ? m0 + r8 : M - 1) * K + ck;
+      gstep[u] = kGroup;
+    } else {
+      const int bb = b - 8, tl = n0 / 16 + bb / 2 < T ? n0 / 16 + bb / 2 : T - 1;
+      src[u] = qw + ((int64_t)tl * G * 2 + bb % 2) * 1024 + lane * 16;
+      gstep[u] = 2048;
+    }
+    dst[u] = b * 1024;
+  }
+  // scale copy: dword d = 2*SB*wave + lane (lane < 2*SB) of the group's 64*SB
+  // scale bytes; dwords past N re-read the row's last dword
+  const bool scopy = lane < 2 * SB;
+  const int sd = 2 * SB * wave + lane;
+  const int scol = n0 + sd * (4 / SB) < N ? n0 + sd * (4 / SB) : N - 4 / SB;
+  const int8_t* ssrc = reinterpret_cast<const int8_t*>(iscale) + (int64_t)scol * SB;
+  auto issue = [&](int g, int8_t* S) {
+    const int gc = g < G ? g : G - 1;                 // past the end: a surplus copy, never read
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(src[u] + (int64_t)gc * gstep[u]),
+          (__attribute__((address_space(3))) void*)(S + dst[u]), 16, 0, 0);
+    if (scopy)
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(ssrc + (int64_t)gc * N * SB),
+          (__attribute__((address_space(3))) void*)(S + AB + 8 * SB * wave), 4, 0, 0);
+  };
+
+  // fragments: A row ra, B column 32 wn + lr (tile 2 wn + lr/16, lane slot
+  // 16 m + lr%16 of half hf); the k chunk of MFMA m is 4 hf + m for both
+  const int ra = wm * 32 + lr;
+  constexpr int boff = BM * 128;                      // weight half-blocks follow the rows
+  const int bcol = ((2 * wn + lr / 16) * 2 + hf) * 1024 + (lr % 16) * 16;
+  const int scol_l = (32 * wn + lr) * SB;
+  v16i acc = v16i{0};
+  v16i pp = v16i{0};
+  int32_t spp = 0;
+  // step l: MFMAs of group l into p; then the previous group's partial times
+  // its scale (its MFMAs have finished under this group's)
+  auto compute = [&](const int8_t* S, bool apply_prev) {
+    v4i av[2], bv[2];
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm) {
+      const int m = 2 * kh + mm;
+      av[mm] = *reinterpret_cast<const v4i*>(S + ra * 128 + 16 * ((4 * hf + m) ^ ((ra >> 1) & 7)));
+      bv[mm] = *reinterpret_cast<const v4i*>(S + boff + bcol + 256 * m);
+    }
+    int32_t sc = (int32_t)*reinterpret_cast<const ST*>(S + AB + scol_l);
+    v16i p = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[0], bv[0], v16i{0}, 0, 0, 0);
+    p = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[1], bv[1], p, 0, 0, 0);
+    if (apply_prev) {
+      opaque_reg(spp);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = mad24(pp[r], spp, acc[r]);
+      opaque_reg(acc);                               // one group at a time: no partials kept live
+    }
+    pp = p;
+    spp = sc;
+  };
+  auto step = [&](int l, auto j) {
+    constexpr int J = decltype(j)::value;
+    wait_vm_lds0<(NST - 2) * LOADS>();
+    lds_barrier();
+    issue(l + NST - 1, stage(IC<(J + NST - 1) % NST>{}));
+    compute(stage(IC<J>{}), l > 0);
+  };
+  issue(0, S0);
+  issue(1, S1);
+  issue(2, S2);
+  issue(3, S3);
+  issue(4, S4);
+  issue(5, S5);
+  issue(6, S6);
+  issue(7, S7);
+  auto steps = [&](int l) {
+    step(l + 0, IC<0>{});
+    if (l + 1 >= G) return false;
+    step(l + 1, IC<1>{});
+    if (l + 2 >= G) return false;
+    step(l + 2, IC<2>{});
+    if (l + 3 >= G) return false;
+    step(l + 3, IC<3>{});
+    if (l + 4 >= G) return false;
+    step(l + 4, IC<4>{});
+    if (l + 5 >= G) return false;
+    step(l + 5, IC<5>{});
+    if (l + 6 >= G) return false;
+    step(l + 6, IC<6>{});
+    if (l + 7 >= G) return false;
+    step(l + 7, IC<7>{});
+    if (l + 8 >= G) return false;
+    step(l + 8, IC<8>{});
+    return true;
+  };
+  if constexpr (GC > 0) {
+#pragma unroll
+    for (int l = 0; l < G; l += NST) if (!steps(l)) break;
+  } else {
+#pragma unroll 1
+    for (int l = 0; l < G; l += NST) if (!steps(l)) break;
+  }
+  opaque_reg(spp);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = mad24(pp[r], spp, acc[r]);
+
+  // the two k halves meet: waves 4-7 park their sums in stage 0, waves 0-3 add
+  wait_vm_lds0<0>();
+  lds_barrier();
+  int32_t* R = reinterpret_cast<int32_t*>(S0);
+  if (kh == 1) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) R[((wave % 4) * 16 + r) * 64 + lane] = acc[r];
+  }
+  wait_lds0();
+  lds_barrier();
+  if (kh == 1) return;
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    acc[r] = (int32_t)((uint32_t)acc[r] + (uint32_t)R[((wave % 4) * 16 + r) * 64 + lane]);
+
+  const int j = n0 + wn * 32 + lr;
+  if (j >= N) return;
+  float sxr[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int i = m0 + wm * 32 + 8 * (r / 4) + 4 * hf + (r % 4);
+    sxr[r] = sx[i < M ? i : M - 1];
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int i = m0 + wm * 32 + 8 * (r / 4) + 4 * hf + (r % 4);
+    if (i >= M) continue;
+    const int64_t o = (int64_t)i * N + j;
+    const float t0 = (float)acc[r] * sxr[r];
+    y.put(o, t0 * inv_alpha);
+    if (acc_out) acc_out[o] = acc[r];
+  }
+}
+
+// ------------------------------------------------------------------ launchers
+// waves per split workgroup: about 4096 waves over the chip (16 per CU), at
+// least two groups per wave, at most 16 (8 for four row blocks: LDS)
+static int split_waves(int64_t N, int64_t K, int mr) {
+  const int64_t T = N / 16, G = K / kGroup;
+  int ks = 1;
+  const int cap = split_max_waves(mr);
+  while (ks < cap && T * ks < 4096 && 2 * (2 * ks) <= G) ks *= 2;
+  return ks;
+}
+
+template <typename ST>
+static void launch_w8is_t(const int8_t* qx, const float* sx, const int8_t* qw, const ST* iscale,
+                          float inv_alpha, int M, int N, int K, OutY y, int32_t* acc_out,
+                          hipStream_t stream) {
+  if (M <= 64) {
+    const int mr = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+    const int ks = split_waves(N, K, mr);
+    dim3 grid((unsigned)(N / 16)), block((unsigned)(ks * kWave));
+    const uint4* w = reinterpret_cast<const uint4*>(qw);
+    if (mr == 1)
+      hipLaunchKernelGGL((k_w8is_split<1, 4, ST>), grid, block, 0, stream, qx, sx, w, iscale,
+                         inv_alpha, M, N, K, y, acc_out);
+    else if (mr == 2)
+      hipLaunchKernelGGL((k_w8is_split<2, 3, ST>), grid, block, 0, stream, qx, sx, w, iscale,
+                         inv_alpha, M, N, K, y, acc_out);
+    else
+      hipLaunchKernelGGL((k_w8is_split<4, 2, ST>), grid, block, 0, stream, qx, sx, w, iscale,
+                         inv_alpha, M, N, K, y, acc_out);
+    return;
+  }
+  const int tiles = ((M + 63) / 64) * ((N + 63) / 64);
+  const int G = K / kGroup;
+  dim3 grid((unsigned)tiles), block(kW8isWaves * 64);
+  if (G == 112)
+    hipLaunchKernelGGL((k_w8is_tiled<112, ST>), grid, block, 0, stream, qx, sx, qw, iscale,
+                       inv_alpha, M, N, K, y, acc_out);
+  else if (G == 32)
+    hipLaunchKernelGGL((k_w8is_tiled<32, ST>), grid, block, 0, stream, qx, sx, qw, iscale,
+                       inv_alpha, M, N, K, y, acc_out);
+  else
+    hipLaunchKernelGGL((k_w8is_tiled<0, ST>), grid, block, 0, stream, qx, sx, qw, iscale,
+                       inv_alpha, M, N, K, y, acc_out);
+}
+
+hipError_t launch_w8a8_is(const int8_t* qx, const float* sx, const int8_t* qw, const void* iscale,
+                          int iscale_bytes, int alpha, int64_t M, int64_t N, int64_t K, OutY y,
+                          int32_t* acc_out, hipStream_t stream) {
+  const float inv_alpha = 1.0f / (float)alpha;        // exact: alpha is 2^n
+  const int m = (int)M, n = (int)N, k = (int)K;
+  if (iscale_bytes == 1)
+    launch_w8is_t(qx, sx, qw, static_cast<const uint8_t*>(iscale), inv_alpha, m, n, k, y, acc_out,
+                  stream);
+  else if (iscale_bytes == 2)
+    launch_w8is_t(qx, sx, qw, static_cast<const uint16_t*>(iscale), inv_alpha, m, n, k, y, acc_out,
+                  stream);
+  else
+    launch_w8is_t(qx, sx, qw, static_cast<const int32_t*>(iscale), inv_alpha, m, n, k, y, acc_out,
+                  stream);
+  return hipGetLastError();
+}
+
+const char* w8a8_is_kernel_name(int64_t M, int64_t N, int64_t K) {
+  (void)N;
+  (void)K;
+  return M <= 64 ? "k_w8is_split" : "k_w8is_tiled";
+}
+
+}  // namespace bgt

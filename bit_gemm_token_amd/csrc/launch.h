@@ -14,10 +14,12 @@ hipError_t launch_quant_rows(const void* x, int x_type, int64_t rows, int64_t co
                              bool asym, void* q, float* scale, int32_t* zero, int32_t* rowsum,
                              hipStream_t stream);
 
-// Group quantization + packing; also leaves min(positive s) and max(s) as float
-// bits in iscale[0], iscale[1] (scratch until launch_integer_scales overwrites them).
-hipError_t launch_group_quant_pack(const float* w, int64_t K, int64_t N, uint8_t* packed,
-                                   float* fscale, int32_t* iscale, hipStream_t stream);
+// Group quantization + packing (int4 nibbles, or int8 codes in the int8 fragment
+// layout); also leaves min(positive s) and max(s) as float bits in iscale[0],
+// iscale[1] (scratch until launch_integer_scales overwrites them).
+hipError_t launch_group_quant_pack(bool int8_codes, const float* w, int64_t K, int64_t N,
+                                   void* packed, float* fscale, int32_t* iscale,
+                                   hipStream_t stream);
 
 hipError_t launch_integer_scales(const float* fscale, int64_t count, int alpha, int32_t* iscale,
                                  hipStream_t stream);
@@ -46,6 +48,13 @@ hipError_t launch_narrow_scales(const int32_t* in, int64_t count, int out_bytes,
 
 // name of the kernel a W4A8 GEMM of this shape dispatches to (diagnostics)
 const char* w4a8_kernel_name(int64_t M, int64_t K, bool float_scale);
+
+// fine-grained W8A8 with the integer-scale epilogue; qw in the int8 fragment
+// layout of bgt_pack_weights_int8, iscale of iscale_bytes bytes per element
+hipError_t launch_w8a8_is(const int8_t* qx, const float* sx, const int8_t* qw, const void* iscale,
+                          int iscale_bytes, int alpha, int64_t M, int64_t N, int64_t K, OutY y,
+                          int32_t* acc_out, hipStream_t stream);
+const char* w8a8_is_kernel_name(int64_t M, int64_t N, int64_t K);
 
 hipError_t launch_w8a8_zp(const uint8_t* qx, const float* sx, const int32_t* zx,
                           const int32_t* rowsum_x, const uint8_t* qw, const float* sw,

@@ -1,17 +1,20 @@
-// pack_int4.hip -- offline group-wise int4 weight quantization and packing (gfx950).
+// pack_int4.hip -- offline group-wise weight quantization and packing (gfx950):
+// int4 codes for the W4A8 GEMMs and int8 codes for the fine-grained W8A8 one.
 //
 // Per column j and group l of 128 rows of W (K x N row-major), following the
 // Integer Scale page (方法, Fig. 3(a): weights split into groups quantized
 // independently) with the symmetric closed forms of the "Quantization" notes
-// page at q_max = 7:
-//     s = max|w| / 7,  q = clip(round(w / s), -7, 7),  fscale = s,
+// page at q_max = 7 (int4) or 127 (int8; the down-projection recipe of the
+// Integer Scale page, 5.4):
+//     s = max|w| / q_max,  q = clip(round(w / s), -q_max, q_max),  fscale = s,
 // then the integer scales round(s * alpha) of Fig. 3(c).
 //
 // One thread per (column, group): the 128 values of its group are a strided
 // column walk, coalesced across the 256 threads of a workgroup (consecutive
-// columns). The thread builds the group's 64 packed bytes in registers and
-// writes them as four 16-byte stores into the four lane slots of the
-// (16-column tile, group) block of the packed layout.
+// columns). The thread builds the group's codes in registers and writes them
+// with 16-byte stores into the lane slots of the (16-column tile, group)
+// block of the device layout (int4: one 1 KiB block, four stores; int8: two
+// 1 KiB halves, eight stores).
 #include "device_common.h"
 #include "launch.h"
 
@@ -27,9 +30,12 @@ __device__ __forceinline__ void code_slot(int r, int& word, int& shift) {
   shift = 8 * (e % 4) + 4 * ((e % 8) >= 4);
 }
 
+template <bool W8>
 __global__ __launch_bounds__(kPThreads) void k_group_quant_pack(
     const float* __restrict__ w, int64_t K, int64_t N, uint4* __restrict__ packed,
     float* __restrict__ fscale, int32_t* __restrict__ minmax) {
+  constexpr float kQmax = W8 ? 127.0f : 7.0f;
+  constexpr int kQ = W8 ? 127 : 7;
   const int64_t j = (int64_t)blockIdx.x * kPThreads + threadIdx.x;
   const int64_t l = blockIdx.y;
   const int64_t G = K / kGroup;
@@ -44,23 +50,39 @@ __global__ __launch_bounds__(kPThreads) void k_group_quant_pack(
       v[r] = col[(int64_t)r * N];
       a = fmaxf(a, fabsf(v[r]));
     }
-    s = a / 7.0f;
-    uint32_t words[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) words[i] = 0u;
-#pragma unroll
-    for (int r = 0; r < kGroup; ++r) {
-      int code = 0;
-      if (s != 0.0f) code = clamp_int((int)round_away(v[r] / s), -7, 7);
-      int word, shift;
-      code_slot(r, word, shift);
-      words[word] |= ((uint32_t)code & 0xFu) << shift;
-    }
+    s = a / kQmax;
     const int64_t t = j / 16, c = j % 16;
-    uint4* blk = packed + (t * G + l) * 64 + c;
+    if constexpr (W8) {
+      // half h, slot sl = (r % 64) / 16: lane 16*sl + c holds codes r = 64h + 16sl .. +15
+      uint4* blk = packed + (t * G + l) * 128 + c;
 #pragma unroll
-    for (int sl = 0; sl < 4; ++sl)
-      blk[16 * sl] = make_uint4(words[4 * sl], words[4 * sl + 1], words[4 * sl + 2], words[4 * sl + 3]);
+      for (int q = 0; q < 8; ++q) {
+        uint32_t wd[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          int code = 0;
+          if (s != 0.0f) code = clamp_int((int)round_away(v[16 * q + e] / s), -kQ, kQ);
+          wd[e / 4] |= ((uint32_t)code & 0xFFu) << (8 * (e % 4));
+        }
+        blk[(q / 4) * 64 + 16 * (q % 4)] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+      }
+    } else {
+      uint32_t words[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) words[i] = 0u;
+#pragma unroll
+      for (int r = 0; r < kGroup; ++r) {
+        int code = 0;
+        if (s != 0.0f) code = clamp_int((int)round_away(v[r] / s), -kQ, kQ);
+        int word, shift;
+        code_slot(r, word, shift);
+        words[word] |= ((uint32_t)code & 0xFu) << shift;
+      }
+      uint4* blk = packed + (t * G + l) * 64 + c;
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl)
+        blk[16 * sl] = make_uint4(words[4 * sl], words[4 * sl + 1], words[4 * sl + 2], words[4 * sl + 3]);
+    }
     fscale[l * N + j] = s;
   }
   // min over positive scales and max over all scales, as ordered float bits
@@ -85,12 +107,18 @@ __global__ __launch_bounds__(kPThreads) void k_integer_scales(
   if (i < count) iscale[i] = (int32_t)round_away(fscale[i] * alpha);   // exact product: alpha = 2^n
 }
 
-hipError_t launch_group_quant_pack(const float* w, int64_t K, int64_t N, uint8_t* packed,
-                                   float* fscale, int32_t* iscale, hipStream_t stream) {
+hipError_t launch_group_quant_pack(bool int8_codes, const float* w, int64_t K, int64_t N,
+                                   void* packed, float* fscale, int32_t* iscale,
+                                   hipStream_t stream) {
   hipLaunchKernelGGL(k_init_minmax, dim3(1), dim3(1), 0, stream, iscale);
   dim3 grid((unsigned)((N + kPThreads - 1) / kPThreads), (unsigned)(K / kGroup));
-  hipLaunchKernelGGL(k_group_quant_pack, grid, dim3(kPThreads), 0, stream, w, K, N,
-                     reinterpret_cast<uint4*>(packed), fscale, iscale);
+  uint4* out = static_cast<uint4*>(packed);
+  if (int8_codes)
+    hipLaunchKernelGGL(k_group_quant_pack<true>, grid, dim3(kPThreads), 0, stream, w, K, N, out,
+                       fscale, iscale);
+  else
+    hipLaunchKernelGGL(k_group_quant_pack<false>, grid, dim3(kPThreads), 0, stream, w, K, N, out,
+                       fscale, iscale);
   return hipGetLastError();
 }
 

@@ -253,12 +253,66 @@ int bgt_w8a8_gemm_zp(const uint8_t* qx, const float* sx, const int32_t* zx,
                      const int32_t* zw, const int32_t* colsum_w, int64_t M, int64_t N,
                      int64_t K, float* y, int32_t* acc_out, void* stream);
 
+/*
+ * bgt_pack_weights_int8 -- offline group-wise int8 weight quantization for the
+ * fine-grained W8A8 layer of the [IS] page's LLaMA-3 scheme (5.4: 8-bit
+ * weights for the down projection, groups of 128), with integer scales.
+ * Per column j and group l, the closed forms of bgt_pack_weights_int4 at
+ * q_max = 127:
+ *     s_lj = max |w| / 127,   q_kj = clip(round(w_kj / s_lj), -127, 127)   (s = 0 -> q = 0),
+ *     fscale[l][j] = s_lj,    iscale[l][j] = round(s_lj * alpha).
+ * alpha as in bgt_pack_weights_int4 (0 = the amplifier search). The scales
+ * are q_max ratio 127/7 smaller than the int4 ones, so the same alpha gives
+ * integer scales about 18 times smaller.
+ *
+ * Int8 fragment layout, N*K bytes. With G = K/128:
+ *     t = j/16, c = j%16, l = k/128, r = k%128,
+ *     h = r/64, s = (r%64)/16, e = r%16,
+ *     byte(k, j) = (((t*G + l)*2 + h)*64 + 16*s + c)*16 + e.
+ * Each (16-column tile, group) pair is one contiguous 2 KiB block of two
+ * 1 KiB halves (64 k each); within a half, 16 bytes per lane of a 64-wide
+ * wavefront.
+ *
+ *   w       K x N float32 (finite).
+ *   qw      N*K bytes, 16-byte aligned.  fscale, iscale: (K/128) x N.
+ * Returns BGT_ERR_RANGE if some iscale would reach 2^23,
+ * BGT_WARN_ACC_MAY_OVERFLOW when the worst-case accumulator
+ * 2064512 * G * max(iscale) (|q_x|, |q_w| <= 127, 128 products per group)
+ * reaches 2^31. Synchronous.
+ */
+int bgt_pack_weights_int8(const float* w, int64_t K, int64_t N, int64_t group, int alpha,
+                          int8_t* qw, float* fscale, int32_t* iscale, int* alpha_out,
+                          void* stream);
+
+/*
+ * bgt_w8a8_gemm_is -- fine-grained W8A8 GEMM with the Integer Scale epilogue
+ * ([IS] 5.4 LLaMA-3 scheme; epilogue of 方法 Fig. 3(c)):
+ *     p_ilj  = sum_{k in group l} qx[i][k] * q_w[k][j]          (int32, |p| < 2^23)
+ *     A_ij   = sum_l p_ilj * iscale[l][j]                        (int32, mod 2^32)
+ *     y_ij   = ((float)A_ij * sx[i]) * (1/alpha).
+ *
+ *   qx      M x K int8 (bgt_quantize_act SYM), sx [M] float32.
+ *   qw      the int8 fragment layout of bgt_pack_weights_int8.
+ *   iscale  (K/128) x N, elements of `width` bytes (1: uint8, 2: uint16,
+ *           4: int32), every value in [0, 2^23); 16-byte aligned.
+ *   alpha   power of two in [1, 2^30], the one the integer scales were made with.
+ *   y       M x N of element type y_type (fp32 result rounded once).
+ *   acc_out optional M x N int32 (NULL = not written): A_ij itself.
+ * Requirements: as bgt_w4a8_gemm_is; qx, qw, iscale, y, acc_out 16-byte aligned.
+ */
+int bgt_w8a8_gemm_is(const int8_t* qx, const float* sx, const int8_t* qw, const void* iscale,
+                     int width, int alpha, int64_t M, int64_t N, int64_t K, void* y, int y_type,
+                     int32_t* acc_out, void* stream);
+
+/* Diagnostics: name of the kernel bgt_w8a8_gemm_is launches for this shape. */
+const char* bgt_w8a8_is_kernel_name(int64_t M, int64_t N, int64_t K);
+
 /* Human-readable text of a status code (static storage). */
 const char* bgt_status_string(int status);
 
 /* ABI version of this header (major*100 + minor): 101 adds the narrow
  * integer-scale entry points, 102 the fused linear layer, 103 fp16 / bf16
- * activation and output types. */
+ * activation and output types, 104 the fine-grained W8A8 integer-scale GEMM. */
 int bgt_abi_version(void);
 
 /* Diagnostics: name of the GEMM kernel that bgt_w4a8_gemm_is (float_scale = 0)

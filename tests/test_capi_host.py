@@ -37,7 +37,7 @@ def test_status_strings(L):
     assert bgt.status_string(0) == "ok"
     for st in (-1, -2, -3, -4, -5, -6, -7, 1):
         assert "error" in bgt.status_string(st) or "warning" in bgt.status_string(st)
-    assert L.bgt_abi_version() == 103
+    assert L.bgt_abi_version() == 104
 
 
 def test_quantize_act_validation(L):
@@ -186,3 +186,50 @@ def test_python_binding_rejects_cpu_tensors():
     with pytest.raises((ValueError, TypeError)):
         bgt.w4a8_gemm_is(torch.zeros(2, 128, dtype=torch.int8), torch.ones(2), torch.zeros(1024, dtype=torch.uint8),
                          torch.zeros(1, 16, dtype=torch.int32), 1024, 16)
+
+
+def test_pack_int8_validation(L):
+    a = ctypes.c_int(0)
+    pk = L.bgt_pack_weights_int8
+
+    def call(w=FAKE, K=256, N=32, g=128, alpha=0, qw=FAKE, fs=FAKE, isc=FAKE, aout=True):
+        return pk(w, K, N, g, alpha, qw, fs, isc, ctypes.byref(a) if aout else None, None)
+
+    assert call(w=None) == bgt.BGT_ERR_NULL
+    assert call(qw=None) == bgt.BGT_ERR_NULL
+    assert call(aout=False) == bgt.BGT_ERR_NULL
+    assert call(g=256) == bgt.BGT_ERR_SHAPE
+    assert call(K=130) == bgt.BGT_ERR_SHAPE
+    assert call(N=8) == bgt.BGT_ERR_SHAPE
+    assert call(alpha=6) == bgt.BGT_ERR_ALPHA
+    assert call(qw=MIS) == bgt.BGT_ERR_ALIGN
+
+
+def test_w8a8_is_validation(L):
+    g = L.bgt_w8a8_gemm_is
+
+    def call(qx=FAKE, sx=FAKE, qw=FAKE, isc=FAKE, width=4, alpha=1 << 18, M=16, N=64, K=256,
+             y=FAKE, yt=0, acc=None):
+        return g(qx, sx, qw, isc, width, alpha, M, N, K, y, yt, acc, None)
+
+    assert call(qx=None) == bgt.BGT_ERR_NULL
+    assert call(qw=None) == bgt.BGT_ERR_NULL
+    assert call(isc=None) == bgt.BGT_ERR_NULL
+    assert call(y=None) == bgt.BGT_ERR_NULL
+    assert call(width=3) == bgt.BGT_ERR_MODE
+    assert call(yt=5) == bgt.BGT_ERR_MODE
+    assert call(M=0) == bgt.BGT_ERR_SHAPE
+    assert call(N=40) == bgt.BGT_ERR_SHAPE
+    assert call(K=100) == bgt.BGT_ERR_SHAPE
+    assert call(K=65536 + 128) == bgt.BGT_ERR_SHAPE
+    assert call(alpha=0) == bgt.BGT_ERR_ALPHA
+    assert call(alpha=3) == bgt.BGT_ERR_ALPHA
+    assert call(qx=MIS) == bgt.BGT_ERR_ALIGN
+    assert call(qw=MIS) == bgt.BGT_ERR_ALIGN
+    assert call(isc=MIS) == bgt.BGT_ERR_ALIGN
+    assert call(y=MIS) == bgt.BGT_ERR_ALIGN
+    assert call(acc=MIS) == bgt.BGT_ERR_ALIGN
+    assert bgt.w8a8_is_kernel_name(4, 4096, 14336) == "k_w8is_split"
+    assert bgt.w8a8_is_kernel_name(65, 4096, 14336) == "k_w8is_tiled"
+    assert bgt.w8a8_is_kernel_name(0, 4096, 14336) == "invalid shape"
+
