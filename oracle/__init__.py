@@ -265,6 +265,31 @@ def w8a8_gemm_is(qx, sx, codes, iscale, alpha: int, g: int = 128, rows=None, col
     return w4a8_gemm_is(qx, sx, codes, iscale, alpha, g, rows, cols)
 
 
+def moe_w4a8_gemm_is(qx, sx, codes, iscale, alpha: int, offs, tok, g: int = 128, cols=None):
+    """Grouped (mixture-of-experts) integer-scale GEMM: expert e's slots
+    offs[e] .. offs[e+1]-1 each multiply activation row tok[slot] by expert
+    e's weights (codes[e], K x N; iscale[e]), with the O3 definition; y rows
+    follow the slots. Returns (A int64 [R x ncols], y float32, overflow count)."""
+    offs = np.asarray(offs, np.int64)
+    tok = np.asarray(tok, np.int64)
+    E = len(offs) - 1
+    R = int(offs[-1])
+    N = codes.shape[2]
+    nc = N if cols is None else len(cols)
+    A = np.zeros((R, nc), np.int64)
+    y = np.zeros((R, nc), np.float32)
+    ov = 0
+    for e in range(E):
+        a, b = int(offs[e]), int(offs[e + 1])
+        if b == a:
+            continue
+        rows = tok[a:b]
+        Ae, ye, oe = w4a8_gemm_is(qx[rows], sx[rows], codes[e], iscale[e], alpha, g, cols=cols)
+        A[a:b], y[a:b] = Ae, ye
+        ov += oe
+    return A, y, ov
+
+
 def w4a8_gemm_fs(qx, sx, codes, fscale, g: int = 128, rows=None, cols=None):
     """Float-scale W4A8 GEMM (ascending-group fmaf chain). Parity unpinned beyond
     the shared integer partials and the error bound checked in the tests."""

@@ -28,6 +28,8 @@ STREAM_PERM = 2     # outlier-channel permutation
 STREAM_W = 3        # weight normals
 STREAM_W_OUT = 4    # weight outlier Bernoulli draws
 STREAM_LAYER = 10   # + layer index, for the decoder-block stack
+STREAM_ROUTE = 5    # router logits of the mixture-of-experts workload
+STREAM_EXPERT = 20  # + expert index, expert weights
 
 K_LAYER = 4096
 N_LAYER = 22016
@@ -35,6 +37,13 @@ GROUP = 128
 ALPHA = 1024
 DECODE_M = (1, 4, 16, 64, 256)
 PREFILL_M = (512, 1024, 2048, 4096)
+
+# Mixtral-8x7B experts: 8 experts per layer, 2 routed per token; the expert
+# FFN linears are w1 / w3 (hidden 4096 -> 14336) and w2 (14336 -> 4096)
+MIXTRAL_E = 8
+MIXTRAL_TOPK = 2
+MIXTRAL_HIDDEN = 4096
+MIXTRAL_FFN = 14336
 
 # LLaMA-2-7B decoder-block linears (in_features K, out_features N)
 LLAMA2_7B_BLOCK = (
@@ -133,3 +142,43 @@ def block_inputs(seed: int = 0, M: int = 1):
         w = weights(seed, k, n, std=0.02, stream=STREAM_LAYER + li)
         out.append((name, x, w))
     return out
+
+
+def moe_routing(seed: int, T: int, E: int = MIXTRAL_E, topk: int = MIXTRAL_TOPK,
+                skew: float = 0.5):
+    """Synthetic routing of T tokens to topk distinct experts each.
+
+    Router logits are N(0,1) per (token, expert) plus a fixed per-expert bias
+    N(0, skew^2), so some experts receive more tokens than others as trained
+    routers do; each token takes its topk largest logits (ties broken by the
+    lower expert index). Returns the (T, topk) int32 expert indices, largest
+    logit first.
+    """
+    g = rng(seed, STREAM_ROUTE)
+    bias = g.standard_normal(E) * skew
+    logits = g.standard_normal((T, E)) + bias[None, :]
+    order = np.argsort(-logits, axis=1, kind="stable")
+    return np.ascontiguousarray(order[:, :topk].astype(np.int32))
+
+
+def route_by_expert(experts: np.ndarray, E: int):
+    """Sort the (token, expert) pairs by expert, tokens in order within an
+    expert: returns offsets (E+1 int32, expert e's slots are offs[e] ..
+    offs[e+1]-1) and the token of each slot (R = T*topk int32)."""
+    T, topk = experts.shape
+    flat_e = experts.reshape(-1)
+    flat_t = np.repeat(np.arange(T, dtype=np.int32), topk)
+    order = np.argsort(flat_e, kind="stable")
+    tok = np.ascontiguousarray(flat_t[order].astype(np.int32))
+    counts = np.bincount(flat_e, minlength=E)
+    offs = np.zeros(E + 1, np.int32)
+    offs[1:] = np.cumsum(counts)
+    return offs, tok
+
+
+def expert_weights(seed: int, E: int, K: int, N: int, std: float = 0.02,
+                   outlier_prob: float = 0.001) -> np.ndarray:
+    """(E, K, N) float32 expert weight matrices, one stream per expert."""
+    return np.stack([weights(seed + 1000 * STREAM_EXPERT + e, K, N, std=std,
+                             outlier_prob=outlier_prob) for e in range(E)])
+

@@ -728,3 +728,74 @@ def test_w8is_searched_alpha_rule(orc):
     a = pw["alpha"]
     assert smin * a >= 1 and smin * (a // 2) < 1
     assert pw["iscale"].min() >= 1
+
+
+# ------------------------------------------- grouped (mixture-of-experts) IS GEMM
+# [IS] 5.3: the integer-scale W4A8 layer applied to the experts of Mixtral 8x7B.
+
+def _moe_case(seed, T, E, K, N, topk=2):
+    g = synth.rng(seed, 60)
+    qx = g.integers(-127, 128, size=(T, K)).astype(np.int8)
+    sx = g.uniform(0.001, 0.1, size=T).astype(np.float32)
+    codes = g.integers(-7, 8, size=(E, K, N)).astype(np.int8)
+    isc = g.integers(0, 300, size=(E, K // 128, N)).astype(np.int32)
+    offs, tok = synth.route_by_expert(synth.moe_routing(seed, T, E, topk), E)
+    return qx, sx, codes, isc, offs, tok
+
+
+def test_moe_routing_is_a_valid_top_k(orc):
+    ex = synth.moe_routing(3, 50, 8, 2)
+    assert ex.shape == (50, 2) and ex.min() >= 0 and ex.max() < 8
+    assert np.all(ex[:, 0] != ex[:, 1])
+    offs, tok = synth.route_by_expert(ex, 8)
+    assert offs[0] == 0 and offs[-1] == 100 and np.all(np.diff(offs) >= 0)
+    np.testing.assert_array_equal(np.bincount(tok, minlength=50), np.full(50, 2))
+    for e in range(8):
+        t = tok[offs[e]:offs[e + 1]]
+        assert np.all(np.diff(t) > 0)                      # tokens ascending, no repeats
+        assert all(e in ex[i] for i in t)
+
+
+def test_moe_single_expert_is_the_dense_gemm(orc):
+    qx, sx, codes, isc, _, _ = _moe_case(4, 9, 1, 256, 32, topk=1)
+    offs = np.array([0, 9], np.int32)
+    tok = np.arange(9, dtype=np.int32)
+    A, y, ov = orc.moe_w4a8_gemm_is(qx, sx, codes, isc, 1024, offs, tok)
+    A0, y0, ov0 = orc.w4a8_gemm_is(qx, sx, codes[0], isc[0], 1024)
+    np.testing.assert_array_equal(A, A0)
+    np.testing.assert_array_equal(y, y0)
+    assert ov == ov0 == 0
+
+
+def test_moe_each_slot_is_its_token_times_its_expert(orc):
+    T, E, K, N = 6, 4, 256, 16
+    qx, sx, codes, isc, offs, tok = _moe_case(5, T, E, K, N)
+    A, y, _ = orc.moe_w4a8_gemm_is(qx, sx, codes, isc, 1024, offs, tok)
+    for e in range(E):
+        for r in range(offs[e], offs[e + 1]):
+            t = tok[r]
+            # brute force with Python integers over k (independent of the grouping code)
+            for j in range(N):
+                ref = sum(int(qx[t, k]) * int(codes[e, k, j]) * int(isc[e, k // 128, j]) for k in range(K))
+                assert A[r, j] == ref
+            Ar, yr, _ = orc.w4a8_gemm_is(qx[t:t + 1], sx[t:t + 1], codes[e], isc[e], 1024)
+            np.testing.assert_array_equal(y[r], yr[0])
+
+
+def test_moe_token_permutation_permutes_rows(orc):
+    # relabelling the tokens (and the routing with them) leaves each slot's row unchanged
+    T, E, K, N = 12, 8, 128, 32
+    qx, sx, codes, isc, offs, tok = _moe_case(6, T, E, K, N)
+    _, y, _ = orc.moe_w4a8_gemm_is(qx, sx, codes, isc, 1024, offs, tok)
+    perm = synth.rng(6, 61).permutation(T)
+    inv = np.argsort(perm)
+    _, y2, _ = orc.moe_w4a8_gemm_is(qx[perm], sx[perm], codes, isc, 1024, offs, inv[tok].astype(np.int32))
+    np.testing.assert_array_equal(y, y2)
+
+
+def test_moe_experts_without_tokens(orc):
+    T, E, K, N = 1, 8, 128, 16
+    qx, sx, codes, isc, offs, tok = _moe_case(7, T, E, K, N)
+    assert (np.diff(offs) > 0).sum() == 2                  # one token reaches two experts
+    A, y, _ = orc.moe_w4a8_gemm_is(qx, sx, codes, isc, 1024, offs, tok)
+    assert A.shape == (2, N)
