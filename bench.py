@@ -35,7 +35,11 @@ the activation quantizer); --workload w8is (fine-grained W8A8 with integer
 scales at the LLaMA-3-8B down projection K=14336, N=4096, alpha=2^16: a
 decode step over M in {1,4,16,64} in GB/s with algorithmic bytes
 N*K + 4*G*N + M*K + 4*M + 4*M*N per GEMM, plus per-launch GEMM rates at
-M in {256,1024,4096}).
+M in {256,1024,4096}); --workload moe (the grouped W4A8-IS GEMM at the
+Mixtral-8x7B expert w1 shape, 8 experts, top-2 routing: a decode step over
+T in {1,4,16,64} tokens in GB/s, with algorithmic bytes the active experts'
+weights and scales + T*K + 4*T + routing + 4*R*N per launch, plus per-launch
+rates at T in {512,4096}).
 
 Profiling aids (not benchmark lines): --profile-m M runs only the
 quantizer and the integer-scale GEMM at that M (decode layer shape) for
@@ -545,6 +549,113 @@ def run_w8is(args, torch, bgt, dev):
     }, (x, w)
 
 
+MOE_K, MOE_N, MOE_E, MOE_TOPK = synth.MIXTRAL_HIDDEN, synth.MIXTRAL_FFN, synth.MIXTRAL_E, synth.MIXTRAL_TOPK
+MOE_DECODE_T = (1, 4, 16, 64)
+MOE_PREFILL_T = (512, 4096)
+
+
+def moe_bytes(T, R, n_active, N, K, E):
+    """Algorithmic bytes of one grouped launch: the weights and scales of the
+    experts that receive tokens, each token's codes and scale once, the
+    routing, and the R x N fp32 output."""
+    G = K // 128
+    return n_active * (N * K // 2 + 4 * G * N) + T * K + 4 * T + 4 * (E + 1) + 4 * R + 4 * R * N
+
+
+def run_moe(args, torch, bgt, dev):
+    """Grouped W4A8-IS GEMM at the Mixtral-8x7B expert w1/w3 shape (8 experts,
+    top-2, K=4096, N=14336, alpha 1024): one step is quant_act + grouped GEMM
+    for each T in {1, 4, 16, 64} tokens (GB/s); per-launch rates also at
+    T in {512, 4096} (TOPS)."""
+    K, N, E, topk = MOE_K, MOE_N, MOE_E, MOE_TOPK
+    Ts, Ps = list(MOE_DECODE_T), list(MOE_PREFILL_T)
+    x = synth.activations(700, max(Ps), K)
+    w = synth.expert_weights(701, E, K, N)
+    xd = torch.from_numpy(x).to(dev)
+    G = K // 128
+    packed = torch.empty((E, N * K // 2), dtype=torch.uint8, device=dev)
+    isc = torch.empty((E, G, N), dtype=torch.int32, device=dev)
+    fsc = torch.empty((E, G, N), dtype=torch.float32, device=dev)
+    for e in range(E):
+        bgt.pack_weights_int4(torch.from_numpy(w[e]).to(dev), alpha=synth.ALPHA, packed=packed[e],
+                              fscale=fsc[e], iscale=isc[e])
+    del w
+    per = packed.numel() + isc.numel() * 4
+    Rr = max(2, math.ceil(2 * MALL_BYTES / per))
+    rot = [(packed.clone(), isc.clone()) for _ in range(Rr)]
+    route = {}
+    for T in Ts + Ps:
+        offs, tok = synth.route_by_expert(synth.moe_routing(700 + T, T, E, topk), E)
+        route[T] = (torch.from_numpy(offs).to(dev), torch.from_numpy(tok).to(dev),
+                    int((np.diff(offs) > 0).sum()), len(tok))
+    xs = {T: xd[:T].contiguous() for T in Ts + Ps}
+    qbuf = {T: (torch.empty((T, K), dtype=torch.int8, device=dev),
+                torch.empty(T, dtype=torch.float32, device=dev)) for T in Ts + Ps}
+    ybuf = {T: torch.empty((route[T][3], N), dtype=torch.float32, device=dev) for T in Ts + Ps}
+    for T in Ts + Ps:
+        bgt.quantize_act(xs[T], q=qbuf[T][0], scale=qbuf[T][1])
+
+    def gemm(T, j):
+        pk, ic = rot[j % Rr]
+        offs, tok, _, _ = route[T]
+        q, s = qbuf[T]
+        bgt.w4a8_moe_gemm_is(q, s, offs, tok, pk, ic, synth.ALPHA, N, y=ybuf[T])
+
+    def step(k):
+        for i, T in enumerate(Ts):
+            q, s = qbuf[T]
+            bgt.quantize_act(xs[T], q=q, scale=s)
+            gemm(T, k * len(Ts) + i)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(k)
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms_step = graph_steps(torch, step, args.steps, args.warmup) if args.launch == "graph" else eager_ms
+
+    per_t = {T: graph_launch_us(torch, lambda j, T=T: gemm(T, j), 2 * Rr if T <= 64 else Rr,
+                                reps=5 if T <= 64 else 3) for T in Ts + Ps}
+    sweep = {}
+    for T in Ts + Ps:
+        us = float(np.mean(per_t[T]))
+        _, _, na, R = route[T]
+        b = moe_bytes(T, R, na, N, K, E)
+        sweep[str(T)] = {"gemm_us": round(us, 3), "experts_active": na, "slots": R,
+                         "gemm_GBps": round(b / us / 1e3, 1),
+                         "gemm_TOPS": round(2 * R * N * K / us / 1e6, 2),
+                         "hbm_frac": round(b / us / 1e3 / HBM_PEAK_GBS, 4),
+                         "mfma_frac": round(2 * R * N * K / us / 1e6 / INT8_PEAK_TOPS, 4),
+                         "kernel": bgt.w4a8_moe_kernel_name(T, K)}
+    step_bytes = sum(moe_bytes(T, route[T][3], route[T][2], N, K, E) + quant_bytes(T, K) for T in Ts)
+    durs = [u for T in Ts for u in per_t[T]]
+    avg_us = float(np.mean(durs))
+    avg_bytes = float(np.mean([moe_bytes(T, route[T][3], route[T][2], N, K, E) for T in Ts]))
+    achieved = avg_bytes / avg_us / 1e3
+    return {
+        "metric": "grouped (MoE) W4A8 integer-scale GEMM HBM GB/s, Mixtral-8x7B w1 K=4096 N=14336 E=8 top-2",
+        "value": round(step_bytes / (ms_step * 1e-3) / 1e9, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8xint4->int32",
+        "data": "synthetic (seeded; X ~N(0,1) + 1% channels x20, W ~N(0,0.02) + 0.1% x10, "
+                "top-2 of biased normal router logits)",
+        "config": {"workload": "MoE decode sweep: quant_act + grouped W4A8-IS GEMM, Mixtral-8x7B "
+                               "experts (w1: K=4096 N=14336, E=8, top-2), T in {1,4,16,64} tokens per step",
+                   "launch": "hip_graph" if args.launch == "graph" else "eager",
+                   "weight_buffers_rotated": Rr},
+        "eager": {"ms_per_step": round(eager_ms, 4),
+                  "value": round(step_bytes / (eager_ms * 1e-3) / 1e9, 1)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": bgt.w4a8_moe_kernel_name(1, K), "launch_T": Ts,
+                     "avg_launch_us": round(avg_us, 3), "bytes_per_launch": int(avg_bytes)},
+        "sweep": sweep,
+    }, (x, None)
+
+
 def run_profile_m(args, torch, bgt, dev, M):
     """Quantizer + integer-scale GEMM at one M of the decode layer, nothing else."""
     K, N = synth.K_LAYER, synth.N_LAYER
@@ -580,7 +691,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "w8a8", "w8is"])
+    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "w8a8", "w8is", "moe"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--iscale-bits", type=int, default=32, choices=[8, 16, 32],
                     help="decode workload: integer scales stored as uint8 / uint16 / int32 "
@@ -620,6 +731,8 @@ def main():
         out, (x, w) = run_prefill(args, torch, bgt, dev)
     elif args.workload == "w8is":
         out, (x, w) = run_w8is(args, torch, bgt, dev)
+    elif args.workload == "moe":
+        out, (x, w) = run_moe(args, torch, bgt, dev)
     else:
         out, (x, w) = run_w8a8(args, torch, bgt, dev)
     if not args.no_cpu_baseline and args.workload in ("decode", "prefill"):

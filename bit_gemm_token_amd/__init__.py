@@ -12,6 +12,7 @@ Entry points (same names as the C ABI without the ``bgt_`` prefix):
     w4a8_gemm_is(qx, sx, packed, iscale, alpha, N)   -> y
     w4a8_gemm_fs(qx, sx, packed, fscale, N)          -> y
     w8a8_gemm_zp(qx, sx, zx, rowsum_x, qw, sw, zw, colsum_w) -> y
+    w4a8_moe_gemm_is(qx, sx, offsets, slot_token, packed, iscale, alpha, N) -> y
     pack_weights_int8(w, alpha=0)          -> dict(qw, fscale, iscale, alpha, status)
     w8a8_gemm_is(qx, sx, qw, iscale, alpha, N)       -> y
 """
@@ -45,8 +46,10 @@ EXPORTED = (
     "bgt_narrow_iscale", "bgt_w4a8_gemm_is_narrow", "bgt_w4a8_linear_is", "bgt_w4a8_linear_fused",
     "bgt_quantize_act_ex", "bgt_w4a8_gemm_is_ex", "bgt_w4a8_gemm_fs_ex",
     "bgt_pack_weights_int8", "bgt_w8a8_gemm_is", "bgt_w8a8_is_kernel_name",
+    "bgt_w4a8_moe_gemm_is", "bgt_w4a8_moe_kernel_name",
 )
-_NAMES = ("bgt_status_string", "bgt_w4a8_kernel_name", "bgt_w8a8_is_kernel_name")
+_NAMES = ("bgt_status_string", "bgt_w4a8_kernel_name", "bgt_w8a8_is_kernel_name",
+          "bgt_w4a8_moe_kernel_name")
 
 _lib = None
 
@@ -85,6 +88,9 @@ def lib():
         L.bgt_pack_weights_int8.argtypes = [P, I64, I64, I64, I, P, P, P, ctypes.POINTER(I), P]
         L.bgt_w8a8_gemm_is.argtypes = [P, P, P, P, I, I, I64, I64, I64, P, I, P, P]
         L.bgt_w8a8_is_kernel_name.argtypes = [I64, I64, I64]
+        L.bgt_w4a8_moe_gemm_is.argtypes = [P, P, I64, P, P, I64, I64, P, P, I, I, I64, I64, P, I,
+                                           P, P]
+        L.bgt_w4a8_moe_kernel_name.argtypes = [I64, I64]
         for f in EXPORTED:
             getattr(L, f).restype = ctypes.c_char_p if f in _NAMES else I
         _lib = L
@@ -416,3 +422,43 @@ def w8a8_gemm_is(qx, sx, qw, iscale, alpha: int, N: int, y=None, acc_out=None, o
                                 _stream(qx.device))
     _raise("bgt_w8a8_gemm_is", st)
     return y
+
+
+def w4a8_moe_kernel_name(T: int, K: int) -> str:
+    """Name of the kernel a grouped W4A8 call with T tokens launches."""
+    return lib().bgt_w4a8_moe_kernel_name(int(T), int(K)).decode()
+
+
+def w4a8_moe_gemm_is(qx, sx, offsets, slot_token, packed, iscale, alpha: int, N: int, y=None,
+                     acc_out=None, out_dtype=None):
+    """Grouped (mixture-of-experts) W4A8 GEMM with the integer-scale epilogue.
+
+    qx (T x K int8) and sx (T) are the tokens; offsets (E+1 int32) and
+    slot_token (R int32) the expert-sorted routing; packed (E x N*K/2 uint8)
+    and iscale (E x K/128 x N; uint8, uint16 or int32) the experts' weights.
+    Returns y (R x N; float32, float16 or bfloat16), row r for slot r."""
+    torch = _torch()
+    widths = {torch.uint8: 1, torch.uint16: 2, torch.int32: 4}
+    if not isinstance(iscale, torch.Tensor) or iscale.dtype not in widths:
+        raise TypeError("iscale must be a uint8, uint16 or int32 tensor")
+    _check(qx, "qx", torch.int8)
+    T, K = qx.shape
+    _check(sx, "sx", torch.float32, (T,))
+    _check(offsets, "offsets", torch.int32)
+    E = offsets.numel() - 1
+    _check(slot_token, "slot_token", torch.int32)
+    R = slot_token.numel()
+    _check(packed, "packed", torch.uint8, (E, N * K // 2))
+    _check(iscale, "iscale", iscale.dtype, (E, K // GROUP, N))
+    if y is None:
+        y = torch.empty((R, N), dtype=out_dtype or torch.float32, device=qx.device)
+    _check(y, "y", y.dtype, (R, N))
+    yt = _elem_type(y, "y")
+    if acc_out is not None:
+        _check(acc_out, "acc_out", torch.int32, (R, N))
+    st = lib().bgt_w4a8_moe_gemm_is(_ptr(qx), _ptr(sx), T, _ptr(offsets), _ptr(slot_token), E, R,
+                                    _ptr(packed), _ptr(iscale), widths[iscale.dtype], int(alpha),
+                                    N, K, _ptr(y), yt, _ptr(acc_out), _stream(qx.device))
+    _raise("bgt_w4a8_moe_gemm_is", st)
+    return y
+

@@ -43,7 +43,7 @@ int searched_alpha_log2(float smin) {
 
 extern "C" {
 
-int bgt_abi_version(void) { return 104; }
+int bgt_abi_version(void) { return 105; }
 
 int bgt_w4a8_linear_fused(int64_t M, int64_t K, const void* x, int64_t ldx) {
   return bgt::w4a8_linear_fused(M, K, x, ldx) ? 1 : 0;
@@ -232,6 +232,33 @@ int bgt_narrow_iscale(const int32_t* iscale, int64_t count, int width, void* out
   for (int32_t v : h)
     if (v < 0 || v > top) return BGT_ERR_RANGE;
   return hip_status(bgt::launch_narrow_scales(iscale, count, width, out, s));
+}
+
+int bgt_w4a8_moe_gemm_is(const int8_t* qx, const float* sx, int64_t T,
+                         const int32_t* expert_offsets, const int32_t* slot_token, int64_t E,
+                         int64_t R, const uint8_t* packed, const void* iscale, int width,
+                         int alpha, int64_t N, int64_t K, void* y, int y_type, int32_t* acc_out,
+                         void* stream) {
+  if (!qx || !sx || !expert_offsets || !slot_token || !packed || !iscale || !y)
+    return BGT_ERR_NULL;
+  if (width != 1 && width != 2 && width != 4) return BGT_ERR_MODE;
+  if (!valid_type(y_type)) return BGT_ERR_MODE;
+  int st = check_gemm_shape(T, N, K, 65536);
+  if (st != BGT_OK) return st;
+  if (E < 1 || E > 256 || R < 1 || R > T * E || R > (1 << 24)) return BGT_ERR_SHAPE;
+  if (!pow2_alpha(alpha)) return BGT_ERR_ALPHA;
+  if (!aligned16(qx) || !aligned16(packed) || !aligned16(iscale) || !aligned16(y) ||
+      (acc_out && !aligned16(acc_out)))
+    return BGT_ERR_ALIGN;
+  return hip_status(bgt::launch_w4a8_moe(qx, sx, T, expert_offsets, slot_token, E, R, packed,
+                                         iscale, width, alpha, N, K, bgt::OutY{y, y_type},
+                                         acc_out, static_cast<hipStream_t>(stream)));
+}
+
+const char* bgt_w4a8_moe_kernel_name(int64_t T, int64_t K) {
+  if (T < 1 || T > 65536 || K < BGT_GROUP || K > 65536 || K % BGT_GROUP != 0)
+    return "invalid shape";
+  return bgt::w4a8_moe_kernel_name(T, K);
 }
 
 int bgt_w8a8_gemm_is(const int8_t* qx, const float* sx, const int8_t* qw, const void* iscale,

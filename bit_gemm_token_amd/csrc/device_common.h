@@ -53,6 +53,23 @@ struct OutY {
   }
 };
 
+// Expert routing of a grouped (mixture-of-experts) GEMM. The routed slots are
+// sorted by expert: the slots of expert e are offs[e] .. offs[e+1]-1; slot r
+// multiplies activation row tok[r] with expert e's weights and writes output
+// row r. Expert e's packed weights and scales start wstride bytes and sstride
+// elements after expert e-1's. Kernels clamp offsets to [0, R] and token
+// indices to [0, T-1], so malformed routing cannot reach outside the buffers.
+struct Route {
+  const int32_t* offs;
+  const int32_t* tok;
+  int E, T, R;
+  int64_t wstride, sstride;
+};
+
+__device__ __forceinline__ int clamp_route(int v, int lo, int hi) {
+  return v < lo ? lo : (v > hi ? hi : v);
+}
+
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 

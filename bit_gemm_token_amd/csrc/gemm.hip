@@ -367,12 +367,12 @@ __device__ __forceinline__ uint4 lds_read_own_copy(const uint4* p) {
 }
 
 
-template <int WM, int WN, int TMW, int TNW, bool FS, typename ST>
+template <int WM, int WN, int TMW, int TNW, bool FS, typename ST, bool GR = false>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_w4a8_prefill(
     const int8_t* __restrict__ qx, const float* __restrict__ sx,
     const uint4* __restrict__ packed, const ST* __restrict__ iscale,
     const float* __restrict__ fscale, float inv_alpha, int M, int N, int K,
-    OutY y, int32_t* __restrict__ acc_out) {
+    OutY y, int32_t* __restrict__ acc_out, Route rt) {
   static_assert(TMW == 2 && TNW == 2, "four 32 x 32 blocks per wave");
   constexpr int NW = WM * WN, NT = NW * 64;
   constexpr int BM = WM * TMW * 32, BN = WN * TNW * 32, NB = TMW * TNW;
@@ -398,7 +398,26 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
   const int wm = wave / WN, wn = wave % WN;
   const int lr = lane % 32, hf = lane / 32;
   int tm, tn;
-  tile_of(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
+  // grouped GEMM: the grid covers ceil(R/BM) + E row tiles, an upper bound on
+  // the sum over experts of ceil(rows/BM); row tile tm is found in the list of
+  // the experts' tiles (experts in order), and tiles past its end exit
+  tile_of(blockIdx.x, GR ? (rt.R + BM - 1) / BM + rt.E : (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
+  int r0 = 0;
+  if constexpr (GR) {
+    int e = 0, a = 0;
+    for (; e < rt.E; ++e) {
+      a = clamp_route(rt.offs[e], 0, rt.R);
+      const int b = clamp_route(rt.offs[e + 1], a, rt.R);
+      const int nt = (b - a + BM - 1) / BM;
+      if (tm < nt) { M = b - a; break; }
+      tm -= nt;
+    }
+    if (e == rt.E) return;
+    r0 = a;
+    packed += e * rt.wstride / 16;
+    if (FS) fscale += e * rt.sstride;
+    else iscale += e * rt.sstride;
+  }
   const int m0 = tm * BM, n0 = tn * BN;
 
   // ---- copies of one group (a group index past the end is clamped to the
@@ -406,13 +425,16 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
   // they keep the number of copies per step fixed for the wait counts)
   // A: lane L of block b fills row 8b + L/8, chunk slot L%8, with the row's
   // global chunk (L%8) ^ ((row / 2) % 8), row = 8b + L/8.
-  const int8_t* abase = qx + (int64_t)m0 * K;
-  int aoff[A_INSTR];
+  // (grouped: the slot's activation row, as a 64-bit offset from X)
+  using AO = typename std::conditional<GR, int64_t, int>::type;
+  const int8_t* abase = GR ? qx : qx + (int64_t)m0 * K;
+  AO aoff[A_INSTR];
 #pragma unroll
   for (int i = 0; i < A_INSTR; ++i) {
     const int r = 8 * (i * NW + wave) + lane / 8;
     const int rr = m0 + r < M ? r : M - 1 - m0;
-    aoff[i] = rr * K + 16 * ((lane % 8) ^ ((r >> 1) & 7));
+    const AO ro = GR ? (AO)clamp_route(rt.tok[r0 + m0 + rr], 0, rt.T - 1) * K : (AO)rr * K;
+    aoff[i] = ro + 16 * ((lane % 8) ^ ((r >> 1) & 7));
   }
   // scales: wave w copies the 64-column slice w % (BN/64) into a 256-byte
   // slot (several waves write the same slice with the same values); each lane
@@ -603,7 +625,8 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int i = m0 + wm * (TMW * 32) + a * 32 + 8 * (r / 4) + 4 * hf + (r % 4);
-      srow[a][r] = sx[i < M ? i : M - 1];
+      const int ic = i < M ? i : M - 1;
+      srow[a][r] = sx[GR ? clamp_route(rt.tok[r0 + ic], 0, rt.T - 1) : ic];
     }
   const bool full = m0 + BM <= M && n0 + BN <= N;
 #pragma unroll
@@ -614,7 +637,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
     for (int r = 0; r < 16; ++r) {
       const int i = m0 + wm * (TMW * 32) + a * 32 + 8 * (r / 4) + 4 * hf + (r % 4);
       if (!full && (i >= M || j >= N)) continue;
-      const int64_t o = (int64_t)i * N + j;
+      const int64_t o = (int64_t)(r0 + i) * N + j;
       if (FS) {
         y.put(o, facc[k][r] * srow[a][r]);
       } else {
@@ -827,13 +850,14 @@ __global__ __launch_bounds__(NW * 64) void k_w8a8_zp(
 //      ascending fma chain).
 // Every load is a register load, so the compiler's wait counts stay exact.
 // =====================================================================
-template <bool FS, int W, int D, int G, int MR, typename ST, bool FQ, int IT>
+template <bool FS, int W, int D, int G, int MR, typename ST, bool FQ, int IT, bool GR = false>
 __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
     const int8_t* __restrict__ qx, const float* __restrict__ sx,
     const uint4* __restrict__ packed, const ST* __restrict__ iscale,
     const float* __restrict__ fscale, float inv_alpha, int M, int N,
     OutY y, int32_t* __restrict__ acc_out,
-    const void* __restrict__ xf, int ldx, int8_t* __restrict__ q_out, float* __restrict__ s_out) {
+    const void* __restrict__ xf, int ldx, int8_t* __restrict__ q_out, float* __restrict__ s_out,
+    Route rt) {
   constexpr int CGM = MR == 1 ? 32 : 8;
   constexpr int CG = G < CGM ? G : CGM;              // groups per X chunk (<= 64 KiB)
   constexpr int NCH = G / CG;                        // chunks
@@ -847,6 +871,7 @@ __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
   static_assert(G % D == 0 && G % CG == 0 && CFR % W == 0, "shape of the pipeline");
   static_assert(SCW % SEL == 0, "scale staging");
   static_assert(!FQ || (MR == 1 && NCH == 1 && !FS), "fused quantization: one row block, one chunk");
+  static_assert(!(GR && FQ), "grouped GEMM takes quantized activations");
   constexpr int NBUF = NCH > 1 ? 2 : 1;
   __shared__ __align__(16) int8_t sA[NBUF * CFR * 1024];
   __shared__ __align__(16) SL sS[G * SCW];           // [group][column of the workgroup]
@@ -860,15 +885,41 @@ __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
   const bool tvalid = t < T;
   const int tc = tvalid ? t : T - 1;
 
+  // grouped GEMM: this workgroup serves expert blockIdx.y, whose slots are
+  // r0 .. r0+M-1 (at most the 16*MR rows of a workgroup); an expert without
+  // slots reads nothing
+  int r0 = 0;
+  if constexpr (GR) {
+    const int e = blockIdx.y;
+    r0 = clamp_route(rt.offs[e], 0, rt.R);
+    const int r1 = clamp_route(rt.offs[e + 1], r0, rt.R);
+    M = r1 - r0 < 16 * MR ? r1 - r0 : 16 * MR;
+    if (M == 0) return;
+    packed += e * rt.wstride / 16;
+    if (FS) fscale += e * rt.sstride;
+    else iscale += e * rt.sstride;
+  }
+
   // ---- X chunk staging: this wave's fragments f = wave + W*i of chunk ch
-  // (32-bit offsets from the X base)
+  // (32-bit offsets from the X base; grouped: the rows of the expert's slots,
+  // looked up once)
+  int xo[GR ? FPW : 1];
+  if constexpr (GR) {
+#pragma unroll
+    for (int i = 0; i < FPW; ++i) {
+      const int f = wave + W * i, rb = (f / 2) % MR;
+      const int row = 16 * rb + c < M ? 16 * rb + c : M - 1;
+      xo[i] = clamp_route(rt.tok[r0 + row], 0, rt.T - 1) * K;
+    }
+  }
   v4i xa[FPW];
   auto load_chunk = [&](int ch) {
 #pragma unroll
     for (int i = 0; i < FPW; ++i) {
       const int f = wave + W * i, gl = f / (2 * MR), rb = (f / 2) % MR, h = f % 2;
       const int row = 16 * rb + c < M ? 16 * rb + c : M - 1;
-      xa[i] = load_v4i(qx + (row * K + 128 * (ch * CG + gl) + 64 * h + 16 * s4));
+      const int ro = GR ? xo[GR ? i : 0] : row * K;
+      xa[i] = load_v4i(qx + (ro + 128 * (ch * CG + gl) + 64 * h + 16 * s4));
     }
   };
   auto store_chunk = [&](int buf) {
@@ -992,7 +1043,9 @@ __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
     if (threadIdx.x >= M && threadIdx.x < 16) sX[threadIdx.x] = 0.0f;
   } else {
     // token scales of the (at most 64) rows, read back from LDS at the end
-    const float sxi = threadIdx.x < 16 * MR ? sx[threadIdx.x < M ? threadIdx.x : M - 1] : 0.0f;
+    const int ti = threadIdx.x < M ? threadIdx.x : M - 1;
+    const int tr = GR ? clamp_route(rt.tok[r0 + ti], 0, rt.T - 1) : ti;
+    const float sxi = threadIdx.x < 16 * MR ? sx[tr] : 0.0f;
     store_chunk(0);
     if (threadIdx.x < 16 * MR) sX[threadIdx.x] = sxi;
   }
@@ -1069,7 +1122,7 @@ __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * rb + 4 * s4 + r;
         if (i >= M) continue;
-        const int64_t o = (int64_t)i * N + j;
+        const int64_t o = (int64_t)(r0 + i) * N + j;
         const float si = sX[i];
         if (FS) {
           y.put(o, facc[rb][r] * si);
@@ -1226,13 +1279,13 @@ static void launch_decode(int mr, dim3 grid, dim3 block, hipStream_t stream, con
   float* ns = nullptr;
   switch (mr) {
     case 1: hipLaunchKernelGGL((k_w4a8_decode<FS, kDecodeW, decode_depth(1), G, 1, ST, false, kF32>), grid, block, 0, stream,
-                               qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out, nx, 0, nq, ns); break;
+                               qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out, nx, 0, nq, ns, Route{}); break;
     case 2: hipLaunchKernelGGL((k_w4a8_decode<FS, kDecodeW, decode_depth(2), G, 2, ST, false, kF32>), grid, block, 0, stream,
-                               qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out, nx, 0, nq, ns); break;
+                               qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out, nx, 0, nq, ns, Route{}); break;
     case 3: hipLaunchKernelGGL((k_w4a8_decode<FS, kDecodeW, decode_depth(3), G, 3, ST, false, kF32>), grid, block, 0, stream,
-                               qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out, nx, 0, nq, ns); break;
+                               qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out, nx, 0, nq, ns, Route{}); break;
     default: hipLaunchKernelGGL((k_w4a8_decode<FS, kDecodeW, decode_depth(4), G, 4, ST, false, kF32>), grid, block, 0, stream,
-                                qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out, nx, 0, nq, ns); break;
+                                qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out, nx, 0, nq, ns, Route{}); break;
   }
 }
 
@@ -1258,7 +1311,7 @@ static void launch_w4a8_t(const int8_t* qx, const float* sx, const uint8_t* pack
     const uint4* pk = reinterpret_cast<const uint4*>(packed);
     const int tiles = ((M + 255) / 256) * ((N + 127) / 128);
     hipLaunchKernelGGL((k_w4a8_prefill<4, 2, 2, 2, FS, ST>), dim3(tiles), dim3(512), 0, stream,
-                       qx, sx, pk, iscale, fscale, inv_alpha, M, N, K, y, acc_out);
+                       qx, sx, pk, iscale, fscale, inv_alpha, M, N, K, y, acc_out, Route{});
   }
 }
 
@@ -1295,11 +1348,11 @@ static void launch_linear_fused(const void* x, int ldx, const uint8_t* packed, c
   if (K / kGroup == 32)
     hipLaunchKernelGGL((k_w4a8_decode<false, kDecodeW, decode_depth(1), 32, 1, ST, true, IT>), grid,
                        block, 0, stream, nullptr, nullptr, pk, iscale, nullptr, inv_alpha, M, N,
-                       y, nullptr, x, ldx, q_out, s_out);
+                       y, nullptr, x, ldx, q_out, s_out, Route{});
   else
     hipLaunchKernelGGL((k_w4a8_decode<false, kDecodeW, decode_depth(1), 16, 1, ST, true, IT>), grid,
                        block, 0, stream, nullptr, nullptr, pk, iscale, nullptr, inv_alpha, M, N,
-                       y, nullptr, x, ldx, q_out, s_out);
+                       y, nullptr, x, ldx, q_out, s_out, Route{});
 }
 
 bool w4a8_linear_fused(int64_t M, int64_t K, const void* x, int64_t ldx) {
@@ -1343,6 +1396,68 @@ hipError_t launch_w4a8_linear(const void* x, int x_type, int64_t ldx, const uint
   else
     launch_linear_fused_st<kF32>(x, ld, packed, iscale, iscale_bytes, inv_alpha, M, N, K, q_out, s_out, y, stream);
   return hipGetLastError();
+}
+
+// Grouped (mixture-of-experts) integer-scale GEMM: T <= 64 activation rows
+// (so every expert has at most 64 slots) on the decode path takes the decode
+// kernel with one workgroup row per expert; otherwise the tiled kernel over
+// the experts' row tiles.
+template <typename ST>
+static void launch_moe_t(const int8_t* qx, const float* sx, const uint8_t* packed,
+                         const ST* iscale, float inv_alpha, int N, int K, const Route& rt,
+                         OutY y, int32_t* acc_out, hipStream_t stream) {
+  const uint4* pk = reinterpret_cast<const uint4*>(packed);
+  const int G = K / kGroup;
+  if (rt.T <= 64 && (G == 16 || G == 32)) {
+    const int mr = (rt.T + 15) / 16;
+    const dim3 grid((N / 16 + kDecodeW - 1) / kDecodeW, rt.E), block(kDecodeW * kWave);
+    const void* nx = nullptr;
+    int8_t* nq = nullptr;
+    float* ns = nullptr;
+    const float* nf = nullptr;
+#define BGT_MOE_DECODE(GG, MRR)                                                                  \
+  hipLaunchKernelGGL((k_w4a8_decode<false, kDecodeW, decode_depth(MRR), GG, MRR, ST, false, kF32, \
+                                    true>),                                                      \
+                     grid, block, 0, stream, qx, sx, pk, iscale, nf, inv_alpha, 0, N, y, acc_out, \
+                     nx, 0, nq, ns, rt)
+    if (G == 32) {
+      if (mr == 1) BGT_MOE_DECODE(32, 1);
+      else if (mr == 2) BGT_MOE_DECODE(32, 2);
+      else BGT_MOE_DECODE(32, 4);
+    } else {
+      if (mr == 1) BGT_MOE_DECODE(16, 1);
+      else if (mr == 2) BGT_MOE_DECODE(16, 2);
+      else BGT_MOE_DECODE(16, 4);
+    }
+#undef BGT_MOE_DECODE
+    return;
+  }
+  const int tiles = ((rt.R + 255) / 256 + rt.E) * ((N + 127) / 128);
+  hipLaunchKernelGGL((k_w4a8_prefill<4, 2, 2, 2, false, ST, true>), dim3(tiles), dim3(512), 0,
+                     stream, qx, sx, pk, iscale, nullptr, inv_alpha, 0, N, K, y, acc_out, rt);
+}
+
+hipError_t launch_w4a8_moe(const int8_t* qx, const float* sx, int64_t T, const int32_t* offs,
+                           const int32_t* tok, int64_t E, int64_t R, const uint8_t* packed,
+                           const void* iscale, int iscale_bytes, int alpha, int64_t N, int64_t K,
+                           OutY y, int32_t* acc_out, hipStream_t stream) {
+  const float inv_alpha = 1.0f / (float)alpha;   // exact: alpha = 2^n
+  Route rt{offs, tok, (int)E, (int)T, (int)R, N * K / 2, (K / kGroup) * N};
+  if (iscale_bytes == 4)
+    launch_moe_t(qx, sx, packed, static_cast<const int32_t*>(iscale), inv_alpha, (int)N, (int)K,
+                 rt, y, acc_out, stream);
+  else if (iscale_bytes == 2)
+    launch_moe_t(qx, sx, packed, static_cast<const uint16_t*>(iscale), inv_alpha, (int)N, (int)K,
+                 rt, y, acc_out, stream);
+  else
+    launch_moe_t(qx, sx, packed, static_cast<const uint8_t*>(iscale), inv_alpha, (int)N, (int)K,
+                 rt, y, acc_out, stream);
+  return hipGetLastError();
+}
+
+const char* w4a8_moe_kernel_name(int64_t T, int64_t K) {
+  const int64_t G = K / kGroup;
+  return T <= 64 && (G == 16 || G == 32) ? "k_w4a8_decode<IS,grouped>" : "k_w4a8_prefill<4,2,2,2,IS,grouped>";
 }
 
 hipError_t launch_w8a8_zp(const uint8_t* qx, const float* sx, const int32_t* zx,

@@ -49,6 +49,15 @@ hipError_t launch_narrow_scales(const int32_t* in, int64_t count, int out_bytes,
 // name of the kernel a W4A8 GEMM of this shape dispatches to (diagnostics)
 const char* w4a8_kernel_name(int64_t M, int64_t K, bool float_scale);
 
+// grouped (mixture-of-experts) W4A8 integer-scale GEMM: E experts' packed
+// weights and scales back to back; slots sorted by expert (offs: E+1 offsets,
+// tok: the activation row of each of the R slots); y has R rows
+hipError_t launch_w4a8_moe(const int8_t* qx, const float* sx, int64_t T, const int32_t* offs,
+                           const int32_t* tok, int64_t E, int64_t R, const uint8_t* packed,
+                           const void* iscale, int iscale_bytes, int alpha, int64_t N, int64_t K,
+                           OutY y, int32_t* acc_out, hipStream_t stream);
+const char* w4a8_moe_kernel_name(int64_t T, int64_t K);
+
 // fine-grained W8A8 with the integer-scale epilogue; qw in the int8 fragment
 // layout of bgt_pack_weights_int8, iscale of iscale_bytes bytes per element
 hipError_t launch_w8a8_is(const int8_t* qx, const float* sx, const int8_t* qw, const void* iscale,

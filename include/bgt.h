@@ -254,6 +254,42 @@ int bgt_w8a8_gemm_zp(const uint8_t* qx, const float* sx, const int32_t* zx,
                      int64_t K, float* y, int32_t* acc_out, void* stream);
 
 /*
+ * bgt_w4a8_moe_gemm_is -- grouped (mixture-of-experts) W4A8 GEMM with the
+ * Integer Scale epilogue: the layer of [IS] 5.3 (the integer-scale W4A8
+ * scheme applied to Mixtral 8x7B), where each token is routed to a few of E
+ * experts and every expert is its own fine-grained W4A8 linear layer.
+ * The R routed (token, expert) slots are sorted by expert; for every slot r
+ * of expert e (expert_offsets[e] <= r < expert_offsets[e+1]):
+ *     y[r][j] = the integer-scale output of bgt_w4a8_gemm_is for activation
+ *               row slot_token[r] of (qx, sx) and expert e's weights.
+ *
+ *   qx, sx          T x K int8 codes and [T] scales of the tokens (bgt_quantize_act SYM).
+ *   expert_offsets  [E+1] int32 on the device: 0 = offs[0] <= ... <= offs[E] = R.
+ *   slot_token      [R] int32 on the device, each in [0, T); a token appears at
+ *                   most once per expert (so no expert has more than T slots).
+ *   packed          E x (N*K/2) bytes: expert e's bgt_pack_weights_int4 layout
+ *                   at byte e*N*K/2.
+ *   iscale          E x (K/128) x N elements of `width` bytes (1, 2, 4), all
+ *                   made with the one amplifier alpha; values in [0, 2^23).
+ *   y               R x N of element type y_type, row r = slot r.
+ *   acc_out         optional R x N int32 (the integer accumulators).
+ * Routing outside these rules cannot make the kernels read or write outside
+ * the buffers (offsets are clamped to [0, R], tokens to [0, T), at most 64
+ * rows per expert are computed on the T <= 64 path), but gives unspecified
+ * rows of y. Requirements: 1 <= T <= 65536, N and K as bgt_w4a8_gemm_is,
+ * 1 <= E <= 256, 1 <= R <= min(T*E, 2^24); qx, packed, iscale, y, acc_out
+ * 16-byte aligned. Experts without slots read no weights on the T <= 64 path.
+ */
+int bgt_w4a8_moe_gemm_is(const int8_t* qx, const float* sx, int64_t T,
+                         const int32_t* expert_offsets, const int32_t* slot_token, int64_t E,
+                         int64_t R, const uint8_t* packed, const void* iscale, int width,
+                         int alpha, int64_t N, int64_t K, void* y, int y_type, int32_t* acc_out,
+                         void* stream);
+
+/* Diagnostics: name of the kernel bgt_w4a8_moe_gemm_is launches for T tokens. */
+const char* bgt_w4a8_moe_kernel_name(int64_t T, int64_t K);
+
+/*
  * bgt_pack_weights_int8 -- offline group-wise int8 weight quantization for the
  * fine-grained W8A8 layer of the [IS] page's LLaMA-3 scheme (5.4: 8-bit
  * weights for the down projection, groups of 128), with integer scales.
@@ -312,7 +348,8 @@ const char* bgt_status_string(int status);
 
 /* ABI version of this header (major*100 + minor): 101 adds the narrow
  * integer-scale entry points, 102 the fused linear layer, 103 fp16 / bf16
- * activation and output types, 104 the fine-grained W8A8 integer-scale GEMM. */
+ * activation and output types, 104 the fine-grained W8A8 integer-scale GEMM,
+ * 105 the grouped (mixture-of-experts) W4A8 integer-scale GEMM. */
 int bgt_abi_version(void);
 
 /* Diagnostics: name of the GEMM kernel that bgt_w4a8_gemm_is (float_scale = 0)

@@ -37,7 +37,7 @@ def test_status_strings(L):
     assert bgt.status_string(0) == "ok"
     for st in (-1, -2, -3, -4, -5, -6, -7, 1):
         assert "error" in bgt.status_string(st) or "warning" in bgt.status_string(st)
-    assert L.bgt_abi_version() == 104
+    assert L.bgt_abi_version() == 105
 
 
 def test_quantize_act_validation(L):
@@ -232,4 +232,35 @@ def test_w8a8_is_validation(L):
     assert bgt.w8a8_is_kernel_name(4, 4096, 14336) == "k_w8is_split"
     assert bgt.w8a8_is_kernel_name(65, 4096, 14336) == "k_w8is_tiled"
     assert bgt.w8a8_is_kernel_name(0, 4096, 14336) == "invalid shape"
+
+
+def test_moe_validation(L):
+    g = L.bgt_w4a8_moe_gemm_is
+
+    def call(qx=FAKE, sx=FAKE, T=16, offs=FAKE, tok=FAKE, E=8, R=32, pk=FAKE, isc=FAKE, width=4,
+             alpha=1024, N=64, K=256, y=FAKE, yt=0, acc=None):
+        return g(qx, sx, T, offs, tok, E, R, pk, isc, width, alpha, N, K, y, yt, acc, None)
+
+    assert call(qx=None) == bgt.BGT_ERR_NULL
+    assert call(offs=None) == bgt.BGT_ERR_NULL
+    assert call(tok=None) == bgt.BGT_ERR_NULL
+    assert call(pk=None) == bgt.BGT_ERR_NULL
+    assert call(width=8) == bgt.BGT_ERR_MODE
+    assert call(yt=3) == bgt.BGT_ERR_MODE
+    assert call(T=0) == bgt.BGT_ERR_SHAPE
+    assert call(E=0) == bgt.BGT_ERR_SHAPE
+    assert call(E=257) == bgt.BGT_ERR_SHAPE
+    assert call(R=0) == bgt.BGT_ERR_SHAPE
+    assert call(R=16 * 8 + 1) == bgt.BGT_ERR_SHAPE
+    assert call(N=24) == bgt.BGT_ERR_SHAPE
+    assert call(K=192) == bgt.BGT_ERR_SHAPE
+    assert call(alpha=12) == bgt.BGT_ERR_ALPHA
+    assert call(qx=MIS) == bgt.BGT_ERR_ALIGN
+    assert call(pk=MIS) == bgt.BGT_ERR_ALIGN
+    assert call(isc=MIS) == bgt.BGT_ERR_ALIGN
+    assert call(y=MIS) == bgt.BGT_ERR_ALIGN
+    assert call(acc=MIS) == bgt.BGT_ERR_ALIGN
+    assert bgt.w4a8_moe_kernel_name(16, 4096) == "k_w4a8_decode<IS,grouped>"
+    assert bgt.w4a8_moe_kernel_name(16, 14336) == "k_w4a8_prefill<4,2,2,2,IS,grouped>"
+    assert bgt.w4a8_moe_kernel_name(65, 4096) == "k_w4a8_prefill<4,2,2,2,IS,grouped>"
 

@@ -1,0 +1,142 @@
+"""GPU parity of the grouped (mixture-of-experts) W4A8 integer-scale GEMM.
+
+bgt_w4a8_moe_gemm_is must give, for every routed slot, the oracle's int32
+accumulators and outputs bit-exactly: on the decode path (T <= 64 tokens,
+K/128 in {16, 32}: one workgroup row per expert, experts without tokens
+skipped) and on the tiled path (the experts' row tiles in one launch), with
+skewed and degenerate routings, narrow scales, fp16 / bf16 outputs, and the
+Mixtral-8x7B expert shapes (w1/w3: 4096 -> 14336, w2: 14336 -> 4096) on
+sampled columns.
+"""
+import numpy as np
+import pytest
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+ALPHA = 1024
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def bgt():
+    import bit_gemm_token_amd
+    bit_gemm_token_amd.lib()
+    return bit_gemm_token_amd
+
+
+@pytest.fixture(scope="module")
+def orc():
+    import oracle
+    oracle.build()
+    return oracle
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def to_dev(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def _experts(orc, seed, E, K, N):
+    w = synth.expert_weights(seed, E, K, N)
+    pws = [orc.pack_weights(w[e], 128, ALPHA) for e in range(E)]
+    codes = np.stack([p["codes"] for p in pws])
+    packed = np.stack([p["packed"] for p in pws])
+    isc = np.stack([p["iscale"] for p in pws])
+    return codes, packed, isc
+
+
+def _run(bgt, orc, dev, T, E, K, N, seed, routing=None, width=4, out_dtype=None, cols=None):
+    x = synth.activations(seed, T, K)
+    oq, os_ = orc.quant_sym_i8(x)
+    if routing is None:
+        routing = synth.moe_routing(seed, T, E, min(2, E))
+    offs, tok = synth.route_by_expert(routing, E)
+    codes, packed, isc = _experts(orc, seed + 7, E, K, N)
+    R = len(tok)
+    isc_d = to_dev(isc, dev)
+    if width != 4:
+        isc_d = bgt.narrow_iscale(isc_d, width)
+    acc = torch.full((R, N), -1, dtype=torch.int32, device=dev)
+    y = bgt.w4a8_moe_gemm_is(to_dev(oq, dev), to_dev(os_, dev), to_dev(offs, dev), to_dev(tok, dev),
+                             to_dev(packed, dev), isc_d, ALPHA, N, acc_out=acc, out_dtype=out_dtype)
+    oA, oy, ov = orc.moe_w4a8_gemm_is(oq, os_, codes, isc, ALPHA, offs, tok, cols=cols)
+    assert ov == 0
+    got_a = acc.cpu().numpy().astype(np.int64)
+    if cols is not None:
+        got_a = got_a[:, cols]
+    np.testing.assert_array_equal(got_a, oA)
+    oy = oy.astype(np.float32)
+    if out_dtype is None:
+        got = y.cpu().numpy()
+        if cols is not None:
+            got = got[:, cols]
+        assert not np.isnan(got).any()
+        np.testing.assert_array_equal(got.view(np.int32), oy.view(np.int32))
+    else:
+        bits = y.view(torch.int16).cpu().numpy().view(np.uint16)
+        want = oy.astype(np.float16).view(np.uint16) if out_dtype == torch.float16 \
+            else orc.f32_to_bf16_bits(oy)
+        np.testing.assert_array_equal(bits, want)
+    return offs
+
+
+@pytest.mark.parametrize("T,E,K,N", [(1, 8, 4096, 64), (5, 8, 4096, 208), (16, 8, 2048, 96),
+                                     (33, 8, 4096, 48), (64, 8, 2048, 16), (20, 3, 4096, 80)])
+def test_moe_decode_path(bgt, orc, dev, T, E, K, N):
+    say(f"moe {bgt.w4a8_moe_kernel_name(T, K)} T={T} E={E} K={K} N={N}")
+    offs = _run(bgt, orc, dev, T, E, K, N, seed=T * 31 + K + N)
+    if T == 1:
+        assert (np.diff(offs) > 0).sum() == 2             # six experts read nothing
+
+
+@pytest.mark.parametrize("T,E,K,N", [(65, 8, 512, 144), (300, 8, 256, 48), (20, 8, 1152, 64),
+                                     (130, 4, 640, 400), (257, 8, 128, 16)])
+def test_moe_tiled_path(bgt, orc, dev, T, E, K, N):
+    say(f"moe {bgt.w4a8_moe_kernel_name(T, K)} T={T} E={E} K={K} N={N}")
+    _run(bgt, orc, dev, T, E, K, N, seed=T * 37 + K + N)
+
+
+@pytest.mark.parametrize("T,K", [(64, 4096), (200, 512)])
+def test_moe_all_tokens_one_expert(bgt, orc, dev, T, K):
+    # maximal imbalance: expert 5 takes every token, expert 2 one, the rest none
+    say(f"moe skewed T={T} K={K}")
+    routing = np.full((T, 1), 5, np.int32)
+    routing[0, 0] = 2
+    _run(bgt, orc, dev, T, 8, K, 64, seed=T + 3, routing=routing)
+
+
+@pytest.mark.parametrize("T,K", [(12, 4096), (150, 384)])
+@pytest.mark.parametrize("width", [1, 2])
+def test_moe_narrow_scales(bgt, orc, dev, width, T, K):
+    say(f"moe width={width} T={T} K={K}")
+    _run(bgt, orc, dev, T, 8, K, 96, seed=T + K + width, width=width)
+
+
+@pytest.mark.parametrize("T,K", [(8, 2048), (100, 256)])
+def test_moe_half_outputs(bgt, orc, dev, T, K):
+    for dt in (torch.float16, torch.bfloat16):
+        say(f"moe y={dt} T={T} K={K}")
+        _run(bgt, orc, dev, T, 8, K, 48, seed=T + 11, out_dtype=dt)
+
+
+@pytest.mark.parametrize("T,K,N", [(16, 4096, 14336), (512, 4096, 14336), (16, 14336, 4096)])
+def test_moe_mixtral_shapes_sampled(bgt, orc, dev, T, K, N):
+    """Mixtral-8x7B experts (8, top-2) at the w1/w3 and w2 shapes, in the
+    launches the bench times; sampled output columns against the oracle."""
+    say(f"moe mixtral {bgt.w4a8_moe_kernel_name(T, K)} T={T} K={K} N={N} (sampled)")
+    cols = np.unique(np.concatenate([np.arange(0, 32), np.arange(N - 32, N),
+                                     np.random.default_rng(T).choice(N, 160, replace=False)]))
+    _run(bgt, orc, dev, T, 8, K, N, seed=T + 21, cols=cols)
