@@ -189,4 +189,21 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // suffices, with no fence that would also drain the loads still in flight.
 __device__ __forceinline__ void lds_barrier() { __builtin_amdgcn_s_barrier(); }
 
+// Tile order of the tiled GEMMs: workgroup ids are dealt round-robin to the 8
+// XCDs, so consecutive ids of one XCD are remapped to consecutive tiles (when
+// the tile count is a multiple of 8), and tiles go in groups of 4 row tiles
+// per column tile, so the tiles resident on one XCD share activation rows and
+// weight columns in its L2.
+__device__ __forceinline__ void tile_of(int pid, int ntm, int ntn, int& tm, int& tn) {
+  const int total = ntm * ntn;
+  if ((total & 7) == 0) pid = (pid & 7) * (total >> 3) + (pid >> 3);   // XCD-contiguous
+  constexpr int GM = 4;                                               // grouped order
+  const int group = pid / (GM * ntn);
+  const int first = group * GM;
+  const int gsz = ntm - first < GM ? ntm - first : GM;
+  const int in = pid - group * GM * ntn;
+  tm = first + in % gsz;
+  tn = in / gsz;
+}
+
 }  // namespace bgt

@@ -342,17 +342,6 @@ __global__ __launch_bounds__(MAXT) __attribute__((amdgpu_waves_per_eu(WPE))) voi
 // =====================================================================
 constexpr int kBRow = 144;   // LDS bytes per unpacked B column: 128 + 16 pad
 
-__device__ __forceinline__ void tile_of(int pid, int ntm, int ntn, int& tm, int& tn) {
-  const int total = ntm * ntn;
-  if ((total & 7) == 0) pid = (pid & 7) * (total >> 3) + (pid >> 3);   // XCD-contiguous
-  constexpr int GM = 4;                                               // grouped order
-  const int group = pid / (GM * ntn);
-  const int first = group * GM;
-  const int gsz = ntm - first < GM ? ntm - first : GM;
-  const int in = pid - group * GM * ntn;
-  tm = first + in % gsz;
-  tn = in / gsz;
-}
 
 // 16-byte LDS read of data that this lane's own LDS copy wrote, after the
 // caller's s_waitcnt on vmcnt. Written as one asm block that waits for its

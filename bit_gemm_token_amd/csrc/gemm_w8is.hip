@@ -332,6 +332,194 @@ __global__ __launch_bounds__(kW8isWaves * 64) void k_w8is_tiled(
   }
 }
 
+// =====================================================================
+// Wide tiled kernel (large M): 256 x 128 output tiles, 8 waves of 64 x 64
+// (2 x 2 blocks of 32 x 32, v_mfma_i32_32x32x32_i8 over the whole group).
+// Three LDS-copy stages of one group, two in flight: 256 activation rows
+// (XOR-swizzled 16-byte chunks), the 8 weight tiles' 2 KiB fragment blocks as
+// stored, and the group's 128 scales: seven copies per wave per stage. Per
+// group each wave runs its four blocks in turn (four MFMAs each, into a fresh
+// accumulator) and scales block k-1's partial with its column's integer
+// scale under block k's MFMAs.
+// =====================================================================
+template <int GC, typename ST>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k_w8is_wide(
+    const int8_t* __restrict__ qx, const float* __restrict__ sx, const int8_t* __restrict__ qw,
+    const ST* __restrict__ iscale, float inv_alpha, int M, int N, int K, OutY y,
+    int32_t* __restrict__ acc_out) {
+  constexpr int NW = 8, WN = 2, BM = 256, BN = 128;
+  constexpr int SB = sizeof(ST);
+  constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
+  constexpr int AB = A_BYTES + B_BYTES, STG = AB + 512;
+  constexpr int A_CP = BM / 8 / NW;                   // 1 KiB activation copies per wave (4)
+  constexpr int B_CP = B_BYTES / 1024 / NW;           // 1 KiB weight copies per wave (2)
+  constexpr int LOADS = A_CP + B_CP + 1;              // + the scale copy
+  __shared__ __align__(16) int8_t S0[STG];
+  __shared__ __align__(16) int8_t S1[STG];
+  __shared__ __align__(16) int8_t S2[STG];
+  auto stage = [&](auto ic) -> int8_t* {
+    constexpr int i = decltype(ic)::value;
+    if constexpr (i == 0) return S0;
+    else if constexpr (i == 1) return S1;
+    else return S2;
+  };
+  const int G = GC > 0 ? GC : K / kGroup;
+  const int T = N / 16;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid % kWave;
+  const int wm = wave / WN, wn = wave % WN;
+  const int lr = lane % 32, hf = lane / 32;
+  int tm, tn;
+  tile_of(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  // activation copy i of this wave: block b = NW*i + wave (rows 8b .. 8b+7),
+  // lane L fills row 8b + L/8, slot L%8 with chunk (L%8) ^ ((row/2) % 8)
+  // (32-bit offsets from the tile's first row)
+  const int8_t* abase = qx + (int64_t)m0 * K;
+  int aoff[A_CP];
+#pragma unroll
+  for (int i = 0; i < A_CP; ++i) {
+    const int r = 8 * (NW * i + wave) + lane / 8;
+    const int rr = m0 + r < M ? r : M - 1 - m0;
+    aoff[i] = rr * K + 16 * ((lane % 8) ^ ((r >> 1) & 7));
+  }
+  // weight copy u: half-block q = 2*wave + u = (tile q/2 of the 8, half q%2)
+  const int8_t* bsrc[B_CP];
+#pragma unroll
+  for (int u = 0; u < B_CP; ++u) {
+    const int q = B_CP * wave + u;
+    const int tl = n0 / 16 + q / 2 < T ? n0 / 16 + q / 2 : T - 1;
+    bsrc[u] = qw + ((int64_t)tl * G * 2 + q % 2) * 1024 + lane * 16;
+  }
+  // scale copy: dword d = 4*SB*wave + lane (lane < 4*SB) of the group's 128*SB
+  // bytes; dwords past N re-read the row's last dword
+  const bool scopy = lane < 4 * SB;
+  const int sd = 4 * SB * wave + lane;
+  const int scol = n0 + sd * (4 / SB) < N ? n0 + sd * (4 / SB) : N - 4 / SB;
+  const int8_t* ssrc = reinterpret_cast<const int8_t*>(iscale) + (int64_t)scol * SB;
+  auto issue = [&](int g, int8_t* S) {
+    const int gc = g < G ? g : G - 1;                 // past the end: surplus copies, never read
+#pragma unroll
+    for (int i = 0; i < A_CP; ++i)
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(abase + aoff[i] + (int64_t)gc * kGroup),
+          (__attribute__((address_space(3))) void*)(S + (NW * i + wave) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int u = 0; u < B_CP; ++u)
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(bsrc[u] + (int64_t)gc * 2048),
+          (__attribute__((address_space(3))) void*)(S + A_BYTES + (B_CP * wave + u) * 1024), 16, 0, 0);
+    if (scopy)
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(ssrc + (int64_t)gc * N * SB),
+          (__attribute__((address_space(3))) void*)(S + AB + 16 * SB * wave), 4, 0, 0);
+  };
+
+  // fragments of block (a, b): A row wm*64 + 32a + lr, B column wn*64 + 32b + lr
+  // (tile col/16, lane slot 16m + col%16 of half hf); MFMA m takes k chunk 4hf + m
+  v4i av[2][4], bv[2][4];
+  int32_t sc[2];
+  auto read_frags = [&](const int8_t* S) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const int ra = wm * 64 + 32 * a + lr;
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        av[a][m] = *reinterpret_cast<const v4i*>(S + ra * 128 + 16 * ((4 * hf + m) ^ ((ra >> 1) & 7)));
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int cl = wn * 64 + 32 * b + lr;
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        bv[b][m] = *reinterpret_cast<const v4i*>(S + A_BYTES + ((cl / 16 * 2 + hf) * 64 + 16 * m + cl % 16) * 16);
+      sc[b] = (int32_t)*reinterpret_cast<const ST*>(S + AB + cl * SB);
+    }
+  };
+
+  v16i acc[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) acc[k] = v16i{0};
+  v16i pp = v16i{0};
+  int32_t spp = 0;
+  // block k of the group: its MFMA chain, then the previous block's partial
+  // times its scale (block 3 of the previous group for k = 0)
+  auto block = [&](auto kk, bool apply) {
+    constexpr int k = decltype(kk)::value, kp = (k + 3) % 4;
+    v16i p = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[k / 2][0], bv[k % 2][0], v16i{0}, 0, 0, 0);
+#pragma unroll
+    for (int m = 1; m < 4; ++m)
+      p = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[k / 2][m], bv[k % 2][m], p, 0, 0, 0);
+    if (apply) {
+      opaque_reg(spp);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[kp][r] = mad24(pp[r], spp, acc[kp][r]);
+      opaque_reg(acc[kp]);
+    }
+    pp = p;
+    spp = sc[k % 2];
+  };
+  auto step = [&](int l, auto j) {
+    constexpr int J = decltype(j)::value;
+    wait_vm_lds0<LOADS>();                            // group l landed (l+1 may be in flight)
+    lds_barrier();                                    // ... in every wave; stage of l-1 free
+    issue(l + 2, stage(IC<(J + 2) % 3>{}));
+    read_frags(stage(IC<J>{}));
+    block(IC<0>{}, l > 0);
+    block(IC<1>{}, true);
+    block(IC<2>{}, true);
+    block(IC<3>{}, true);
+  };
+  issue(0, S0);
+  issue(1, S1);
+  auto steps = [&](int l) {
+    step(l + 0, IC<0>{});
+    if (l + 1 >= G) return false;
+    step(l + 1, IC<1>{});
+    if (l + 2 >= G) return false;
+    step(l + 2, IC<2>{});
+    return true;
+  };
+  if constexpr (GC > 0) {
+#pragma unroll
+    for (int l = 0; l < G; l += 3) if (!steps(l)) break;
+  } else {
+#pragma unroll 1
+    for (int l = 0; l < G; l += 3) if (!steps(l)) break;
+  }
+  opaque_reg(spp);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[3][r] = mad24(pp[r], spp, acc[3][r]);
+  wait_vm_lds0<0>();                                  // surplus copies of the last steps
+
+  // one conversion per output; the lane's 32 token scales first
+  float srow[2][16];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = m0 + wm * 64 + 32 * a + 8 * (r / 4) + 4 * hf + (r % 4);
+      srow[a][r] = sx[i < M ? i : M - 1];
+    }
+  const bool full = m0 + BM <= M && n0 + BN <= N;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int a = k / 2, b = k % 2;
+    const int j = n0 + wn * 64 + 32 * b + lr;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = m0 + wm * 64 + 32 * a + 8 * (r / 4) + 4 * hf + (r % 4);
+      if (!full && (i >= M || j >= N)) continue;
+      const int64_t o = (int64_t)i * N + j;
+      const float t0 = (float)acc[k][r] * srow[a][r];
+      y.put(o, t0 * inv_alpha);
+      if (acc_out) acc_out[o] = acc[k][r];
+    }
+  }
+}
+
 // ------------------------------------------------------------------ launchers
 // waves per split workgroup: about 4096 waves over the chip (16 per CU), at
 // least two groups per wave, at most 16 (8 for four row blocks: LDS)
@@ -341,6 +529,15 @@ static int split_waves(int64_t N, int64_t K, int mr) {
   const int cap = split_max_waves(mr);
   while (ks < cap && T * ks < 4096 && 2 * (2 * ks) <= G) ks *= 2;
   return ks;
+}
+
+// M > 64: the 256 x 128 tile copies 3x the bytes of a 64 x 64 tile per group
+// for 8x the work; with one workgroup per CU (LDS), pick the tile whose rounds
+// of 256 workgroups move fewer bytes in total
+static bool w8is_use_wide(int M, int N) {
+  const int64_t small = ((M + 63) / 64) * (int64_t)((N + 63) / 64);
+  const int64_t wide = ((M + 255) / 256) * (int64_t)((N + 127) / 128);
+  return ((wide + 255) / 256) * 97 < ((small + 255) / 256) * 32;
 }
 
 template <typename ST>
@@ -363,8 +560,22 @@ static void launch_w8is_t(const int8_t* qx, const float* sx, const int8_t* qw, c
                          inv_alpha, M, N, K, y, acc_out);
     return;
   }
-  const int tiles = ((M + 63) / 64) * ((N + 63) / 64);
   const int G = K / kGroup;
+  if (w8is_use_wide(M, N)) {
+    const int tiles = ((M + 255) / 256) * ((N + 127) / 128);
+    dim3 grid((unsigned)tiles), block(512);
+    if (G == 112)
+      hipLaunchKernelGGL((k_w8is_wide<112, ST>), grid, block, 0, stream, qx, sx, qw, iscale,
+                         inv_alpha, M, N, K, y, acc_out);
+    else if (G == 32)
+      hipLaunchKernelGGL((k_w8is_wide<32, ST>), grid, block, 0, stream, qx, sx, qw, iscale,
+                         inv_alpha, M, N, K, y, acc_out);
+    else
+      hipLaunchKernelGGL((k_w8is_wide<0, ST>), grid, block, 0, stream, qx, sx, qw, iscale,
+                         inv_alpha, M, N, K, y, acc_out);
+    return;
+  }
+  const int tiles = ((M + 63) / 64) * ((N + 63) / 64);
   dim3 grid((unsigned)tiles), block(kW8isWaves * 64);
   if (G == 112)
     hipLaunchKernelGGL((k_w8is_tiled<112, ST>), grid, block, 0, stream, qx, sx, qw, iscale,
@@ -395,9 +606,9 @@ hipError_t launch_w8a8_is(const int8_t* qx, const float* sx, const int8_t* qw, c
 }
 
 const char* w8a8_is_kernel_name(int64_t M, int64_t N, int64_t K) {
-  (void)N;
   (void)K;
-  return M <= 64 ? "k_w8is_split" : "k_w8is_tiled";
+  if (M <= 64) return "k_w8is_split";
+  return w8is_use_wide((int)M, (int)N) ? "k_w8is_wide" : "k_w8is_tiled";
 }
 
 }  // namespace bgt

@@ -126,3 +126,91 @@ def test_graph_replays_match_eager_w8a8(dev, bgt):
         assert not np.isnan(got).any(), f"replay {rep}: unwritten outputs"
         assert np.array_equal(got.view(np.int32), r.view(np.int32)), f"replay {rep}: graph differs from eager"
         print(f"  replay {rep}: equal to eager", flush=True)
+
+
+def _replay_check(dev, run, outs, refill, reps=4):
+    """Capture run() once, then for each replay refill the inputs, replay, and
+    compare every output with an eager run on the same inputs."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run(outs)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(outs)
+    for rep in range(reps):
+        refill(rep)
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [o.cpu().numpy().copy() for o in outs]
+        refs = [torch.full_like(o, float("nan")) for o in outs]
+        run(refs)
+        torch.cuda.synchronize()
+        for a, r in zip(got, refs):
+            r = r.cpu().numpy()
+            assert not np.isnan(a).any(), f"replay {rep}: unwritten outputs"
+            assert np.array_equal(a.view(np.int32), r.view(np.int32)), f"replay {rep}: differs from eager"
+        print(f"  replay {rep}: equal to eager", flush=True)
+
+
+def test_graph_replays_match_eager_w8a8_is(dev, bgt):
+    K, N = 1024, 512
+    Ms = (3, 40, 130)
+    print(f"graph replay w8a8_is: K={K} N={N} M={Ms}", flush=True)
+    w = synth.weights(12, K, N, std=0.02, outlier_prob=0.001)
+    pw = bgt.pack_weights_int8(torch.from_numpy(w).to(dev), alpha=1 << 16)
+    xs = {M: torch.zeros((M, K), dtype=torch.float32, device=dev) for M in Ms}
+    qs = {M: (torch.empty((M, K), dtype=torch.int8, device=dev),
+              torch.empty(M, dtype=torch.float32, device=dev)) for M in Ms}
+    outs = [torch.empty((M, N), dtype=torch.float32, device=dev) for M in Ms]
+
+    def run(ys):
+        for M, y in zip(Ms, ys):
+            q, s = qs[M]
+            bgt.quantize_act(xs[M], q=q, scale=s)
+            bgt.w8a8_gemm_is(q, s, pw["qw"], pw["iscale"], pw["alpha"], N, y=y)
+
+    def refill(rep):
+        for M in Ms:
+            xs[M].copy_(torch.from_numpy(synth.activations(300 + rep, M, K)))
+
+    _replay_check(dev, run, outs, refill)
+
+
+def test_graph_replays_match_eager_moe(dev, bgt):
+    E, K, N = 8, 2048, 256
+    Ts = (16, 100)
+    print(f"graph replay moe: E={E} K={K} N={N} T={Ts}", flush=True)
+    w = synth.expert_weights(13, E, K, N)
+    packed = torch.empty((E, N * K // 2), dtype=torch.uint8, device=dev)
+    isc = torch.empty((E, K // 128, N), dtype=torch.int32, device=dev)
+    fsc = torch.empty((E, K // 128, N), dtype=torch.float32, device=dev)
+    for e in range(E):
+        bgt.pack_weights_int4(torch.from_numpy(w[e]).to(dev), alpha=1024, packed=packed[e],
+                              fscale=fsc[e], iscale=isc[e])
+    routes = {}
+    for T in Ts:
+        offs, tok = synth.route_by_expert(synth.moe_routing(T, T, E, 2), E)
+        routes[T] = (torch.from_numpy(offs).to(dev), torch.from_numpy(tok).to(dev), len(tok))
+    xs = {T: torch.zeros((T, K), dtype=torch.float32, device=dev) for T in Ts}
+    qs = {T: (torch.empty((T, K), dtype=torch.int8, device=dev),
+              torch.empty(T, dtype=torch.float32, device=dev)) for T in Ts}
+    outs = [torch.empty((routes[T][2], N), dtype=torch.float32, device=dev) for T in Ts]
+
+    def run(ys):
+        for T, y in zip(Ts, ys):
+            q, s = qs[T]
+            offs, tok, _ = routes[T]
+            bgt.quantize_act(xs[T], q=q, scale=s)
+            bgt.w4a8_moe_gemm_is(q, s, offs, tok, packed, isc, 1024, N, y=y)
+
+    def refill(rep):
+        for T in Ts:
+            xs[T].copy_(torch.from_numpy(synth.activations(400 + rep, T, K)))
+
+    _replay_check(dev, run, outs, refill)

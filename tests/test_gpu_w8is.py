@@ -80,7 +80,8 @@ def _case(orc, seed, M, K, N, alpha=ALPHA):
 SHAPES = [(1, 128, 16), (1, 4096, 64), (3, 384, 48), (16, 1152, 96), (5, 14336, 32),   # split
           (17, 2048, 80), (33, 512, 144), (64, 4096, 16), (40, 256, 208),
           (65, 512, 144), (128, 4096, 64), (200, 640, 400), (257, 256, 16),          # tiled
-          (96, 14336, 48), (130, 1280, 80)]
+          (96, 14336, 48), (130, 1280, 80),
+          (1024, 512, 4096), (1000, 384, 4000), (1100, 4096, 2048)]               # wide
 
 
 @pytest.mark.parametrize("M,K,N", SHAPES)
@@ -120,6 +121,22 @@ def test_w8is_narrow_scales(bgt, orc, dev, width, M, K, N):
     np.testing.assert_array_equal(y.cpu().numpy().view(np.int32), oy.astype(np.float32).view(np.int32))
 
 
+@pytest.mark.parametrize("width", [1, 2])
+def test_w8is_wide_narrow_scales(bgt, orc, dev, width):
+    M, K, N = 1000, 256, 4000
+    alpha = 1 << 14 if width == 1 else 1 << 18
+    assert bgt.w8a8_is_kernel_name(M, N, K) == "k_w8is_wide"
+    say(f"w8a8_gemm_is wide width={width} M={M} K={K} N={N}")
+    oq, os_, ow = _case(orc, 23 + width, M, K, N, alpha)
+    isc = bgt.narrow_iscale(to_dev(ow["iscale"], dev), width)
+    acc = torch.full((M, N), -1, dtype=torch.int32, device=dev)
+    y = bgt.w8a8_gemm_is(to_dev(oq, dev), to_dev(os_, dev), to_dev(ow["qw"], dev), isc, alpha, N,
+                         acc_out=acc, out_dtype=torch.bfloat16)
+    oA, oy, _ = orc.w8a8_gemm_is(oq, os_, ow["codes"], ow["iscale"], alpha)
+    np.testing.assert_array_equal(acc.cpu().numpy().astype(np.int64), oA)
+    np.testing.assert_array_equal(dev_bits16(y), orc.f32_to_bf16_bits(oy.astype(np.float32)))
+
+
 @pytest.mark.parametrize("kind", ["f16", "bf16"])
 @pytest.mark.parametrize("M,K,N", [(4, 2048, 48), (100, 512, 80)])
 def test_w8is_half_outputs(bgt, orc, dev, kind, M, K, N):
@@ -134,27 +151,24 @@ def test_w8is_half_outputs(bgt, orc, dev, kind, M, K, N):
     np.testing.assert_array_equal(dev_bits16(y), want)
 
 
-def test_w8is_wraps_like_the_oracle(bgt, orc, dev):
+@pytest.mark.parametrize("m,N", [(3, 32), (70, 32), (1100, 4000)])
+def test_w8is_wraps_like_the_oracle(bgt, orc, dev, m, N):
     # extreme codes and scales: A leaves int32; device and oracle agree mod 2^32
-    M, K, N = 3, 1024, 32
-    qx = np.full((M, K), 127, np.int8)
-    qx[1] = -127
+    K = 1024
+    qx = np.full((m, K), 127, np.int8)
+    qx[1::3] = -127
     codes = np.full((K, N), 127, np.int8)
     isc = np.full((K // 128, N), 3000, np.int32)
-    sx = np.ones(M, np.float32)
+    sx = np.ones(m, np.float32)
+    say(f"w8a8_gemm_is wrap-around {bgt.w8a8_is_kernel_name(m, N, K)} M={m} N={N}")
     oA, oy, ov = orc.w8a8_gemm_is(qx, sx, codes, isc, 1)
-    assert ov == M * N
-    for m, label in ((M, "split"), (70, "tiled")):
-        qxm = np.resize(qx, (m, K))
-        sxm = np.ones(m, np.float32)
-        say(f"w8a8_gemm_is wrap-around {label} M={m}")
-        acc = torch.zeros((m, N), dtype=torch.int32, device=dev)
-        y = bgt.w8a8_gemm_is(to_dev(qxm, dev), to_dev(sxm, dev), to_dev(orc.layout_int8(codes), dev),
-                             to_dev(isc, dev), 1, N, acc_out=acc)
-        oAm, oym, _ = orc.w8a8_gemm_is(qxm, sxm, codes, isc, 1)
-        wrapped = ((oAm + 2 ** 31) % 2 ** 32) - 2 ** 31
-        np.testing.assert_array_equal(acc.cpu().numpy().astype(np.int64), wrapped)
-        np.testing.assert_array_equal(y.cpu().numpy().view(np.int32), oym.astype(np.float32).view(np.int32))
+    assert ov == m * N
+    acc = torch.zeros((m, N), dtype=torch.int32, device=dev)
+    y = bgt.w8a8_gemm_is(to_dev(qx, dev), to_dev(sx, dev), to_dev(orc.layout_int8(codes), dev),
+                         to_dev(isc, dev), 1, N, acc_out=acc)
+    wrapped = ((oA + 2 ** 31) % 2 ** 32) - 2 ** 31
+    np.testing.assert_array_equal(acc.cpu().numpy().astype(np.int64), wrapped)
+    np.testing.assert_array_equal(y.cpu().numpy().view(np.int32), oy.astype(np.float32).view(np.int32))
 
 
 @pytest.mark.parametrize("M", [16, 4096])
