@@ -72,25 +72,40 @@ METRIC = "W4A8 integer-scale GEMM TOPS + HBM GB/s, K=4096 N=22016, M=1..4096"
 
 
 # HBM bytes per GEMM launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
-# (read counts x2.0, write counts x1.0, both from a plain copy of known size;
-# profiles/w4a8_gemm_kernels__M1_to_M4096__hbm_bytes.txt), keyed by
-# (kernel, M). They hold only for the kernel source they were taken on: when
-# gemm.hip differs from that source, traffic is reported as null.
-TRAFFIC_GEMM_SHA = "34a9ce114de72d48"
-TRAFFIC = {("k_w4a8_decode<IS>", 1): 48162780,
-           ("k_w4a8_decode<IS>", 4): 48530386,
-           ("k_w4a8_decode<IS>", 16): 49980330,
-           ("k_w4a8_decode<IS>", 64): 55824137,
-           ("k_w4a8_prefill<4,2,2,2,IS>", 256): 79137927,
-           ("k_w4a8_prefill<4,2,2,2,IS>", 4096): 922100563,
-           ("k_w8a8_zp<9,32>", 256): 29644447}
+# (each scaled by the factor a plain copy of known size gives;
+# profiles/*hbm_bytes.txt), keyed by (kernel, M). They hold only for the
+# kernel sources they were taken on: when a source file differs from the one
+# measured (sha256 prefix below), traffic is reported as null.
+TRAFFIC_SRC_SHA = {"gemm.hip": "45072830adedd0fe", "gemm_w8is.hip": "f46c53234f1e0e63"}
+TRAFFIC_SRC = {"k_w4a8_decode<IS>": "gemm.hip", "k_w4a8_prefill<4,2,2,2,IS>": "gemm.hip",
+               "k_w8a8_zp<9,32>": "gemm.hip", "k_w4a8_decode<IS,grouped>": "gemm.hip",
+               "k_w8is_split": "gemm_w8is.hip"}
+TRAFFIC = {
+    ("k_w4a8_decode<IS>", 1): 48157202,
+    ("k_w4a8_decode<IS>", 4): 48538204,
+    ("k_w4a8_decode<IS>", 16): 49988021,
+    ("k_w4a8_decode<IS>", 64): 55878032,
+    ("k_w4a8_prefill<4,2,2,2,IS>", 256): 79307531,
+    ("k_w4a8_prefill<4,2,2,2,IS>", 4096): 922280754,
+    ("k_w8a8_zp<9,32>", 256): 29681440,
+    ("k_w8is_split", 1): 62579916,
+    ("k_w8is_split", 4): 62972800,
+    ("k_w8is_split", 16): 64545442,
+    ("k_w8is_split", 64): 70844608,
+    ("k_w4a8_decode<IS,grouped>", 1): 62687393,
+    ("k_w4a8_decode<IS,grouped>", 4): 125518026,
+    ("k_w4a8_decode<IS,grouped>", 16): 189674295,
+    ("k_w4a8_decode<IS,grouped>", 64): 259254798,
+}
 
 
 def measured_traffic(kernel, Ms):
     import hashlib
-    src = os.path.join(ROOT, "bit_gemm_token_amd", "csrc", "gemm.hip")
-    with open(src, "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest()[:16] != TRAFFIC_GEMM_SHA:
+    name = TRAFFIC_SRC.get(kernel)
+    if name is None or TRAFFIC_SRC_SHA.get(name) is None:
+        return None
+    with open(os.path.join(ROOT, "bit_gemm_token_amd", "csrc", name), "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest()[:16] != TRAFFIC_SRC_SHA[name]:
             return None
     vals = [TRAFFIC.get((kernel, M)) for M in Ms]
     return None if any(v is None for v in vals) else int(np.mean(vals))
@@ -110,32 +125,41 @@ def gemm_ops(M, N, K):
 
 
 # --------------------------------------------------------------------- CPU side
-def cpu_baseline(x, w, M=16):
-    """Time the oracle (as it stands) on the M=16 case of the decode workload.
+def cpu_baseline(x, w, Ms=None, min_seconds=10.0, unit="GB/s"):
+    """Time the oracle (as it stands) on the decode step: per-token
+    quantization plus the integer-scale GEMM over all columns for every M of
+    the step, repeated until at least min_seconds of CPU work have run; in
+    GB/s of the step's algorithmic bytes, or TOPS of its GEMM ops.
 
-    Offline weight packing is excluded, as it is on the GPU side; the timed
-    part is per-token quantization plus the integer-scale GEMM over all
-    22016 columns.
+    Offline weight packing is excluded, as it is on the GPU side.
     """
     import oracle
     oracle.build()
+    Ms = list(synth.DECODE_M) if Ms is None else Ms
     K, N = x.shape[1], w.shape[1]
-    xs = np.ascontiguousarray(x[:M])
     pw = oracle.pack_weights(w, 128, 1024)
+    xs = {M: np.ascontiguousarray(x[:M]) for M in Ms}
+    step_bytes = sum(quant_bytes(M, K) + gemm_bytes(M, N, K) for M in Ms)
+    step_ops = sum(gemm_ops(M, N, K) for M in Ms)
+    steps = 0
     t0 = time.perf_counter()
-    q, s = oracle.quant_sym_i8(xs)
-    t1 = time.perf_counter()
-    oracle.w4a8_gemm_is(q, s, pw["codes"], pw["iscale"], pw["alpha"])
-    t2 = time.perf_counter()
-    byts = quant_bytes(M, K) + gemm_bytes(M, N, K)
+    while True:
+        for M in Ms:
+            q, s = oracle.quant_sym_i8(xs[M])
+            oracle.w4a8_gemm_is(q, s, pw["codes"], pw["iscale"], pw["alpha"])
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    value = steps * step_bytes / el / 1e9 if unit == "GB/s" else steps * step_ops / el / 1e12
     return {
-        "value": round(byts / (t2 - t0) / 1e9, 4),
-        "unit": "GB/s",
+        "value": round(value, 4),
+        "unit": unit,
         "cores": cores,
         "kind": "oracle",
-        "sample": f"quant_act + w4a8_gemm_is at M={M}, K={K}, N={N} (one of the five sweep points; "
-                  f"quant {t1 - t0:.3f} s, GEMM {t2 - t1:.2f} s; offline packing excluded)",
+        "sample": f"{steps} passes of quant_act + w4a8_gemm_is at M in {Ms}, K={K}, N={N} "
+                  f"in {el:.1f} s; offline packing excluded",
     }
 
 
@@ -542,7 +566,8 @@ def run_w8is(args, torch, bgt, dev):
         "eager": {"ms_per_step": round(eager_ms, 4),
                   "value": round(step_bytes / (eager_ms * 1e-3) / 1e9, 1)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(kern, Ms) if sb == 4 else None,
                      "kernel": kern, "launch_M": Ms, "avg_launch_us": round(avg_us, 3),
                      "bytes_per_launch": int(avg_bytes)},
         "sweep": sweep,
@@ -649,7 +674,8 @@ def run_moe(args, torch, bgt, dev):
         "eager": {"ms_per_step": round(eager_ms, 4),
                   "value": round(step_bytes / (eager_ms * 1e-3) / 1e9, 1)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(bgt.w4a8_moe_kernel_name(1, K), Ts),
                      "kernel": bgt.w4a8_moe_kernel_name(1, K), "launch_T": Ts,
                      "avg_launch_us": round(avg_us, 3), "bytes_per_launch": int(avg_bytes)},
         "sweep": sweep,
@@ -657,7 +683,50 @@ def run_moe(args, torch, bgt, dev):
 
 
 def run_profile_m(args, torch, bgt, dev, M):
-    """Quantizer + integer-scale GEMM at one M of the decode layer, nothing else."""
+    """Quantizer + integer-scale GEMM at one M of the workload's layer, nothing
+    else (decode: W4A8 K=4096 N=22016; w8is: W8A8 K=14336 N=4096; moe: the
+    grouped GEMM at M tokens, Mixtral w1 shape)."""
+    if args.workload == "w8is":
+        K, N = W8IS_K, W8IS_N
+        x = synth.activations(900, M, K)
+        w = synth.weights(901, K, N, std=0.02, outlier_prob=0.001)
+        pw = bgt.pack_weights_int8(torch.from_numpy(w).to(dev), alpha=W8IS_ALPHA)
+        xd = torch.from_numpy(x).to(dev)
+        q = torch.empty((M, K), dtype=torch.int8, device=dev)
+        s = torch.empty(M, dtype=torch.float32, device=dev)
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+        for _ in range(args.warmup + args.steps):
+            bgt.quantize_act(xd, q=q, scale=s)
+            bgt.w8a8_gemm_is(q, s, pw["qw"], pw["iscale"], W8IS_ALPHA, N, y=y)
+        torch.cuda.synchronize()
+        return {"profile_m": M, "launches": args.warmup + args.steps,
+                "kernel": bgt.w8a8_is_kernel_name(M, N, K), "gemm_bytes": w8is_bytes(M, N, K)}
+    if args.workload == "moe":
+        K, N, E = MOE_K, MOE_N, MOE_E
+        x = synth.activations(700, M, K)
+        w = synth.expert_weights(701, E, K, N)
+        packed = torch.empty((E, N * K // 2), dtype=torch.uint8, device=dev)
+        isc = torch.empty((E, K // 128, N), dtype=torch.int32, device=dev)
+        fsc = torch.empty((E, K // 128, N), dtype=torch.float32, device=dev)
+        for e in range(E):
+            bgt.pack_weights_int4(torch.from_numpy(w[e]).to(dev), alpha=synth.ALPHA,
+                                  packed=packed[e], fscale=fsc[e], iscale=isc[e])
+        offs, tok = synth.route_by_expert(synth.moe_routing(700 + M, M, E, MOE_TOPK), E)
+        od, td = torch.from_numpy(offs).to(dev), torch.from_numpy(tok).to(dev)
+        xd = torch.from_numpy(x).to(dev)
+        q = torch.empty((M, K), dtype=torch.int8, device=dev)
+        s = torch.empty(M, dtype=torch.float32, device=dev)
+        y = torch.empty((len(tok), N), dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+        for _ in range(args.warmup + args.steps):
+            bgt.quantize_act(xd, q=q, scale=s)
+            bgt.w4a8_moe_gemm_is(q, s, od, td, packed, isc, synth.ALPHA, N, y=y)
+        torch.cuda.synchronize()
+        na = int((np.diff(offs) > 0).sum())
+        return {"profile_m": M, "launches": args.warmup + args.steps,
+                "kernel": bgt.w4a8_moe_kernel_name(M, K),
+                "gemm_bytes": moe_bytes(M, len(tok), na, N, K, E)}
     K, N = synth.K_LAYER, synth.N_LAYER
     x, w = synth.layer_inputs(0, M=M, K=K, N=N)
     xd = torch.from_numpy(x).to(dev)
@@ -736,7 +805,8 @@ def main():
     else:
         out, (x, w) = run_w8a8(args, torch, bgt, dev)
     if not args.no_cpu_baseline and args.workload in ("decode", "prefill"):
-        out["cpu_baseline"] = cpu_baseline(x, w)
+        out["cpu_baseline"] = (cpu_baseline(x, w) if args.workload == "decode"
+                               else cpu_baseline(x, w, Ms=[256], unit="TOPS"))
     print(json.dumps(out), flush=True)
 
 
