@@ -1,7 +1,10 @@
 """Writes scale_table_synthetic.txt: the integer-scale analysis of the
 "Integer Scale" page's Fig. 4 (amplified-scale width, amplifier search per
 layer, weight MSE between integer and float scales under several amplifiers)
-on the synthetic layers. Calls only the CPU oracle and the seeded generators.
+on the synthetic layers; and scale_table_int8_synthetic.txt, the same for the
+fine-grained int8 weights of the page's LLaMA-3 scheme (5.4), with the relative
+error of the whole W8A8 path against X.W. Calls only the CPU oracle and the
+seeded generators.
 
     python tests/golden/make_scale_table.py
 """
@@ -56,6 +59,49 @@ def main():
         for name, cnt, smin, n, mx, wide, mses in rows:
             f.write(f"{name} | {cnt} | {smin:.6g} | {n} | {mx} | {wide} | "
                     + " ".join(f"{m:.4g}" for m in mses) + "\n")
+    print("wrote", out)
+    int8_table()
+
+
+LOG2_ALPHAS_8 = (10, 12, 14, 15, 16, 18)
+
+
+def int8_table():
+    """The int8-weight analogue on 512 columns of the synthetic LLaMA-3-8B down
+    projection (14336 x 4096, 0.1% of weights x10) with 16 tokens of the
+    synthetic activations: per amplifier, the largest integer scale, how many
+    exceed 8 bits, the weight MSE against float scales, and the relative
+    Frobenius error of the integer-scale W8A8 output against X.W (float
+    scales: the last column of the header line)."""
+    K, N, M = 14336, 512, 16
+    w = synth.weights(901, K, N, std=0.02, outlier_prob=0.001)
+    x = synth.activations(900, M, K)
+    codes, fs = oracle.group_quant_int8(w, synth.GROUP)
+    qx, sx = oracle.quant_sym_i8(x)
+    ref = x.astype(np.float64) @ w.astype(np.float64)
+    nref = np.linalg.norm(ref)
+    y_fs = oracle.w4a8_gemm_fs(qx, sx, codes, fs)
+    rel_fs = np.linalg.norm(y_fs - ref) / nref
+    n = oracle.amplifier_log2(fs)
+    smin = float(fs[fs > 0].min())
+    out = os.path.join(HERE, "scale_table_int8_synthetic.txt")
+    with open(out, "w") as f:
+        f.write("# Integer scales for fine-grained int8 weights (q_max 127), the W8A8 scheme of the\n"
+                "# \"Integer Scale\" page (5.4 LLaMA-3): written by tests/golden/make_scale_table.py from\n"
+                "# the CPU oracle; 512 columns of a synthetic 14336x4096 down projection, N(0, 0.02)\n"
+                "# with 0.1% of elements x10, group 128; 16 synthetic tokens.\n"
+                f"# scales {fs.size} | min float scale {smin:.6g} | searched log2(alpha) {n} | "
+                f"float-scale output error {rel_fs:.5f}\n"
+                "# columns: log2(alpha) | max integer scale | scales above 255 | "
+                "weight MSE (integer vs float scales) | output error vs X.W\n")
+        for la in LOG2_ALPHAS_8:
+            a = 1 << la
+            isc = oracle.integer_scales(fs, a)
+            mse, mx, wide = oracle.weight_mse_is_fs(codes, fs, isc, a)
+            _, y, ov = oracle.w8a8_gemm_is(qx, sx, codes, isc, a)
+            assert ov == 0
+            rel = np.linalg.norm(y - ref) / nref
+            f.write(f"{la} | {mx} | {wide} | {mse:.4g} | {rel:.5f}\n")
     print("wrote", out)
 
 

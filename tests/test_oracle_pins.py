@@ -350,6 +350,27 @@ def test_scale_table_fixture_relations():
         assert wide == 0 and mx <= 255
 
 
+def test_int8_scale_table_fixture_relations():
+    # the int8-weight table written from the oracle by tests/golden/make_scale_table.py:
+    # the searched amplifier rule holds, the largest integer scale doubles with alpha
+    # (round(2x) = 2 round(x) or differs by one), the weight MSE falls as alpha grows,
+    # and the output error falls towards the float-scale error
+    path = os.path.join(os.path.dirname(__file__), "golden", "scale_table_int8_synthetic.txt")
+    lines = open(path, encoding="utf-8").read().splitlines()
+    head = [ln for ln in lines if ln.startswith("# scales")][0]
+    fields = dict(f.strip().rsplit(" ", 1) for f in head[2:].split("|"))
+    smin, n = float(fields["min float scale"]), int(fields["searched log2(alpha)"])
+    err_fs = float(fields["float-scale output error"])
+    assert smin * 2.0 ** n >= 1.0 > smin * 2.0 ** (n - 1)
+    rows = [[float(v) for v in ln.split("|")] for ln in lines if ln.strip() and not ln.startswith("#")]
+    assert len(rows) == 6
+    for (la0, mx0, _, mse0, e0), (la1, mx1, _, mse1, e1) in zip(rows, rows[1:]):
+        assert abs(mx1 - mx0 * 2 ** (la1 - la0)) <= 2 ** (la1 - la0)
+        assert mse1 < mse0 and e1 <= e0
+    assert rows[-1][4] >= err_fs * 0.999 and rows[-1][4] < err_fs * 1.01
+    assert rows[0][4] > 5 * err_fs                # alpha = 2^10 is far too coarse for int8
+
+
 # ----------------------------------------------------- bf16 output rounding
 
 def test_bf16_ties_to_even_and_exact_values(orc):
