@@ -593,6 +593,8 @@ def run_moe(args, torch, bgt, dev):
     for each T in {1, 4, 16, 64} tokens (GB/s); per-launch rates also at
     T in {512, 4096} (TOPS)."""
     K, N, E, topk = MOE_K, MOE_N, MOE_E, MOE_TOPK
+    if args.moe_linear == "w2":
+        K, N = N, K
     Ts, Ps = list(MOE_DECODE_T), list(MOE_PREFILL_T)
     x = synth.activations(700, max(Ps), K)
     w = synth.expert_weights(701, E, K, N)
@@ -661,14 +663,16 @@ def run_moe(args, torch, bgt, dev):
     avg_bytes = float(np.mean([moe_bytes(T, route[T][3], route[T][2], N, K, E) for T in Ts]))
     achieved = avg_bytes / avg_us / 1e3
     return {
-        "metric": "grouped (MoE) W4A8 integer-scale GEMM HBM GB/s, Mixtral-8x7B w1 K=4096 N=14336 E=8 top-2",
+        "metric": f"grouped (MoE) W4A8 integer-scale GEMM HBM GB/s, Mixtral-8x7B {args.moe_linear} "
+                  f"K={K} N={N} E=8 top-2",
         "value": round(step_bytes / (ms_step * 1e-3) / 1e9, 1), "unit": "GB/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8xint4->int32",
         "data": "synthetic (seeded; X ~N(0,1) + 1% channels x20, W ~N(0,0.02) + 0.1% x10, "
                 "top-2 of biased normal router logits)",
-        "config": {"workload": "MoE decode sweep: quant_act + grouped W4A8-IS GEMM, Mixtral-8x7B "
-                               "experts (w1: K=4096 N=14336, E=8, top-2), T in {1,4,16,64} tokens per step",
+        "config": {"workload": f"MoE decode sweep: quant_act + grouped W4A8-IS GEMM, Mixtral-8x7B "
+                               f"experts ({args.moe_linear}: K={K} N={N}, E=8, top-2), "
+                               "T in {1,4,16,64} tokens per step",
                    "launch": "hip_graph" if args.launch == "graph" else "eager",
                    "weight_buffers_rotated": Rr},
         "eager": {"ms_per_step": round(eager_ms, 4),
@@ -773,6 +777,8 @@ def main():
     ap.add_argument("--launch", default="graph", choices=["graph", "eager"],
                     help="decode workload: replay each step from a HIP graph (default) or "
                          "issue every launch from Python")
+    ap.add_argument("--moe-linear", default="w1", choices=["w1", "w2"],
+                    help="moe workload: the expert linear (w1/w3: 4096 -> 14336, w2: 14336 -> 4096)")
     ap.add_argument("--profile-m", type=int, default=0)
     ap.add_argument("--copy-probe-mb", type=int, default=0)
     args = ap.parse_args()

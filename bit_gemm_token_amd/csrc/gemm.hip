@@ -839,6 +839,15 @@ __global__ __launch_bounds__(NW * 64) void k_w8a8_zp(
 //      ascending fma chain).
 // Every load is a register load, so the compiler's wait counts stay exact.
 // =====================================================================
+// groups per staged X chunk: the largest divisor of G up to 32 (one row
+// block) or 8 (more), so a chunk is at most 64 KiB, that is a multiple of the
+// weight ring depth D
+constexpr int decode_chunk_groups(int G, int MR, int D) {
+  int c = MR == 1 ? 32 : 8;
+  while (c > D && (G % c != 0 || c % D != 0)) --c;
+  return c;
+}
+
 template <bool FS, int W, int D, int G, int MR, typename ST, bool FQ, int IT, bool GR = false>
 __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
     const int8_t* __restrict__ qx, const float* __restrict__ sx,
@@ -847,8 +856,7 @@ __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
     OutY y, int32_t* __restrict__ acc_out,
     const void* __restrict__ xf, int ldx, int8_t* __restrict__ q_out, float* __restrict__ s_out,
     Route rt) {
-  constexpr int CGM = MR == 1 ? 32 : 8;
-  constexpr int CG = G < CGM ? G : CGM;              // groups per X chunk (<= 64 KiB)
+  constexpr int CG = decode_chunk_groups(G, MR, D);  // groups per X chunk (<= 64 KiB)
   constexpr int NCH = G / CG;                        // chunks
   constexpr int CFR = CG * MR * 2;                   // 1 KiB fragments per chunk
   constexpr int FPW = CFR / W;                       // fragments per wave per chunk
@@ -1387,17 +1395,24 @@ hipError_t launch_w4a8_linear(const void* x, int x_type, int64_t ldx, const uint
   return hipGetLastError();
 }
 
-// Grouped (mixture-of-experts) integer-scale GEMM: T <= 64 activation rows
-// (so every expert has at most 64 slots) on the decode path takes the decode
-// kernel with one workgroup row per expert; otherwise the tiled kernel over
-// the experts' row tiles.
+// Grouped (mixture-of-experts) integer-scale GEMM: few tokens (so every
+// expert has at most 16*MR slots) take the decode kernel with one workgroup
+// row per expert: T <= 64 for K/128 in {16, 32} (the expert w1/w3 shapes),
+// T <= 32 for K/128 = 112 (Mixtral's w2, whose 112 groups of scales leave LDS
+// room for at most two row blocks); otherwise the tiled kernel over the
+// experts' row tiles.
+static bool moe_decode_path(int64_t T, int64_t K) {
+  const int64_t G = K / kGroup;
+  return (T <= 64 && (G == 16 || G == 32)) || (T <= 32 && G == 112);
+}
+
 template <typename ST>
 static void launch_moe_t(const int8_t* qx, const float* sx, const uint8_t* packed,
                          const ST* iscale, float inv_alpha, int N, int K, const Route& rt,
                          OutY y, int32_t* acc_out, hipStream_t stream) {
   const uint4* pk = reinterpret_cast<const uint4*>(packed);
   const int G = K / kGroup;
-  if (rt.T <= 64 && (G == 16 || G == 32)) {
+  if (moe_decode_path(rt.T, K)) {
     const int mr = (rt.T + 15) / 16;
     const dim3 grid((N / 16 + kDecodeW - 1) / kDecodeW, rt.E), block(kDecodeW * kWave);
     const void* nx = nullptr;
@@ -1413,6 +1428,9 @@ static void launch_moe_t(const int8_t* qx, const float* sx, const uint8_t* packe
       if (mr == 1) BGT_MOE_DECODE(32, 1);
       else if (mr == 2) BGT_MOE_DECODE(32, 2);
       else BGT_MOE_DECODE(32, 4);
+    } else if (G == 112) {
+      if (mr == 1) BGT_MOE_DECODE(112, 1);
+      else BGT_MOE_DECODE(112, 2);
     } else {
       if (mr == 1) BGT_MOE_DECODE(16, 1);
       else if (mr == 2) BGT_MOE_DECODE(16, 2);
@@ -1445,8 +1463,7 @@ hipError_t launch_w4a8_moe(const int8_t* qx, const float* sx, int64_t T, const i
 }
 
 const char* w4a8_moe_kernel_name(int64_t T, int64_t K) {
-  const int64_t G = K / kGroup;
-  return T <= 64 && (G == 16 || G == 32) ? "k_w4a8_decode<IS,grouped>" : "k_w4a8_prefill<4,2,2,2,IS,grouped>";
+  return moe_decode_path(T, K) ? "k_w4a8_decode<IS,grouped>" : "k_w4a8_prefill<4,2,2,2,IS,grouped>";
 }
 
 hipError_t launch_w8a8_zp(const uint8_t* qx, const float* sx, const int32_t* zx,

@@ -2,8 +2,8 @@
 
 bgt_w4a8_moe_gemm_is must give, for every routed slot, the oracle's int32
 accumulators and outputs bit-exactly: on the decode path (T <= 64 tokens,
-K/128 in {16, 32}: one workgroup row per expert, experts without tokens
-skipped) and on the tiled path (the experts' row tiles in one launch), with
+K/128 in {16, 32}, and T <= 32 for K/128 = 112: one workgroup row per expert,
+experts without tokens skipped) and on the tiled path (the experts' row tiles in one launch), with
 skewed and degenerate routings, narrow scales, fp16 / bf16 outputs, and the
 Mixtral-8x7B expert shapes (w1/w3: 4096 -> 14336, w2: 14336 -> 4096) on
 sampled columns.
@@ -94,7 +94,8 @@ def _run(bgt, orc, dev, T, E, K, N, seed, routing=None, width=4, out_dtype=None,
 
 
 @pytest.mark.parametrize("T,E,K,N", [(1, 8, 4096, 64), (5, 8, 4096, 208), (16, 8, 2048, 96),
-                                     (33, 8, 4096, 48), (64, 8, 2048, 16), (20, 3, 4096, 80)])
+                                     (33, 8, 4096, 48), (64, 8, 2048, 16), (20, 3, 4096, 80),
+                                     (1, 8, 14336, 48), (12, 8, 14336, 80), (32, 5, 14336, 32)])
 def test_moe_decode_path(bgt, orc, dev, T, E, K, N):
     say(f"moe {bgt.w4a8_moe_kernel_name(T, K)} T={T} E={E} K={K} N={N}")
     offs = _run(bgt, orc, dev, T, E, K, N, seed=T * 31 + K + N)
@@ -118,7 +119,7 @@ def test_moe_all_tokens_one_expert(bgt, orc, dev, T, K):
     _run(bgt, orc, dev, T, 8, K, 64, seed=T + 3, routing=routing)
 
 
-@pytest.mark.parametrize("T,K", [(12, 4096), (150, 384)])
+@pytest.mark.parametrize("T,K", [(12, 4096), (150, 384), (9, 14336)])
 @pytest.mark.parametrize("width", [1, 2])
 def test_moe_narrow_scales(bgt, orc, dev, width, T, K):
     say(f"moe width={width} T={T} K={K}")
