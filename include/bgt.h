@@ -1,6 +1,8 @@
 /*
  * bgt.h -- C ABI of libbgt: the fine-grained W4A8 integer-scale linear layer
- * Y = X.W on AMD MI355X (gfx950), plus its two controls.
+ * Y = X.W on AMD MI355X (gfx950), its two controls (float-scale W4A8,
+ * zero-point W8A8), and two variants of the same epilogue: fine-grained W8A8
+ * with integer scales and the grouped (mixture-of-experts) W4A8 GEMM.
  *
  * Pages cited:
  *   [IS] "Integer Scale: A Free Lunch for Faster Fine-grained Quantization of
@@ -36,7 +38,8 @@ extern "C" {
 
 /* Status codes. */
 #define BGT_OK                     0
-#define BGT_WARN_ACC_MAY_OVERFLOW  1   /* pack: 113792 * G * max(iscale) >= 2^31       */
+#define BGT_WARN_ACC_MAY_OVERFLOW  1   /* pack: worst-case |A| = 128*127*q_max * G *
+                                          max(iscale) reaches 2^31 (q_max 7 or 127)     */
 #define BGT_ERR_NULL              -1   /* a required pointer is NULL                    */
 #define BGT_ERR_SHAPE             -2   /* a size is out of range or not a multiple     */
 #define BGT_ERR_ALIGN             -3   /* a pointer or leading dimension is misaligned */
