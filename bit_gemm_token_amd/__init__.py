@@ -6,15 +6,21 @@ turns non-zero status codes into exceptions. Every step of the computation
 runs in the HIP kernels of libbgt; there is no fallback. If the library is not
 built, importing the entry points raises.
 
-Entry points (same names as the C ABI without the ``bgt_`` prefix):
+Entry points (same names as the C ABI without the ``bgt_`` prefix; the _ex
+and _narrow C variants are reached through the dtype of the tensors passed):
     quantize_act(x, mode="sym")            -> (q, scale[, zero], rowsum)
     pack_weights_int4(w, alpha=1024)       -> dict(packed, fscale, iscale, alpha, status)
+    narrow_iscale(iscale, width)           -> iscale as uint8 / uint16
     w4a8_gemm_is(qx, sx, packed, iscale, alpha, N)   -> y
-    w4a8_gemm_fs(qx, sx, packed, fscale, N)          -> y
+    w4a8_gemm_is_narrow(qx, sx, packed, iscale, alpha, N, out_dtype=None) -> y
+    w4a8_linear_is(x, packed, iscale, alpha, N)      -> (y, qx, sx)
+    w4a8_linear_fused(x)                   -> bool (one launch for this x)
+    w4a8_gemm_fs(qx, sx, packed, fscale, N, out_dtype=None) -> y
     w8a8_gemm_zp(qx, sx, zx, rowsum_x, qw, sw, zw, colsum_w) -> y
     w4a8_moe_gemm_is(qx, sx, offsets, slot_token, packed, iscale, alpha, N) -> y
     pack_weights_int8(w, alpha=0)          -> dict(qw, fscale, iscale, alpha, status)
     w8a8_gemm_is(qx, sx, qw, iscale, alpha, N)       -> y
+    w4a8_kernel_name / w8a8_is_kernel_name / w4a8_moe_kernel_name -> kernel a shape runs
 """
 from __future__ import annotations
 
