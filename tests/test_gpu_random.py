@@ -1,4 +1,4 @@
-"""GPU parity on seeded random shapes, for every GEMM entry point.
+"""GPU parity on seeded random shapes, for every GEMM entry point and the quantizer.
 
 Shapes, amplifiers, scale widths, output types and routings are drawn from a
 fixed seed, so each case is reproducible by its id; the draws cover every
@@ -201,3 +201,64 @@ def test_random_linear(bgt, orc, dev, case):
     np.testing.assert_array_equal(sx.cpu().numpy().view(np.int32), os_.view(np.int32))
     _, oy, _ = orc.w4a8_gemm_is(oq, os_, ow["codes"], ow["iscale"], 1024)
     _check_y(orc, y, oy, kind)
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_random_w8a8_zp(bgt, orc, dev, case):
+    g = np.random.default_rng(17000 + case)
+    M, K, N = _draw_shape(g, 64 if case % 2 else 600, 48, 128)
+    relu = bool(case % 3 == 0)
+    say(f"random w8a8_zp #{case}: M={M} K={K} N={N} relu={relu}")
+    x, w = synth.w8a8_inputs(18000 + case, M, K, N, relu=relu)
+    qx, sx, zx, rx = bgt.quantize_act(to_dev(x, dev), mode="asym")
+    qw, sw, zw, cw = bgt.quantize_act(to_dev(np.ascontiguousarray(w.T), dev), mode="asym")
+    oqx, osx, ozx, orx = orc.quant_asym_u8(x)
+    oqw, osw, ozw, ocw = orc.quant_asym_u8(np.ascontiguousarray(w.T))
+    for got, want in ((qx, oqx), (zx, ozx), (rx, orx), (qw, oqw), (zw, ozw), (cw, ocw)):
+        np.testing.assert_array_equal(got.cpu().numpy(), want)
+    for got, want in ((sx, osx), (sw, osw)):
+        np.testing.assert_array_equal(got.cpu().numpy().view(np.int32), want.view(np.int32))
+    acc = torch.full((M, N), -1, dtype=torch.int32, device=dev)
+    y = bgt.w8a8_gemm_zp(qx, sx, zx, rx, qw, sw, zw, cw, acc_out=acc)
+    oA, oy, ov = orc.w8a8_gemm_zp(oqx, osx, ozx, orx, oqw, osw, ozw, ocw)
+    assert ov == 0
+    np.testing.assert_array_equal(acc.cpu().numpy().astype(np.int64), oA)
+    _check_y(orc, y, oy, "f32")
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_random_quantize(bgt, orc, dev, case):
+    # any row count, any column count (vector and scalar paths), padded rows, three input types
+    g = np.random.default_rng(19000 + case)
+    rows = int(g.integers(1, 300))
+    cols = int(g.integers(1, 5000)) if case % 2 else 16 * int(g.integers(1, 600))
+    pad = int(g.choice([0, 0, 4, 7]))
+    kind = str(g.choice(["f32", "f16", "bf16"]))
+    asym = bool(case % 3 == 0)
+    say(f"random quantize #{case}: rows={rows} cols={cols} pad={pad} x={kind} asym={asym}")
+    x = synth.activations(20000 + case, rows, cols, outlier_frac=0.0 if asym else 0.01,
+                          mean=0.5 if asym else 0.0)
+    if kind == "f32":
+        xh, xw = x, x
+    elif kind == "f16":
+        xh = x.astype(np.float16)
+        xw = xh.astype(np.float32)
+    else:
+        xh = orc.f32_to_bf16_bits(x)
+        xw = orc.bf16_bits_to_f32(xh)
+    buf = np.zeros((rows, cols + pad), xh.dtype)
+    buf[:, :cols] = xh
+    xd = to_dev(buf if kind != "bf16" else buf.view(np.int16), dev)
+    if kind == "bf16":
+        xd = xd.view(torch.bfloat16)
+    xd = xd[:, :cols]
+    if asym:
+        q, s, z, r = bgt.quantize_act(xd, mode="asym")
+        oq, os_, oz, orow = orc.quant_asym_u8(xw)
+        np.testing.assert_array_equal(z.cpu().numpy(), oz)
+        np.testing.assert_array_equal(r.cpu().numpy(), orow)
+    else:
+        q, s, _ = bgt.quantize_act(xd)
+        oq, os_ = orc.quant_sym_i8(xw)
+    np.testing.assert_array_equal(q.cpu().numpy(), oq)
+    np.testing.assert_array_equal(s.cpu().numpy().view(np.int32), os_.view(np.int32))
