@@ -70,6 +70,25 @@ def test_pack_int8_matches_oracle(bgt, orc, dev, K, N, alpha):
     np.testing.assert_array_equal(got["iscale"].cpu().numpy(), ref["iscale"])
 
 
+def test_pack_int8_range_error(bgt, dev):
+    say("pack_weights_int8 range error")
+    w = np.full((128, 16), 100.0, np.float32)        # s = 100/127, s * 2^24 >= 2^23
+    with pytest.raises(bgt.BgtError) as e:
+        bgt.pack_weights_int8(to_dev(w, dev), alpha=1 << 24)
+    assert e.value.status == bgt.BGT_ERR_RANGE
+
+
+def test_pack_int8_overflow_warning(bgt, dev):
+    say("pack_weights_int8 accumulator warning")
+    # s = 1/127 -> iscale 129 at 2^14; 2064512 * 16 * 129 >= 2^31, but not for int4's bound
+    w = np.full((2048, 16), 1.0, np.float32)
+    pw = bgt.pack_weights_int8(to_dev(w, dev), alpha=1 << 14)
+    assert pw["status"] == bgt.BGT_WARN_ACC_MAY_OVERFLOW
+    assert 113792 * 16 * 129 < 2 ** 31 <= 2064512 * 16 * 129
+    ok = bgt.pack_weights_int8(to_dev(np.full((128, 16), 1.0, np.float32), dev), alpha=1 << 14)
+    assert ok["status"] == bgt.BGT_OK                 # one group: 2064512 * 129 < 2^31
+
+
 def _case(orc, seed, M, K, N, alpha=ALPHA):
     x = synth.activations(seed, M, K)
     w = synth.weights(seed + 1, K, N, std=0.02, outlier_prob=0.001)
