@@ -214,3 +214,30 @@ def test_graph_replays_match_eager_moe(dev, bgt):
             xs[T].copy_(torch.from_numpy(synth.activations(400 + rep, T, K)))
 
     _replay_check(dev, run, outs, refill)
+
+
+def test_graph_replays_match_eager_linear(dev, bgt):
+    # the entry point the decode bench captures: fused quantization + GEMM for
+    # M <= 4, quantizer + GEMM otherwise; 1-byte integer scales
+    K, N = 4096, 1024
+    Ms = (1, 4, 16)
+    print(f"graph replay linear: K={K} N={N} M={Ms}", flush=True)
+    w = synth.weights(14, K, N, std=0.02, outlier_prob=0.001)
+    pw = bgt.pack_weights_int4(torch.from_numpy(w).to(dev), alpha=1024)
+    isc = bgt.narrow_iscale(pw["iscale"], 1)
+    xs = {M: torch.zeros((M, K), dtype=torch.float32, device=dev) for M in Ms}
+    qs = {M: (torch.empty((M, K), dtype=torch.int8, device=dev),
+              torch.empty(M, dtype=torch.float32, device=dev)) for M in Ms}
+    outs = [torch.empty((M, N), dtype=torch.float32, device=dev) for M in Ms]
+    assert bgt.w4a8_linear_fused(xs[1]) and not bgt.w4a8_linear_fused(xs[16])
+
+    def run(ys):
+        for M, y in zip(Ms, ys):
+            q, s = qs[M]
+            bgt.w4a8_linear_is(xs[M], pw["packed"], isc, pw["alpha"], N, qx=q, sx=s, y=y)
+
+    def refill(rep):
+        for M in Ms:
+            xs[M].copy_(torch.from_numpy(synth.activations(500 + rep, M, K)))
+
+    _replay_check(dev, run, outs, refill)
