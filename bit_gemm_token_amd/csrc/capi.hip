@@ -8,6 +8,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "bgt.h"
@@ -222,15 +223,20 @@ int bgt_narrow_iscale(const int32_t* iscale, int64_t count, int width, void* out
   if (count < 1 || count > ((int64_t)1 << 36)) return BGT_ERR_SHAPE;
   if (!aligned16(iscale) || !aligned16(out)) return BGT_ERR_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // range check on the host (an offline step): every value in [0, 2^(8*width))
-  std::vector<int32_t> h((size_t)count);
-  hipError_t e = hipMemcpyAsync(h.data(), iscale, (size_t)count * sizeof(int32_t),
-                                hipMemcpyDeviceToHost, s);
-  if (e == hipSuccess) e = hipStreamSynchronize(s);
-  if (e != hipSuccess) return BGT_ERR_HIP;
+  // range check on the host (an offline step): every value in [0, 2^(8*width)),
+  // read back in chunks of at most 4 Mi values
   const int32_t top = width == 1 ? 255 : 65535;
-  for (int32_t v : h)
-    if (v < 0 || v > top) return BGT_ERR_RANGE;
+  const int64_t chunk = std::min<int64_t>(count, (int64_t)1 << 22);
+  std::vector<int32_t> h((size_t)chunk);
+  for (int64_t i0 = 0; i0 < count; i0 += chunk) {
+    const int64_t n = std::min<int64_t>(chunk, count - i0);
+    hipError_t e = hipMemcpyAsync(h.data(), iscale + i0, (size_t)n * sizeof(int32_t),
+                                  hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return BGT_ERR_HIP;
+    for (int64_t k = 0; k < n; ++k)
+      if (h[(size_t)k] < 0 || h[(size_t)k] > top) return BGT_ERR_RANGE;
+  }
   return hip_status(bgt::launch_narrow_scales(iscale, count, width, out, s));
 }
 
