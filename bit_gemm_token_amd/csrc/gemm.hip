@@ -882,16 +882,18 @@ __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
   const bool tvalid = t < T;
   const int tc = tvalid ? t : T - 1;
 
-  // grouped GEMM: this workgroup serves expert blockIdx.y, whose slots are
-  // r0 .. r0+M-1 (at most the 16*MR rows of a workgroup); an expert without
+  // grouped GEMM: this workgroup serves expert blockIdx.y, row pass
+  // blockIdx.z: the expert's slots r0 .. r0+M-1 with r0 = first slot +
+  // 16*MR*z (the 16*MR rows of a workgroup); an expert or a pass without
   // slots reads nothing
   int r0 = 0;
   if constexpr (GR) {
     const int e = blockIdx.y;
-    r0 = clamp_route(rt.offs[e], 0, rt.R);
-    const int r1 = clamp_route(rt.offs[e + 1], r0, rt.R);
-    M = r1 - r0 < 16 * MR ? r1 - r0 : 16 * MR;
-    if (M == 0) return;
+    const int ra = clamp_route(rt.offs[e], 0, rt.R);
+    const int rb = clamp_route(rt.offs[e + 1], ra, rt.R);
+    r0 = ra + (int)blockIdx.z * 16 * MR;
+    if (r0 >= rb) return;
+    M = rb - r0 < 16 * MR ? rb - r0 : 16 * MR;
     packed += e * rt.wstride / 16;
     if (FS) fscale += e * rt.sstride;
     else iscale += e * rt.sstride;
@@ -1395,15 +1397,24 @@ hipError_t launch_w4a8_linear(const void* x, int x_type, int64_t ldx, const uint
   return hipGetLastError();
 }
 
-// Grouped (mixture-of-experts) integer-scale GEMM: few tokens (so every
-// expert has at most 16*MR slots) take the decode kernel with one workgroup
-// row per expert: T <= 64 for K/128 in {16, 32} (the expert w1/w3 shapes),
-// T <= 32 for K/128 = 112 (Mixtral's w2, whose 112 groups of scales leave LDS
-// room for at most two row blocks); otherwise the tiled kernel over the
-// experts' row tiles.
+// Grouped (mixture-of-experts) integer-scale GEMM: few tokens (T <= 64) with
+// K/128 in {16, 32} (the expert w1/w3 shapes) or 112 (Mixtral's w2) take the
+// decode kernel with one workgroup row per expert and row pass; otherwise the
+// tiled kernel over the experts' row tiles.
 static bool moe_decode_path(int64_t T, int64_t K) {
   const int64_t G = K / kGroup;
-  return (T <= 64 && (G == 16 || G == 32)) || (T <= 32 && G == 112);
+  return T <= 64 && (G == 16 || G == 32 || G == 112);
+}
+
+// Row blocks per workgroup of the grouped decode kernel: enough for 1.5x the
+// mean slots per expert (at most 4; at most 2 for 112 groups, whose scales
+// leave LDS room for two); experts with more slots take further row passes
+// (grid z), each streaming the expert's weights again.
+static int moe_row_blocks(int64_t R, int64_t E, int64_t K) {
+  const int64_t mean = (R + E - 1) / E;
+  int mr = (int)((3 * mean / 2 + 15) / 16);
+  mr = mr < 1 ? 1 : (mr == 3 ? 4 : (mr > 4 ? 4 : mr));
+  return K / kGroup == 112 && mr > 2 ? 2 : mr;
 }
 
 template <typename ST>
@@ -1413,8 +1424,10 @@ static void launch_moe_t(const int8_t* qx, const float* sx, const uint8_t* packe
   const uint4* pk = reinterpret_cast<const uint4*>(packed);
   const int G = K / kGroup;
   if (moe_decode_path(rt.T, K)) {
-    const int mr = (rt.T + 15) / 16;
-    const dim3 grid((N / 16 + kDecodeW - 1) / kDecodeW, rt.E), block(kDecodeW * kWave);
+    // every expert has at most T slots (a token reaches an expert once)
+    const int mr = moe_row_blocks(rt.R, rt.E, K);
+    const int passes = (rt.T + 16 * mr - 1) / (16 * mr);
+    const dim3 grid((N / 16 + kDecodeW - 1) / kDecodeW, rt.E, passes), block(kDecodeW * kWave);
     const void* nx = nullptr;
     int8_t* nq = nullptr;
     float* ns = nullptr;

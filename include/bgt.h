@@ -277,9 +277,9 @@ int bgt_w8a8_gemm_zp(const uint8_t* qx, const float* sx, const int32_t* zx,
  *   y               R x N of element type y_type, row r = slot r.
  *   acc_out         optional R x N int32 (the integer accumulators).
  * Routing outside these rules cannot make the kernels read or write outside
- * the buffers (offsets are clamped to [0, R], tokens to [0, T), at most 64
- * rows per expert are computed on the T <= 64 path), but gives unspecified
- * rows of y. Requirements: 1 <= T <= 65536, N and K as bgt_w4a8_gemm_is,
+ * the buffers (offsets are clamped to [0, R], tokens to [0, T), at most T
+ * rows per expert, rounded up to a multiple of 16, are computed on the
+ * T <= 64 path), but gives unspecified rows of y. Requirements: 1 <= T <= 65536, N and K as bgt_w4a8_gemm_is,
  * 1 <= E <= 256, 1 <= R <= min(T*E, 2^24); qx, packed, iscale, y, acc_out
  * 16-byte aligned. Experts without slots read no weights on the T <= 64 path.
  */

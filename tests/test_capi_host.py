@@ -261,8 +261,8 @@ def test_moe_validation(L):
     assert call(y=MIS) == bgt.BGT_ERR_ALIGN
     assert call(acc=MIS) == bgt.BGT_ERR_ALIGN
     assert bgt.w4a8_moe_kernel_name(16, 4096) == "k_w4a8_decode<IS,grouped>"
-    assert bgt.w4a8_moe_kernel_name(32, 14336) == "k_w4a8_decode<IS,grouped>"
-    assert bgt.w4a8_moe_kernel_name(33, 14336) == "k_w4a8_prefill<4,2,2,2,IS,grouped>"
+    assert bgt.w4a8_moe_kernel_name(64, 14336) == "k_w4a8_decode<IS,grouped>"
+    assert bgt.w4a8_moe_kernel_name(65, 14336) == "k_w4a8_prefill<4,2,2,2,IS,grouped>"
     assert bgt.w4a8_moe_kernel_name(16, 1152) == "k_w4a8_prefill<4,2,2,2,IS,grouped>"
     assert bgt.w4a8_moe_kernel_name(65, 4096) == "k_w4a8_prefill<4,2,2,2,IS,grouped>"
 

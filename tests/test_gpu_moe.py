@@ -2,8 +2,8 @@
 
 bgt_w4a8_moe_gemm_is must give, for every routed slot, the oracle's int32
 accumulators and outputs bit-exactly: on the decode path (T <= 64 tokens,
-K/128 in {16, 32}, and T <= 32 for K/128 = 112: one workgroup row per expert,
-experts without tokens skipped) and on the tiled path (the experts' row tiles in one launch), with
+K/128 in {16, 32, 112}: one workgroup row per expert and row pass, experts
+without tokens skipped) and on the tiled path (the experts' row tiles in one launch), with
 skewed and degenerate routings, narrow scales, fp16 / bf16 outputs, and the
 Mixtral-8x7B expert shapes (w1/w3: 4096 -> 14336, w2: 14336 -> 4096) on
 sampled columns.
@@ -95,7 +95,8 @@ def _run(bgt, orc, dev, T, E, K, N, seed, routing=None, width=4, out_dtype=None,
 
 @pytest.mark.parametrize("T,E,K,N", [(1, 8, 4096, 64), (5, 8, 4096, 208), (16, 8, 2048, 96),
                                      (33, 8, 4096, 48), (64, 8, 2048, 16), (20, 3, 4096, 80),
-                                     (1, 8, 14336, 48), (12, 8, 14336, 80), (32, 5, 14336, 32)])
+                                     (1, 8, 14336, 48), (12, 8, 14336, 80), (32, 5, 14336, 32),
+                                     (64, 8, 14336, 48), (50, 2, 2048, 32)])
 def test_moe_decode_path(bgt, orc, dev, T, E, K, N):
     say(f"moe {bgt.w4a8_moe_kernel_name(T, K)} T={T} E={E} K={K} N={N}")
     offs = _run(bgt, orc, dev, T, E, K, N, seed=T * 31 + K + N)
@@ -110,9 +111,10 @@ def test_moe_tiled_path(bgt, orc, dev, T, E, K, N):
     _run(bgt, orc, dev, T, E, K, N, seed=T * 37 + K + N)
 
 
-@pytest.mark.parametrize("T,K", [(64, 4096), (200, 512)])
+@pytest.mark.parametrize("T,K", [(64, 4096), (200, 512), (64, 14336), (40, 2048)])
 def test_moe_all_tokens_one_expert(bgt, orc, dev, T, K):
     # maximal imbalance: expert 5 takes every token, expert 2 one, the rest none
+    # (on the decode path the busy expert takes several row passes)
     say(f"moe skewed T={T} K={K}")
     routing = np.full((T, 1), 5, np.int32)
     routing[0, 0] = 2
@@ -133,7 +135,8 @@ def test_moe_half_outputs(bgt, orc, dev, T, K):
         _run(bgt, orc, dev, T, 8, K, 48, seed=T + 11, out_dtype=dt)
 
 
-@pytest.mark.parametrize("T,K,N", [(16, 4096, 14336), (512, 4096, 14336), (16, 14336, 4096)])
+@pytest.mark.parametrize("T,K,N", [(16, 4096, 14336), (64, 4096, 14336), (512, 4096, 14336),
+                                   (16, 14336, 4096), (64, 14336, 4096)])
 def test_moe_mixtral_shapes_sampled(bgt, orc, dev, T, K, N):
     """Mixtral-8x7B experts (8, top-2) at the w1/w3 and w2 shapes, in the
     launches the bench times; sampled output columns against the oracle."""
