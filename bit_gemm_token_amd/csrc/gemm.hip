@@ -1437,6 +1437,15 @@ static void launch_moe_t(const int8_t* qx, const float* sx, const uint8_t* packe
                                     true>),                                                      \
                      grid, block, 0, stream, qx, sx, pk, iscale, nf, inv_alpha, 0, N, y, acc_out, \
                      nx, 0, nq, ns, rt)
+    if (G == 112 && rt.R <= 4) {
+      // at most four experts busy with narrow (N = 4096) layers: 4-wave
+      // workgroups put each expert's tiles on twice as many CUs
+      const dim3 g4((N / 16 + 3) / 4, rt.E, passes), b4(4 * kWave);
+      hipLaunchKernelGGL((k_w4a8_decode<false, 4, decode_depth(1), 112, 1, ST, false, kF32, true>),
+                         g4, b4, 0, stream, qx, sx, pk, iscale, nf, inv_alpha, 0, N, y, acc_out,
+                         nx, 0, nq, ns, rt);
+      return;
+    }
     if (G == 32) {
       if (mr == 1) BGT_MOE_DECODE(32, 1);
       else if (mr == 2) BGT_MOE_DECODE(32, 2);
