@@ -14,7 +14,7 @@
 // i.e. one B operand of v_mfma_i32_16x16x64_i8 per half, read with one
 // contiguous 16-byte load per lane.
 //
-// Two kernels:
+// Three kernels:
 //   split (M <= 64, weight streaming): one workgroup per 16-column tile, its
 //     KS waves split the groups; each wave keeps D groups of weights, their
 //     activation fragments and scales in flight in registers, runs two MFMAs
@@ -26,6 +26,9 @@
 //     flight; waves 0-3 and 4-7 take the two 64-k halves of a group on a 2 x 2
 //     arrangement of 32 x 32 blocks (v_mfma_i32_32x32x32_i8), apply the
 //     group's scale to their half's partial and meet once at the end.
+//   wide (large M): 256 x 128 tiles, 8 waves of 64 x 64, three copy stages;
+//     3x the ops per copied byte of the 64 x 64 tile, chosen when its rounds
+//     of workgroups move fewer copy bytes.
 #include <type_traits>
 
 #include "device_common.h"
