@@ -21,8 +21,8 @@ import torch  # noqa: E402
 
 import bit_gemm_token_amd as bgt  # noqa: E402
 
-if torch.cuda.is_available():
-    pytest.skip("fake device pointers: runs only where no GPU is visible", allow_module_level=True)
+pytestmark = pytest.mark.skipif(torch.cuda.is_available(),
+                                reason="fake device pointers: runs only where no GPU is visible")
 
 P = ctypes.c_void_p
 ALIGNED = 0x10000
