@@ -656,7 +656,7 @@ def run_moe(args, torch, bgt, dev):
                          "gemm_TOPS": round(2 * R * N * K / us / 1e6, 2),
                          "hbm_frac": round(b / us / 1e3 / HBM_PEAK_GBS, 4),
                          "mfma_frac": round(2 * R * N * K / us / 1e6 / INT8_PEAK_TOPS, 4),
-                         "kernel": bgt.w4a8_moe_kernel_name(T, K)}
+                         "kernel": bgt.w4a8_moe_kernel_name(T, E, route[T][3], K)}
     step_bytes = sum(moe_bytes(T, route[T][3], route[T][2], N, K, E) + quant_bytes(T, K) for T in Ts)
     durs = [u for T in Ts for u in per_t[T]]
     avg_us = float(np.mean(durs))
@@ -679,8 +679,8 @@ def run_moe(args, torch, bgt, dev):
                   "value": round(step_bytes / (eager_ms * 1e-3) / 1e9, 1)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(bgt.w4a8_moe_kernel_name(1, K), Ts),
-                     "kernel": bgt.w4a8_moe_kernel_name(1, K), "launch_T": Ts,
+                     "traffic": measured_traffic(bgt.w4a8_moe_kernel_name(1, E, route[1][3], K), Ts),
+                     "kernel": bgt.w4a8_moe_kernel_name(1, E, route[1][3], K), "launch_T": Ts,
                      "avg_launch_us": round(avg_us, 3), "bytes_per_launch": int(avg_bytes)},
         "sweep": sweep,
     }, (x, None)
@@ -729,7 +729,7 @@ def run_profile_m(args, torch, bgt, dev, M):
         torch.cuda.synchronize()
         na = int((np.diff(offs) > 0).sum())
         return {"profile_m": M, "launches": args.warmup + args.steps,
-                "kernel": bgt.w4a8_moe_kernel_name(M, K),
+                "kernel": bgt.w4a8_moe_kernel_name(M, E, len(tok), K),
                 "gemm_bytes": moe_bytes(M, len(tok), na, N, K, E)}
     K, N = synth.K_LAYER, synth.N_LAYER
     x, w = synth.layer_inputs(0, M=M, K=K, N=N)

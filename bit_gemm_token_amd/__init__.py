@@ -96,7 +96,7 @@ def lib():
         L.bgt_w8a8_is_kernel_name.argtypes = [I64, I64, I64]
         L.bgt_w4a8_moe_gemm_is.argtypes = [P, P, I64, P, P, I64, I64, P, P, I, I, I64, I64, P, I,
                                            P, P]
-        L.bgt_w4a8_moe_kernel_name.argtypes = [I64, I64]
+        L.bgt_w4a8_moe_kernel_name.argtypes = [I64, I64, I64, I64]
         for f in EXPORTED:
             getattr(L, f).restype = ctypes.c_char_p if f in _NAMES else I
         _lib = L
@@ -430,9 +430,10 @@ def w8a8_gemm_is(qx, sx, qw, iscale, alpha: int, N: int, y=None, acc_out=None, o
     return y
 
 
-def w4a8_moe_kernel_name(T: int, K: int) -> str:
-    """Name of the kernel a grouped W4A8 call with T tokens launches."""
-    return lib().bgt_w4a8_moe_kernel_name(int(T), int(K)).decode()
+def w4a8_moe_kernel_name(T: int, E: int, R: int, K: int) -> str:
+    """Name of the kernel a grouped W4A8 call with T tokens, E experts and R
+    routed slots launches."""
+    return lib().bgt_w4a8_moe_kernel_name(int(T), int(E), int(R), int(K)).decode()
 
 
 def w4a8_moe_gemm_is(qx, sx, offsets, slot_token, packed, iscale, alpha: int, N: int, y=None,

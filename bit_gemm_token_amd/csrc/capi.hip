@@ -44,7 +44,7 @@ int searched_alpha_log2(float smin) {
 
 extern "C" {
 
-int bgt_abi_version(void) { return 105; }
+int bgt_abi_version(void) { return 106; }
 
 int bgt_w4a8_linear_fused(int64_t M, int64_t K, const void* x, int64_t ldx) {
   return bgt::w4a8_linear_fused(M, K, x, ldx) ? 1 : 0;
@@ -261,10 +261,11 @@ int bgt_w4a8_moe_gemm_is(const int8_t* qx, const float* sx, int64_t T,
                                          acc_out, static_cast<hipStream_t>(stream)));
 }
 
-const char* bgt_w4a8_moe_kernel_name(int64_t T, int64_t K) {
-  if (T < 1 || T > 65536 || K < BGT_GROUP || K > 65536 || K % BGT_GROUP != 0)
+const char* bgt_w4a8_moe_kernel_name(int64_t T, int64_t E, int64_t R, int64_t K) {
+  if (T < 1 || T > 65536 || K < BGT_GROUP || K > 65536 || K % BGT_GROUP != 0 || E < 1 ||
+      E > 256 || R < 1 || R > T * E || R > (int64_t{1} << 24))
     return "invalid shape";
-  return bgt::w4a8_moe_kernel_name(T, K);
+  return bgt::w4a8_moe_kernel_name(T, E, R, K);
 }
 
 int bgt_w8a8_gemm_is(const int8_t* qx, const float* sx, const int8_t* qw, const void* iscale,

@@ -1401,11 +1401,6 @@ hipError_t launch_w4a8_linear(const void* x, int x_type, int64_t ldx, const uint
 // K/128 in {16, 32} (the expert w1/w3 shapes) or 112 (Mixtral's w2) take the
 // decode kernel with one workgroup row per expert and row pass; otherwise the
 // tiled kernel over the experts' row tiles.
-static bool moe_decode_path(int64_t T, int64_t K) {
-  const int64_t G = K / kGroup;
-  return T <= 64 && (G == 16 || G == 32 || G == 112);
-}
-
 // Row blocks per workgroup of the grouped decode kernel: enough for 1.5x the
 // mean slots per expert (at most 4; at most 2 for 112 groups, whose scales
 // leave LDS room for two); experts with more slots take further row passes
@@ -1417,13 +1412,28 @@ static int moe_row_blocks(int64_t R, int64_t E, int64_t K) {
   return K / kGroup == 112 && mr > 2 ? 2 : mr;
 }
 
+// The grouped decode kernel streams each busy expert's weights once per row
+// pass, the tiled kernel once per 256-row tile but with its MFMA tiles mostly
+// empty at a few hundred slots per expert: the decode kernel serves every
+// T <= 64 and, up to T = 1024, routings whose mean expert needs at most four
+// passes (measured crossover at the Mixtral shapes), while its worst-case grid
+// (every expert with T slots; passes without slots exit at once) stays small.
+static bool moe_decode_path(int64_t T, int64_t R, int64_t E, int64_t K) {
+  const int64_t G = K / kGroup;
+  if (!(G == 16 || G == 32 || G == 112)) return false;
+  if (T <= 64) return true;
+  const int64_t rows = 16 * moe_row_blocks(R, E, K);
+  const int64_t mean = (R + E - 1) / E;
+  return T <= 1024 && (mean + rows - 1) / rows <= 4 && E * ((T + rows - 1) / rows) <= 2048;
+}
+
 template <typename ST>
 static void launch_moe_t(const int8_t* qx, const float* sx, const uint8_t* packed,
                          const ST* iscale, float inv_alpha, int N, int K, const Route& rt,
                          OutY y, int32_t* acc_out, hipStream_t stream) {
   const uint4* pk = reinterpret_cast<const uint4*>(packed);
   const int G = K / kGroup;
-  if (moe_decode_path(rt.T, K)) {
+  if (moe_decode_path(rt.T, rt.R, rt.E, K)) {
     // every expert has at most T slots (a token reaches an expert once)
     const int mr = moe_row_blocks(rt.R, rt.E, K);
     const int passes = (rt.T + 16 * mr - 1) / (16 * mr);
@@ -1484,8 +1494,9 @@ hipError_t launch_w4a8_moe(const int8_t* qx, const float* sx, int64_t T, const i
   return hipGetLastError();
 }
 
-const char* w4a8_moe_kernel_name(int64_t T, int64_t K) {
-  return moe_decode_path(T, K) ? "k_w4a8_decode<IS,grouped>" : "k_w4a8_prefill<4,2,2,2,IS,grouped>";
+const char* w4a8_moe_kernel_name(int64_t T, int64_t E, int64_t R, int64_t K) {
+  return moe_decode_path(T, R, E, K) ? "k_w4a8_decode<IS,grouped>"
+                                     : "k_w4a8_prefill<4,2,2,2,IS,grouped>";
 }
 
 hipError_t launch_w8a8_zp(const uint8_t* qx, const float* sx, const int32_t* zx,

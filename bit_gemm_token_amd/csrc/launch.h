@@ -56,7 +56,7 @@ hipError_t launch_w4a8_moe(const int8_t* qx, const float* sx, int64_t T, const i
                            const int32_t* tok, int64_t E, int64_t R, const uint8_t* packed,
                            const void* iscale, int iscale_bytes, int alpha, int64_t N, int64_t K,
                            OutY y, int32_t* acc_out, hipStream_t stream);
-const char* w4a8_moe_kernel_name(int64_t T, int64_t K);
+const char* w4a8_moe_kernel_name(int64_t T, int64_t E, int64_t R, int64_t K);
 
 // fine-grained W8A8 with the integer-scale epilogue; qw in the int8 fragment
 // layout of bgt_pack_weights_int8, iscale of iscale_bytes bytes per element

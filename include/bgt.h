@@ -279,9 +279,14 @@ int bgt_w8a8_gemm_zp(const uint8_t* qx, const float* sx, const int32_t* zx,
  * Routing outside these rules cannot make the kernels read or write outside
  * the buffers (offsets are clamped to [0, R], tokens to [0, T), at most T
  * rows per expert, rounded up to a multiple of 16, are computed on the
- * T <= 64 path), but gives unspecified rows of y. Requirements: 1 <= T <= 65536, N and K as bgt_w4a8_gemm_is,
- * 1 <= E <= 256, 1 <= R <= min(T*E, 2^24); qx, packed, iscale, y, acc_out
- * 16-byte aligned. Experts without slots read no weights on the T <= 64 path.
+ * grouped decode path), but gives unspecified rows of y. Requirements:
+ * 1 <= T <= 65536, N and K as bgt_w4a8_gemm_is, 1 <= E <= 256,
+ * 1 <= R <= min(T*E, 2^24); qx, packed, iscale, y, acc_out 16-byte aligned.
+ * Kernels: with K/128 in {16, 32, 112}, a weight-streaming grouped decode
+ * kernel for T <= 64 and, up to T = 1024, whenever the mean expert (R/E
+ * slots) fits four row passes of 64 slots (32 at K/128 = 112); experts
+ * without slots read no weights there. Otherwise one tiled launch over the
+ * experts' 256-row tiles.
  */
 int bgt_w4a8_moe_gemm_is(const int8_t* qx, const float* sx, int64_t T,
                          const int32_t* expert_offsets, const int32_t* slot_token, int64_t E,
@@ -289,8 +294,9 @@ int bgt_w4a8_moe_gemm_is(const int8_t* qx, const float* sx, int64_t T,
                          int alpha, int64_t N, int64_t K, void* y, int y_type, int32_t* acc_out,
                          void* stream);
 
-/* Diagnostics: name of the kernel bgt_w4a8_moe_gemm_is launches for T tokens. */
-const char* bgt_w4a8_moe_kernel_name(int64_t T, int64_t K);
+/* Diagnostics: name of the kernel bgt_w4a8_moe_gemm_is launches for T tokens,
+ * E experts and R slots ("invalid shape" outside the entry point's limits). */
+const char* bgt_w4a8_moe_kernel_name(int64_t T, int64_t E, int64_t R, int64_t K);
 
 /*
  * bgt_pack_weights_int8 -- offline group-wise int8 weight quantization for the
@@ -352,7 +358,8 @@ const char* bgt_status_string(int status);
 /* ABI version of this header (major*100 + minor): 101 adds the narrow
  * integer-scale entry points, 102 the fused linear layer, 103 fp16 / bf16
  * activation and output types, 104 the fine-grained W8A8 integer-scale GEMM,
- * 105 the grouped (mixture-of-experts) W4A8 integer-scale GEMM. */
+ * 105 the grouped (mixture-of-experts) W4A8 integer-scale GEMM, 106 the
+ * expert count and slot count in bgt_w4a8_moe_kernel_name. */
 int bgt_abi_version(void);
 
 /* Diagnostics: name of the GEMM kernel that bgt_w4a8_gemm_is (float_scale = 0)

@@ -37,7 +37,7 @@ def test_status_strings(L):
     assert bgt.status_string(0) == "ok"
     for st in (-1, -2, -3, -4, -5, -6, -7, 1):
         assert "error" in bgt.status_string(st) or "warning" in bgt.status_string(st)
-    assert L.bgt_abi_version() == 105
+    assert L.bgt_abi_version() == 106
 
 
 def test_quantize_act_validation(L):
@@ -260,9 +260,17 @@ def test_moe_validation(L):
     assert call(isc=MIS) == bgt.BGT_ERR_ALIGN
     assert call(y=MIS) == bgt.BGT_ERR_ALIGN
     assert call(acc=MIS) == bgt.BGT_ERR_ALIGN
-    assert bgt.w4a8_moe_kernel_name(16, 4096) == "k_w4a8_decode<IS,grouped>"
-    assert bgt.w4a8_moe_kernel_name(64, 14336) == "k_w4a8_decode<IS,grouped>"
-    assert bgt.w4a8_moe_kernel_name(65, 14336) == "k_w4a8_prefill<4,2,2,2,IS,grouped>"
-    assert bgt.w4a8_moe_kernel_name(16, 1152) == "k_w4a8_prefill<4,2,2,2,IS,grouped>"
-    assert bgt.w4a8_moe_kernel_name(65, 4096) == "k_w4a8_prefill<4,2,2,2,IS,grouped>"
+    dec, til = "k_w4a8_decode<IS,grouped>", "k_w4a8_prefill<4,2,2,2,IS,grouped>"
+    name = bgt.w4a8_moe_kernel_name                 # (T, E, R, K)
+    assert name(16, 8, 32, 4096) == dec
+    assert name(64, 8, 128, 14336) == dec
+    assert name(16, 8, 32, 1152) == til                 # 9 groups: no decode kernel
+    # Mixtral-8x7B top-2: four row passes of 64 slots (w1, 32 groups) or 32 (w2,
+    # 112 groups) for the mean expert, T <= 1024
+    assert name(512, 8, 1024, 4096) == dec and name(1024, 8, 2048, 4096) == dec
+    assert name(512, 8, 1024, 14336) == dec and name(1024, 8, 2048, 14336) == til
+    assert name(1025, 8, 2050, 4096) == til and name(2048, 8, 4096, 4096) == til
+    assert name(1024, 256, 2048, 4096) == til           # worst-case grid too large
+    assert name(0, 8, 1, 4096) == "invalid shape" and name(4, 8, 33, 4096) == "invalid shape"
+    assert name(4, 0, 1, 4096) == "invalid shape" and name(4, 8, 8, 4100) == "invalid shape"
 

@@ -135,7 +135,7 @@ def test_moe_token_offsets_past_2_31(bgt, orc, dev, big_x):
     T, K, bq, bs, qx, sx = big_x
     E, N = 2, 32
     offs, tok = synth.route_by_expert(synth.moe_routing(75, T, E, 1), E)
-    say(f"w4a8_moe_gemm_is T={T} E={E} R={len(tok)} K={K} N={N} kernel={bgt.w4a8_moe_kernel_name(T, K)}")
+    say(f"w4a8_moe_gemm_is T={T} E={E} R={len(tok)} K={K} N={N} kernel={bgt.w4a8_moe_kernel_name(T, E, len(tok), K)}")
     ws = synth.expert_weights(75, E, K, N)
     ows = [orc.pack_weights(ws[e], 128, ALPHA) for e in range(E)]
     pws = [bgt.pack_weights_int4(torch.from_numpy(ws[e]).to(dev), alpha=ALPHA) for e in range(E)]

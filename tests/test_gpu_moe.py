@@ -93,25 +93,40 @@ def _run(bgt, orc, dev, T, E, K, N, seed, routing=None, width=4, out_dtype=None,
     return offs
 
 
+DECODE = "k_w4a8_decode<IS,grouped>"
+TILED = "k_w4a8_prefill<4,2,2,2,IS,grouped>"
+
+
 @pytest.mark.parametrize("T,E,K,N", [(1, 8, 4096, 64), (5, 8, 4096, 208), (16, 8, 2048, 96),
                                      (33, 8, 4096, 48), (64, 8, 2048, 16), (20, 3, 4096, 80),
                                      (1, 8, 14336, 48), (12, 8, 14336, 80), (32, 5, 14336, 32),
-                                     (64, 8, 14336, 48), (50, 2, 2048, 32)])
+                                     (64, 8, 14336, 48), (50, 2, 2048, 32),
+                                     # more tokens, up to four row passes per mean expert
+                                     (128, 8, 4096, 64), (300, 8, 2048, 48), (520, 8, 4096, 32),
+                                     (1000, 8, 4096, 16), (200, 8, 14336, 32), (300, 6, 14336, 16)])
 def test_moe_decode_path(bgt, orc, dev, T, E, K, N):
-    say(f"moe {bgt.w4a8_moe_kernel_name(T, K)} T={T} E={E} K={K} N={N}")
+    name = bgt.w4a8_moe_kernel_name(T, E, T * min(2, E), K)
+    say(f"moe {name} T={T} E={E} K={K} N={N}")
+    assert name == DECODE
     offs = _run(bgt, orc, dev, T, E, K, N, seed=T * 31 + K + N)
     if T == 1:
         assert (np.diff(offs) > 0).sum() == 2             # six experts read nothing
 
 
 @pytest.mark.parametrize("T,E,K,N", [(65, 8, 512, 144), (300, 8, 256, 48), (20, 8, 1152, 64),
-                                     (130, 4, 640, 400), (257, 8, 128, 16)])
+                                     (130, 4, 640, 400), (257, 8, 128, 16),
+                                     # past the decode kernel's range: T > 1024, or more than
+                                     # four row passes for the mean expert
+                                     (1100, 8, 4096, 16), (600, 8, 14336, 16), (700, 2, 2048, 32)])
 def test_moe_tiled_path(bgt, orc, dev, T, E, K, N):
-    say(f"moe {bgt.w4a8_moe_kernel_name(T, K)} T={T} E={E} K={K} N={N}")
+    name = bgt.w4a8_moe_kernel_name(T, E, T * min(2, E), K)
+    say(f"moe {name} T={T} E={E} K={K} N={N}")
+    assert name == TILED
     _run(bgt, orc, dev, T, E, K, N, seed=T * 37 + K + N)
 
 
-@pytest.mark.parametrize("T,K", [(64, 4096), (200, 512), (64, 14336), (40, 2048)])
+@pytest.mark.parametrize("T,K", [(64, 4096), (200, 512), (64, 14336), (40, 2048), (300, 4096),
+                                 (200, 14336)])
 def test_moe_all_tokens_one_expert(bgt, orc, dev, T, K):
     # maximal imbalance: expert 5 takes every token, expert 2 one, the rest none
     # (on the decode path the busy expert takes several row passes)
@@ -136,11 +151,11 @@ def test_moe_half_outputs(bgt, orc, dev, T, K):
 
 
 @pytest.mark.parametrize("T,K,N", [(16, 4096, 14336), (64, 4096, 14336), (512, 4096, 14336),
-                                   (16, 14336, 4096), (64, 14336, 4096)])
+                                   (16, 14336, 4096), (64, 14336, 4096), (512, 14336, 4096)])
 def test_moe_mixtral_shapes_sampled(bgt, orc, dev, T, K, N):
     """Mixtral-8x7B experts (8, top-2) at the w1/w3 and w2 shapes, in the
     launches the bench times; sampled output columns against the oracle."""
-    say(f"moe mixtral {bgt.w4a8_moe_kernel_name(T, K)} T={T} K={K} N={N} (sampled)")
+    say(f"moe mixtral {bgt.w4a8_moe_kernel_name(T, 8, 2 * T, K)} T={T} K={K} N={N} (sampled)")
     cols = np.unique(np.concatenate([np.arange(0, 32), np.arange(N - 32, N),
                                      np.random.default_rng(T).choice(N, 160, replace=False)]))
     _run(bgt, orc, dev, T, 8, K, N, seed=T + 21, cols=cols)

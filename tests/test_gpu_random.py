@@ -158,7 +158,7 @@ def test_random_moe(bgt, orc, dev, case):
     routing = synth.moe_routing(11000 + case, T, E, topk)
     offs, tok = synth.route_by_expert(routing, E)
     say(f"random moe #{case}: T={T} E={E} topk={topk} K={K} N={N} y={kind} "
-        f"kernel={bgt.w4a8_moe_kernel_name(T, K)}")
+        f"kernel={bgt.w4a8_moe_kernel_name(T, E, len(tok), K)}")
     x = synth.activations(12000 + case, T, K)
     w = synth.expert_weights(13000 + case, E, K, N)
     oq, os_ = orc.quant_sym_i8(x)
