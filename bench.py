@@ -76,26 +76,26 @@ METRIC = "W4A8 integer-scale GEMM TOPS + HBM GB/s, K=4096 N=22016, M=1..4096"
 # profiles/*hbm_bytes.txt), keyed by (kernel, M). They hold only for the
 # kernel sources they were taken on: when a source file differs from the one
 # measured (sha256 prefix below), traffic is reported as null.
-TRAFFIC_SRC_SHA = {"gemm.hip": "6b5659509327c549", "gemm_w8is.hip": "e4fcff966f541e75"}
+TRAFFIC_SRC_SHA = {"gemm.hip": "f40c40e390163263", "gemm_w8is.hip": "e4fcff966f541e75"}
 TRAFFIC_SRC = {"k_w4a8_decode<IS>": "gemm.hip", "k_w4a8_prefill<4,2,2,2,IS>": "gemm.hip",
                "k_w8a8_zp<9,32>": "gemm.hip", "k_w4a8_decode<IS,grouped>": "gemm.hip",
                "k_w8is_split": "gemm_w8is.hip"}
 TRAFFIC = {
-    ("k_w4a8_decode<IS>", 1): 48170463,
-    ("k_w4a8_decode<IS>", 4): 48538068,
-    ("k_w4a8_decode<IS>", 16): 49987928,
-    ("k_w4a8_decode<IS>", 64): 55878024,
-    ("k_w4a8_prefill<4,2,2,2,IS>", 256): 79307564,
-    ("k_w4a8_prefill<4,2,2,2,IS>", 4096): 922399501,
-    ("k_w8a8_zp<9,32>", 256): 29667094,
-    ("k_w8is_split", 1): 62579757,
-    ("k_w8is_split", 4): 62973003,
-    ("k_w8is_split", 16): 64545666,
-    ("k_w8is_split", 64): 70844597,
-    ("k_w4a8_decode<IS,grouped>", 1): 62687383,
-    ("k_w4a8_decode<IS,grouped>", 4): 125517996,
-    ("k_w4a8_decode<IS,grouped>", 16): 189674116,
-    ("k_w4a8_decode<IS,grouped>", 64): 259161082,
+    ("k_w4a8_decode<IS>", 1): 48170363,
+    ("k_w4a8_decode<IS>", 4): 48537926,
+    ("k_w4a8_decode<IS>", 16): 49987998,
+    ("k_w4a8_decode<IS>", 64): 55877793,
+    ("k_w4a8_prefill<4,2,2,2,IS>", 256): 79307362,
+    ("k_w4a8_prefill<4,2,2,2,IS>", 4096): 922293796,
+    ("k_w8a8_zp<9,32>", 256): 29667044,
+    ("k_w8is_split", 1): 62579649,
+    ("k_w8is_split", 4): 62972745,
+    ("k_w8is_split", 16): 64545406,
+    ("k_w8is_split", 64): 70844453,
+    ("k_w4a8_decode<IS,grouped>", 1): 62687595,
+    ("k_w4a8_decode<IS,grouped>", 4): 125517673,
+    ("k_w4a8_decode<IS,grouped>", 16): 189674122,
+    ("k_w4a8_decode<IS,grouped>", 64): 259161746,
 }
 
 
