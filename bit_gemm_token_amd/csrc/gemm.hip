@@ -859,13 +859,13 @@ __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
   constexpr int CG = decode_chunk_groups(G, MR, D);  // groups per X chunk (<= 64 KiB)
   constexpr int NCH = G / CG;                        // chunks
   constexpr int CFR = CG * MR * 2;                   // 1 KiB fragments per chunk
-  constexpr int FPW = CFR / W;                       // fragments per wave per chunk
+  constexpr int FPW = (CFR + W - 1) / W;             // fragments per wave per chunk (the last may be short)
   using SL = typename std::conditional<FS, int32_t, ST>::type;   // scale element as stored
   constexpr int SCW = W * 16;                        // scale columns of the workgroup
   constexpr int SEL = 16 / sizeof(SL);               // scale elements per 16-byte chunk
   constexpr int SCT = G * SCW / SEL;                 // 16-byte scale chunks of the workgroup
   constexpr int SCH = (SCT + W * 64 - 1) / (W * 64); // ... per thread
-  static_assert(G % D == 0 && G % CG == 0 && CFR % W == 0, "shape of the pipeline");
+  static_assert(G % D == 0 && G % CG == 0, "shape of the pipeline");
   static_assert(SCW % SEL == 0, "scale staging");
   static_assert(!FQ || (MR == 1 && NCH == 1 && !FS), "fused quantization: one row block, one chunk");
   static_assert(!(GR && FQ), "grouped GEMM takes quantized activations");
@@ -908,7 +908,7 @@ __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
     for (int i = 0; i < FPW; ++i) {
       const int f = wave + W * i, rb = (f / 2) % MR;
       const int row = 16 * rb + c < M ? 16 * rb + c : M - 1;
-      xo[i] = clamp_route(rt.tok[r0 + row], 0, rt.T - 1) * K;
+      xo[i] = (CFR % W == 0 || f < CFR) ? clamp_route(rt.tok[r0 + row], 0, rt.T - 1) * K : 0;
     }
   }
   v4i xa[FPW];
@@ -918,13 +918,15 @@ __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
       const int f = wave + W * i, gl = f / (2 * MR), rb = (f / 2) % MR, h = f % 2;
       const int row = 16 * rb + c < M ? 16 * rb + c : M - 1;
       const int ro = GR ? xo[GR ? i : 0] : row * K;
-      xa[i] = load_v4i(qx + (ro + 128 * (ch * CG + gl) + 64 * h + 16 * s4));
+      if (CFR % W == 0 || f < CFR)                   // wave-uniform
+        xa[i] = load_v4i(qx + (ro + 128 * (ch * CG + gl) + 64 * h + 16 * s4));
     }
   };
   auto store_chunk = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < FPW; ++i)
-      *reinterpret_cast<v4i*>(sA + (buf * CFR + wave + W * i) * 1024 + lane * 16) = xa[i];
+      if (CFR % W == 0 || wave + W * i < CFR)
+        *reinterpret_cast<v4i*>(sA + (buf * CFR + wave + W * i) * 1024 + lane * 16) = xa[i];
   };
   // fused quantization (FQ, M <= 4): the rows (element type IT, widened to
   // fp32), each thread XV groups of 4 of every row, requested before the
@@ -986,7 +988,8 @@ __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
     // rows M..15 of the fragment block are zero codes
 #pragma unroll
     for (int i = 0; i < FPW; ++i)
-      if (c >= M) *reinterpret_cast<v4i*>(sA + (wave + W * i) * 1024 + lane * 16) = v4i{0, 0, 0, 0};
+      if (c >= M && (CFR % W == 0 || wave + W * i < CFR))
+        *reinterpret_cast<v4i*>(sA + (wave + W * i) * 1024 + lane * 16) = v4i{0, 0, 0, 0};
     wait_lds0();
     lds_barrier();
     // codes of one float4: MODE 0 all zero (s = 0), 1 corrected product, 2 division
@@ -1191,7 +1194,10 @@ struct W4Plan { W4Path path; int mr; };
 // (decode kernel when K is a multiple of 16 groups and the X block fits LDS;
 // else the stream kernel while its loader waves and exchange area fit a
 // workgroup; else the skinny kernel); larger M takes the LDS-tiled MFMA kernel.
-constexpr int kDecodeW = 8;                        // waves (tiles) per decode workgroup
+constexpr int kDecodeW = 8;                        // waves (tiles) per decode workgroup (fused, grouped)
+// dense decode: waves per workgroup from the tile count T = N/16, so that the
+// T/W workgroups (one per CU, each streaming W tiles) spread over the 256 CUs
+constexpr int decode_waves(int T) { return T <= 1024 ? 4 : (T <= 1536 ? 6 : 8); }
 // group blocks in flight per wave: fewer when each wave also holds several row blocks
 constexpr int decode_depth(int mr) { return mr == 1 ? 16 : 8; }
 
@@ -1268,23 +1274,34 @@ const char* w4a8_kernel_name(int64_t M, int64_t K, bool float_scale) {
   return names[fs][p.path == W4Path::Stream ? 0 : 1][p.mr - 1];
 }
 
-template <bool FS, int G, typename ST>
-static void launch_decode(int mr, dim3 grid, dim3 block, hipStream_t stream, const int8_t* qx,
-                          const float* sx, const uint4* pk, const ST* iscale,
-                          const float* fscale, float inv_alpha, int M, int N, OutY y,
-                          int32_t* acc_out) {
+template <bool FS, int G, int W, typename ST>
+static void launch_decode_w(int mr, hipStream_t stream, const int8_t* qx, const float* sx,
+                            const uint4* pk, const ST* iscale, const float* fscale,
+                            float inv_alpha, int M, int N, OutY y, int32_t* acc_out) {
   const void* nx = nullptr;
   int8_t* nq = nullptr;
   float* ns = nullptr;
+  const dim3 grid((N / 16 + W - 1) / W), block(W * kWave);
   switch (mr) {
-    case 1: hipLaunchKernelGGL((k_w4a8_decode<FS, kDecodeW, decode_depth(1), G, 1, ST, false, kF32>), grid, block, 0, stream,
+    case 1: hipLaunchKernelGGL((k_w4a8_decode<FS, W, decode_depth(1), G, 1, ST, false, kF32>), grid, block, 0, stream,
                                qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out, nx, 0, nq, ns, Route{}); break;
-    case 2: hipLaunchKernelGGL((k_w4a8_decode<FS, kDecodeW, decode_depth(2), G, 2, ST, false, kF32>), grid, block, 0, stream,
+    case 2: hipLaunchKernelGGL((k_w4a8_decode<FS, W, decode_depth(2), G, 2, ST, false, kF32>), grid, block, 0, stream,
                                qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out, nx, 0, nq, ns, Route{}); break;
-    case 3: hipLaunchKernelGGL((k_w4a8_decode<FS, kDecodeW, decode_depth(3), G, 3, ST, false, kF32>), grid, block, 0, stream,
+    case 3: hipLaunchKernelGGL((k_w4a8_decode<FS, W, decode_depth(3), G, 3, ST, false, kF32>), grid, block, 0, stream,
                                qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out, nx, 0, nq, ns, Route{}); break;
-    default: hipLaunchKernelGGL((k_w4a8_decode<FS, kDecodeW, decode_depth(4), G, 4, ST, false, kF32>), grid, block, 0, stream,
+    default: hipLaunchKernelGGL((k_w4a8_decode<FS, W, decode_depth(4), G, 4, ST, false, kF32>), grid, block, 0, stream,
                                 qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out, nx, 0, nq, ns, Route{}); break;
+  }
+}
+
+template <bool FS, int G, typename ST>
+static void launch_decode(int mr, hipStream_t stream, const int8_t* qx, const float* sx,
+                          const uint4* pk, const ST* iscale, const float* fscale, float inv_alpha,
+                          int M, int N, OutY y, int32_t* acc_out) {
+  switch (decode_waves(N / 16)) {
+    case 4: launch_decode_w<FS, G, 4>(mr, stream, qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out); break;
+    case 6: launch_decode_w<FS, G, 6>(mr, stream, qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out); break;
+    default: launch_decode_w<FS, G, 8>(mr, stream, qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out); break;
   }
 }
 
@@ -1296,13 +1313,11 @@ static void launch_w4a8_t(const int8_t* qx, const float* sx, const uint8_t* pack
   if (FS) acc_out = nullptr;
   if (plan.path == W4Path::Decode) {
     // one 16-column tile per wave, all rows per workgroup
-    const int T = N / 16;
-    const dim3 grid((T + kDecodeW - 1) / kDecodeW), block(kDecodeW * kWave);
     const uint4* pk = reinterpret_cast<const uint4*>(packed);
     if (K / kGroup == 32)
-      launch_decode<FS, 32>(plan.mr, grid, block, stream, qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out);
+      launch_decode<FS, 32>(plan.mr, stream, qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out);
     else
-      launch_decode<FS, 16>(plan.mr, grid, block, stream, qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out);
+      launch_decode<FS, 16>(plan.mr, stream, qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out);
   } else if (plan.path != W4Path::Tiled) {
     launch_small_m<FS>(plan, qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream);
   } else {
