@@ -825,12 +825,14 @@ __global__ __launch_bounds__(NW * 64) void k_w8a8_zp(
 
 // =====================================================================
 // Decode kernel (M <= 64, weight streaming): one wave owns one 16-column tile
-// for all K and all MR 16-row blocks of X, so no partial sums cross waves.
+// for all K and all MR 16-row blocks of X, so no partial sums cross waves; a
+// workgroup of W waves serves W consecutive tiles.
 //   X: the workgroup stages X (16*MR rows, clamped past M) in LDS in MFMA
 //      fragment order, one K chunk of CG groups (at most 64 KiB) at a time,
 //      double-buffered: fragment (g, rb, h) of a chunk = 1 KiB where lane L
 //      holds row 16rb + L%16, k = 128g + 64h + 16(L/16) .. +15. The next
-//      chunk's rows are loaded into registers under the current chunk's work.
+//      chunk's rows are loaded into registers under the current chunk's work;
+//      the chunk's fragments are dealt round-robin to the W waves.
 //   W: each wave keeps D packed 1 KiB group blocks of its tile (16 bytes per
 //      lane, non-temporal) and their D scales in flight, refilling one slot
 //      per group; unpack by nibble-to-high-half (codes enter as 16*q), two
@@ -1412,10 +1414,10 @@ hipError_t launch_w4a8_linear(const void* x, int x_type, int64_t ldx, const uint
   return hipGetLastError();
 }
 
-// Grouped (mixture-of-experts) integer-scale GEMM: few tokens (T <= 64) with
-// K/128 in {16, 32} (the expert w1/w3 shapes) or 112 (Mixtral's w2) take the
-// decode kernel with one workgroup row per expert and row pass; otherwise the
-// tiled kernel over the experts' row tiles.
+// Grouped (mixture-of-experts) integer-scale GEMM: with K/128 in {16, 32}
+// (the expert w1/w3 shapes) or 112 (Mixtral's w2), routings within the rule
+// of moe_decode_path take the decode kernel with one workgroup row per expert
+// and row pass; otherwise the tiled kernel over the experts' row tiles.
 // Row blocks per workgroup of the grouped decode kernel: enough for 1.5x the
 // mean slots per expert (at most 4; at most 2 for 112 groups, whose scales
 // leave LDS room for two); experts with more slots take further row passes
