@@ -170,7 +170,10 @@ SHAPES = [(1, 128, 16), (3, 384, 48), (16, 1024, 144), (17, 512, 64), (33, 256, 
           # K of 16 or 32 groups with M <= 64: the one-wave-per-tile kernel (ragged rows,
           # row blocks, tile sets with idle waves)
           (1, 2048, 64), (5, 4096, 48), (17, 2048, 96), (33, 4096, 80), (40, 4096, 16),
-          (64, 2048, 160)]
+          (64, 2048, 160),
+          # the same kernel with 6 and 8 waves per workgroup (N/16 > 1024 and > 1536 tiles;
+          # the last workgroup partly past N)
+          (3, 4096, 16400), (20, 2048, 24576), (1, 4096, 24592), (50, 2048, 28672)]
 
 
 @pytest.mark.parametrize("M,K,N", SHAPES)
