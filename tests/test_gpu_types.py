@@ -101,7 +101,8 @@ def _w4_case(orc, seed, M, K, N):
 
 
 @pytest.mark.parametrize("kind", ["f16", "bf16"])
-@pytest.mark.parametrize("M,K,N", [(1, 4096, 272), (17, 2048, 96), (3, 384, 48), (300, 512, 208)])
+@pytest.mark.parametrize("M,K,N", [(1, 4096, 272), (17, 2048, 96), (3, 384, 48), (300, 512, 208),
+                                   (2, 2048, 24592)])
 def test_gemm_is_half_outputs(bgt, orc, dev, kind, M, K, N):
     say(f"w4a8_gemm_is y={kind} M={M} K={K} N={N}")
     oq, os_, ow = _w4_case(orc, 7 * M + K + N, M, K, N)
