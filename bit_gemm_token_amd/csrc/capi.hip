@@ -52,7 +52,7 @@ int bgt_w4a8_linear_fused(int64_t M, int64_t K, const void* x, int64_t ldx) {
 
 const char* bgt_w4a8_kernel_name(int64_t M, int64_t N, int64_t K, int float_scale) {
   if (check_gemm_shape(M, N, K, 65536) != BGT_OK) return "invalid shape";
-  return bgt::w4a8_kernel_name(M, K, float_scale != 0);
+  return bgt::w4a8_kernel_name(M, N, K, float_scale != 0);
 }
 
 const char* bgt_status_string(int status) {

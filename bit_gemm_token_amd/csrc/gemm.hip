@@ -842,15 +842,17 @@ __global__ __launch_bounds__(NW * 64) void k_w8a8_zp(
 // Every load is a register load, so the compiler's wait counts stay exact.
 // =====================================================================
 // groups per staged X chunk: the largest divisor of G up to 32 (one row
-// block) or 8 (more), so a chunk is at most 64 KiB, that is a multiple of the
-// weight ring depth D
-constexpr int decode_chunk_groups(int G, int MR, int D) {
-  int c = MR == 1 ? 32 : 8;
+// block; 16 on 2-wave workgroups, so a wave stages at most 16 fragments) or 8
+// (more), so a chunk is at most 64 KiB, that is a multiple of the weight ring
+// depth D
+constexpr int decode_chunk_groups(int G, int MR, int D, int W) {
+  int c = MR == 1 ? (W >= 4 ? 32 : 16) : 8;
   while (c > D && (G % c != 0 || c % D != 0)) --c;
   return c;
 }
 
-template <bool FS, int W, int D, int G, int MR, typename ST, bool FQ, int IT, bool GR = false>
+template <bool FS, int W, int D, int G, int MR, typename ST, bool FQ, int IT, bool GR = false,
+          int GQ = G>
 __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
     const int8_t* __restrict__ qx, const float* __restrict__ sx,
     const uint4* __restrict__ packed, const ST* __restrict__ iscale,
@@ -858,7 +860,7 @@ __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
     OutY y, int32_t* __restrict__ acc_out,
     const void* __restrict__ xf, int ldx, int8_t* __restrict__ q_out, float* __restrict__ s_out,
     Route rt) {
-  constexpr int CG = decode_chunk_groups(G, MR, D);  // groups per X chunk (<= 64 KiB)
+  constexpr int CG = decode_chunk_groups(G, MR, D, W);  // groups per X chunk (<= 64 KiB)
   constexpr int NCH = G / CG;                        // chunks
   constexpr int CFR = CG * MR * 2;                   // 1 KiB fragments per chunk
   constexpr int FPW = (CFR + W - 1) / W;             // fragments per wave per chunk (the last may be short)
@@ -875,7 +877,12 @@ __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
   __shared__ __align__(16) int8_t sA[NBUF * CFR * 1024];
   __shared__ __align__(16) SL sS[G * SCW];           // [group][column of the workgroup]
   __shared__ float sX[16 * MR];                      // token scales
-  constexpr int K = G * kGroup;
+  // G groups in the pipeline; the last G - GQ are padding (K = 128 GQ): their
+  // loads repeat group GQ-1 and their staged scales are zero, so they add
+  // exactly nothing (0 * p in the integer epilogue, fma(p, +0, acc) = acc)
+  static_assert(GQ <= G && (GQ == G || (!FQ && !GR)), "padded groups: dense launches only");
+  constexpr int K = GQ * kGroup;
+  auto gq = [](int g) { return GQ == G || g < GQ ? g : GQ - 1; };
   const int T = N / 16;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
@@ -921,7 +928,7 @@ __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
       const int row = 16 * rb + c < M ? 16 * rb + c : M - 1;
       const int ro = GR ? xo[GR ? i : 0] : row * K;
       if (CFR % W == 0 || f < CFR)                   // wave-uniform
-        xa[i] = load_v4i(qx + (ro + 128 * (ch * CG + gl) + 64 * h + 16 * s4));
+        xa[i] = load_v4i(qx + (ro + 128 * gq(ch * CG + gl) + 64 * h + 16 * s4));
     }
   };
   auto store_chunk = [&](int buf) {
@@ -954,14 +961,16 @@ __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
   for (int u = 0; u < SCH; ++u) {
     const int q = threadIdx.x + W * 64 * u, g = q / (SCW / SEL), c0 = (q % (SCW / SEL)) * SEL;
     const int col = blockIdx.x * SCW + c0 < N ? blockIdx.x * SCW + c0 : N - SEL;
-    if (SCT % (W * 64) == 0 || q < SCT)
+    if (GQ < G && g >= GQ)
+      sv[u] = v4i{0, 0, 0, 0};
+    else if (SCT % (W * 64) == 0 || q < SCT)
       sv[u] = load_v4i(reinterpret_cast<const int8_t*>(scl + ((int64_t)g * N + col)));
   }
   // ---- first D groups of the tile in flight
-  const uint4* wsrc = packed + (int64_t)tc * G * 64 + lane;
+  const uint4* wsrc = packed + (int64_t)tc * GQ * 64 + lane;
   uint4 wb[D];
 #pragma unroll
-  for (int j = 0; j < D; ++j) wb[j] = load_u4_nt(wsrc + (int64_t)j * 64);
+  for (int j = 0; j < D; ++j) wb[j] = load_u4_nt(wsrc + (int64_t)gq(j) * 64);
   if constexpr (FQ) {
     // ---- per-token quantization of the rows, as the quantizer computes it:
     // a = max|x|, s = a / 127, q = clamp(round(x / s), -127, 127) (s = 0 -> 0).
@@ -1103,7 +1112,7 @@ __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
     for (int gl = 0; gl < CG; ++gl) {
       const int g = ch * CG + gl;
       group(g, wb[gl % D]);
-      if (!LAST || gl + D < CG) wb[gl % D] = load_u4_nt(wsrc + (int64_t)(g + D) * 64);
+      if (!LAST || gl + D < CG) wb[gl % D] = load_u4_nt(wsrc + (int64_t)gq(g + D) * 64);
       __builtin_amdgcn_sched_barrier(0);             // keep each group's fragments short-lived
     }
     if (!LAST) {
@@ -1199,14 +1208,24 @@ struct W4Plan { W4Path path; int mr; };
 constexpr int kDecodeW = 8;                        // waves (tiles) per decode workgroup (fused, grouped)
 // dense decode: waves per workgroup from the tile count T = N/16, so that the
 // T/W workgroups (one per CU, each streaming W tiles) spread over the 256 CUs
-constexpr int decode_waves(int T) { return T <= 1024 ? 4 : (T <= 1536 ? 6 : 8); }
+// (2-wave workgroups for one row block only: more would not fit the registers)
+constexpr int decode_waves(int T, int mr) {
+  return T <= 512 && mr == 1 ? 2 : (T <= 1024 ? 4 : (T <= 1536 ? 6 : 8));
+}
 // group blocks in flight per wave: fewer when each wave also holds several row blocks
 constexpr int decode_depth(int mr) { return mr == 1 ? 16 : 8; }
 
-static W4Plan plan_w4a8(int M, int K, bool fs) {
+// K = 11008 (86 groups, run as 96 with the last ten masked) and K = 14336 (112)
+// take the decode kernel for one row block on 2- or 4-wave workgroups, whose
+// LDS holds their scales (with more row blocks the weight-split kernels win)
+static bool decode_padded(int G, int N, int mr) {
+  return (G == 86 || G == 112) && mr == 1 && decode_waves(N / 16, mr) <= 4;
+}
+
+static W4Plan plan_w4a8(int M, int N, int K, bool fs) {
   if (M > 64) return {W4Path::Tiled, 0};
   const int mr = (M + 15) / 16, G = K / kGroup;
-  if (G == 16 || G == 32) return {W4Path::Decode, mr};
+  if (G == 16 || G == 32 || decode_padded(G, N, mr)) return {W4Path::Decode, mr};
   int gpw = 0, maxt = 0;
   switch (mr) {
     case 1: gpw = StreamCfg<1>::GPW; maxt = StreamCfg<1>::MAXT; break;
@@ -1261,7 +1280,7 @@ static void launch_small_m(const W4Plan& plan, const int8_t* qx, const float* sx
   }
 }
 
-const char* w4a8_kernel_name(int64_t M, int64_t K, bool float_scale) {
+const char* w4a8_kernel_name(int64_t M, int64_t N, int64_t K, bool float_scale) {
   static const char* names[2][3][4] = {
       {{"k_w4a8_stream<1,IS>", "k_w4a8_stream<2,IS>", "k_w4a8_stream<3,IS>", "k_w4a8_stream<4,IS>"},
        {"k_w4a8_skinny<1,4,IS>", "k_w4a8_skinny<2,4,IS>", "k_w4a8_skinny<3,4,IS>", "k_w4a8_skinny<4,4,IS>"},
@@ -1269,14 +1288,14 @@ const char* w4a8_kernel_name(int64_t M, int64_t K, bool float_scale) {
       {{"k_w4a8_stream<1,FS>", "k_w4a8_stream<2,FS>", "k_w4a8_stream<3,FS>", "k_w4a8_stream<4,FS>"},
        {"k_w4a8_skinny<1,1,FS>", "k_w4a8_skinny<2,1,FS>", "k_w4a8_skinny<3,1,FS>", "k_w4a8_skinny<4,1,FS>"},
        {"k_w4a8_prefill<4,2,2,2,FS>", "", "", ""}}};
-  const W4Plan p = plan_w4a8((int)M, (int)K, float_scale);
+  const W4Plan p = plan_w4a8((int)M, (int)N, (int)K, float_scale);
   const int fs = float_scale ? 1 : 0;
   if (p.path == W4Path::Tiled) return names[fs][2][0];
   if (p.path == W4Path::Decode) return float_scale ? "k_w4a8_decode<FS>" : "k_w4a8_decode<IS>";
   return names[fs][p.path == W4Path::Stream ? 0 : 1][p.mr - 1];
 }
 
-template <bool FS, int G, int W, typename ST>
+template <bool FS, int G, int GQ, int W, int MRMAX, typename ST>
 static void launch_decode_w(int mr, hipStream_t stream, const int8_t* qx, const float* sx,
                             const uint4* pk, const ST* iscale, const float* fscale,
                             float inv_alpha, int M, int N, OutY y, int32_t* acc_out) {
@@ -1284,26 +1303,39 @@ static void launch_decode_w(int mr, hipStream_t stream, const int8_t* qx, const 
   int8_t* nq = nullptr;
   float* ns = nullptr;
   const dim3 grid((N / 16 + W - 1) / W), block(W * kWave);
-  switch (mr) {
-    case 1: hipLaunchKernelGGL((k_w4a8_decode<FS, W, decode_depth(1), G, 1, ST, false, kF32>), grid, block, 0, stream,
-                               qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out, nx, 0, nq, ns, Route{}); break;
-    case 2: hipLaunchKernelGGL((k_w4a8_decode<FS, W, decode_depth(2), G, 2, ST, false, kF32>), grid, block, 0, stream,
-                               qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out, nx, 0, nq, ns, Route{}); break;
-    case 3: hipLaunchKernelGGL((k_w4a8_decode<FS, W, decode_depth(3), G, 3, ST, false, kF32>), grid, block, 0, stream,
-                               qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out, nx, 0, nq, ns, Route{}); break;
-    default: hipLaunchKernelGGL((k_w4a8_decode<FS, W, decode_depth(4), G, 4, ST, false, kF32>), grid, block, 0, stream,
-                                qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out, nx, 0, nq, ns, Route{}); break;
+#define BGT_DECODE(MRR)                                                                           \
+  hipLaunchKernelGGL((k_w4a8_decode<FS, W, decode_depth(MRR), G, MRR, ST, false, kF32, false, GQ>), \
+                     grid, block, 0, stream, qx, sx, pk, iscale, fscale, inv_alpha, M, N, y,        \
+                     acc_out, nx, 0, nq, ns, Route{})
+  if constexpr (MRMAX == 1) {
+    BGT_DECODE(1);
+  } else {
+    switch (mr) {
+      case 1: BGT_DECODE(1); break;
+      case 2: BGT_DECODE(2); break;
+      case 3: BGT_DECODE(3); break;
+      default: BGT_DECODE(4); break;
+    }
   }
+#undef BGT_DECODE
 }
 
-template <bool FS, int G, typename ST>
+template <bool FS, int G, int GQ, typename ST>
 static void launch_decode(int mr, hipStream_t stream, const int8_t* qx, const float* sx,
                           const uint4* pk, const ST* iscale, const float* fscale, float inv_alpha,
                           int M, int N, OutY y, int32_t* acc_out) {
-  switch (decode_waves(N / 16)) {
-    case 4: launch_decode_w<FS, G, 4>(mr, stream, qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out); break;
-    case 6: launch_decode_w<FS, G, 6>(mr, stream, qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out); break;
-    default: launch_decode_w<FS, G, 8>(mr, stream, qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out); break;
+  const int w = decode_waves(N / 16, mr);
+  if (w == 2) {
+    launch_decode_w<FS, G, GQ, 2, 1>(1, stream, qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out);
+  } else if constexpr (G > 32) {
+    // 96 or 112 groups: one row block on 4-wave workgroups (decode_padded)
+    launch_decode_w<FS, G, GQ, 4, 1>(1, stream, qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out);
+  } else {
+    switch (w) {
+      case 4: launch_decode_w<FS, G, GQ, 4, 4>(mr, stream, qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out); break;
+      case 6: launch_decode_w<FS, G, GQ, 6, 4>(mr, stream, qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out); break;
+      default: launch_decode_w<FS, G, GQ, 8, 4>(mr, stream, qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out); break;
+    }
   }
 }
 
@@ -1311,15 +1343,17 @@ template <bool FS, typename ST>
 static void launch_w4a8_t(const int8_t* qx, const float* sx, const uint8_t* packed,
                           const ST* iscale, const float* fscale, float inv_alpha, int M, int N,
                           int K, OutY y, int32_t* acc_out, hipStream_t stream) {
-  const W4Plan plan = plan_w4a8(M, K, FS);
+  const W4Plan plan = plan_w4a8(M, N, K, FS);
   if (FS) acc_out = nullptr;
   if (plan.path == W4Path::Decode) {
     // one 16-column tile per wave, all rows per workgroup
     const uint4* pk = reinterpret_cast<const uint4*>(packed);
-    if (K / kGroup == 32)
-      launch_decode<FS, 32>(plan.mr, stream, qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out);
-    else
-      launch_decode<FS, 16>(plan.mr, stream, qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out);
+    switch (K / kGroup) {
+      case 32: launch_decode<FS, 32, 32>(plan.mr, stream, qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out); break;
+      case 16: launch_decode<FS, 16, 16>(plan.mr, stream, qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out); break;
+      case 86: launch_decode<FS, 96, 86>(plan.mr, stream, qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out); break;
+      default: launch_decode<FS, 112, 112>(plan.mr, stream, qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out); break;
+    }
   } else if (plan.path != W4Path::Tiled) {
     launch_small_m<FS>(plan, qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream);
   } else {

@@ -47,7 +47,7 @@ hipError_t launch_narrow_scales(const int32_t* in, int64_t count, int out_bytes,
                                 hipStream_t stream);
 
 // name of the kernel a W4A8 GEMM of this shape dispatches to (diagnostics)
-const char* w4a8_kernel_name(int64_t M, int64_t K, bool float_scale);
+const char* w4a8_kernel_name(int64_t M, int64_t N, int64_t K, bool float_scale);
 
 // grouped (mixture-of-experts) W4A8 integer-scale GEMM: E experts' packed
 // weights and scales back to back; slots sorted by expert (offs: E+1 offsets,

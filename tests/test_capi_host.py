@@ -232,6 +232,17 @@ def test_w8a8_is_validation(L):
     assert bgt.w8a8_is_kernel_name(4, 4096, 14336) == "k_w8is_split"
     assert bgt.w8a8_is_kernel_name(65, 4096, 14336) == "k_w8is_tiled"
     assert bgt.w8a8_is_kernel_name(0, 4096, 14336) == "invalid shape"
+    # dense W4A8: the decode kernel for K of 16 or 32 groups, and for 86 / 112
+    # groups with one row block (M <= 16) where 2- or 4-wave workgroups apply
+    # (N/16 <= 1024 tiles)
+    w4 = bgt.w4a8_kernel_name                       # (M, N, K)
+    assert w4(16, 22016, 4096) == "k_w4a8_decode<IS>" and w4(64, 4096, 2048) == "k_w4a8_decode<IS>"
+    assert w4(1, 4096, 11008) == "k_w4a8_decode<IS>" and w4(16, 16384, 14336) == "k_w4a8_decode<IS>"
+    assert w4(17, 4096, 14336) != "k_w4a8_decode<IS>" and w4(64, 4096, 11008) != "k_w4a8_decode<IS>"
+    assert w4(1, 16400, 11008).startswith("k_w4a8_st") or w4(1, 16400, 11008).startswith("k_w4a8_sk")
+    assert w4(1, 4096, 12288) != "k_w4a8_decode<IS>"  # 96 groups: not a decode shape
+    assert w4(65, 4096, 11008) == "k_w4a8_prefill<4,2,2,2,IS>"
+    assert w4(16, 4096, 11008, True) == "k_w4a8_decode<FS>"
 
 
 def test_moe_validation(L):

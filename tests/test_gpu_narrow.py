@@ -84,6 +84,7 @@ def _case(orc, dev, seed, M, K, N, alpha):
 
 NARROW_SHAPES = [(1, 2048, 64), (5, 4096, 48), (33, 4096, 80), (64, 2048, 160),   # decode
                  (2, 2048, 16400), (20, 2048, 24592),                             # 6, 8 waves
+                 (3, 11008, 48), (16, 14336, 32),                                 # 86, 112 groups
                  (3, 384, 48), (17, 512, 64), (40, 1152, 32),                     # stream / skinny
                  (65, 512, 144), (200, 640, 400), (257, 256, 528)]                # tiled
 
