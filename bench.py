@@ -76,26 +76,26 @@ METRIC = "W4A8 integer-scale GEMM TOPS + HBM GB/s, K=4096 N=22016, M=1..4096"
 # profiles/*hbm_bytes.txt), keyed by (kernel, M). They hold only for the
 # kernel sources they were taken on: when a source file differs from the one
 # measured (sha256 prefix below), traffic is reported as null.
-TRAFFIC_SRC_SHA = {"gemm.hip": "06a1195034ae4823", "gemm_w8is.hip": "e4fcff966f541e75"}
+TRAFFIC_SRC_SHA = {"gemm.hip": "71795a04cc3fd7f8", "gemm_w8is.hip": "e4fcff966f541e75"}
 TRAFFIC_SRC = {"k_w4a8_decode<IS>": "gemm.hip", "k_w4a8_prefill<4,2,2,2,IS>": "gemm.hip",
                "k_w8a8_zp<9,32>": "gemm.hip", "k_w4a8_decode<IS,grouped>": "gemm.hip",
                "k_w8is_split": "gemm_w8is.hip"}
 TRAFFIC = {
-    ("k_w4a8_decode<IS>", 1): 48185513,
-    ("k_w4a8_decode<IS>", 4): 48546272,
-    ("k_w4a8_decode<IS>", 16): 49996238,
-    ("k_w4a8_decode<IS>", 64): 55925433,
-    ("k_w4a8_prefill<4,2,2,2,IS>", 256): 79307230,
-    ("k_w4a8_prefill<4,2,2,2,IS>", 4096): 922222329,
-    ("k_w8a8_zp<9,32>", 256): 29681392,
-    ("k_w8is_split", 1): 62579760,
-    ("k_w8is_split", 4): 62973048,
-    ("k_w8is_split", 16): 64545732,
-    ("k_w8is_split", 64): 70844553,
-    ("k_w4a8_decode<IS,grouped>", 1): 62672987,
-    ("k_w4a8_decode<IS,grouped>", 4): 125517799,
-    ("k_w4a8_decode<IS,grouped>", 16): 189674167,
-    ("k_w4a8_decode<IS,grouped>", 64): 259162095,
+    ("k_w4a8_decode<IS>", 1): 48190998,
+    ("k_w4a8_decode<IS>", 4): 48554828,
+    ("k_w4a8_decode<IS>", 16): 50004964,
+    ("k_w4a8_decode<IS>", 64): 55914897,
+    ("k_w4a8_prefill<4,2,2,2,IS>", 256): 79307207,
+    ("k_w4a8_prefill<4,2,2,2,IS>", 4096): 922280127,
+    ("k_w8a8_zp<9,32>", 256): 29681407,
+    ("k_w8is_split", 1): 62579842,
+    ("k_w8is_split", 4): 62972917,
+    ("k_w8is_split", 16): 64545536,
+    ("k_w8is_split", 64): 70844568,
+    ("k_w4a8_decode<IS,grouped>", 1): 62680449,
+    ("k_w4a8_decode<IS,grouped>", 4): 125518144,
+    ("k_w4a8_decode<IS,grouped>", 16): 189674135,
+    ("k_w4a8_decode<IS,grouped>", 64): 259160321,
 }
 
 
