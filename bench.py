@@ -784,7 +784,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the layer shards column-parallel with no exchange; see the design notes)",
+              "(the layer would shard column-parallel over N, with no exchange between GPUs)",
               file=sys.stderr)
         sys.exit(2)
 

@@ -24,8 +24,7 @@
  *        (LLaMA-3 scheme: fine-grained W8A8 for the down projection).
  *   [EX] "extreme quantization LLMs" (apxml.com): data packing of sub-byte codes.
  *
- * Readings where the pages are silent or garbled (each also listed in the
- * design notes): round() is C roundf (half away from zero, the "四舍五入" of
+ * Readings where the pages are silent or garbled: round() is C roundf (half away from zero, the "四舍五入" of
  * [QB] §2.2); x/s is a true IEEE division; a zero range gives scale 0 and
  * codes 0; the amplifier search starts at 2^0 and returns 1 when the smallest
  * scale is already >= 1; int4 codes are clipped to [-7,7] (qmax = 2^(b-1)-1
