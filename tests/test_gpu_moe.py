@@ -136,7 +136,7 @@ def test_moe_all_tokens_one_expert(bgt, orc, dev, T, K):
     _run(bgt, orc, dev, T, 8, K, 64, seed=T + 3, routing=routing)
 
 
-@pytest.mark.parametrize("T,K", [(12, 4096), (150, 384), (9, 14336)])
+@pytest.mark.parametrize("T,K", [(12, 4096), (150, 384), (9, 14336), (200, 4096), (200, 14336)])
 @pytest.mark.parametrize("width", [1, 2])
 def test_moe_narrow_scales(bgt, orc, dev, width, T, K):
     say(f"moe width={width} T={T} K={K}")
