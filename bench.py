@@ -679,7 +679,9 @@ def run_moe(args, torch, bgt, dev):
                   "value": round(step_bytes / (eager_ms * 1e-3) / 1e9, 1)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(bgt.w4a8_moe_kernel_name(1, E, route[1][3], K), Ts),
+                     # counters were taken on the w1 shape only
+                     "traffic": (measured_traffic(bgt.w4a8_moe_kernel_name(1, E, route[1][3], K), Ts)
+                                 if args.moe_linear == "w1" else None),
                      "kernel": bgt.w4a8_moe_kernel_name(1, E, route[1][3], K), "launch_T": Ts,
                      "avg_launch_us": round(avg_us, 3), "bytes_per_launch": int(avg_bytes)},
         "sweep": sweep,
