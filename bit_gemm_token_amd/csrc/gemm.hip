@@ -1198,7 +1198,7 @@ static size_t stream_lds_bytes(int MR, int GPW, bool FS, int G) {
   return 2 * area;                                 // two copies, tile parity
 }
 
-enum class W4Path { Decode, Stream, Skinny, Tiled };
+enum class W4Path { Decode, Stream, Skinny, Tiled, Wide };
 struct W4Plan { W4Path path; int mr; };
 
 // The kernel a W4A8 GEMM of this shape runs: small M streams the weights
@@ -1222,7 +1222,11 @@ static bool decode_padded(int G, int N, int mr) {
   return (G == 86 || G == 112) && mr == 1 && decode_waves(N / 16, mr) <= 4;
 }
 
+// rows from which the 256 x 256 tile kernel takes over from the 256 x 128 one
+constexpr int kWideMinM = 1024;
+
 static W4Plan plan_w4a8(int M, int N, int K, bool fs) {
+  if (M >= kWideMinM) return {W4Path::Wide, 0};
   if (M > 64) return {W4Path::Tiled, 0};
   const int mr = (M + 15) / 16, G = K / kGroup;
   if (G == 16 || G == 32 || decode_padded(G, N, mr)) return {W4Path::Decode, mr};
@@ -1290,6 +1294,7 @@ const char* w4a8_kernel_name(int64_t M, int64_t N, int64_t K, bool float_scale) 
        {"k_w4a8_prefill<4,2,2,2,FS>", "", "", ""}}};
   const W4Plan p = plan_w4a8((int)M, (int)N, (int)K, float_scale);
   const int fs = float_scale ? 1 : 0;
+  if (p.path == W4Path::Wide) return float_scale ? "k_w4a8_wide<FS>" : "k_w4a8_wide<IS>";
   if (p.path == W4Path::Tiled) return names[fs][2][0];
   if (p.path == W4Path::Decode) return float_scale ? "k_w4a8_decode<FS>" : "k_w4a8_decode<IS>";
   return names[fs][p.path == W4Path::Stream ? 0 : 1][p.mr - 1];
@@ -1354,6 +1359,9 @@ static void launch_w4a8_t(const int8_t* qx, const float* sx, const uint8_t* pack
       case 86: launch_decode<FS, 96, 86>(plan.mr, stream, qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out); break;
       default: launch_decode<FS, 112, 112>(plan.mr, stream, qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out); break;
     }
+  } else if (plan.path == W4Path::Wide) {
+    launch_w4a8_wide(FS, qx, sx, packed, iscale, sizeof(ST), fscale, inv_alpha, M, N, K, y,
+                     acc_out, stream);
   } else if (plan.path != W4Path::Tiled) {
     launch_small_m<FS>(plan, qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream);
   } else {

@@ -31,6 +31,11 @@ hipError_t launch_w4a8(bool float_scale, const int8_t* qx, const float* sx, cons
                        int64_t M, int64_t N, int64_t K, OutY y, int32_t* acc_out,
                        hipStream_t stream);
 
+// the large-M W4A8 GEMM (256 x 256 tiles); inv_alpha = 1/alpha (exact)
+void launch_w4a8_wide(bool float_scale, const int8_t* qx, const float* sx, const uint8_t* packed,
+                      const void* iscale, int iscale_bytes, const float* fscale, float inv_alpha,
+                      int M, int N, int K, OutY y, int32_t* acc_out, hipStream_t stream);
+
 // per-token quantization of x (M x K of element type x_type, leading dimension
 // ldx) into q_out /
 // s_out, then the integer-scale GEMM into y; one launch when
