@@ -41,6 +41,17 @@ T in {1,4,16,64} tokens in GB/s, with algorithmic bytes the active experts'
 weights and scales + T*K + 4*T + routing + 4*R*N per launch, plus per-launch
 rates at T in {512,4096}).
 
+The default line also carries the compute-bound half of the metric: `prefill`
+(the integer-scale GEMM and its float-scale control at M in {512, 1024, 2048,
+4096} on the same layer, median / p10 / p90 of event-bracketed launches) with
+its own `roofline_prefill` (int8 MFMA bound), a measured device-copy rate
+(`copy_sanity`) and, in `kernels`, a roofline for every kernel the decode step
+launches (the fused quantize+GEMM launches of M <= 4 under their own name);
+`roofline` is the one with the largest summed time.
+
+--workload block: the seven linears of a LLaMA-2-7B-shaped decoder block at
+M = 1 (GB/s) and M = 512 (TOPS); --workload single: one 16 x 4096 x 4096 GEMM.
+
 Profiling aids (not benchmark lines): --profile-m M runs only the
 quantizer and the integer-scale GEMM at that M (decode layer shape) for
 --steps iterations; --copy-probe-mb S copies an S MiB buffer --steps times
@@ -124,6 +135,51 @@ def gemm_ops(M, N, K):
     return 2 * M * N * K
 
 
+def pct(vals, q):
+    return round(float(np.percentile(np.asarray(vals, dtype=np.float64), q)), 3)
+
+
+def spread(vals):
+    """median / p10 / p90 of a list of per-launch durations (us)."""
+    return {"us_median": pct(vals, 50), "us_p10": pct(vals, 10), "us_p90": pct(vals, 90)}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def copy_sanity(torch, dev, mib=512, reps=10):
+    """A plain device-to-device copy of `mib` MiB (torch), timed with events:
+    the practical HBM rate on this machine (read + write bytes / time)."""
+    n = (mib << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    ts = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        ts.append((e0, e1))
+    torch.cuda.synchronize()
+    us = [x.elapsed_time(y) * 1e3 for x, y in ts]
+    med = float(np.median(us))
+    del a, b
+    return {"bytes_each_way": n * 4, "us_median": round(med, 2),
+            "GBps": round(2 * n * 4 / med / 1e3, 1), "kind": "torch copy_ (read + write)"}
+
+
 # --------------------------------------------------------------------- CPU side
 def cpu_baseline(x, w, Ms=None, min_seconds=10.0, unit="GB/s"):
     """Time the oracle (as it stands) on the decode step: per-token
@@ -157,6 +213,7 @@ def cpu_baseline(x, w, Ms=None, min_seconds=10.0, unit="GB/s"):
         "value": round(value, 4),
         "unit": unit,
         "cores": cores,
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": f"{steps} passes of quant_act + w4a8_gemm_is at M in {Ms}, K={K}, N={N} "
                   f"in {el:.1f} s; offline packing excluded",
@@ -287,7 +344,8 @@ def run_decode(args, torch, bgt, dev):
     ms_step = graph_steps(torch, step, args.steps, args.warmup) if args.launch == "graph" else eager_ms
 
     # per-launch GEMM duration (and quantization + GEMM duration): back-to-back
-    # launches at one M, weight copies rotating as in the step
+    # launches at one M, weight copies rotating as in the step; ten replays of
+    # the graph give ten samples (each the mean over 2R launches)
     per_m, lin_m = {}, {}
     for M in Ms:
         q, s = qbuf[M]
@@ -299,40 +357,45 @@ def run_decode(args, torch, bgt, dev):
         def launch_lin(j, M=M):
             packed, iscale, _ = rot.get(j)
             linear(M, packed, iscale)
-        per_m[M] = graph_launch_us(torch, launch, 2 * rot.R)
-        lin_m[M] = graph_launch_us(torch, launch_lin, 2 * rot.R)
+        per_m[M] = graph_launch_us(torch, launch, 2 * rot.R, reps=10)
+        lin_m[M] = graph_launch_us(torch, launch_lin, 2 * rot.R, reps=10)
 
     eager_per_m = {M: [] for M in Ms}
     for M, e0, e1 in eager_events:
         eager_per_m[M].append(e0.elapsed_time(e1) * 1e3)     # us
     step_bytes = sum(gemm_bytes(M, N, K, sb) + quant_bytes(M, K) for M in Ms)
+
+    # what the step launches at each M: one fused kernel (quantization in the
+    # GEMM's prologue: reads the fp32 rows, writes codes and token scales), or
+    # the quantizer and then the GEMM kernel
+    fused = {M: bool(args.fused_quant and bgt.w4a8_linear_fused(xs[M])) for M in Ms}
+    launches = []                                   # (kernel, M, durations, bytes, ops)
+    for M in Ms:
+        if fused[M]:
+            launches.append((bgt.w4a8_kernel_name(M, N, K) + "+fused-quant", M, lin_m[M],
+                             gemm_bytes(M, N, K, sb) + 4 * M * K, gemm_ops(M, N, K)))
+        else:
+            launches.append((bgt.w4a8_kernel_name(M, N, K), M, per_m[M], gemm_bytes(M, N, K, sb),
+                             gemm_ops(M, N, K)))
     sweep = {}
     for M in Ms:
         us = float(np.mean(per_m[M]))
         b = gemm_bytes(M, N, K, sb)
-        sweep[str(M)] = {"gemm_us": round(us, 3), "gemm_GBps": round(b / us / 1e3, 1),
+        sweep[str(M)] = {"gemm_us": round(us, 3), **{"gemm_" + k: v for k, v in spread(per_m[M]).items()},
+                         "gemm_GBps": round(b / us / 1e3, 1),
                          "gemm_TOPS": round(gemm_ops(M, N, K) / us / 1e6, 2),
                          "hbm_frac": round(b / us / 1e3 / HBM_PEAK_GBS, 4),
+                         "mfma_frac": round(gemm_ops(M, N, K) / us / 1e6 / INT8_PEAK_TOPS, 4),
                          "quant_gemm_us": round(float(np.mean(lin_m[M])), 3),
-                         "quant_gemm_launches": 1 if args.fused_quant and bgt.w4a8_linear_fused(xs[M]) else 2,
+                         **{"quant_gemm_" + k: v for k, v in spread(lin_m[M]).items()},
+                         "quant_gemm_launches": 1 if fused[M] else 2,
                          "eager_quant_gemm_us_median": round(float(np.median(eager_per_m[M])), 3),
-                         "kernel": bgt.w4a8_kernel_name(M, N, K)}
-    # dominant GEMM kernel: largest summed time over the step
-    by_kernel = {}
-    for M in Ms:
-        k = bgt.w4a8_kernel_name(M, N, K)
-        by_kernel.setdefault(k, []).append(M)
-    dom = max(by_kernel, key=lambda k: sum(np.mean(per_m[M]) for M in by_kernel[k]))
-    dMs = by_kernel[dom]
-    durs = [u for M in dMs for u in per_m[M]]
-    avg_us = float(np.mean(durs))
-    avg_bytes = float(np.mean([gemm_bytes(M, N, K, sb) for M in dMs]))
-    achieved = avg_bytes / avg_us / 1e3
-    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(dom, dMs) if sb == 4 else None,
-            "kernel": dom, "launch_M": dMs, "avg_launch_us": round(avg_us, 3),
-            "bytes_per_launch": int(avg_bytes)}
+                         "kernel": bgt.w4a8_kernel_name(M, N, K) + ("+fused-quant" if fused[M] else "")}
+    kernels = kernel_rooflines(launches)
+    dom = max(kernels, key=lambda k: k["total_us"])
+    roof = dict(dom["roofline"])
+    roof["traffic"] = (measured_traffic(dom["kernel"], dom["launch_M"])
+                       if sb == 4 and roof["bound"] == "hbm" else None)
     out = {
         "metric": METRIC, "value": round(step_bytes / (ms_step * 1e-3) / 1e9, 1), "unit": "GB/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
@@ -346,52 +409,105 @@ def run_decode(args, torch, bgt, dev):
                    "weight_buffers_rotated": rot.R},
         "eager": {"ms_per_step": round(eager_ms, 4),
                   "value": round(step_bytes / (eager_ms * 1e-3) / 1e9, 1)},
-        "roofline": roof, "sweep": sweep,
+        "roofline": roof, "kernels": [{k: v for k, v in e.items() if k != "roofline"} | e["roofline"]
+                                      for e in kernels],
+        "sweep": sweep,
     }
-    return out, (x, w)
+    return out, (x, w), (pw, rot)
+
+
+def kernel_rooflines(launches):
+    """Group timed launches by kernel; per kernel the summed mean duration, and a
+    roofline over its launches: the bound is whichever of the HBM time
+    (algorithmic bytes / 8 TB/s) and the MFMA time (ops / 5 POP/s) is larger
+    summed over them; achieved = mean bytes (or ops) per launch / mean launch
+    duration."""
+    by = {}
+    for name, M, durs, b, ops in launches:
+        by.setdefault(name, []).append((M, durs, b, ops))
+    out = []
+    for name, items in by.items():
+        Ms = [m for m, _, _, _ in items]
+        durs = [u for _, d, _, _ in items for u in d]
+        avg_us = float(np.mean(durs))
+        mb = float(np.mean([b for _, _, b, _ in items]))
+        mo = float(np.mean([o for _, _, _, o in items]))
+        t_hbm = sum(b for _, _, b, _ in items) / HBM_PEAK_GBS
+        t_mfma = sum(o for _, _, _, o in items) / INT8_PEAK_TOPS / 1e3
+        if t_hbm >= t_mfma:
+            ach = mb / avg_us / 1e3
+            r = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                 "frac": round(ach / HBM_PEAK_GBS, 4)}
+        else:
+            ach = mo / avg_us / 1e6
+            r = {"bound": "mfma", "achieved": round(ach, 1), "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
+                 "frac": round(ach / INT8_PEAK_TOPS, 4)}
+        r.update({"traffic": None, "kernel": name, "launch_M": Ms, "avg_launch_us": round(avg_us, 3),
+                  "bytes_per_launch": int(mb), "ops_per_launch": int(mo)})
+        out.append({"kernel": name, "launch_M": Ms,
+                    "total_us": round(sum(float(np.mean(d)) for _, d, _, _ in items), 3), "roofline": r})
+    return out
+
+
+def prefill_sweep(torch, bgt, dev, xd, pw, rot, Ms, warmup=3, timed=10, out_dtype=None):
+    """Per-launch durations of the integer-scale GEMM and its float-scale
+    control at each M (K=4096, N=22016), weight copies rotating; median, p10,
+    p90 over `timed` event-bracketed launches."""
+    K, N = synth.K_LAYER, synth.N_LAYER
+    qs = {M: bgt.quantize_act(xd[:M].contiguous())[:2] for M in Ms}
+    odt = out_dtype or torch.float32
+    res = {}
+    for fs in (False, True):
+        for M in Ms:
+            q, s = qs[M]
+            y = torch.empty((M, N), dtype=odt, device=dev)
+            ts = []
+            for it in range(warmup + timed):
+                packed, iscale, fscale = rot.next()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                if fs:
+                    bgt.w4a8_gemm_fs(q, s, packed, fscale, N, y=y)
+                else:
+                    bgt.w4a8_gemm_is_narrow(q, s, packed, iscale, pw["alpha"], N, y=y)
+                e1.record()
+                if it >= warmup:
+                    ts.append((e0, e1))
+            torch.cuda.synchronize()
+            us = [a.elapsed_time(b) * 1e3 for a, b in ts]
+            med = float(np.median(us))
+            tops = gemm_ops(M, N, K) / med / 1e6
+            res[("fs" if fs else "is") + str(M)] = {
+                **spread(us), "TOPS": round(tops, 1), "mfma_frac": round(tops / INT8_PEAK_TOPS, 4),
+                "GBps": round(gemm_bytes(M, N, K, out_bytes=2 if out_dtype is not None and out_dtype != torch.float32 else 4) / med / 1e3, 1),
+                "kernel": bgt.w4a8_kernel_name(M, N, K, fs)}
+            del y
+    big = max(Ms)
+    r = res["is%d" % big]
+    roof = {"bound": "mfma", "achieved": r["TOPS"], "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
+            "frac": r["mfma_frac"],
+            "traffic": measured_traffic(r["kernel"], [big]) if out_dtype in (None, torch.float32) else None,
+            "kernel": r["kernel"], "launch_M": [big], "avg_launch_us": r["us_median"],
+            "ops_per_launch": gemm_ops(big, N, K), "timing": "median of event-bracketed launches"}
+    return res, roof
 
 
 def run_prefill(args, torch, bgt, dev):
+    """The compute-bound half on its own: the integer-scale GEMM and its
+    float-scale control at M in {512, 1024, 2048, 4096} (value: TOPS of the
+    integer-scale GEMMs over the sweep)."""
     K, N = synth.K_LAYER, synth.N_LAYER
     Ms = list(synth.PREFILL_M)
     x, w = synth.layer_inputs(0, M=max(Ms), K=K, N=N)
     xd = torch.from_numpy(x).to(dev)
     pw = bgt.pack_weights_int4(torch.from_numpy(w).to(dev), alpha=synth.ALPHA)
     rot = Rotor(torch, pw["packed"], pw["iscale"], pw["fscale"])
-    qs = {M: bgt.quantize_act(xd[:M].contiguous())[:2] for M in Ms}
     odt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[args.out_dtype]
-    ob = 4 if args.out_dtype == "f32" else 2
-    ys = {M: torch.empty((M, N), dtype=odt, device=dev) for M in Ms}
-    res = {}
-    tot_ops = 0
-    tot_us = 0.0
-    for fs in (False, True):
-        for M in Ms:
-            q, s = qs[M]
-            ts = []
-            for it in range(args.warmup + args.steps):
-                packed, iscale, fscale = rot.next()
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record()
-                if fs:
-                    bgt.w4a8_gemm_fs(q, s, packed, fscale, N, y=ys[M])
-                else:
-                    bgt.w4a8_gemm_is_narrow(q, s, packed, iscale, pw["alpha"], N, y=ys[M])
-                e1.record()
-                if it >= args.warmup:
-                    ts.append((e0, e1))
-            torch.cuda.synchronize()
-            us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in ts]))
-            tops = gemm_ops(M, N, K) / us / 1e6
-            res[("fs" if fs else "is") + str(M)] = {
-                "us_median": round(us, 2), "TOPS": round(tops, 1),
-                "mfma_frac": round(tops / INT8_PEAK_TOPS, 4), "kernel": bgt.w4a8_kernel_name(M, N, K, fs)}
-            if not fs:
-                tot_ops += gemm_ops(M, N, K)
-                tot_us += us
-    big = max(Ms)
-    r = res["is%d" % big]
+    res, roof = prefill_sweep(torch, bgt, dev, xd, pw, rot, Ms, warmup=args.warmup, timed=args.steps,
+                              out_dtype=odt)
+    tot_ops = sum(gemm_ops(M, N, K) for M in Ms)
+    tot_us = sum(res["is%d" % M]["us_median"] for M in Ms)
     out = {
         "metric": METRIC, "value": round(tot_ops / tot_us / 1e6, 1), "unit": "TOPS",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -399,14 +515,132 @@ def run_prefill(args, torch, bgt, dev):
         "vs_baseline": None, "dtype": "int8xint4->int32", "data": "synthetic (seeded)",
         "config": {"workload": "prefill sweep: W4A8-IS GEMM K=4096 N=22016, M in {512,1024,2048,4096}",
                    "output": {"f32": "float32", "f16": "float16", "bf16": "bfloat16"}[args.out_dtype]},
-        "roofline": {"bound": "mfma", "achieved": r["TOPS"], "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
-                     "frac": r["mfma_frac"],
-                     "traffic": measured_traffic(r["kernel"], [big]) if ob == 4 else None,
-                     "kernel": r["kernel"], "launch_M": [big],
-                     "avg_launch_us": r["us_median"]},
+        "roofline": roof,
         "sweep": res,
     }
     return out, (x, w)
+
+
+def linear_workload(args, torch, bgt, dev, layers, Ms, fused_quant=True):
+    """Quantizer + integer-scale GEMM for each (name, K, N, packed weights) of
+    `layers` at each M: a step per M (all layers in order, graph-replayed),
+    weight copies rotating so weight bytes come from HBM; per-launch durations
+    of what each step launches. Returns per-M step times and launch records."""
+    per_layer = [p["packed"].numel() + p["iscale"].numel() * 4 for _, _, _, p, _ in layers]
+    R = max(2, math.ceil(2 * MALL_BYTES / sum(per_layer)))
+    rot = [[(p["packed"].clone(), p["iscale"].clone()) for _, _, _, p, _ in layers] for _ in range(R)]
+    res = {}
+    for M in Ms:
+        bufs = []
+        for name, K, N, p, xs in layers:
+            xd = torch.from_numpy(np.ascontiguousarray(xs[:M])).to(dev)
+            bufs.append((xd, torch.empty((M, K), dtype=torch.int8, device=dev),
+                         torch.empty(M, dtype=torch.float32, device=dev),
+                         torch.empty((M, N), dtype=torch.float32, device=dev)))
+
+        def lin(i, r, M=M, bufs=bufs):
+            name, K, N, p, _ = layers[i]
+            xd, q, sc, y = bufs[i]
+            pk, isc = rot[r % R][i]
+            if fused_quant:
+                bgt.w4a8_linear_is(xd, pk, isc, p["alpha"], N, qx=q, sx=sc, y=y)
+            else:
+                bgt.quantize_act(xd, q=q, scale=sc)
+                bgt.w4a8_gemm_is(q, sc, pk, isc, p["alpha"], N, y=y)
+
+        def gemm(i, r, M=M, bufs=bufs):
+            name, K, N, p, _ = layers[i]
+            xd, q, sc, y = bufs[i]
+            pk, isc = rot[r % R][i]
+            bgt.w4a8_gemm_is(q, sc, pk, isc, p["alpha"], N, y=y)
+
+        def step(k):
+            for i in range(len(layers)):
+                lin(i, k)
+        for k in range(args.warmup):
+            step(k)
+        torch.cuda.synchronize()
+        ms_step = graph_steps(torch, step, args.steps, args.warmup)
+        n = 2 * R if M <= 64 else R
+        launches = []
+        layer_res = {}
+        for i, (name, K, N, p, _) in enumerate(layers):
+            fused = bool(fused_quant and bgt.w4a8_linear_fused(bufs[i][0]))
+            d_lin = graph_launch_us(torch, lambda j, i=i: lin(i, j), n, reps=10 if M <= 64 else 5)
+            d_gemm = graph_launch_us(torch, lambda j, i=i: gemm(i, j), n, reps=10 if M <= 64 else 5)
+            kname = bgt.w4a8_kernel_name(M, N, K) + ("+fused-quant" if fused else "")
+            b = gemm_bytes(M, N, K) + (4 * M * K if fused else 0)
+            launches.append((kname, M, d_lin if fused else d_gemm, b, gemm_ops(M, N, K)))
+            layer_res[name] = {"K": K, "N": N, "kernel": kname,
+                               "quant_gemm_us": round(float(np.mean(d_lin)), 3),
+                               "gemm_us": round(float(np.mean(d_gemm)), 3),
+                               **{"gemm_" + k: v for k, v in spread(d_gemm).items()},
+                               "quant_gemm_launches": 1 if fused else 2}
+        step_bytes = sum(gemm_bytes(M, N, K) + quant_bytes(M, K) for _, K, N, _, _ in layers)
+        step_ops = sum(gemm_ops(M, N, K) for _, K, N, _, _ in layers)
+        kernels = kernel_rooflines(launches)
+        dom = max(kernels, key=lambda k: k["total_us"])
+        res[M] = {"ms_per_step": round(ms_step, 4),
+                  "GBps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+                  "TOPS": round(step_ops / (ms_step * 1e-3) / 1e12, 2),
+                  "step_bytes": step_bytes, "step_ops": step_ops, "layers": layer_res,
+                  "roofline": dom["roofline"],
+                  "kernels": [{k: v for k, v in e.items() if k != "roofline"} | e["roofline"]
+                              for e in kernels]}
+        del bufs
+    return res, R
+
+
+def run_block(args, torch, bgt, dev):
+    """The seven linears of a LLaMA-2-7B-shaped decoder block (q, k, v, o
+    4096 -> 4096; gate, up 4096 -> 11008; down 11008 -> 4096), all W4A8
+    integer-scale, group 128, amplifier 1024, random N(0, 0.02) weights; one
+    step is quant_act + GEMM for every linear. M = 1 (decode: value in GB/s of
+    the block's algorithmic bytes) and M = 512 (prefill: TOPS)."""
+    Ms = (1, 512)
+    layers = []
+    for name, x, w in synth.block_inputs(0, max(Ms)):
+        K, N = w.shape
+        p = bgt.pack_weights_int4(torch.from_numpy(w).to(dev), alpha=synth.ALPHA)
+        layers.append((name, K, N, p, x))
+        del w
+    res, R = linear_workload(args, torch, bgt, dev, layers, Ms, fused_quant=args.fused_quant)
+    r1, r512 = res[1], res[512]
+    return {
+        "metric": "LLaMA-2-7B block linears, W4A8 integer-scale: GB/s at M=1, TOPS at M=512",
+        "value": r1["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": r1["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8xint4->int32",
+        "data": "synthetic (seeded; X ~N(0,1) + 1% channels x20, W ~N(0,0.02))",
+        "config": {"workload": "LLaMA-2-7B block: q,k,v,o 4096x4096, gate,up 4096x11008, down "
+                               "11008x4096; quant_act + W4A8-IS GEMM per linear, g=128 alpha=1024; "
+                               "value at M=1, M=512 in `prefill`",
+                   "launch": "hip_graph", "weight_buffers_rotated": R},
+        "roofline": r1["roofline"], "decode": r1,
+        "prefill": {k: v for k, v in r512.items()},
+        "roofline_prefill": r512["roofline"],
+    }, (None, None)
+
+
+def run_single(args, torch, bgt, dev):
+    """One W4A8 integer-scale GEMM: X 16 x 4096 N(0,1) with 1% channels x20,
+    W 4096 x 4096 N(0, 0.02), alpha 1024, seed 0; a step is quant_act + GEMM."""
+    x, w = synth.single_gemm_inputs(0)
+    K, N = w.shape
+    p = bgt.pack_weights_int4(torch.from_numpy(w).to(dev), alpha=synth.ALPHA)
+    res, R = linear_workload(args, torch, bgt, dev, [("single", K, N, p, x)], (16,),
+                             fused_quant=args.fused_quant)
+    r = res[16]
+    return {
+        "metric": "single W4A8 integer-scale GEMM M=16 K=4096 N=4096, HBM GB/s",
+        "value": r["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": r["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8xint4->int32",
+        "data": "synthetic (seed 0; X ~N(0,1) + 1% channels x20, W ~N(0,0.02))",
+        "config": {"workload": "single layer: quant_act + W4A8-IS GEMM, M=16 K=4096 N=4096, g=128, "
+                               "alpha=1024", "launch": "hip_graph", "weight_buffers_rotated": R},
+        "roofline": r["roofline"], "detail": r,
+    }, (None, None)
 
 
 def run_w8a8(args, torch, bgt, dev):
@@ -766,8 +1000,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "w8a8", "w8is", "moe"])
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "prefill", "w8a8", "w8is", "moe", "block", "single"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="decode workload: leave out the prefill sweep (M = 512..4096) of the same layer")
     ap.add_argument("--iscale-bits", type=int, default=32, choices=[8, 16, 32],
                     help="decode workload: integer scales stored as uint8 / uint16 / int32 "
                          "(same values; bytes counted at the stored width)")
@@ -803,13 +1040,29 @@ def main():
         print(json.dumps(r), flush=True)
         return
     if args.workload == "decode":
-        out, (x, w) = run_decode(args, torch, bgt, dev)
+        out, (x, w), (pw, rot) = run_decode(args, torch, bgt, dev)
+        if not args.no_prefill:
+            # the compute-bound half of the metric (M = 512 .. 4096) on the same
+            # layer and weight copies
+            Ms = list(synth.PREFILL_M)
+            xp = torch.from_numpy(synth.activations(0, max(Ms), synth.K_LAYER)).to(dev)
+            res, roof = prefill_sweep(torch, bgt, dev, xp, pw, rot, Ms)
+            del xp
+            out["prefill"] = {"workload": "W4A8-IS GEMM and its float-scale control, K=4096 N=22016, "
+                                          "M in {512,1024,2048,4096}, fp32 y",
+                              "sweep": res}
+            out["roofline_prefill"] = roof
+        out["copy_sanity"] = copy_sanity(torch, dev)
     elif args.workload == "prefill":
         out, (x, w) = run_prefill(args, torch, bgt, dev)
     elif args.workload == "w8is":
         out, (x, w) = run_w8is(args, torch, bgt, dev)
     elif args.workload == "moe":
         out, (x, w) = run_moe(args, torch, bgt, dev)
+    elif args.workload == "block":
+        out, (x, w) = run_block(args, torch, bgt, dev)
+    elif args.workload == "single":
+        out, (x, w) = run_single(args, torch, bgt, dev)
     else:
         out, (x, w) = run_w8a8(args, torch, bgt, dev)
     if not args.no_cpu_baseline and args.workload in ("decode", "prefill"):

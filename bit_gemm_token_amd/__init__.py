@@ -52,7 +52,7 @@ EXPORTED = (
     "bgt_narrow_iscale", "bgt_w4a8_gemm_is_narrow", "bgt_w4a8_linear_is", "bgt_w4a8_linear_fused",
     "bgt_quantize_act_ex", "bgt_w4a8_gemm_is_ex", "bgt_w4a8_gemm_fs_ex",
     "bgt_pack_weights_int8", "bgt_w8a8_gemm_is", "bgt_w8a8_is_kernel_name",
-    "bgt_w4a8_moe_gemm_is", "bgt_w4a8_moe_kernel_name",
+    "bgt_w4a8_moe_gemm_is", "bgt_w4a8_moe_kernel_name", "bgt_repack_int4_canonical",
 )
 _NAMES = ("bgt_status_string", "bgt_w4a8_kernel_name", "bgt_w8a8_is_kernel_name",
           "bgt_w4a8_moe_kernel_name")
@@ -97,6 +97,7 @@ def lib():
         L.bgt_w4a8_moe_gemm_is.argtypes = [P, P, I64, P, P, I64, I64, P, P, I, I, I64, I64, P, I,
                                            P, P]
         L.bgt_w4a8_moe_kernel_name.argtypes = [I64, I64, I64, I64]
+        L.bgt_repack_int4_canonical.argtypes = [P, I64, I64, P, P]
         for f in EXPORTED:
             getattr(L, f).restype = ctypes.c_char_p if f in _NAMES else I
         _lib = L
@@ -256,6 +257,20 @@ def w4a8_gemm_is(qx, sx, packed, iscale, alpha: int, N: int, y=None, acc_out=Non
 
 
 _NARROW = {1: "uint8", 2: "uint16", 4: "int32"}
+
+
+def repack_int4_canonical(canonical, K: int, N: int, packed=None):
+    """int4 codes in the canonical layout (W^T, K contiguous, two per byte, even
+    k in the low nibble; N*K/2 uint8) rewritten into the GEMMs' layout; returns
+    the packed tensor (N*K/2 uint8)."""
+    torch = _torch()
+    _check(canonical, "canonical", torch.uint8, (N * K // 2,))
+    packed = torch.empty(N * K // 2, dtype=torch.uint8, device=canonical.device) if packed is None else packed
+    _check(packed, "packed", torch.uint8, (N * K // 2,))
+    st = lib().bgt_repack_int4_canonical(_ptr(canonical), int(K), int(N), _ptr(packed),
+                                         _stream(canonical.device))
+    _raise("bgt_repack_int4_canonical", st)
+    return packed
 
 
 def narrow_iscale(iscale, width: int, out=None):

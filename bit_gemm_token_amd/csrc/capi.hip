@@ -44,7 +44,7 @@ int searched_alpha_log2(float smin) {
 
 extern "C" {
 
-int bgt_abi_version(void) { return 106; }
+int bgt_abi_version(void) { return 107; }
 
 int bgt_w4a8_linear_fused(int64_t M, int64_t K, const void* x, int64_t ldx) {
   return bgt::w4a8_linear_fused(M, K, x, ldx) ? 1 : 0;
@@ -215,6 +215,16 @@ int bgt_w4a8_gemm_fs_ex(const int8_t* qx, const float* sx, const uint8_t* packed
   return hip_status(bgt::launch_w4a8(true, qx, sx, packed, nullptr, 4, fscale, 1, M, N, K,
                                      bgt::OutY{y, y_type}, nullptr,
                                      static_cast<hipStream_t>(stream)));
+}
+
+int bgt_repack_int4_canonical(const uint8_t* canonical, int64_t K, int64_t N, uint8_t* packed,
+                              void* stream) {
+  if (!canonical || !packed) return BGT_ERR_NULL;
+  if (K < BGT_GROUP || K > 65536 || K % BGT_GROUP != 0) return BGT_ERR_SHAPE;
+  if (N < 16 || N > (1 << 24) || N % 16 != 0) return BGT_ERR_SHAPE;
+  if (!aligned16(canonical) || !aligned16(packed)) return BGT_ERR_ALIGN;
+  return hip_status(bgt::launch_repack_canonical(canonical, K, N, packed,
+                                                 static_cast<hipStream_t>(stream)));
 }
 
 int bgt_narrow_iscale(const int32_t* iscale, int64_t count, int width, void* out, void* stream) {

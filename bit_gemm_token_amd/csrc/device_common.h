@@ -51,6 +51,18 @@ struct OutY {
     else if (type == kF16) static_cast<__half*>(p)[o] = __float2half(v);
     else static_cast<__hip_bfloat16*>(p)[o] = __float2bfloat16(v);
   }
+  // the same, as a non-temporal store (output written once, not re-read)
+  __device__ __forceinline__ void put_nt(int64_t o, float v) const {
+    if (type == kF32) {
+      __builtin_nontemporal_store(v, static_cast<float*>(p) + o);
+    } else {
+      const __half h = __float2half(v);
+      const __hip_bfloat16 b = __float2bfloat16(v);
+      const uint16_t bits = type == kF16 ? *reinterpret_cast<const uint16_t*>(&h)
+                                         : *reinterpret_cast<const uint16_t*>(&b);
+      __builtin_nontemporal_store(bits, static_cast<uint16_t*>(p) + o);
+    }
+  }
 };
 
 // Expert routing of a grouped (mixture-of-experts) GEMM. The routed slots are

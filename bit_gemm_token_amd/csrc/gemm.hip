@@ -628,11 +628,11 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
       if (!full && (i >= M || j >= N)) continue;
       const int64_t o = (int64_t)(r0 + i) * N + j;
       if (FS) {
-        y.put(o, facc[k][r] * srow[a][r]);
+        y.put_nt(o, facc[k][r] * srow[a][r]);
       } else {
         const float t0 = (float)acc[k][r] * srow[a][r];
-        y.put(o, t0 * inv_alpha);
-        if (acc_out) acc_out[o] = acc[k][r];
+        y.put_nt(o, t0 * inv_alpha);
+        if (acc_out) __builtin_nontemporal_store(acc[k][r], acc_out + o);
       }
     }
   }

@@ -21,6 +21,11 @@ hipError_t launch_group_quant_pack(bool int8_codes, const float* w, int64_t K, i
                                    void* packed, float* fscale, int32_t* iscale,
                                    hipStream_t stream);
 
+// canonical int4 layout (W^T, K contiguous, even k in the low nibble) ->
+// kernel-native layout; K % 128 == 0, N % 16 == 0
+hipError_t launch_repack_canonical(const uint8_t* canonical, int64_t K, int64_t N,
+                                   uint8_t* packed, hipStream_t stream);
+
 hipError_t launch_integer_scales(const float* fscale, int64_t count, int alpha, int32_t* iscale,
                                  hipStream_t stream);
 

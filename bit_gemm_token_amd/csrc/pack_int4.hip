@@ -15,6 +15,8 @@
 // with 16-byte stores into the lane slots of the (16-column tile, group)
 // block of the device layout (int4: one 1 KiB block, four stores; int8: two
 // 1 KiB halves, eight stores).
+#include <algorithm>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -148,6 +150,48 @@ hipError_t launch_narrow_scales(const int32_t* in, int64_t count, int out_bytes,
   else
     hipLaunchKernelGGL(k_narrow_scales<uint8_t>, grid, dim3(kPThreads), 0, stream, in, count,
                        static_cast<uint8_t*>(out));
+  return hipGetLastError();
+}
+
+// Canonical -> kernel-native int4 layout. The canonical layout holds W^T with K
+// contiguous, two codes per byte, even k in the low nibble: the 16 codes
+// k0 .. k0+15 of column j (k0 a multiple of 16) are the 8 bytes at (j*K +
+// k0)/2, nibble i = code k0+i. A native 16-byte chunk (tile t, group g, lane
+// 16s + c) holds column 16t + c: bytes 0..7 the codes 128g + 16s + e, bytes
+// 8..15 the codes 128g + 64 + 16s + e (e = 0..15), each dword's byte b
+// carrying e_b (low nibble) and e_{b+4} (high nibble). One thread per native
+// chunk: two 8-byte canonical reads, and per 8 codes a perfect shuffle of the
+// nibbles (e0 e1 .. e7 -> e0 e4 e1 e5 e2 e6 e3 e7).
+__device__ __forceinline__ uint32_t nibble_shuffle(uint32_t x) {
+  x = (x & 0xFF0000FFu) | ((x & 0x00FF0000u) >> 8) | ((x & 0x0000FF00u) << 8);
+  return (x & 0xF00FF00Fu) | ((x & 0x0F000F00u) >> 4) | ((x & 0x00F000F0u) << 4);
+}
+
+__global__ __launch_bounds__(256) void k_repack_canonical(const uint2* __restrict__ canonical,
+                                                          int64_t K, int64_t N,
+                                                          uint4* __restrict__ packed) {
+  const int64_t G = K / kGroup;
+  const int64_t chunks = N * K / 32;
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < chunks;
+       q += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = q / (64 * G), g = (q / 64) % G;
+    const int lane = (int)(q % 64), s4 = lane / 16, c = lane % 16;
+    const int64_t j = 16 * t + c;
+    const int64_t k0 = kGroup * g + 16 * s4;
+    const uint2 a = canonical[(j * K + k0) / 16];          // codes k0 .. k0+15 (h = 0)
+    const uint2 b = canonical[(j * K + k0 + 64) / 16];     // codes k0+64 .. k0+79 (h = 1)
+    packed[q] = make_uint4(nibble_shuffle(a.x), nibble_shuffle(a.y), nibble_shuffle(b.x),
+                           nibble_shuffle(b.y));
+  }
+}
+
+hipError_t launch_repack_canonical(const uint8_t* canonical, int64_t K, int64_t N,
+                                   uint8_t* packed, hipStream_t stream) {
+  const int64_t chunks = N * K / 32;
+  const int64_t blocks = std::min<int64_t>((chunks + 255) / 256, 65536);
+  hipLaunchKernelGGL(k_repack_canonical, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     reinterpret_cast<const uint2*>(canonical), K, N,
+                     reinterpret_cast<uint4*>(packed));
   return hipGetLastError();
 }
 

@@ -77,6 +77,11 @@ extern "C" {
  *     rowsum_i = sum_k q_ik.
  * Applied to W^T (N x K) this is the per-channel weight quantization of the
  * W8A8 control ([QN] Per-Channel Quantization): rowsum is then colsum_w.
+ * ASYM precondition: the range is the row's raw min and max (no forced zero),
+ * so a row represents its values only when min <= 0 <= max. For a row of one
+ * sign z clips to 0 or 255 and the codes saturate; the result is still the
+ * formula above (no status reports it), and bgt_w8a8_gemm_zp on such rows is
+ * the formula's value, not X.W.
  *
  *   x       rows x cols float32, leading dimension ld >= cols (elements).
  *   q       rows x cols int8 (SYM) or uint8 (ASYM), dense (leading dim cols).
@@ -155,6 +160,27 @@ int bgt_pack_weights_int4(const float* w, int64_t K, int64_t N, int64_t group, i
 int bgt_w4a8_gemm_is(const int8_t* qx, const float* sx, const uint8_t* packed,
                      const int32_t* iscale, int alpha, int64_t M, int64_t N, int64_t K,
                      float* y, int32_t* acc_out, void* stream);
+
+/*
+ * bgt_repack_int4_canonical -- accept int4 weights in the canonical layout.
+ * The pages allow any packing of sub-byte codes into standard bytes (the
+ * apxml extreme-quantization page, 实现与评估考量, "data packing"); the
+ * canonical layout read here is the plain one: the codes of W^T with K
+ * contiguous per output column, two per byte, even k in the low nibble,
+ *     canonical byte (j*K + k)/2, nibble k % 2 (0 = low), 4-bit two's complement,
+ * for the K x N codes q_kj. The call rewrites them into the kernel-native
+ * layout of bgt_pack_weights_int4 (the codes themselves are unchanged), so
+ * weights quantized elsewhere can be fed to the GEMMs with the caller's own
+ * scales. Asynchronous on `stream`.
+ *
+ *   canonical  N*K/2 bytes (device, caller-owned, read only).
+ *   packed     N*K/2 bytes (device, caller-owned): the native layout.
+ * Requirements: K % 128 == 0, 128 <= K <= 65536, N % 16 == 0, 16 <= N <= 2^24;
+ * both pointers non-NULL (BGT_ERR_NULL) and 16-byte aligned (BGT_ERR_ALIGN).
+ * Nothing is written on a rejected call.
+ */
+int bgt_repack_int4_canonical(const uint8_t* canonical, int64_t K, int64_t N, uint8_t* packed,
+                              void* stream);
 
 /*
  * bgt_narrow_iscale -- store integer scales in narrower elements ([IS] 方法:
@@ -250,6 +276,9 @@ int bgt_w4a8_gemm_fs_ex(const int8_t* qx, const float* sx, const uint8_t* packed
  *   y  M x N float32; acc_out optional M x N int32.
  * Requirements: 1 <= M <= 65536, N % 16 == 0, 16 <= N <= 2^24,
  * K % 128 == 0, 128 <= K <= 32768 (so |A| <= K*255^2 < 2^31).
+ * Rows of X and of W^T whose range does not contain 0 saturate in the
+ * quantizer (see bgt_quantize_act): y is then the expansion's value for the
+ * saturated codes.
  */
 int bgt_w8a8_gemm_zp(const uint8_t* qx, const float* sx, const int32_t* zx,
                      const int32_t* rowsum_x, const uint8_t* qw, const float* sw,
@@ -359,7 +388,8 @@ const char* bgt_status_string(int status);
  * integer-scale entry points, 102 the fused linear layer, 103 fp16 / bf16
  * activation and output types, 104 the fine-grained W8A8 integer-scale GEMM,
  * 105 the grouped (mixture-of-experts) W4A8 integer-scale GEMM, 106 the
- * expert count and slot count in bgt_w4a8_moe_kernel_name. */
+ * expert count and slot count in bgt_w4a8_moe_kernel_name, 107 the canonical
+ * int4 layout (bgt_repack_int4_canonical). */
 int bgt_abi_version(void);
 
 /* Diagnostics: name of the GEMM kernel that bgt_w4a8_gemm_is (float_scale = 0)

@@ -59,6 +59,8 @@ def _load():
         lib.orc_weight_mse_is_fs.restype = ctypes.c_double
         lib.orc_pack_int4.argtypes = [P, I64, I64, P]
         lib.orc_unpack_int4.argtypes = [P, I64, I64, P]
+        lib.orc_pack_int4_canonical.argtypes = [P, I64, I64, P]
+        lib.orc_unpack_int4_canonical.argtypes = [P, I64, I64, P]
         lib.orc_w4a8_gemm_is.argtypes = [P, P, P, P, I, I64, I64, I64, I64, P, I64, P, I64, P, P]
         lib.orc_w4a8_gemm_is.restype = I64
         lib.orc_w4a8_gemm_fs.argtypes = [P, P, P, P, I64, I64, I64, I64, P, I64, P, I64, P]
@@ -214,6 +216,23 @@ def unpack_int4(packed, K: int, N: int):
     packed = _c(packed, np.uint8)
     out = np.empty((K, N), np.int8)
     _load().orc_unpack_int4(_p(packed), K, N, _p(out))
+    return out
+
+
+def pack_int4_canonical(codes):
+    """K x N int4 codes in the canonical layout: W^T, K contiguous, two codes
+    per byte with even k in the low nibble (N*K/2 bytes)."""
+    codes = _c(codes, np.int8)
+    K, N = codes.shape
+    out = np.empty(N * K // 2, np.uint8)
+    _load().orc_pack_int4_canonical(_p(codes), K, N, _p(out))
+    return out
+
+
+def unpack_int4_canonical(packed, K: int, N: int):
+    packed = _c(packed, np.uint8)
+    out = np.empty((K, N), np.int8)
+    _load().orc_unpack_int4_canonical(_p(packed), K, N, _p(out))
     return out
 
 

@@ -320,6 +320,33 @@ EXPORT void orc_unpack_int4(const uint8_t* packed, int64_t K, int64_t N, int8_t*
         }
 }
 
+/* Canonical int4 layout (the "data packing" of the apxml extreme-quantization
+ * page, 实现与评估考量: several low-bit codes stored in one standard byte; the
+ * order is this library's reading): the codes of W^T, K contiguous per output
+ * column, two per byte, even k in the low nibble:
+ *     byte(k, j) = (j*K + k) / 2,   nibble = k % 2 (0 = low),
+ * 4-bit two's complement. */
+EXPORT void orc_pack_int4_canonical(const int8_t* codes, int64_t K, int64_t N, uint8_t* out)
+{
+    memset(out, 0, (size_t)(N * K / 2));
+    for (int64_t j = 0; j < N; ++j)
+        for (int64_t k = 0; k < K; ++k) {
+            const int64_t b = (j * K + k) / 2;
+            const uint8_t nib = (uint8_t)(codes[k * N + j] & 0xF);
+            out[b] |= (k % 2) ? (uint8_t)(nib << 4) : nib;
+        }
+}
+
+EXPORT void orc_unpack_int4_canonical(const uint8_t* in, int64_t K, int64_t N, int8_t* codes)
+{
+    for (int64_t j = 0; j < N; ++j)
+        for (int64_t k = 0; k < K; ++k) {
+            const uint8_t byte = in[(j * K + k) / 2];
+            const int nib = (k % 2) ? (byte >> 4) & 0xF : byte & 0xF;
+            codes[k * N + j] = (int8_t)(nib >= 8 ? nib - 16 : nib);
+        }
+}
+
 /* Int8 fragment layout of the fine-grained W8A8 weights (the byte formula
  * stated with bgt_pack_weights_int8): for t = j/16, c = j%16, l = k/128,
  * r = k%128, h = r/64, s = (r%64)/16, e = r%16,

@@ -37,7 +37,7 @@ def test_status_strings(L):
     assert bgt.status_string(0) == "ok"
     for st in (-1, -2, -3, -4, -5, -6, -7, 1):
         assert "error" in bgt.status_string(st) or "warning" in bgt.status_string(st)
-    assert L.bgt_abi_version() == 106
+    assert L.bgt_abi_version() == 107
 
 
 def test_quantize_act_validation(L):
@@ -158,6 +158,18 @@ def test_narrow_iscale_validation(L):
     assert n(FAKE, 0, 1, FAKE, None) == bgt.BGT_ERR_SHAPE
     assert n(MIS, 64, 2, FAKE, None) == bgt.BGT_ERR_ALIGN
     assert n(FAKE, 64, 2, MIS, None) == bgt.BGT_ERR_ALIGN
+
+
+def test_repack_canonical_validation(L):
+    r = L.bgt_repack_int4_canonical
+    assert r(None, 256, 32, FAKE, None) == bgt.BGT_ERR_NULL
+    assert r(FAKE, 256, 32, None, None) == bgt.BGT_ERR_NULL
+    assert r(FAKE, 200, 32, FAKE, None) == bgt.BGT_ERR_SHAPE     # K not a multiple of 128
+    assert r(FAKE, 0, 32, FAKE, None) == bgt.BGT_ERR_SHAPE
+    assert r(FAKE, 256, 24, FAKE, None) == bgt.BGT_ERR_SHAPE     # N not a multiple of 16
+    assert r(FAKE, 131072, 32, FAKE, None) == bgt.BGT_ERR_SHAPE
+    assert r(MIS, 256, 32, FAKE, None) == bgt.BGT_ERR_ALIGN
+    assert r(FAKE, 256, 32, MIS, None) == bgt.BGT_ERR_ALIGN
 
 
 def test_gemm_fs_validation(L):

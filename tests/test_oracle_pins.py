@@ -107,6 +107,18 @@ def test_asym_min_max_map_to_ends(orc):
     assert np.all(ok | (q == 255))
 
 
+def test_asym_one_sided_row_saturates(orc):
+    # the raw-range reading: a row whose values are all positive gets s = (max - min)/255
+    # and z = clip(round(-min/s), 0, 255) = 0, so codes above (max - min)/s saturate at 255;
+    # the header states the precondition (the row range must contain 0) for the W8A8 control
+    x = np.array([[1.0, 2.0, 3.0, 4.0]], np.float32)
+    q, s, z, rs = orc.quant_asym_u8(x)
+    assert s[0] == np.float32(3.0) / np.float32(255.0) and z[0] == 0
+    assert q.tolist() == [[85, 170, 255, 255]]
+    xh = s[0] * (q.astype(np.float64) - z[0])
+    assert abs(xh[0, 3] - 4.0) > 0.5                     # not representable: saturated
+
+
 def test_asym_degenerate_row(orc):
     x = np.full((1, 16), 3.0, np.float32)
     q, s, z, rs = orc.quant_asym_u8(x)
@@ -190,24 +202,51 @@ def test_pack_twos_complement(orc):
     assert p[0] == 0x8F
 
 
+def test_canonical_layout_byte_positions(orc):
+    # byte (j*K + k)/2, even k low nibble, odd k high nibble, two's complement
+    K, N = 256, 32
+    for (k, j, v) in [(0, 0, 1), (1, 0, -1), (2, 1, 7), (255, 31, -8), (128, 5, 3), (77, 9, -2)]:
+        codes = np.zeros((K, N), np.int8)
+        codes[k, j] = v
+        p = orc.pack_int4_canonical(codes)
+        b = (j * K + k) // 2
+        nz = np.flatnonzero(p)
+        assert nz.tolist() == [b]
+        want = (v & 0xF) << 4 if k % 2 else v & 0xF
+        assert int(p[b]) == want
+
+
+def test_canonical_layout_round_trip_and_native(orc):
+    g = synth.rng(11, 3)
+    codes = g.integers(-8, 8, size=(384, 48)).astype(np.int8)
+    can = orc.pack_int4_canonical(codes)
+    assert can.size == 384 * 48 // 2
+    np.testing.assert_array_equal(orc.unpack_int4_canonical(can, 384, 48), codes)
+    # both layouts hold the same codes: unpacking either gives the matrix back
+    np.testing.assert_array_equal(orc.unpack_int4(orc.pack_int4(codes), 384, 48), codes)
+    # a column's 16-code runs are contiguous 8-byte runs in the canonical layout
+    j, k0 = 7, 192
+    run = can[(j * 384 + k0) // 2:(j * 384 + k0) // 2 + 8]
+    lo, hi = (run & 0xF).astype(np.int8), (run >> 4).astype(np.int8)
+    vals = np.empty(16, np.int8)
+    vals[0::2], vals[1::2] = lo, hi
+    vals = np.where(vals >= 8, vals - 16, vals)
+    np.testing.assert_array_equal(vals, codes[k0:k0 + 16, j])
+
+
 # --------------------------------------------------------------- amplifier search
 
-def _search_as_printed(scale_min):
-    # the procedure printed on the [IS] 方法 page, executed as written
-    n, tmp = 0, scale_min
-    while tmp < 1:
-        tmp = scale_min * (2 ** n)
-        n += 1
-    return 2 ** (n - 1)
-
-
 @pytest.mark.parametrize("smin", [0.3, 2.0 ** -10, 0.001, 0.0009, 0.5, 0.75, 2.0 ** -20 * 1.5, 0.999])
-def test_amplifier_matches_printed_search(orc, smin):
+def test_amplifier_follows_search_rule(orc, smin):
+    # the rule the page states: the smallest power of two, from 2^0 up, that brings the
+    # smallest (nonzero) scale to at least 1
+    rule = golden("amplifier_rule.txt")
     f = np.array([[smin, 0.9, 5.0], [0.0, 1.0, 0.4 + smin]], np.float32)
     n = orc.amplifier_log2(f)
-    assert 2 ** n == _search_as_printed(float(np.float32(smin)))
     s = float(np.float32(smin))
-    assert s * 2 ** n >= 1 and s * 2 ** (n - 1) < 1           # smallest such power
+    assert n >= rule["min_exponent"]
+    assert s * 2 ** n >= rule["stop_threshold"]
+    assert n == rule["min_exponent"] or s * 2 ** (n - 1) < rule["stop_threshold"]
 
 
 def test_amplifier_closed_form_sweep(orc):
@@ -218,8 +257,8 @@ def test_amplifier_closed_form_sweep(orc):
 
 
 def test_amplifier_edges(orc):
-    # scales already >= 1: the printed code would return 2^-1; the text says the
-    # search starts from 1, so the amplifier is 1. Zero scales are ignored.
+    # scales already >= 1: the search starts from 2^0, so the amplifier is 1.
+    # Zero scales are ignored.
     assert orc.amplifier_log2(np.array([1.0, 3.0], np.float32)) == 0
     assert orc.amplifier_log2(np.array([0.0, 0.0], np.float32)) == 0
     assert orc.amplifier_log2(np.array([0.0, 0.25], np.float32)) == 2
