@@ -21,6 +21,7 @@ and _narrow C variants are reached through the dtype of the tensors passed):
     pack_weights_int8(w, alpha=0)          -> dict(qw, fscale, iscale, alpha, status)
     w8a8_gemm_is(qx, sx, qw, iscale, alpha, N)       -> y
     w4a8_kernel_name / w8a8_is_kernel_name / w4a8_moe_kernel_name -> kernel a shape runs
+    set_prefill_kernel("auto" | "wide" | "tiled")   tile kernel of the W4A8 GEMMs for M > 64
 """
 from __future__ import annotations
 
@@ -53,6 +54,7 @@ EXPORTED = (
     "bgt_quantize_act_ex", "bgt_w4a8_gemm_is_ex", "bgt_w4a8_gemm_fs_ex",
     "bgt_pack_weights_int8", "bgt_w8a8_gemm_is", "bgt_w8a8_is_kernel_name",
     "bgt_w4a8_moe_gemm_is", "bgt_w4a8_moe_kernel_name", "bgt_repack_int4_canonical",
+    "bgt_set_prefill_kernel",
 )
 _NAMES = ("bgt_status_string", "bgt_w4a8_kernel_name", "bgt_w8a8_is_kernel_name",
           "bgt_w4a8_moe_kernel_name")
@@ -98,6 +100,7 @@ def lib():
                                            P, P]
         L.bgt_w4a8_moe_kernel_name.argtypes = [I64, I64, I64, I64]
         L.bgt_repack_int4_canonical.argtypes = [P, I64, I64, P, P]
+        L.bgt_set_prefill_kernel.argtypes = [I]
         for f in EXPORTED:
             getattr(L, f).restype = ctypes.c_char_p if f in _NAMES else I
         _lib = L
@@ -106,6 +109,17 @@ def lib():
 
 def status_string(status: int) -> str:
     return lib().bgt_status_string(int(status)).decode()
+
+
+PREFILL_KERNELS = {"auto": 0, "wide": 1, "tiled": 2}
+
+
+def set_prefill_kernel(mode: str = "auto"):
+    """Tile kernel of the dense W4A8 GEMMs for M > 64: "auto" (by launch
+    rounds), "wide" (256 x 256 tiles) or "tiled" (256 x 128). Process-wide."""
+    if mode not in PREFILL_KERNELS:
+        raise ValueError(f"mode must be one of {sorted(PREFILL_KERNELS)}")
+    _raise("bgt_set_prefill_kernel", lib().bgt_set_prefill_kernel(PREFILL_KERNELS[mode]))
 
 
 def w4a8_kernel_name(M: int, N: int, K: int, float_scale: bool = False) -> str:

@@ -44,7 +44,7 @@ int searched_alpha_log2(float smin) {
 
 extern "C" {
 
-int bgt_abi_version(void) { return 107; }
+int bgt_abi_version(void) { return 108; }
 
 int bgt_w4a8_linear_fused(int64_t M, int64_t K, const void* x, int64_t ldx) {
   return bgt::w4a8_linear_fused(M, K, x, ldx) ? 1 : 0;
@@ -55,6 +55,10 @@ const char* bgt_w4a8_kernel_name(int64_t M, int64_t N, int64_t K, int float_scal
   return bgt::w4a8_kernel_name(M, N, K, float_scale != 0);
 }
 
+int bgt_set_prefill_kernel(int mode) {
+  return bgt::set_prefill_kernel(mode) == 0 ? BGT_OK : BGT_ERR_MODE;
+}
+
 const char* bgt_status_string(int status) {
   switch (status) {
     case BGT_OK: return "ok";
@@ -63,7 +67,7 @@ const char* bgt_status_string(int status) {
     case BGT_ERR_SHAPE: return "error: size out of range or not a required multiple";
     case BGT_ERR_ALIGN: return "error: pointer or leading dimension misaligned";
     case BGT_ERR_ALPHA: return "error: amplifier must be a power of two in [1, 2^30]";
-    case BGT_ERR_MODE: return "error: unknown quantization mode, element type or scale width";
+    case BGT_ERR_MODE: return "error: unknown quantization mode, element type, scale width or kernel choice";
     case BGT_ERR_HIP: return "error: HIP call failed";
     case BGT_ERR_RANGE: return "error: integer scale out of range (pack: >= 2^23; narrow: above the element type)";
     default: return "unknown status";

@@ -18,6 +18,7 @@
 // The K order inside one MFMA does not matter as long as A and B use the same
 // one (it is a dot product), which is what lets the packed weight layout put
 // each lane's 16 bytes next to each other.
+#include <atomic>
 #include <mutex>
 #include <type_traits>
 #include <vector>
@@ -1222,12 +1223,47 @@ static bool decode_padded(int G, int N, int mr) {
   return (G == 86 || G == 112) && mr == 1 && decode_waves(N / 16, mr) <= 4;
 }
 
-// rows from which the 256 x 256 tile kernel takes over from the 256 x 128 one
-constexpr int kWideMinM = 1024;
+// Large M (> 64): the 256 x 256 tile kernel or the 256 x 128 one. Both run
+// one workgroup per CU (their LDS rings fill a CU), so a launch takes
+// ceil(tiles / CUs) rounds; at K = 4096 a round costs about 80 us for the
+// 256 x 256 tiles and about 48 us for the 256 x 128 ones (N = 22016, M = 256
+// .. 4096), so the wide kernel is taken when 5 * its rounds <= 3 * the other's.
+// set_prefill_kernel() forces one of them (benchmarks, tests).
+static std::atomic<int> g_prefill_kernel{0};        // PrefillKernel
+
+static int device_cus() {
+  static std::atomic<int> cached{0};
+  int n = cached.load();
+  if (n > 0) return n;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) {
+    (void)hipGetLastError();
+    return 256;                                      // MI355X; planning without a device
+  }
+  cached.store(n);
+  return n;
+}
+
+static bool wide_tiles_win(int M, int N) {
+  const int64_t cus = device_cus(), tm = (M + 255) / 256;
+  const int64_t rw = (tm * ((N + 255) / 256) + cus - 1) / cus;
+  const int64_t rt = (tm * ((N + 127) / 128) + cus - 1) / cus;
+  return 5 * rw <= 3 * rt;
+}
+
+int set_prefill_kernel(int mode) {
+  if (mode < kPrefillAuto || mode > kPrefillTiled) return -1;
+  g_prefill_kernel.store(mode);
+  return 0;
+}
 
 static W4Plan plan_w4a8(int M, int N, int K, bool fs) {
-  if (M >= kWideMinM) return {W4Path::Wide, 0};
-  if (M > 64) return {W4Path::Tiled, 0};
+  if (M > 64) {
+    const int f = g_prefill_kernel.load();
+    const bool wide = f == kPrefillWide || (f == kPrefillAuto && wide_tiles_win(M, N));
+    return {wide ? W4Path::Wide : W4Path::Tiled, 0};
+  }
   const int mr = (M + 15) / 16, G = K / kGroup;
   if (G == 16 || G == 32 || decode_padded(G, N, mr)) return {W4Path::Decode, mr};
   int gpw = 0, maxt = 0;

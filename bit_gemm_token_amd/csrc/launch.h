@@ -59,6 +59,11 @@ hipError_t launch_narrow_scales(const int32_t* in, int64_t count, int out_bytes,
 // name of the kernel a W4A8 GEMM of this shape dispatches to (diagnostics)
 const char* w4a8_kernel_name(int64_t M, int64_t N, int64_t K, bool float_scale);
 
+// large-M W4A8 kernel choice: automatic, or forced to the 256 x 256 / 256 x 128
+// tile kernel; returns 0, or -1 for an unknown mode
+enum PrefillKernel { kPrefillAuto = 0, kPrefillWide = 1, kPrefillTiled = 2 };
+int set_prefill_kernel(int mode);
+
 // grouped (mixture-of-experts) W4A8 integer-scale GEMM: E experts' packed
 // weights and scales back to back; slots sorted by expert (offs: E+1 offsets,
 // tok: the activation row of each of the R slots); y has R rows

@@ -389,13 +389,28 @@ const char* bgt_status_string(int status);
  * activation and output types, 104 the fine-grained W8A8 integer-scale GEMM,
  * 105 the grouped (mixture-of-experts) W4A8 integer-scale GEMM, 106 the
  * expert count and slot count in bgt_w4a8_moe_kernel_name, 107 the canonical
- * int4 layout (bgt_repack_int4_canonical). */
+ * int4 layout (bgt_repack_int4_canonical), 108 bgt_set_prefill_kernel. */
 int bgt_abi_version(void);
 
 /* Diagnostics: name of the GEMM kernel that bgt_w4a8_gemm_is (float_scale = 0)
  * or bgt_w4a8_gemm_fs (float_scale = 1) launches for this shape, as it
  * appears in profiler traces (static storage; "invalid shape" if rejected). */
 const char* bgt_w4a8_kernel_name(int64_t M, int64_t N, int64_t K, int float_scale);
+
+/* Tuning / testing control (no page defines it): which tile kernel the dense
+ * W4A8 GEMMs (integer and float scale) take for M > 64. Both compute the same
+ * bits; they differ only in speed.
+ *   BGT_PREFILL_AUTO  (default) the 256 x 256 tile kernel when its launch takes
+ *                     few enough rounds of one workgroup per CU (5 * its
+ *                     rounds <= 3 * the 256 x 128 kernel's), else 256 x 128;
+ *   BGT_PREFILL_WIDE  always the 256 x 256 tile kernel;
+ *   BGT_PREFILL_TILED always the 256 x 128 tile kernel.
+ * Process-wide; takes effect for GEMMs launched after the call (set it before
+ * capturing a graph). Returns BGT_OK, or BGT_ERR_MODE for another value. */
+#define BGT_PREFILL_AUTO 0
+#define BGT_PREFILL_WIDE 1
+#define BGT_PREFILL_TILED 2
+int bgt_set_prefill_kernel(int mode);
 
 #ifdef __cplusplus
 }

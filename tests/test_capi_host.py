@@ -37,7 +37,7 @@ def test_status_strings(L):
     assert bgt.status_string(0) == "ok"
     for st in (-1, -2, -3, -4, -5, -6, -7, 1):
         assert "error" in bgt.status_string(st) or "warning" in bgt.status_string(st)
-    assert L.bgt_abi_version() == 107
+    assert L.bgt_abi_version() == 108
 
 
 def test_quantize_act_validation(L):
@@ -255,6 +255,32 @@ def test_w8a8_is_validation(L):
     assert w4(1, 4096, 12288) != "k_w4a8_decode<IS>"  # 96 groups: not a decode shape
     assert w4(65, 4096, 11008) == "k_w4a8_prefill<4,2,2,2,IS>"
     assert w4(16, 4096, 11008, True) == "k_w4a8_decode<FS>"
+
+
+def test_prefill_kernel_choice(L):
+    # M > 64, N = 22016 on 256 CUs: 256 x 256 tiles when 5 * their launch
+    # rounds <= 3 * those of the 256 x 128 tiles (M = 512: 1 vs 2 rounds;
+    # 1024: 2 vs 3; 1536: 3 vs 5; 2048: 3 vs 6; 4096: 6 vs 11)
+    w4 = bgt.w4a8_kernel_name
+    wide, tiled = "k_w4a8_wide<IS>", "k_w4a8_prefill<4,2,2,2,IS>"
+    try:
+        assert [w4(M, 22016, 4096) for M in (256, 512, 1024, 1536, 2048, 4096)] == \
+            [tiled, wide, tiled, wide, wide, wide]
+        assert w4(4096, 256, 4096) == tiled              # 16 vs 32 tiles: one round each
+        assert w4(2048, 22016, 4096, True) == "k_w4a8_wide<FS>"
+        assert w4(64, 22016, 4096) == "k_w4a8_decode<IS>"     # the decode range is unaffected
+        bgt.set_prefill_kernel("wide")
+        assert w4(65, 256, 128) == wide and w4(1024, 22016, 4096) == wide
+        assert w4(16, 22016, 4096) == "k_w4a8_decode<IS>"
+        bgt.set_prefill_kernel("tiled")
+        assert w4(4096, 22016, 4096) == tiled and w4(4096, 22016, 4096, True) == "k_w4a8_prefill<4,2,2,2,FS>"
+        assert L.bgt_set_prefill_kernel(3) == bgt.BGT_ERR_MODE
+        assert L.bgt_set_prefill_kernel(-1) == bgt.BGT_ERR_MODE
+        with pytest.raises(ValueError):
+            bgt.set_prefill_kernel("fast")
+    finally:
+        bgt.set_prefill_kernel("auto")
+    assert w4(1024, 22016, 4096) == tiled
 
 
 def test_moe_validation(L):

@@ -1,6 +1,7 @@
 """GPU parity of the large-M W4A8 kernel (256 x 256 output tiles) against the oracle.
 
-The kernel runs for M >= 1024. Cases span several tiles with ragged rows and
+The module forces that kernel for every M > 64 (bgt_set_prefill_kernel), so
+small shapes reach it too. Cases span several tiles with ragged rows and
 ragged column tiles (N not a multiple of 256, down to one 16-column tile),
 group counts of 1, 2, 3, 5 and 32 (the pipeline's three stages wrap at
 different points), integer scales of 4, 2 and 1 bytes, the float-scale
@@ -28,7 +29,9 @@ def dev():
 def bgt():
     import bit_gemm_token_amd
     bit_gemm_token_amd.lib()
-    return bit_gemm_token_amd
+    bit_gemm_token_amd.set_prefill_kernel("wide")
+    yield bit_gemm_token_amd
+    bit_gemm_token_amd.set_prefill_kernel("auto")
 
 
 def say(*a):
