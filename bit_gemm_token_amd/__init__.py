@@ -22,6 +22,7 @@ and _narrow C variants are reached through the dtype of the tensors passed):
     w8a8_gemm_is(qx, sx, qw, iscale, alpha, N)       -> y
     w4a8_kernel_name / w8a8_is_kernel_name / w4a8_moe_kernel_name -> kernel a shape runs
     set_prefill_kernel("auto" | "wide" | "tiled")   tile kernel of the W4A8 GEMMs for M > 64
+    w4a8_workspace_bytes(M, N, K)          -> split-K workspace the integer-scale GEMM uses
 """
 from __future__ import annotations
 
@@ -54,7 +55,7 @@ EXPORTED = (
     "bgt_quantize_act_ex", "bgt_w4a8_gemm_is_ex", "bgt_w4a8_gemm_fs_ex",
     "bgt_pack_weights_int8", "bgt_w8a8_gemm_is", "bgt_w8a8_is_kernel_name",
     "bgt_w4a8_moe_gemm_is", "bgt_w4a8_moe_kernel_name", "bgt_repack_int4_canonical",
-    "bgt_set_prefill_kernel",
+    "bgt_set_prefill_kernel", "bgt_w4a8_workspace_bytes",
 )
 _NAMES = ("bgt_status_string", "bgt_w4a8_kernel_name", "bgt_w8a8_is_kernel_name",
           "bgt_w4a8_moe_kernel_name")
@@ -101,8 +102,10 @@ def lib():
         L.bgt_w4a8_moe_kernel_name.argtypes = [I64, I64, I64, I64]
         L.bgt_repack_int4_canonical.argtypes = [P, I64, I64, P, P]
         L.bgt_set_prefill_kernel.argtypes = [I]
+        L.bgt_w4a8_workspace_bytes.argtypes = [I64, I64, I64]
         for f in EXPORTED:
             getattr(L, f).restype = ctypes.c_char_p if f in _NAMES else I
+        L.bgt_w4a8_workspace_bytes.restype = I64
         _lib = L
     return _lib
 
@@ -120,6 +123,13 @@ def set_prefill_kernel(mode: str = "auto"):
     if mode not in PREFILL_KERNELS:
         raise ValueError(f"mode must be one of {sorted(PREFILL_KERNELS)}")
     _raise("bgt_set_prefill_kernel", lib().bgt_set_prefill_kernel(PREFILL_KERNELS[mode]))
+
+
+def w4a8_workspace_bytes(M: int, N: int, K: int) -> int:
+    """Device workspace (bytes) the integer-scale W4A8 GEMM uses at this shape."""
+    r = lib().bgt_w4a8_workspace_bytes(M, N, K)
+    _raise("bgt_w4a8_workspace_bytes", r if r < 0 else 0)
+    return r
 
 
 def w4a8_kernel_name(M: int, N: int, K: int, float_scale: bool = False) -> str:

@@ -55,6 +55,12 @@ const char* bgt_w4a8_kernel_name(int64_t M, int64_t N, int64_t K, int float_scal
   return bgt::w4a8_kernel_name(M, N, K, float_scale != 0);
 }
 
+int64_t bgt_w4a8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  const int st = check_gemm_shape(M, N, K, 65536);
+  if (st != BGT_OK) return st;
+  return (int64_t)bgt::w4a8_split_bytes(M, N, K, false);
+}
+
 int bgt_set_prefill_kernel(int mode) {
   return bgt::set_prefill_kernel(mode) == 0 ? BGT_OK : BGT_ERR_MODE;
 }

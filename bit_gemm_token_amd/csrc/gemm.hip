@@ -362,7 +362,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
     const int8_t* __restrict__ qx, const float* __restrict__ sx,
     const uint4* __restrict__ packed, const ST* __restrict__ iscale,
     const float* __restrict__ fscale, float inv_alpha, int M, int N, int K,
-    OutY y, int32_t* __restrict__ acc_out, Route rt) {
+    OutY y, int32_t* __restrict__ acc_out, Route rt, int splits, int32_t* __restrict__ part) {
   static_assert(TMW == 2 && TNW == 2, "four 32 x 32 blocks per wave");
   constexpr int NW = WM * WN, NT = NW * 64;
   constexpr int BM = WM * TMW * 32, BN = WN * TNW * 32, NB = TMW * TNW;
@@ -381,7 +381,14 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
   __shared__ __align__(16) uint4 SP1[BN * 4];
   __shared__ __align__(16) uint4 SP2[BN * 4];
 
-  const int G = K / kGroup, T = N / 16;
+  // split K (integer scale only): workgroup id = ks * tiles + tile; split ks
+  // runs groups g0 .. g0+G-1 = [ks*GT/splits, (ks+1)*GT/splits) and leaves its
+  // integer-scaled int32 sums in part[ks] (M x N) for k_split_reduce
+  const int GT = K / kGroup, T = N / 16;
+  const int ntiles = (int)gridDim.x / splits;
+  const int ks = (int)blockIdx.x / ntiles, tb = (int)blockIdx.x - ks * ntiles;
+  const int g0 = (int)((int64_t)ks * GT / splits);
+  const int G = (int)((int64_t)(ks + 1) * GT / splits) - g0;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave;
@@ -391,7 +398,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
   // grouped GEMM: the grid covers ceil(R/BM) + E row tiles, an upper bound on
   // the sum over experts of ceil(rows/BM); row tile tm is found in the list of
   // the experts' tiles (experts in order), and tiles past its end exit
-  tile_of(blockIdx.x, GR ? (rt.R + BM - 1) / BM + rt.E : (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
+  tile_of(tb, GR ? (rt.R + BM - 1) / BM + rt.E : (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
   int r0 = 0;
   if constexpr (GR) {
     int e = 0, a = 0;
@@ -444,10 +451,10 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
   for (int u = 0; u < B_CH; ++u) {
     const int q = tid + NT * u, tl = q / 64, lb = q % 64;
     const int tg = n0 / 16 + tl < T ? n0 / 16 + tl : T - 1;
-    bsrc[u] = packed + (int64_t)tg * G * 64 + lb;
+    bsrc[u] = packed + (int64_t)tg * GT * 64 + lb;
   }
   auto issue_group = [&](int g, int8_t* SA, uint4* SP) {
-    const int gc = g < G ? g : G - 1;
+    const int gc = (g < G ? g : G - 1) + g0;
     const int8_t* base = abase + (int64_t)gc * kGroup;
 #pragma unroll
     for (int i = 0; i < A_INSTR; ++i)
@@ -606,6 +613,21 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
   epilogue(IC<NB - 1>{}, pc[(NB - 1) % 2], spc);
   wait_vm_lds0<0>();                                // surplus copies of the last steps
 
+  if (!FS && part != nullptr) {                     // split K: this split's sums
+    int32_t* pp = part + (int64_t)ks * M * N;
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const int a = k / TNW, b = k % TNW;
+      const int j = n0 + wn * (TNW * 32) + b * 32 + lr;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = m0 + wm * (TMW * 32) + a * 32 + 8 * (r / 4) + 4 * hf + (r % 4);
+        if (i < M && j < N) pp[(int64_t)i * N + j] = acc[k][r];
+      }
+    }
+    return;
+  }
+
   // ---- one conversion per output. The lane's 32 token scales are loaded
   // first (row indices clamped), so the stores below need no waits; full
   // tiles store without per-element predicates.
@@ -637,6 +659,27 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
       }
     }
   }
+}
+
+// Split-K reduction of the 256 x 128 tile kernel: out = sum of the splits'
+// integer-scaled int32 sums (exact mod 2^32 in any order), then the one
+// conversion per output as in the GEMM epilogue. Four consecutive outputs
+// (one row: N is a multiple of 16) per thread.
+__global__ __launch_bounds__(256) void k_split_reduce(const int32_t* __restrict__ part, int splits,
+                                                      int64_t MN, int N, const float* __restrict__ sx,
+                                                      float inv_alpha, OutY y,
+                                                      int32_t* __restrict__ acc_out) {
+  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e >= MN) return;
+  v4i a = *reinterpret_cast<const v4i*>(part + e);
+  for (int k = 1; k < splits; ++k) a += *reinterpret_cast<const v4i*>(part + k * MN + e);
+  const float si = sx[e / N];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float t0 = (float)a[r] * si;
+    y.put(e + r, t0 * inv_alpha);
+  }
+  if (acc_out) *reinterpret_cast<v4i*>(acc_out + e) = a;
 }
 
 // =====================================================================
@@ -1380,10 +1423,64 @@ static void launch_decode(int mr, hipStream_t stream, const int8_t* qx, const fl
   }
 }
 
+// Split K of the 256 x 128 tile kernel (integer scale): when its tiles fill
+// at most half of the CUs, the groups are split in 2, 4, ... (at least 4
+// groups per split) while the workgroups still fit the CUs once; the splits'
+// int32 sums meet in k_split_reduce. The float-scale control keeps one
+// ascending fma chain per output (its rounding depends on the order).
+static int split_count(int M, int N, int K) {
+  const int64_t tiles = (int64_t)((M + 255) / 256) * ((N + 127) / 128), cus = device_cus();
+  const int G = K / kGroup;
+  int s = 1;
+  while (tiles * s * 2 <= cus && s * 2 * 4 <= G) s *= 2;
+  return s;
+}
+
+size_t w4a8_split_bytes(int64_t M, int64_t N, int64_t K, bool float_scale) {
+  if (float_scale || plan_w4a8((int)M, (int)N, (int)K, false).path != W4Path::Tiled) return 0;
+  const int s = split_count((int)M, (int)N, (int)K);
+  return s > 1 ? (size_t)s * (size_t)M * (size_t)N * sizeof(int32_t) : 0;
+}
+
+// The library's split-K workspace: one buffer per device, grown on demand
+// (never while the stream is being captured into a graph: such a launch runs
+// unsplit unless the buffer is already large enough). nullptr if unavailable.
+static int32_t* split_workspace(size_t bytes, hipStream_t stream) {
+  struct Buf { int dev; void* p; size_t n; };
+  static std::mutex mu;
+  static std::vector<Buf> bufs;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> g(mu);
+  Buf* b = nullptr;
+  for (Buf& x : bufs)
+    if (x.dev == dev) b = &x;
+  if (b != nullptr && b->n >= bytes) return static_cast<int32_t*>(b->p);
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  const size_t n = (bytes + (16u << 20) - 1) & ~((size_t)(16u << 20) - 1);
+  void* p = nullptr;
+  if (hipMalloc(&p, n) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (b != nullptr) {
+    (void)hipFree(b->p);                           // waits for the device; earlier users are done
+    b->p = p;
+    b->n = n;
+  } else {
+    bufs.push_back({dev, p, n});
+  }
+  return static_cast<int32_t*>(p);
+}
+
 template <bool FS, typename ST>
 static void launch_w4a8_t(const int8_t* qx, const float* sx, const uint8_t* packed,
                           const ST* iscale, const float* fscale, float inv_alpha, int M, int N,
-                          int K, OutY y, int32_t* acc_out, hipStream_t stream) {
+                          int K, OutY y, int32_t* acc_out, hipStream_t stream, int32_t* ws) {
   const W4Plan plan = plan_w4a8(M, N, K, FS);
   if (FS) acc_out = nullptr;
   if (plan.path == W4Path::Decode) {
@@ -1401,32 +1498,44 @@ static void launch_w4a8_t(const int8_t* qx, const float* sx, const uint8_t* pack
   } else if (plan.path != W4Path::Tiled) {
     launch_small_m<FS>(plan, qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream);
   } else {
-    // 256 x 128 tiles, 8 waves of 64 x 64
+    // 256 x 128 tiles, 8 waves of 64 x 64; split K when the tiles are few
     const uint4* pk = reinterpret_cast<const uint4*>(packed);
     const int tiles = ((M + 255) / 256) * ((N + 127) / 128);
-    hipLaunchKernelGGL((k_w4a8_prefill<4, 2, 2, 2, FS, ST>), dim3(tiles), dim3(512), 0, stream,
-                       qx, sx, pk, iscale, fscale, inv_alpha, M, N, K, y, acc_out, Route{});
+    int splits = FS ? 1 : split_count(M, N, K);
+    int32_t* part = nullptr;
+    if (splits > 1) {
+      part = ws != nullptr ? ws : split_workspace((size_t)splits * M * N * sizeof(int32_t), stream);
+      if (part == nullptr) splits = 1;
+    }
+    hipLaunchKernelGGL((k_w4a8_prefill<4, 2, 2, 2, FS, ST>), dim3(tiles * splits), dim3(512), 0,
+                       stream, qx, sx, pk, iscale, fscale, inv_alpha, M, N, K, y, acc_out, Route{},
+                       splits, part);
+    if (splits > 1) {
+      const int64_t MN = (int64_t)M * N;
+      hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)((MN / 4 + 255) / 256)), dim3(256), 0,
+                         stream, part, splits, MN, N, sx, inv_alpha, y, acc_out);
+    }
   }
 }
 
 hipError_t launch_w4a8(bool float_scale, const int8_t* qx, const float* sx, const uint8_t* packed,
                        const void* iscale, int iscale_bytes, const float* fscale, int alpha,
                        int64_t M64, int64_t N64, int64_t K64, OutY y, int32_t* acc_out,
-                       hipStream_t stream) {
+                       hipStream_t stream, int32_t* ws) {
   const int M = (int)M64, N = (int)N64, K = (int)K64;
   const float inv_alpha = 1.0f / (float)alpha;   // exact: alpha = 2^n
   if (float_scale)
     launch_w4a8_t<true>(qx, sx, packed, static_cast<const int32_t*>(nullptr), fscale, inv_alpha,
-                        M, N, K, y, nullptr, stream);
+                        M, N, K, y, nullptr, stream, nullptr);
   else if (iscale_bytes == 4)
     launch_w4a8_t<false>(qx, sx, packed, static_cast<const int32_t*>(iscale), nullptr, inv_alpha,
-                         M, N, K, y, acc_out, stream);
+                         M, N, K, y, acc_out, stream, ws);
   else if (iscale_bytes == 2)
     launch_w4a8_t<false>(qx, sx, packed, static_cast<const uint16_t*>(iscale), nullptr, inv_alpha,
-                         M, N, K, y, acc_out, stream);
+                         M, N, K, y, acc_out, stream, ws);
   else
     launch_w4a8_t<false>(qx, sx, packed, static_cast<const uint8_t*>(iscale), nullptr, inv_alpha,
-                         M, N, K, y, acc_out, stream);
+                         M, N, K, y, acc_out, stream, ws);
   return hipGetLastError();
 }
 
@@ -1568,7 +1677,7 @@ static void launch_moe_t(const int8_t* qx, const float* sx, const uint8_t* packe
   }
   const int tiles = ((rt.R + 255) / 256 + rt.E) * ((N + 127) / 128);
   hipLaunchKernelGGL((k_w4a8_prefill<4, 2, 2, 2, false, ST, true>), dim3(tiles), dim3(512), 0,
-                     stream, qx, sx, pk, iscale, nullptr, inv_alpha, 0, N, K, y, acc_out, rt);
+                     stream, qx, sx, pk, iscale, nullptr, inv_alpha, 0, N, K, y, acc_out, rt, 1, nullptr);
 }
 
 hipError_t launch_w4a8_moe(const int8_t* qx, const float* sx, int64_t T, const int32_t* offs,

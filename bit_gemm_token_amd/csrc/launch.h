@@ -31,10 +31,16 @@ hipError_t launch_integer_scales(const float* fscale, int64_t count, int alpha, 
 
 // iscale holds (K/128) x N integer scales of iscale_bytes bytes each (4: int32,
 // 2: uint16, 1: uint8); ignored (and fscale used) when float_scale is set.
+// ws: split-K workspace of at least w4a8_split_bytes() bytes, or nullptr for
+// the library's own (allocated on first need; unavailable while the stream is
+// being captured, when the GEMM runs unsplit).
 hipError_t launch_w4a8(bool float_scale, const int8_t* qx, const float* sx, const uint8_t* packed,
                        const void* iscale, int iscale_bytes, const float* fscale, int alpha,
                        int64_t M, int64_t N, int64_t K, OutY y, int32_t* acc_out,
-                       hipStream_t stream);
+                       hipStream_t stream, int32_t* ws = nullptr);
+
+// bytes of split-K workspace a W4A8 GEMM of this shape uses (0: none)
+size_t w4a8_split_bytes(int64_t M, int64_t N, int64_t K, bool float_scale);
 
 // the large-M W4A8 GEMM (256 x 256 tiles); inv_alpha = 1/alpha (exact)
 void launch_w4a8_wide(bool float_scale, const int8_t* qx, const float* sx, const uint8_t* packed,

@@ -389,7 +389,8 @@ const char* bgt_status_string(int status);
  * activation and output types, 104 the fine-grained W8A8 integer-scale GEMM,
  * 105 the grouped (mixture-of-experts) W4A8 integer-scale GEMM, 106 the
  * expert count and slot count in bgt_w4a8_moe_kernel_name, 107 the canonical
- * int4 layout (bgt_repack_int4_canonical), 108 bgt_set_prefill_kernel. */
+ * int4 layout (bgt_repack_int4_canonical), 108 bgt_set_prefill_kernel and
+ * bgt_w4a8_workspace_bytes. */
 int bgt_abi_version(void);
 
 /* Diagnostics: name of the GEMM kernel that bgt_w4a8_gemm_is (float_scale = 0)
@@ -407,6 +408,18 @@ const char* bgt_w4a8_kernel_name(int64_t M, int64_t N, int64_t K, int float_scal
  *   BGT_PREFILL_TILED always the 256 x 128 tile kernel.
  * Process-wide; takes effect for GEMMs launched after the call (set it before
  * capturing a graph). Returns BGT_OK, or BGT_ERR_MODE for another value. */
+/* Device workspace the integer-scale W4A8 GEMMs (bgt_w4a8_gemm_is, _narrow,
+ * _ex) use for this shape, in bytes: 0 for most shapes; S*M*N*4 when the
+ * 256 x 128 tile kernel splits K into S parts (M > 64 with few tiles: the
+ * tiles fill at most half of the CUs, at least 4 groups per part), whose
+ * int32 sums are then added (exact mod 2^32) by a second kernel. The library
+ * keeps one such buffer per device, allocated on first need and reused; a
+ * GEMM launched while its stream is being captured into a graph does not
+ * allocate and runs unsplit unless the buffer is already large enough.
+ * Calls that overlap on one device (several streams) share the buffer and
+ * race. Negative: the status of an invalid shape. */
+int64_t bgt_w4a8_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
 #define BGT_PREFILL_AUTO 0
 #define BGT_PREFILL_WIDE 1
 #define BGT_PREFILL_TILED 2

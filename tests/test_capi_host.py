@@ -27,7 +27,7 @@ def L():
 def test_header_symbols_exported(L):
     with open(os.path.join(ROOT, "include", "bgt.h")) as f:
         hdr = f.read()
-    declared = set(re.findall(r"^(?:int|const char\*)\s+(bgt_\w+)\s*\(", hdr, re.M))
+    declared = set(re.findall(r"^(?:int|int64_t|const char\*)\s+(bgt_\w+)\s*\(", hdr, re.M))
     assert declared == set(bgt.EXPORTED)
     for name in declared:
         assert getattr(L, name) is not None
@@ -255,6 +255,20 @@ def test_w8a8_is_validation(L):
     assert w4(1, 4096, 12288) != "k_w4a8_decode<IS>"  # 96 groups: not a decode shape
     assert w4(65, 4096, 11008) == "k_w4a8_prefill<4,2,2,2,IS>"
     assert w4(16, 4096, 11008, True) == "k_w4a8_decode<FS>"
+
+
+def test_workspace_bytes():
+    # split K of the 256 x 128 tile kernel on 256 CUs: S doubles while
+    # tiles * 2S <= 256 and 8S <= K/128
+    wb = bgt.w4a8_workspace_bytes                  # (M, N, K)
+    assert wb(512, 4096, 4096) == 4 * 512 * 4096 * 4        # 64 tiles -> 4 splits
+    assert wb(65, 4096, 4096) == 8 * 65 * 4096 * 4          # 32 tiles -> 8 (4 groups each)
+    assert wb(129, 528, 2560) == 4 * 129 * 528 * 4          # 5 tiles, 20 groups -> 4 (5 each)
+    assert wb(512, 4096, 11008) == 4 * 512 * 4096 * 4       # 86 groups, uneven parts
+    assert wb(100, 256, 512) == 0                           # 4 groups: no split
+    assert wb(256, 22016, 4096) == 0                        # 172 tiles
+    assert wb(4096, 22016, 4096) == 0 and wb(64, 22016, 4096) == 0   # wide, decode
+    assert bgt.lib().bgt_w4a8_workspace_bytes(0, 4096, 4096) == bgt.BGT_ERR_SHAPE
 
 
 def test_prefill_kernel_choice(L):
