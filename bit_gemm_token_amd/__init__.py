@@ -55,7 +55,7 @@ EXPORTED = (
     "bgt_quantize_act_ex", "bgt_w4a8_gemm_is_ex", "bgt_w4a8_gemm_fs_ex",
     "bgt_pack_weights_int8", "bgt_w8a8_gemm_is", "bgt_w8a8_is_kernel_name",
     "bgt_w4a8_moe_gemm_is", "bgt_w4a8_moe_kernel_name", "bgt_repack_int4_canonical",
-    "bgt_set_prefill_kernel", "bgt_w4a8_workspace_bytes",
+    "bgt_set_prefill_kernel", "bgt_w4a8_workspace_bytes", "bgt_w4a8_gemm_is_noalloc",
 )
 _NAMES = ("bgt_status_string", "bgt_w4a8_kernel_name", "bgt_w8a8_is_kernel_name",
           "bgt_w4a8_moe_kernel_name")
@@ -103,6 +103,7 @@ def lib():
         L.bgt_repack_int4_canonical.argtypes = [P, I64, I64, P, P]
         L.bgt_set_prefill_kernel.argtypes = [I]
         L.bgt_w4a8_workspace_bytes.argtypes = [I64, I64, I64]
+        L.bgt_w4a8_gemm_is_noalloc.argtypes = [P, P, P, P, I, I64, I64, I64, P, P, P]
         for f in EXPORTED:
             getattr(L, f).restype = ctypes.c_char_p if f in _NAMES else I
         L.bgt_w4a8_workspace_bytes.restype = I64

@@ -44,7 +44,7 @@ int searched_alpha_log2(float smin) {
 
 extern "C" {
 
-int bgt_abi_version(void) { return 108; }
+int bgt_abi_version(void) { return 109; }
 
 int bgt_w4a8_linear_fused(int64_t M, int64_t K, const void* x, int64_t ldx) {
   return bgt::w4a8_linear_fused(M, K, x, ldx) ? 1 : 0;
@@ -188,6 +188,25 @@ int bgt_w4a8_gemm_is_ex(const int8_t* qx, const float* sx, const uint8_t* packed
   return hip_status(bgt::launch_w4a8(false, qx, sx, packed, iscale, width, nullptr, alpha, M, N,
                                      K, bgt::OutY{y, y_type}, acc_out,
                                      static_cast<hipStream_t>(stream)));
+}
+
+int bgt_w4a8_gemm_is_noalloc(const int8_t* qx, const float* sx, const uint8_t* packed,
+                             const int32_t* iscale, int alpha, int64_t M, int64_t N, int64_t K,
+                             float* y, int32_t* acc_out, void* stream) {
+  if (!qx || !sx || !packed || !iscale || !y) return BGT_ERR_NULL;
+  int st = check_gemm_shape(M, N, K, 65536);
+  if (st != BGT_OK) return st;
+  if (!pow2_alpha(alpha)) return BGT_ERR_ALPHA;
+  if (!aligned16(qx) || !aligned16(packed) || !aligned16(iscale) || !aligned16(y) ||
+      (acc_out && !aligned16(acc_out)))
+    return BGT_ERR_ALIGN;
+  size_t cap = 0;
+  int32_t* ws = bgt::noalloc_scratch(&cap);
+  if (bgt::w4a8_split_bytes(M, N, K, false) > cap) return BGT_ERR_SHAPE;
+  if (ws == nullptr) return BGT_ERR_HIP;
+  return hip_status(bgt::launch_w4a8(false, qx, sx, packed, iscale, 4, nullptr, alpha, M, N, K,
+                                     bgt::OutY{y, BGT_F32}, acc_out,
+                                     static_cast<hipStream_t>(stream), ws));
 }
 
 int bgt_w4a8_linear_is(const void* x, int x_type, int64_t ldx, const uint8_t* packed,

@@ -1477,6 +1477,32 @@ static int32_t* split_workspace(size_t bytes, hipStream_t stream) {
   return static_cast<int32_t*>(p);
 }
 
+// Scratch of the no-allocation entry point (bgt_w4a8_gemm_is_noalloc): the
+// split-K sums in a static device array. Each GPU the library runs on holds
+// its own copy, at its own address, until the process ends; host code uses
+// only the address hipGetSymbolAddress returns for the current device, looked
+// up once per device. 32 MiB = 256 CUs x one 256 x 128 int32 tile each, the
+// most a split launch writes on a 256-CU device (tiles x splits <= CUs).
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+__device__ __align__(256) int32_t scratch[kNoAllocScratchBytes / sizeof(int32_t)];
+
+int32_t* noalloc_scratch(size_t* capacity) {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int32_t*> ptrs[kMaxDev];
+  *capacity = kNoAllocScratchBytes;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return nullptr;
+  int32_t* p = ptrs[dev].load();
+  if (p != nullptr) return p;
+  void* a = nullptr;
+  if (hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)) != hipSuccess || a == nullptr) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  ptrs[dev].store(static_cast<int32_t*>(a));
+  return static_cast<int32_t*>(a);
+}
+
 template <bool FS, typename ST>
 static void launch_w4a8_t(const int8_t* qx, const float* sx, const uint8_t* packed,
                           const ST* iscale, const float* fscale, float inv_alpha, int M, int N,

@@ -42,6 +42,10 @@ hipError_t launch_w4a8(bool float_scale, const int8_t* qx, const float* sx, cons
 // bytes of split-K workspace a W4A8 GEMM of this shape uses (0: none)
 size_t w4a8_split_bytes(int64_t M, int64_t N, int64_t K, bool float_scale);
 
+// the no-allocation scratch on the current device (nullptr if its address
+// cannot be obtained) and its size in bytes
+int32_t* noalloc_scratch(size_t* capacity);
+
 // the large-M W4A8 GEMM (256 x 256 tiles); inv_alpha = 1/alpha (exact)
 void launch_w4a8_wide(bool float_scale, const int8_t* qx, const float* sx, const uint8_t* packed,
                       const void* iscale, int iscale_bytes, const float* fscale, float inv_alpha,

@@ -162,6 +162,25 @@ int bgt_w4a8_gemm_is(const int8_t* qx, const float* sx, const uint8_t* packed,
                      float* y, int32_t* acc_out, void* stream);
 
 /*
+ * bgt_w4a8_gemm_is_noalloc -- bgt_w4a8_gemm_is for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same arguments, requirements and
+ * results, computed by the same kernels, and no hipMalloc / hipFree or other
+ * allocating call. Where the GEMM splits K (see bgt_w4a8_workspace_bytes) it
+ * keeps the split sums in a static device array of 32 MiB instead of the
+ * library's workspace; each GPU holds its own copy from the library's load
+ * until the process ends. On a 256-CU device every valid shape fits (a split
+ * launch writes at most one 256 x 128 int32 tile per CU); a shape needing
+ * more returns BGT_ERR_SHAPE, and BGT_ERR_HIP if the array's address cannot
+ * be obtained. Nothing carries over between calls (every split sum read is
+ * first written by the same call), but all calls on one GPU share the array:
+ * calls that overlap on one GPU (several streams or threads) race.
+ */
+int bgt_w4a8_gemm_is_noalloc(const int8_t* qx, const float* sx, const uint8_t* packed,
+                             const int32_t* iscale, int alpha, int64_t M, int64_t N, int64_t K,
+                             float* y, int32_t* acc_out, void* stream);
+
+/*
  * bgt_repack_int4_canonical -- accept int4 weights in the canonical layout.
  * The pages allow any packing of sub-byte codes into standard bytes (the
  * apxml extreme-quantization page, 实现与评估考量, "data packing"); the
@@ -390,7 +409,7 @@ const char* bgt_status_string(int status);
  * 105 the grouped (mixture-of-experts) W4A8 integer-scale GEMM, 106 the
  * expert count and slot count in bgt_w4a8_moe_kernel_name, 107 the canonical
  * int4 layout (bgt_repack_int4_canonical), 108 bgt_set_prefill_kernel and
- * bgt_w4a8_workspace_bytes. */
+ * bgt_w4a8_workspace_bytes, 109 bgt_w4a8_gemm_is_noalloc. */
 int bgt_abi_version(void);
 
 /* Diagnostics: name of the GEMM kernel that bgt_w4a8_gemm_is (float_scale = 0)

@@ -37,7 +37,7 @@ def test_status_strings(L):
     assert bgt.status_string(0) == "ok"
     for st in (-1, -2, -3, -4, -5, -6, -7, 1):
         assert "error" in bgt.status_string(st) or "warning" in bgt.status_string(st)
-    assert L.bgt_abi_version() == 108
+    assert L.bgt_abi_version() == 109
 
 
 def test_quantize_act_validation(L):
@@ -255,6 +255,23 @@ def test_w8a8_is_validation(L):
     assert w4(1, 4096, 12288) != "k_w4a8_decode<IS>"  # 96 groups: not a decode shape
     assert w4(65, 4096, 11008) == "k_w4a8_prefill<4,2,2,2,IS>"
     assert w4(16, 4096, 11008, True) == "k_w4a8_decode<FS>"
+
+
+def test_gemm_is_noalloc_validation(L):
+    g = L.bgt_w4a8_gemm_is_noalloc
+
+    def call(qx=FAKE, sx=FAKE, pk=FAKE, isc=FAKE, alpha=1024, M=512, N=4096, K=4096, y=FAKE, acc=None):
+        return g(qx, sx, pk, isc, alpha, M, N, K, y, acc, None)
+
+    assert call(qx=None) == bgt.BGT_ERR_NULL
+    assert call(isc=None) == bgt.BGT_ERR_NULL
+    assert call(y=None) == bgt.BGT_ERR_NULL
+    assert call(M=0) == bgt.BGT_ERR_SHAPE
+    assert call(N=24) == bgt.BGT_ERR_SHAPE
+    assert call(K=192) == bgt.BGT_ERR_SHAPE
+    assert call(alpha=12) == bgt.BGT_ERR_ALPHA
+    assert call(qx=MIS) == bgt.BGT_ERR_ALIGN
+    assert call(acc=MIS) == bgt.BGT_ERR_ALIGN
 
 
 def test_workspace_bytes():
