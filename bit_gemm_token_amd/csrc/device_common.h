@@ -46,6 +46,10 @@ __device__ __forceinline__ float load_x1(const void* x, int64_t i) {
 struct OutY {
   void* p;
   int type;
+  // the same output from column c on (row stride unchanged)
+  OutY cols(int64_t c) const {
+    return OutY{static_cast<char*>(p) + c * (type == kF32 ? 4 : 2), type};
+  }
   __device__ __forceinline__ void put(int64_t o, float v) const {
     if (type == kF32) static_cast<float*>(p)[o] = v;
     else if (type == kF16) static_cast<__half*>(p)[o] = __float2half(v);

@@ -361,7 +361,7 @@ template <int WM, int WN, int TMW, int TNW, bool FS, typename ST, bool GR = fals
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_w4a8_prefill(
     const int8_t* __restrict__ qx, const float* __restrict__ sx,
     const uint4* __restrict__ packed, const ST* __restrict__ iscale,
-    const float* __restrict__ fscale, float inv_alpha, int M, int N, int K,
+    const float* __restrict__ fscale, float inv_alpha, int M, int N, int K, int ldn,
     OutY y, int32_t* __restrict__ acc_out, Route rt, int splits, int32_t* __restrict__ part) {
   static_assert(TMW == 2 && TNW == 2, "four 32 x 32 blocks per wave");
   constexpr int NW = WM * WN, NT = NW * 64;
@@ -462,7 +462,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
           (const __attribute__((address_space(1))) void*)(base + aoff[i]),
           (__attribute__((address_space(3))) void*)(SA + (i * NW + wave) * 1024), 16, 0, 0);
     __builtin_amdgcn_global_load_lds(
-        (const __attribute__((address_space(1))) void*)(ssrc + ((int64_t)gc * N + soff) * SB),
+        (const __attribute__((address_space(1))) void*)(ssrc + ((int64_t)gc * ldn + soff) * SB),
         (__attribute__((address_space(3))) void*)(SA + A_BYTES + sslot * 256), 4, 0, 0);
 #pragma unroll
     for (int u = 0; u < B_CH; ++u)
@@ -649,7 +649,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
     for (int r = 0; r < 16; ++r) {
       const int i = m0 + wm * (TMW * 32) + a * 32 + 8 * (r / 4) + 4 * hf + (r % 4);
       if (!full && (i >= M || j >= N)) continue;
-      const int64_t o = (int64_t)(r0 + i) * N + j;
+      const int64_t o = (int64_t)(r0 + i) * ldn + j;
       if (FS) {
         y.put_nt(o, facc[k][r] * srow[a][r]);
       } else {
@@ -666,20 +666,22 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
 // conversion per output as in the GEMM epilogue. Four consecutive outputs
 // (one row: N is a multiple of 16) per thread.
 __global__ __launch_bounds__(256) void k_split_reduce(const int32_t* __restrict__ part, int splits,
-                                                      int64_t MN, int N, const float* __restrict__ sx,
+                                                      int64_t MN, int N, int ldn,
+                                                      const float* __restrict__ sx,
                                                       float inv_alpha, OutY y,
                                                       int32_t* __restrict__ acc_out) {
   const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (e >= MN) return;
   v4i a = *reinterpret_cast<const v4i*>(part + e);
   for (int k = 1; k < splits; ++k) a += *reinterpret_cast<const v4i*>(part + k * MN + e);
-  const float si = sx[e / N];
+  const int64_t i = e / N, o = i * ldn + (e - i * N);   // part is M x N, y rows ldn apart
+  const float si = sx[i];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const float t0 = (float)a[r] * si;
-    y.put(e + r, t0 * inv_alpha);
+    y.put(o + r, t0 * inv_alpha);
   }
-  if (acc_out) *reinterpret_cast<v4i*>(acc_out + e) = a;
+  if (acc_out) *reinterpret_cast<v4i*>(acc_out + o) = a;
 }
 
 // =====================================================================
@@ -1243,7 +1245,9 @@ static size_t stream_lds_bytes(int MR, int GPW, bool FS, int G) {
 }
 
 enum class W4Path { Decode, Stream, Skinny, Tiled, Wide };
-struct W4Plan { W4Path path; int mr; };
+// wide_cols > 0 (wide path): the 256 x 256 tile kernel covers columns
+// 0 .. wide_cols-1 and the 256 x 128 one the rest (see plan_w4a8)
+struct W4Plan { W4Path path; int mr; int wide_cols = 0; };
 
 // The kernel a W4A8 GEMM of this shape runs: small M streams the weights
 // (decode kernel when K is a multiple of 16 groups and the X block fits LDS;
@@ -1270,8 +1274,12 @@ static bool decode_padded(int G, int N, int mr) {
 // one workgroup per CU (their LDS rings fill a CU), so a launch takes
 // ceil(tiles / CUs) rounds; at K = 4096 a round costs about 80 us for the
 // 256 x 256 tiles and about 48 us for the 256 x 128 ones (N = 22016, M = 256
-// .. 4096), so the wide kernel is taken when 5 * its rounds <= 3 * the other's.
-// set_prefill_kernel() forces one of them (benchmarks, tests).
+// .. 4096): costs below are in units of 16 us, 5 and 3 per round. When the
+// 256 x 256 tiles would leave a last, partial round, the wide launch keeps
+// the whole column tiles that fill its full rounds and the 256 x 128 kernel
+// takes the remaining columns in a second launch, if those fit one round.
+// set_prefill_kernel() forces one kernel (benchmarks, tests; forcing the wide
+// one keeps the split of the last round).
 static std::atomic<int> g_prefill_kernel{0};        // PrefillKernel
 
 static int device_cus() {
@@ -1288,11 +1296,24 @@ static int device_cus() {
   return n;
 }
 
-static bool wide_tiles_win(int M, int N) {
+// columns of the wide launch when its last round goes to the 256 x 128
+// kernel, else 0
+static int wide_split_cols(int M, int N) {
+  const int64_t cus = device_cus(), tm = (M + 255) / 256, tn = (N + 255) / 256;
+  const int64_t R = tm * tn / cus;                  // full rounds of 256 x 256 tiles
+  if (R < 1 || tm * tn % cus == 0) return 0;
+  const int64_t c1 = R * cus / tm;                  // whole column tiles in them
+  if (c1 < 1 || c1 >= tn) return 0;
+  const int64_t rest = tm * ((N - 256 * c1 + 127) / 128);
+  return rest <= cus ? (int)(256 * c1) : 0;
+}
+
+static bool wide_tiles_win(int M, int N, int split_cols) {
   const int64_t cus = device_cus(), tm = (M + 255) / 256;
-  const int64_t rw = (tm * ((N + 255) / 256) + cus - 1) / cus;
+  const int64_t tw = tm * ((N + 255) / 256);
   const int64_t rt = (tm * ((N + 127) / 128) + cus - 1) / cus;
-  return 5 * rw <= 3 * rt;
+  const int64_t cw = split_cols > 0 ? 5 * (tw / cus) + 3 : 5 * ((tw + cus - 1) / cus);
+  return cw <= 3 * rt;
 }
 
 int set_prefill_kernel(int mode) {
@@ -1304,8 +1325,10 @@ int set_prefill_kernel(int mode) {
 static W4Plan plan_w4a8(int M, int N, int K, bool fs) {
   if (M > 64) {
     const int f = g_prefill_kernel.load();
-    const bool wide = f == kPrefillWide || (f == kPrefillAuto && wide_tiles_win(M, N));
-    return {wide ? W4Path::Wide : W4Path::Tiled, 0};
+    if (f == kPrefillTiled) return {W4Path::Tiled, 0};
+    const int wc = wide_split_cols(M, N);
+    if (f == kPrefillWide || wide_tiles_win(M, N, wc)) return {W4Path::Wide, 0, wc};
+    return {W4Path::Tiled, 0};
   }
   const int mr = (M + 15) / 16, G = K / kGroup;
   if (G == 16 || G == 32 || decode_padded(G, N, mr)) return {W4Path::Decode, mr};
@@ -1437,9 +1460,14 @@ static int split_count(int M, int N, int K) {
 }
 
 size_t w4a8_split_bytes(int64_t M, int64_t N, int64_t K, bool float_scale) {
-  if (float_scale || plan_w4a8((int)M, (int)N, (int)K, false).path != W4Path::Tiled) return 0;
-  const int s = split_count((int)M, (int)N, (int)K);
-  return s > 1 ? (size_t)s * (size_t)M * (size_t)N * sizeof(int32_t) : 0;
+  if (float_scale) return 0;
+  const W4Plan p = plan_w4a8((int)M, (int)N, (int)K, false);
+  int64_t n = N;                                    // columns of the 256 x 128 launch
+  if (p.path == W4Path::Wide) n = p.wide_cols > 0 ? N - p.wide_cols : 0;
+  else if (p.path != W4Path::Tiled) n = 0;
+  if (n == 0) return 0;
+  const int s = split_count((int)M, (int)n, (int)K);
+  return s > 1 ? (size_t)s * (size_t)M * (size_t)n * sizeof(int32_t) : 0;
 }
 
 // The library's split-K workspace: one buffer per device, grown on demand
@@ -1503,6 +1531,31 @@ int32_t* noalloc_scratch(size_t* capacity) {
   return static_cast<int32_t*>(a);
 }
 
+// 256 x 128 tiles, 8 waves of 64 x 64, over N columns whose scales, y and
+// acc_out rows are ldn elements apart; split K when the tiles are few
+template <bool FS, typename ST>
+static void launch_tiled(const int8_t* qx, const float* sx, const uint8_t* packed,
+                         const ST* iscale, const float* fscale, float inv_alpha, int M, int N,
+                         int K, int ldn, OutY y, int32_t* acc_out, hipStream_t stream,
+                         int32_t* ws) {
+  const uint4* pk = reinterpret_cast<const uint4*>(packed);
+  const int tiles = ((M + 255) / 256) * ((N + 127) / 128);
+  int splits = FS ? 1 : split_count(M, N, K);
+  int32_t* part = nullptr;
+  if (splits > 1) {
+    part = ws != nullptr ? ws : split_workspace((size_t)splits * M * N * sizeof(int32_t), stream);
+    if (part == nullptr) splits = 1;
+  }
+  hipLaunchKernelGGL((k_w4a8_prefill<4, 2, 2, 2, FS, ST>), dim3(tiles * splits), dim3(512), 0,
+                     stream, qx, sx, pk, iscale, fscale, inv_alpha, M, N, K, ldn, y, acc_out,
+                     Route{}, splits, part);
+  if (splits > 1) {
+    const int64_t MN = (int64_t)M * N;
+    hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)((MN / 4 + 255) / 256)), dim3(256), 0,
+                       stream, part, splits, MN, N, ldn, sx, inv_alpha, y, acc_out);
+  }
+}
+
 template <bool FS, typename ST>
 static void launch_w4a8_t(const int8_t* qx, const float* sx, const uint8_t* packed,
                           const ST* iscale, const float* fscale, float inv_alpha, int M, int N,
@@ -1519,28 +1572,20 @@ static void launch_w4a8_t(const int8_t* qx, const float* sx, const uint8_t* pack
       default: launch_decode<FS, 112, 112>(plan.mr, stream, qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out); break;
     }
   } else if (plan.path == W4Path::Wide) {
-    launch_w4a8_wide(FS, qx, sx, packed, iscale, sizeof(ST), fscale, inv_alpha, M, N, K, y,
+    const int nw = plan.wide_cols > 0 ? plan.wide_cols : N;
+    launch_w4a8_wide(FS, qx, sx, packed, iscale, sizeof(ST), fscale, inv_alpha, M, nw, K, N, y,
                      acc_out, stream);
+    if (nw < N) {                                   // the last round's columns
+      const int G = K / kGroup;
+      launch_tiled<FS, ST>(qx, sx, packed + (int64_t)(nw / 16) * G * 1024,
+                           FS ? iscale : iscale + nw, FS ? fscale + nw : fscale, inv_alpha, M,
+                           N - nw, K, N, y.cols(nw), acc_out ? acc_out + nw : nullptr, stream, ws);
+    }
   } else if (plan.path != W4Path::Tiled) {
     launch_small_m<FS>(plan, qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out, stream);
   } else {
-    // 256 x 128 tiles, 8 waves of 64 x 64; split K when the tiles are few
-    const uint4* pk = reinterpret_cast<const uint4*>(packed);
-    const int tiles = ((M + 255) / 256) * ((N + 127) / 128);
-    int splits = FS ? 1 : split_count(M, N, K);
-    int32_t* part = nullptr;
-    if (splits > 1) {
-      part = ws != nullptr ? ws : split_workspace((size_t)splits * M * N * sizeof(int32_t), stream);
-      if (part == nullptr) splits = 1;
-    }
-    hipLaunchKernelGGL((k_w4a8_prefill<4, 2, 2, 2, FS, ST>), dim3(tiles * splits), dim3(512), 0,
-                       stream, qx, sx, pk, iscale, fscale, inv_alpha, M, N, K, y, acc_out, Route{},
-                       splits, part);
-    if (splits > 1) {
-      const int64_t MN = (int64_t)M * N;
-      hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)((MN / 4 + 255) / 256)), dim3(256), 0,
-                         stream, part, splits, MN, N, sx, inv_alpha, y, acc_out);
-    }
+    launch_tiled<FS, ST>(qx, sx, packed, iscale, fscale, inv_alpha, M, N, K, N, y, acc_out, stream,
+                         ws);
   }
 }
 
@@ -1703,7 +1748,8 @@ static void launch_moe_t(const int8_t* qx, const float* sx, const uint8_t* packe
   }
   const int tiles = ((rt.R + 255) / 256 + rt.E) * ((N + 127) / 128);
   hipLaunchKernelGGL((k_w4a8_prefill<4, 2, 2, 2, false, ST, true>), dim3(tiles), dim3(512), 0,
-                     stream, qx, sx, pk, iscale, nullptr, inv_alpha, 0, N, K, y, acc_out, rt, 1, nullptr);
+                     stream, qx, sx, pk, iscale, nullptr, inv_alpha, 0, N, K, N, y, acc_out, rt, 1,
+                     nullptr);
 }
 
 hipError_t launch_w4a8_moe(const int8_t* qx, const float* sx, int64_t T, const int32_t* offs,

@@ -58,7 +58,7 @@ template <bool FS, typename ST>
 __global__ __launch_bounds__(kWNW * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_w4a8_wide(
     const int8_t* __restrict__ qx, const float* __restrict__ sx,
     const uint8_t* __restrict__ packed, const ST* __restrict__ iscale,
-    const float* __restrict__ fscale, float inv_alpha, int M, int N, int K, OutY y,
+    const float* __restrict__ fscale, float inv_alpha, int M, int N, int K, int ldn, OutY y,
     int32_t* __restrict__ acc_out) {
   constexpr int NW = kWNW;
   constexpr int A_MAX = (kWACopies + NW - 1) / NW;   // 5 activation copies for waves 0..3,
@@ -127,7 +127,7 @@ __global__ __launch_bounds__(kWNW * 64) __attribute__((amdgpu_waves_per_eu(2))) 
           (__attribute__((address_space(3))) void*)(ws + (2 * wave + u) * 1024), 16, 0, 0);
     if (lane < 32)
       __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)((ssrc + (int64_t)g * N * SB) + soff),
+          (const __attribute__((address_space(1))) void*)((ssrc + (int64_t)g * ldn * SB) + soff),
           (__attribute__((address_space(3))) void*)(ws + kWB + wave * 128), 4, 0, 0);
   };
 
@@ -325,7 +325,7 @@ __global__ __launch_bounds__(kWNW * 64) __attribute__((amdgpu_waves_per_eu(2))) 
     for (int r = 0; r < 16; ++r) {
       const int i = m0 + rb * 32 + 8 * (r / 4) + 4 * hf + (r % 4);
       if (!full && (i >= M || j >= N)) continue;
-      const int64_t o = (int64_t)i * N + j;
+      const int64_t o = (int64_t)i * ldn + j;
       if (FS) {
         y.put_nt(o, facc[rb][r] * srow[r]);
       } else {
@@ -340,27 +340,27 @@ __global__ __launch_bounds__(kWNW * 64) __attribute__((amdgpu_waves_per_eu(2))) 
 template <bool FS, typename ST>
 static void launch_wide_t(const int8_t* qx, const float* sx, const uint8_t* packed,
                           const ST* iscale, const float* fscale, float inv_alpha, int M, int N,
-                          int K, OutY y, int32_t* acc_out, hipStream_t stream) {
+                          int K, int ldn, OutY y, int32_t* acc_out, hipStream_t stream) {
   const int tiles = ((M + kWBM - 1) / kWBM) * ((N + kWBN - 1) / kWBN);
   hipLaunchKernelGGL((k_w4a8_wide<FS, ST>), dim3(tiles), dim3(kWNW * 64), 0, stream, qx, sx,
-                     packed, iscale, fscale, inv_alpha, M, N, K, y, acc_out);
+                     packed, iscale, fscale, inv_alpha, M, N, K, ldn, y, acc_out);
 }
 
 void launch_w4a8_wide(bool float_scale, const int8_t* qx, const float* sx, const uint8_t* packed,
                       const void* iscale, int iscale_bytes, const float* fscale, float inv_alpha,
-                      int M, int N, int K, OutY y, int32_t* acc_out, hipStream_t stream) {
+                      int M, int N, int K, int ldn, OutY y, int32_t* acc_out, hipStream_t stream) {
   if (float_scale)
     launch_wide_t<true>(qx, sx, packed, static_cast<const int32_t*>(nullptr), fscale, inv_alpha,
-                        M, N, K, y, nullptr, stream);
+                        M, N, K, ldn, y, nullptr, stream);
   else if (iscale_bytes == 4)
     launch_wide_t<false>(qx, sx, packed, static_cast<const int32_t*>(iscale), nullptr, inv_alpha,
-                         M, N, K, y, acc_out, stream);
+                         M, N, K, ldn, y, acc_out, stream);
   else if (iscale_bytes == 2)
     launch_wide_t<false>(qx, sx, packed, static_cast<const uint16_t*>(iscale), nullptr, inv_alpha,
-                         M, N, K, y, acc_out, stream);
+                         M, N, K, ldn, y, acc_out, stream);
   else
     launch_wide_t<false>(qx, sx, packed, static_cast<const uint8_t*>(iscale), nullptr, inv_alpha,
-                         M, N, K, y, acc_out, stream);
+                         M, N, K, ldn, y, acc_out, stream);
 }
 
 }  // namespace bgt

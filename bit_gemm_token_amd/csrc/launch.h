@@ -46,10 +46,11 @@ size_t w4a8_split_bytes(int64_t M, int64_t N, int64_t K, bool float_scale);
 // cannot be obtained) and its size in bytes
 int32_t* noalloc_scratch(size_t* capacity);
 
-// the large-M W4A8 GEMM (256 x 256 tiles); inv_alpha = 1/alpha (exact)
+// the large-M W4A8 GEMM (256 x 256 tiles) over N columns whose scales, y and
+// acc_out rows are ldn elements apart; inv_alpha = 1/alpha (exact)
 void launch_w4a8_wide(bool float_scale, const int8_t* qx, const float* sx, const uint8_t* packed,
                       const void* iscale, int iscale_bytes, const float* fscale, float inv_alpha,
-                      int M, int N, int K, OutY y, int32_t* acc_out, hipStream_t stream);
+                      int M, int N, int K, int ldn, OutY y, int32_t* acc_out, hipStream_t stream);
 
 // per-token quantization of x (M x K of element type x_type, leading dimension
 // ldx) into q_out /

@@ -285,23 +285,31 @@ def test_workspace_bytes():
     assert wb(100, 256, 512) == 0                           # 4 groups: no split
     assert wb(256, 22016, 4096) == 0                        # 172 tiles
     assert wb(4096, 22016, 4096) == 0 and wb(64, 22016, 4096) == 0   # wide, decode
+    # wide launches whose last round goes to the 256 x 128 kernel: its columns
+    # (22016 - 85 * 256 = 256 at M = 1536 and 3072: 6 and 12 tiles) split in 8
+    assert wb(1536, 22016, 4096) == 8 * 1536 * 256 * 4
+    assert wb(3072, 22016, 4096) == 8 * 3072 * 256 * 4
+    assert wb(2048, 22016, 4096) == 0                       # no split of the last round
     assert bgt.lib().bgt_w4a8_workspace_bytes(0, 4096, 4096) == bgt.BGT_ERR_SHAPE
 
 
 def test_prefill_kernel_choice(L):
-    # M > 64, N = 22016 on 256 CUs: 256 x 256 tiles when 5 * their launch
-    # rounds <= 3 * those of the 256 x 128 tiles (M = 512: 1 vs 2 rounds;
-    # 1024: 2 vs 3; 1536: 3 vs 5; 2048: 3 vs 6; 4096: 6 vs 11)
+    # M > 64, N = 22016 on 256 CUs, costs 5 per round of 256 x 256 tiles and 3
+    # per round of 256 x 128 ones; a partial last round of 256 x 256 tiles goes
+    # to the 256 x 128 kernel (cost 3) when its columns fit one round there:
+    # M = 256: 5 vs 3; 512: 5 vs 6; 768: 5+3 vs 9; 1024: 5+3 vs 9;
+    # 1536: 10+3 vs 15; 2048: 15 (176 tiles left, 352 of 256 x 128) vs 18;
+    # 4096: 25+3 vs 33
     w4 = bgt.w4a8_kernel_name
     wide, tiled = "k_w4a8_wide<IS>", "k_w4a8_prefill<4,2,2,2,IS>"
     try:
-        assert [w4(M, 22016, 4096) for M in (256, 512, 1024, 1536, 2048, 4096)] == \
-            [tiled, wide, tiled, wide, wide, wide]
+        assert [w4(M, 22016, 4096) for M in (256, 512, 768, 1024, 1536, 2048, 4096)] == \
+            [tiled, wide, wide, wide, wide, wide, wide]
         assert w4(4096, 256, 4096) == tiled              # 16 vs 32 tiles: one round each
         assert w4(2048, 22016, 4096, True) == "k_w4a8_wide<FS>"
         assert w4(64, 22016, 4096) == "k_w4a8_decode<IS>"     # the decode range is unaffected
         bgt.set_prefill_kernel("wide")
-        assert w4(65, 256, 128) == wide and w4(1024, 22016, 4096) == wide
+        assert w4(65, 256, 128) == wide and w4(256, 22016, 4096) == wide
         assert w4(16, 22016, 4096) == "k_w4a8_decode<IS>"
         bgt.set_prefill_kernel("tiled")
         assert w4(4096, 22016, 4096) == tiled and w4(4096, 22016, 4096, True) == "k_w4a8_prefill<4,2,2,2,FS>"
@@ -311,7 +319,7 @@ def test_prefill_kernel_choice(L):
             bgt.set_prefill_kernel("fast")
     finally:
         bgt.set_prefill_kernel("auto")
-    assert w4(1024, 22016, 4096) == tiled
+    assert w4(256, 22016, 4096) == tiled
 
 
 def test_moe_validation(L):

@@ -1,7 +1,10 @@
 """GPU parity of the large-M W4A8 kernel (256 x 256 output tiles) against the oracle.
 
 The module forces that kernel for every M > 64 (bgt_set_prefill_kernel), so
-small shapes reach it too. Cases span several tiles with ragged rows and
+small shapes reach it too. Shapes with more tiles than one round of CUs and a
+partial last round run the 256 x 256 kernel on the columns of the full rounds
+and the 256 x 128 kernel on the rest (row stride N in both; the rest split in
+K when its tiles are few). Cases span several tiles with ragged rows and
 ragged column tiles (N not a multiple of 256, down to one 16-column tile),
 group counts of 1, 2, 3, 5 and 32 (the pipeline's three stages wrap at
 different points), integer scales of 4, 2 and 1 bytes, the float-scale
@@ -156,3 +159,33 @@ def test_wide_overflow_wraps_like_oracle(bgt, orc, dev):
     wrapped = ((oA + 2 ** 31) % 2 ** 32 - 2 ** 31).astype(np.int64)
     np.testing.assert_array_equal(acc.cpu().numpy().astype(np.int64), wrapped)
     assert_bits(y.cpu().numpy(), oy, "y_wrap")
+
+
+# (M, K, N, columns of the 256 x 256 launch) on 256 CUs
+SPLIT_SHAPES = [
+    (1024, 256, 16640, 16384),     # 260 tiles: 64 column tiles wide, 256 columns left
+    (1031, 1024, 16400, 13056),    # 325 tiles, ragged rows; 3344 columns left, ragged
+    (1024, 1024, 16640, 16384),    # the 8 tiles left split K in 2
+]
+
+
+@pytest.mark.parametrize("M,K,N,NW", SPLIT_SHAPES)
+def test_wide_last_round_split(bgt, orc, dev, M, K, N, NW):
+    say(f"wide + last round M={M} K={K} N={N} (wide columns {NW})")
+    assert bgt.w4a8_kernel_name(M, N, K).startswith("k_w4a8_wide")
+    oq, os_, ow, d = case(orc, dev, 3 * M + K + N, M, K, N)
+    y = nan_like((M, N), dev)
+    acc = torch.full((M, N), -1, dtype=torch.int32, device=dev)
+    bgt.w4a8_gemm_is(d["qx"], d["sx"], d["packed"], d["iscale"], 1024, N, y=y, acc_out=acc)
+    oA, oy, ov = orc.w4a8_gemm_is(oq, os_, ow["codes"], ow["iscale"], 1024)
+    assert ov == 0
+    np.testing.assert_array_equal(acc.cpu().numpy().astype(np.int64), oA)
+    assert_bits(y.cpu().numpy(), oy, "y_is")
+    yf = nan_like((M, N), dev)
+    bgt.w4a8_gemm_fs(d["qx"], d["sx"], d["packed"], d["fscale"], N, y=yf)
+    assert_bits(yf.cpu().numpy(), orc.w4a8_gemm_fs(oq, os_, ow["codes"], ow["fscale"]), "y_fs")
+    isc = bgt.narrow_iscale(d["iscale"], 2)
+    yn = nan_like((M, N), dev, torch.bfloat16)
+    bgt.w4a8_gemm_is_narrow(d["qx"], d["sx"], d["packed"], isc, 1024, N, y=yn)
+    want = orc.f32_to_bf16_bits(oy.astype(np.float32))
+    np.testing.assert_array_equal(yn.view(torch.int16).cpu().numpy().view(np.uint16), want)
