@@ -87,37 +87,40 @@ METRIC = "W4A8 integer-scale GEMM TOPS + HBM GB/s, K=4096 N=22016, M=1..4096"
 # profiles/*hbm_bytes.txt), keyed by (kernel, M). They hold only for the
 # kernel sources they were taken on: when a source file differs from the one
 # measured (sha256 prefix below), traffic is reported as null.
-TRAFFIC_SRC_SHA = {"gemm.hip": "71795a04cc3fd7f8", "gemm_w8is.hip": "e4fcff966f541e75"}
-TRAFFIC_SRC = {"k_w4a8_decode<IS>": "gemm.hip", "k_w4a8_prefill<4,2,2,2,IS>": "gemm.hip",
-               "k_w8a8_zp<9,32>": "gemm.hip", "k_w4a8_decode<IS,grouped>": "gemm.hip",
-               "k_w8is_split": "gemm_w8is.hip"}
+TRAFFIC_SRC_SHA = {"gemm.hip": "58d5e5d151787d11", "gemm_wide.hip": "f50d8edccd0caea5",
+                   "gemm_w8is.hip": "e4fcff966f541e75"}
+# sources of the launches one call makes (the wide path also runs the 256 x 128
+# kernel over the last round's columns)
+TRAFFIC_SRC = {"k_w4a8_decode<IS>": ("gemm.hip",), "k_w4a8_prefill<4,2,2,2,IS>": ("gemm.hip",),
+               "k_w4a8_wide<IS>": ("gemm.hip", "gemm_wide.hip"), "k_w8a8_zp<9,32>": ("gemm.hip",),
+               "k_w8is_split": ("gemm_w8is.hip",)}
 TRAFFIC = {
-    ("k_w4a8_decode<IS>", 1): 48190998,
-    ("k_w4a8_decode<IS>", 4): 48554828,
-    ("k_w4a8_decode<IS>", 16): 50004964,
-    ("k_w4a8_decode<IS>", 64): 55914897,
-    ("k_w4a8_prefill<4,2,2,2,IS>", 256): 79307207,
-    ("k_w4a8_prefill<4,2,2,2,IS>", 4096): 922280127,
-    ("k_w8a8_zp<9,32>", 256): 29681407,
+    ("k_w4a8_decode<IS>", 1): 48180849,
+    ("k_w4a8_decode<IS>", 4): 48546813,
+    ("k_w4a8_decode<IS>", 16): 49993966,
+    ("k_w4a8_decode<IS>", 64): 55923917,
+    ("k_w4a8_prefill<4,2,2,2,IS>", 256): 79254298,
+    ("k_w4a8_wide<IS>", 512): 149892108,
+    ("k_w4a8_wide<IS>", 1024): 207378789,
+    ("k_w4a8_wide<IS>", 2048): 384204748,
+    ("k_w4a8_wide<IS>", 4096): 754850797,
+    ("k_w8a8_zp<9,32>", 256): 29671271,
     ("k_w8is_split", 1): 62579842,
     ("k_w8is_split", 4): 62972917,
     ("k_w8is_split", 16): 64545536,
     ("k_w8is_split", 64): 70844568,
-    ("k_w4a8_decode<IS,grouped>", 1): 62680449,
-    ("k_w4a8_decode<IS,grouped>", 4): 125518144,
-    ("k_w4a8_decode<IS,grouped>", 16): 189674135,
-    ("k_w4a8_decode<IS,grouped>", 64): 259160321,
 }
 
 
 def measured_traffic(kernel, Ms):
     import hashlib
-    name = TRAFFIC_SRC.get(kernel)
-    if name is None or TRAFFIC_SRC_SHA.get(name) is None:
+    names = TRAFFIC_SRC.get(kernel)
+    if names is None:
         return None
-    with open(os.path.join(ROOT, "bit_gemm_token_amd", "csrc", name), "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest()[:16] != TRAFFIC_SRC_SHA[name]:
-            return None
+    for name in names:
+        with open(os.path.join(ROOT, "bit_gemm_token_amd", "csrc", name), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest()[:16] != TRAFFIC_SRC_SHA[name]:
+                return None
     vals = [TRAFFIC.get((kernel, M)) for M in Ms]
     return None if any(v is None for v in vals) else int(np.mean(vals))
 
@@ -394,8 +397,7 @@ def run_decode(args, torch, bgt, dev):
     kernels = kernel_rooflines(launches)
     dom = max(kernels, key=lambda k: k["total_us"])
     roof = dict(dom["roofline"])
-    roof["traffic"] = (measured_traffic(dom["kernel"], dom["launch_M"])
-                       if sb == 4 and roof["bound"] == "hbm" else None)
+    roof["traffic"] = measured_traffic(dom["kernel"], dom["launch_M"]) if sb == 4 else None
     out = {
         "metric": METRIC, "value": round(step_bytes / (ms_step * 1e-3) / 1e9, 1), "unit": "GB/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
