@@ -66,6 +66,21 @@ __device__ __forceinline__ int quant_code(float x, float s, int z) {
   return clamp_int((int)r, -127, 127);
 }
 
+// The same code with x / s as Markstein's corrected quotient (P. Markstein,
+// IBM J. Res. Dev. 1990): with r = 1/s correctly rounded, q0 = x*r,
+// e = fma(-q0, s, x) is exact and fma(e, r, q0) is x / s correctly rounded,
+// as long as s, r and the residual stay normal (the caller keeps s within
+// [2^-100, 2^100]; |x| <= 255 s here). Three operations instead of the
+// division's scale / reciprocal / refine / fixup sequence.
+template <bool ASYM>
+__device__ __forceinline__ int quant_code_rcp(float x, float s, float r, int z) {
+  const float q0 = x * r;
+  const float q = __builtin_fmaf(__builtin_fmaf(-q0, s, x), r, q0);
+  const float c = round_away(q);
+  if (ASYM) return clamp_int((int)c + z, 0, 255);
+  return clamp_int((int)c, -127, 127);
+}
+
 // Vector path: cols % 16 == 0, ld % 4 == 0, x and q 16-byte aligned.
 template <bool ASYM, int IT>
 __global__ __launch_bounds__(kQThreads) void k_quant_rows_vec(
@@ -115,9 +130,22 @@ __global__ __launch_bounds__(kQThreads) void k_quant_rows_vec(
   }
 
   int sum = 0;
+  // row-uniform: the corrected quotient where s keeps it exact, else the division
+  const bool rcp = s >= 0x1.0p-100f && s <= 0x1.0p100f;
+  const float rs = rcp ? 1.0f / s : 0.0f;
   auto emit = [&](int64_t v, float4 f) {
-    const int c0 = quant_code<ASYM>(f.x, s, z), c1 = quant_code<ASYM>(f.y, s, z);
-    const int c2 = quant_code<ASYM>(f.z, s, z), c3 = quant_code<ASYM>(f.w, s, z);
+    int c0, c1, c2, c3;
+    if (rcp) {
+      c0 = quant_code_rcp<ASYM>(f.x, s, rs, z);
+      c1 = quant_code_rcp<ASYM>(f.y, s, rs, z);
+      c2 = quant_code_rcp<ASYM>(f.z, s, rs, z);
+      c3 = quant_code_rcp<ASYM>(f.w, s, rs, z);
+    } else {
+      c0 = quant_code<ASYM>(f.x, s, z);
+      c1 = quant_code<ASYM>(f.y, s, z);
+      c2 = quant_code<ASYM>(f.z, s, z);
+      c3 = quant_code<ASYM>(f.w, s, z);
+    }
     sum += c0 + c1 + c2 + c3;
     qr[v] = (uint32_t)(c0 & 0xFF) | ((uint32_t)(c1 & 0xFF) << 8) |
             ((uint32_t)(c2 & 0xFF) << 16) | ((uint32_t)(c3 & 0xFF) << 24);

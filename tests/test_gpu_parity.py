@@ -96,6 +96,40 @@ def test_quantize_sym_ties_exact(bgt, orc, dev):
     assert q.cpu().numpy()[0, :7].tolist() == [127, 1, -1, 3, -64, 1, -127]
 
 
+@pytest.mark.parametrize("mode", ["sym", "asym"])
+def test_quantize_scale_range(bgt, orc, dev, mode):
+    # rows scaled from 2^-120 to 2^120: the quantizer takes x*r corrected by
+    # one fma (r = 1/s) for s in [2^-100, 2^100] and the division outside, and
+    # must give the division's codes everywhere; rows 0 and 1 put quotients
+    # exactly on and one ulp beside half-integers
+    say(f"quantize_act {mode} across scales")
+    K = 1024
+    g = synth.rng(17, 3)
+    base = g.standard_normal((24, K)).astype(np.float32)
+    base = np.sign(base) * (np.abs(base) + np.float32(0.25))   # |x| >= 2^-122: no subnormal inputs
+    base[0] = (g.integers(-254, 255, K) / 2.0).astype(np.float32)
+    base[0, 0] = 127.0
+    base[1] = np.nextafter(base[0], np.float32(np.inf))
+    base[1, 0] = 127.0
+    exps = [0, 0, -120, -110, -101, -100, -99, -90, -60, -30, -10, -1, 1, 10, 30, 60, 90, 99, 100, 101,
+            110, 115, 120, 5]
+    x = np.stack([np.ldexp(base[i], e) for i, e in enumerate(exps)]).astype(np.float32)
+    assert np.isfinite(x).all()
+    if mode == "sym":
+        q, s, _ = bgt.quantize_act(to_dev(x, dev))
+        oq, os_ = orc.quant_sym_i8(x)
+        np.testing.assert_array_equal(s.cpu().numpy(), os_)
+        np.testing.assert_array_equal(q.cpu().numpy(), oq)
+    else:
+        x[2::2] += np.float32(0.75) * np.abs(x[2::2]).max(1, keepdims=True)
+        q, s, z, rs = bgt.quantize_act(to_dev(x, dev), mode="asym")
+        oq, os_, oz, ors = orc.quant_asym_u8(x)
+        np.testing.assert_array_equal(s.cpu().numpy(), os_)
+        np.testing.assert_array_equal(z.cpu().numpy(), oz)
+        np.testing.assert_array_equal(q.cpu().numpy(), oq)
+        np.testing.assert_array_equal(rs.cpu().numpy(), ors)
+
+
 @pytest.mark.parametrize("M,K,relu", [(256, 4096, False), (256, 4096, True), (9, 300, False),
                                       (4096, 4096, False)])
 def test_quantize_asym(bgt, orc, dev, M, K, relu):
