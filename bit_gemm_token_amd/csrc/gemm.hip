@@ -1282,7 +1282,7 @@ static bool decode_padded(int G, int N, int mr) {
 // one keeps the split of the last round).
 static std::atomic<int> g_prefill_kernel{0};        // PrefillKernel
 
-static int device_cus() {
+int device_cus() {
   static std::atomic<int> cached{0};
   int n = cached.load();
   if (n > 0) return n;
@@ -1473,7 +1473,7 @@ size_t w4a8_split_bytes(int64_t M, int64_t N, int64_t K, bool float_scale) {
 // The library's split-K workspace: one buffer per device, grown on demand
 // (never while the stream is being captured into a graph: such a launch runs
 // unsplit unless the buffer is already large enough). nullptr if unavailable.
-static int32_t* split_workspace(size_t bytes, hipStream_t stream) {
+int32_t* split_workspace(size_t bytes, hipStream_t stream) {
   struct Buf { int dev; void* p; size_t n; };
   static std::mutex mu;
   static std::vector<Buf> bufs;
@@ -1503,6 +1503,13 @@ static int32_t* split_workspace(size_t bytes, hipStream_t stream) {
     bufs.push_back({dev, p, n});
   }
   return static_cast<int32_t*>(p);
+}
+
+void launch_split_reduce(const int32_t* part, int splits, int M, int N, int ldn, const float* sx,
+                         float inv_alpha, OutY y, int32_t* acc_out, hipStream_t stream) {
+  const int64_t MN = (int64_t)M * N;
+  hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)((MN / 4 + 255) / 256)), dim3(256), 0, stream,
+                     part, splits, MN, N, ldn, sx, inv_alpha, y, acc_out);
 }
 
 // Scratch of the no-allocation entry point (bgt_w4a8_gemm_is_noalloc): the
@@ -1549,11 +1556,7 @@ static void launch_tiled(const int8_t* qx, const float* sx, const uint8_t* packe
   hipLaunchKernelGGL((k_w4a8_prefill<4, 2, 2, 2, FS, ST>), dim3(tiles * splits), dim3(512), 0,
                      stream, qx, sx, pk, iscale, fscale, inv_alpha, M, N, K, ldn, y, acc_out,
                      Route{}, splits, part);
-  if (splits > 1) {
-    const int64_t MN = (int64_t)M * N;
-    hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)((MN / 4 + 255) / 256)), dim3(256), 0,
-                       stream, part, splits, MN, N, ldn, sx, inv_alpha, y, acc_out);
-  }
+  if (splits > 1) launch_split_reduce(part, splits, M, N, ldn, sx, inv_alpha, y, acc_out, stream);
 }
 
 template <bool FS, typename ST>

@@ -349,7 +349,7 @@ template <int GC, typename ST>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k_w8is_wide(
     const int8_t* __restrict__ qx, const float* __restrict__ sx, const int8_t* __restrict__ qw,
     const ST* __restrict__ iscale, float inv_alpha, int M, int N, int K, OutY y,
-    int32_t* __restrict__ acc_out) {
+    int32_t* __restrict__ acc_out, int splits, int32_t* __restrict__ part) {
   constexpr int NW = 8, WN = 2, BM = 256, BN = 128;
   constexpr int SB = sizeof(ST);
   constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
@@ -366,7 +366,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
     else if constexpr (i == 1) return S1;
     else return S2;
   };
-  const int G = GC > 0 ? GC : K / kGroup;
+  // split K (GC == 0 launches only): workgroup id = ks * tiles + tile; split
+  // ks runs groups g0 .. g0+G-1 = [ks*GT/splits, (ks+1)*GT/splits) and leaves
+  // its integer-scaled int32 sums in part[ks] (M x N) for the reduction
+  const int GT = K / kGroup;
+  const int ntiles = (int)gridDim.x / splits;
+  const int ks = (int)blockIdx.x / ntiles, tb = (int)blockIdx.x - ks * ntiles;
+  const int g0 = (int)((int64_t)ks * GT / splits);
+  const int G = GC > 0 ? GC : (int)((int64_t)(ks + 1) * GT / splits) - g0;
   const int T = N / 16;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -374,7 +381,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int wm = wave / WN, wn = wave % WN;
   const int lr = lane % 32, hf = lane / 32;
   int tm, tn;
-  tile_of(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
+  tile_of(tb, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
   // activation copy i of this wave: block b = NW*i + wave (rows 8b .. 8b+7),
@@ -394,7 +401,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
   for (int u = 0; u < B_CP; ++u) {
     const int q = B_CP * wave + u;
     const int tl = n0 / 16 + q / 2 < T ? n0 / 16 + q / 2 : T - 1;
-    bsrc[u] = qw + ((int64_t)tl * G * 2 + q % 2) * 1024 + lane * 16;
+    bsrc[u] = qw + ((int64_t)tl * GT * 2 + q % 2) * 1024 + lane * 16;
   }
   // scale copy: dword d = 4*SB*wave + lane (lane < 4*SB) of the group's 128*SB
   // bytes; dwords past N re-read the row's last dword
@@ -403,7 +410,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int scol = n0 + sd * (4 / SB) < N ? n0 + sd * (4 / SB) : N - 4 / SB;
   const int8_t* ssrc = reinterpret_cast<const int8_t*>(iscale) + (int64_t)scol * SB;
   auto issue = [&](int g, int8_t* S) {
-    const int gc = g < G ? g : G - 1;                 // past the end: surplus copies, never read
+    const int gc = (g < G ? g : G - 1) + g0;          // past the end: surplus copies, never read
 #pragma unroll
     for (int i = 0; i < A_CP; ++i)
       __builtin_amdgcn_global_load_lds(
@@ -497,6 +504,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
   for (int r = 0; r < 16; ++r) acc[3][r] = mad24(pp[r], spp, acc[3][r]);
   wait_vm_lds0<0>();                                  // surplus copies of the last steps
 
+  if (part != nullptr) {                              // split K: this split's sums
+    int32_t* pp2 = part + (int64_t)ks * M * N;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int a = k / 2, b = k % 2;
+      const int j = n0 + wn * 64 + 32 * b + lr;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = m0 + wm * 64 + 32 * a + 8 * (r / 4) + 4 * hf + (r % 4);
+        if (i < M && j < N) pp2[(int64_t)i * N + j] = acc[k][r];
+      }
+    }
+    return;
+  }
+
   // one conversion per output; the lane's 32 token scales first
   float srow[2][16];
 #pragma unroll
@@ -536,8 +558,20 @@ static int split_waves(int64_t N, int64_t K, int mr) {
 
 // M > 64: the 256 x 128 tile copies 3x the bytes of a 64 x 64 tile per group
 // for 8x the work; with one workgroup per CU (LDS), pick the tile whose rounds
-// of 256 workgroups move fewer bytes in total
-static bool w8is_use_wide(int M, int N) {
+// of 256 workgroups move fewer bytes in total. When the 256 x 128 tiles fill
+// at most half of the CUs, their groups split into S parts instead (S doubles
+// while tiles * 2S fits the CUs, at least 8 groups per part), the parts'
+// int32 sums added by a second kernel (exact mod 2^32), and that tile is taken.
+static int w8is_splits(int M, int N, int K) {
+  const int64_t wide = ((M + 255) / 256) * (int64_t)((N + 127) / 128), cus = device_cus();
+  const int G = K / kGroup;
+  int s = 1;
+  while (wide * s * 2 <= cus && s * 2 * 8 <= G) s *= 2;
+  return s;
+}
+
+static bool w8is_use_wide(int M, int N, int K) {
+  if (w8is_splits(M, N, K) > 1) return true;
   const int64_t small = ((M + 63) / 64) * (int64_t)((N + 63) / 64);
   const int64_t wide = ((M + 255) / 256) * (int64_t)((N + 127) / 128);
   return ((wide + 255) / 256) * 97 < ((small + 255) / 256) * 32;
@@ -564,18 +598,30 @@ static void launch_w8is_t(const int8_t* qx, const float* sx, const int8_t* qw, c
     return;
   }
   const int G = K / kGroup;
-  if (w8is_use_wide(M, N)) {
+  if (w8is_use_wide(M, N, K)) {
     const int tiles = ((M + 255) / 256) * ((N + 127) / 128);
+    int splits = w8is_splits(M, N, K);
+    int32_t* part = nullptr;
+    if (splits > 1) {
+      part = split_workspace((size_t)splits * M * N * sizeof(int32_t), stream);
+      if (part == nullptr) splits = 1;
+    }
+    if (splits > 1) {
+      hipLaunchKernelGGL((k_w8is_wide<0, ST>), dim3((unsigned)(tiles * splits)), dim3(512), 0,
+                         stream, qx, sx, qw, iscale, inv_alpha, M, N, K, y, acc_out, splits, part);
+      launch_split_reduce(part, splits, M, N, N, sx, inv_alpha, y, acc_out, stream);
+      return;
+    }
     dim3 grid((unsigned)tiles), block(512);
     if (G == 112)
       hipLaunchKernelGGL((k_w8is_wide<112, ST>), grid, block, 0, stream, qx, sx, qw, iscale,
-                         inv_alpha, M, N, K, y, acc_out);
+                         inv_alpha, M, N, K, y, acc_out, 1, nullptr);
     else if (G == 32)
       hipLaunchKernelGGL((k_w8is_wide<32, ST>), grid, block, 0, stream, qx, sx, qw, iscale,
-                         inv_alpha, M, N, K, y, acc_out);
+                         inv_alpha, M, N, K, y, acc_out, 1, nullptr);
     else
       hipLaunchKernelGGL((k_w8is_wide<0, ST>), grid, block, 0, stream, qx, sx, qw, iscale,
-                         inv_alpha, M, N, K, y, acc_out);
+                         inv_alpha, M, N, K, y, acc_out, 1, nullptr);
     return;
   }
   const int tiles = ((M + 63) / 64) * ((N + 63) / 64);
@@ -609,9 +655,8 @@ hipError_t launch_w8a8_is(const int8_t* qx, const float* sx, const int8_t* qw, c
 }
 
 const char* w8a8_is_kernel_name(int64_t M, int64_t N, int64_t K) {
-  (void)K;
   if (M <= 64) return "k_w8is_split";
-  return w8is_use_wide((int)M, (int)N) ? "k_w8is_wide" : "k_w8is_tiled";
+  return w8is_use_wide((int)M, (int)N, (int)K) ? "k_w8is_wide" : "k_w8is_tiled";
 }
 
 }  // namespace bgt

@@ -39,6 +39,19 @@ hipError_t launch_w4a8(bool float_scale, const int8_t* qx, const float* sx, cons
                        int64_t M, int64_t N, int64_t K, OutY y, int32_t* acc_out,
                        hipStream_t stream, int32_t* ws = nullptr);
 
+// CUs of the current device (256 when it cannot be queried)
+int device_cus();
+
+// the library's split-K workspace on the current device, at least `bytes`
+// (allocated or grown on first need, never while `stream` is being captured);
+// nullptr if unavailable
+int32_t* split_workspace(size_t bytes, hipStream_t stream);
+
+// adds `splits` M x N int32 parts (exact mod 2^32) and converts each output
+// once: y = ((float)sum * sx[i]) * inv_alpha; y and acc_out rows ldn apart
+void launch_split_reduce(const int32_t* part, int splits, int M, int N, int ldn, const float* sx,
+                         float inv_alpha, OutY y, int32_t* acc_out, hipStream_t stream);
+
 // bytes of split-K workspace a W4A8 GEMM of this shape uses (0: none)
 size_t w4a8_split_bytes(int64_t M, int64_t N, int64_t K, bool float_scale);
 

@@ -242,7 +242,8 @@ def test_w8a8_is_validation(L):
     assert call(y=MIS) == bgt.BGT_ERR_ALIGN
     assert call(acc=MIS) == bgt.BGT_ERR_ALIGN
     assert bgt.w8a8_is_kernel_name(4, 4096, 14336) == "k_w8is_split"
-    assert bgt.w8a8_is_kernel_name(65, 4096, 14336) == "k_w8is_tiled"
+    assert bgt.w8a8_is_kernel_name(65, 4096, 14336) == "k_w8is_wide"   # 32 tiles, K split in 8
+    assert bgt.w8a8_is_kernel_name(100, 4096, 1024) == "k_w8is_tiled"  # 8 groups: no split
     assert bgt.w8a8_is_kernel_name(0, 4096, 14336) == "invalid shape"
     # dense W4A8: the decode kernel for K of 16 or 32 groups, and for 86 / 112
     # groups with one row block (M <= 16) where 2- or 4-wave workgroups apply

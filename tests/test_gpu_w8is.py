@@ -140,6 +140,30 @@ def test_w8is_narrow_scales(bgt, orc, dev, width, M, K, N):
     np.testing.assert_array_equal(y.cpu().numpy().view(np.int32), oy.astype(np.float32).view(np.int32))
 
 
+# (M, K, N): the 256 x 128 tiles fill at most half of the CUs, so the groups
+# split in S parts (65 x 4096: 4 parts of 8 groups; 3200: 25 groups in parts
+# of 12 and 13; 14336: 8 parts of 14) whose int32 sums a second kernel adds
+@pytest.mark.parametrize("M,K,N", [(65, 4096, 4096), (300, 3200, 528), (512, 14336, 1024)])
+def test_w8is_split_k(bgt, orc, dev, M, K, N):
+    assert bgt.w8a8_is_kernel_name(M, N, K) == "k_w8is_wide"
+    say(f"w8a8_gemm_is split K M={M} K={K} N={N}")
+    oq, os_, ow = _case(orc, 7 * M + K, M, K, N)
+    y = torch.full((M, N), float("nan"), dtype=torch.float32, device=dev)
+    acc = torch.full((M, N), -1, dtype=torch.int32, device=dev)
+    bgt.w8a8_gemm_is(to_dev(oq, dev), to_dev(os_, dev), to_dev(ow["qw"], dev),
+                     to_dev(ow["iscale"], dev), ALPHA, N, y=y, acc_out=acc)
+    oA, oy, ov = orc.w8a8_gemm_is(oq, os_, ow["codes"], ow["iscale"], ALPHA)
+    assert ov == 0
+    np.testing.assert_array_equal(acc.cpu().numpy().astype(np.int64), oA)
+    got = y.cpu().numpy()
+    assert not np.isnan(got).any()
+    np.testing.assert_array_equal(got.view(np.int32), oy.astype(np.float32).view(np.int32))
+    isc = bgt.narrow_iscale(to_dev(ow["iscale"], dev), 2)
+    yb = bgt.w8a8_gemm_is(to_dev(oq, dev), to_dev(os_, dev), to_dev(ow["qw"], dev), isc, ALPHA, N,
+                          out_dtype=torch.bfloat16)
+    np.testing.assert_array_equal(dev_bits16(yb), orc.f32_to_bf16_bits(oy.astype(np.float32)))
+
+
 @pytest.mark.parametrize("width", [1, 2])
 def test_w8is_wide_narrow_scales(bgt, orc, dev, width):
     M, K, N = 1000, 256, 4000
