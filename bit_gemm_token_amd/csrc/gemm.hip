@@ -871,14 +871,15 @@ __global__ __launch_bounds__(NW * 64) void k_w8a8_zp(
 
 // =====================================================================
 // Decode kernel (M <= 64, weight streaming): one wave owns one 16-column tile
-// for all K and all MR 16-row blocks of X, so no partial sums cross waves; a
-// workgroup of W waves serves W consecutive tiles.
+// for all K and MR/RS of the MR 16-row blocks of X (RS waves share a tile, each
+// streaming its weights), so no partial sums cross waves; a workgroup of W*RS
+// waves serves W consecutive tiles.
 //   X: the workgroup stages X (16*MR rows, clamped past M) in LDS in MFMA
 //      fragment order, one K chunk of CG groups (at most 64 KiB) at a time,
 //      double-buffered: fragment (g, rb, h) of a chunk = 1 KiB where lane L
 //      holds row 16rb + L%16, k = 128g + 64h + 16(L/16) .. +15. The next
 //      chunk's rows are loaded into registers under the current chunk's work;
-//      the chunk's fragments are dealt round-robin to the W waves.
+//      the chunk's fragments are dealt round-robin to the W*RS waves.
 //   W: each wave keeps D packed 1 KiB group blocks of its tile (16 bytes per
 //      lane, non-temporal) and their D scales in flight, refilling one slot
 //      per group; unpack by nibble-to-high-half (codes enter as 16*q), two
@@ -898,8 +899,8 @@ constexpr int decode_chunk_groups(int G, int MR, int D, int W) {
 }
 
 template <bool FS, int W, int D, int G, int MR, typename ST, bool FQ, int IT, bool GR = false,
-          int GQ = G>
-__global__ __launch_bounds__(W * 64) void k_w4a8_decode(
+          int GQ = G, int RS = 1>
+__global__ __launch_bounds__(W * RS * 64) void k_w4a8_decode(
     const int8_t* __restrict__ qx, const float* __restrict__ sx,
     const uint4* __restrict__ packed, const ST* __restrict__ iscale,
     const float* __restrict__ fscale, float inv_alpha, int M, int N,
@@ -909,16 +910,19 @@ __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
   constexpr int CG = decode_chunk_groups(G, MR, D, W);  // groups per X chunk (<= 64 KiB)
   constexpr int NCH = G / CG;                        // chunks
   constexpr int CFR = CG * MR * 2;                   // 1 KiB fragments per chunk
-  constexpr int FPW = (CFR + W - 1) / W;             // fragments per wave per chunk (the last may be short)
+  constexpr int NWV = W * RS;                        // waves of the workgroup
+  constexpr int MRW = MR / RS;                       // row blocks per wave
+  constexpr int FPW = (CFR + NWV - 1) / NWV;         // fragments per wave per chunk (the last may be short)
   using SL = typename std::conditional<FS, int32_t, ST>::type;   // scale element as stored
   constexpr int SCW = W * 16;                        // scale columns of the workgroup
   constexpr int SEL = 16 / sizeof(SL);               // scale elements per 16-byte chunk
   constexpr int SCT = G * SCW / SEL;                 // 16-byte scale chunks of the workgroup
-  constexpr int SCH = (SCT + W * 64 - 1) / (W * 64); // ... per thread
+  constexpr int SCH = (SCT + NWV * 64 - 1) / (NWV * 64); // ... per thread
   static_assert(G % D == 0 && G % CG == 0, "shape of the pipeline");
   static_assert(SCW % SEL == 0, "scale staging");
   static_assert(!FQ || (MR == 1 && NCH == 1 && !FS), "fused quantization: one row block, one chunk");
   static_assert(!(GR && FQ), "grouped GEMM takes quantized activations");
+  static_assert(RS >= 1 && MR % RS == 0 && (RS == 1 || (!FQ && !GR)), "row split: dense launches");
   constexpr int NBUF = NCH > 1 ? 2 : 1;
   __shared__ __align__(16) int8_t sA[NBUF * CFR * 1024];
   __shared__ __align__(16) SL sS[G * SCW];           // [group][column of the workgroup]
@@ -933,7 +937,8 @@ __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   const int c = lane % 16, s4 = lane / 16;
-  const int t = blockIdx.x * W + wave;
+  const int tw = wave % W, hr = wave / W;          // tile of the workgroup, row-block share
+  const int t = blockIdx.x * W + tw;
   const bool tvalid = t < T;
   const int tc = tvalid ? t : T - 1;
 
@@ -954,34 +959,34 @@ __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
     else iscale += e * rt.sstride;
   }
 
-  // ---- X chunk staging: this wave's fragments f = wave + W*i of chunk ch
+  // ---- X chunk staging: this wave's fragments f = wave + NWV*i of chunk ch
   // (32-bit offsets from the X base; grouped: the rows of the expert's slots,
   // looked up once)
   int xo[GR ? FPW : 1];
   if constexpr (GR) {
 #pragma unroll
     for (int i = 0; i < FPW; ++i) {
-      const int f = wave + W * i, rb = (f / 2) % MR;
+      const int f = wave + NWV * i, rb = (f / 2) % MR;
       const int row = 16 * rb + c < M ? 16 * rb + c : M - 1;
-      xo[i] = (CFR % W == 0 || f < CFR) ? clamp_route(rt.tok[r0 + row], 0, rt.T - 1) * K : 0;
+      xo[i] = (CFR % NWV == 0 || f < CFR) ? clamp_route(rt.tok[r0 + row], 0, rt.T - 1) * K : 0;
     }
   }
   v4i xa[FPW];
   auto load_chunk = [&](int ch) {
 #pragma unroll
     for (int i = 0; i < FPW; ++i) {
-      const int f = wave + W * i, gl = f / (2 * MR), rb = (f / 2) % MR, h = f % 2;
+      const int f = wave + NWV * i, gl = f / (2 * MR), rb = (f / 2) % MR, h = f % 2;
       const int row = 16 * rb + c < M ? 16 * rb + c : M - 1;
       const int ro = GR ? xo[GR ? i : 0] : row * K;
-      if (CFR % W == 0 || f < CFR)                   // wave-uniform
+      if (CFR % NWV == 0 || f < CFR)                 // wave-uniform
         xa[i] = load_v4i(qx + (ro + 128 * gq(ch * CG + gl) + 64 * h + 16 * s4));
     }
   };
   auto store_chunk = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < FPW; ++i)
-      if (CFR % W == 0 || wave + W * i < CFR)
-        *reinterpret_cast<v4i*>(sA + (buf * CFR + wave + W * i) * 1024 + lane * 16) = xa[i];
+      if (CFR % NWV == 0 || wave + NWV * i < CFR)
+        *reinterpret_cast<v4i*>(sA + (buf * CFR + wave + NWV * i) * 1024 + lane * 16) = xa[i];
   };
   // fused quantization (FQ, M <= 4): the rows (element type IT, widened to
   // fp32), each thread XV groups of 4 of every row, requested before the
@@ -1005,11 +1010,11 @@ __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
   v4i sv[SCH];
 #pragma unroll
   for (int u = 0; u < SCH; ++u) {
-    const int q = threadIdx.x + W * 64 * u, g = q / (SCW / SEL), c0 = (q % (SCW / SEL)) * SEL;
+    const int q = threadIdx.x + NWV * 64 * u, g = q / (SCW / SEL), c0 = (q % (SCW / SEL)) * SEL;
     const int col = blockIdx.x * SCW + c0 < N ? blockIdx.x * SCW + c0 : N - SEL;
     if (GQ < G && g >= GQ)
       sv[u] = v4i{0, 0, 0, 0};
-    else if (SCT % (W * 64) == 0 || q < SCT)
+    else if (SCT % (NWV * 64) == 0 || q < SCT)
       sv[u] = load_v4i(reinterpret_cast<const int8_t*>(scl + ((int64_t)g * N + col)));
   }
   // ---- first D groups of the tile in flight
@@ -1110,23 +1115,25 @@ __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
   }
 #pragma unroll
   for (int u = 0; u < SCH; ++u) {
-    const int q = threadIdx.x + W * 64 * u;
-    if (SCT % (W * 64) == 0 || q < SCT) *reinterpret_cast<v4i*>(sS + q * SEL) = sv[u];
+    const int q = threadIdx.x + NWV * 64 * u;
+    if (SCT % (NWV * 64) == 0 || q < SCT) *reinterpret_cast<v4i*>(sS + q * SEL) = sv[u];
   }
   if (NCH > 1) load_chunk(1);
   wait_lds0();
   lds_barrier();
 
-  int acc[MR][4];
-  float facc[MR][4];
+  // this wave's row blocks: hr*MRW .. hr*MRW + MRW - 1
+  int acc[MRW][4];
+  float facc[MRW][4];
 #pragma unroll
-  for (int rb = 0; rb < MR; ++rb)
+  for (int rb = 0; rb < MRW; ++rb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) { acc[rb][r] = 0; facc[rb][r] = 0.0f; }
   auto group = [&](int g, const uint4& w) {
-    int32_t sc = (int32_t)sS[g * SCW + wave * 16 + c];
+    int32_t sc = (int32_t)sS[g * SCW + tw * 16 + c];
     if (sizeof(SL) < 4) opaque_reg(sc);              // keep the 24-bit multiply-adds as written
-    const int8_t* base = sA + ((g / CG) % NBUF) * CFR * 1024 + (g % CG) * MR * 2048 + lane * 16;
+    const int8_t* base = sA + ((g / CG) % NBUF) * CFR * 1024 + (g % CG) * MR * 2048 + hr * MRW * 2048 +
+                         lane * 16;
     uint32_t x0, x1, x2, x3, x4, x5, x6, x7;
     unpack_x16(w.x, x0, x1);
     unpack_x16(w.y, x2, x3);
@@ -1135,7 +1142,7 @@ __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
     const v4i b0 = {(int)x0, (int)x1, (int)x2, (int)x3};
     const v4i b1 = {(int)x4, (int)x5, (int)x6, (int)x7};
 #pragma unroll
-    for (int rb = 0; rb < MR; ++rb) {
+    for (int rb = 0; rb < MRW; ++rb) {
       const v4i a0 = *reinterpret_cast<const v4i*>(base + rb * 2048);
       const v4i a1 = *reinterpret_cast<const v4i*>(base + rb * 2048 + 1024);
       v4i p = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, v4i{0, 0, 0, 0}, 0, 0, 0);
@@ -1176,10 +1183,10 @@ __global__ __launch_bounds__(W * 64) void k_w4a8_decode(
   if (tvalid) {
     const int j = t * 16 + c;
 #pragma unroll
-    for (int rb = 0; rb < MR; ++rb)
+    for (int rb = 0; rb < MRW; ++rb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int i = 16 * rb + 4 * s4 + r;
+        const int i = 16 * (hr * MRW + rb) + 4 * s4 + r;
         if (i >= M) continue;
         const int64_t o = (int64_t)(r0 + i) * N + j;
         const float si = sX[i];
@@ -1262,6 +1269,10 @@ constexpr int decode_waves(int T, int mr) {
 }
 // group blocks in flight per wave: fewer when each wave also holds several row blocks
 constexpr int decode_depth(int mr) { return mr == 1 ? 16 : 8; }
+// waves per 16-column tile: with four row blocks on 4- or 6-wave workgroups
+// each tile's blocks are split over two waves, so a SIMD holds two or three
+// waves of half the VALU work each (16 waves would leave too few registers)
+constexpr int decode_row_split(int mr, int w) { return mr == 4 && w <= 6 ? 2 : 1; }
 
 // K = 11008 (86 groups, run as 96 with the last ten masked) and K = 14336 (112)
 // take the decode kernel for one row block on 2- or 4-wave workgroups, whose
@@ -1409,11 +1420,12 @@ static void launch_decode_w(int mr, hipStream_t stream, const int8_t* qx, const 
   const void* nx = nullptr;
   int8_t* nq = nullptr;
   float* ns = nullptr;
-  const dim3 grid((N / 16 + W - 1) / W), block(W * kWave);
+  const dim3 grid((N / 16 + W - 1) / W);
 #define BGT_DECODE(MRR)                                                                           \
-  hipLaunchKernelGGL((k_w4a8_decode<FS, W, decode_depth(MRR), G, MRR, ST, false, kF32, false, GQ>), \
-                     grid, block, 0, stream, qx, sx, pk, iscale, fscale, inv_alpha, M, N, y,        \
-                     acc_out, nx, 0, nq, ns, Route{})
+  hipLaunchKernelGGL((k_w4a8_decode<FS, W, decode_depth(MRR), G, MRR, ST, false, kF32, false, GQ, \
+                                    decode_row_split(MRR, W)>),                                      \
+                     grid, dim3(W * decode_row_split(MRR, W) * kWave), 0, stream, qx, sx, pk, iscale,  \
+                     fscale, inv_alpha, M, N, y, acc_out, nx, 0, nq, ns, Route{})
   if constexpr (MRMAX == 1) {
     BGT_DECODE(1);
   } else {
