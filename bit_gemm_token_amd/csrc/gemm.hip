@@ -1717,6 +1717,15 @@ static bool moe_decode_path(int64_t T, int64_t R, int64_t E, int64_t K) {
   return T <= 1024 && (mean + rows - 1) / rows <= 4 && E * ((T + rows - 1) / rows) <= 2048;
 }
 
+// Past the decode range the experts' row tiles take the 256 x 128 tile kernel.
+// The 256 x 256 one runs them only when set_prefill_kernel() forces it (and
+// the gathered row offsets fit 32 bits): at the Mixtral expert shapes it
+// measured no faster (w1, T = 2048 / 4096: 515 / 772 us against 525 / 771)
+// or slower (w2: 466 / 708 against 404 / 665).
+static bool moe_wide_path(int64_t T, int64_t K) {
+  return g_prefill_kernel.load() == kPrefillWide && T * K < ((int64_t)1 << 31);
+}
+
 template <typename ST>
 static void launch_moe_t(const int8_t* qx, const float* sx, const uint8_t* packed,
                          const ST* iscale, float inv_alpha, int N, int K, const Route& rt,
@@ -1761,6 +1770,11 @@ static void launch_moe_t(const int8_t* qx, const float* sx, const uint8_t* packe
 #undef BGT_MOE_DECODE
     return;
   }
+  if (moe_wide_path(rt.T, K)) {
+    launch_w4a8_wide_grouped(qx, sx, packed, iscale, sizeof(ST), inv_alpha, N, K, rt, y, acc_out,
+                             stream);
+    return;
+  }
   const int tiles = ((rt.R + 255) / 256 + rt.E) * ((N + 127) / 128);
   hipLaunchKernelGGL((k_w4a8_prefill<4, 2, 2, 2, false, ST, true>), dim3(tiles), dim3(512), 0,
                      stream, qx, sx, pk, iscale, nullptr, inv_alpha, 0, N, K, N, y, acc_out, rt, 1,
@@ -1786,8 +1800,8 @@ hipError_t launch_w4a8_moe(const int8_t* qx, const float* sx, int64_t T, const i
 }
 
 const char* w4a8_moe_kernel_name(int64_t T, int64_t E, int64_t R, int64_t K) {
-  return moe_decode_path(T, R, E, K) ? "k_w4a8_decode<IS,grouped>"
-                                     : "k_w4a8_prefill<4,2,2,2,IS,grouped>";
+  if (moe_decode_path(T, R, E, K)) return "k_w4a8_decode<IS,grouped>";
+  return moe_wide_path(T, K) ? "k_w4a8_wide<IS,grouped>" : "k_w4a8_prefill<4,2,2,2,IS,grouped>";
 }
 
 hipError_t launch_w8a8_zp(const uint8_t* qx, const float* sx, const int32_t* zx,

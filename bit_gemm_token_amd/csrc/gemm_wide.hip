@@ -54,12 +54,12 @@ constexpr int kWW = kWB + kWS;                    // B + scale stage (17 KiB); t
 
 }  // namespace
 
-template <bool FS, typename ST>
+template <bool FS, typename ST, bool GR = false>
 __global__ __launch_bounds__(kWNW * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_w4a8_wide(
     const int8_t* __restrict__ qx, const float* __restrict__ sx,
     const uint8_t* __restrict__ packed, const ST* __restrict__ iscale,
     const float* __restrict__ fscale, float inv_alpha, int M, int N, int K, int ldn, OutY y,
-    int32_t* __restrict__ acc_out) {
+    int32_t* __restrict__ acc_out, Route rt) {
   constexpr int NW = kWNW;
   constexpr int A_MAX = (kWACopies + NW - 1) / NW;   // 5 activation copies for waves 0..3,
   constexpr int A_FULL = kWACopies - NW * (A_MAX - 1);   // 4 for the others
@@ -77,21 +77,44 @@ __global__ __launch_bounds__(kWNW * 64) __attribute__((amdgpu_waves_per_eu(2))) 
   const int lane = tid % kWave;
   const int lr = lane % 32, hf = lane / 32;
   int tm, tn;
-  tile_of(blockIdx.x, (M + kWBM - 1) / kWBM, (N + kWBN - 1) / kWBN, tm, tn);
+  // grouped GEMM: the grid covers ceil(R/256) + E row tiles, an upper bound on
+  // the sum over experts of ceil(rows/256); row tile tm is found in the list
+  // of the experts' tiles (experts in order), and tiles past its end exit.
+  // The expert's slots r0 .. r0+M-1 are its rows; slot r reads activation row
+  // tok[r] (row offsets fit 32 bits: T*K < 2^31, checked by the launcher)
+  tile_of(blockIdx.x, GR ? (rt.R + kWBM - 1) / kWBM + rt.E : (M + kWBM - 1) / kWBM,
+          (N + kWBN - 1) / kWBN, tm, tn);
+  int r0 = 0;
+  if constexpr (GR) {
+    int e = 0, a = 0;
+    for (; e < rt.E; ++e) {
+      a = clamp_route(rt.offs[e], 0, rt.R);
+      const int b = clamp_route(rt.offs[e + 1], a, rt.R);
+      const int nt = (b - a + kWBM - 1) / kWBM;
+      if (tm < nt) { M = b - a; break; }
+      tm -= nt;
+    }
+    if (e == rt.E) return;
+    r0 = a;
+    packed += e * rt.wstride;
+    if (FS) fscale += e * rt.sstride;
+    else iscale += e * rt.sstride;
+  }
   const int m0 = tm * kWBM, n0 = tn * kWBN;
 
   // ---- copy sources. A: copy i = wave + NW*t fills the 64 16-byte units
   // 64i .. 64i+63 of the stage; unit u holds row u/9, chunk u%9 of the group
   // (chunk 8 is the row's padding: it gets chunk 0, never read). Rows past M
   // read row M-1 (their outputs are never stored).
-  const int8_t* abase = qx + (int64_t)m0 * K;
+  const int8_t* abase = GR ? qx : qx + (int64_t)m0 * K;
   uint32_t aoff[A_MAX];                            // unsigned: base + zero-extended offset
 #pragma unroll
   for (int t = 0; t < A_MAX; ++t) {
     const int u = 64 * (wave + NW * t) + lane;
     const int r = u / 9, c = u % 9;
     const int rr = m0 + r < M ? r : M - 1 - m0;
-    aoff[t] = (uint32_t)(rr * K + 16 * (c < 8 ? c : 0));
+    const int ro = GR ? clamp_route(rt.tok[r0 + m0 + rr], 0, rt.T - 1) : rr;
+    aoff[t] = (uint32_t)ro * (uint32_t)K + (uint32_t)(16 * (c < 8 ? c : 0));
   }
   // B: wave w copies the packed group blocks of tiles 2w and 2w+1 (tiles past
   // N/16 read the last tile; their outputs are never stored)
@@ -319,13 +342,14 @@ __global__ __launch_bounds__(kWNW * 64) __attribute__((amdgpu_waves_per_eu(2))) 
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int i = m0 + rb * 32 + 8 * (r / 4) + 4 * hf + (r % 4);
-      srow[r] = sx[i < M ? i : M - 1];
+      const int ic = i < M ? i : M - 1;
+      srow[r] = sx[GR ? clamp_route(rt.tok[r0 + ic], 0, rt.T - 1) : ic];
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int i = m0 + rb * 32 + 8 * (r / 4) + 4 * hf + (r % 4);
       if (!full && (i >= M || j >= N)) continue;
-      const int64_t o = (int64_t)i * ldn + j;
+      const int64_t o = (int64_t)(r0 + i) * ldn + j;
       if (FS) {
         y.put_nt(o, facc[rb][r] * srow[r]);
       } else {
@@ -343,7 +367,16 @@ static void launch_wide_t(const int8_t* qx, const float* sx, const uint8_t* pack
                           int K, int ldn, OutY y, int32_t* acc_out, hipStream_t stream) {
   const int tiles = ((M + kWBM - 1) / kWBM) * ((N + kWBN - 1) / kWBN);
   hipLaunchKernelGGL((k_w4a8_wide<FS, ST>), dim3(tiles), dim3(kWNW * 64), 0, stream, qx, sx,
-                     packed, iscale, fscale, inv_alpha, M, N, K, ldn, y, acc_out);
+                     packed, iscale, fscale, inv_alpha, M, N, K, ldn, y, acc_out, Route{});
+}
+
+template <typename ST>
+static void launch_wide_grouped_t(const int8_t* qx, const float* sx, const uint8_t* packed,
+                                  const ST* iscale, float inv_alpha, int N, int K, const Route& rt,
+                                  OutY y, int32_t* acc_out, hipStream_t stream) {
+  const int tiles = ((rt.R + kWBM - 1) / kWBM + rt.E) * ((N + kWBN - 1) / kWBN);
+  hipLaunchKernelGGL((k_w4a8_wide<false, ST, true>), dim3(tiles), dim3(kWNW * 64), 0, stream, qx,
+                     sx, packed, iscale, nullptr, inv_alpha, 0, N, K, N, y, acc_out, rt);
 }
 
 void launch_w4a8_wide(bool float_scale, const int8_t* qx, const float* sx, const uint8_t* packed,
@@ -361,6 +394,20 @@ void launch_w4a8_wide(bool float_scale, const int8_t* qx, const float* sx, const
   else
     launch_wide_t<false>(qx, sx, packed, static_cast<const uint8_t*>(iscale), nullptr, inv_alpha,
                          M, N, K, ldn, y, acc_out, stream);
+}
+
+void launch_w4a8_wide_grouped(const int8_t* qx, const float* sx, const uint8_t* packed,
+                              const void* iscale, int iscale_bytes, float inv_alpha, int N, int K,
+                              const Route& rt, OutY y, int32_t* acc_out, hipStream_t stream) {
+  if (iscale_bytes == 4)
+    launch_wide_grouped_t(qx, sx, packed, static_cast<const int32_t*>(iscale), inv_alpha, N, K, rt,
+                          y, acc_out, stream);
+  else if (iscale_bytes == 2)
+    launch_wide_grouped_t(qx, sx, packed, static_cast<const uint16_t*>(iscale), inv_alpha, N, K,
+                          rt, y, acc_out, stream);
+  else
+    launch_wide_grouped_t(qx, sx, packed, static_cast<const uint8_t*>(iscale), inv_alpha, N, K, rt,
+                          y, acc_out, stream);
 }
 
 }  // namespace bgt

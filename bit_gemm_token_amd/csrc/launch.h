@@ -64,6 +64,11 @@ int32_t* noalloc_scratch(size_t* capacity);
 void launch_w4a8_wide(bool float_scale, const int8_t* qx, const float* sx, const uint8_t* packed,
                       const void* iscale, int iscale_bytes, const float* fscale, float inv_alpha,
                       int M, int N, int K, int ldn, OutY y, int32_t* acc_out, hipStream_t stream);
+// the same kernel over the experts' row tiles of a grouped GEMM (integer
+// scale; rows of y and acc_out are slots; requires T*K < 2^31)
+void launch_w4a8_wide_grouped(const int8_t* qx, const float* sx, const uint8_t* packed,
+                              const void* iscale, int iscale_bytes, float inv_alpha, int N, int K,
+                              const Route& rt, OutY y, int32_t* acc_out, hipStream_t stream);
 
 // per-token quantization of x (M x K of element type x_type, leading dimension
 // ldx) into q_out /

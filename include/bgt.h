@@ -429,8 +429,17 @@ const char* bgt_w4a8_kernel_name(int64_t M, int64_t N, int64_t K, int float_scal
  *                     rounds <= 3 * the 256 x 128 kernel's), else 256 x 128;
  *   BGT_PREFILL_WIDE  always the 256 x 256 tile kernel;
  *   BGT_PREFILL_TILED always the 256 x 128 tile kernel.
+ * The grouped GEMM (bgt_w4a8_moe_gemm_is) past its decode range takes the
+ * 256 x 128 kernel over the experts' row tiles, and the 256 x 256 one under
+ * BGT_PREFILL_WIDE (when T*K < 2^31).
  * Process-wide; takes effect for GEMMs launched after the call (set it before
  * capturing a graph). Returns BGT_OK, or BGT_ERR_MODE for another value. */
+
+#define BGT_PREFILL_AUTO 0
+#define BGT_PREFILL_WIDE 1
+#define BGT_PREFILL_TILED 2
+int bgt_set_prefill_kernel(int mode);
+
 /* Device workspace the integer-scale W4A8 GEMMs (bgt_w4a8_gemm_is, _narrow,
  * _ex) use for this shape, in bytes: 0 for most shapes; S*M*N*4 when the
  * 256 x 128 tile kernel splits K into S parts (M > 64 with few tiles: the
@@ -442,11 +451,6 @@ const char* bgt_w4a8_kernel_name(int64_t M, int64_t N, int64_t K, int float_scal
  * Calls that overlap on one device (several streams) share the buffer and
  * race. Negative: the status of an invalid shape. */
 int64_t bgt_w4a8_workspace_bytes(int64_t M, int64_t N, int64_t K);
-
-#define BGT_PREFILL_AUTO 0
-#define BGT_PREFILL_WIDE 1
-#define BGT_PREFILL_TILED 2
-int bgt_set_prefill_kernel(int mode);
 
 #ifdef __cplusplus
 }

@@ -6,7 +6,9 @@ K/128 in {16, 32, 112}: one workgroup row per expert and row pass, experts
 without tokens skipped) and on the tiled path (the experts' row tiles in one launch), with
 skewed and degenerate routings, narrow scales, fp16 / bf16 outputs, and the
 Mixtral-8x7B expert shapes (w1/w3: 4096 -> 14336, w2: 14336 -> 4096) on
-sampled columns.
+sampled columns. The 256 x 256 tile kernel over the experts' row tiles runs
+when bgt_set_prefill_kernel forces it: on small, ragged, skewed and
+Mixtral-sized routings, with narrow scales and half outputs.
 """
 import numpy as np
 import pytest
@@ -95,6 +97,7 @@ def _run(bgt, orc, dev, T, E, K, N, seed, routing=None, width=4, out_dtype=None,
 
 DECODE = "k_w4a8_decode<IS,grouped>"
 TILED = "k_w4a8_prefill<4,2,2,2,IS,grouped>"
+WIDE = "k_w4a8_wide<IS,grouped>"
 
 
 @pytest.mark.parametrize("T,E,K,N", [(1, 8, 4096, 64), (5, 8, 4096, 208), (16, 8, 2048, 96),
@@ -117,12 +120,54 @@ def test_moe_decode_path(bgt, orc, dev, T, E, K, N):
                                      (130, 4, 640, 400), (257, 8, 128, 16),
                                      # past the decode kernel's range: T > 1024, or more than
                                      # four row passes for the mean expert
-                                     (1100, 8, 4096, 16), (600, 8, 14336, 16), (700, 2, 2048, 32)])
+                                     (1100, 8, 4096, 16), (600, 8, 14336, 16), (700, 2, 2048, 32),
+                                     (1100, 16, 512, 48)])
 def test_moe_tiled_path(bgt, orc, dev, T, E, K, N):
     name = bgt.w4a8_moe_kernel_name(T, E, T * min(2, E), K)
     say(f"moe {name} T={T} E={E} K={K} N={N}")
     assert name == TILED
     _run(bgt, orc, dev, T, E, K, N, seed=T * 37 + K + N)
+
+
+@pytest.fixture
+def forced(bgt):
+    yield bgt.set_prefill_kernel
+    bgt.set_prefill_kernel("auto")
+
+
+@pytest.mark.parametrize("T,E,K,N", [(65, 8, 512, 144), (300, 8, 256, 48), (20, 8, 1152, 64),
+                                     (130, 4, 640, 400), (257, 8, 128, 16), (600, 8, 14336, 16),
+                                     (1100, 8, 4096, 16), (700, 2, 2048, 32), (1200, 4, 512, 400),
+                                     (2100, 8, 14336, 16), (1500, 3, 384, 272)])
+def test_moe_wide_forced(bgt, orc, dev, forced, T, E, K, N):
+    forced("wide")
+    name = bgt.w4a8_moe_kernel_name(T, E, T * min(2, E), K)
+    say(f"moe forced {name} T={T} E={E} K={K} N={N}")
+    assert name == WIDE
+    _run(bgt, orc, dev, T, E, K, N, seed=T * 43 + K + N)
+
+
+def test_moe_wide_forced_skewed_narrow_half(bgt, orc, dev, forced):
+    forced("wide")
+    T, K = 300, 4096
+    say(f"moe forced wide: one busy expert, narrow scales, half outputs T={T} K={K}")
+    routing = np.full((T, 1), 5, np.int32)
+    routing[0, 0] = 2
+    _run(bgt, orc, dev, T, 8, K, 64, seed=T + 5, routing=routing)
+    for width in (1, 2):
+        _run(bgt, orc, dev, 150, 8, 384, 96, seed=150 + width, width=width)
+    for dt in (torch.float16, torch.bfloat16):
+        _run(bgt, orc, dev, 100, 8, 256, 48, seed=117, out_dtype=dt)
+
+
+def test_moe_wide_forced_mixtral_sampled(bgt, orc, dev, forced):
+    forced("wide")
+    T, K, N = 4096, 4096, 14336
+    assert bgt.w4a8_moe_kernel_name(T, 8, 2 * T, K) == WIDE
+    say(f"moe forced wide mixtral T={T} K={K} N={N} (sampled)")
+    cols = np.unique(np.concatenate([np.arange(0, 32), np.arange(N - 32, N),
+                                     np.random.default_rng(T + 1).choice(N, 160, replace=False)]))
+    _run(bgt, orc, dev, T, 8, K, N, seed=T + 23, cols=cols)
 
 
 @pytest.mark.parametrize("T,K", [(64, 4096), (200, 512), (64, 14336), (40, 2048), (300, 4096),
@@ -151,7 +196,8 @@ def test_moe_half_outputs(bgt, orc, dev, T, K):
 
 
 @pytest.mark.parametrize("T,K,N", [(16, 4096, 14336), (64, 4096, 14336), (512, 4096, 14336),
-                                   (16, 14336, 4096), (64, 14336, 4096), (512, 14336, 4096)])
+                                   (4096, 4096, 14336), (16, 14336, 4096), (64, 14336, 4096),
+                                   (512, 14336, 4096), (4096, 14336, 4096)])
 def test_moe_mixtral_shapes_sampled(bgt, orc, dev, T, K, N):
     """Mixtral-8x7B experts (8, top-2) at the w1/w3 and w2 shapes, in the
     launches the bench times; sampled output columns against the oracle."""
