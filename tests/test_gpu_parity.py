@@ -208,6 +208,9 @@ SHAPES = [(1, 128, 16), (3, 384, 48), (16, 1024, 144), (17, 512, 64), (33, 256, 
           # the same kernel with 6 and 8 waves per workgroup (N/16 > 1024 and > 1536 tiles;
           # the last workgroup partly past N)
           (3, 4096, 16400), (20, 2048, 24576), (1, 4096, 24592), (50, 2048, 28672),
+          # four row blocks split over two waves per tile on 4- and 6-wave workgroups
+          # (the second wave's last block ragged at M = 49, 57, 61)
+          (49, 4096, 4096), (57, 2048, 20480), (61, 4096, 16400),
           # 86 groups (run as 96, the last ten masked) and 112 groups, one row block on 2-wave
           # (N <= 8192) and 4-wave workgroups; more rows take the weight-split kernels
           (1, 11008, 64), (16, 11008, 80), (2, 11008, 8208), (5, 14336, 48), (16, 14336, 4096),
