@@ -889,11 +889,12 @@ __global__ __launch_bounds__(NW * 64) void k_w8a8_zp(
 // Every load is a register load, so the compiler's wait counts stay exact.
 // =====================================================================
 // groups per staged X chunk: the largest divisor of G up to 32 (one row
-// block; 16 on 2-wave workgroups, so a wave stages at most 16 fragments) or 8
-// (more), so a chunk is at most 64 KiB, that is a multiple of the weight ring
-// depth D
-constexpr int decode_chunk_groups(int G, int MR, int D, int W) {
-  int c = MR == 1 ? (W >= 4 ? 32 : 16) : 8;
+// block; 16 on 2-wave workgroups, so a wave stages at most 16 fragments,
+// unless the rows are quantized in the kernel and written to LDS directly)
+// or 8 (more), so a chunk is at most 64 KiB, that is a multiple of the weight
+// ring depth D
+constexpr int decode_chunk_groups(int G, int MR, int D, int W, bool FQ) {
+  int c = MR == 1 ? (W >= 4 || FQ ? 32 : 16) : 8;
   while (c > D && (G % c != 0 || c % D != 0)) --c;
   return c;
 }
@@ -907,7 +908,7 @@ __global__ __launch_bounds__(W * RS * 64) void k_w4a8_decode(
     OutY y, int32_t* __restrict__ acc_out,
     const void* __restrict__ xf, int ldx, int8_t* __restrict__ q_out, float* __restrict__ s_out,
     Route rt) {
-  constexpr int CG = decode_chunk_groups(G, MR, D, W);  // groups per X chunk (<= 64 KiB)
+  constexpr int CG = decode_chunk_groups(G, MR, D, W, FQ);  // groups per X chunk (<= 64 KiB)
   constexpr int NCH = G / CG;                        // chunks
   constexpr int CFR = CG * MR * 2;                   // 1 KiB fragments per chunk
   constexpr int NWV = W * RS;                        // waves of the workgroup
@@ -989,10 +990,12 @@ __global__ __launch_bounds__(W * RS * 64) void k_w4a8_decode(
         *reinterpret_cast<v4i*>(sA + (buf * CFR + wave + NWV * i) * 1024 + lane * 16) = xa[i];
   };
   // fused quantization (FQ, M <= 4): the rows (element type IT, widened to
-  // fp32), each thread XV groups of 4 of every row, requested before the
-  // scales and the weights
-  constexpr int XV = FQ ? K / 4 / (W * 64) : 1;
-  static_assert(!FQ || XV * W * 64 * 4 == K, "row split");
+  // fp32), each thread XV groups of 4 of every row (the last one partial when
+  // K/4 is not a multiple of the workgroup's threads: zeros past the row),
+  // requested before the scales and the weights
+  constexpr int XV = FQ ? (K / 4 + W * 64 - 1) / (W * 64) : 1;
+  constexpr bool XR = FQ && XV * W * 64 * 4 != K;
+  auto xin = [&](int v) { return !XR || v < XV - 1 || (int)threadIdx.x + W * 64 * v < K / 4; };
   float4 xv[4][XV];
   if constexpr (FQ) {
 #pragma unroll
@@ -1000,7 +1003,8 @@ __global__ __launch_bounds__(W * RS * 64) void k_w4a8_decode(
 #pragma unroll
       for (int v = 0; v < XV; ++v)
         if (i < M)
-          xv[i][v] = load_x4<IT>(xf, (int64_t)i * (ldx / 4) + threadIdx.x + W * 64 * v);
+          xv[i][v] = xin(v) ? load_x4<IT>(xf, (int64_t)i * (ldx / 4) + threadIdx.x + W * 64 * v)
+                            : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   } else {
     load_chunk(0);
   }
@@ -1097,6 +1101,7 @@ __global__ __launch_bounds__(W * RS * 64) void k_w4a8_decode(
         }
 #pragma unroll
         for (int v = 0; v < XV; ++v) {
+          if (!xin(v)) continue;
           const int k = 4 * (threadIdx.x + W * 64 * v);
           // fragment (group g, half h) lane 16*(k%64/16) + row, byte k%16
           const int g = k / 128, h = (k % 128) / 64, sq = (k % 64) / 16;
@@ -1260,7 +1265,7 @@ struct W4Plan { W4Path path; int mr; int wide_cols = 0; };
 // (decode kernel when K is a multiple of 16 groups and the X block fits LDS;
 // else the stream kernel while its loader waves and exchange area fit a
 // workgroup; else the skinny kernel); larger M takes the LDS-tiled MFMA kernel.
-constexpr int kDecodeW = 8;                        // waves (tiles) per decode workgroup (fused, grouped)
+constexpr int kDecodeW = 8;                        // waves (tiles) per grouped decode workgroup
 // dense decode: waves per workgroup from the tile count T = N/16, so that the
 // T/W workgroups (one per CU, each streaming W tiles) spread over the 256 CUs
 // (2-wave workgroups for one row block only: more would not fit the registers)
@@ -1627,21 +1632,41 @@ hipError_t launch_w4a8(bool float_scale, const int8_t* qx, const float* sx, cons
 
 // Quantize + GEMM in one launch for M <= 4 on the decode path (the decode
 // kernel quantizes the fp32 rows itself); otherwise the quantizer and the GEMM.
+// Waves (tiles) per workgroup as for the unfused decode launch, but enough
+// that a thread's share of the rows (held until they are quantized) is at
+// most 8 groups of 4 elements, M*K/4 <= 8*64*W: the quantizing prologue's
+// critical path grows with that share (measured at M = 4: 8 waves 11.2 us
+// against 2 waves 11.4 us at N = 4096; at M = 1, 2 waves 6.6 against 8.4)
+template <int IT, typename ST, int W>
+static void launch_linear_fused_w(const void* x, int ldx, const uint4* pk, const ST* iscale,
+                                  float inv_alpha, int M, int N, int K, int8_t* q_out,
+                                  float* s_out, OutY y, hipStream_t stream) {
+  const dim3 grid((N / 16 + W - 1) / W), block(W * kWave);
+  if (K / kGroup == 32)
+    hipLaunchKernelGGL((k_w4a8_decode<false, W, decode_depth(1), 32, 1, ST, true, IT>), grid,
+                       block, 0, stream, nullptr, nullptr, pk, iscale, nullptr, inv_alpha, M, N,
+                       y, nullptr, x, ldx, q_out, s_out, Route{});
+  else
+    hipLaunchKernelGGL((k_w4a8_decode<false, W, decode_depth(1), 16, 1, ST, true, IT>), grid,
+                       block, 0, stream, nullptr, nullptr, pk, iscale, nullptr, inv_alpha, M, N,
+                       y, nullptr, x, ldx, q_out, s_out, Route{});
+}
+
 template <int IT, typename ST>
 static void launch_linear_fused(const void* x, int ldx, const uint8_t* packed, const ST* iscale,
                                 float inv_alpha, int M, int N, int K, int8_t* q_out,
                                 float* s_out, OutY y, hipStream_t stream) {
-  const int T = N / 16;
-  const dim3 grid((T + kDecodeW - 1) / kDecodeW), block(kDecodeW * kWave);
+  int w = decode_waves(N / 16, 1);
+  while (w < 8 && M * K > 2048 * w) w += 2;
   const uint4* pk = reinterpret_cast<const uint4*>(packed);
-  if (K / kGroup == 32)
-    hipLaunchKernelGGL((k_w4a8_decode<false, kDecodeW, decode_depth(1), 32, 1, ST, true, IT>), grid,
-                       block, 0, stream, nullptr, nullptr, pk, iscale, nullptr, inv_alpha, M, N,
-                       y, nullptr, x, ldx, q_out, s_out, Route{});
+  if (w == 2)
+    launch_linear_fused_w<IT, ST, 2>(x, ldx, pk, iscale, inv_alpha, M, N, K, q_out, s_out, y, stream);
+  else if (w == 4)
+    launch_linear_fused_w<IT, ST, 4>(x, ldx, pk, iscale, inv_alpha, M, N, K, q_out, s_out, y, stream);
+  else if (w == 6)
+    launch_linear_fused_w<IT, ST, 6>(x, ldx, pk, iscale, inv_alpha, M, N, K, q_out, s_out, y, stream);
   else
-    hipLaunchKernelGGL((k_w4a8_decode<false, kDecodeW, decode_depth(1), 16, 1, ST, true, IT>), grid,
-                       block, 0, stream, nullptr, nullptr, pk, iscale, nullptr, inv_alpha, M, N,
-                       y, nullptr, x, ldx, q_out, s_out, Route{});
+    launch_linear_fused_w<IT, ST, 8>(x, ldx, pk, iscale, inv_alpha, M, N, K, q_out, s_out, y, stream);
 }
 
 bool w4a8_linear_fused(int64_t M, int64_t K, const void* x, int64_t ldx) {

@@ -75,7 +75,12 @@ def _check(bgt, orc, dev, x, ow, N, width=4, ldx_pad=0, expect_fused=None):
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 4096, 1376), (2, 4096, 272), (3, 2048, 528), (4, 4096, 400),
-                                   (4, 2048, 16)])
+                                   (4, 2048, 16),
+                                   # 4, 6 and 8 waves per workgroup (N/16 tiles past 512, 1024,
+                                   # 1536); on 6 waves each thread's last group of four row
+                                   # elements is partial (K/4 not a multiple of 384)
+                                   (2, 4096, 11008), (4, 2048, 8208), (3, 2048, 20480),
+                                   (1, 4096, 28672)])
 def test_linear_fused(bgt, orc, dev, M, K, N):
     say(f"w4a8_linear_is fused M={M} K={K} N={N}")
     x = synth.activations(40 + M, M, K)
