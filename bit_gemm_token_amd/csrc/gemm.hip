@@ -892,26 +892,26 @@ __global__ __launch_bounds__(NW * 64) void k_w8a8_zp(
 // block; 16 on 2-wave workgroups, so a wave stages at most 16 fragments,
 // unless the rows are quantized in the kernel and written to LDS directly)
 // or 8 (more), so a chunk is at most 64 KiB, that is a multiple of the weight
-// ring depth D
-constexpr int decode_chunk_groups(int G, int MR, int D, int W, bool FQ) {
-  int c = MR == 1 ? (W >= 4 || FQ ? 32 : 16) : 8;
+// ring depth D; NW = the workgroup's waves
+constexpr int decode_chunk_groups(int G, int MR, int D, int NW, bool FQ) {
+  int c = MR == 1 ? (NW >= 4 || FQ ? 32 : 16) : 8;
   while (c > D && (G % c != 0 || c % D != 0)) --c;
   return c;
 }
 
 template <bool FS, int W, int D, int G, int MR, typename ST, bool FQ, int IT, bool GR = false,
-          int GQ = G, int RS = 1>
-__global__ __launch_bounds__(W * RS * 64) void k_w4a8_decode(
+          int GQ = G, int RS = 1, int KS = 1>
+__global__ __launch_bounds__(W * RS * KS * 64) void k_w4a8_decode(
     const int8_t* __restrict__ qx, const float* __restrict__ sx,
     const uint4* __restrict__ packed, const ST* __restrict__ iscale,
     const float* __restrict__ fscale, float inv_alpha, int M, int N,
     OutY y, int32_t* __restrict__ acc_out,
     const void* __restrict__ xf, int ldx, int8_t* __restrict__ q_out, float* __restrict__ s_out,
     Route rt) {
-  constexpr int CG = decode_chunk_groups(G, MR, D, W, FQ);  // groups per X chunk (<= 64 KiB)
+  constexpr int NWV = W * RS * KS;                   // waves of the workgroup
+  constexpr int CG = decode_chunk_groups(G, MR, D, NWV, FQ);  // groups per X chunk (<= 64 KiB)
   constexpr int NCH = G / CG;                        // chunks
   constexpr int CFR = CG * MR * 2;                   // 1 KiB fragments per chunk
-  constexpr int NWV = W * RS;                        // waves of the workgroup
   constexpr int MRW = MR / RS;                       // row blocks per wave
   constexpr int FPW = (CFR + NWV - 1) / NWV;         // fragments per wave per chunk (the last may be short)
   using SL = typename std::conditional<FS, int32_t, ST>::type;   // scale element as stored
@@ -924,6 +924,10 @@ __global__ __launch_bounds__(W * RS * 64) void k_w4a8_decode(
   static_assert(!FQ || (MR == 1 && NCH == 1 && !FS), "fused quantization: one row block, one chunk");
   static_assert(!(GR && FQ), "grouped GEMM takes quantized activations");
   static_assert(RS >= 1 && MR % RS == 0 && (RS == 1 || (!FQ && !GR)), "row split: dense launches");
+  static_assert(KS == 1 || (RS == 1 && MR == 1 && NCH == 1 && !FS && !GR && G % KS == 0),
+                "K split: one row block and one X chunk, integer scale");
+  constexpr int GK = G / KS;                         // groups per wave
+  constexpr int DK = D < GK ? D : GK;                // ... of them in flight
   constexpr int NBUF = NCH > 1 ? 2 : 1;
   __shared__ __align__(16) int8_t sA[NBUF * CFR * 1024];
   __shared__ __align__(16) SL sS[G * SCW];           // [group][column of the workgroup]
@@ -938,7 +942,8 @@ __global__ __launch_bounds__(W * RS * 64) void k_w4a8_decode(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   const int c = lane % 16, s4 = lane / 16;
-  const int tw = wave % W, hr = wave / W;          // tile of the workgroup, row-block share
+  // tile of the workgroup, row-block share, K share
+  const int tw = wave % W, hr = (wave / W) % RS, ks = wave / (W * RS);
   const int t = blockIdx.x * W + tw;
   const bool tvalid = t < T;
   const int tc = tvalid ? t : T - 1;
@@ -993,9 +998,9 @@ __global__ __launch_bounds__(W * RS * 64) void k_w4a8_decode(
   // fp32), each thread XV groups of 4 of every row (the last one partial when
   // K/4 is not a multiple of the workgroup's threads: zeros past the row),
   // requested before the scales and the weights
-  constexpr int XV = FQ ? (K / 4 + W * 64 - 1) / (W * 64) : 1;
-  constexpr bool XR = FQ && XV * W * 64 * 4 != K;
-  auto xin = [&](int v) { return !XR || v < XV - 1 || (int)threadIdx.x + W * 64 * v < K / 4; };
+  constexpr int XV = FQ ? (K / 4 + NWV * 64 - 1) / (NWV * 64) : 1;
+  constexpr bool XR = FQ && XV * NWV * 64 * 4 != K;
+  auto xin = [&](int v) { return !XR || v < XV - 1 || (int)threadIdx.x + NWV * 64 * v < K / 4; };
   float4 xv[4][XV];
   if constexpr (FQ) {
 #pragma unroll
@@ -1003,7 +1008,7 @@ __global__ __launch_bounds__(W * RS * 64) void k_w4a8_decode(
 #pragma unroll
       for (int v = 0; v < XV; ++v)
         if (i < M)
-          xv[i][v] = xin(v) ? load_x4<IT>(xf, (int64_t)i * (ldx / 4) + threadIdx.x + W * 64 * v)
+          xv[i][v] = xin(v) ? load_x4<IT>(xf, (int64_t)i * (ldx / 4) + threadIdx.x + NWV * 64 * v)
                             : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   } else {
     load_chunk(0);
@@ -1021,11 +1026,13 @@ __global__ __launch_bounds__(W * RS * 64) void k_w4a8_decode(
     else if (SCT % (NWV * 64) == 0 || q < SCT)
       sv[u] = load_v4i(reinterpret_cast<const int8_t*>(scl + ((int64_t)g * N + col)));
   }
-  // ---- first D groups of the tile in flight
+  // ---- first D groups of the tile in flight (K split: of this wave's GK
+  // groups from g0w, DK in flight)
   const uint4* wsrc = packed + (int64_t)tc * GQ * 64 + lane;
-  uint4 wb[D];
+  const int g0w = ks * GK;
+  uint4 wb[DK];
 #pragma unroll
-  for (int j = 0; j < D; ++j) wb[j] = load_u4_nt(wsrc + (int64_t)gq(j) * 64);
+  for (int j = 0; j < DK; ++j) wb[j] = load_u4_nt(wsrc + (int64_t)gq(g0w + j) * 64);
   if constexpr (FQ) {
     // ---- per-token quantization of the rows, as the quantizer computes it:
     // a = max|x|, s = a / 127, q = clamp(round(x / s), -127, 127) (s = 0 -> 0).
@@ -1033,7 +1040,7 @@ __global__ __launch_bounds__(W * RS * 64) void k_w4a8_decode(
     // 1990): with r = 1/s correctly rounded, q0 = x*r, e = fma(-q0, s, x)
     // (exact), fma(e, r, q0) is x / s correctly rounded while s, r and the
     // residual stay normal; rows with an extreme scale take the division.
-    __shared__ float sAm[4 * W];
+    __shared__ float sAm[4 * NWV];
     float am[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -1050,12 +1057,12 @@ __global__ __launch_bounds__(W * RS * 64) void k_w4a8_decode(
       for (int i = 0; i < 4; ++i) am[i] = fmaxf(am[i], __shfl_xor(am[i], o, kWave));
     if (lane == 0)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sAm[i * W + wave] = am[i];
+      for (int i = 0; i < 4; ++i) sAm[i * NWV + wave] = am[i];
     // rows M..15 of the fragment block are zero codes
 #pragma unroll
     for (int i = 0; i < FPW; ++i)
-      if (c >= M && (CFR % W == 0 || wave + W * i < CFR))
-        *reinterpret_cast<v4i*>(sA + (wave + W * i) * 1024 + lane * 16) = v4i{0, 0, 0, 0};
+      if (c >= M && (CFR % NWV == 0 || wave + NWV * i < CFR))
+        *reinterpret_cast<v4i*>(sA + (wave + NWV * i) * 1024 + lane * 16) = v4i{0, 0, 0, 0};
     wait_lds0();
     lds_barrier();
     // codes of one float4: MODE 0 all zero (s = 0), 1 corrected product, 2 division
@@ -1077,9 +1084,9 @@ __global__ __launch_bounds__(W * RS * 64) void k_w4a8_decode(
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (i < M) {
-        float a = sAm[i * W];
+        float a = sAm[i * NWV];
 #pragma unroll
-        for (int w = 1; w < W; ++w) a = fmaxf(a, sAm[i * W + w]);
+        for (int w = 1; w < NWV; ++w) a = fmaxf(a, sAm[i * NWV + w]);
         const float sc = a / 127.0f;
         const float r = 1.0f / sc;
         if (threadIdx.x == i) {
@@ -1102,7 +1109,7 @@ __global__ __launch_bounds__(W * RS * 64) void k_w4a8_decode(
 #pragma unroll
         for (int v = 0; v < XV; ++v) {
           if (!xin(v)) continue;
-          const int k = 4 * (threadIdx.x + W * 64 * v);
+          const int k = 4 * (threadIdx.x + NWV * 64 * v);
           // fragment (group g, half h) lane 16*(k%64/16) + row, byte k%16
           const int g = k / 128, h = (k % 128) / 64, sq = (k % 64) / 16;
           *reinterpret_cast<uint32_t*>(sA + (g * 2 + h) * 1024 + (16 * sq + i) * 16 + k % 16) = word[v];
@@ -1180,9 +1187,34 @@ __global__ __launch_bounds__(W * RS * 64) void k_w4a8_decode(
       lds_barrier();
     }
   };
+  if constexpr (KS > 1) {
+#pragma unroll
+    for (int gl = 0; gl < GK; ++gl) {
+      const int g = g0w + gl;
+      group(g, wb[gl % DK]);
+      if (gl + DK < GK) wb[gl % DK] = load_u4_nt(wsrc + (int64_t)gq(g + DK) * 64);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // K split: the other waves' int32 sums of the tile meet wave ks = 0's
+    // in LDS (wrapping adds, exact in any order), which converts
+    __shared__ int32_t sRed[(KS > 1 ? KS - 1 : 1) * W * 4 * kWave];
+    if (ks > 0)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sRed[(((ks - 1) * W + tw) * 4 + r) * kWave + lane] = acc[0][r];
+    wait_lds0();
+    lds_barrier();
+    if (ks > 0) return;
+#pragma unroll
+    for (int k = 1; k < KS; ++k)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        acc[0][r] = (int32_t)((uint32_t)acc[0][r] +
+                              (uint32_t)sRed[(((k - 1) * W + tw) * 4 + r) * kWave + lane]);
+  } else {
 #pragma unroll 1
-  for (int ch = 0; ch < NCH - 1; ++ch) chunk(ch, std::false_type{});
-  chunk(NCH - 1, std::true_type{});
+    for (int ch = 0; ch < NCH - 1; ++ch) chunk(ch, std::false_type{});
+    chunk(NCH - 1, std::true_type{});
+  }
 
   // ---- one conversion per output
   if (tvalid) {
@@ -1278,6 +1310,14 @@ constexpr int decode_depth(int mr) { return mr == 1 ? 16 : 8; }
 // each tile's blocks are split over two waves, so a SIMD holds two or three
 // waves of half the VALU work each (16 waves would leave too few registers)
 constexpr int decode_row_split(int mr, int w) { return mr == 4 && w <= 6 ? 2 : 1; }
+// waves per 16-column tile splitting K (integer scale, one row block, 16 or 32
+// groups): 2-wave workgroups (N/16 <= 512 tiles) take 8 waves, each streaming
+// a quarter of the tile's groups, all of them in flight (one round trip to
+// memory instead of two); their sums meet in LDS. (On 4-wave workgroups a
+// split in two measured no faster: 688 tiles already fill the CUs.)
+constexpr int decode_k_split(int mr, int w, bool fs, int g, int gq) {
+  return mr != 1 || fs || g != gq || (g != 16 && g != 32) || w != 2 ? 1 : 4;
+}
 
 // K = 11008 (86 groups, run as 96 with the last ten masked) and K = 14336 (112)
 // take the decode kernel for one row block on 2- or 4-wave workgroups, whose
@@ -1428,9 +1468,12 @@ static void launch_decode_w(int mr, hipStream_t stream, const int8_t* qx, const 
   const dim3 grid((N / 16 + W - 1) / W);
 #define BGT_DECODE(MRR)                                                                           \
   hipLaunchKernelGGL((k_w4a8_decode<FS, W, decode_depth(MRR), G, MRR, ST, false, kF32, false, GQ, \
-                                    decode_row_split(MRR, W)>),                                      \
-                     grid, dim3(W * decode_row_split(MRR, W) * kWave), 0, stream, qx, sx, pk, iscale,  \
-                     fscale, inv_alpha, M, N, y, acc_out, nx, 0, nq, ns, Route{})
+                                    decode_row_split(MRR, W),                                     \
+                                    decode_k_split(MRR, W, FS, G, GQ)>),                          \
+                     grid,                                                                        \
+                     dim3(W * decode_row_split(MRR, W) * decode_k_split(MRR, W, FS, G, GQ) * kWave), \
+                     0, stream, qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out, nx, 0, nq, \
+                     ns, Route{})
   if constexpr (MRMAX == 1) {
     BGT_DECODE(1);
   } else {
@@ -1641,15 +1684,16 @@ template <int IT, typename ST, int W>
 static void launch_linear_fused_w(const void* x, int ldx, const uint4* pk, const ST* iscale,
                                   float inv_alpha, int M, int N, int K, int8_t* q_out,
                                   float* s_out, OutY y, hipStream_t stream) {
-  const dim3 grid((N / 16 + W - 1) / W), block(W * kWave);
+  constexpr int KS = decode_k_split(1, W, false, 32, 32);
+  const dim3 grid((N / 16 + W - 1) / W), block(W * KS * kWave);
   if (K / kGroup == 32)
-    hipLaunchKernelGGL((k_w4a8_decode<false, W, decode_depth(1), 32, 1, ST, true, IT>), grid,
-                       block, 0, stream, nullptr, nullptr, pk, iscale, nullptr, inv_alpha, M, N,
-                       y, nullptr, x, ldx, q_out, s_out, Route{});
+    hipLaunchKernelGGL((k_w4a8_decode<false, W, decode_depth(1), 32, 1, ST, true, IT, false, 32, 1, KS>),
+                       grid, block, 0, stream, nullptr, nullptr, pk, iscale, nullptr, inv_alpha, M,
+                       N, y, nullptr, x, ldx, q_out, s_out, Route{});
   else
-    hipLaunchKernelGGL((k_w4a8_decode<false, W, decode_depth(1), 16, 1, ST, true, IT>), grid,
-                       block, 0, stream, nullptr, nullptr, pk, iscale, nullptr, inv_alpha, M, N,
-                       y, nullptr, x, ldx, q_out, s_out, Route{});
+    hipLaunchKernelGGL((k_w4a8_decode<false, W, decode_depth(1), 16, 1, ST, true, IT, false, 16, 1, KS>),
+                       grid, block, 0, stream, nullptr, nullptr, pk, iscale, nullptr, inv_alpha, M,
+                       N, y, nullptr, x, ldx, q_out, s_out, Route{});
 }
 
 template <int IT, typename ST>
@@ -1657,7 +1701,7 @@ static void launch_linear_fused(const void* x, int ldx, const uint8_t* packed, c
                                 float inv_alpha, int M, int N, int K, int8_t* q_out,
                                 float* s_out, OutY y, hipStream_t stream) {
   int w = decode_waves(N / 16, 1);
-  while (w < 8 && M * K > 2048 * w) w += 2;
+  while (w < 8 && M * K > 2048 * w * decode_k_split(1, w, false, 32, 32)) w += 2;
   const uint4* pk = reinterpret_cast<const uint4*>(packed);
   if (w == 2)
     launch_linear_fused_w<IT, ST, 2>(x, ldx, pk, iscale, inv_alpha, M, N, K, q_out, s_out, y, stream);
