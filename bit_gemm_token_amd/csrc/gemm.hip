@@ -893,6 +893,13 @@ __global__ __launch_bounds__(NW * 64) void k_w8a8_zp(
 // unless the rows are quantized in the kernel and written to LDS directly)
 // or 8 (more), so a chunk is at most 64 KiB, that is a multiple of the weight
 // ring depth D; NW = the workgroup's waves
+// the largest divisor of n up to d (groups in flight of a wave's n groups)
+constexpr int ring_depth(int n, int d) {
+  int r = d < n ? d : n;
+  while (n % r != 0) --r;
+  return r;
+}
+
 constexpr int decode_chunk_groups(int G, int MR, int D, int NW, bool FQ) {
   int c = MR == 1 ? (NW >= 4 || FQ ? 32 : 16) : 8;
   while (c > D && (G % c != 0 || c % D != 0)) --c;
@@ -900,7 +907,7 @@ constexpr int decode_chunk_groups(int G, int MR, int D, int NW, bool FQ) {
 }
 
 template <bool FS, int W, int D, int G, int MR, typename ST, bool FQ, int IT, bool GR = false,
-          int GQ = G, int RS = 1, int KS = 1>
+          int GQ = G, int RS = 1, int KS = 1, bool CX = false>
 __global__ __launch_bounds__(W * RS * KS * 64) void k_w4a8_decode(
     const int8_t* __restrict__ qx, const float* __restrict__ sx,
     const uint4* __restrict__ packed, const ST* __restrict__ iscale,
@@ -921,21 +928,26 @@ __global__ __launch_bounds__(W * RS * KS * 64) void k_w4a8_decode(
   constexpr int SCH = (SCT + NWV * 64 - 1) / (NWV * 64); // ... per thread
   static_assert(G % D == 0 && G % CG == 0, "shape of the pipeline");
   static_assert(SCW % SEL == 0, "scale staging");
-  static_assert(!FQ || (MR == 1 && NCH == 1 && !FS), "fused quantization: one row block, one chunk");
+  static_assert(!FQ || (MR == 1 && (NCH == 1 || CX) && !FS),
+                "fused quantization: one row block, one chunk (or compact rows)");
+  static_assert(!CX || FQ, "compact rows: quantized in the kernel");
   static_assert(!(GR && FQ), "grouped GEMM takes quantized activations");
   static_assert(RS >= 1 && MR % RS == 0 && (RS == 1 || (!FQ && !GR)), "row split: dense launches");
-  static_assert(KS == 1 || (RS == 1 && MR == 1 && NCH == 1 && !FS && !GR && G % KS == 0),
-                "K split: one row block and one X chunk, integer scale");
+  static_assert(KS == 1 || (RS == 1 && MR == 1 && (NCH == 1 || CX) && !FS && !GR && G % KS == 0),
+                "K split: one row block and one X chunk (or compact rows), integer scale");
   constexpr int GK = G / KS;                         // groups per wave
-  constexpr int DK = D < GK ? D : GK;                // ... of them in flight
+  constexpr int DK = ring_depth(GK, D);              // ... of them in flight
   constexpr int NBUF = NCH > 1 ? 2 : 1;
-  __shared__ __align__(16) int8_t sA[NBUF * CFR * 1024];
+  // X in LDS: MFMA fragment order, one or two chunks; compact rows (CX): the
+  // (at most four) quantized rows, row r at byte r*K, fragments gathered at
+  // read time (rows past M read row M-1; their outputs are not stored)
+  __shared__ __align__(16) int8_t sA[CX ? 4 * GQ * kGroup : NBUF * CFR * 1024];
   __shared__ __align__(16) SL sS[G * SCW];           // [group][column of the workgroup]
   __shared__ float sX[16 * MR];                      // token scales
   // G groups in the pipeline; the last G - GQ are padding (K = 128 GQ): their
   // loads repeat group GQ-1 and their staged scales are zero, so they add
   // exactly nothing (0 * p in the integer epilogue, fma(p, +0, acc) = acc)
-  static_assert(GQ <= G && (GQ == G || (!FQ && !GR)), "padded groups: dense launches only");
+  static_assert(GQ <= G && (GQ == G || CX || (!FQ && !GR)), "padded groups: dense launches only");
   constexpr int K = GQ * kGroup;
   auto gq = [](int g) { return GQ == G || g < GQ ? g : GQ - 1; };
   const int T = N / 16;
@@ -1061,7 +1073,7 @@ __global__ __launch_bounds__(W * RS * KS * 64) void k_w4a8_decode(
     // rows M..15 of the fragment block are zero codes
 #pragma unroll
     for (int i = 0; i < FPW; ++i)
-      if (c >= M && (CFR % NWV == 0 || wave + NWV * i < CFR))
+      if (!CX && c >= M && (CFR % NWV == 0 || wave + NWV * i < CFR))
         *reinterpret_cast<v4i*>(sA + (wave + NWV * i) * 1024 + lane * 16) = v4i{0, 0, 0, 0};
     wait_lds0();
     lds_barrier();
@@ -1112,7 +1124,10 @@ __global__ __launch_bounds__(W * RS * KS * 64) void k_w4a8_decode(
           const int k = 4 * (threadIdx.x + NWV * 64 * v);
           // fragment (group g, half h) lane 16*(k%64/16) + row, byte k%16
           const int g = k / 128, h = (k % 128) / 64, sq = (k % 64) / 16;
-          *reinterpret_cast<uint32_t*>(sA + (g * 2 + h) * 1024 + (16 * sq + i) * 16 + k % 16) = word[v];
+          if (CX)
+            *reinterpret_cast<uint32_t*>(sA + i * K + k) = word[v];
+          else
+            *reinterpret_cast<uint32_t*>(sA + (g * 2 + h) * 1024 + (16 * sq + i) * 16 + k % 16) = word[v];
           if (blockIdx.x == 0) *reinterpret_cast<uint32_t*>(q_out + (int64_t)i * K + k) = word[v];
         }
       }
@@ -1130,7 +1145,7 @@ __global__ __launch_bounds__(W * RS * KS * 64) void k_w4a8_decode(
     const int q = threadIdx.x + NWV * 64 * u;
     if (SCT % (NWV * 64) == 0 || q < SCT) *reinterpret_cast<v4i*>(sS + q * SEL) = sv[u];
   }
-  if (NCH > 1) load_chunk(1);
+  if constexpr (NCH > 1 && !FQ) load_chunk(1);
   wait_lds0();
   lds_barrier();
 
@@ -1144,8 +1159,9 @@ __global__ __launch_bounds__(W * RS * KS * 64) void k_w4a8_decode(
   auto group = [&](int g, const uint4& w) {
     int32_t sc = (int32_t)sS[g * SCW + tw * 16 + c];
     if (sizeof(SL) < 4) opaque_reg(sc);              // keep the 24-bit multiply-adds as written
-    const int8_t* base = sA + ((g / CG) % NBUF) * CFR * 1024 + (g % CG) * MR * 2048 + hr * MRW * 2048 +
-                         lane * 16;
+    const int8_t* base = CX ? sA + (c < M ? c : M - 1) * K + kGroup * gq(g) + 16 * s4
+                            : sA + ((g / CG) % NBUF) * CFR * 1024 + (g % CG) * MR * 2048 +
+                                  hr * MRW * 2048 + lane * 16;
     uint32_t x0, x1, x2, x3, x4, x5, x6, x7;
     unpack_x16(w.x, x0, x1);
     unpack_x16(w.y, x2, x3);
@@ -1155,8 +1171,8 @@ __global__ __launch_bounds__(W * RS * KS * 64) void k_w4a8_decode(
     const v4i b1 = {(int)x4, (int)x5, (int)x6, (int)x7};
 #pragma unroll
     for (int rb = 0; rb < MRW; ++rb) {
-      const v4i a0 = *reinterpret_cast<const v4i*>(base + rb * 2048);
-      const v4i a1 = *reinterpret_cast<const v4i*>(base + rb * 2048 + 1024);
+      const v4i a0 = *reinterpret_cast<const v4i*>(base + (CX ? 0 : rb * 2048));
+      const v4i a1 = *reinterpret_cast<const v4i*>(base + (CX ? 64 : rb * 2048 + 1024));
       v4i p = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, v4i{0, 0, 0, 0}, 0, 0, 0);
       p = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, p, 0, 0, 0);
 #pragma unroll
@@ -1187,22 +1203,28 @@ __global__ __launch_bounds__(W * RS * KS * 64) void k_w4a8_decode(
       lds_barrier();
     }
   };
-  if constexpr (KS > 1) {
+  if constexpr (KS > 1 || CX) {
+    // this wave's GK groups from g0w, DK at a time (ring slot j)
+#pragma unroll 1
+    for (int gb = 0; gb < GK; gb += DK) {
 #pragma unroll
-    for (int gl = 0; gl < GK; ++gl) {
-      const int g = g0w + gl;
-      group(g, wb[gl % DK]);
-      if (gl + DK < GK) wb[gl % DK] = load_u4_nt(wsrc + (int64_t)gq(g + DK) * 64);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int j = 0; j < DK; ++j) {
+        const int g = g0w + gb + j;
+        group(g, wb[j]);
+        if (GK > DK && gb + j + DK < GK) wb[j] = load_u4_nt(wsrc + (int64_t)gq(g + DK) * 64);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     // K split: the other waves' int32 sums of the tile meet wave ks = 0's
     // in LDS (wrapping adds, exact in any order), which converts
     __shared__ int32_t sRed[(KS > 1 ? KS - 1 : 1) * W * 4 * kWave];
-    if (ks > 0)
+    if (KS > 1 && ks > 0)
 #pragma unroll
       for (int r = 0; r < 4; ++r) sRed[(((ks - 1) * W + tw) * 4 + r) * kWave + lane] = acc[0][r];
-    wait_lds0();
-    lds_barrier();
+    if constexpr (KS > 1) {
+      wait_lds0();
+      lds_barrier();
+    }
     if (ks > 0) return;
 #pragma unroll
     for (int k = 1; k < KS; ++k)
@@ -1675,25 +1697,40 @@ hipError_t launch_w4a8(bool float_scale, const int8_t* qx, const float* sx, cons
 
 // Quantize + GEMM in one launch for M <= 4 on the decode path (the decode
 // kernel quantizes the fp32 rows itself); otherwise the quantizer and the GEMM.
-// Waves (tiles) per workgroup as for the unfused decode launch, but enough
-// that a thread's share of the rows (held until they are quantized) is at
-// most 8 groups of 4 elements, M*K/4 <= 8*64*W: the quantizing prologue's
-// critical path grows with that share (measured at M = 4: 8 waves 11.2 us
-// against 2 waves 11.4 us at N = 4096; at M = 1, 2 waves 6.6 against 8.4)
+// 16 or 32 groups: X staged in fragment order; waves per workgroup as for the
+// unfused decode launch (2-wave workgroups split K over four waves per tile),
+// raised until a thread's share of the rows (held until they are quantized)
+// is at most 8 groups of 4 elements, M*K/4 <= 8*64*waves: the quantizing
+// prologue's critical path grows with that share. 86 groups (run as 96) and
+// 112: the rows staged compactly, so any K fits LDS, on 2-wave workgroups
+// splitting K in four (N/16 <= 512 tiles) or on 8-wave ones.
+template <int IT, typename ST, int W, int GG, int GQQ>
+static void launch_linear_fused_g(const void* x, int ldx, const uint4* pk, const ST* iscale,
+                                  float inv_alpha, int M, int N, int8_t* q_out, float* s_out,
+                                  OutY y, hipStream_t stream) {
+  constexpr int KS = W == 2 ? 4 : 1;
+  constexpr bool CX = !(GG == 16 || GG == 32);
+  const dim3 grid((N / 16 + W - 1) / W), block(W * KS * kWave);
+  hipLaunchKernelGGL((k_w4a8_decode<false, W, decode_depth(1), GG, 1, ST, true, IT, false, GQQ, 1,
+                                    KS, CX>),
+                     grid, block, 0, stream, nullptr, nullptr, pk, iscale, nullptr, inv_alpha, M, N,
+                     y, nullptr, x, ldx, q_out, s_out, Route{});
+}
+
 template <int IT, typename ST, int W>
 static void launch_linear_fused_w(const void* x, int ldx, const uint4* pk, const ST* iscale,
                                   float inv_alpha, int M, int N, int K, int8_t* q_out,
                                   float* s_out, OutY y, hipStream_t stream) {
-  constexpr int KS = decode_k_split(1, W, false, 32, 32);
-  const dim3 grid((N / 16 + W - 1) / W), block(W * KS * kWave);
-  if (K / kGroup == 32)
-    hipLaunchKernelGGL((k_w4a8_decode<false, W, decode_depth(1), 32, 1, ST, true, IT, false, 32, 1, KS>),
-                       grid, block, 0, stream, nullptr, nullptr, pk, iscale, nullptr, inv_alpha, M,
-                       N, y, nullptr, x, ldx, q_out, s_out, Route{});
-  else
-    hipLaunchKernelGGL((k_w4a8_decode<false, W, decode_depth(1), 16, 1, ST, true, IT, false, 16, 1, KS>),
-                       grid, block, 0, stream, nullptr, nullptr, pk, iscale, nullptr, inv_alpha, M,
-                       N, y, nullptr, x, ldx, q_out, s_out, Route{});
+  if (K / kGroup == 32) {
+    launch_linear_fused_g<IT, ST, W, 32, 32>(x, ldx, pk, iscale, inv_alpha, M, N, q_out, s_out, y, stream);
+  } else if (K / kGroup == 16) {
+    launch_linear_fused_g<IT, ST, W, 16, 16>(x, ldx, pk, iscale, inv_alpha, M, N, q_out, s_out, y, stream);
+  } else if constexpr (W == 2 || W == 8) {           // compact rows (see launch_linear_fused)
+    if (K / kGroup == 86)
+      launch_linear_fused_g<IT, ST, W, 96, 86>(x, ldx, pk, iscale, inv_alpha, M, N, q_out, s_out, y, stream);
+    else
+      launch_linear_fused_g<IT, ST, W, 112, 112>(x, ldx, pk, iscale, inv_alpha, M, N, q_out, s_out, y, stream);
+  }
 }
 
 template <int IT, typename ST>
@@ -1701,7 +1738,9 @@ static void launch_linear_fused(const void* x, int ldx, const uint8_t* packed, c
                                 float inv_alpha, int M, int N, int K, int8_t* q_out,
                                 float* s_out, OutY y, hipStream_t stream) {
   int w = decode_waves(N / 16, 1);
-  while (w < 8 && M * K > 2048 * w * decode_k_split(1, w, false, 32, 32)) w += 2;
+  if (K / kGroup == 86 || K / kGroup == 112) w = w == 2 ? 2 : 8;   // 2 waves split K in 4, else 8
+  else
+    while (w < 8 && M * K > 2048 * w * decode_k_split(1, w, false, 32, 32)) w += 2;
   const uint4* pk = reinterpret_cast<const uint4*>(packed);
   if (w == 2)
     launch_linear_fused_w<IT, ST, 2>(x, ldx, pk, iscale, inv_alpha, M, N, K, q_out, s_out, y, stream);
@@ -1715,7 +1754,7 @@ static void launch_linear_fused(const void* x, int ldx, const uint8_t* packed, c
 
 bool w4a8_linear_fused(int64_t M, int64_t K, const void* x, int64_t ldx) {
   const int64_t G = K / kGroup;
-  return M <= 4 && (G == 16 || G == 32) && (reinterpret_cast<uintptr_t>(x) & 15u) == 0 &&
+  return M <= 4 && (G == 16 || G == 32 || G == 86 || G == 112) && (reinterpret_cast<uintptr_t>(x) & 15u) == 0 &&
          ldx % 4 == 0 && ldx <= (1ll << 28);
 }
 

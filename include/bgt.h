@@ -242,8 +242,8 @@ int bgt_w4a8_gemm_is_ex(const int8_t* qx, const float* sx, const uint8_t* packed
  * bgt_w4a8_linear_is -- the whole decode-time linear layer from fp32
  * activations: per-token quantization of x exactly as bgt_quantize_act SYM
  * computes it (codes into qx, scales into sx), then bgt_w4a8_gemm_is_narrow
- * on those codes. For M <= 4 with K/128 = 16 or 32, x 16-byte aligned and
- * ldx % 4 == 0 this is one launch: every workgroup of the decode kernel
+ * on those codes. For M <= 4 with K/128 = 16, 32, 86 or 112, x 16-byte aligned
+ * and ldx % 4 == 0 this is one launch: every workgroup of the decode kernel
  * quantizes the rows itself while its weight stream is in flight, so the
  * separate quantizer launch disappears (the fusion of the quantization into
  * the GEMM that [QB] §2.4.1 dynamic quantization invites); otherwise it is the

@@ -80,7 +80,12 @@ def _check(bgt, orc, dev, x, ow, N, width=4, ldx_pad=0, expect_fused=None):
                                    # 1536); on 6 waves each thread's last group of four row
                                    # elements is partial (K/4 not a multiple of 384)
                                    (2, 4096, 11008), (4, 2048, 8208), (3, 2048, 20480),
-                                   (1, 4096, 28672)])
+                                   (1, 4096, 28672),
+                                   # 86 groups (run as 96, the last ten masked) and 112: rows
+                                   # staged compactly, 2-wave workgroups splitting K in four
+                                   # (N/16 <= 512 tiles) or 8-wave workgroups
+                                   (1, 11008, 4096), (4, 11008, 4096), (2, 14336, 4096),
+                                   (3, 14336, 528), (1, 11008, 8208), (4, 14336, 16384)])
 def test_linear_fused(bgt, orc, dev, M, K, N):
     say(f"w4a8_linear_is fused M={M} K={K} N={N}")
     x = synth.activations(40 + M, M, K)
