@@ -73,7 +73,7 @@ void launch_w4a8_wide_grouped(const int8_t* qx, const float* sx, const uint8_t* 
 // per-token quantization of x (M x K of element type x_type, leading dimension
 // ldx) into q_out /
 // s_out, then the integer-scale GEMM into y; one launch when
-// w4a8_linear_fused() holds (M <= 4, K/128 in {16, 32}, x 16-byte aligned,
+// w4a8_linear_fused() holds (M <= 4, K/128 in {16, 32, 86, 112}, x 16-byte aligned,
 // ldx % 4 == 0), else the quantizer and the GEMM.
 bool w4a8_linear_fused(int64_t M, int64_t K, const void* x, int64_t ldx);
 hipError_t launch_w4a8_linear(const void* x, int x_type, int64_t ldx, const uint8_t* packed,
