@@ -1814,15 +1814,20 @@ static int moe_row_blocks(int64_t R, int64_t E, int64_t K) {
 // pass, the tiled kernel once per 256-row tile but with its MFMA tiles mostly
 // empty at a few hundred slots per expert: the decode kernel serves every
 // T <= 64 and, up to T = 1024, routings whose mean expert needs at most four
-// passes (measured crossover at the Mixtral shapes), while its worst-case grid
-// (every expert with T slots; passes without slots exit at once) stays small.
+// passes of 32 rows (112 groups) or fewer than four of 64 rows (16, 32
+// groups), while its worst-case grid (every expert with T slots; passes
+// without slots exit at once) stays small. Crossovers measured at the Mixtral
+// shapes: w1 (32 groups) decode 309 us against tiled 332 us at a mean of 224
+// slots (T = 896), 352 against 320 us at 256 (T = 1024); w2 (112 groups)
+// decode 198 against tiled 250 us at a mean of 128 (T = 512).
 static bool moe_decode_path(int64_t T, int64_t R, int64_t E, int64_t K) {
   const int64_t G = K / kGroup;
   if (!(G == 16 || G == 32 || G == 112)) return false;
   if (T <= 64) return true;
   const int64_t rows = 16 * moe_row_blocks(R, E, K);
   const int64_t mean = (R + E - 1) / E;
-  return T <= 1024 && (mean + rows - 1) / rows <= 4 && E * ((T + rows - 1) / rows) <= 2048;
+  const bool fits = G == 112 ? (mean + rows - 1) / rows <= 4 : mean < 4 * rows;
+  return T <= 1024 && fits && E * ((T + rows - 1) / rows) <= 2048;
 }
 
 // Past the decode range the experts' row tiles take the 256 x 128 tile kernel.

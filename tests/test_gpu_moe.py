@@ -105,6 +105,7 @@ WIDE = "k_w4a8_wide<IS,grouped>"
                                      (1, 8, 14336, 48), (12, 8, 14336, 80), (32, 5, 14336, 32),
                                      (64, 8, 14336, 48), (50, 2, 2048, 32),
                                      # more tokens, up to four row passes per mean expert
+                                     # (fewer than four of 64 rows at 16 or 32 groups)
                                      (128, 8, 4096, 64), (300, 8, 2048, 48), (520, 8, 4096, 32),
                                      (1000, 8, 4096, 16), (200, 8, 14336, 32), (300, 6, 14336, 16)])
 def test_moe_decode_path(bgt, orc, dev, T, E, K, N):
@@ -119,8 +120,10 @@ def test_moe_decode_path(bgt, orc, dev, T, E, K, N):
 @pytest.mark.parametrize("T,E,K,N", [(65, 8, 512, 144), (300, 8, 256, 48), (20, 8, 1152, 64),
                                      (130, 4, 640, 400), (257, 8, 128, 16),
                                      # past the decode kernel's range: T > 1024, or more than
-                                     # four row passes for the mean expert
+                                     # four row passes for the mean expert (four full ones of
+                                     # 64 rows at 32 groups)
                                      (1100, 8, 4096, 16), (600, 8, 14336, 16), (700, 2, 2048, 32),
+                                     (1024, 8, 4096, 32),
                                      (1100, 16, 512, 48)])
 def test_moe_tiled_path(bgt, orc, dev, T, E, K, N):
     name = bgt.w4a8_moe_kernel_name(T, E, T * min(2, E), K)
