@@ -205,21 +205,78 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // suffices, with no fence that would also drain the loads still in flight.
 __device__ __forceinline__ void lds_barrier() { __builtin_amdgcn_s_barrier(); }
 
+// Grouped tile order of the tiled GEMMs: tiles go in groups of 4 row tiles per
+// column tile, so the tiles resident on one XCD share activation rows and
+// weight columns in its L2.
+__device__ __forceinline__ void tile_grouped(int t, int ntm, int ntn, int& tm, int& tn) {
+  constexpr int GM = 4;
+  const int group = t / (GM * ntn);
+  const int first = group * GM;
+  const int gsz = ntm - first < GM ? ntm - first : GM;
+  const int in = t - group * GM * ntn;
+  tm = first + in % gsz;
+  tn = in / gsz;
+}
+
 // Tile order of the tiled GEMMs: workgroup ids are dealt round-robin to the 8
 // XCDs, so consecutive ids of one XCD are remapped to consecutive tiles (when
-// the tile count is a multiple of 8), and tiles go in groups of 4 row tiles
-// per column tile, so the tiles resident on one XCD share activation rows and
-// weight columns in its L2.
+// the tile count is a multiple of 8), then taken in grouped order.
 __device__ __forceinline__ void tile_of(int pid, int ntm, int ntn, int& tm, int& tn) {
   const int total = ntm * ntn;
   if ((total & 7) == 0) pid = (pid & 7) * (total >> 3) + (pid >> 3);   // XCD-contiguous
-  constexpr int GM = 4;                                               // grouped order
-  const int group = pid / (GM * ntn);
-  const int first = group * GM;
-  const int gsz = ntm - first < GM ? ntm - first : GM;
-  const int in = pid - group * GM * ntn;
-  tm = first + in % gsz;
-  tn = in / gsz;
+  tile_grouped(pid, ntm, ntn, tm, tn);
+}
+
+// Row tiles of bm slots of expert i of a grouped GEMM (0 past the last expert).
+__device__ __forceinline__ int expert_row_tiles(const Route& rt, int i, int bm) {
+  if (i >= rt.E) return 0;
+  const int lo = clamp_route(rt.offs[i], 0, rt.R);
+  const int hi = clamp_route(rt.offs[i + 1], lo, rt.R);
+  return (hi - lo + bm - 1) / bm;
+}
+
+// Tile of workgroup pid in a grouped (mixture-of-experts) tiled GEMM. The
+// routing's row tiles (expert i has ceil(rows_i / bm), experts in order) times
+// ntn column tiles are dealt so that each XCD (pid % 8) takes an equal
+// contiguous run of them in grouped order; the launch's grid is only an upper
+// bound on that count (the host does not read the routing), and its spare
+// workgroups, which return false here, are spread over the XCDs instead of
+// filling the last ones. The wave reads the offsets 64 experts per load and
+// sums and scans them with lane shuffles. On true: the tile's expert e, its
+// first slot a and slot count rows, its row tile tm within the expert and
+// column tile tn (all wave-uniform).
+__device__ __forceinline__ bool grouped_tile(int pid, int bm, int ntn, const Route& rt, int& e,
+                                             int& a, int& rows, int& tm, int& tn) {
+  const int lane = threadIdx.x % kWave;
+  int rtiles = 0;
+  for (int base = 0; base < rt.E; base += kWave) rtiles += wave_sum(expert_row_tiles(rt, base + lane, bm));
+  rtiles = __builtin_amdgcn_readfirstlane(rtiles);
+  const int real = rtiles * ntn;
+  const int x = pid & 7, j = pid >> 3, q = real >> 3, rem = real & 7;
+  if (j >= q + (x < rem ? 1 : 0)) return false;
+  int gtm;
+  tile_grouped(x * q + (x < rem ? x : rem) + j, rtiles, ntn, gtm, tn);
+  for (int base = 0; base < rt.E; base += kWave) {
+    const int nt = expert_row_tiles(rt, base + lane, bm);
+    int incl = nt;                                   // inclusive prefix over the lanes
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int v = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += v;
+    }
+    const int excl = incl - nt;
+    const unsigned long long hit = __ballot(gtm >= excl && gtm < incl);
+    if (hit != 0ull) {
+      const int l = (int)__builtin_ctzll(hit);
+      e = __builtin_amdgcn_readfirstlane(base + l);
+      tm = __builtin_amdgcn_readfirstlane(gtm - __shfl(excl, l, kWave));
+      a = clamp_route(rt.offs[e], 0, rt.R);
+      rows = clamp_route(rt.offs[e + 1], a, rt.R) - a;
+      return true;
+    }
+    gtm -= __builtin_amdgcn_readfirstlane(__shfl(incl, kWave - 1, kWave));
+  }
+  return false;
 }
 
 }  // namespace bgt

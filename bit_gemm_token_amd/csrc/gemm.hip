@@ -396,24 +396,19 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
   const int lr = lane % 32, hf = lane / 32;
   int tm, tn;
   // grouped GEMM: the grid covers ceil(R/BM) + E row tiles, an upper bound on
-  // the sum over experts of ceil(rows/BM); row tile tm is found in the list of
-  // the experts' tiles (experts in order), and tiles past its end exit
-  tile_of(tb, GR ? (rt.R + BM - 1) / BM + rt.E : (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
+  // the sum over experts of ceil(rows/BM); the experts' row tiles (experts in
+  // order) are dealt evenly over the XCDs and the spare workgroups exit
   int r0 = 0;
   if constexpr (GR) {
-    int e = 0, a = 0;
-    for (; e < rt.E; ++e) {
-      a = clamp_route(rt.offs[e], 0, rt.R);
-      const int b = clamp_route(rt.offs[e + 1], a, rt.R);
-      const int nt = (b - a + BM - 1) / BM;
-      if (tm < nt) { M = b - a; break; }
-      tm -= nt;
-    }
-    if (e == rt.E) return;
+    int e, a, rows;
+    if (!grouped_tile(tb, BM, (N + BN - 1) / BN, rt, e, a, rows, tm, tn)) return;
+    M = rows;
     r0 = a;
     packed += e * rt.wstride / 16;
     if (FS) fscale += e * rt.sstride;
     else iscale += e * rt.sstride;
+  } else {
+    tile_of(tb, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
   }
   const int m0 = tm * BM, n0 = tn * BN;
 
@@ -1813,21 +1808,21 @@ static int moe_row_blocks(int64_t R, int64_t E, int64_t K) {
 // The grouped decode kernel streams each busy expert's weights once per row
 // pass, the tiled kernel once per 256-row tile but with its MFMA tiles mostly
 // empty at a few hundred slots per expert: the decode kernel serves every
-// T <= 64 and, up to T = 1024, routings whose mean expert needs at most four
-// passes of 32 rows (112 groups) or fewer than four of 64 rows (16, 32
-// groups), while its worst-case grid (every expert with T slots; passes
-// without slots exit at once) stays small. Crossovers measured at the Mixtral
-// shapes: w1 (32 groups) decode 309 us against tiled 332 us at a mean of 224
-// slots (T = 896), 352 against 320 us at 256 (T = 1024); w2 (112 groups)
-// decode 198 against tiled 250 us at a mean of 128 (T = 512).
+// T <= 64 and, up to T = 1024, routings whose mean expert needs at most two
+// row passes of 64 slots (16, 32 groups) or three of 32 slots (112 groups),
+// while its worst-case grid (every expert with T slots; passes without slots
+// exit at once) stays small. Crossovers measured at the Mixtral shapes (same
+// call, decode / tiled us): w1 (32 groups) 196 / 204 at a mean of 128 slots
+// (T = 512), 256 / 233 at 160 (T = 640); w2 (112 groups) 171 / 268 at 96
+// (T = 384), 178 / 152 at 112 (T = 448).
 static bool moe_decode_path(int64_t T, int64_t R, int64_t E, int64_t K) {
   const int64_t G = K / kGroup;
   if (!(G == 16 || G == 32 || G == 112)) return false;
   if (T <= 64) return true;
   const int64_t rows = 16 * moe_row_blocks(R, E, K);
   const int64_t mean = (R + E - 1) / E;
-  const bool fits = G == 112 ? (mean + rows - 1) / rows <= 4 : mean < 4 * rows;
-  return T <= 1024 && fits && E * ((T + rows - 1) / rows) <= 2048;
+  return T <= 1024 && (mean + rows - 1) / rows <= (G == 112 ? 3 : 2) &&
+         E * ((T + rows - 1) / rows) <= 2048;
 }
 
 // Past the decode range the experts' row tiles take the 256 x 128 tile kernel.

@@ -78,27 +78,21 @@ __global__ __launch_bounds__(kWNW * 64) __attribute__((amdgpu_waves_per_eu(2))) 
   const int lr = lane % 32, hf = lane / 32;
   int tm, tn;
   // grouped GEMM: the grid covers ceil(R/256) + E row tiles, an upper bound on
-  // the sum over experts of ceil(rows/256); row tile tm is found in the list
-  // of the experts' tiles (experts in order), and tiles past its end exit.
+  // the sum over experts of ceil(rows/256); the experts' row tiles (experts in
+  // order) are dealt evenly over the XCDs and the spare workgroups exit.
   // The expert's slots r0 .. r0+M-1 are its rows; slot r reads activation row
   // tok[r] (row offsets fit 32 bits: T*K < 2^31, checked by the launcher)
-  tile_of(blockIdx.x, GR ? (rt.R + kWBM - 1) / kWBM + rt.E : (M + kWBM - 1) / kWBM,
-          (N + kWBN - 1) / kWBN, tm, tn);
   int r0 = 0;
   if constexpr (GR) {
-    int e = 0, a = 0;
-    for (; e < rt.E; ++e) {
-      a = clamp_route(rt.offs[e], 0, rt.R);
-      const int b = clamp_route(rt.offs[e + 1], a, rt.R);
-      const int nt = (b - a + kWBM - 1) / kWBM;
-      if (tm < nt) { M = b - a; break; }
-      tm -= nt;
-    }
-    if (e == rt.E) return;
+    int e, a, rows;
+    if (!grouped_tile(blockIdx.x, kWBM, (N + kWBN - 1) / kWBN, rt, e, a, rows, tm, tn)) return;
+    M = rows;
     r0 = a;
     packed += e * rt.wstride;
     if (FS) fscale += e * rt.sstride;
     else iscale += e * rt.sstride;
+  } else {
+    tile_of(blockIdx.x, (M + kWBM - 1) / kWBM, (N + kWBN - 1) / kWBN, tm, tn);
   }
   const int m0 = tm * kWBM, n0 = tn * kWBN;
 

@@ -332,7 +332,7 @@ int bgt_w8a8_gemm_zp(const uint8_t* qx, const float* sx, const int32_t* zx,
  * 1 <= R <= min(T*E, 2^24); qx, packed, iscale, y, acc_out 16-byte aligned.
  * Kernels: with K/128 in {16, 32, 112}, a weight-streaming grouped decode
  * kernel for T <= 64 and, up to T = 1024, whenever the mean expert (R/E
- * slots) needs fewer than four row passes of 64 slots (at most four of 32 at
+ * slots) needs at most two row passes of 64 slots (three of 32 at
  * K/128 = 112); experts
  * without slots read no weights there. Otherwise one tiled launch over the
  * experts' 256-row tiles.

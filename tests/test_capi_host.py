@@ -354,11 +354,11 @@ def test_moe_validation(L):
     assert name(16, 8, 32, 4096) == dec
     assert name(64, 8, 128, 14336) == dec
     assert name(16, 8, 32, 1152) == til                 # 9 groups: no decode kernel
-    # Mixtral-8x7B top-2: fewer than four row passes of 64 slots (w1, 32 groups)
-    # or at most four of 32 (w2, 112 groups) for the mean expert, T <= 1024
-    assert name(512, 8, 1024, 4096) == dec and name(1000, 8, 2000, 4096) == dec
-    assert name(1024, 8, 2048, 4096) == til            # mean 256: four full passes
-    assert name(512, 8, 1024, 14336) == dec and name(1024, 8, 2048, 14336) == til
+    # Mixtral-8x7B top-2: at most two row passes of 64 slots (w1, 32 groups) or
+    # three of 32 (w2, 112 groups) for the mean expert, T <= 1024
+    assert name(512, 8, 1024, 4096) == dec and name(520, 8, 1040, 4096) == til
+    assert name(384, 8, 768, 14336) == dec and name(448, 8, 896, 14336) == til
+    assert name(1024, 8, 2048, 4096) == til and name(1024, 8, 2048, 14336) == til
     assert name(1025, 8, 2050, 4096) == til and name(2048, 8, 4096, 4096) == til
     assert name(1024, 256, 2048, 4096) == til           # worst-case grid too large
     assert name(0, 8, 1, 4096) == "invalid shape" and name(4, 8, 33, 4096) == "invalid shape"

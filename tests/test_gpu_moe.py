@@ -104,10 +104,10 @@ WIDE = "k_w4a8_wide<IS,grouped>"
                                      (33, 8, 4096, 48), (64, 8, 2048, 16), (20, 3, 4096, 80),
                                      (1, 8, 14336, 48), (12, 8, 14336, 80), (32, 5, 14336, 32),
                                      (64, 8, 14336, 48), (50, 2, 2048, 32),
-                                     # more tokens, up to four row passes per mean expert
-                                     # (fewer than four of 64 rows at 16 or 32 groups)
-                                     (128, 8, 4096, 64), (300, 8, 2048, 48), (520, 8, 4096, 32),
-                                     (1000, 8, 4096, 16), (200, 8, 14336, 32), (300, 6, 14336, 16)])
+                                     # more tokens, up to two row passes of 64 slots (16, 32
+                                     # groups) or three of 32 (112 groups) per mean expert
+                                     (128, 8, 4096, 64), (300, 8, 2048, 48), (512, 8, 4096, 32),
+                                     (200, 8, 14336, 32), (384, 8, 14336, 16), (250, 6, 14336, 16)])
 def test_moe_decode_path(bgt, orc, dev, T, E, K, N):
     name = bgt.w4a8_moe_kernel_name(T, E, T * min(2, E), K)
     say(f"moe {name} T={T} E={E} K={K} N={N}")
@@ -119,11 +119,11 @@ def test_moe_decode_path(bgt, orc, dev, T, E, K, N):
 
 @pytest.mark.parametrize("T,E,K,N", [(65, 8, 512, 144), (300, 8, 256, 48), (20, 8, 1152, 64),
                                      (130, 4, 640, 400), (257, 8, 128, 16),
-                                     # past the decode kernel's range: T > 1024, or more than
-                                     # four row passes for the mean expert (four full ones of
-                                     # 64 rows at 32 groups)
+                                     # past the decode kernel's range: T > 1024, or more row
+                                     # passes for the mean expert
                                      (1100, 8, 4096, 16), (600, 8, 14336, 16), (700, 2, 2048, 32),
-                                     (1024, 8, 4096, 32),
+                                     (1024, 8, 4096, 32), (520, 8, 4096, 32), (1000, 8, 4096, 16),
+                                     (300, 6, 14336, 16),
                                      (1100, 16, 512, 48)])
 def test_moe_tiled_path(bgt, orc, dev, T, E, K, N):
     name = bgt.w4a8_moe_kernel_name(T, E, T * min(2, E), K)
@@ -182,6 +182,36 @@ def test_moe_all_tokens_one_expert(bgt, orc, dev, T, K):
     routing = np.full((T, 1), 5, np.int32)
     routing[0, 0] = 2
     _run(bgt, orc, dev, T, 8, K, 64, seed=T + 3, routing=routing)
+
+
+# The grouped tile kernels deal the routing's row tiles evenly over the XCDs
+# (workgroup id % 8) and let the rest of the grid, an upper bound computed
+# without the routing, exit: grids that are not a multiple of 8, experts
+# without slots between busy ones, one busy expert, row tiles of several
+# experts in one column run; every output compared.
+SPREAD = [
+    (300, 11, 512, 272, None),        # grid (3 + 11) x 3 = 42 workgroups
+    (400, 8, 1024, 144, (2, 5)),      # two busy experts, six idle
+    (700, 16, 256, 48, (9,)),         # one busy expert with 700 slots (three row tiles)
+    (1100, 5, 384, 400, None),        # 5 experts, 4 column tiles of 128 (one ragged)
+    (200, 130, 256, 48, None),        # 130 experts: the offsets are read 64 experts at a time
+]
+
+
+@pytest.mark.parametrize("T,E,K,N,busy", SPREAD)
+@pytest.mark.parametrize("kernel", ["tiled", "wide"])
+def test_moe_tile_spread(bgt, orc, dev, forced, T, E, K, N, busy, kernel):
+    if kernel == "wide":
+        forced("wide")
+    routing = None
+    if busy is not None:
+        routing = np.asarray([[busy[(t + i) % len(busy)] for i in range(len(busy))]
+                              for t in range(T)], np.int32)
+    R = T * (len(busy) if busy is not None else min(2, E))
+    name = bgt.w4a8_moe_kernel_name(T, E, R, K)
+    say(f"moe spread {name} T={T} E={E} K={K} N={N} busy={busy}")
+    assert name == (WIDE if kernel == "wide" else TILED)
+    _run(bgt, orc, dev, T, E, K, N, seed=T * 41 + E + K + N, routing=routing)
 
 
 @pytest.mark.parametrize("T,K", [(12, 4096), (150, 384), (9, 14336), (200, 4096), (200, 14336)])
