@@ -7,8 +7,9 @@
 // Quantization with q in [0, 255] and also produces the row sum of the codes,
 // the activation-side term of its zero-point expansion.
 //
-// One 256-thread workgroup per row. The row is read once with 16-byte loads
-// and kept in registers (up to kVecPerThread float4 per thread); the row
+// One 256-thread workgroup per row. The row is read once with 16-byte loads,
+// all of a thread's loads issued before the first is used (one round trip to
+// memory), and kept in registers (up to kVecPerThread float4 per thread); the row
 // statistic is a wave64 shuffle reduction followed by a 4-wave LDS step; the
 // codes are written as packed 4-byte words (one word per float4), so both
 // the read and the write of a row are fully coalesced.
@@ -19,7 +20,9 @@ namespace bgt {
 
 constexpr int kQThreads = 256;
 constexpr int kQWaves = kQThreads / kWave;
-constexpr int kVecPerThread = 12;   // rows up to 256*4*12 = 12288 floats stay in registers
+// float4 slots per thread held in registers: 4 for rows up to 4096 elements, 16
+// (rows up to 16384) beyond; longer rows stream their rest a second time
+constexpr int kVecShort = 4, kVecLong = 16;
 
 template <bool ASYM>
 struct RowStat {
@@ -82,7 +85,7 @@ __device__ __forceinline__ int quant_code_rcp(float x, float s, float r, int z) 
 }
 
 // Vector path: cols % 16 == 0, ld % 4 == 0, x and q 16-byte aligned.
-template <bool ASYM, int IT>
+template <bool ASYM, int IT, int kVecPerThread>
 __global__ __launch_bounds__(kQThreads) void k_quant_rows_vec(
     const void* __restrict__ x, int64_t cols, int64_t ld, uint8_t* __restrict__ q,
     float* __restrict__ scale, int32_t* __restrict__ zero, int32_t* __restrict__ rowsum) {
@@ -93,14 +96,24 @@ __global__ __launch_bounds__(kQThreads) void k_quant_rows_vec(
   const int64_t nvec = cols / 4;
   const int t = threadIdx.x;
 
+  // every slot of the row is requested before any is used (one round trip to
+  // memory, not one per slot): slot u exists for the whole workgroup when
+  // u*256 < nvec (a uniform branch); a thread past the row's end in its last
+  // slot loads the row's last vector (in bounds) and leaves it out below
   float4 cache[kVecPerThread];
+#pragma unroll
+  for (int u = 0; u < kVecPerThread; ++u) {
+    if ((int64_t)u * kQThreads < nvec) {
+      const int64_t v = t + (int64_t)u * kQThreads;
+      cache[u] = load_x4<IT>(x, xr + (v < nvec ? v : nvec - 1));
+    }
+  }
   RowStat<ASYM> st{ASYM ? -INFINITY : 0.0f, ASYM ? INFINITY : 0.0f};
 #pragma unroll
   for (int u = 0; u < kVecPerThread; ++u) {
     const int64_t v = t + (int64_t)u * kQThreads;
     if (v < nvec) {
-      float4 f = load_x4<IT>(x, xr + v);
-      cache[u] = f;
+      const float4 f = cache[u];
       if (ASYM) {
         st.a = fmaxf(st.a, fmaxf(fmaxf(f.x, f.y), fmaxf(f.z, f.w)));
         st.b = fminf(st.b, fminf(fminf(f.x, f.y), fminf(f.z, f.w)));
@@ -215,8 +228,11 @@ static void launch_quant_rows_t(bool vec, bool asym, dim3 grid, dim3 block, hipS
                                 const void* x, int64_t cols, int64_t ld, uint8_t* qb, float* scale,
                                 int32_t* zero, int32_t* rowsum) {
   if (vec) {
-    if (asym) hipLaunchKernelGGL((k_quant_rows_vec<true, IT>), grid, block, 0, stream, x, cols, ld, qb, scale, zero, rowsum);
-    else hipLaunchKernelGGL((k_quant_rows_vec<false, IT>), grid, block, 0, stream, x, cols, ld, qb, scale, zero, rowsum);
+    const bool shortrow = cols <= 4 * kQThreads * kVecShort;
+    if (asym && shortrow) hipLaunchKernelGGL((k_quant_rows_vec<true, IT, kVecShort>), grid, block, 0, stream, x, cols, ld, qb, scale, zero, rowsum);
+    else if (asym) hipLaunchKernelGGL((k_quant_rows_vec<true, IT, kVecLong>), grid, block, 0, stream, x, cols, ld, qb, scale, zero, rowsum);
+    else if (shortrow) hipLaunchKernelGGL((k_quant_rows_vec<false, IT, kVecShort>), grid, block, 0, stream, x, cols, ld, qb, scale, zero, rowsum);
+    else hipLaunchKernelGGL((k_quant_rows_vec<false, IT, kVecLong>), grid, block, 0, stream, x, cols, ld, qb, scale, zero, rowsum);
   } else {
     if (asym) hipLaunchKernelGGL((k_quant_rows_scalar<true, IT>), grid, block, 0, stream, x, cols, ld, qb, scale, zero, rowsum);
     else hipLaunchKernelGGL((k_quant_rows_scalar<false, IT>), grid, block, 0, stream, x, cols, ld, qb, scale, zero, rowsum);
