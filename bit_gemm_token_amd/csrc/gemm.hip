@@ -1020,6 +1020,14 @@ __global__ __launch_bounds__(W * RS * KS * 64) void k_w4a8_decode(
   } else {
     load_chunk(0);
   }
+  // token scales of the (at most 64) rows, read back from LDS at the end;
+  // requested before the weights so that storing them waits for no weight
+  float sxi = 0.0f;
+  if constexpr (!FQ) {
+    const int ti = threadIdx.x < M ? threadIdx.x : M - 1;
+    const int tr = GR ? clamp_route(rt.tok[r0 + ti], 0, rt.T - 1) : ti;
+    if (threadIdx.x < 16 * MR) sxi = sx[tr];
+  }
   // ---- the workgroup's scales for all groups, 16-byte chunks of SEL
   // elements (columns past N clamped; chunk q lands at byte 16q of sS)
   const SL* scl = FS ? reinterpret_cast<const SL*>(fscale) : reinterpret_cast<const SL*>(iscale);
@@ -1128,10 +1136,6 @@ __global__ __launch_bounds__(W * RS * KS * 64) void k_w4a8_decode(
       }
     if (threadIdx.x >= M && threadIdx.x < 16) sX[threadIdx.x] = 0.0f;
   } else {
-    // token scales of the (at most 64) rows, read back from LDS at the end
-    const int ti = threadIdx.x < M ? threadIdx.x : M - 1;
-    const int tr = GR ? clamp_route(rt.tok[r0 + ti], 0, rt.T - 1) : ti;
-    const float sxi = threadIdx.x < 16 * MR ? sx[tr] : 0.0f;
     store_chunk(0);
     if (threadIdx.x < 16 * MR) sX[threadIdx.x] = sxi;
   }
