@@ -15,24 +15,29 @@ namespace bgt {
 // codes of the C ABI).
 constexpr int kF32 = 0, kF16 = 1, kBF16 = 2;
 
-// Four consecutive activation elements x[4*i .. 4*i+3] of element type IT,
-// widened to fp32 (exact for fp16 and bf16); one 16-byte (fp32) or 8-byte
-// load. And one element.
+// Four consecutive activation elements of element type IT as stored (16 bytes
+// of fp32, 8 of fp16 / bf16), and widened to fp32 (exact for fp16 and bf16).
+template <int IT> struct XRaw { using T = uint2; };
+template <> struct XRaw<kF32> { using T = float4; };
+
+template <int IT>
+__device__ __forceinline__ float4 widen_x4(const typename XRaw<IT>::T& u) {
+  if constexpr (IT == kF32) {
+    return u;
+  } else if constexpr (IT == kF16) {
+    const __half2 a = *reinterpret_cast<const __half2*>(&u.x);
+    const __half2 b = *reinterpret_cast<const __half2*>(&u.y);
+    return make_float4(__low2float(a), __high2float(a), __low2float(b), __high2float(b));
+  } else {
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
+  }
+}
+
+// x[4*i .. 4*i+3] widened to fp32: one 16-byte (fp32) or 8-byte load.
 template <int IT>
 __device__ __forceinline__ float4 load_x4(const void* x, int64_t i) {
-  if constexpr (IT == kF32) {
-    return reinterpret_cast<const float4*>(x)[i];
-  } else {
-    const uint2 u = reinterpret_cast<const uint2*>(x)[i];
-    if constexpr (IT == kF16) {
-      const __half2 a = *reinterpret_cast<const __half2*>(&u.x);
-      const __half2 b = *reinterpret_cast<const __half2*>(&u.y);
-      return make_float4(__low2float(a), __high2float(a), __low2float(b), __high2float(b));
-    } else {
-      return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
-                         __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
-    }
-  }
+  return widen_x4<IT>(reinterpret_cast<const typename XRaw<IT>::T*>(x)[i]);
 }
 template <int IT>
 __device__ __forceinline__ float load_x1(const void* x, int64_t i) {

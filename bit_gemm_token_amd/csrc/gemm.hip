@@ -1003,20 +1003,24 @@ __global__ __launch_bounds__(W * RS * KS * 64) void k_w4a8_decode(
   };
   // fused quantization (FQ, M <= 4): the rows (element type IT, widened to
   // fp32), each thread XV groups of 4 of every row (the last one partial when
-  // K/4 is not a multiple of the workgroup's threads: zeros past the row),
-  // requested before the scales and the weights
+  // K/4 is not a multiple of the workgroup's threads: the groups past the
+  // row's end count for nothing), requested before the scales and the weights
   constexpr int XV = FQ ? (K / 4 + NWV * 64 - 1) / (NWV * 64) : 1;
   constexpr bool XR = FQ && XV * NWV * 64 * 4 != K;
   auto xin = [&](int v) { return !XR || v < XV - 1 || (int)threadIdx.x + NWV * 64 * v < K / 4; };
-  float4 xv[4][XV];
+  // (the rows are read as stored, every load unconditional, from the row
+  // start past the row's end, and widened only after the weights are
+  // requested: a load under a lane condition, or converted in its own block,
+  // makes the compiler wait for it before the next, one round trip each)
+  typename XRaw<IT>::T xr[4][XV];
   if constexpr (FQ) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int v = 0; v < XV; ++v)
         if (i < M)
-          xv[i][v] = xin(v) ? load_x4<IT>(xf, (int64_t)i * (ldx / 4) + threadIdx.x + NWV * 64 * v)
-                            : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+          xr[i][v] = reinterpret_cast<const typename XRaw<IT>::T*>(xf)[
+              (int64_t)i * (ldx / 4) + (xin(v) ? threadIdx.x + NWV * 64 * v : 0)];
   } else {
     load_chunk(0);
   }
@@ -1031,15 +1035,20 @@ __global__ __launch_bounds__(W * RS * KS * 64) void k_w4a8_decode(
   // ---- the workgroup's scales for all groups, 16-byte chunks of SEL
   // elements (columns past N clamped; chunk q lands at byte 16q of sS)
   const SL* scl = FS ? reinterpret_cast<const SL*>(fscale) : reinterpret_cast<const SL*>(iscale);
+  // (loads unconditional from an in-bounds group, the padding's zeros selected
+  // afterwards, as for the rows above; chunks past SCT are never stored)
   v4i sv[SCH];
 #pragma unroll
   for (int u = 0; u < SCH; ++u) {
     const int q = threadIdx.x + NWV * 64 * u, g = q / (SCW / SEL), c0 = (q % (SCW / SEL)) * SEL;
     const int col = blockIdx.x * SCW + c0 < N ? blockIdx.x * SCW + c0 : N - SEL;
-    if (GQ < G && g >= GQ)
-      sv[u] = v4i{0, 0, 0, 0};
-    else if (SCT % (NWV * 64) == 0 || q < SCT)
-      sv[u] = load_v4i(reinterpret_cast<const int8_t*>(scl + ((int64_t)g * N + col)));
+    const int gl = g < GQ ? g : GQ - 1;
+    sv[u] = load_v4i(reinterpret_cast<const int8_t*>(scl + ((int64_t)gl * N + col)));
+  }
+#pragma unroll
+  for (int u = 0; u < SCH; ++u) {
+    const int q = threadIdx.x + NWV * 64 * u, g = q / (SCW / SEL);
+    if (GQ < G && g >= GQ) sv[u] = v4i{0, 0, 0, 0};
   }
   // ---- first D groups of the tile in flight (K split: of this wave's GK
   // groups from g0w, DK in flight)
@@ -1056,15 +1065,19 @@ __global__ __launch_bounds__(W * RS * KS * 64) void k_w4a8_decode(
     // (exact), fma(e, r, q0) is x / s correctly rounded while s, r and the
     // residual stay normal; rows with an extreme scale take the division.
     __shared__ float sAm[4 * NWV];
+    float4 xv[4][XV];
     float am[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       am[i] = 0.0f;
       if (i < M)
 #pragma unroll
-        for (int v = 0; v < XV; ++v)
-          am[i] = fmaxf(am[i], fmaxf(fmaxf(fabsf(xv[i][v].x), fabsf(xv[i][v].y)),
-                                     fmaxf(fabsf(xv[i][v].z), fabsf(xv[i][v].w))));
+        for (int v = 0; v < XV; ++v) {
+          xv[i][v] = widen_x4<IT>(xr[i][v]);        // past the row's end: not counted, not stored
+          const float a = fmaxf(fmaxf(fabsf(xv[i][v].x), fabsf(xv[i][v].y)),
+                                fmaxf(fabsf(xv[i][v].z), fabsf(xv[i][v].w)));
+          am[i] = fmaxf(am[i], xin(v) ? a : 0.0f);
+        }
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1)                 // the four rows' butterflies side by side
