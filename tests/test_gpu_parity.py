@@ -58,8 +58,10 @@ def assert_f32_exact(got, ref, what):
 
 # ----------------------------------------------------------------- quantize_act
 
+# rows held in 4 register slots per thread (K <= 4096), in 16 (K <= 16384, the
+# last one partial at 4160 and 11008), and past 16384 (the rest streamed again)
 @pytest.mark.parametrize("M,K", [(1, 128), (3, 4096), (16, 4096), (33, 512), (5, 11008), (2, 16384),
-                                 (7, 100), (4, 4097)])
+                                 (7, 100), (4, 4097), (3, 4160), (2, 20480), (3, 32768)])
 def test_quantize_sym(bgt, orc, dev, M, K):
     say(f"quantize_act sym M={M} K={K}")
     x = synth.activations(M + K, M, K)
@@ -131,7 +133,7 @@ def test_quantize_scale_range(bgt, orc, dev, mode):
 
 
 @pytest.mark.parametrize("M,K,relu", [(256, 4096, False), (256, 4096, True), (9, 300, False),
-                                      (4096, 4096, False)])
+                                      (4096, 4096, False), (5, 14336, True), (3, 20480, False)])
 def test_quantize_asym(bgt, orc, dev, M, K, relu):
     say(f"quantize_act asym M={M} K={K} relu={relu}")
     x = synth.activations(M, M, K, outlier_frac=0.0, mean=0.5, relu=relu)
