@@ -1842,13 +1842,16 @@ static bool moe_decode_path(int64_t T, int64_t R, int64_t E, int64_t K) {
          E * ((T + rows - 1) / rows) <= 2048;
 }
 
-// Past the decode range the experts' row tiles take the 256 x 128 tile kernel.
-// The 256 x 256 one runs them only when set_prefill_kernel() forces it (and
-// the gathered row offsets fit 32 bits): at the Mixtral expert shapes it
-// measured no faster (w1, T = 2048 / 4096: 515 / 772 us against 525 / 771)
-// or slower (w2: 466 / 708 against 404 / 665).
+// Past the decode range the experts' row tiles take the 256 x 256 tile kernel
+// when K/128 <= 32 (and the gathered row offsets fit 32 bits), else the
+// 256 x 128 one; set_prefill_kernel() forces either. With the row tiles dealt
+// evenly over the XCDs, same call (us, 256 x 128 / 256 x 256): Mixtral w1
+// (32 groups) T = 1024 343 / 311, T = 2048 546 / 531, T = 4096 888 / 823;
+// w2 (112 groups) T = 1024 285 / 249, T = 2048 432 / 465, T = 4096 725 / 724.
 static bool moe_wide_path(int64_t T, int64_t K) {
-  return g_prefill_kernel.load() == kPrefillWide && T * K < ((int64_t)1 << 31);
+  const int f = g_prefill_kernel.load();
+  if (f == kPrefillTiled || T * K >= ((int64_t)1 << 31)) return false;
+  return f == kPrefillWide || K / kGroup <= 32;
 }
 
 template <typename ST>

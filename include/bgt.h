@@ -431,8 +431,9 @@ const char* bgt_w4a8_kernel_name(int64_t M, int64_t N, int64_t K, int float_scal
  *   BGT_PREFILL_WIDE  always the 256 x 256 tile kernel;
  *   BGT_PREFILL_TILED always the 256 x 128 tile kernel.
  * The grouped GEMM (bgt_w4a8_moe_gemm_is) past its decode range takes the
- * 256 x 128 kernel over the experts' row tiles, and the 256 x 256 one under
- * BGT_PREFILL_WIDE (when T*K < 2^31).
+ * 256 x 256 kernel over the experts' row tiles when K/128 <= 32 (AUTO) or
+ * under BGT_PREFILL_WIDE, in both cases only when T*K < 2^31; otherwise, and
+ * under BGT_PREFILL_TILED, the 256 x 128 kernel.
  * Process-wide; takes effect for GEMMs launched after the call (set it before
  * capturing a graph). Returns BGT_OK, or BGT_ERR_MODE for another value. */
 

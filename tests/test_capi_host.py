@@ -350,17 +350,26 @@ def test_moe_validation(L):
     assert call(y=MIS) == bgt.BGT_ERR_ALIGN
     assert call(acc=MIS) == bgt.BGT_ERR_ALIGN
     dec, til = "k_w4a8_decode<IS,grouped>", "k_w4a8_prefill<4,2,2,2,IS,grouped>"
+    wide = "k_w4a8_wide<IS,grouped>"
     name = bgt.w4a8_moe_kernel_name                 # (T, E, R, K)
     assert name(16, 8, 32, 4096) == dec
     assert name(64, 8, 128, 14336) == dec
-    assert name(16, 8, 32, 1152) == til                 # 9 groups: no decode kernel
+    assert name(16, 8, 32, 1152) == wide                # 9 groups: no decode kernel
     # Mixtral-8x7B top-2: at most two row passes of 64 slots (w1, 32 groups) or
-    # three of 32 (w2, 112 groups) for the mean expert, T <= 1024
-    assert name(512, 8, 1024, 4096) == dec and name(520, 8, 1040, 4096) == til
+    # three of 32 (w2, 112 groups) for the mean expert, T <= 1024; past that
+    # 256 x 256 tiles at 32 groups or fewer, 256 x 128 at 112
+    assert name(512, 8, 1024, 4096) == dec and name(520, 8, 1040, 4096) == wide
     assert name(384, 8, 768, 14336) == dec and name(448, 8, 896, 14336) == til
-    assert name(1024, 8, 2048, 4096) == til and name(1024, 8, 2048, 14336) == til
-    assert name(1025, 8, 2050, 4096) == til and name(2048, 8, 4096, 4096) == til
-    assert name(1024, 256, 2048, 4096) == til           # worst-case grid too large
+    assert name(1024, 8, 2048, 4096) == wide and name(1024, 8, 2048, 14336) == til
+    assert name(1025, 8, 2050, 4096) == wide and name(4096, 8, 8192, 14336) == til
+    assert name(1024, 256, 2048, 4096) == wide          # worst-case grid too large
+    try:
+        bgt.set_prefill_kernel("tiled")
+        assert name(1025, 8, 2050, 4096) == til and name(16, 8, 32, 1152) == til
+        bgt.set_prefill_kernel("wide")
+        assert name(4096, 8, 8192, 14336) == wide and name(16, 8, 32, 4096) == dec
+    finally:
+        bgt.set_prefill_kernel("auto")
     assert name(0, 8, 1, 4096) == "invalid shape" and name(4, 8, 33, 4096) == "invalid shape"
     assert name(4, 0, 1, 4096) == "invalid shape" and name(4, 8, 8, 4100) == "invalid shape"
 

@@ -117,6 +117,12 @@ def test_moe_decode_path(bgt, orc, dev, T, E, K, N):
         assert (np.diff(offs) > 0).sum() == 2             # six experts read nothing
 
 
+@pytest.fixture
+def forced(bgt):
+    yield bgt.set_prefill_kernel
+    bgt.set_prefill_kernel("auto")
+
+
 @pytest.mark.parametrize("T,E,K,N", [(65, 8, 512, 144), (300, 8, 256, 48), (20, 8, 1152, 64),
                                      (130, 4, 640, 400), (257, 8, 128, 16),
                                      # past the decode kernel's range: T > 1024, or more row
@@ -125,17 +131,25 @@ def test_moe_decode_path(bgt, orc, dev, T, E, K, N):
                                      (1024, 8, 4096, 32), (520, 8, 4096, 32), (1000, 8, 4096, 16),
                                      (300, 6, 14336, 16),
                                      (1100, 16, 512, 48)])
-def test_moe_tiled_path(bgt, orc, dev, T, E, K, N):
+def test_moe_tiled_path(bgt, orc, dev, forced, T, E, K, N):
+    # past the decode range: the 256 x 128 tile kernel (forced; automatic at
+    # K/128 > 32)
+    forced("tiled")
     name = bgt.w4a8_moe_kernel_name(T, E, T * min(2, E), K)
     say(f"moe {name} T={T} E={E} K={K} N={N}")
     assert name == TILED
     _run(bgt, orc, dev, T, E, K, N, seed=T * 37 + K + N)
 
 
-@pytest.fixture
-def forced(bgt):
-    yield bgt.set_prefill_kernel
-    bgt.set_prefill_kernel("auto")
+@pytest.mark.parametrize("T,E,K,N", [(1100, 8, 4096, 16), (65, 8, 512, 144), (600, 8, 14336, 16),
+                                     (2100, 8, 14336, 16), (520, 8, 4096, 32)])
+def test_moe_auto_tile_kernel(bgt, orc, dev, T, E, K, N):
+    # past the decode range, automatically: 256 x 256 tiles at K/128 <= 32,
+    # 256 x 128 beyond
+    name = bgt.w4a8_moe_kernel_name(T, E, T * min(2, E), K)
+    say(f"moe auto {name} T={T} E={E} K={K} N={N}")
+    assert name == (WIDE if K // 128 <= 32 else TILED)
+    _run(bgt, orc, dev, T, E, K, N, seed=T * 47 + K + N)
 
 
 @pytest.mark.parametrize("T,E,K,N", [(65, 8, 512, 144), (300, 8, 256, 48), (20, 8, 1152, 64),
@@ -201,8 +215,7 @@ SPREAD = [
 @pytest.mark.parametrize("T,E,K,N,busy", SPREAD)
 @pytest.mark.parametrize("kernel", ["tiled", "wide"])
 def test_moe_tile_spread(bgt, orc, dev, forced, T, E, K, N, busy, kernel):
-    if kernel == "wide":
-        forced("wide")
+    forced(kernel)
     routing = None
     if busy is not None:
         routing = np.asarray([[busy[(t + i) % len(busy)] for i in range(len(busy))]
