@@ -87,7 +87,7 @@ METRIC = "W4A8 integer-scale GEMM TOPS + HBM GB/s, K=4096 N=22016, M=1..4096"
 # profiles/*hbm_bytes.txt), keyed by (kernel, M). They hold only for the
 # kernel sources they were taken on: when a source file differs from the one
 # measured (sha256 prefix below), traffic is reported as null.
-TRAFFIC_SRC_SHA = {"gemm.hip": "ebe22251b782c750", "gemm_wide.hip": "6b38f7952bb95fee",
+TRAFFIC_SRC_SHA = {"gemm.hip": "db482199e1f895b1", "gemm_wide.hip": "6b38f7952bb95fee",
                    "gemm_w8is.hip": "b6d9392e0b9147a4"}
 # sources of the launches one call makes (the wide path also runs the 256 x 128
 # kernel over the last round's columns)
@@ -95,16 +95,16 @@ TRAFFIC_SRC = {"k_w4a8_decode<IS>": ("gemm.hip",), "k_w4a8_prefill<4,2,2,2,IS>":
                "k_w4a8_wide<IS>": ("gemm.hip", "gemm_wide.hip"), "k_w8a8_zp<9,32>": ("gemm.hip",),
                "k_w8is_split": ("gemm_w8is.hip",)}
 TRAFFIC = {
-    ("k_w4a8_decode<IS>", 1): 48187142,
-    ("k_w4a8_decode<IS>", 4): 48552999,
-    ("k_w4a8_decode<IS>", 16): 50000554,
-    ("k_w4a8_decode<IS>", 64): 58587896,
-    ("k_w4a8_prefill<4,2,2,2,IS>", 256): 79253996,
-    ("k_w4a8_wide<IS>", 512): 149896669,
-    ("k_w4a8_wide<IS>", 1024): 207380767,
-    ("k_w4a8_wide<IS>", 2048): 384208782,
-    ("k_w4a8_wide<IS>", 4096): 754846459,
-    ("k_w8a8_zp<9,32>", 256): 29681382,
+    ("k_w4a8_decode<IS>", 1): 48187961,
+    ("k_w4a8_decode<IS>", 4): 48550127,
+    ("k_w4a8_decode<IS>", 16): 50000285,
+    ("k_w4a8_decode<IS>", 64): 58573331,
+    ("k_w4a8_prefill<4,2,2,2,IS>", 256): 79253955,
+    ("k_w4a8_wide<IS>", 512): 149896594,
+    ("k_w4a8_wide<IS>", 1024): 207380705,
+    ("k_w4a8_wide<IS>", 2048): 384205949,
+    ("k_w4a8_wide<IS>", 4096): 754841719,
+    ("k_w8a8_zp<9,32>", 256): 29681378,
     ("k_w8is_split", 1): 62579868,
     ("k_w8is_split", 4): 62972922,
     ("k_w8is_split", 16): 64545584,
