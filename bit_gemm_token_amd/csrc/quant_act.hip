@@ -7,10 +7,10 @@
 // Quantization with q in [0, 255] and also produces the row sum of the codes,
 // the activation-side term of its zero-point expansion.
 //
-// One 256-thread workgroup per row. The row is read once with 16-byte loads,
+// One 1024-thread workgroup per row. The row is read once with 16-byte loads,
 // all of a thread's loads issued before the first is used (one round trip to
 // memory), and kept in registers (up to kVecPerThread float4 per thread); the row
-// statistic is a wave64 shuffle reduction followed by a 4-wave LDS step; the
+// statistic is a wave64 shuffle reduction followed by a 16-wave LDS step; the
 // codes are written as packed 4-byte words (one word per float4), so both
 // the read and the write of a row are fully coalesced.
 #include "device_common.h"
@@ -18,11 +18,13 @@
 
 namespace bgt {
 
-constexpr int kQThreads = 256;
+constexpr int kQThreads = 1024;
 constexpr int kQWaves = kQThreads / kWave;
-// float4 slots per thread held in registers: 4 for rows up to 4096 elements, 16
-// (rows up to 16384) beyond; longer rows stream their rest a second time
-constexpr int kVecShort = 4, kVecLong = 16;
+// float4 slots per thread held in registers: 1 for rows up to 4096 elements, 4
+// (rows up to 16384) beyond; longer rows stream their rest a second time. With
+// 1024 threads the per-thread work after the row statistic (the quotient and
+// rounding of each element) is a quarter of a 256-thread row's
+constexpr int kVecShort = 1, kVecLong = 4;
 
 template <bool ASYM>
 struct RowStat {
@@ -98,7 +100,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_rows_vec(
 
   // every slot of the row is requested before any is used (one round trip to
   // memory, not one per slot): slot u exists for the whole workgroup when
-  // u*256 < nvec (a uniform branch); a thread past the row's end in its last
+  // u*kQThreads < nvec (a uniform branch); a thread past the row's end in its last
   // slot loads the row's last vector (in bounds) and leaves it out below
   float4 cache[kVecPerThread];
 #pragma unroll
