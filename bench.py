@@ -88,7 +88,7 @@ METRIC = "W4A8 integer-scale GEMM TOPS + HBM GB/s, K=4096 N=22016, M=1..4096"
 # kernel sources they were taken on: when a source file differs from the one
 # measured (sha256 prefix below), traffic is reported as null.
 TRAFFIC_SRC_SHA = {"gemm.hip": "db482199e1f895b1", "gemm_wide.hip": "6b38f7952bb95fee",
-                   "gemm_w8is.hip": "b6d9392e0b9147a4"}
+                   "gemm_w8is.hip": "1301029dd06003ab"}
 # sources of the launches one call makes (the wide path also runs the 256 x 128
 # kernel over the last round's columns)
 TRAFFIC_SRC = {"k_w4a8_decode<IS>": ("gemm.hip",), "k_w4a8_prefill<4,2,2,2,IS>": ("gemm.hip",),
@@ -105,10 +105,10 @@ TRAFFIC = {
     ("k_w4a8_wide<IS>", 2048): 384205949,
     ("k_w4a8_wide<IS>", 4096): 754841719,
     ("k_w8a8_zp<9,32>", 256): 29681378,
-    ("k_w8is_split", 1): 62579868,
-    ("k_w8is_split", 4): 62972922,
-    ("k_w8is_split", 16): 64545584,
-    ("k_w8is_split", 64): 70844530,
+    ("k_w8is_split", 1): 62568942,
+    ("k_w8is_split", 4): 62961976,
+    ("k_w8is_split", 16): 64534582,
+    ("k_w8is_split", 64): 69604498,
 }
 
 

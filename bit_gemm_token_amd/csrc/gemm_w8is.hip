@@ -20,6 +20,10 @@
 //     activation fragments and scales in flight in registers, runs two MFMAs
 //     per group and row block and applies the group's integer scale with a
 //     24-bit multiply-add. The waves' int32 sums (exact, any order) meet in LDS.
+//     For M > 16 a workgroup takes two column tiles over one part of the
+//     groups instead (each activation fragment serves both tiles, halving the
+//     activation reads that dominate there); the parts' sums are added by the
+//     reduction kernel.
 //   tiled (M > 64): 64 x 64 output tiles, 8 waves, nine LDS-copy stages of one
 //     group (activations row-major with XOR-swizzled 16-byte chunks, weights
 //     straight from the fragment layout, the group's 64 scales), eight in
@@ -40,24 +44,35 @@ namespace bgt {
 // Split kernel
 // =====================================================================
 constexpr int kSplitMaxWaves = 16;
+constexpr int kSplitCTWaves = 8;                   // waves of a workgroup of several column tiles
 constexpr int split_max_waves(int mr) { return mr == 4 ? 8 : kSplitMaxWaves; }
+constexpr int split_bound(int mr, int ct) { return ct > 1 ? kSplitCTWaves : split_max_waves(mr); }
 
-template <int MR, int D, typename ST>
-__global__ __launch_bounds__(split_max_waves(MR) * 64) void k_w8is_split(
+// CT > 1 (M > 16): a workgroup covers CT adjacent column tiles over one of
+// `splits` parts of the groups, and each wave applies every activation
+// fragment it loads to all CT tiles, so the activation rows are read CT
+// times less often; workgroup b takes tiles CT*(b / splits) .. + CT - 1 and
+// part b % splits (splits divides 8, so each XCD's workgroups share one
+// part's rows in their L2). The part's int32 sums go to part[s] (M x N, exact
+// mod 2^32) for the reduction kernel, which adds the parts and converts.
+template <int MR, int D, int CT, typename ST>
+__global__ __launch_bounds__(split_bound(MR, CT) * 64) void k_w8is_split(
     const int8_t* __restrict__ qx, const float* __restrict__ sx, const uint4* __restrict__ qw,
     const ST* __restrict__ iscale, float inv_alpha, int M, int N, int K, OutY y,
-    int32_t* __restrict__ acc_out) {
+    int32_t* __restrict__ acc_out, int splits, int32_t* __restrict__ part) {
   __shared__ int32_t red[split_max_waves(MR) * MR * 4 * 64];
   const int G = K / kGroup;
   const int KS = blockDim.x / kWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   const int c = lane % 16, s4 = lane / 16;
-  const int t = blockIdx.x;
-  const int g0 = wave * G / KS, g1 = (wave + 1) * G / KS;   // this wave's groups
+  const int sp = CT > 1 ? (int)blockIdx.x % splits : 0;
+  const int t = CT > 1 ? ((int)blockIdx.x / splits) * CT : (int)blockIdx.x;
+  const int gb = CT > 1 ? sp * G / splits : 0, gw = CT > 1 ? (sp + 1) * G / splits - gb : G;
+  const int g0 = gb + wave * gw / KS, g1 = gb + (wave + 1) * gw / KS;   // this wave's groups
 
-  const uint4* wsrc = qw + (int64_t)t * G * 128 + lane;       // + 128 g + 64 h
-  const ST* ssrc = iscale + 16 * t + c;                       // + N g
+  const uint4* wsrc = qw + (int64_t)t * G * 128 + lane;       // + 128 G ct + 128 g + 64 h
+  const ST* ssrc = iscale + 16 * t + c;                       // + 16 ct + N g
   // activation fragments: row 16 rb + c, bytes 16 s4 .. of each 64-k half;
   // rows past M are zero
   const int8_t* xsrc[MR];
@@ -68,13 +83,16 @@ __global__ __launch_bounds__(split_max_waves(MR) * 64) void k_w8is_split(
     xsrc[rb] = qx + (int64_t)(xrow[rb] ? 16 * rb + c : 0) * K + 16 * s4;
   }
 
-  uint4 wb[D][2];
+  uint4 wb[D][CT][2];
   v4i xb[D][MR][2];
-  int32_t sb[D];
+  int32_t sb[D][CT];
   auto fetch = [&](int j, int g) {
-    wb[j][0] = load_u4_nt(wsrc + (int64_t)g * 128);
-    wb[j][1] = load_u4_nt(wsrc + (int64_t)g * 128 + 64);
-    sb[j] = (int32_t)ssrc[(int64_t)g * N];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      wb[j][ct][0] = load_u4_nt(wsrc + ((int64_t)ct * G + g) * 128);
+      wb[j][ct][1] = load_u4_nt(wsrc + ((int64_t)ct * G + g) * 128 + 64);
+      sb[j][ct] = (int32_t)ssrc[(int64_t)g * N + 16 * ct];
+    }
 #pragma unroll
     for (int rb = 0; rb < MR; ++rb)
 #pragma unroll
@@ -84,11 +102,13 @@ __global__ __launch_bounds__(split_max_waves(MR) * 64) void k_w8is_split(
       }
   };
 
-  int acc[MR][4];
+  int acc[CT][MR][4];
 #pragma unroll
-  for (int rb = 0; rb < MR; ++rb)
+  for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[rb][r] = 0;
+    for (int rb = 0; rb < MR; ++rb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[ct][rb][r] = 0;
 
 #pragma unroll
   for (int j = 0; j < D; ++j)
@@ -98,40 +118,54 @@ __global__ __launch_bounds__(split_max_waves(MR) * 64) void k_w8is_split(
 #pragma unroll
     for (int j = 0; j < D; ++j) {
       if (g + j < g1) {
-        int32_t sc = sb[j];
-        if (sizeof(ST) < 4) opaque_reg(sc);            // keep the 24-bit multiply-adds as written
-        const v4i b0 = {(int)wb[j][0].x, (int)wb[j][0].y, (int)wb[j][0].z, (int)wb[j][0].w};
-        const v4i b1 = {(int)wb[j][1].x, (int)wb[j][1].y, (int)wb[j][1].z, (int)wb[j][1].w};
 #pragma unroll
-        for (int rb = 0; rb < MR; ++rb) {
-          v4i p = __builtin_amdgcn_mfma_i32_16x16x64_i8(xb[j][rb][0], b0, v4i{0, 0, 0, 0}, 0, 0, 0);
-          p = __builtin_amdgcn_mfma_i32_16x16x64_i8(xb[j][rb][1], b1, p, 0, 0, 0);
+        for (int ct = 0; ct < CT; ++ct) {
+          int32_t sc = sb[j][ct];
+          if (sizeof(ST) < 4) opaque_reg(sc);          // keep the 24-bit multiply-adds as written
+          const v4i b0 = {(int)wb[j][ct][0].x, (int)wb[j][ct][0].y, (int)wb[j][ct][0].z,
+                          (int)wb[j][ct][0].w};
+          const v4i b1 = {(int)wb[j][ct][1].x, (int)wb[j][ct][1].y, (int)wb[j][ct][1].z,
+                          (int)wb[j][ct][1].w};
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[rb][r] = mad24(p[r], sc, acc[rb][r]);
+          for (int rb = 0; rb < MR; ++rb) {
+            v4i p = __builtin_amdgcn_mfma_i32_16x16x64_i8(xb[j][rb][0], b0, v4i{0, 0, 0, 0}, 0, 0, 0);
+            p = __builtin_amdgcn_mfma_i32_16x16x64_i8(xb[j][rb][1], b1, p, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[ct][rb][r] = mad24(p[r], sc, acc[ct][rb][r]);
+          }
         }
         if (g + j + D < g1) fetch(j, g + j + D);
       }
     }
   }
 
-  // the waves' sums meet in LDS: red[wave][rb*4 + r][lane]; then thread
-  // e < MR*256 adds element (rb*4 + r, lane) over the waves (wrapping adds)
+  // the waves' sums meet in LDS, one column tile at a time:
+  // red[wave][rb*4 + r][lane]; then thread e < MR*256 adds element
+  // (rb*4 + r, lane) over the waves (wrapping adds)
 #pragma unroll
-  for (int rb = 0; rb < MR; ++rb)
+  for (int ct = 0; ct < CT; ++ct) {
+    if (ct > 0) __syncthreads();                     // the previous tile's sums are read
 #pragma unroll
-    for (int r = 0; r < 4; ++r) red[(wave * MR * 4 + rb * 4 + r) * 64 + lane] = acc[rb][r];
-  __syncthreads();
-  for (int e = threadIdx.x; e < MR * 4 * 64; e += blockDim.x) {
-    const int i4 = e / 64, ln = e % 64;
-    const int row = 16 * (i4 / 4) + 4 * (ln / 16) + i4 % 4;
-    if (row >= M) continue;
-    uint32_t a = 0u;
-    for (int w = 0; w < KS; ++w) a += (uint32_t)red[(w * MR * 4 + i4) * 64 + ln];
-    const int32_t A = (int32_t)a;
-    const int64_t o = (int64_t)row * N + 16 * t + ln % 16;
-    const float t0 = (float)A * sx[row];
-    y.put(o, t0 * inv_alpha);
-    if (acc_out) acc_out[o] = A;
+    for (int rb = 0; rb < MR; ++rb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[(wave * MR * 4 + rb * 4 + r) * 64 + lane] = acc[ct][rb][r];
+    __syncthreads();
+    for (int e = threadIdx.x; e < MR * 4 * 64; e += blockDim.x) {
+      const int i4 = e / 64, ln = e % 64;
+      const int row = 16 * (i4 / 4) + 4 * (ln / 16) + i4 % 4;
+      if (row >= M) continue;
+      uint32_t a = 0u;
+      for (int w = 0; w < KS; ++w) a += (uint32_t)red[(w * MR * 4 + i4) * 64 + ln];
+      const int32_t A = (int32_t)a;
+      const int64_t o = (int64_t)row * N + 16 * (t + ct) + ln % 16;
+      if constexpr (CT > 1) {
+        part[(int64_t)sp * M * N + o] = A;
+      } else {
+        const float t0 = (float)A * sx[row];
+        y.put(o, t0 * inv_alpha);
+        if (acc_out) acc_out[o] = A;
+      }
+    }
   }
 }
 
@@ -556,6 +590,20 @@ static int split_waves(int64_t N, int64_t K, int mr) {
   return ks;
 }
 
+// M in 17..64: kSplitCT column tiles per split workgroup, whose groups split
+// into S parts when that pays: S doubles (to at most 8) while the workgroups
+// still fit the CUs and every part keeps at least two groups for each of its
+// eight waves. 1: the one-tile launch, no parts.
+constexpr int kSplitCT = 2;
+static int w8is_split_parts(int M, int N, int K) {
+  if (M <= 16 || (N / 16) % kSplitCT != 0) return 1;
+  const int64_t cus = device_cus(), wg = N / 16 / kSplitCT;
+  const int G = K / kGroup;
+  int s = 1;
+  while (s < 8 && wg * 2 * s <= cus && G / (2 * s) >= 2 * kSplitCTWaves) s *= 2;
+  return s;
+}
+
 // M > 64: the 256 x 128 tile copies 3x the bytes of a 64 x 64 tile per group
 // for 8x the work; with one workgroup per CU (LDS), pick the tile whose rounds
 // of 256 workgroups move fewer bytes in total. When the 256 x 128 tiles fill
@@ -583,18 +631,35 @@ static void launch_w8is_t(const int8_t* qx, const float* sx, const int8_t* qw, c
                           hipStream_t stream) {
   if (M <= 64) {
     const int mr = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+    const uint4* w = reinterpret_cast<const uint4*>(qw);
+    int splits = w8is_split_parts(M, N, K);
+    int32_t* part = nullptr;
+    if (splits > 1) {
+      part = split_workspace((size_t)splits * M * N * sizeof(int32_t), stream);
+      if (part == nullptr) splits = 1;
+    }
+    if (splits > 1) {
+      dim3 grid((unsigned)(N / 16 / kSplitCT * splits)), block(kSplitCTWaves * kWave);
+      if (mr == 2)
+        hipLaunchKernelGGL((k_w8is_split<2, 3, kSplitCT, ST>), grid, block, 0, stream, qx, sx, w,
+                           iscale, inv_alpha, M, N, K, y, acc_out, splits, part);
+      else
+        hipLaunchKernelGGL((k_w8is_split<4, 2, kSplitCT, ST>), grid, block, 0, stream, qx, sx, w,
+                           iscale, inv_alpha, M, N, K, y, acc_out, splits, part);
+      launch_split_reduce(part, splits, M, N, N, sx, inv_alpha, y, acc_out, stream);
+      return;
+    }
     const int ks = split_waves(N, K, mr);
     dim3 grid((unsigned)(N / 16)), block((unsigned)(ks * kWave));
-    const uint4* w = reinterpret_cast<const uint4*>(qw);
     if (mr == 1)
-      hipLaunchKernelGGL((k_w8is_split<1, 4, ST>), grid, block, 0, stream, qx, sx, w, iscale,
-                         inv_alpha, M, N, K, y, acc_out);
+      hipLaunchKernelGGL((k_w8is_split<1, 4, 1, ST>), grid, block, 0, stream, qx, sx, w, iscale,
+                         inv_alpha, M, N, K, y, acc_out, 1, nullptr);
     else if (mr == 2)
-      hipLaunchKernelGGL((k_w8is_split<2, 3, ST>), grid, block, 0, stream, qx, sx, w, iscale,
-                         inv_alpha, M, N, K, y, acc_out);
+      hipLaunchKernelGGL((k_w8is_split<2, 3, 1, ST>), grid, block, 0, stream, qx, sx, w, iscale,
+                         inv_alpha, M, N, K, y, acc_out, 1, nullptr);
     else
-      hipLaunchKernelGGL((k_w8is_split<4, 2, ST>), grid, block, 0, stream, qx, sx, w, iscale,
-                         inv_alpha, M, N, K, y, acc_out);
+      hipLaunchKernelGGL((k_w8is_split<4, 2, 1, ST>), grid, block, 0, stream, qx, sx, w, iscale,
+                         inv_alpha, M, N, K, y, acc_out, 1, nullptr);
     return;
   }
   const int G = K / kGroup;

@@ -393,10 +393,14 @@ int bgt_pack_weights_int8(const float* w, int64_t K, int64_t N, int64_t group, i
  *   y       M x N of element type y_type (fp32 result rounded once).
  *   acc_out optional M x N int32 (NULL = not written): A_ij itself.
  * Requirements: as bgt_w4a8_gemm_is; qx, qw, iscale, y, acc_out 16-byte aligned.
- * For M > 64 with few 256 x 128 tiles (they fill at most half of the CUs) the
- * groups split into S parts whose int32 sums meet in the library's split-K
- * workspace (see bgt_w4a8_workspace_bytes: S*M*N*4 bytes, allocated on first
- * need, never during graph capture, where the GEMM then runs unsplit).
+ * The groups split into S parts whose int32 sums meet in the library's
+ * split-K workspace (the buffer described at bgt_w4a8_workspace_bytes:
+ * S*M*N*4 bytes, allocated on first need, never during graph capture, where
+ * the GEMM then runs unsplit) in two cases: for M > 64 with few 256 x 128
+ * tiles (they fill at most half of the CUs), and for 16 < M <= 64 with N/16
+ * even, where a workgroup takes two 16-column tiles over one part (S doubles
+ * to at most 8 while the workgroups fit the CUs and every part keeps at least
+ * 16 groups).
  */
 int bgt_w8a8_gemm_is(const int8_t* qx, const float* sx, const int8_t* qw, const void* iscale,
                      int width, int alpha, int64_t M, int64_t N, int64_t K, void* y, int y_type,

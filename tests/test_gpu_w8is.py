@@ -100,7 +100,9 @@ SHAPES = [(1, 128, 16), (1, 4096, 64), (3, 384, 48), (16, 1152, 96), (5, 14336, 
           (17, 2048, 80), (33, 512, 144), (64, 4096, 16), (40, 256, 208),
           (65, 512, 144), (128, 4096, 64), (200, 640, 400), (257, 256, 16),          # tiled
           (96, 14336, 48), (130, 1280, 80),
-          (1024, 512, 4096), (1000, 384, 4000), (1100, 4096, 2048)]               # wide
+          (1024, 512, 4096), (1000, 384, 4000), (1100, 4096, 2048),               # wide
+          (20, 4096, 96), (40, 4480, 64), (33, 8192, 160), (64, 14336, 32),        # split, 2 tiles
+          (17, 4096, 4096)]                                                          # over parts
 
 
 @pytest.mark.parametrize("M,K,N", SHAPES)
@@ -119,7 +121,8 @@ def test_w8is_gemm(bgt, orc, dev, M, K, N):
     np.testing.assert_array_equal(got.view(np.int32), oy.astype(np.float32).view(np.int32))
 
 
-@pytest.mark.parametrize("M,K,N", [(2, 2048, 64), (20, 384, 48), (70, 1024, 80), (300, 256, 144)])
+@pytest.mark.parametrize("M,K,N", [(2, 2048, 64), (20, 384, 48), (70, 1024, 80), (300, 256, 144),
+                                   (24, 4096, 64), (60, 8192, 32)])
 @pytest.mark.parametrize("width", [1, 2])
 def test_w8is_narrow_scales(bgt, orc, dev, width, M, K, N):
     # width 1: alpha 2^14 keeps every integer scale below 2^8; width 2: alpha
@@ -181,7 +184,7 @@ def test_w8is_wide_narrow_scales(bgt, orc, dev, width):
 
 
 @pytest.mark.parametrize("kind", ["f16", "bf16"])
-@pytest.mark.parametrize("M,K,N", [(4, 2048, 48), (100, 512, 80)])
+@pytest.mark.parametrize("M,K,N", [(4, 2048, 48), (100, 512, 80), (40, 4096, 64)])
 def test_w8is_half_outputs(bgt, orc, dev, kind, M, K, N):
     say(f"w8a8_gemm_is y={kind} M={M} K={K} N={N}")
     oq, os_, ow = _case(orc, 19 * M + K, M, K, N)
@@ -214,7 +217,7 @@ def test_w8is_wraps_like_the_oracle(bgt, orc, dev, m, N):
     np.testing.assert_array_equal(y.cpu().numpy().view(np.int32), oy.astype(np.float32).view(np.int32))
 
 
-@pytest.mark.parametrize("M", [16, 4096])
+@pytest.mark.parametrize("M", [16, 64, 4096])
 def test_w8is_down_proj_sampled(bgt, orc, dev, M):
     """The LLaMA-3-8B down projection (K = 14336, N = 4096), packed on the GPU
     (layout and scales checked whole), in the launch the bench times; sampled
