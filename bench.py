@@ -87,7 +87,7 @@ METRIC = "W4A8 integer-scale GEMM TOPS + HBM GB/s, K=4096 N=22016, M=1..4096"
 # profiles/*hbm_bytes.txt), keyed by (kernel, M). They hold only for the
 # kernel sources they were taken on: when a source file differs from the one
 # measured (sha256 prefix below), traffic is reported as null.
-TRAFFIC_SRC_SHA = {"gemm.hip": "db482199e1f895b1", "gemm_wide.hip": "6b38f7952bb95fee",
+TRAFFIC_SRC_SHA = {"gemm.hip": "7c95a1badb659f9e", "gemm_wide.hip": "6b38f7952bb95fee",
                    "gemm_w8is.hip": "1301029dd06003ab"}
 # sources of the launches one call makes (the wide path also runs the 256 x 128
 # kernel over the last round's columns)
@@ -95,16 +95,16 @@ TRAFFIC_SRC = {"k_w4a8_decode<IS>": ("gemm.hip",), "k_w4a8_prefill<4,2,2,2,IS>":
                "k_w4a8_wide<IS>": ("gemm.hip", "gemm_wide.hip"), "k_w8a8_zp<9,32>": ("gemm.hip",),
                "k_w8is_split": ("gemm_w8is.hip",)}
 TRAFFIC = {
-    ("k_w4a8_decode<IS>", 1): 48187961,
-    ("k_w4a8_decode<IS>", 4): 48550127,
-    ("k_w4a8_decode<IS>", 16): 50000285,
-    ("k_w4a8_decode<IS>", 64): 58573331,
-    ("k_w4a8_prefill<4,2,2,2,IS>", 256): 79253955,
-    ("k_w4a8_wide<IS>", 512): 149896594,
-    ("k_w4a8_wide<IS>", 1024): 207380705,
-    ("k_w4a8_wide<IS>", 2048): 384205949,
-    ("k_w4a8_wide<IS>", 4096): 754841719,
-    ("k_w8a8_zp<9,32>", 256): 29681378,
+    ("k_w4a8_decode<IS>", 1): 48194641,
+    ("k_w4a8_decode<IS>", 4): 48561393,
+    ("k_w4a8_decode<IS>", 16): 50010826,
+    ("k_w4a8_decode<IS>", 64): 58482425,
+    ("k_w4a8_prefill<4,2,2,2,IS>", 256): 79241723,
+    ("k_w4a8_wide<IS>", 512): 149896694,
+    ("k_w4a8_wide<IS>", 1024): 207369511,
+    ("k_w4a8_wide<IS>", 2048): 384209919,
+    ("k_w4a8_wide<IS>", 4096): 754830981,
+    ("k_w8a8_zp<9,32>", 256): 29681405,
     ("k_w8is_split", 1): 62568942,
     ("k_w8is_split", 4): 62961976,
     ("k_w8is_split", 16): 64534582,

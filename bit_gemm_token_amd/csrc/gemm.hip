@@ -1345,12 +1345,14 @@ constexpr int decode_depth(int mr) { return mr == 1 ? 16 : 8; }
 // waves of half the VALU work each (16 waves would leave too few registers)
 constexpr int decode_row_split(int mr, int w) { return mr == 4 && w <= 6 ? 2 : 1; }
 // waves per 16-column tile splitting K (integer scale, one row block, 16 or 32
-// groups): 2-wave workgroups (N/16 <= 512 tiles) take 8 waves, each streaming
-// a quarter of the tile's groups, all of them in flight (one round trip to
-// memory instead of two); their sums meet in LDS. (On 4-wave workgroups a
-// split in two measured no faster: 688 tiles already fill the CUs.)
+// groups): workgroups of one or two tiles (N/16 <= 512 tiles) take 4 waves per
+// tile, each streaming a quarter of the tile's groups, all of them in flight
+// (one round trip to memory instead of two); their sums meet in LDS. Where
+// that split applies and N/16 <= 256, the tiles go one per workgroup (4
+// waves), so N = 4096 runs on 256 workgroups rather than 128 of two tiles. (On 4-wave workgroups
+// a split in two measured no faster: 688 tiles already fill the CUs.)
 constexpr int decode_k_split(int mr, int w, bool fs, int g, int gq) {
-  return mr != 1 || fs || g != gq || (g != 16 && g != 32) || w != 2 ? 1 : 4;
+  return mr != 1 || fs || g != gq || (g != 16 && g != 32) || (w != 2 && w != 1) ? 1 : 4;
 }
 
 // K = 11008 (86 groups, run as 96 with the last ten masked) and K = 14336 (112)
@@ -1526,6 +1528,12 @@ static void launch_decode(int mr, hipStream_t stream, const int8_t* qx, const fl
                           const uint4* pk, const ST* iscale, const float* fscale, float inv_alpha,
                           int M, int N, OutY y, int32_t* acc_out) {
   const int w = decode_waves(N / 16, mr);
+  if constexpr (!FS && GQ == G && (G == 16 || G == 32)) {
+    if (w == 2 && N / 16 <= 256) {
+      launch_decode_w<FS, G, GQ, 1, 1>(1, stream, qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out);
+      return;
+    }
+  }
   if (w == 2) {
     launch_decode_w<FS, G, GQ, 2, 1>(1, stream, qx, sx, pk, iscale, fscale, inv_alpha, M, N, y, acc_out);
   } else if constexpr (G > 32) {
@@ -1710,17 +1718,19 @@ hipError_t launch_w4a8(bool float_scale, const int8_t* qx, const float* sx, cons
 // Quantize + GEMM in one launch for M <= 4 on the decode path (the decode
 // kernel quantizes the fp32 rows itself); otherwise the quantizer and the GEMM.
 // 16 or 32 groups: X staged in fragment order; waves per workgroup as for the
-// unfused decode launch (2-wave workgroups split K over four waves per tile),
-// raised until a thread's share of the rows (held until they are quantized)
-// is at most 8 groups of 4 elements, M*K/4 <= 8*64*waves: the quantizing
-// prologue's critical path grows with that share. 86 groups (run as 96) and
+// unfused decode launch (workgroups of one or two tiles split K over four
+// waves per tile; one tile where the 4 waves' share of the rows stays within
+// 8 groups of 4 elements per thread), raised until a thread's share of the
+// rows (held until they are quantized) is at most 8 groups of 4 elements,
+// M*K/4 <= 8*64*waves: the quantizing prologue's critical path grows with
+// that share. 86 groups (run as 96) and
 // 112: the rows staged compactly, so any K fits LDS, on 2-wave workgroups
 // splitting K in four (N/16 <= 512 tiles) or on 8-wave ones.
 template <int IT, typename ST, int W, int GG, int GQQ>
 static void launch_linear_fused_g(const void* x, int ldx, const uint4* pk, const ST* iscale,
                                   float inv_alpha, int M, int N, int8_t* q_out, float* s_out,
                                   OutY y, hipStream_t stream) {
-  constexpr int KS = W == 2 ? 4 : 1;
+  constexpr int KS = W <= 2 ? 4 : 1;
   constexpr bool CX = !(GG == 16 || GG == 32);
   const dim3 grid((N / 16 + W - 1) / W), block(W * KS * kWave);
   hipLaunchKernelGGL((k_w4a8_decode<false, W, decode_depth(1), GG, 1, ST, true, IT, false, GQQ, 1,
@@ -1753,8 +1763,11 @@ static void launch_linear_fused(const void* x, int ldx, const uint8_t* packed, c
   if (K / kGroup == 86 || K / kGroup == 112) w = w == 2 ? 2 : 8;   // 2 waves split K in 4, else 8
   else
     while (w < 8 && M * K > 2048 * w * decode_k_split(1, w, false, 32, 32)) w += 2;
+  if (w == 2 && N / 16 <= 256 && (K / kGroup == 16 || K / kGroup == 32) && M * K <= 2048 * 4) w = 1;
   const uint4* pk = reinterpret_cast<const uint4*>(packed);
-  if (w == 2)
+  if (w == 1)
+    launch_linear_fused_w<IT, ST, 1>(x, ldx, pk, iscale, inv_alpha, M, N, K, q_out, s_out, y, stream);
+  else if (w == 2)
     launch_linear_fused_w<IT, ST, 2>(x, ldx, pk, iscale, inv_alpha, M, N, K, q_out, s_out, y, stream);
   else if (w == 4)
     launch_linear_fused_w<IT, ST, 4>(x, ldx, pk, iscale, inv_alpha, M, N, K, q_out, s_out, y, stream);

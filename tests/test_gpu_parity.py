@@ -213,9 +213,11 @@ SHAPES = [(1, 128, 16), (3, 384, 48), (16, 1024, 144), (17, 512, 64), (33, 256, 
           # four row blocks split over two waves per tile on 4- and 6-wave workgroups
           # (the second wave's last block ragged at M = 49, 57, 61)
           (49, 4096, 4096), (57, 2048, 20480), (61, 4096, 16400),
-          # one row block on 2-wave workgroups, K split over four waves per tile
-          # (8 or 4 groups each; the last workgroup partly past N at 8208 columns)
+          # one row block, K split over four waves per tile (8 or 4 groups each): one tile
+          # per workgroup up to 256 tiles, two above (the last workgroup partly past N at
+          # 8176 columns)
           (16, 4096, 4096), (7, 2048, 8192), (12, 4096, 8176), (1, 2048, 16),
+          (9, 4096, 4080), (3, 2048, 400),
           # 86 groups (run as 96, the last ten masked) and 112 groups, one row block on 2-wave
           # (N <= 8192) and 4-wave workgroups; more rows take the weight-split kernels
           (1, 11008, 64), (16, 11008, 80), (2, 11008, 8208), (5, 14336, 48), (16, 14336, 4096),
