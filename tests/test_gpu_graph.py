@@ -159,7 +159,9 @@ def _replay_check(dev, run, outs, refill, reps=4):
 
 
 def test_graph_replays_match_eager_w8a8_is(dev, bgt):
-    K, N = 1024, 512
+    # M = 3: one column tile per workgroup; M = 40: two tiles per workgroup over two parts of the
+    # groups plus the reduction; M = 130: the 256 x 128 tile with K split, plus the reduction
+    K, N = 4096, 512
     Ms = (3, 40, 130)
     print(f"graph replay w8a8_is: K={K} N={N} M={Ms}", flush=True)
     w = synth.weights(12, K, N, std=0.02, outlier_prob=0.001)
