@@ -102,7 +102,7 @@ SHAPES = [(1, 128, 16), (1, 4096, 64), (3, 384, 48), (16, 1152, 96), (5, 14336, 
           (96, 14336, 48), (130, 1280, 80),
           (1024, 512, 4096), (1000, 384, 4000), (1100, 4096, 2048),               # wide
           (20, 4096, 96), (40, 4480, 64), (33, 8192, 160), (64, 14336, 32),        # split, 2 tiles
-          (17, 4096, 4096)]                                                          # over parts
+          (17, 4096, 4096), (17, 32768, 32)]                       # over parts (2 .. 8 parts)
 
 
 @pytest.mark.parametrize("M,K,N", SHAPES)
